@@ -1,0 +1,240 @@
+"""Oracle for the sparsely-gated MoE forward pass (test infrastructure only).
+
+A thin ctypes wrapper over ``moe_oracle.cpp``: a plain CPU implementation of
+the pages' equations in fp64, shared with nothing on the GPU path. Only the
+tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg may
+import this package.
+
+Inputs are numpy arrays in the storage layouts of ``datagen`` (fp32 arrays as
+float32, bf16 arrays as uint16 bit patterns); outputs are float64/int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_D = ctypes.c_double
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with g++/OpenMP (plain -O2, no fast-math)."""
+    global _lib
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-fopenmp",
+                               _SRC, "-o", tmp])
+        os.replace(tmp, _LIB_PATH)
+        _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_softplus.argtypes = [_D]
+        lib.oracle_softplus.restype = _D
+        lib.oracle_phi.argtypes = [_D]
+        lib.oracle_phi.restype = _D
+        lib.oracle_cv_squared.argtypes = [_I, _P]
+        lib.oracle_cv_squared.restype = _D
+        lib.oracle_gate.argtypes = [_I64, _P, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D, _I,
+                                    _P, _P, _P, _P, _P, _P]
+        lib.oracle_load.argtypes = [_I64, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D, _I, _P]
+        lib.oracle_y_rows.argtypes = [_I64, _P, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D,
+                                      _I, _P, _P, _P, _P, _I, _P]
+        lib.oracle_expert_pairs.argtypes = [_I64, _P, _P, _I, _I, _P, _I, _P, _P, _P, _P, _I, _P]
+        lib.oracle_route.argtypes = [_I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
+        lib.oracle_forward.argtypes = [_I64, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D,
+                                       _I, _P, _P, _P, _P, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P]
+        for f in ("oracle_gate", "oracle_load", "oracle_y_rows", "oracle_expert_pairs",
+                  "oracle_route", "oracle_forward"):
+            getattr(lib, f).restype = _I
+        _lib = lib
+    return _lib
+
+
+def _arr(a, dtype=None):
+    if a is None:
+        return None, 0
+    a = np.ascontiguousarray(a) if dtype is None else np.ascontiguousarray(a, dtype=dtype)
+    if a.dtype == np.uint16:
+        return a, 1
+    if a.dtype != np.float32:
+        a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, 0
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"{what}: oracle rejected the arguments (code {rc})")
+
+
+def softplus(u: float) -> float:
+    return _load().oracle_softplus(float(u))
+
+
+def phi(z: float) -> float:
+    return _load().oracle_phi(float(z))
+
+
+def cv_squared(v) -> float:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    return _load().oracle_cv_squared(v.size, v.ctypes.data)
+
+
+class _Gate:
+    """Common gate arguments, kept alive for the duration of a call."""
+
+    def __init__(self, inp: Dict[str, np.ndarray], train: bool):
+        self.x, self.x_dt = _arr(inp["x"])
+        self.wg, self.w_dt = _arr(inp["w_gate"])
+        self.wn, wn_dt = _arr(inp["w_noise"])
+        if wn_dt != self.w_dt:
+            raise ValueError("w_gate and w_noise must share a dtype")
+        bg = inp.get("gate_bias")
+        self.bg = None if bg is None else np.ascontiguousarray(bg, dtype=np.float32)
+        eps = inp.get("eps") if train else None
+        self.eps = None if eps is None else np.ascontiguousarray(eps, dtype=np.float32)
+        self.B, self.d = self.x.shape
+        self.n = self.wg.shape[0]
+        if self.wg.shape != (self.n, self.d) or self.wn.shape != (self.n, self.d):
+            raise ValueError("w_gate/w_noise must be [n, d]")
+        if self.eps is not None and self.eps.shape != (self.B, self.n):
+            raise ValueError("eps must be [B, n]")
+
+    def args(self):
+        return (_ptr(self.x), self.x_dt, _ptr(self.wg), _ptr(self.wn), self.w_dt, _ptr(self.bg),
+                _ptr(self.eps))
+
+
+def gate(inp: Dict[str, np.ndarray], k: int, train: bool = True, noise_floor: float = 1e-2,
+         rows: Optional[Sequence[int]] = None, decide_fp32: bool = True,
+         want_logits: bool = False) -> Dict[str, np.ndarray]:
+    """Noisy top-k gating for all rows or a list of rows."""
+    g = _Gate(inp, train)
+    n = g.n
+    rws = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = g.B if rws is None else rws.size
+    out = {"topk_idx": np.empty((nr, k), np.int32), "topk_gate": np.empty((nr, k), np.float64),
+           "thresh": np.empty((nr, 2), np.float64)}
+    if want_logits:
+        for key in ("clean", "sigma", "H"):
+            out[key] = np.empty((nr, n), np.float64)
+    rc = _load().oracle_gate(nr, _ptr(rws), g.d, n, k, *g.args(), int(train), float(noise_floor),
+                             int(decide_fp32), _ptr(out.get("clean")), _ptr(out.get("sigma")),
+                             _ptr(out.get("H")), _ptr(out["topk_idx"]), _ptr(out["topk_gate"]),
+                             _ptr(out["thresh"]))
+    _check(rc, "gate")
+    return out
+
+
+def load(inp: Dict[str, np.ndarray], k: int, train: bool = True, noise_floor: float = 1e-2,
+         decide_fp32: bool = True) -> np.ndarray:
+    """Load vector (eq 10) over the whole batch."""
+    g = _Gate(inp, train)
+    out = np.empty(g.n, np.float64)
+    rc = _load().oracle_load(g.B, g.d, g.n, k, *g.args(), int(train), float(noise_floor),
+                             int(decide_fp32), out.ctypes.data)
+    _check(rc, "load")
+    return out
+
+
+def _experts(inp):
+    w1, e_dt = _arr(inp["w1"])
+    w2, e2 = _arr(inp["w2"])
+    b1, _ = _arr(inp.get("b1"))
+    b2, _ = _arr(inp.get("b2"))
+    if e2 != e_dt:
+        raise ValueError("w1 and w2 must share a dtype")
+    for b in (b1, b2):
+        if b is not None and (b.dtype == np.uint16) != (e_dt == 1):
+            raise ValueError("biases must share the expert dtype")
+    h = w1.shape[1]
+    return w1, b1, w2, b2, e_dt, h
+
+
+def y_rows(inp: Dict[str, np.ndarray], k: int, rows: Optional[Sequence[int]] = None,
+           train: bool = True, noise_floor: float = 1e-2, decide_fp32: bool = True) -> np.ndarray:
+    """MoE output (eq 1) for all rows or a list of rows."""
+    g = _Gate(inp, train)
+    w1, b1, w2, b2, e_dt, h = _experts(inp)
+    rws = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = g.B if rws is None else rws.size
+    y = np.empty((nr, g.d), np.float64)
+    rc = _load().oracle_y_rows(nr, _ptr(rws), g.d, h, g.n, k, *g.args(), int(train),
+                               float(noise_floor), int(decide_fp32), _ptr(w1), _ptr(b1), _ptr(w2),
+                               _ptr(b2), e_dt, y.ctypes.data)
+    _check(rc, "y_rows")
+    return y
+
+
+def expert_pairs(inp: Dict[str, np.ndarray], tokens: Sequence[int], experts: Sequence[int]) -> np.ndarray:
+    """E_e(x_t) for each listed (token, expert) pair."""
+    x, x_dt = _arr(inp["x"])
+    w1, b1, w2, b2, e_dt, h = _experts(inp)
+    t = np.ascontiguousarray(tokens, dtype=np.int64)
+    e = np.ascontiguousarray(experts, dtype=np.int32)
+    if t.shape != e.shape:
+        raise ValueError("tokens and experts must have the same length")
+    d = x.shape[1]
+    out = np.empty((t.size, d), np.float64)
+    rc = _load().oracle_expert_pairs(t.size, t.ctypes.data, e.ctypes.data, d, h, _ptr(x), x_dt,
+                                     _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), e_dt, out.ctypes.data)
+    _check(rc, "expert_pairs")
+    return out
+
+
+def route(topk_idx: np.ndarray, topk_gate: np.ndarray, n: int) -> Dict[str, np.ndarray]:
+    """Stable expert-major routing of the (token, slot) pairs, plus Importance."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    gates = np.ascontiguousarray(topk_gate, dtype=np.float64)
+    B, k = idx.shape
+    out = {"counts": np.empty(n, np.int32), "offsets": np.empty(n + 1, np.int32),
+           "perm_token": np.empty(B * k, np.int32), "perm_gate": np.empty(B * k, np.float64),
+           "slot_pos": np.empty(B * k, np.int32), "importance": np.empty(n, np.float64)}
+    rc = _load().oracle_route(B, n, k, idx.ctypes.data, gates.ctypes.data,
+                              *[out[key].ctypes.data for key in ("counts", "offsets", "perm_token",
+                                                                 "perm_gate", "slot_pos",
+                                                                 "importance")])
+    _check(rc, "route")
+    return out
+
+
+def forward(inp: Dict[str, np.ndarray], k: int, train: bool = True, noise_floor: float = 1e-2,
+            w_importance: float = 0.1, w_load: float = 0.1,
+            decide_fp32: bool = True) -> Dict[str, np.ndarray]:
+    """The whole forward pass of the implementation notes on the batch."""
+    g = _Gate(inp, train)
+    w1, b1, w2, b2, e_dt, h = _experts(inp)
+    B, d, n = g.B, g.d, g.n
+    out = {"y": np.empty((B, d), np.float64), "topk_idx": np.empty((B, k), np.int32),
+           "topk_gate": np.empty((B, k), np.float64), "thresh": np.empty((B, 2), np.float64),
+           "importance": np.empty(n, np.float64), "load": np.empty(n, np.float64),
+           "losses": np.empty(3, np.float64)}
+    rc = _load().oracle_forward(B, d, h, n, k, *g.args(), int(train), float(noise_floor),
+                                int(decide_fp32), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), e_dt,
+                                float(w_importance), float(w_load),
+                                *[out[key].ctypes.data for key in ("y", "topk_idx", "topk_gate",
+                                                                   "thresh", "importance", "load",
+                                                                   "losses")])
+    _check(rc, "forward")
+    return out

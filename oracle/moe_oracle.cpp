@@ -1,0 +1,448 @@
+// Oracle: a plain, slow CPU definition of the sparsely-gated MoE forward pass.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or load
+// this file; only the tests, the smoke check and the benchmark's CPU-baseline
+// leg use it. It shares no code with the HIP path.
+//
+// Source of every formula: "Mixture of Experts: Outrageously Large Neural
+// Networks" (intuitivepapers.ai explainer of Shazeer et al., 2017), sections
+// "How a mixture-of-experts layer works" (eq 1), "Noisy top-k gating"
+// (eqs 2-5), "Why experts collapse, and the balancing losses" (eqs 6-7 and the
+// coefficient of variation), "A differentiable count of examples" (eqs 8-11),
+// "Hierarchical MoE" (eq 12) and "Implementation notes" (the forward-pass
+// pseudo-code, whose step order is followed here).
+//
+// Arithmetic: every sum and transcendental in double precision. Inputs are the
+// same rounded fp32 or bf16 values the GPU reads, widened exactly. Loops are
+// plain; OpenMP splits only independent rows or experts, and every reduction
+// over rows runs in a fixed block order, so results do not depend on the
+// thread count.
+//
+// Readings where the pages are open (each also listed in the design notes):
+//  * noise std = Softplus(x.W_noise) + noise_floor; the implementation notes
+//    add a floor of 0.01, eq 4 has none, so the floor is a parameter.
+//  * Selection order: larger noisy logit first, equal logits -> lower expert
+//    index first. The selection is decided on the logits rounded to fp32 (the
+//    precision the GPU decides in) when decide_fp32 != 0; every value that is
+//    returned (gates, thresholds, P) is computed from the fp64 logits.
+//  * Threshold of eq 8: (k+1)-th largest logit if expert i is in the top k,
+//    k-th largest otherwise; with k == n there is no (k+1)-th and P = 1.
+//  * With train == 0 the noise is off, H = clean, and P(x, i) is the hard
+//    indicator [i in top k] (the sigma -> 0 limit of eq 9).
+//  * CV^2 uses the population variance (the worked example divides the sum of
+//    squared deviations by the number of experts); CV^2 = 0 when n == 1 or
+//    the mean is 0.
+//  * An optional gate bias is added to the clean logit (so it enters H and the
+//    numerator of eq 9 alike).
+//  * Experts: E_i(x) = ReLU(x.W1_i + b1_i).W2_i + b2_i with optional biases.
+//
+// Weight layouts: w_gate/w_noise [n][d] (row i = expert i), w1 [n][h][d]
+// (row j = hidden unit j), w2 [n][d][h] (row c = output unit c).
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <numeric>
+#include <vector>
+
+namespace {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+constexpr int64_t kRowBlock = 256;  // fixed reduction blocks over rows
+
+inline double widen(const void* p, int64_t i, int dt) {
+  if (dt == kF32) return (double)((const float*)p)[i];
+  uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// Widen a contiguous run [off, off+len) into dst.
+void widen_run(const void* p, int64_t off, int64_t len, int dt, double* dst) {
+  for (int64_t i = 0; i < len; ++i) dst[i] = widen(p, off + i, dt);
+}
+
+// Softplus(u) = log(1 + e^u), evaluated in the form that cannot overflow.
+inline double softplus(double u) { return std::max(u, 0.0) + std::log1p(std::exp(-std::fabs(u))); }
+
+// Standard normal CDF.
+inline double Phi(double z) { return 0.5 * std::erfc(-z / std::sqrt(2.0)); }
+
+struct GateArgs {
+  int d, n, k;
+  const void* x;
+  int x_dt;
+  const void* wg;
+  const void* wn;
+  int w_dt;
+  const float* bg;   // [n] or null
+  const float* eps;  // [B][n], or null when train == 0
+  int64_t eps_row_stride;
+  int train;
+  double floor;
+  int decide_fp32;
+};
+
+// Per-row gate state.
+struct RowGate {
+  std::vector<double> clean, sigma, H;
+  std::vector<int> order;  // all n experts, best first
+  std::vector<int> in_top; // 1 if expert is one of the k selected
+  double vk = 0, vk1 = 0;  // k-th and (k+1)-th largest logits
+  std::vector<double> gate;  // [k] in rank order
+  explicit RowGate(int n) : clean(n), sigma(n), H(n), order(n), in_top(n) {}
+};
+
+// Eq 4 (noisy logits), then the keep-top-k of eqs 3/5 and the softmax over
+// the kept logits, for token t.
+void gate_row(const GateArgs& g, int64_t t, RowGate& r, std::vector<double>& xrow,
+              std::vector<double>& wrow) {
+  const int d = g.d, n = g.n, k = g.k;
+  widen_run(g.x, t * (int64_t)d, d, g.x_dt, xrow.data());
+  for (int i = 0; i < n; ++i) {
+    // clean logit (x . W_g)_i (+ bias)
+    widen_run(g.wg, (int64_t)i * d, d, g.w_dt, wrow.data());
+    double c = 0.0;
+    for (int j = 0; j < d; ++j) c += xrow[j] * wrow[j];
+    if (g.bg) c += (double)g.bg[i];
+    r.clean[i] = c;
+    if (g.train) {
+      widen_run(g.wn, (int64_t)i * d, d, g.w_dt, wrow.data());
+      double u = 0.0;
+      for (int j = 0; j < d; ++j) u += xrow[j] * wrow[j];
+      double s = softplus(u) + g.floor;
+      r.sigma[i] = s;
+      r.H[i] = c + (double)g.eps[t * g.eps_row_stride + i] * s;
+    } else {
+      r.sigma[i] = 0.0;
+      r.H[i] = c;
+    }
+  }
+  // top_k(H, k+1): rank experts by logit, larger first, ties to the lower index.
+  std::iota(r.order.begin(), r.order.end(), 0);
+  if (g.decide_fp32) {
+    std::vector<float> key(n);
+    for (int i = 0; i < n; ++i) key[i] = (float)r.H[i];
+    std::stable_sort(r.order.begin(), r.order.end(), [&](int a, int b) { return key[a] > key[b]; });
+  } else {
+    std::stable_sort(r.order.begin(), r.order.end(), [&](int a, int b) { return r.H[a] > r.H[b]; });
+  }
+  std::fill(r.in_top.begin(), r.in_top.end(), 0);
+  for (int j = 0; j < k; ++j) r.in_top[r.order[j]] = 1;
+  r.vk = r.H[r.order[k - 1]];
+  r.vk1 = (k < n) ? r.H[r.order[k]] : -std::numeric_limits<double>::infinity();
+  // softmax over the kept logits (the others are -inf and get gate 0)
+  r.gate.assign(k, 0.0);
+  const double top = r.H[r.order[0]];
+  double z = 0.0;
+  for (int j = 0; j < k; ++j) {
+    r.gate[j] = std::exp(r.H[r.order[j]] - top);
+    z += r.gate[j];
+  }
+  for (int j = 0; j < k; ++j) r.gate[j] /= z;
+}
+
+// Eqs 8-9: probability that expert i stays in the top k under a fresh draw of
+// its own noise, the other experts' noise held fixed.
+inline double prob_in_top_k(const GateArgs& g, const RowGate& r, int i) {
+  if (!g.train) return r.in_top[i] ? 1.0 : 0.0;
+  const double thr = r.in_top[i] ? r.vk1 : r.vk;  // kth_excluding(H, k, i)
+  return Phi((r.clean[i] - thr) / r.sigma[i]);
+}
+
+// E_i(x) for one token row: ReLU(W1_i x + b1_i), then W2_i . hidden + b2_i.
+void expert_apply(int d, int h, const double* xrow, const void* w1, const void* b1,
+                  const void* w2, const void* b2, int e_dt, int64_t e, double* out,
+                  std::vector<double>& hid, std::vector<double>& wrow) {
+  for (int j = 0; j < h; ++j) {
+    widen_run(w1, (e * h + j) * (int64_t)d, d, e_dt, wrow.data());
+    double a = 0.0;
+    for (int c = 0; c < d; ++c) a += xrow[c] * wrow[c];
+    if (b1) a += widen(b1, e * h + j, e_dt);
+    hid[j] = a > 0.0 ? a : 0.0;
+  }
+  for (int c = 0; c < d; ++c) {
+    widen_run(w2, (e * d + c) * (int64_t)h, h, e_dt, wrow.data());
+    double a = 0.0;
+    for (int j = 0; j < h; ++j) a += hid[j] * wrow[j];
+    if (b2) a += widen(b2, e * d + c, e_dt);
+    out[c] = a;
+  }
+}
+
+// Squared coefficient of variation with the population variance.
+double cv_squared(int n, const double* v) {
+  if (n <= 1) return 0.0;
+  double mean = 0.0;
+  for (int i = 0; i < n; ++i) mean += v[i];
+  mean /= n;
+  if (mean == 0.0) return 0.0;
+  double var = 0.0;
+  for (int i = 0; i < n; ++i) var += (v[i] - mean) * (v[i] - mean);
+  var /= n;
+  return var / (mean * mean);
+}
+
+GateArgs make_args(int d, int n, int k, const void* x, int x_dt, const void* wg, const void* wn,
+                   int w_dt, const float* bg, const float* eps, int train, double floor,
+                   int decide_fp32) {
+  GateArgs g;
+  g.d = d; g.n = n; g.k = k; g.x = x; g.x_dt = x_dt; g.wg = wg; g.wn = wn; g.w_dt = w_dt;
+  g.bg = bg; g.eps = eps; g.eps_row_stride = n; g.train = train; g.floor = floor;
+  g.decide_fp32 = decide_fp32;
+  return g;
+}
+
+bool bad_args(int64_t B, int d, int n, int k, int train, const void* eps) {
+  return B < 0 || d < 1 || n < 1 || k < 1 || k > n || (train && !eps);
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_version(void) { return 1; }
+
+double oracle_softplus(double u) { return softplus(u); }
+double oracle_phi(double z) { return Phi(z); }
+double oracle_cv_squared(int n, const double* v) { return cv_squared(n, v); }
+
+// Gating for a list of token rows (rows == null: rows 0..nrows-1).
+// Outputs per listed row r (any may be null):
+//   clean/sigma/H [nrows][n]; topk_idx [nrows][k] (rank order);
+//   topk_gate [nrows][k]; thresh [nrows][2] = (k-th, (k+1)-th) largest logit.
+int oracle_gate(int64_t nrows, const int64_t* rows, int d, int n, int k,
+                const void* x, int x_dt, const void* wg, const void* wn, int w_dt,
+                const float* bg, const float* eps, int train, double floor, int decide_fp32,
+                double* clean, double* sigma, double* H,
+                int32_t* topk_idx, double* topk_gate, double* thresh) {
+  if (bad_args(nrows, d, n, k, train, eps)) return 1;
+  const GateArgs g = make_args(d, n, k, x, x_dt, wg, wn, w_dt, bg, eps, train, floor, decide_fp32);
+#pragma omp parallel
+  {
+    RowGate r(n);
+    std::vector<double> xrow(d), wrow(d);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t q = 0; q < nrows; ++q) {
+      const int64_t t = rows ? rows[q] : q;
+      gate_row(g, t, r, xrow, wrow);
+      if (clean) std::copy(r.clean.begin(), r.clean.end(), clean + q * n);
+      if (sigma) std::copy(r.sigma.begin(), r.sigma.end(), sigma + q * n);
+      if (H) std::copy(r.H.begin(), r.H.end(), H + q * n);
+      for (int j = 0; j < k; ++j) {
+        if (topk_idx) topk_idx[q * k + j] = r.order[j];
+        if (topk_gate) topk_gate[q * k + j] = r.gate[j];
+      }
+      if (thresh) {
+        thresh[q * 2 + 0] = r.vk;
+        thresh[q * 2 + 1] = r.vk1;
+      }
+    }
+  }
+  return 0;
+}
+
+// Eqs 8-10 over the whole batch of B tokens: load[i] = sum_t P(x_t, i).
+// Rows are summed in blocks of 256 in ascending order, then the blocks in
+// ascending order.
+int oracle_load(int64_t B, int d, int n, int k, const void* x, int x_dt, const void* wg,
+                const void* wn, int w_dt, const float* bg, const float* eps, int train,
+                double floor, int decide_fp32, double* load) {
+  if (bad_args(B, d, n, k, train, eps)) return 1;
+  const GateArgs g = make_args(d, n, k, x, x_dt, wg, wn, w_dt, bg, eps, train, floor, decide_fp32);
+  const int64_t nblk = (B + kRowBlock - 1) / kRowBlock;
+  std::vector<double> part((size_t)nblk * n, 0.0);
+#pragma omp parallel
+  {
+    RowGate r(n);
+    std::vector<double> xrow(d), wrow(d);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t b = 0; b < nblk; ++b) {
+      double* acc = part.data() + b * n;
+      for (int64_t t = b * kRowBlock; t < std::min(B, (b + 1) * kRowBlock); ++t) {
+        gate_row(g, t, r, xrow, wrow);
+        for (int i = 0; i < n; ++i) acc[i] += prob_in_top_k(g, r, i);
+      }
+    }
+  }
+  for (int i = 0; i < n; ++i) load[i] = 0.0;
+  for (int64_t b = 0; b < nblk; ++b)
+    for (int i = 0; i < n; ++i) load[i] += part[b * n + i];
+  return 0;
+}
+
+// Eq 1 for a list of token rows: y_t = sum over experts i in ascending index
+// with G(x_t)_i > 0 of G(x_t)_i * E_i(x_t). y is [nrows][d].
+int oracle_y_rows(int64_t nrows, const int64_t* rows, int d, int h, int n, int k,
+                  const void* x, int x_dt, const void* wg, const void* wn, int w_dt,
+                  const float* bg, const float* eps, int train, double floor, int decide_fp32,
+                  const void* w1, const void* b1, const void* w2, const void* b2, int e_dt,
+                  double* y) {
+  if (bad_args(nrows, d, n, k, train, eps) || h < 1) return 1;
+  const GateArgs g = make_args(d, n, k, x, x_dt, wg, wn, w_dt, bg, eps, train, floor, decide_fp32);
+#pragma omp parallel
+  {
+    RowGate r(n);
+    std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h), eo(d);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t q = 0; q < nrows; ++q) {
+      const int64_t t = rows ? rows[q] : q;
+      gate_row(g, t, r, xrow, wrow);
+      // dense gate row G(x_t), zero outside the top k
+      std::vector<double> G(n, 0.0);
+      for (int j = 0; j < k; ++j) G[r.order[j]] = r.gate[j];
+      double* yr = y + q * d;
+      for (int c = 0; c < d; ++c) yr[c] = 0.0;
+      for (int i = 0; i < n; ++i) {
+        if (G[i] == 0.0) continue;
+        expert_apply(d, h, xrow.data(), w1, b1, w2, b2, e_dt, i, eo.data(), hid, wrow);
+        for (int c = 0; c < d; ++c) yr[c] += G[i] * eo[c];
+      }
+    }
+  }
+  return 0;
+}
+
+// E_e(x_t) for a list of (token, expert) pairs; out is [npairs][d].
+int oracle_expert_pairs(int64_t npairs, const int64_t* tokens, const int32_t* experts, int d,
+                        int h, const void* x, int x_dt, const void* w1, const void* b1,
+                        const void* w2, const void* b2, int e_dt, double* out) {
+  if (npairs < 0 || d < 1 || h < 1) return 1;
+#pragma omp parallel
+  {
+    std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t q = 0; q < npairs; ++q) {
+      widen_run(x, tokens[q] * (int64_t)d, d, x_dt, xrow.data());
+      expert_apply(d, h, xrow.data(), w1, b1, w2, b2, e_dt, experts[q], out + q * d, hid, wrow);
+    }
+  }
+  return 0;
+}
+
+// The per-expert row sets nonzero(G[:, e]) of the implementation notes, made
+// stable: segment e lists the tokens routed to expert e in ascending order.
+// Also Importance (eq 6): imp[e] = sum over those tokens of their gate.
+//   counts [n], offsets [n+1], perm_token [B*k], perm_gate [B*k],
+//   slot_pos [B*k] (slot_pos[t*k + j] = position of (t, j) in the permutation).
+int oracle_route(int64_t B, int n, int k, const int32_t* topk_idx, const double* topk_gate,
+                 int32_t* counts, int32_t* offsets, int32_t* perm_token, double* perm_gate,
+                 int32_t* slot_pos, double* importance) {
+  if (B < 0 || n < 1 || k < 1 || k > n) return 1;
+  for (int64_t q = 0; q < B * k; ++q)
+    if (topk_idx[q] < 0 || topk_idx[q] >= n) return 2;
+  std::vector<int64_t> cnt(n, 0);
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int e = 0; e < n; ++e) {
+    int64_t c = 0;
+    for (int64_t t = 0; t < B; ++t)
+      for (int j = 0; j < k; ++j)
+        if (topk_idx[t * k + j] == e) ++c;
+    cnt[e] = c;
+  }
+  std::vector<int64_t> off(n + 1, 0);
+  for (int e = 0; e < n; ++e) off[e + 1] = off[e] + cnt[e];
+  for (int e = 0; e < n; ++e) {
+    if (counts) counts[e] = (int32_t)cnt[e];
+    if (offsets) offsets[e] = (int32_t)off[e];
+  }
+  if (offsets) offsets[n] = (int32_t)off[n];
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int e = 0; e < n; ++e) {
+    int64_t pos = off[e];
+    double imp = 0.0;
+    for (int64_t t = 0; t < B; ++t)
+      for (int j = 0; j < k; ++j)
+        if (topk_idx[t * k + j] == e) {
+          if (perm_token) perm_token[pos] = (int32_t)t;
+          if (perm_gate) perm_gate[pos] = topk_gate[t * k + j];
+          if (slot_pos) slot_pos[t * k + j] = (int32_t)pos;
+          imp += topk_gate[t * k + j];
+          ++pos;
+        }
+    if (importance) importance[e] = imp;
+  }
+  return 0;
+}
+
+// The whole forward pass of the implementation notes on a batch of B tokens.
+// Outputs (any may be null except y):
+//   y [B][d]; topk_idx/topk_gate [B][k]; thresh [B][2]; importance/load [n];
+//   losses[3] = {CV^2(Importance), CV^2(Load), w_imp*CV^2(Imp) + w_load*CV^2(Load)}.
+int oracle_forward(int64_t B, int d, int h, int n, int k, const void* x, int x_dt,
+                   const void* wg, const void* wn, int w_dt, const float* bg, const float* eps,
+                   int train, double floor, int decide_fp32, const void* w1, const void* b1,
+                   const void* w2, const void* b2, int e_dt, double w_imp, double w_load,
+                   double* y, int32_t* topk_idx_out, double* topk_gate_out, double* thresh_out,
+                   double* importance, double* load, double* losses) {
+  if (bad_args(B, d, n, k, train, eps) || h < 1 || !y) return 1;
+  const GateArgs g = make_args(d, n, k, x, x_dt, wg, wn, w_dt, bg, eps, train, floor, decide_fp32);
+  // Gating: clean logits, noise std, noisy logits, top_k(H, k+1), softmax, G.
+  std::vector<int32_t> idx((size_t)B * k);
+  std::vector<double> gate((size_t)B * k), thr((size_t)B * 2);
+  std::vector<double> G((size_t)B * n, 0.0);
+  const int64_t nblk = (B + kRowBlock - 1) / kRowBlock;
+  std::vector<double> load_part((size_t)nblk * n, 0.0);
+#pragma omp parallel
+  {
+    RowGate r(n);
+    std::vector<double> xrow(d), wrow(d);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t b = 0; b < nblk; ++b) {
+      for (int64_t t = b * kRowBlock; t < std::min(B, (b + 1) * kRowBlock); ++t) {
+        gate_row(g, t, r, xrow, wrow);
+        for (int j = 0; j < k; ++j) {
+          idx[t * k + j] = r.order[j];
+          gate[t * k + j] = r.gate[j];
+          G[t * n + r.order[j]] = r.gate[j];
+        }
+        thr[t * 2] = r.vk;
+        thr[t * 2 + 1] = r.vk1;
+        // P(x_t, i) of eq 9, accumulated for eq 10 in this row block
+        double* acc = load_part.data() + b * n;
+        for (int i = 0; i < n; ++i) acc[i] += prob_in_top_k(g, r, i);
+      }
+    }
+  }
+  // Expert loop: y[rows] += G[rows, i] * E_i(X[rows]) for each expert in turn.
+  for (int64_t q = 0; q < B * d; ++q) y[q] = 0.0;
+  for (int i = 0; i < n; ++i) {
+#pragma omp parallel
+    {
+      std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h), eo(d);
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t t = 0; t < B; ++t) {
+        const double gi = G[t * n + i];
+        if (gi == 0.0) continue;
+        widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+        expert_apply(d, h, xrow.data(), w1, b1, w2, b2, e_dt, i, eo.data(), hid, wrow);
+        for (int c = 0; c < d; ++c) y[t * d + c] += gi * eo[c];
+      }
+    }
+  }
+  // Importance (eq 6): column sums of G in ascending token order.
+  std::vector<double> imp(n, 0.0), ld(n, 0.0);
+  for (int64_t t = 0; t < B; ++t)
+    for (int i = 0; i < n; ++i) imp[i] += G[t * n + i];
+  // Load (eq 10): block partials in ascending block order.
+  for (int64_t b = 0; b < nblk; ++b)
+    for (int i = 0; i < n; ++i) ld[i] += load_part[b * n + i];
+  const double cv_imp = cv_squared(n, imp.data());
+  const double cv_load = cv_squared(n, ld.data());
+  if (topk_idx_out) std::copy(idx.begin(), idx.end(), topk_idx_out);
+  if (topk_gate_out) std::copy(gate.begin(), gate.end(), topk_gate_out);
+  if (thresh_out) std::copy(thr.begin(), thr.end(), thresh_out);
+  if (importance) std::copy(imp.begin(), imp.end(), importance);
+  if (load) std::copy(ld.begin(), ld.end(), load);
+  if (losses) {
+    losses[0] = cv_imp;
+    losses[1] = cv_load;
+    losses[2] = w_imp * cv_imp + w_load * cv_load;  // eqs 7 and 11
+  }
+  return 0;
+}
+
+}  // extern "C"
