@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE-layer forward pass on one MI355X.
+
+One step = one ``moe_forward`` call (noisy top-k gating, routing, expert FFNs,
+weighted sum, Importance/Load and both losses, training mode) over a batch of
+65536 tokens, d_model 512, 4096 experts 512-1024-512, k = 4, bf16 storage with
+fp32 accumulation and fp32 gate math. Inputs are synthetic (seeded Philox
+normals, weights ~ N(0, 1/fan_in)) and resident in HBM before timing starts.
+
+Prints one JSON line: tokens/s, the expert-FFN kernel's achieved HBM bandwidth
+against the 8 TB/s peak, per-stage times, and the oracle's CPU throughput on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer forward tokens/sec at 4096 experts k=4; % MFMA peak and % HBM BW"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def to_device(a, torch, np):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def time_calls(fn, iters, torch):
+    """Average device time of fn() over iters calls, bracketed by HIP events on
+    the current stream (the stream the library launches on)."""
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(iters):
+        fn()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def cpu_baseline(w, inp, target_s):
+    """The oracle's whole forward pass on the first S tokens of the workload,
+    S grown until one run takes about target_s seconds."""
+    import numpy as np
+
+    import datagen as dg
+    import oracle
+
+    def run(S):
+        sub = dict(inp)
+        sub["x"] = inp["x"][:S]
+        sub["eps"] = inp["eps"][:S]
+        t0 = time.perf_counter()
+        oracle.forward(sub, w.k)
+        return time.perf_counter() - t0
+
+    S = 256
+    t = run(S)
+    if t < target_s / 4:
+        S = int(min(w.tokens, max(256, S * target_s / max(t, 1e-3))))
+        t = run(S)
+    threads = oracle.threads()
+    return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle forward pass (fp64, {threads} OpenMP threads) on the first {S} "
+                      f"tokens of the same workload: gating over all {w.n_experts} experts, "
+                      f"expert FFNs, weighted sum, Importance/Load and losses; {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="flat_bf16_n4096")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target length of the oracle CPU-baseline run (0 skips it)")
+    ap.add_argument("--stage-iters", type=int, default=10)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {a.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import datagen as dg
+    import sparsely_gated_mixture_moe_amd as moe
+
+    w = dg.WORKLOADS[a.workload]
+    if w.hierarchical:
+        raise SystemExit("the hierarchical workload is not part of this benchmark")
+    B, d, h, n, k = w.tokens, w.d_model, w.d_hidden, w.n_experts, w.k
+    log(f"generating {w.name}: {w.description}")
+    t0 = time.time()
+    inp = dg.make_inputs(w)
+    log(f"inputs generated in {time.time() - t0:.1f} s; uploading")
+    g = {key: to_device(v, torch, np) for key, v in inp.items()}
+    torch.cuda.synchronize()
+
+    f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,
+                       gate_bias=g.get("gate_bias"), train=True)
+    dev = g["x"].device
+    y = torch.empty((B, d), dtype=g["x"].dtype, device=dev)
+    topk_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    topk_gate = torch.empty((B, k), dtype=torch.float32, device=dev)
+    thresh = torch.empty((B, 2), dtype=torch.float32, device=dev)
+    counts = torch.empty(n, dtype=torch.int32, device=dev)
+
+    def step():
+        f(g["x"], g["eps"], y, topk_idx=topk_idx, topk_gate=topk_gate, thresh=thresh,
+          counts=counts)
+
+    log(f"warmup {a.warmup} steps")
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {a.steps} steps")
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(a.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / a.steps
+    log(f"{ms_step:.3f} ms/step (wall {1000 * wall / a.steps:.3f} ms/step)")
+
+    # Stage times: each entry point on its own, on the routing of the step above.
+    it = a.stage_iters
+    route = moe.moe_route(topk_idx, topk_gate, n, d_model=d)
+    ws = moe.workspace(f.dims, f.opts, dev)
+    eo = torch.empty((B * k, d), dtype=g["x"].dtype, device=dev)
+    stages = {
+        "gate": time_calls(lambda: moe.moe_gate(g["x"], g["w_gate"], g["w_noise"], g["eps"], k,
+                                                gate_bias=g.get("gate_bias")), it, torch),
+        "route": time_calls(lambda: moe.moe_route(topk_idx, topk_gate, n, d_model=d, ws=ws),
+                            it, torch),
+        "expert_ffn": time_calls(lambda: moe.moe_expert_ffn(
+            g["x"], route["offsets"], route["perm_token"], g["w1"], g["w2"], k, ws=ws, out=eo),
+            it, torch),
+        "combine": time_calls(lambda: moe.moe_combine(eo, route["slot_pos"], topk_gate,
+                                                      n_experts=n, out=y), it, torch),
+        "aux_losses": time_calls(lambda: moe.moe_aux_losses(
+            g["x"], g["w_gate"], g["w_noise"], topk_idx, thresh, counts, route["importance"],
+            gate_bias=g.get("gate_bias"), ws=ws), it, torch),
+    }
+    torch.cuda.synchronize()
+    log("stages (ms): " + ", ".join(f"{k_}={v:.3f}" for k_, v in stages.items()))
+
+    # Roofline of the dominant kernel, the expert FFN: algorithmic bytes per launch =
+    # the weights of every expert that received rows (2 d h elements each) + the
+    # gathered input rows + the written output rows.
+    cnt = counts.cpu().numpy()
+    esize = 2 if w.expert_dtype == dg.BF16 else 4
+    asize = 2 if w.act_dtype == dg.BF16 else 4
+    used = int((cnt > 0).sum())
+    rows = int(cnt.sum())
+    ffn_bytes = used * 2 * d * h * esize + 2 * rows * d * asize
+    ffn_flops = 4.0 * rows * d * h
+    ffn_ms = stages["expert_ffn"]
+    achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+    step_bytes = (B * d * asize + B * n * 4 + 2 * n * d * (2 if w.gate_dtype == dg.BF16 else 4)
+                  + used * 2 * d * h * esize + B * d * asize)
+    step_flops = 2.0 * B * d * 2 * n * 2 + ffn_flops  # gate GEMM twice (selection, load) + FFN
+    mfma_peak = BF16_PEAK_TFLOPS if w.expert_dtype == dg.BF16 else FP32_PEAK_TFLOPS
+
+    result = {
+        "metric": METRIC,
+        "value": B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "n_experts": n,
+                   "k": k, "train": 1, "act_dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
+                   "gate_dtype": "bf16" if w.gate_dtype == dg.BF16 else "f32"},
+        "roofline": {"kernel": "ffn_kernel (moe_expert_ffn)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": ffn_bytes, "avg_launch_ms": ffn_ms,
+                     "mfma_frac": ffn_flops / (ffn_ms * 1e-3) / (mfma_peak * 1e12)},
+        "step": {"alg_bytes": step_bytes, "alg_flops": step_flops,
+                 "hbm_frac": step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                 "mfma_frac": step_flops / (ms_step * 1e-3) / (mfma_peak * 1e12)},
+        "stages_ms": stages,
+        "wall_ms_per_step": 1000 * wall / a.steps,
+        "cpu_baseline": None,
+    }
+    if a.cpu_seconds > 0:
+        log("timing the oracle on the host cores")
+        result["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

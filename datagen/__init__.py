@@ -186,7 +186,7 @@ _ZIPF_JSON = os.path.join(_HERE, "zipf_tau.json")
 
 
 def zipf_tau() -> float:
-    """Calibrated Zipf exponent scale for the gate bias (see calibrate_zipf.py)."""
+    """Calibrated Zipf scale of the gate bias (written by tests/golden/calibrate_zipf_tau.py)."""
     with open(_ZIPF_JSON) as f:
         return float(json.load(f)["tau"])
 
@@ -231,11 +231,13 @@ def gen(w: Workload, name: str, offset: int = 0, count: Optional[int] = None) ->
     return normal(w.seed, TID[name], offset, count, scale, dtype)
 
 
-def make_inputs(w: Workload, with_bias: bool = False, experts: bool = True) -> Dict[str, np.ndarray]:
+def make_inputs(w: Workload, with_bias: bool = False, experts: bool = True,
+                gate_bias_tau: Optional[float] = None) -> Dict[str, np.ndarray]:
     """All inputs of a flat workload as shaped numpy arrays.
 
     ``with_bias`` adds the expert biases b1/b2 (otherwise they are absent).
     ``experts=False`` skips the expert weights (for gating-only uses).
+    ``gate_bias_tau`` overrides the stored Zipf scale (used when calibrating it).
     """
     if w.hierarchical:
         raise ValueError("use make_hier_inputs for hierarchical workloads")
@@ -246,7 +248,7 @@ def make_inputs(w: Workload, with_bias: bool = False, experts: bool = True) -> D
         "w_noise": gen(w, "w_noise").reshape(n, d),
         "eps": gen(w, "eps").reshape(B, n),
     }
-    bg = gate_bias(w)
+    bg = gate_bias(w, gate_bias_tau)
     if bg is not None:
         out["gate_bias"] = bg
     if experts:

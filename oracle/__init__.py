@@ -46,6 +46,7 @@ def _load():
         if not os.path.exists(_LIB_PATH):
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_threads.restype = _I
         lib.oracle_softplus.argtypes = [_D]
         lib.oracle_softplus.restype = _D
         lib.oracle_phi.argtypes = [_D]
@@ -86,6 +87,11 @@ def _ptr(a):
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"{what}: oracle rejected the arguments (code {rc})")
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return _load().oracle_threads()
 
 
 def softplus(u: float) -> float:

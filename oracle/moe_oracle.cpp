@@ -46,6 +46,8 @@
 #include <numeric>
 #include <vector>
 
+#include <omp.h>
+
 namespace {
 
 constexpr int kF32 = 0;
@@ -205,6 +207,7 @@ bool bad_args(int64_t B, int d, int n, int k, int train, const void* eps) {
 extern "C" {
 
 int oracle_version(void) { return 1; }
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 double oracle_softplus(double u) { return softplus(u); }
 double oracle_phi(double z) { return Phi(z); }

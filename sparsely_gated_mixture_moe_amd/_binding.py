@@ -1,0 +1,337 @@
+"""ctypes binding of ``libmoe_mi355x.so`` (the C ABI of include/moe.h).
+
+Argument marshalling only: every entry point checks tensor dtypes, shapes,
+devices and contiguity, passes raw device pointers and torch's current HIP
+stream to the library, and raises ``MoeError`` with the library's message on a
+nonzero status. All computation happens in the library's HIP kernels; there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("d_model", ctypes.c_int32),
+                ("d_hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int), ("expert_dtype", ctypes.c_int),
+                ("gate_dtype", ctypes.c_int)]
+
+
+class MoeGateOpts(ctypes.Structure):
+    _fields_ = [("train", ctypes.c_int32), ("noise_floor", ctypes.c_float),
+                ("w_importance", ctypes.c_float), ("w_load", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sparsely_gated_mixture_moe_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_abi_version.restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_workspace_size.argtypes = [ctypes.POINTER(MoeDims), ctypes.POINTER(MoeGateOpts)]
+        L.moe_workspace_size.restype = ctypes.c_size_t
+        D, O = ctypes.POINTER(MoeDims), ctypes.POINTER(MoeGateOpts)
+        S = ctypes.c_size_t
+        L.moe_gate.argtypes = [D, O, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
+        L.moe_route.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
+        L.moe_expert_ffn.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
+        L.moe_combine.argtypes = [D, _P, _P, _P, _P, _P]
+        L.moe_aux_losses.argtypes = [D, O, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
+        L.moe_forward.argtypes = [D, O] + [_P] * 19 + [S, _P]
+        for f in ("moe_gate", "moe_route", "moe_expert_ffn", "moe_combine", "moe_aux_losses",
+                  "moe_forward"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        L = lib()
+        raise MoeError(f"{what}: {L.moe_status_string(status).decode()}: "
+                       f"{L.moe_last_error().decode()}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise MoeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise MoeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise MoeError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MoeError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_dims(tokens: int, d_model: int, d_hidden: int, n_experts: int, k: int,
+              act_dtype: int, expert_dtype: int, gate_dtype: int) -> MoeDims:
+    return MoeDims(tokens, d_model, d_hidden, n_experts, k, act_dtype, expert_dtype, gate_dtype)
+
+
+def make_opts(train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
+              w_load: float = 0.1) -> MoeGateOpts:
+    return MoeGateOpts(int(bool(train)), noise_floor, w_importance, w_load)
+
+
+def moe_workspace_size(dims: MoeDims, opts: Optional[MoeGateOpts] = None) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(dims),
+                                        ctypes.byref(opts) if opts is not None else None))
+
+
+def workspace(dims: MoeDims, opts: Optional[MoeGateOpts], device) -> torch.Tensor:
+    """A device byte buffer of moe_workspace_size() bytes (torch's allocator
+    returns 512-byte aligned blocks)."""
+    nbytes = moe_workspace_size(dims, opts)
+    if nbytes == 0 and dims.tokens > 0:
+        _check(1, "moe_workspace_size")
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _gate_dims(x, w_gate, k, d_hidden=128, w1=None) -> MoeDims:
+    B, d = x.shape
+    n = w_gate.shape[0]
+    e_dt = _dt(w1) if w1 is not None else _dt(x)
+    return make_dims(B, d, d_hidden if w1 is None else w1.shape[1], n, k, _dt(x), e_dt, _dt(w_gate))
+
+
+def moe_gate(x, w_gate, w_noise, eps, k: int, *, train: bool = True, noise_floor: float = 1e-2,
+             gate_bias=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Noisy top-k gating -> (topk_idx [B,k] int32, topk_gate [B,k] fp32, thresh [B,2] fp32)."""
+    _dev(x, "x")
+    B, d = x.shape
+    _dev(w_gate, "w_gate")
+    n = w_gate.shape[0]
+    _dev(w_noise, "w_noise", w_gate.dtype, (n, d))
+    _dev(gate_bias, "gate_bias", torch.float32, (n,))
+    _dev(eps, "eps", torch.float32, (B, n))
+    dims = _gate_dims(x, w_gate, k)
+    opts = make_opts(train, noise_floor)
+    dev = x.device
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((B, k), dtype=torch.float32, device=dev)
+    thr = torch.empty((B, 2), dtype=torch.float32, device=dev)
+    st = lib().moe_gate(ctypes.byref(dims), ctypes.byref(opts), _ptr(x), _ptr(w_gate),
+                        _ptr(w_noise), _ptr(gate_bias), _ptr(eps), _ptr(idx), _ptr(gate), _ptr(thr),
+                        None, 0, _stream(stream))
+    _check(st, "moe_gate")
+    return idx, gate, thr
+
+
+def moe_route(topk_idx, topk_gate, n_experts: int, *, d_model: int = 64,
+              ws: Optional[torch.Tensor] = None, with_importance: bool = True,
+              stream=None) -> Dict[str, torch.Tensor]:
+    """Stable expert-major routing: counts, offsets, perm_token, perm_gate, slot_pos, importance."""
+    _dev(topk_idx, "topk_idx", torch.int32)
+    B, k = topk_idx.shape
+    _dev(topk_gate, "topk_gate", torch.float32, (B, k))
+    dims = make_dims(B, d_model, 128, n_experts, k, MOE_F32, MOE_F32, MOE_F32)
+    dev = topk_idx.device
+    if ws is None:
+        ws = workspace(dims, None, dev)
+    out = {"counts": torch.empty(n_experts, dtype=torch.int32, device=dev),
+           "offsets": torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
+           "perm_token": torch.empty(B * k, dtype=torch.int32, device=dev),
+           "perm_gate": torch.empty(B * k, dtype=torch.float32, device=dev),
+           "slot_pos": torch.empty(B * k, dtype=torch.int32, device=dev)}
+    if with_importance:
+        out["importance"] = torch.empty(n_experts, dtype=torch.float32, device=dev)
+    st = lib().moe_route(ctypes.byref(dims), _ptr(topk_idx), _ptr(topk_gate), _ptr(out["counts"]),
+                         _ptr(out["offsets"]), _ptr(out["perm_token"]), _ptr(out["perm_gate"]),
+                         _ptr(out["slot_pos"]), _ptr(out.get("importance")), _ptr(ws), ws.numel(),
+                         _stream(stream))
+    _check(st, "moe_route")
+    return out
+
+
+def moe_expert_ffn(x, offsets, perm_token, w1, w2, k: int, *, b1=None, b2=None,
+                   ws: Optional[torch.Tensor] = None, out=None, stream=None) -> torch.Tensor:
+    """expert_out [B*k, d] in permutation order: E_e(x[perm_token[p]]) per segment."""
+    _dev(x, "x")
+    B, d = x.shape
+    _dev(w1, "w1", x.dtype)
+    n, h, _ = w1.shape
+    _dev(w2, "w2", x.dtype, (n, d, h))
+    _dev(b1, "b1", x.dtype, (n, h))
+    _dev(b2, "b2", x.dtype, (n, d))
+    _dev(offsets, "offsets", torch.int32, (n + 1,))
+    _dev(perm_token, "perm_token", torch.int32, (B * k,))
+    dims = make_dims(B, d, h, n, k, _dt(x), _dt(w1), _dt(x))
+    if ws is None:
+        ws = workspace(dims, None, x.device)
+    if out is None:
+        out = torch.empty((B * k, d), dtype=x.dtype, device=x.device)
+    _dev(out, "expert_out", x.dtype, (B * k, d))
+    st = lib().moe_expert_ffn(ctypes.byref(dims), _ptr(x), _ptr(offsets), _ptr(perm_token),
+                              _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out), _ptr(ws),
+                              ws.numel(), _stream(stream))
+    _check(st, "moe_expert_ffn")
+    return out
+
+
+def moe_combine(expert_out, slot_pos, topk_gate, *, n_experts: int = 1, out=None,
+                stream=None) -> torch.Tensor:
+    """y [B, d] = sum_j topk_gate[t, j] * expert_out[slot_pos[t*k + j]]."""
+    _dev(topk_gate, "topk_gate", torch.float32)
+    B, k = topk_gate.shape
+    _dev(expert_out, "expert_out")
+    d = expert_out.shape[1]
+    _dev(slot_pos, "slot_pos", torch.int32, (B * k,))
+    dims = make_dims(B, d, 128, max(n_experts, k), k, _dt(expert_out), _dt(expert_out),
+                     _dt(expert_out))
+    if out is None:
+        out = torch.empty((B, d), dtype=expert_out.dtype, device=expert_out.device)
+    _dev(out, "y", expert_out.dtype, (B, d))
+    st = lib().moe_combine(ctypes.byref(dims), _ptr(expert_out), _ptr(slot_pos), _ptr(topk_gate),
+                           _ptr(out), _stream(stream))
+    _check(st, "moe_combine")
+    return out
+
+
+def moe_aux_losses(x, w_gate, w_noise, topk_idx, thresh, counts, importance, *, train: bool = True,
+                   noise_floor: float = 1e-2, w_importance: float = 0.1, w_load: float = 0.1,
+                   gate_bias=None, ws: Optional[torch.Tensor] = None,
+                   stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(load [n], losses [3] = CV2(imp), CV2(load), weighted sum)."""
+    _dev(x, "x")
+    B, d = x.shape
+    _dev(w_gate, "w_gate")
+    n = w_gate.shape[0]
+    _dev(w_noise, "w_noise", w_gate.dtype, (n, d))
+    _dev(gate_bias, "gate_bias", torch.float32, (n,))
+    _dev(topk_idx, "topk_idx", torch.int32)
+    k = topk_idx.shape[1]
+    _dev(thresh, "thresh", torch.float32, (B, 2))
+    _dev(counts, "counts", torch.int32, (n,))
+    _dev(importance, "importance", torch.float32, (n,))
+    dims = _gate_dims(x, w_gate, k)
+    opts = make_opts(train, noise_floor, w_importance, w_load)
+    if ws is None:
+        ws = workspace(dims, opts, x.device)
+    load = torch.empty(n, dtype=torch.float32, device=x.device)
+    losses = torch.empty(3, dtype=torch.float32, device=x.device)
+    st = lib().moe_aux_losses(ctypes.byref(dims), ctypes.byref(opts), _ptr(x), _ptr(w_gate),
+                              _ptr(w_noise), _ptr(gate_bias), _ptr(topk_idx), _ptr(thresh),
+                              _ptr(counts), _ptr(importance), _ptr(load), _ptr(losses), _ptr(ws),
+                              ws.numel(), _stream(stream))
+    _check(st, "moe_aux_losses")
+    return load, losses
+
+
+class MoeForward:
+    """Holds the layer's weights, options and a workspace for repeated
+    ``moe_forward`` calls. Tensors stay owned by the caller."""
+
+    def __init__(self, x_shape, w_gate, w_noise, w1, w2, k: int, *, b1=None, b2=None,
+                 gate_bias=None, train: bool = True, noise_floor: float = 1e-2,
+                 w_importance: float = 0.1, w_load: float = 0.1, act_dtype=None):
+        B, d = x_shape
+        n, h, _ = w1.shape
+        self.w_gate, self.w_noise, self.w1, self.w2, self.b1, self.b2 = w_gate, w_noise, w1, w2, b1, b2
+        self.gate_bias = gate_bias
+        _dev(w_gate, "w_gate", shape=(n, d))
+        _dev(w_noise, "w_noise", w_gate.dtype, (n, d))
+        _dev(w1, "w1")
+        _dev(w2, "w2", w1.dtype, (n, d, h))
+        _dev(b1, "b1", w1.dtype, (n, h))
+        _dev(b2, "b2", w1.dtype, (n, d))
+        _dev(gate_bias, "gate_bias", torch.float32, (n,))
+        adt = _dt(w1) if act_dtype is None else act_dtype
+        self.dims = make_dims(B, d, h, n, k, adt, _dt(w1), _dt(w_gate))
+        self.opts = make_opts(train, noise_floor, w_importance, w_load)
+        dev = w1.device
+        self.ws = workspace(self.dims, self.opts, dev)
+        self.importance = torch.empty(n, dtype=torch.float32, device=dev)
+        self.load = torch.empty(n, dtype=torch.float32, device=dev)
+        self.losses = torch.empty(3, dtype=torch.float32, device=dev)
+
+    def __call__(self, x, eps, y=None, *, topk_idx=None, topk_gate=None, thresh=None, counts=None,
+                 perm_token=None, stream=None):
+        d = self.dims
+        _dev(x, "x", self.w1.dtype, (d.tokens, d.d_model))
+        _dev(eps, "eps", torch.float32, (d.tokens, d.n_experts))
+        if y is None:
+            y = torch.empty((d.tokens, d.d_model), dtype=x.dtype, device=x.device)
+        _dev(y, "y", x.dtype, (d.tokens, d.d_model))
+        for name, t, dt, shp in (("topk_idx", topk_idx, torch.int32, (d.tokens, d.k)),
+                                 ("topk_gate", topk_gate, torch.float32, (d.tokens, d.k)),
+                                 ("thresh", thresh, torch.float32, (d.tokens, 2)),
+                                 ("counts", counts, torch.int32, (d.n_experts,)),
+                                 ("perm_token", perm_token, torch.int32, (d.tokens * d.k,))):
+            _dev(t, name, dt, shp)
+        st = lib().moe_forward(ctypes.byref(self.dims), ctypes.byref(self.opts), _ptr(x),
+                               _ptr(self.w_gate), _ptr(self.w_noise), _ptr(self.gate_bias),
+                               _ptr(eps), _ptr(self.w1), _ptr(self.b1), _ptr(self.w2),
+                               _ptr(self.b2), _ptr(y), _ptr(self.importance), _ptr(self.load),
+                               _ptr(self.losses), _ptr(topk_idx), _ptr(topk_gate), _ptr(thresh),
+                               _ptr(counts), _ptr(perm_token), _ptr(self.ws), self.ws.numel(),
+                               _stream(stream))
+        _check(st, "moe_forward")
+        return y
+
+
+def moe_forward(x, w_gate, w_noise, eps, w1, w2, k: int, *, b1=None, b2=None, gate_bias=None,
+                train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
+                w_load: float = 0.1, return_routing: bool = False, stream=None):
+    """One call of the whole forward pass; returns a dict of device tensors."""
+    f = MoeForward(tuple(x.shape), w_gate, w_noise, w1, w2, k, b1=b1, b2=b2, gate_bias=gate_bias,
+                   train=train, noise_floor=noise_floor, w_importance=w_importance, w_load=w_load)
+    B, n = x.shape[0], w1.shape[0]
+    extra = {}
+    if return_routing:
+        dev = x.device
+        extra = {"topk_idx": torch.empty((B, k), dtype=torch.int32, device=dev),
+                 "topk_gate": torch.empty((B, k), dtype=torch.float32, device=dev),
+                 "thresh": torch.empty((B, 2), dtype=torch.float32, device=dev),
+                 "counts": torch.empty(n, dtype=torch.int32, device=dev),
+                 "perm_token": torch.empty(B * k, dtype=torch.int32, device=dev)}
+    y = f(x, eps, **extra, stream=stream)
+    out = {"y": y, "importance": f.importance, "load": f.load, "losses": f.losses}
+    out.update(extra)
+    return out

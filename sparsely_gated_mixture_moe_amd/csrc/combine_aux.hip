@@ -1,0 +1,137 @@
+// The gate-weighted sum of eq 1 (section "How a mixture-of-experts layer
+// works") and the small reductions of the balancing losses (eqs 7 and 11,
+// section "Why experts collapse, and the balancing losses").
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// y[t] = sum_j gate[t, j] * expert_out[slot_pos[t*k + j]], fp32 accumulation
+// in slot order. One thread per 16-byte unit of an output row: every read and
+// write is a full 16-byte access and a row is read contiguously.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ eo,
+                                                      const int32_t* __restrict__ slot_pos,
+                                                      const float* __restrict__ gate,
+                                                      int64_t tokens, int k, int d,
+                                                      int64_t eo_rows, T* __restrict__ y) {
+  constexpr int UE = Elem<T>::kPerUnit;
+  const int units = d / UE;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = gid / units;
+  const int u = (int)(gid - t * units);
+  if (t >= tokens) return;
+  float acc[UE];
+#pragma unroll
+  for (int i = 0; i < UE; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int sp = slot_pos[t * k + j];
+    if (sp < 0 || sp >= eo_rows) continue;
+    const float g = gate[t * k + j];
+    const U16 v = ld_unit(eo + (int64_t)sp * d + u * UE);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += g * __uint_as_float(v.w[i] << 16);
+        acc[2 * i + 1] += g * __uint_as_float(v.w[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += g * __uint_as_float(v.w[i]);
+    }
+  }
+  U16 o;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o.w[i] = f32_to_bf16_bits(acc[2 * i]) | (f32_to_bf16_bits(acc[2 * i + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.w[i] = __float_as_uint(acc[i]);
+  }
+  st_unit(y + t * d + u * UE, o);
+}
+
+__global__ void counts_to_load_kernel(const int32_t* __restrict__ counts, int n,
+                                      float* __restrict__ load) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n) load[e] = (float)counts[e];
+}
+
+// CV^2 = population variance / mean^2 of importance and of load, in fp64 with a
+// fixed reduction order; losses = {CV2(imp), CV2(load), w_imp CV2(imp) + w_load CV2(load)}.
+__global__ __launch_bounds__(256) void cv2_losses_kernel(const float* __restrict__ imp,
+                                                         const float* __restrict__ load, int n,
+                                                         float w_imp, float w_load,
+                                                         float* __restrict__ losses) {
+  __shared__ double red[256];
+  double cv[2];
+  for (int v = 0; v < 2; ++v) {
+    const float* x = v ? load : imp;
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n; i += 256) s += (double)x[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+      __syncthreads();
+    }
+    const double mean = red[0] / n;
+    __syncthreads();
+    double q = 0.0;
+    for (int i = threadIdx.x; i < n; i += 256) {
+      const double dv = (double)x[i] - mean;
+      q += dv * dv;
+    }
+    red[threadIdx.x] = q;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+      __syncthreads();
+    }
+    const double var = red[0] / n;
+    __syncthreads();
+    cv[v] = (n <= 1 || mean == 0.0) ? 0.0 : var / (mean * mean);
+  }
+  if (threadIdx.x == 0) {
+    losses[0] = (float)cv[0];
+    losses[1] = (float)cv[1];
+    losses[2] = (float)((double)w_imp * cv[0] + (double)w_load * cv[1]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int64_t tokens, int k, int d, Dt dt, const void* expert_out,
+                          const int32_t* slot_pos, const float* topk_gate, void* y,
+                          hipStream_t s) {
+  if (tokens == 0) return hipSuccess;
+  const int ue = dt == kBF16 ? 8 : 4;
+  const int64_t threads = tokens * (d / ue);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  const int64_t rows = tokens * k;
+  if (dt == kBF16)
+    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const bf16*>(expert_out), slot_pos, topk_gate, tokens, k, d,
+                       rows, reinterpret_cast<bf16*>(y));
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const float*>(expert_out), slot_pos, topk_gate, tokens, k,
+                       d, rows, reinterpret_cast<float*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_counts_to_load(const int32_t* counts, int n, float* load, hipStream_t s) {
+  hipLaunchKernelGGL(counts_to_load_kernel, dim3((n + 255) / 256), dim3(256), 0, s, counts, n, load);
+  return hipGetLastError();
+}
+
+hipError_t launch_cv2_losses(const float* importance, const float* load, int n, float w_imp,
+                             float w_load, float* losses, hipStream_t s) {
+  hipLaunchKernelGGL(cv2_losses_kernel, dim3(1), dim3(256), 0, s, importance, load, n, w_imp,
+                     w_load, losses);
+  return hipGetLastError();
+}
+
+}  // namespace moe

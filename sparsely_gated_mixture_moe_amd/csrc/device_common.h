@@ -1,0 +1,124 @@
+// Device-side building blocks shared by the gfx950 kernels: storage types,
+// 16-byte operand units, the CDNA4 matrix-core (MFMA) wrappers and the scalar
+// functions of the gate.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// bf16 is stored as its bit pattern.
+struct bf16 {
+  uint16_t bits;
+};
+
+typedef short short8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// A 16-byte operand unit: 8 bf16 or 4 fp32 consecutive elements of a row.
+struct alignas(16) U16 {
+  uint32_t w[4];
+};
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kPerUnit = 4;
+};
+template <>
+struct Elem<bf16> {
+  static constexpr int kPerUnit = 8;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ U16 ld_unit(const void* p) { return *reinterpret_cast<const U16*>(p); }
+__device__ __forceinline__ void st_unit(void* p, const U16& v) { *reinterpret_cast<U16*>(p) = v; }
+__device__ __forceinline__ U16 zero_unit() { return U16{{0u, 0u, 0u, 0u}}; }
+
+// Four bf16 (8 bytes) widened to a unit of four fp32.
+__device__ __forceinline__ U16 widen4_bf16(const void* p) {
+  uint2 v = *reinterpret_cast<const uint2*>(p);
+  U16 r;
+  r.w[0] = v.x << 16;
+  r.w[1] = v.x & 0xFFFF0000u;
+  r.w[2] = v.y << 16;
+  r.w[3] = v.y & 0xFFFF0000u;
+  return r;
+}
+
+__device__ __forceinline__ short8 as_short8(const U16& u) {
+  short8 s;
+  __builtin_memcpy(&s, &u, 16);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core K-blocks. A "K-block" is the K range that one 16-byte unit per
+// lane covers across a wave.
+//
+// 16x16 tiles (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x4_f32): lane l
+// supplies row (A) or column (B) l % 16 and unit q = l / 16 of the K-block, so
+// a K-block is 4 units: 32 bf16 or 16 fp32. For fp32 the four elements of a
+// lane's unit feed four successive 16x16x4 steps; step s then contracts the K
+// indices {4q + s}, which covers the K-block once because A and B use the same
+// assignment. Output: lane l holds column l % 16, rows 4 (l / 16) + r, r < 4.
+//
+// 32x32 tiles (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2_f32): lane l
+// supplies row/column l % 32 and unit l / 32, so a K-block is 2 units: 16 bf16
+// or 8 fp32 (four 32x32x2 steps). Output: lane l holds column l % 32, rows
+// 8 (j / 4) + 4 (l / 32) + j % 4 for j < 16.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<bf16> {
+  __device__ __forceinline__ static void k16(f32x4& acc, const U16& a, const U16& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_short8(a), as_short8(b), acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static void k32(f32x16& acc, const U16& a, const U16& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_short8(a), as_short8(b), acc, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<float> {
+  __device__ __forceinline__ static void k16(f32x4& acc, const U16& a, const U16& b) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w[s]), __uint_as_float(b.w[s]),
+                                                 acc, 0, 0, 0);
+  }
+  __device__ __forceinline__ static void k32(f32x16& acc, const U16& a, const U16& b) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w[s]), __uint_as_float(b.w[s]),
+                                                 acc, 0, 0, 0);
+  }
+};
+
+// Softplus(u) = log(1 + e^u) in the form that cannot overflow.
+__device__ __forceinline__ float softplus_f(float u) {
+  return fmaxf(u, 0.0f) + log1pf(__expf(-fabsf(u)));
+}
+
+// Standard normal CDF.
+__device__ __forceinline__ float phi_f(float z) { return 0.5f * erfcf(-z * 0.70710678118654752f); }
+
+// Ranking order of (logit, expert) pairs: larger logit first, equal logits to
+// the lower expert index.
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+}  // namespace moe

@@ -1,0 +1,300 @@
+// Expert FFNs on their routed rows (section "How a mixture-of-experts layer
+// works": each expert is input layer -> ReLU hidden layer -> output layer, and
+// is evaluated only on the inputs whose gate is nonzero) as a grouped matrix
+// product over the contiguous per-expert segments that routing produced.
+//
+// Work unit: (expert e, up to BM consecutive rows of its segment). A small
+// planning kernel lists these units from the segment offsets; one workgroup
+// takes one unit:
+//   * gather its BM rows of x into LDS (16-byte units, XOR-swizzled by row so
+//     the matrix-core operand reads are conflict-free);
+//   * for each chunk of HC hidden units:
+//       GEMM1  Hc^T = W1[chunk] . X^T   W1 rows stream from HBM straight into
+//                                      the A operands (16 contiguous bytes per
+//                                      lane), X^T comes from LDS;
+//       bias + ReLU, round to the storage type, stage Hc in LDS;
+//       GEMM2  Out += Hc . W2[:, chunk]^T  W2 rows stream from HBM into the B
+//                                         operands; Out stays in registers;
+//   * add b2 and write the rows to expert_out in segment order.
+// Every expert weight is read from HBM once per work unit; with ~64 rows per
+// expert (4096 experts, k = 4, 65536 tokens) the kernel is bound by streaming
+// the expert weights, the shrinking-batch regime of "Keeping each expert's
+// batch large".
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <typename T, int D>
+struct FfnShape {
+  static constexpr int NW = (D >= 128) ? 4 : 2;          // waves per workgroup
+  static constexpr int HC = 32 * NW;                     // hidden units per chunk
+  static constexpr int BM = (sizeof(T) == 4 && D >= 512) ? 32 : 64;  // rows per unit
+  static constexpr int TT = BM / 32;                     // 32-row token tiles
+  static constexpr int CT2 = D / 32 / NW;                // 32-col output tiles per wave
+  static constexpr int UE = Elem<T>::kPerUnit;
+  static constexpr int XU = D / UE;                      // 16-byte units per x row
+  static constexpr int HU = HC / UE;                     // units per hidden-chunk row
+  static constexpr int XSW = XU >= 16 ? 16 : XU;
+  static constexpr int HSW = HU >= 16 ? 16 : HU;
+  static_assert(CT2 >= 1, "output tiles per wave");
+};
+
+struct FfnParams {
+  const void* x;
+  const int32_t* offsets;
+  const int32_t* perm_token;
+  const void* w1;
+  const void* b1;
+  const void* w2;
+  const void* b2;
+  void* out;
+  const int32_t* blocks;  // [0] = count, then (expert, first row) pairs
+  int h;
+};
+
+template <typename T>
+__device__ __forceinline__ float load_scalar(const void* p, int64_t i) {
+  if constexpr (sizeof(T) == 2) {
+    return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  } else {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_scalar(void* p, int64_t i, float v) {
+  if constexpr (sizeof(T) == 2) {
+    reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16_bits(v);
+  } else {
+    reinterpret_cast<float*>(p)[i] = v;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__((FfnShape<T, D>::NW * 64)) void ffn_kernel(FfnParams p) {
+  using S = FfnShape<T, D>;
+  constexpr int NT = S::NW * 64;
+  constexpr int UE = S::UE;
+  __shared__ U16 xs[S::BM * S::XU];
+  __shared__ U16 hs[S::BM * S::HU];
+
+  const int blk = blockIdx.x;
+  if (blk >= p.blocks[0]) return;
+  const int e = p.blocks[1 + 2 * blk];
+  const int row0 = p.blocks[2 + 2 * blk];
+  const int seg0 = p.offsets[e];
+  const int rows = min(S::BM, p.offsets[e + 1] - seg0 - row0);
+  const int64_t seg = (int64_t)seg0 + row0;
+  const int h = p.h;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // Gather the unit's rows of x.
+  for (int u = tid; u < S::BM * S::XU; u += NT) {
+    const int r = u / S::XU;
+    const int c = u - r * S::XU;
+    U16 v = zero_unit();
+    if (r < rows) {
+      const int64_t tok = p.perm_token[seg + r];
+      v = ld_unit(reinterpret_cast<const T*>(p.x) + tok * D + c * UE);
+    }
+    xs[r * S::XU + (c ^ (r & (S::XSW - 1)))] = v;
+  }
+  __syncthreads();
+
+  const T* w1e = reinterpret_cast<const T*>(p.w1) + (int64_t)e * h * D;
+  const T* w2e = reinterpret_cast<const T*>(p.w2) + (int64_t)e * D * h;
+
+  f32x16 acc2[S::TT][S::CT2];
+#pragma unroll
+  for (int tt = 0; tt < S::TT; ++tt)
+#pragma unroll
+    for (int i = 0; i < S::CT2; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc2[tt][i][j] = 0.f;
+
+  for (int hc = 0; hc < h; hc += S::HC) {
+    // GEMM1: rows = hidden units hc + 32*wave + (0..31), columns = tokens.
+    f32x16 acc1[S::TT];
+#pragma unroll
+    for (int tt = 0; tt < S::TT; ++tt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc1[tt][j] = 0.f;
+    const T* wrow = w1e + (int64_t)(hc + 32 * wave + l32) * D;
+#pragma unroll 4
+    for (int kb = 0; kb < D / (2 * UE); ++kb) {
+      const U16 a = ld_unit(wrow + kb * 2 * UE + hi * UE);
+      const int c = kb * 2 + hi;
+#pragma unroll
+      for (int tt = 0; tt < S::TT; ++tt) {
+        const int r = tt * 32 + l32;
+        Mfma<T>::k32(acc1[tt], a, xs[r * S::XU + (c ^ (r & (S::XSW - 1)))]);
+      }
+    }
+    __syncthreads();  // the previous chunk's GEMM2 has finished reading hs
+
+    // bias + ReLU, round, stage Hc[token][hidden] in LDS.
+#pragma unroll
+    for (int tt = 0; tt < S::TT; ++tt) {
+      const int tok = tt * 32 + l32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int hl = 32 * wave + 8 * g + 4 * hi;  // first of 4 consecutive hidden units
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = acc1[tt][4 * g + i];
+          if (p.b1) a += load_scalar<T>(p.b1, (int64_t)e * h + hc + hl + i);
+          v[i] = a > 0.f ? a : 0.f;
+        }
+        const int cu = hl / UE;
+        const int cs = cu ^ (tok & (S::HSW - 1));
+        char* dst = reinterpret_cast<char*>(&hs[tok * S::HU + cs]);
+        if constexpr (sizeof(T) == 2) {
+          uint2 pk;
+          pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+          pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+          *reinterpret_cast<uint2*>(dst + (hl % UE) * 2) = pk;
+        } else {
+          U16 pk;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pk.w[i] = __float_as_uint(v[i]);
+          *reinterpret_cast<U16*>(dst) = pk;
+        }
+      }
+    }
+    __syncthreads();
+
+    // GEMM2: Out[token][col] += Hc[token][:] . W2[col][hc:hc+HC].
+#pragma unroll 2
+    for (int kb = 0; kb < S::HC / (2 * UE); ++kb) {
+      const int c = kb * 2 + hi;
+      U16 a[S::TT];
+#pragma unroll
+      for (int tt = 0; tt < S::TT; ++tt) {
+        const int r = tt * 32 + l32;
+        a[tt] = hs[r * S::HU + (c ^ (r & (S::HSW - 1)))];
+      }
+#pragma unroll
+      for (int i = 0; i < S::CT2; ++i) {
+        const int col = (wave * S::CT2 + i) * 32 + l32;
+        const U16 b = ld_unit(w2e + (int64_t)col * h + hc + kb * 2 * UE + hi * UE);
+#pragma unroll
+        for (int tt = 0; tt < S::TT; ++tt) Mfma<T>::k32(acc2[tt][i], a[tt], b);
+      }
+    }
+  }
+
+  // b2, then write the rows in segment order.
+#pragma unroll
+  for (int i = 0; i < S::CT2; ++i) {
+    const int col = (wave * S::CT2 + i) * 32 + l32;
+    const float bias = p.b2 ? load_scalar<T>(p.b2, (int64_t)e * D + col) : 0.f;
+#pragma unroll
+    for (int tt = 0; tt < S::TT; ++tt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int tok = tt * 32 + 8 * (j / 4) + 4 * hi + (j % 4);
+        if (tok < rows) store_scalar<T>(p.out, (seg + tok) * D + col, acc2[tt][i][j] + bias);
+      }
+  }
+}
+
+// Lists the work units: expert e gets ceil(count_e / BM) units. One workgroup;
+// thread t owns a contiguous span of experts.
+__global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ offsets, int n, int bm,
+                                                 int32_t* __restrict__ blocks) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int e0 = min(n, t * per), e1 = min(n, e0 + per);
+  int s = 0;
+  for (int e = e0; e < e1; ++e) s += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  part[t] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = (t >= o) ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int pos = part[t] - s;
+  for (int e = e0; e < e1; ++e) {
+    const int cnt = offsets[e + 1] - offsets[e];
+    for (int r = 0; r < cnt; r += bm) {
+      blocks[1 + 2 * pos] = e;
+      blocks[2 + 2 * pos] = r;
+      ++pos;
+    }
+  }
+  if (t == 1023) blocks[0] = part[t];
+}
+
+template <typename T, int D>
+hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* offsets, int n,
+                        hipStream_t s) {
+  using S = FfnShape<T, D>;
+  hipLaunchKernelGGL(ffn_plan, dim3(1), dim3(1024), 0, s, offsets, n, S::BM,
+                     const_cast<int32_t*>(p.blocks));
+  if (max_blocks > 0)
+    hipLaunchKernelGGL((ffn_kernel<T, D>), dim3((unsigned)max_blocks), dim3(S::NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+int bm_for(int d) {
+  switch (d) {
+    case 64: return FfnShape<T, 64>::BM;
+    case 128: return FfnShape<T, 128>::BM;
+    case 256: return FfnShape<T, 256>::BM;
+    case 512: return FfnShape<T, 512>::BM;
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+int ffn_rows_per_block(int d, Dt dt) { return dt == kBF16 ? bm_for<bf16>(d) : bm_for<float>(d); }
+
+int64_t ffn_max_blocks(int64_t rows, int n, int d, Dt dt) {
+  const int bm = ffn_rows_per_block(d, dt);
+  if (bm <= 0) return 0;
+  return (rows + bm - 1) / bm + n;
+}
+
+bool ffn_supported(int d, int h, Dt dt) {
+  (void)dt;
+  return (d == 64 || d == 128 || d == 256 || d == 512) && h >= 128 && h % 128 == 0;
+}
+
+hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const void* x,
+                      const int32_t* offsets, const int32_t* perm_token, const void* w1,
+                      const void* b1, const void* w2, const void* b2, void* expert_out,
+                      int32_t* blocks, hipStream_t s) {
+  FfnParams p{x, offsets, perm_token, w1, b1, w2, b2, expert_out, blocks, h};
+  const int64_t mb = ffn_max_blocks(tokens * k, n, d, dt);
+  if (dt == kBF16) {
+    switch (d) {
+      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, s);
+      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, s);
+      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, s);
+      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, s);
+    }
+  } else {
+    switch (d) {
+      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, s);
+      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, s);
+      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, s);
+      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -1,0 +1,383 @@
+// Template of the gating kernel; instantiated per storage-type combination in
+// gate_bf16.hip, gate_bf16x_f32w.hip and gate_f32.hip.
+#pragma once
+
+// Noisy top-k gating on gfx950 (section "Noisy top-k gating", eqs 3-5, and the
+// forward-pass listing of "Implementation notes"), and the Load pass of
+// "A differentiable count of examples" (eqs 8-10), which shares its main loop.
+//
+// One workgroup owns 128 token rows (8 waves x 16 rows) and sweeps all n
+// experts in chunks: the clean-logit and noise-scale weight rows of a chunk
+// are staged once in LDS (double-buffered, in matrix-core fragment order) and
+// shared by the 8 waves; each wave keeps its 16 rows of x in registers as MFMA
+// A operands for the whole sweep. The logits never reach HBM.
+//
+// Pass 1 epilogue, per (token, expert): sigma = Softplus(u) + floor,
+// H = clean + eps * sigma; each lane keeps, for its 4 rows, the L best (H,
+// expert) pairs of the experts it sees (expert = lane mod 16); at the end the
+// 16 lanes of a row merge their lists (butterfly over lane bits 0-3), and the
+// row's top k, their softmax gates and the k-th/(k+1)-th logits are written.
+//
+// Pass 2 epilogue: P = Phi((clean - thr) / sigma) with thr the (k+1)-th logit
+// for selected experts and the k-th otherwise; column sums over the block's
+// rows in a fixed order go to a per-block partial, reduced afterwards in block
+// order. Pass 2 recomputes the matrix products instead of storing B x n logits.
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace gate_detail {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+static_assert(kGateRows == kWaves * 16, "gate rows per block");
+
+struct GateParams {
+  const void* x;
+  const void* wg;
+  const void* wn;
+  const float* bias;
+  const float* eps;
+  int64_t B;
+  int n, k;
+  float floor;
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* thresh;
+  const int32_t* sel_idx;
+  const float* sel_thr;
+  float* partial;
+};
+
+template <typename CT>
+struct GateShape;
+template <>
+struct GateShape<bf16> {
+  static constexpr int kChunk = 32;  // experts per LDS chunk
+};
+template <>
+struct GateShape<float> {
+  static constexpr int kChunk = 16;
+};
+
+// Loads the 16-byte unit of x (compute type CT) at element offset `off`.
+template <typename XS, typename CT>
+__device__ __forceinline__ U16 load_x_unit(const void* x, int64_t off) {
+  if constexpr (sizeof(XS) == sizeof(CT)) {
+    return ld_unit(reinterpret_cast<const char*>(x) + off * sizeof(XS));
+  } else {
+    return widen4_bf16(reinterpret_cast<const char*>(x) + off * sizeof(XS));  // bf16 -> fp32
+  }
+}
+
+// L-entry descending list insertion of a (value, index) pair known to rank
+// after every equal value already in the list (its index is larger).
+template <int L>
+__device__ __forceinline__ void insert_new(float (&lv)[L], int (&li)[L], float v, int id) {
+  if (v > lv[L - 1]) {
+    lv[L - 1] = v;
+    li[L - 1] = id;
+#pragma unroll
+    for (int s = L - 1; s > 0; --s) {
+      const bool sw = lv[s] > lv[s - 1];
+      const float tv = lv[s];
+      const int ti = li[s];
+      lv[s] = sw ? lv[s - 1] : tv;
+      li[s] = sw ? li[s - 1] : ti;
+      lv[s - 1] = sw ? tv : lv[s - 1];
+      li[s - 1] = sw ? ti : li[s - 1];
+    }
+  }
+}
+
+// Insertion with the full ranking order (used when merging lists).
+template <int L>
+__device__ __forceinline__ void insert_any(float (&lv)[L], int (&li)[L], float v, int id) {
+  if (ranks_before(v, id, lv[L - 1], li[L - 1])) {
+    lv[L - 1] = v;
+    li[L - 1] = id;
+#pragma unroll
+    for (int s = L - 1; s > 0; --s) {
+      const bool sw = ranks_before(lv[s], li[s], lv[s - 1], li[s - 1]);
+      const float tv = lv[s];
+      const int ti = li[s];
+      lv[s] = sw ? lv[s - 1] : tv;
+      li[s] = sw ? li[s - 1] : ti;
+      lv[s - 1] = sw ? tv : lv[s - 1];
+      li[s - 1] = sw ? ti : li[s - 1];
+    }
+  }
+}
+
+template <typename XS, typename CT, int D, int L, bool TRAIN, bool PASS2>
+__global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
+  constexpr int UE = Elem<CT>::kPerUnit;
+  constexpr int KB = 4 * UE;  // K-block of the 16x16 tiles
+  static_assert(D % KB == 0, "d must be a multiple of the K-block");
+  constexpr int NKB = D / KB;
+  constexpr int EC = GateShape<CT>::kChunk;
+  constexpr int NT = EC / 16;
+  constexpr int NM = TRAIN ? 2 : 1;
+  constexpr int UROW = D / UE;  // units per weight row
+  constexpr int CHUNK_UNITS = NM * EC * UROW;
+  constexpr int LOAD_ITERS = (CHUNK_UNITS + kThreads - 1) / kThreads;
+  static_assert(!PASS2 || TRAIN, "the load pass is only needed with noise");
+
+  __shared__ U16 wbuf[2][CHUNK_UNITS];
+  __shared__ float red[PASS2 ? 2 : 1][kWaves][EC];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 15;  // A-operand row / C column within a 16x16 tile
+  const int q = lane >> 4;   // K unit of the A/B operands; C row group
+  const int64_t B = p.B;
+  const int n = p.n;
+  const int64_t row0 = (int64_t)blockIdx.x * kGateRows + wave * 16;
+
+  // x rows of this wave as A operands for every K-block.
+  U16 xa[NKB];
+  {
+    const int64_t r = row0 + lr;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      xa[kb] = (r < B) ? load_x_unit<XS, CT>(p.x, r * D + kb * KB + q * UE) : zero_unit();
+  }
+
+  // Per-lane state for the C rows row0 + 4q + r, r < 4.
+  float lv[4][L];
+  int li[4][L];
+  int sel[4][L - 1];
+  float thr_k[4], thr_k1[4];
+  if constexpr (!PASS2) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < L; ++j) {
+        lv[r][j] = -INFINITY;
+        li[r][j] = 0x7FFFFFFF;
+      }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = row0 + 4 * q + r;
+      const bool ok = row < B;
+#pragma unroll
+      for (int j = 0; j < L - 1; ++j) sel[r][j] = (ok && j < p.k) ? p.sel_idx[row * p.k + j] : -1;
+      thr_k[r] = ok ? p.sel_thr[row * 2] : 0.f;
+      thr_k1[r] = ok ? p.sel_thr[row * 2 + 1] : 0.f;
+    }
+  }
+
+  U16 stage[LOAD_ITERS];
+  auto gload = [&](int c) {
+#pragma unroll
+    for (int it = 0; it < LOAD_ITERS; ++it) {
+      const int u = tid + it * kThreads;
+      if (u < CHUNK_UNITS) {
+        const int m = u / (EC * UROW);
+        const int rem = u - m * (EC * UROW);
+        const int col = rem / UROW;
+        const int ku = rem - col * UROW;
+        const int e = c * EC + col;
+        const CT* w = reinterpret_cast<const CT*>(m ? p.wn : p.wg);
+        stage[it] = (e < n) ? ld_unit(w + (int64_t)e * D + ku * UE) : zero_unit();
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < LOAD_ITERS; ++it) {
+      const int u = tid + it * kThreads;
+      if (u < CHUNK_UNITS) {
+        const int m = u / (EC * UROW);
+        const int rem = u - m * (EC * UROW);
+        const int col = rem / UROW;
+        const int ku = rem - col * UROW;
+        const int kb = ku >> 2;
+        const int qq = ku & 3;
+        const int frag_lane = (col & 15) + 16 * qq;
+        const int nt = col >> 4;
+        wbuf[buf][((kb * NM + m) * NT + nt) * 64 + frag_lane] = stage[it];
+      }
+    }
+  };
+
+  const int nchunks = (n + EC - 1) / EC;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunks) gload(c + 1);
+
+    float ev[NT][4];
+    if constexpr (TRAIN && !PASS2) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = row0 + 4 * q + r;
+          const int e = c * EC + nt * 16 + lr;
+          ev[nt][r] = (row < B && e < n) ? p.eps[row * n + e] : 0.f;
+        }
+    }
+
+    f32x4 acc[NM][NT];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          Mfma<CT>::k16(acc[m][nt], xa[kb], wbuf[buf][((kb * NM + m) * NT + nt) * 64 + lane]);
+
+    float colsum[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      colsum[nt] = 0.f;
+      const int e = c * EC + nt * 16 + lr;
+      const float bias = (p.bias && e < n) ? p.bias[e] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = row0 + 4 * q + r;
+        if (row < B && e < n) {
+          const float clean = acc[0][nt][r] + bias;
+          if constexpr (!PASS2) {
+            float H = clean;
+            if constexpr (TRAIN) H = clean + ev[nt][r] * (softplus_f(acc[NM - 1][nt][r]) + p.floor);
+            insert_new<L>(lv[r], li[r], H, e);
+          } else {
+            const float sigma = softplus_f(acc[NM - 1][nt][r]) + p.floor;
+            bool member = false;
+#pragma unroll
+            for (int j = 0; j < L - 1; ++j) member |= (sel[r][j] == e);
+            const float thr = member ? thr_k1[r] : thr_k[r];
+            colsum[nt] += phi_f((clean - thr) / sigma);
+          }
+        }
+      }
+    }
+    if constexpr (PASS2) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float s = colsum[nt];
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (q == 0) red[buf][wave][nt * 16 + lr] = s;
+      }
+    }
+
+    if (c + 1 < nchunks) lstore(buf ^ 1);
+    __syncthreads();
+
+    if constexpr (PASS2) {
+      if (tid < EC) {
+        const int e = c * EC + tid;
+        if (e < n) {
+          float s = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) s += red[buf][w][tid];
+          p.partial[(int64_t)blockIdx.x * n + e] = s;
+        }
+      }
+    }
+  }
+
+  if constexpr (!PASS2) {
+    // Merge the 16 lanes that share each row.
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float ov[L];
+        int oi[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+          ov[j] = __shfl_xor(lv[r][j], s);
+          oi[j] = __shfl_xor(li[r][j], s);
+        }
+#pragma unroll
+        for (int j = 0; j < L; ++j) insert_any<L>(lv[r], li[r], ov[j], oi[j]);
+      }
+    }
+    if (lr == 0) {
+      const int k = p.k;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = row0 + 4 * q + r;
+        if (row < B) {
+          // softmax over the k kept logits (the rest are -inf, gate 0)
+          const float top = lv[r][0];
+          float ex[L - 1];
+          float z = 0.f;
+#pragma unroll
+          for (int j = 0; j < L - 1; ++j) {
+            ex[j] = (j < k) ? expf(lv[r][j] - top) : 0.f;
+            z += ex[j];
+          }
+          const float inv = 1.0f / z;
+#pragma unroll
+          for (int j = 0; j < L - 1; ++j) {
+            if (j < k) {
+              p.topk_idx[row * k + j] = li[r][j];
+              p.topk_gate[row * k + j] = ex[j] * inv;
+            }
+          }
+          float vk = lv[r][0], vk1 = lv[r][1];
+#pragma unroll
+          for (int j = 1; j < L; ++j) {
+            if (j == k - 1) vk = lv[r][j];
+            if (j == k) vk1 = lv[r][j];
+          }
+          p.thresh[row * 2] = vk;
+          p.thresh[row * 2 + 1] = vk1;
+        }
+      }
+    }
+  }
+}
+
+template <typename XS, typename CT, int D, int L>
+hipError_t gate_dispatch_train(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
+  const dim3 grid((unsigned)gate_blocks(g.tokens));
+  if (pass2) {
+    hipLaunchKernelGGL((gate_kernel<XS, CT, D, L, true, true>), grid, dim3(kThreads), 0, s, p);
+  } else if (g.train) {
+    hipLaunchKernelGGL((gate_kernel<XS, CT, D, L, true, false>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((gate_kernel<XS, CT, D, L, false, false>), grid, dim3(kThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename XS, typename CT, int D>
+hipError_t gate_dispatch_l(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
+  if (g.k <= 4) return gate_dispatch_train<XS, CT, D, 5>(g, p, pass2, s);
+  return gate_dispatch_train<XS, CT, D, 9>(g, p, pass2, s);
+}
+
+template <typename XS, typename CT>
+hipError_t gate_dispatch_d(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
+  switch (g.d) {
+    case 64: return gate_dispatch_l<XS, CT, 64>(g, p, pass2, s);
+    case 128: return gate_dispatch_l<XS, CT, 128>(g, p, pass2, s);
+    case 256: return gate_dispatch_l<XS, CT, 256>(g, p, pass2, s);
+    case 512: return gate_dispatch_l<XS, CT, 512>(g, p, pass2, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gate_detail
+
+hipError_t gate_dispatch_bf16(const GateLaunch& g, const gate_detail::GateParams& p, bool pass2, hipStream_t s);
+hipError_t gate_dispatch_bf16x_f32w(const GateLaunch& g, const gate_detail::GateParams& p, bool pass2, hipStream_t s);
+hipError_t gate_dispatch_f32(const GateLaunch& g, const gate_detail::GateParams& p, bool pass2, hipStream_t s);
+
+}  // namespace moe

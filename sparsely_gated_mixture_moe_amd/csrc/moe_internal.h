@@ -1,0 +1,70 @@
+// Host-side launch wrappers shared between the kernel translation units and
+// the C ABI. Plain pointers and sizes only; every wrapper enqueues on the
+// given stream and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Dt { kF32 = 0, kBF16 = 1 };
+
+// Gate kernel geometry: 8 waves of 16 token rows each.
+constexpr int kGateRows = 128;
+// Routing: tokens per block of the counting sort.
+constexpr int kRouteTokens = 1024;
+
+struct GateLaunch {
+  const void* x;
+  const void* w_gate;
+  const void* w_noise;
+  const float* bias;  // may be null
+  const float* eps;   // null when !train
+  int64_t tokens;
+  int d, n, k;
+  Dt x_dt, w_dt;
+  int train;
+  float noise_floor;
+};
+
+// Noisy top-k gating: writes topk_idx [B,k], topk_gate [B,k], thresh [B,2].
+hipError_t launch_gate(const GateLaunch& g, int32_t* topk_idx, float* topk_gate, float* thresh,
+                       hipStream_t s);
+
+// Load (eq 10) with train = 1: recomputes the logits, evaluates P for every
+// (token, expert) and writes per-block column sums partial [blocks][n]; then
+// reduces them into load [n].
+int gate_blocks(int64_t tokens);
+hipError_t launch_load(const GateLaunch& g, const int32_t* topk_idx, const float* thresh,
+                       float* partial, float* load, hipStream_t s);
+bool gate_supported(int d, Dt x_dt, Dt w_dt, int k);
+
+// Routing.
+int route_blocks(int64_t tokens);
+hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
+                        const float* topk_gate, int32_t* blockcnt /* [n][route_blocks] */,
+                        int32_t* counts, int32_t* offsets, int32_t* perm_token, float* perm_gate,
+                        int32_t* slot_pos, float* importance, hipStream_t s);
+
+// Expert FFN.
+int ffn_rows_per_block(int d, Dt dt);
+int64_t ffn_max_blocks(int64_t rows, int n, int d, Dt dt);
+bool ffn_supported(int d, int h, Dt dt);
+hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const void* x,
+                      const int32_t* offsets, const int32_t* perm_token, const void* w1,
+                      const void* b1, const void* w2, const void* b2, void* expert_out,
+                      int32_t* blocks /* [2*max_blocks + 1] */, hipStream_t s);
+
+// Weighted sum.
+hipError_t launch_combine(int64_t tokens, int k, int d, Dt dt, const void* expert_out,
+                          const int32_t* slot_pos, const float* topk_gate, void* y,
+                          hipStream_t s);
+
+// Load as the hard count (train = 0) and the CV^2 losses.
+hipError_t launch_counts_to_load(const int32_t* counts, int n, float* load, hipStream_t s);
+hipError_t launch_cv2_losses(const float* importance, const float* load, int n, float w_imp,
+                             float w_load, float* losses, hipStream_t s);
+
+}  // namespace moe

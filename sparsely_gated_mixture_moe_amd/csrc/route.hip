@@ -1,0 +1,196 @@
+// Routing on gfx950: the per-expert row sets of the forward-pass listing
+// ("Implementation notes": rows = nonzero(G[:, i])) laid out as one contiguous
+// block per expert, which is how a single GPU keeps each expert's matrix
+// products as large as the batch allows (section "Keeping each expert's batch
+// large"). It is a stable counting sort of the B*k (token, slot) pairs by
+// expert, plus Importance (eq 6) as a segmented sum.
+//
+//   1. count:   per block of 1024 tokens, an LDS histogram over experts,
+//               written expert-major as blockcnt[e][b].
+//   2. scan_b:  per expert, exclusive prefix over blocks -> counts[e].
+//   3. scan_e:  one workgroup: exclusive prefix of counts -> offsets.
+//   4. scatter: per block, stable ranks. Each wave matches equal experts in its
+//               64 pairs with 16 ballots; the waves of a block then claim
+//               positions from LDS counters one wave at a time, in pair order,
+//               which keeps tokens ascending inside every segment.
+//   5. importance: one wave per expert sums its segment's gates in a fixed
+//               order (no float atomics).
+// All integer work is exact; the only float result (importance) is summed in
+// a fixed order, so the output is deterministic.
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__global__ __launch_bounds__(kThreads) void route_count(const int32_t* __restrict__ idx,
+                                                        int64_t npairs, int pairs_per_block, int n,
+                                                        int nblk, int32_t* __restrict__ blockcnt) {
+  extern __shared__ int hist[];
+  for (int e = threadIdx.x; e < n; e += kThreads) hist[e] = 0;
+  __syncthreads();
+  const int64_t p0 = (int64_t)blockIdx.x * pairs_per_block;
+  const int64_t p1 = min(npairs, p0 + pairs_per_block);
+  for (int64_t p = p0 + threadIdx.x; p < p1; p += kThreads) {
+    const int e = idx[p];
+    if (e >= 0 && e < n) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n; e += kThreads) blockcnt[(int64_t)e * nblk + blockIdx.x] = hist[e];
+}
+
+__global__ void route_scan_blocks(int32_t* __restrict__ blockcnt, int n, int nblk,
+                                  int32_t* __restrict__ counts) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  int32_t* c = blockcnt + (int64_t)e * nblk;
+  int s = 0;
+  for (int b = 0; b < nblk; ++b) {
+    const int v = c[b];
+    c[b] = s;
+    s += v;
+  }
+  counts[e] = s;
+}
+
+// Exclusive scan of n counts by one workgroup; thread t owns a contiguous span.
+__global__ __launch_bounds__(kThreads) void route_scan_experts(const int32_t* __restrict__ counts,
+                                                               int n, int32_t* __restrict__ offsets) {
+  __shared__ int part[kThreads];
+  const int t = threadIdx.x;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int e0 = min(n, t * per), e1 = min(n, e0 + per);
+  int s = 0;
+  for (int e = e0; e < e1; ++e) s += counts[e];
+  part[t] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the span sums.
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const int v = (t >= o) ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - s;
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = run;
+    run += counts[e];
+  }
+  if (t == kThreads - 1) offsets[n] = part[t];
+}
+
+__global__ __launch_bounds__(kThreads) void route_scatter(
+    const int32_t* __restrict__ idx, const float* __restrict__ gate, int64_t npairs, int k,
+    int pairs_per_block, int n, int nbits, int nblk, const int32_t* __restrict__ blockoff,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+    float* __restrict__ perm_gate, int32_t* __restrict__ slot_pos) {
+  extern __shared__ int ctr[];
+  for (int e = threadIdx.x; e < n; e += kThreads)
+    ctr[e] = offsets[e] + blockoff[(int64_t)e * nblk + blockIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t p0 = (int64_t)blockIdx.x * pairs_per_block;
+  const int64_t p1 = min(npairs, p0 + pairs_per_block);
+  for (int64_t base = p0; base < p1; base += kThreads) {
+    const int64_t p = base + threadIdx.x;
+    const bool valid = p < p1;
+    const int e = valid ? idx[p] : -1;
+    const bool live = valid && e >= 0 && e < n;
+    // Lanes holding the same expert: AND over the bits of the key (e + 1; dead lanes 0).
+    const uint32_t key = live ? (uint32_t)(e + 1) : 0u;
+    uint64_t eq = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1u;
+      const uint64_t m = __ballot(bit);
+      eq &= bit ? m : ~m;
+    }
+    const int rank = __popcll(eq & below);
+    const int cnt = __popcll(eq);
+    const int leader = __ffsll((unsigned long long)eq) - 1;
+    int claim = 0;
+    // Waves claim their segment positions in pair order.
+    for (int w = 0; w < kWaves; ++w) {
+      if (wave == w && live && rank == 0) {
+        claim = ctr[e];
+        ctr[e] = claim + cnt;
+      }
+      __syncthreads();
+    }
+    const int start = __shfl(claim, leader);
+    if (live) {
+      const int pos = start + rank;
+      perm_token[pos] = (int32_t)(p / k);
+      perm_gate[pos] = gate[p];
+      slot_pos[p] = pos;
+    } else if (valid) {
+      slot_pos[p] = -1;
+    }
+  }
+}
+
+__global__ void route_importance(const float* __restrict__ perm_gate,
+                                 const int32_t* __restrict__ offsets, int n,
+                                 float* __restrict__ importance) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (e >= n) return;
+  float s = 0.f;
+  for (int i = offsets[e] + lane; i < offsets[e + 1]; i += 64) s += perm_gate[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) importance[e] = s;
+}
+
+__global__ void fill_zero_i32(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+int route_blocks(int64_t tokens) { return (int)((tokens + kRouteTokens - 1) / kRouteTokens); }
+
+hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
+                        const float* topk_gate, int32_t* blockcnt, int32_t* counts,
+                        int32_t* offsets, int32_t* perm_token, float* perm_gate, int32_t* slot_pos,
+                        float* importance, hipStream_t s) {
+  const int nblk = route_blocks(tokens);
+  const int64_t npairs = tokens * k;
+  const int ppb = kRouteTokens * k;
+  const size_t lds = (size_t)n * sizeof(int);
+  int nbits = 1;
+  while ((1u << nbits) <= (uint32_t)n) ++nbits;  // keys 0..n need nbits bits
+  // Up to 32768 experts: 128 KB of LDS counters (set once per process).
+  static const bool lds_attr_set = [] {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(route_count),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * (int)sizeof(int));
+    hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * (int)sizeof(int));
+    return true;
+  }();
+  (void)lds_attr_set;
+  if (nblk > 0) {
+    hipLaunchKernelGGL(route_count, dim3(nblk), dim3(kThreads), lds, s, topk_idx, npairs, ppb, n,
+                       nblk, blockcnt);
+    hipLaunchKernelGGL(route_scan_blocks, dim3((n + 255) / 256), dim3(256), 0, s, blockcnt, n, nblk,
+                       counts);
+  } else {
+    hipLaunchKernelGGL(fill_zero_i32, dim3((n + 255) / 256), dim3(256), 0, s, counts, n);
+  }
+  hipLaunchKernelGGL(route_scan_experts, dim3(1), dim3(kThreads), 0, s, counts, n, offsets);
+  if (nblk > 0)
+    hipLaunchKernelGGL(route_scatter, dim3(nblk), dim3(kThreads), lds, s, topk_idx, topk_gate,
+                       npairs, k, ppb, n, nbits, nblk, blockcnt, offsets, perm_token, perm_gate,
+                       slot_pos);
+  if (importance)
+    hipLaunchKernelGGL(route_importance, dim3((n + 3) / 4), dim3(256), 0, s, perm_gate, offsets, n,
+                       importance);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,131 @@
+"""The C ABI on the host: the library loads, exports every symbol that
+include/moe.h declares, sizes workspaces, and rejects invalid arguments with
+the documented status before touching the device. No call here passes
+validation, so nothing is ever launched (the pointers are fake)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("sparsely_gated_mixture_moe_amd")
+from sparsely_gated_mixture_moe_amd import _binding as B  # noqa: E402
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|int|const char\*|size_t)\s+(moe_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_symbols_are_exported():
+    L = B.lib()
+    names = declared_functions()
+    assert "moe_forward" in names and len(names) >= 10
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in moe.h but not exported"
+    assert L.moe_abi_version() == 1
+
+
+def dims(**kw):
+    base = dict(tokens=1024, d_model=512, d_hidden=1024, n_experts=64, k=4, act_dtype=1,
+                expert_dtype=1, gate_dtype=1)
+    base.update(kw)
+    return B.MoeDims(*[base[f] for f, _ in B.MoeDims._fields_])
+
+
+def opts(**kw):
+    base = dict(train=1, noise_floor=0.01, w_importance=0.1, w_load=0.1)
+    base.update(kw)
+    return B.MoeGateOpts(*[base[f] for f, _ in B.MoeGateOpts._fields_])
+
+
+def P(v=FAKE):
+    return ctypes.c_void_p(v)
+
+
+def call_gate(d, o, x=FAKE, eps=FAKE, out=FAKE):
+    L = B.lib()
+    return L.moe_gate(ctypes.byref(d) if d is not None else None,
+                      ctypes.byref(o) if o is not None else None, P(x), P(), P(), None, P(eps),
+                      P(out), P(out), P(out), None, 0, None)
+
+
+def last_error():
+    return B.lib().moe_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    ({"k": 0}, INVALID, "k = 0"),
+    ({"k": 65}, INVALID, "k = 65"),
+    ({"k": 9, "n_experts": 100}, UNSUPPORTED, "k = 9"),
+    ({"tokens": -1}, INVALID, "tokens"),
+    ({"n_experts": 0}, INVALID, "n_experts"),
+    ({"n_experts": 40000}, INVALID, "n_experts"),
+    ({"d_model": 96}, UNSUPPORTED, "d_model"),
+    ({"d_model": 1024}, UNSUPPORTED, "d_model"),
+    ({"d_hidden": 100}, UNSUPPORTED, "d_hidden"),
+    ({"act_dtype": 0, "expert_dtype": 0, "gate_dtype": 1}, UNSUPPORTED, "bf16 gate"),
+    ({"expert_dtype": 0}, UNSUPPORTED, "expert_dtype"),
+    ({"act_dtype": 7}, INVALID, "dtype"),
+    ({"tokens": 600_000_000}, INVALID, "int32"),
+])
+def test_invalid_dims(kw, status, msg):
+    assert call_gate(dims(**kw), opts()) == status
+    assert msg in last_error()
+    assert B.lib().moe_workspace_size(ctypes.byref(dims(**kw)), ctypes.byref(opts())) == 0
+
+
+def test_null_and_misaligned_pointers():
+    assert call_gate(None, opts()) == INVALID and "dims" in last_error()
+    assert call_gate(dims(), None) == INVALID and "opts" in last_error()
+    assert call_gate(dims(), opts(), x=0) == INVALID and "x is NULL" in last_error()
+    assert call_gate(dims(), opts(), x=FAKE + 4) == INVALID and "aligned" in last_error()
+    assert call_gate(dims(), opts(), eps=0) == INVALID and "eps" in last_error()
+    assert call_gate(dims(), opts(train=2)) == INVALID
+    assert call_gate(dims(), opts(noise_floor=-1.0)) == INVALID
+    assert call_gate(dims(), opts(noise_floor=float("nan"))) == INVALID
+
+
+def test_workspace_checks():
+    L = B.lib()
+    d, o = dims(), opts()
+    need = L.moe_workspace_size(ctypes.byref(d), ctypes.byref(o))
+    # the forward pass holds the routing and one bf16 expert output row per (token, slot)
+    assert need >= 1024 * 4 * 512 * 2
+    args = [ctypes.byref(d), ctypes.byref(o)] + [P()] * 3 + [None] + [P()] + [P()] + [None] + \
+        [P()] + [None] + [P()] * 4 + [None] * 5
+    st = L.moe_forward(*args, P(), need - 256, None)
+    assert st == WORKSPACE and "needed" in last_error()
+    st = L.moe_forward(*args, None, need, None)
+    assert st == WORKSPACE
+    st = L.moe_forward(*args, P(FAKE + 16), need, None)
+    assert st == INVALID and "256-byte" in last_error()
+    # route needs its block histograms
+    st = L.moe_route(ctypes.byref(d), P(), P(), P(), P(), P(), P(), P(), None, P(), 16, None)
+    assert st == WORKSPACE
+
+
+def test_workspace_size_scales_with_workload():
+    L = B.lib()
+    small = L.moe_workspace_size(ctypes.byref(dims(tokens=1000)), ctypes.byref(opts()))
+    big = L.moe_workspace_size(ctypes.byref(dims(tokens=65536, n_experts=4096)),
+                               ctypes.byref(opts()))
+    assert 0 < small < big
+    infer = L.moe_workspace_size(ctypes.byref(dims(tokens=65536, n_experts=4096)),
+                                 ctypes.byref(opts(train=0)))
+    assert infer < big  # no Load partial sums without noise
+    assert L.moe_workspace_size(ctypes.byref(dims(tokens=0)), ctypes.byref(opts())) > 0
+
+
+def test_status_strings():
+    L = B.lib()
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+    assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"

@@ -1,0 +1,317 @@
+"""GPU parity: every entry point of the C ABI against the oracle, on the same
+seeded inputs (marked ``gpu``; run on an MI355X after building the library).
+
+Stage tests feed the oracle's own intermediates (selection, routing, expert
+outputs) to one kernel at a time, so each kernel is checked on inputs that do
+not come from another kernel. The fused ``moe_forward`` is then checked end to
+end, at sizes the oracle finishes in seconds (several tiles plus ragged tails)
+and at the full 65536-token, 4096-expert size on sampled rows and properties.
+"""
+import numpy as np
+import pytest
+
+import datagen as dg
+import oracle
+from parity import (GATE_TOL, LOSS_TOL, TOL_BF16, TOL_F32, announce, check_gating, gpu_inputs,
+                    near_tie_rows, out_tol, rel_err, scalar_rel, softmax_at, to_device, to_host)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import sparsely_gated_mixture_moe_amd as moe  # noqa: E402
+
+FLOOR = 1e-2
+
+
+def wl(name, **kw):
+    return dg.workload(name, **kw)
+
+
+# Small and ragged shapes: several gate row-blocks and expert chunks plus tails.
+GATE_CASES = [
+    ("tiny_fp32", {}),
+    ("tiny_fp32", {"tokens": 300}),
+    ("tiny_fp32", {"tokens": 333, "n_experts": 37, "k": 3, "d_model": 128}),
+    ("tiny_fp32", {"tokens": 130, "n_experts": 5, "k": 5}),
+    ("tiny_fp32", {"tokens": 257, "n_experts": 9, "k": 1}),
+    ("tiny_fp32", {"tokens": 200, "n_experts": 70, "k": 8, "d_model": 256}),
+    ("flat_fp32_n32", {}),
+    ("zipf_bf16_n256", {"tokens": 1500}),
+    ("flat_bf16_n4096", {"tokens": 700}),
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 333, "k": 2, "d_model": 128}),
+]
+
+
+def _gate_ids(c):
+    name, kw = c
+    return name + "".join(f"-{k}{v}" for k, v in kw.items())
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=[_gate_ids(c) for c in GATE_CASES])
+@pytest.mark.parametrize("train", [True, False])
+def test_gate_parity(case, train):
+    name, kw = case
+    w = wl(name, **kw)
+    announce(f"moe_gate {w.name} {kw} train={train}")
+    inp = dg.make_inputs(w, experts=False)
+    ref = oracle.gate(inp, w.k, train=train, noise_floor=FLOOR, want_logits=True)
+    g = gpu_inputs(inp)
+    idx, gate, thr = moe.moe_gate(g["x"], g["w_gate"], g["w_noise"], g["eps"] if train else None,
+                                  w.k, train=train, noise_floor=FLOOR, gate_bias=g.get("gate_bias"))
+    torch.cuda.synchronize()
+    stats = check_gating(ref, ref["H"], to_host(idx), to_host(gate), to_host(thr))
+    print(w.name, kw, train, {k: v for k, v in stats.items() if k != "swapped"},
+          "swapped", len(stats["swapped"]))
+
+
+def _random_topk(B, n, k, seed, skew=0.0):
+    rng = np.random.default_rng(seed)
+    if skew == 0.0:
+        keys = rng.random((B, n))
+    else:
+        keys = rng.random((B, n)) * np.arange(1, n + 1) ** (-skew)
+    idx = np.argsort(-keys, axis=1)[:, :k].astype(np.int32)
+    gate = rng.random((B, k)).astype(np.float32)
+    return idx, gate / gate.sum(1, keepdims=True)
+
+
+ROUTE_CASES = [(256, 16, 2, 0.0), (1000, 37, 3, 0.0), (5000, 256, 4, 1.0), (3, 8, 8, 0.0),
+               (4097, 4096, 4, 0.0), (0, 10, 2, 0.0)]
+
+
+@pytest.mark.parametrize("B,n,k,skew", ROUTE_CASES)
+def test_route_parity(B, n, k, skew):
+    announce(f"moe_route B={B} n={n} k={k} skew={skew}")
+    idx, gate = _random_topk(B, n, k, seed=B + n, skew=skew)
+    ref = oracle.route(idx, gate, n)
+    out = moe.moe_route(to_device(idx), to_device(gate), n)
+    torch.cuda.synchronize()
+    for key in ("counts", "offsets", "perm_token", "slot_pos"):
+        assert np.array_equal(to_host(out[key]), ref[key]), key
+    assert np.array_equal(to_host(out["perm_gate"]), ref["perm_gate"].astype(np.float32))
+    assert rel_err(to_host(out["importance"]), ref["importance"]) <= 1e-5
+
+
+@pytest.mark.parametrize("B,n,k", [(65536, 4096, 4), (131072, 16384, 4)])
+def test_route_full_size_against_stable_sort(B, n, k):
+    """Full-size routing against numpy's stable argsort (a library routine)."""
+    announce(f"moe_route full B={B} n={n}")
+    idx, gate = _random_topk(B, n, k, seed=7)
+    out = moe.moe_route(to_device(idx), to_device(gate), n)
+    torch.cuda.synchronize()
+    order = np.argsort(idx.ravel(), kind="stable")
+    assert np.array_equal(to_host(out["perm_token"]), (order // k).astype(np.int32))
+    assert np.array_equal(to_host(out["counts"]), np.bincount(idx.ravel(), minlength=n))
+    inv = np.empty(B * k, np.int32)
+    inv[order] = np.arange(B * k)
+    assert np.array_equal(to_host(out["slot_pos"]), inv)
+    imp = np.bincount(idx.ravel(), weights=gate.ravel().astype(np.float64), minlength=n)
+    assert rel_err(to_host(out["importance"]), imp) <= 1e-5
+
+
+def test_route_drops_out_of_range_entries():
+    announce("moe_route out-of-range entries")
+    idx = np.array([[0, 3], [-1, 2], [3, 9], [2, 0]], np.int32)
+    gate = np.full((4, 2), 0.5, np.float32)
+    out = moe.moe_route(to_device(idx), to_device(gate), 4)
+    torch.cuda.synchronize()
+    assert to_host(out["counts"]).tolist() == [2, 0, 2, 2]
+    assert to_host(out["offsets"]).tolist() == [0, 2, 2, 4, 6]
+    assert to_host(out["perm_token"])[:6].tolist() == [0, 3, 1, 3, 0, 2]
+    sp = to_host(out["slot_pos"]).tolist()
+    assert sp[2] == -1 and sp[5] == -1
+    assert to_host(out["importance"]).tolist() == [1.0, 0.0, 1.0, 1.0]
+
+
+FFN_CASES = [
+    ("tiny_fp32", {}, True),
+    ("tiny_fp32", {"tokens": 300, "n_experts": 7, "k": 2, "d_model": 128, "d_hidden": 256}, True),
+    ("tiny_fp32", {"tokens": 200, "n_experts": 5, "k": 2, "d_model": 256}, False),
+    ("flat_fp32_n32", {"tokens": 700}, True),
+    ("zipf_bf16_n256", {"tokens": 1200}, True),
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 40, "d_model": 64, "d_hidden": 128}, True),
+    ("flat_bf16_n4096", {"tokens": 600, "n_experts": 64}, False),
+]
+
+
+def _routed(w, inp, train=True):
+    ref = oracle.gate(inp, w.k, train=train, noise_floor=FLOOR)
+    return ref, oracle.route(ref["topk_idx"], ref["topk_gate"], w.n_experts)
+
+
+@pytest.mark.parametrize("case", FFN_CASES, ids=[_gate_ids(c[:2]) + f"-bias{c[2]}" for c in FFN_CASES])
+def test_expert_ffn_parity(case):
+    name, kw, bias = case
+    w = wl(name, **kw)
+    announce(f"moe_expert_ffn {w.name} {kw} bias={bias}")
+    inp = dg.make_inputs(w, with_bias=bias)
+    _, rt = _routed(w, inp)
+    g = gpu_inputs(inp)
+    eo = moe.moe_expert_ffn(g["x"], to_device(rt["offsets"]), to_device(rt["perm_token"]), g["w1"],
+                            g["w2"], w.k, b1=g.get("b1"), b2=g.get("b2"))
+    torch.cuda.synchronize()
+    experts = np.repeat(np.arange(w.n_experts, dtype=np.int32), rt["counts"])
+    ref = oracle.expert_pairs(inp, rt["perm_token"], experts)
+    err = rel_err(to_host(eo), ref)
+    print(w.name, kw, "expert_out err", err)
+    assert err <= out_tol(w.act_dtype == dg.BF16)
+
+
+@pytest.mark.parametrize("case", FFN_CASES[:5], ids=[_gate_ids(c[:2]) for c in FFN_CASES[:5]])
+def test_combine_parity(case):
+    name, kw, bias = case
+    w = wl(name, **kw)
+    announce(f"moe_combine {w.name} {kw}")
+    inp = dg.make_inputs(w, with_bias=bias)
+    ref, rt = _routed(w, inp)
+    experts = np.repeat(np.arange(w.n_experts, dtype=np.int32), rt["counts"])
+    eo = oracle.expert_pairs(inp, rt["perm_token"], experts).astype(np.float32)
+    if w.act_dtype == dg.BF16:
+        eo = dg.f32_to_bf16(eo)
+    y = moe.moe_combine(to_device(eo), to_device(rt["slot_pos"]),
+                        to_device(ref["topk_gate"].astype(np.float32)), n_experts=w.n_experts)
+    torch.cuda.synchronize()
+    y_ref = oracle.y_rows(inp, w.k, noise_floor=FLOOR)
+    err = rel_err(to_host(y), y_ref)
+    print(w.name, kw, "y err", err)
+    assert err <= out_tol(w.act_dtype == dg.BF16)
+
+
+AUX_CASES = GATE_CASES[:4] + [GATE_CASES[6], GATE_CASES[7], GATE_CASES[8]]
+
+
+@pytest.mark.parametrize("case", AUX_CASES, ids=[_gate_ids(c) for c in AUX_CASES])
+@pytest.mark.parametrize("train", [True, False])
+def test_aux_losses_parity(case, train):
+    name, kw = case
+    w = wl(name, **kw)
+    announce(f"moe_aux_losses {w.name} {kw} train={train}")
+    inp = dg.make_inputs(w, experts=False)
+    ref, rt = _routed(w, inp, train=train)
+    load_ref = oracle.load(inp, w.k, train=train, noise_floor=FLOOR)
+    g = gpu_inputs(inp)
+    load, losses = moe.moe_aux_losses(
+        g["x"], g["w_gate"], g["w_noise"], to_device(ref["topk_idx"]),
+        to_device(ref["thresh"].astype(np.float32)), to_device(rt["counts"]),
+        to_device(rt["importance"].astype(np.float32)), train=train, noise_floor=FLOOR,
+        w_importance=0.1, w_load=0.3, gate_bias=g.get("gate_bias"))
+    torch.cuda.synchronize()
+    err = rel_err(to_host(load), load_ref)
+    print(w.name, kw, train, "load err", err)
+    assert err <= GATE_TOL
+    lo = to_host(losses)
+    cv_imp = oracle.cv_squared(rt["importance"].astype(np.float32))
+    cv_load = oracle.cv_squared(load_ref)
+    assert scalar_rel(lo[0], cv_imp) <= LOSS_TOL
+    assert scalar_rel(lo[1], cv_load) <= LOSS_TOL
+    assert scalar_rel(lo[2], 0.1 * cv_imp + 0.3 * cv_load) <= LOSS_TOL
+
+
+def check_forward(w, inp, out, train, rows=None, full_load=True, w_imp=0.1, w_load=0.1):
+    """End-to-end check of moe_forward's outputs against the oracle."""
+    B, n, k = w.tokens, w.n_experts, w.k
+    sel_rows = np.arange(B) if rows is None else np.asarray(rows)
+    g_idx = to_host(out["topk_idx"])
+    g_gate = to_host(out["topk_gate"])
+    g_thr = to_host(out["thresh"])
+    ref = oracle.gate(inp, k, train=train, noise_floor=FLOOR, rows=sel_rows, want_logits=True)
+    stats = check_gating(ref, ref["H"], g_idx, g_gate, g_thr, rows=sel_rows)
+    # routing of the GPU's own selection: the stable sort by expert (a property at any size)
+    order = np.argsort(g_idx.ravel(), kind="stable")
+    counts = to_host(out["counts"])
+    assert np.array_equal(counts, np.bincount(g_idx.ravel(), minlength=n))
+    assert np.array_equal(to_host(out["perm_token"]), (order // k).astype(np.int32))
+    # y on the checked rows; rows whose near-tie selection differs are checked on the GPU's set
+    y = to_host(out["y"])[sel_rows]
+    y_ref = oracle.y_rows(inp, k, rows=sel_rows, train=train, noise_floor=FLOOR)
+    for r in stats["swapped"]:
+        t = int(sel_rows[r])
+        sel = g_idx[t]
+        gates = softmax_at(ref["H"][r], sel)
+        eo = oracle.expert_pairs(inp, [t] * k, sel)
+        y_ref[r] = (gates[:, None] * eo).sum(0)
+    yerr = rel_err(y, y_ref)
+    assert yerr <= out_tol(w.act_dtype == dg.BF16), f"y error {yerr}"
+    # Importance: the gate sums of the GPU's selection; on full-batch checks
+    # against the oracle, adjusted for near-tie rows where the GPU chose another valid set.
+    imp = to_host(out["importance"])
+    assert scalar_rel(imp.sum(), B) <= 1e-5
+    res = {"y_err": yerr, "near_tie": stats["near_tie"], "swapped": len(stats["swapped"])}
+    if rows is None:
+        full = oracle.route(ref["topk_idx"], ref["topk_gate"], n)["importance"]
+        for r in stats["swapped"]:
+            np.subtract.at(full, ref["topk_idx"][r], ref["topk_gate"][r])
+            np.add.at(full, g_idx[r], softmax_at(ref["H"][r], g_idx[r]))
+        ierr = rel_err(imp, full)
+        assert ierr <= GATE_TOL, f"importance error {ierr}"
+        res["imp_err"] = ierr
+    else:
+        full = np.bincount(g_idx.ravel(), weights=g_gate.ravel().astype(np.float64), minlength=n)
+        assert rel_err(imp, full) <= 1e-5
+    load = to_host(out["load"])
+    lo = to_host(out["losses"])
+    if full_load:
+        load_ref = oracle.load(inp, k, train=train, noise_floor=FLOOR)
+        lerr = rel_err(load, load_ref)
+        assert lerr <= GATE_TOL, f"load error {lerr}"
+        res["load_err"] = lerr
+        cv_imp, cv_load = oracle.cv_squared(full), oracle.cv_squared(load_ref)
+        assert scalar_rel(lo[0], cv_imp) <= LOSS_TOL
+        assert scalar_rel(lo[1], cv_load) <= LOSS_TOL
+        assert scalar_rel(lo[2], w_imp * cv_imp + w_load * cv_load) <= LOSS_TOL
+    return res
+
+
+FWD_CASES = [
+    ("tiny_fp32", {}, True),
+    ("tiny_fp32", {"tokens": 333, "n_experts": 37, "k": 3, "d_model": 128}, False),
+    ("tiny_fp32", {"tokens": 100, "n_experts": 4, "k": 4}, False),
+    ("flat_fp32_n32", {}, False),
+    ("zipf_bf16_n256", {"tokens": 4096}, False),
+    ("flat_bf16_n4096", {"tokens": 2048, "n_experts": 512}, False),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=[_gate_ids(c[:2]) for c in FWD_CASES])
+@pytest.mark.parametrize("train", [True, False])
+def test_forward_parity(case, train):
+    name, kw, bias = case
+    w = wl(name, **kw)
+    announce(f"moe_forward {w.name} {kw} train={train} bias={bias}")
+    inp = dg.make_inputs(w, with_bias=bias)
+    g = gpu_inputs(inp)
+    out = moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], w.k,
+                          b1=g.get("b1"), b2=g.get("b2"), gate_bias=g.get("gate_bias"),
+                          train=train, noise_floor=FLOOR, return_routing=True)
+    torch.cuda.synchronize()
+    res = check_forward(w, inp, out, train)
+    print(w.name, kw, train, res)
+
+
+def test_forward_is_deterministic():
+    w = wl("zipf_bf16_n256", tokens=2048)
+    announce("moe_forward determinism")
+    inp = dg.make_inputs(w)
+    g = gpu_inputs(inp)
+    f = moe.MoeForward(tuple(g["x"].shape), g["w_gate"], g["w_noise"], g["w1"], g["w2"], w.k,
+                       gate_bias=g["gate_bias"])
+    y1 = f(g["x"], g["eps"]).clone()
+    l1 = (f.importance.clone(), f.load.clone(), f.losses.clone())
+    y2 = f(g["x"], g["eps"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    for a, b in zip(l1, (f.importance, f.load, f.losses)):
+        assert torch.equal(a, b)
+
+
+def test_empty_batch():
+    w = wl("tiny_fp32", tokens=0)
+    announce("moe_forward empty batch")
+    inp = dg.make_inputs(w)
+    g = gpu_inputs(inp)
+    out = moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], w.k,
+                          return_routing=True)
+    torch.cuda.synchronize()
+    assert to_host(out["y"]).shape == (0, w.d_model)
+    assert np.all(to_host(out["importance"]) == 0) and np.all(to_host(out["load"]) == 0)
+    assert np.all(to_host(out["losses"]) == 0)
