@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target length of the oracle CPU-baseline run (0 skips it)")
     ap.add_argument("--stage-iters", type=int, default=10)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes three times "
+                         "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -98,6 +101,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if a.copy_calibration:
+        nbytes = a.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
+        return
 
     import datagen as dg
     import sparsely_gated_mixture_moe_amd as moe

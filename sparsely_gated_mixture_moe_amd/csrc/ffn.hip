@@ -28,7 +28,7 @@ namespace {
 
 template <typename T, int D>
 struct FfnShape {
-  static constexpr int NW = (D >= 128) ? 4 : 2;          // waves per workgroup
+  static constexpr int NW = D / 64 < 2 ? 2 : (D / 64 > 8 ? 8 : D / 64);  // waves
   static constexpr int HC = 32 * NW;                     // hidden units per chunk
   static constexpr int BM = (sizeof(T) == 4 && D >= 512) ? 32 : 64;  // rows per unit
   static constexpr int TT = BM / 32;                     // 32-row token tiles
@@ -73,7 +73,8 @@ __device__ __forceinline__ void store_scalar(void* p, int64_t i, float v) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__((FfnShape<T, D>::NW * 64)) void ffn_kernel(FfnParams p) {
+__global__ __launch_bounds__((FfnShape<T, D>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   using S = FfnShape<T, D>;
   constexpr int NT = S::NW * 64;
   constexpr int UE = S::UE;
@@ -119,17 +120,44 @@ __global__ __launch_bounds__((FfnShape<T, D>::NW * 64)) void ffn_kernel(FfnParam
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc2[tt][i][j] = 0.f;
 
-  for (int hc = 0; hc < h; hc += S::HC) {
+  // Weight streaming: W1/W2 fragments go from HBM straight into registers
+  // through two prefetch rings (PF1 K-blocks of W1, PF2 K-blocks of W2 ahead
+  // of use). The next phase's first fragments are requested before each
+  // barrier, so the loads stay in flight across the barriers.
+  constexpr int NKB1 = D / (2 * UE);
+  constexpr int NKB2 = S::HC / (2 * UE);
+  constexpr int PF1 = NKB1 < 8 ? NKB1 : 8;
+  constexpr int PF2 = NKB2 < 4 ? NKB2 : 4;
+  const int nch = h / S::HC;
+  auto w1_at = [&](int hc, int kb) {
+    return w1e + (int64_t)(hc + 32 * wave + l32) * D + kb * 2 * UE + hi * UE;
+  };
+  auto w2_at = [&](int hc, int kb, int i) {
+    return w2e + (int64_t)((wave * S::CT2 + i) * 32 + l32) * h + hc + kb * 2 * UE + hi * UE;
+  };
+  U16 pa[PF1];
+  U16 pb[PF2][S::CT2];
+#pragma unroll
+  for (int j = 0; j < PF1; ++j) pa[j] = ld_unit(w1_at(0, j));
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int hc = ch * S::HC;
     // GEMM1: rows = hidden units hc + 32*wave + (0..31), columns = tokens.
     f32x16 acc1[S::TT];
 #pragma unroll
     for (int tt = 0; tt < S::TT; ++tt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc1[tt][j] = 0.f;
-    const T* wrow = w1e + (int64_t)(hc + 32 * wave + l32) * D;
-#pragma unroll 4
-    for (int kb = 0; kb < D / (2 * UE); ++kb) {
-      const U16 a = ld_unit(wrow + kb * 2 * UE + hi * UE);
+#pragma unroll
+    for (int kb = 0; kb < NKB1; ++kb) {
+      const U16 a = pa[kb % PF1];
+      if (kb + PF1 < NKB1) pa[kb % PF1] = ld_unit(w1_at(hc, kb + PF1));
+      if (kb == (NKB1 > PF1 ? NKB1 - PF1 : 0)) {
+#pragma unroll
+        for (int j = 0; j < PF2; ++j)
+#pragma unroll
+          for (int i = 0; i < S::CT2; ++i) pb[j][i] = ld_unit(w2_at(hc, j, i));
+      }
       const int c = kb * 2 + hi;
 #pragma unroll
       for (int tt = 0; tt < S::TT; ++tt) {
@@ -172,8 +200,19 @@ __global__ __launch_bounds__((FfnShape<T, D>::NW * 64)) void ffn_kernel(FfnParam
     __syncthreads();
 
     // GEMM2: Out[token][col] += Hc[token][:] . W2[col][hc:hc+HC].
-#pragma unroll 2
-    for (int kb = 0; kb < S::HC / (2 * UE); ++kb) {
+#pragma unroll
+    for (int kb = 0; kb < NKB2; ++kb) {
+      U16 b[S::CT2];
+#pragma unroll
+      for (int i = 0; i < S::CT2; ++i) b[i] = pb[kb % PF2][i];
+      if (kb + PF2 < NKB2) {
+#pragma unroll
+        for (int i = 0; i < S::CT2; ++i) pb[kb % PF2][i] = ld_unit(w2_at(hc, kb + PF2, i));
+      }
+      if (kb == (NKB2 > PF2 ? NKB2 - PF2 : 0) && ch + 1 < nch) {
+#pragma unroll
+        for (int j = 0; j < PF1; ++j) pa[j] = ld_unit(w1_at(hc + S::HC, j));
+      }
       const int c = kb * 2 + hi;
       U16 a[S::TT];
 #pragma unroll
@@ -182,12 +221,9 @@ __global__ __launch_bounds__((FfnShape<T, D>::NW * 64)) void ffn_kernel(FfnParam
         a[tt] = hs[r * S::HU + (c ^ (r & (S::HSW - 1)))];
       }
 #pragma unroll
-      for (int i = 0; i < S::CT2; ++i) {
-        const int col = (wave * S::CT2 + i) * 32 + l32;
-        const U16 b = ld_unit(w2e + (int64_t)col * h + hc + kb * 2 * UE + hi * UE);
+      for (int i = 0; i < S::CT2; ++i)
 #pragma unroll
-        for (int tt = 0; tt < S::TT; ++tt) Mfma<T>::k32(acc2[tt][i], a[tt], b);
-      }
+        for (int tt = 0; tt < S::TT; ++tt) Mfma<T>::k32(acc2[tt][i], a[tt], b[i]);
     }
   }
 

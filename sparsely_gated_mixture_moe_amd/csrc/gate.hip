@@ -7,12 +7,27 @@ namespace {
 
 using gate_detail::GateParams;
 
-__global__ void load_reduce_kernel(const float* partial, int nblocks, int n, float* load) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= n) return;
+// load[e] = sum over gate blocks b of partial[b][e], in a fixed order: 32
+// experts per workgroup, 8 threads per expert each summing a strided subset
+// of the blocks, then the 8 partial sums in thread order.
+__global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restrict__ partial,
+                                                          int nblocks, int n,
+                                                          float* __restrict__ load) {
+  __shared__ float red[8][32];
+  const int col = threadIdx.x & 31;
+  const int part = threadIdx.x >> 5;
+  const int e = blockIdx.x * 32 + col;
   float s = 0.f;
-  for (int b = 0; b < nblocks; ++b) s += partial[(int64_t)b * n + e];
-  load[e] = s;
+  if (e < n)
+    for (int b = part; b < nblocks; b += 8) s += partial[(int64_t)b * n + e];
+  red[part][col] = s;
+  __syncthreads();
+  if (part == 0 && e < n) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += red[i][col];
+    load[e] = t;
+  }
 }
 
 hipError_t gate_dispatch(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
@@ -68,7 +83,7 @@ hipError_t launch_load(const GateLaunch& g, const int32_t* topk_idx, const float
     hipError_t e = gate_dispatch(g, p, true, s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(load_reduce_kernel, dim3((g.n + 255) / 256), dim3(256), 0, s, partial, nb,
+  hipLaunchKernelGGL(load_reduce_kernel, dim3((g.n + 31) / 32), dim3(256), 0, s, partial, nb,
                      g.n, load);
   return hipGetLastError();
 }

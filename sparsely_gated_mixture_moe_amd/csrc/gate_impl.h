@@ -170,19 +170,25 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
     }
   }
 
+  // Chunk staging. Unit u of a chunk is stored at LDS unit u in fragment order
+  // (u = ((kb * NM + m) * NT + nt) * 64 + fragment lane), so each wave writes
+  // one contiguous kilobyte per instruction and the MFMA B-operand reads are
+  // contiguous too. Fragment lane fl holds expert column nt * 16 + (fl & 15),
+  // K unit kb * 4 + (fl >> 4).
   U16 stage[LOAD_ITERS];
   auto gload = [&](int c) {
 #pragma unroll
     for (int it = 0; it < LOAD_ITERS; ++it) {
       const int u = tid + it * kThreads;
       if (u < CHUNK_UNITS) {
-        const int m = u / (EC * UROW);
-        const int rem = u - m * (EC * UROW);
-        const int col = rem / UROW;
-        const int ku = rem - col * UROW;
-        const int e = c * EC + col;
+        const int fl = u & 63;
+        const int rest = u >> 6;
+        const int nt = rest % NT;
+        const int m = (rest / NT) % NM;
+        const int kb = rest / (NT * NM);
+        const int e = c * EC + nt * 16 + (fl & 15);
         const CT* w = reinterpret_cast<const CT*>(m ? p.wn : p.wg);
-        stage[it] = (e < n) ? ld_unit(w + (int64_t)e * D + ku * UE) : zero_unit();
+        stage[it] = (e < n) ? ld_unit(w + (int64_t)e * D + (kb * 4 + (fl >> 4)) * UE) : zero_unit();
       }
     }
   };
@@ -190,17 +196,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
 #pragma unroll
     for (int it = 0; it < LOAD_ITERS; ++it) {
       const int u = tid + it * kThreads;
-      if (u < CHUNK_UNITS) {
-        const int m = u / (EC * UROW);
-        const int rem = u - m * (EC * UROW);
-        const int col = rem / UROW;
-        const int ku = rem - col * UROW;
-        const int kb = ku >> 2;
-        const int qq = ku & 3;
-        const int frag_lane = (col & 15) + 16 * qq;
-        const int nt = col >> 4;
-        wbuf[buf][((kb * NM + m) * NT + nt) * 64 + frag_lane] = stage[it];
-      }
+      if (u < CHUNK_UNITS) wbuf[buf][u] = stage[it];
     }
   };
 
