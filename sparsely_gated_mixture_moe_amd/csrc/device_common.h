@@ -107,13 +107,48 @@ struct Mfma<float> {
   }
 };
 
-// Softplus(u) = log(1 + e^u) in the form that cannot overflow.
-__device__ __forceinline__ float softplus_f(float u) {
-  return fmaxf(u, 0.0f) + log1pf(__expf(-fabsf(u)));
+// Fast reciprocal (v_rcp_f32, about 1 ulp).
+__device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// log(1 + t) for t in [0, 1] to a few ulp with one native log: with
+// w = 1 + t rounded, log(w) * t / (w - 1) cancels the rounding error of w
+// (Kahan's method; Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", 1991, Theorem 4).
+__device__ __forceinline__ float log1p_small(float t) {
+  const float w = 1.0f + t;
+  const float lw = __logf(w);
+  return (w == 1.0f) ? t : lw * t * rcp_f(w - 1.0f);
 }
 
-// Standard normal CDF.
-__device__ __forceinline__ float phi_f(float z) { return 0.5f * erfcf(-z * 0.70710678118654752f); }
+// Softplus(u) = log(1 + e^u) = max(u, 0) + log(1 + e^-|u|), which cannot overflow.
+__device__ __forceinline__ float softplus_f(float u) {
+  return fmaxf(u, 0.0f) + log1p_small(__expf(-fabsf(u)));
+}
+
+// erfc(x) for x >= 0 by the Chebyshev fit of Numerical Recipes (Press et al.,
+// 2nd ed., section 6.2, "erfcc"): fractional error below 1.2e-7 everywhere.
+__device__ __forceinline__ float erfc_nonneg(float x) {
+  const float t = rcp_f(1.0f + 0.5f * x);
+  float p = 0.17087277f;
+  p = fmaf(t, p, -0.82215223f);
+  p = fmaf(t, p, 1.48851587f);
+  p = fmaf(t, p, -1.13520398f);
+  p = fmaf(t, p, 0.27886807f);
+  p = fmaf(t, p, -0.18628806f);
+  p = fmaf(t, p, 0.09678418f);
+  p = fmaf(t, p, 0.37409196f);
+  p = fmaf(t, p, 1.00002368f);
+  p = fmaf(t, p, -1.26551223f);
+  return t * __expf(fmaf(-x, x, p));
+}
+
+// Standard normal CDF: Phi(z) = erfc(-z / sqrt 2) / 2, using
+// erfc(-a) = 2 - erfc(a) for the upper half.
+__device__ __forceinline__ float phi_f(float z) {
+  const float a = fabsf(z) * 0.70710678118654752f;
+  const float h = 0.5f * erfc_nonneg(a);
+  return z < 0.0f ? h : 1.0f - h;
+}
 
 // Ranking order of (logit, expert) pairs: larger logit first, equal logits to
 // the lower expert index.

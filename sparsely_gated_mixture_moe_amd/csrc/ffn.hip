@@ -30,7 +30,9 @@ template <typename T, int D>
 struct FfnShape {
   static constexpr int NW = D / 64 < 2 ? 2 : (D / 64 > 8 ? 8 : D / 64);  // waves
   static constexpr int HC = 32 * NW;                     // hidden units per chunk
-  static constexpr int BM = (sizeof(T) == 4 && D >= 512) ? 32 : 64;  // rows per unit
+  // rows per work unit: 96 for bf16, so that an expert with up to 96 rows streams its
+  // weights once; fp32 keeps its x tile within 64 KB of LDS
+  static constexpr int BM = sizeof(T) == 2 ? 96 : (D >= 512 ? 32 : 64);
   static constexpr int TT = BM / 32;                     // 32-row token tiles
   static constexpr int CT2 = D / 32 / NW;                // 32-col output tiles per wave
   static constexpr int UE = Elem<T>::kPerUnit;
@@ -81,8 +83,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   __shared__ U16 xs[S::BM * S::XU];
   __shared__ U16 hs[S::BM * S::HU];
 
-  const int blk = blockIdx.x;
-  if (blk >= p.blocks[0]) return;
+  // XCD-aware placement: workgroups are dealt to the 8 XCDs round-robin, so
+  // XCD x = blockIdx % 8 takes the x-th eighth of the unit list in order and
+  // the units of one expert run back to back on one L2.
+  const int count = p.blocks[0];
+  const int per_xcd = (count + 7) / 8;
+  const int slot = blockIdx.x / 8;
+  const int blk = (blockIdx.x % 8) * per_xcd + slot;
+  if (slot >= per_xcd || blk >= count) return;
   const int e = p.blocks[1 + 2 * blk];
   const int row0 = p.blocks[2 + 2 * blk];
   const int seg0 = p.offsets[e];
@@ -126,8 +134,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   // barrier, so the loads stay in flight across the barriers.
   constexpr int NKB1 = D / (2 * UE);
   constexpr int NKB2 = S::HC / (2 * UE);
-  constexpr int PF1 = NKB1 < 8 ? NKB1 : 8;
-  constexpr int PF2 = NKB2 < 4 ? NKB2 : 4;
+  constexpr int PF1 = NKB1 < 5 ? NKB1 : 5;
+  constexpr int PF2 = NKB2 < 2 ? NKB2 : 2;
   const int nch = h / S::HC;
   auto w1_at = [&](int hc, int kb) {
     return w1e + (int64_t)(hc + 32 * wave + l32) * D + kb * 2 * UE + hi * UE;
@@ -278,8 +286,10 @@ hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* o
   using S = FfnShape<T, D>;
   hipLaunchKernelGGL(ffn_plan, dim3(1), dim3(1024), 0, s, offsets, n, S::BM,
                      const_cast<int32_t*>(p.blocks));
+  // every XCD gets ceil(count / 8) slots; the grid covers the largest possible count
+  const int64_t grid = (max_blocks + 7) / 8 * 8;
   if (max_blocks > 0)
-    hipLaunchKernelGGL((ffn_kernel<T, D>), dim3((unsigned)max_blocks), dim3(S::NW * 64), 0, s, p);
+    hipLaunchKernelGGL((ffn_kernel<T, D>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

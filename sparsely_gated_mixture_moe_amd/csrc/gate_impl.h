@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
 #pragma unroll
             for (int j = 0; j < L - 1; ++j) member |= (sel[r][j] == e);
             const float thr = member ? thr_k1[r] : thr_k[r];
-            colsum[nt] += phi_f((clean - thr) / sigma);
+            colsum[nt] += phi_f((clean - thr) * rcp_f(sigma));
           }
         }
       }
