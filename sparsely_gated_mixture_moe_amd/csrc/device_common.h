@@ -115,14 +115,19 @@ __device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x
 // (Kahan's method; Goldberg, "What every computer scientist should know about
 // floating-point arithmetic", 1991, Theorem 4).
 __device__ __forceinline__ float log1p_small(float t) {
-  const float w = 1.0f + t;
-  const float lw = __logf(w);
+  const float w = 1.0f + t;  // in [1, 2]: the native log2 needs no range reduction
+  const float lw = __builtin_amdgcn_logf(w) * 0.69314718055994531f;
   return (w == 1.0f) ? t : lw * t * rcp_f(w - 1.0f);
+}
+
+// e^x through the native 2^x (v_exp_f32); arguments are <= 0 here.
+__device__ __forceinline__ float exp_native(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
 }
 
 // Softplus(u) = log(1 + e^u) = max(u, 0) + log(1 + e^-|u|), which cannot overflow.
 __device__ __forceinline__ float softplus_f(float u) {
-  return fmaxf(u, 0.0f) + log1p_small(__expf(-fabsf(u)));
+  return fmaxf(u, 0.0f) + log1p_small(exp_native(-fabsf(u)));
 }
 
 // erfc(x) for x >= 0 by the Chebyshev fit of Numerical Recipes (Press et al.,
@@ -139,7 +144,7 @@ __device__ __forceinline__ float erfc_nonneg(float x) {
   p = fmaf(t, p, 0.37409196f);
   p = fmaf(t, p, 1.00002368f);
   p = fmaf(t, p, -1.26551223f);
-  return t * __expf(fmaf(-x, x, p));
+  return t * exp_native(fmaf(-x, x, p));
 }
 
 // Standard normal CDF: Phi(z) = erfc(-z / sqrt 2) / 2, using

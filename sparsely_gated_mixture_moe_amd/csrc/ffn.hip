@@ -29,11 +29,12 @@ namespace {
 template <typename T, int D>
 struct FfnShape {
   static constexpr int NW = D / 64 < 2 ? 2 : (D / 64 > 8 ? 8 : D / 64);  // waves
-  static constexpr int HC = 32 * NW;                     // hidden units per chunk
+  static constexpr int HC = 16 * NW;                     // hidden units per chunk
   // rows per work unit: 96 for bf16, so that an expert with up to 96 rows streams its
   // weights once; fp32 keeps its x tile within 64 KB of LDS
   static constexpr int BM = sizeof(T) == 2 ? 96 : (D >= 512 ? 32 : 64);
-  static constexpr int TT = BM / 32;                     // 32-row token tiles
+  static constexpr int T16 = BM / 16;                    // 16-row token tiles (GEMM1)
+  static constexpr int TT = BM / 32;                     // 32-row token tiles (GEMM2)
   static constexpr int CT2 = D / 32 / NW;                // 32-col output tiles per wave
   static constexpr int UE = Elem<T>::kPerUnit;
   static constexpr int XU = D / UE;                      // 16-byte units per x row
@@ -41,6 +42,7 @@ struct FfnShape {
   static constexpr int XSW = XU >= 16 ? 16 : XU;
   static constexpr int HSW = HU >= 16 ? 16 : HU;
   static_assert(CT2 >= 1, "output tiles per wave");
+  static_assert(HU >= 2, "hidden chunk of at least two units");
 };
 
 struct FfnParams {
@@ -132,13 +134,20 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   // through two prefetch rings (PF1 K-blocks of W1, PF2 K-blocks of W2 ahead
   // of use). The next phase's first fragments are requested before each
   // barrier, so the loads stay in flight across the barriers.
-  constexpr int NKB1 = D / (2 * UE);
+  //
+  // GEMM1 runs on 16x16 tiles: wave w owns hidden units hc + 16 w + (0..15)
+  // (A operand, a row of W1 per lane) against all BM tokens (B operand from the
+  // x tile); GEMM2 runs on 32x32 tiles: wave w owns output columns
+  // [32 CT2 w, 32 CT2 (w + 1)) for all tokens.
+  constexpr int NKB1 = D / (4 * UE);
   constexpr int NKB2 = S::HC / (2 * UE);
-  constexpr int PF1 = NKB1 < 5 ? NKB1 : 5;
-  constexpr int PF2 = NKB2 < 2 ? NKB2 : 2;
+  constexpr int PF1 = NKB1 < 7 ? NKB1 : 7;
+  constexpr int PF2 = NKB2 < 3 ? NKB2 : 3;
+  const int l16 = lane & 15;
+  const int q = lane >> 4;
   const int nch = h / S::HC;
   auto w1_at = [&](int hc, int kb) {
-    return w1e + (int64_t)(hc + 32 * wave + l32) * D + kb * 2 * UE + hi * UE;
+    return w1e + (int64_t)(hc + 16 * wave + l16) * D + (kb * 4 + q) * UE;
   };
   auto w2_at = [&](int hc, int kb, int i) {
     return w2e + (int64_t)((wave * S::CT2 + i) * 32 + l32) * h + hc + kb * 2 * UE + hi * UE;
@@ -150,12 +159,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 
   for (int ch = 0; ch < nch; ++ch) {
     const int hc = ch * S::HC;
-    // GEMM1: rows = hidden units hc + 32*wave + (0..31), columns = tokens.
-    f32x16 acc1[S::TT];
+    f32x4 acc1[S::T16];
 #pragma unroll
-    for (int tt = 0; tt < S::TT; ++tt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc1[tt][j] = 0.f;
+    for (int tt = 0; tt < S::T16; ++tt) acc1[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB1; ++kb) {
       const U16 a = pa[kb % PF1];
@@ -166,32 +172,35 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 #pragma unroll
           for (int i = 0; i < S::CT2; ++i) pb[j][i] = ld_unit(w2_at(hc, j, i));
       }
-      const int c = kb * 2 + hi;
+      const int c = kb * 4 + q;
 #pragma unroll
-      for (int tt = 0; tt < S::TT; ++tt) {
-        const int r = tt * 32 + l32;
-        Mfma<T>::k32(acc1[tt], a, xs[r * S::XU + (c ^ (r & (S::XSW - 1)))]);
+      for (int tt = 0; tt < S::T16; ++tt) {
+        const int r = tt * 16 + l16;
+        Mfma<T>::k16(acc1[tt], a, xs[r * S::XU + (c ^ (r & (S::XSW - 1)))]);
       }
     }
     __syncthreads();  // the previous chunk's GEMM2 has finished reading hs
 
-    // bias + ReLU, round, stage Hc[token][hidden] in LDS.
+    // bias + ReLU, round, stage Hc[token][hidden] in LDS: lane l holds token
+    // 16 tt + l % 16 and the 4 consecutive hidden units 16 w + 4 (l / 16) + r.
+    {
+      const int hl = 16 * wave + 4 * q;
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if (p.b1) {
 #pragma unroll
-    for (int tt = 0; tt < S::TT; ++tt) {
-      const int tok = tt * 32 + l32;
+        for (int i = 0; i < 4; ++i) bias[i] = load_scalar<T>(p.b1, (int64_t)e * h + hc + hl + i);
+      }
+      const int cu = hl / UE;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int hl = 32 * wave + 8 * g + 4 * hi;  // first of 4 consecutive hidden units
+      for (int tt = 0; tt < S::T16; ++tt) {
+        const int tok = tt * 16 + l16;
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float a = acc1[tt][4 * g + i];
-          if (p.b1) a += load_scalar<T>(p.b1, (int64_t)e * h + hc + hl + i);
+          const float a = acc1[tt][i] + bias[i];
           v[i] = a > 0.f ? a : 0.f;
         }
-        const int cu = hl / UE;
-        const int cs = cu ^ (tok & (S::HSW - 1));
-        char* dst = reinterpret_cast<char*>(&hs[tok * S::HU + cs]);
+        char* dst = reinterpret_cast<char*>(&hs[tok * S::HU + (cu ^ (tok & (S::HSW - 1)))]);
         if constexpr (sizeof(T) == 2) {
           uint2 pk;
           pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);

@@ -74,7 +74,9 @@ hipError_t launch_gate(const GateLaunch& g, int32_t* topk_idx, float* topk_gate,
 
 hipError_t launch_load(const GateLaunch& g, const int32_t* topk_idx, const float* thresh,
                        float* partial, float* load, hipStream_t s) {
-  const int nb = gate_blocks(g.tokens);
+  // partial has room for gate_blocks() rows: the 32x32 kernel's 256-row blocks need fewer
+  const int rows = gate_uses_g32(g) ? 256 : kGateRows;
+  const int nb = (int)((g.tokens + rows - 1) / rows);
   if (nb > 0) {
     GateParams p = make_params(g);
     p.sel_idx = topk_idx;

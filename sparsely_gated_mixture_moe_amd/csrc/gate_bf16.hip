@@ -1,10 +1,31 @@
 // Gating kernels for x bf16 / gate weights bf16 storage.
-#include "gate_impl.h"
+#include "gate32_impl.h"
 
 namespace moe {
 
 hipError_t gate_dispatch_bf16(const GateLaunch& g, const gate_detail::GateParams& p, bool pass2,
                               hipStream_t s) {
+  using namespace gate_detail;
+  if (g.train && gate_uses_g32(g)) {
+    const dim3 grid((unsigned)((g.tokens + kG32Rows - 1) / kG32Rows));
+    const dim3 block(kG32Threads);
+    const bool k4 = g.k <= 4;
+#define MOE_G32(DD)                                                                        \
+  if (g.d == DD) {                                                                         \
+    if (pass2) {                                                                           \
+      if (k4) hipLaunchKernelGGL((gate32_kernel<DD, 5, true>), grid, block, 0, s, p);      \
+      else hipLaunchKernelGGL((gate32_kernel<DD, 9, true>), grid, block, 0, s, p);         \
+    } else {                                                                               \
+      if (k4) hipLaunchKernelGGL((gate32_kernel<DD, 5, false>), grid, block, 0, s, p);     \
+      else hipLaunchKernelGGL((gate32_kernel<DD, 9, false>), grid, block, 0, s, p);        \
+    }                                                                                      \
+    return hipGetLastError();                                                              \
+  }
+    MOE_G32(128)
+    MOE_G32(256)
+    MOE_G32(512)
+#undef MOE_G32
+  }
   return gate_detail::gate_dispatch_d<bf16, bf16>(g, p, pass2, s);
 }
 

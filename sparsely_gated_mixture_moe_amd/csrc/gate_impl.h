@@ -146,27 +146,34 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   }
 
   // Per-lane state for the C rows row0 + 4q + r, r < 4.
+  bool row_ok[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) row_ok[r] = row0 + 4 * q + r < B;
   float lv[4][L];
   int li[4][L];
+  float shared_thr[4];  // max over the row's 16 lanes of their L-th best: a lower
+                        // bound of the row's L-th best logit
   int sel[4][L - 1];
   float thr_k[4], thr_k1[4];
   if constexpr (!PASS2) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r) {
+      shared_thr[r] = -INFINITY;
 #pragma unroll
       for (int j = 0; j < L; ++j) {
         lv[r][j] = -INFINITY;
         li[r][j] = 0x7FFFFFFF;
       }
+    }
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t row = row0 + 4 * q + r;
-      const bool ok = row < B;
 #pragma unroll
-      for (int j = 0; j < L - 1; ++j) sel[r][j] = (ok && j < p.k) ? p.sel_idx[row * p.k + j] : -1;
-      thr_k[r] = ok ? p.sel_thr[row * 2] : 0.f;
-      thr_k1[r] = ok ? p.sel_thr[row * 2 + 1] : 0.f;
+      for (int j = 0; j < L - 1; ++j)
+        sel[r][j] = (row_ok[r] && j < p.k) ? p.sel_idx[row * p.k + j] : -1;
+      thr_k[r] = row_ok[r] ? p.sel_thr[row * 2] : 0.f;
+      thr_k1[r] = row_ok[r] ? p.sel_thr[row * 2 + 1] : 0.f;
     }
   }
 
@@ -180,15 +187,16 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
 #pragma unroll
     for (int it = 0; it < LOAD_ITERS; ++it) {
       const int u = tid + it * kThreads;
-      if (u < CHUNK_UNITS) {
+      if (CHUNK_UNITS % kThreads == 0 || u < CHUNK_UNITS) {
         const int fl = u & 63;
         const int rest = u >> 6;
         const int nt = rest % NT;
         const int m = (rest / NT) % NM;
         const int kb = rest / (NT * NM);
-        const int e = c * EC + nt * 16 + (fl & 15);
+        // experts past n read row n - 1; their logits are masked in the epilogue
+        const int e = min(c * EC + nt * 16 + (fl & 15), n - 1);
         const CT* w = reinterpret_cast<const CT*>(m ? p.wn : p.wg);
-        stage[it] = (e < n) ? ld_unit(w + (int64_t)e * D + (kb * 4 + (fl >> 4)) * UE) : zero_unit();
+        stage[it] = ld_unit(w + (int64_t)e * D + (kb * 4 + (fl >> 4)) * UE);
       }
     }
   };
@@ -196,32 +204,10 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
 #pragma unroll
     for (int it = 0; it < LOAD_ITERS; ++it) {
       const int u = tid + it * kThreads;
-      if (u < CHUNK_UNITS) wbuf[buf][u] = stage[it];
+      if (CHUNK_UNITS % kThreads == 0 || u < CHUNK_UNITS) wbuf[buf][u] = stage[it];
     }
   };
-
-  const int nchunks = (n + EC - 1) / EC;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nchunks) gload(c + 1);
-
-    float ev[NT][4];
-    if constexpr (TRAIN && !PASS2) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t row = row0 + 4 * q + r;
-          const int e = c * EC + nt * 16 + lr;
-          ev[nt][r] = (row < B && e < n) ? p.eps[row * n + e] : 0.f;
-        }
-    }
-
-    f32x4 acc[NM][NT];
+  auto mfma_chunk = [&](int buf, f32x4 (&acc)[NM][NT]) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -233,56 +219,156 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           Mfma<CT>::k16(acc[m][nt], xa[kb], wbuf[buf][((kb * NM + m) * NT + nt) * 64 + lane]);
-
-    float colsum[NT];
+  };
+  // Noise draws and biases of a chunk. Addresses are clamped into range and
+  // invalid entries are masked later by selects, so no branch splits the block
+  // that overlaps the matrix products with the epilogue.
+  const bool has_bias = p.bias != nullptr;
+  const float* bias_src = has_bias ? p.bias : reinterpret_cast<const float*>(p.wg);
+  auto load_eps = [&](int c, float (&ev)[NT][4], float (&bv)[NT]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      colsum[nt] = 0.f;
-      const int e = c * EC + nt * 16 + lr;
-      const float bias = (p.bias && e < n) ? p.bias[e] : 0.f;
+      const int e = min(c * EC + nt * 16 + lr, n - 1);
+      bv[nt] = bias_src[e];
+      if constexpr (TRAIN && !PASS2) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = row0 + 4 * q + r;
-        if (row < B && e < n) {
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = min(row0 + 4 * q + r, B - 1);
+          ev[nt][r] = p.eps[row * n + e];
+        }
+      }
+    }
+  };
+
+  // Software pipeline over expert chunks: the matrix products of chunk c + 1
+  // and the epilogue of chunk c sit in one straight-line block, so the matrix
+  // cores and the vector ALUs overlap; weights are staged two chunks ahead.
+  const int nchunks = (n + EC - 1) / EC;
+  f32x4 acc[NM][NT], acc_next[NM][NT];
+  float ev[NT][4], ev_next[NT][4], bv[NT], bv_next[NT];
+  gload(0);
+  lstore(0);
+  if (nchunks > 1) gload(1);
+  load_eps(0, ev, bv);
+  __syncthreads();
+  mfma_chunk(0, acc);
+  if (nchunks > 1) lstore(1);
+  __syncthreads();
+  if (nchunks > 2) gload(2);
+
+  for (int c = 0; c < nchunks; ++c) {
+    const bool more = c + 1 < nchunks;
+    // The two waves that share a SIMD (w and w + 4) run this chunk's two
+    // halves in opposite order -- one starts on the matrix core (next chunk's
+    // products; after the last chunk they read a stale buffer and are
+    // discarded) while the other starts on the vector ALUs (this chunk's
+    // epilogue) -- so the two units overlap.
+    float hv[NT][4];
+    bool cand_any = false;
+    float colsum[NT];
+    auto products = [&]() {
+      load_eps(more ? c + 1 : c, ev_next, bv_next);
+      mfma_chunk((c + 1) & 1, acc_next);
+    };
+    auto epilogue = [&]() {
+      // branch-free: invalid rows/experts are masked by selects
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        colsum[nt] = 0.f;
+        const int e = c * EC + nt * 16 + lr;
+        const bool e_ok = e < n;
+        const float bias = has_bias ? bv[nt] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = e_ok && row_ok[r];
           const float clean = acc[0][nt][r] + bias;
           if constexpr (!PASS2) {
             float H = clean;
-            if constexpr (TRAIN) H = clean + ev[nt][r] * (softplus_f(acc[NM - 1][nt][r]) + p.floor);
-            insert_new<L>(lv[r], li[r], H, e);
+            if constexpr (TRAIN) H = fmaf(ev[nt][r], softplus_f(acc[NM - 1][nt][r]) + p.floor, clean);
+            H = ok ? H : -INFINITY;
+            hv[nt][r] = H;
+            cand_any |= (H > lv[r][L - 1]) && (H >= shared_thr[r]);
           } else {
             const float sigma = softplus_f(acc[NM - 1][nt][r]) + p.floor;
             bool member = false;
 #pragma unroll
             for (int j = 0; j < L - 1; ++j) member |= (sel[r][j] == e);
             const float thr = member ? thr_k1[r] : thr_k[r];
-            colsum[nt] += phi_f((clean - thr) * rcp_f(sigma));
+            const float P = phi_f((clean - thr) * rcp_f(sigma));
+            colsum[nt] += ok ? P : 0.f;
           }
         }
       }
+    };
+    if (wave & 4) {
+      epilogue();
+      __builtin_amdgcn_sched_barrier(0);
+      products();
+    } else {
+      products();
+      __builtin_amdgcn_sched_barrier(0);
+      epilogue();
     }
+
     if constexpr (PASS2) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float s = colsum[nt];
         s += __shfl_xor(s, 16);
         s += __shfl_xor(s, 32);
-        if (q == 0) red[buf][wave][nt * 16 + lr] = s;
+        if (q == 0) red[c & 1][wave][nt * 16 + lr] = s;
+      }
+    } else {
+      // Rare path: candidates above both the lane's own L-th best and the
+      // row's shared bound. Experts reach a lane in increasing index order.
+      if (__any(cand_any)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (hv[nt][r] >= shared_thr[r])
+              insert_new<L>(lv[r], li[r], hv[nt][r], c * EC + nt * 16 + lr);
       }
     }
 
-    if (c + 1 < nchunks) lstore(buf ^ 1);
+    if (c + 2 < nchunks) lstore(c & 1);
     __syncthreads();
+    if (c + 3 < nchunks) gload(c + 3);
 
-    if constexpr (PASS2) {
+    if constexpr (!PASS2) {
+      if ((c & 3) == 3) {
+        // Refresh the shared bound: max over the 16 lanes of each row.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float t = lv[r][L - 1];
+          t = fmaxf(t, __shfl_xor(t, 1));
+          t = fmaxf(t, __shfl_xor(t, 2));
+          t = fmaxf(t, __shfl_xor(t, 4));
+          t = fmaxf(t, __shfl_xor(t, 8));
+          shared_thr[r] = t;
+        }
+      }
+    } else {
       if (tid < EC) {
         const int e = c * EC + tid;
         if (e < n) {
           float s = 0.f;
 #pragma unroll
-          for (int w = 0; w < kWaves; ++w) s += red[buf][w][tid];
+          for (int w = 0; w < kWaves; ++w) s += red[c & 1][w][tid];
           p.partial[(int64_t)blockIdx.x * n + e] = s;
         }
       }
+    }
+
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[m][nt] = acc_next[m][nt];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      bv[nt] = bv_next[nt];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ev[nt][r] = ev_next[nt][r];
     }
   }
 
@@ -371,6 +457,13 @@ hipError_t gate_dispatch_d(const GateLaunch& g, const GateParams& p, bool pass2,
 }
 
 }  // namespace gate_detail
+
+// The 32x32 kernel (gate32_impl.h) takes bf16 x and weights, d in {128, 256,
+// 512}, training mode; it uses 256-row blocks instead of 128.
+inline bool gate_uses_g32(const GateLaunch& g) {
+  return g.x_dt == kBF16 && g.w_dt == kBF16 && g.train &&
+         (g.d == 128 || g.d == 256 || g.d == 512);
+}
 
 hipError_t gate_dispatch_bf16(const GateLaunch& g, const gate_detail::GateParams& p, bool pass2, hipStream_t s);
 hipError_t gate_dispatch_bf16x_f32w(const GateLaunch& g, const gate_detail::GateParams& p, bool pass2, hipStream_t s);

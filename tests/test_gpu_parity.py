@@ -39,6 +39,8 @@ GATE_CASES = [
     ("zipf_bf16_n256", {"tokens": 1500}),
     ("flat_bf16_n4096", {"tokens": 700}),
     ("flat_bf16_n4096", {"tokens": 300, "n_experts": 333, "k": 2, "d_model": 128}),
+    ("flat_bf16_n4096", {"tokens": 555, "n_experts": 100, "k": 6, "d_model": 256}),
+    ("flat_bf16_n4096", {"tokens": 257, "n_experts": 17, "k": 8}),
 ]
 
 
@@ -177,7 +179,7 @@ def test_combine_parity(case):
     assert err <= out_tol(w.act_dtype == dg.BF16)
 
 
-AUX_CASES = GATE_CASES[:4] + [GATE_CASES[6], GATE_CASES[7], GATE_CASES[8]]
+AUX_CASES = GATE_CASES[:4] + GATE_CASES[6:]
 
 
 @pytest.mark.parametrize("case", AUX_CASES, ids=[_gate_ids(c) for c in AUX_CASES])
