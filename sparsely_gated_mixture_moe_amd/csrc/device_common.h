@@ -107,6 +107,24 @@ struct Mfma<float> {
   }
 };
 
+// One 16-byte global -> LDS copy per active lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_base + 16 l; lds_base must be the same in
+// every lane. The copy is issued from inline asm, so the compiler neither waits
+// for it nor counts it: the caller must wait for it (s_waitcnt vmcnt, in issue
+// order) before reading the destination. Untracked copies only make the
+// compiler's own vmcnt waits stricter, never too weak. The compiler sets m0
+// (the LDS base) for the asm; an SALU write of m0 needs one wait state before
+// an LDS-DMA instruction reads it, hence the s_nop.
+__device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "{m0}"(m0)
+      : "memory");
+}
+
 // Fast reciprocal (v_rcp_f32, about 1 ulp).
 __device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x); }
 

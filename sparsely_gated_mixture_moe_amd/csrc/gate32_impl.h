@@ -1,6 +1,6 @@
 // Noisy top-k gating and the Load pass on 32x32x16 bf16 matrix-core tiles,
-// for bf16 x and gate weights with d_model >= 128 in training mode (the
-// configuration of the large workloads). Same mathematics as gate_impl.h
+// for bf16 x and gate weights with d_model >= 128, n a multiple of 16, in
+// training mode (the configuration of the large workloads). Same mathematics as gate_impl.h
 // (sections "Noisy top-k gating", eqs 3-5, and "A differentiable count of
 // examples", eqs 8-10); different data movement:
 //
@@ -38,6 +38,11 @@ constexpr int kG32Rows = kG32Waves * 32;
 constexpr int kG32Chunk = 16;
 constexpr int kG32HStride = 20;  // padded row stride (floats) of the transpose tile
 
+template <int V>
+struct IntConst {
+  static constexpr int value = V;
+};
+
 template <int D, int L, bool PASS2>
 __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   constexpr int UE = 8;          // bf16 per 16-byte unit
@@ -46,7 +51,14 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   constexpr int DMA_PER_WAVE = NKB / kG32Waves;
   constexpr int EC = kG32Chunk;
 
-  __shared__ U16 wbuf[2][NKB * 64];
+  // weight double buffer as two objects, so that the compiler can tell a read
+  // of one from a copy in flight into the other
+  __shared__ U16 wbuf0[NKB * 64];
+  __shared__ U16 wbuf1[NKB * 64];
+  // pass 1: noise draws of a chunk, [256 rows][16 experts] fp32, then one copy
+  // of the chunk's 16 biases per wave; four chunks in flight
+  constexpr int ESLOT = kG32Rows * kG32Chunk + kG32Waves * kG32Chunk;
+  __shared__ float ebuf[PASS2 ? 1 : 4][PASS2 ? 1 : ESLOT];
   __shared__ float hbuf[PASS2 ? 1 : kG32Waves][32 * kG32HStride];
   __shared__ int selbuf[PASS2 ? kG32Rows : 1][L - 1];
   __shared__ float thrbuf[PASS2 ? kG32Rows : 1][2];
@@ -105,75 +117,110 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     li[j] = 0x7FFFFFFF;
   }
 
-  // Chunk c -> LDS buffer b. Wave w copies fragments kb = w + 8 i; lane l's
+  // Chunk c -> LDS buffer dst. Wave w copies fragments kb = w + 8 i; lane l's
   // 16 bytes are B column l32 (clean row of expert 16 c + l32, or the noise row
   // of expert 16 c + l32 - 16), K unit 2 kb + hi. Experts past n read row n - 1
   // and are masked in the epilogue.
-  auto dma = [&](int c, int b) {
+  auto dma = [&](int c, U16* dst) {
     const int e = min(c * EC + (l32 & 15), n - 1);
     const bf16* w = clean_lane ? wg : wn;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       const int kb = wave + kG32Waves * i;
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(w + (int64_t)e * D + (kb * 2 + hi) * UE),
-          (__attribute__((address_space(3))) void*)(&wbuf[b][kb * 64]), 16, 0, 0);
+      copy16_to_lds(w + (int64_t)e * D + (kb * 2 + hi) * UE, &dst[kb * 64]);
     }
-  };
-  auto mfma_chunk = [&](int b, f32x16& acc) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) Mfma<bf16>::k32(acc, xa[kb], wbuf[b][kb * 64 + lane]);
   };
   const bool has_bias = p.bias != nullptr;
   const float* bias_src = has_bias ? p.bias : reinterpret_cast<const float*>(p.wg);
-  auto load_chunk_inputs = [&](int c, float (&ev)[8], float& bv) {
-    const int e = min(c * EC + (l32 & 15), n - 1);
-    bv = bias_src[e];
-    if constexpr (!PASS2) {
+  auto load_bias = [&](int c, float& bv) { bv = bias_src[min(c * EC + (l32 & 15), n - 1)]; };
+  auto mfma_chunk = [&](const U16* src, f32x16& acc) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ev[i] = p.eps[min(row0 + rr[i], B - 1) * n + e];
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) Mfma<bf16>::k32(acc, xa[kb], src[kb * 64 + lane]);
+  };
+  // Noise draws of chunk c -> ring slot b (pass 1): wave w copies rows
+  // 32 w + 16 i + (l / 4), experts 4 (l % 4) .. + 3 of the chunk, so the slot
+  // holds the block's [256][16] tile row-major. This kernel runs only when n is
+  // a multiple of 16, so every 16-byte group is aligned and inside its row;
+  // rows past B read row B - 1 and are masked in the epilogue.
+  auto dma_eps = [&](int c, int b) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t row = min(row0 + 16 * i + (lane >> 2), B - 1);
+      const float* src = p.eps + row * n + c * EC + 4 * (lane & 3);
+      copy16_to_lds(src, &ebuf[b][(wave * 32 + 16 * i) * EC]);
+    }
+    // lanes 0-3 copy the chunk's biases (or, without a bias, any in-bounds
+    // floats, which are never read) into this wave's slot
+    if (lane < 4) {
+      copy16_to_lds(bias_src + c * EC + 4 * lane, &ebuf[b][kG32Rows * EC + wave * EC]);
     }
   };
 
   const int nchunks = (n + EC - 1) / EC;
   f32x16 acc, acc_next;
-  float ev[8], ev_next[8], bv, bv_next;
-  dma(0, 0);
-  if (nchunks > 1) dma(1, 1);
-  load_chunk_inputs(0, ev, bv);
+  float bv, bv_next;
+  dma(0, wbuf0);
+  if (nchunks > 1) dma(1, wbuf1);
+  if constexpr (!PASS2) {
+    for (int c = 0; c < 3 && c < nchunks; ++c) dma_eps(c, c);
+  }
+  if constexpr (PASS2) load_bias(0, bv);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  mfma_chunk(0, acc);
+  mfma_chunk(wbuf0, acc);
   __syncthreads();  // every wave has read chunk 0 before buffer 0 is refilled
 
-  for (int c = 0; c < nchunks; ++c) {
-    // Buffer c & 1 held chunk c, whose products every wave formed before the
-    // last barrier; refill it with chunk c + 2 (ready by the end of this pass).
-    if (c + 2 < nchunks) dma(c + 2, c & 1);
+  // One pass per chunk; P = c & 1 is a compile-time constant (the loop below
+  // is unrolled by two) so each pass names its weight buffers statically.
+  auto chunk_pass = [&](const int c, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    U16* const wfill = P ? wbuf1 : wbuf0;       // buffer c & 1: chunk c + 2 goes here
+    const U16* const wnext = P ? wbuf0 : wbuf1;  // buffer (c + 1) & 1: chunk c + 1
+    // Copies issued this pass, oldest first: (pass 2) chunk c + 1's bias into
+    // registers, chunk c + 2's weights into buffer c & 1 (whose chunk c every
+    // wave used before the last barrier), and (pass 1) chunk c + 3's noise
+    // draws and biases into ring slot (c + 3) & 3. The weights must land by
+    // the end of this pass; the noise draws have two more passes.
+    if constexpr (PASS2) load_bias(c + 1 < nchunks ? c + 1 : c, bv_next);
+    if (c + 2 < nchunks) dma(c + 2, wfill);
+    asm volatile("" ::: "memory");
+    if constexpr (!PASS2) {
+      if (c + 3 < nchunks) dma_eps(c + 3, (c + 3) & 3);
+    }
 
     float colsum = 0.f;
     float hpair[8];
-    auto products = [&]() {
-      load_chunk_inputs(c + 1 < nchunks ? c + 1 : c, ev_next, bv_next);
-      mfma_chunk((c + 1) & 1, acc_next);
-    };
+    auto products = [&]() { mfma_chunk(wnext, acc_next); };
     auto epilogue = [&]() {
       // exchange: clean lanes send clean rows j = 8..15, noise lanes send noise rows j = 0..7
       float recv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) recv[i] = __shfl_xor(clean_lane ? acc[8 + i] : acc[i], 16);
+      for (int i = 0; i < 8; ++i) {
+        // two static extracts and one select (kept apart so they are not
+        // folded into a per-lane dynamic index of the accumulator)
+        float hi8 = acc[8 + i], lo8 = acc[i];
+        asm("" : "+v"(hi8));
+        asm("" : "+v"(lo8));
+        recv[i] = __shfl_xor(clean_lane ? hi8 : lo8, 16);
+      }
       const int e = c * EC + (l32 & 15);
       const bool e_ok = e < n;
-      const float bias = has_bias ? bv : 0.f;
+      float bias;
+      if constexpr (PASS2) {
+        bias = has_bias ? bv : 0.f;
+      } else {
+        bias = has_bias ? ebuf[c & 3][kG32Rows * EC + wave * EC + (l32 & 15)] : 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float clean = (clean_lane ? acc[i] : recv[i]) + bias;
         const float u = clean_lane ? recv[i] : acc[8 + i];
         const bool ok = e_ok && row_ok[i];
         if constexpr (!PASS2) {
-          const float H = fmaf(ev[i], softplus_f(u) + p.floor, clean);
+          const float eps = ebuf[c & 3][(wave * 32 + rr[i]) * EC + (l32 & 15)];
+          const float H = fmaf(eps, softplus_f(u) + p.floor, clean);
           hpair[i] = ok ? H : -INFINITY;
         } else {
           const float sigma = softplus_f(u) + p.floor;
@@ -203,11 +250,22 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       const int ecol = l32 & 15;
 #pragma unroll
       for (int i = 0; i < 8; ++i) hb[rr[i] * kG32HStride + ecol] = hpair[i];
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      const float4 h0 = *reinterpret_cast<const float4*>(&hb[l32 * kG32HStride + hi * 8]);
-      const float4 h1 = *reinterpret_cast<const float4*>(&hb[l32 * kG32HStride + hi * 8 + 4]);
-      const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      // A wave's LDS instructions execute in order, so its own writes are
+      // visible to the reads below without a fence. The reads are issued (and
+      // waited for) in one asm block: the compiler would otherwise also wait
+      // for every global->LDS copy still in flight before an LDS read.
+      f32x4 h0, h1;
+      {
+        const uint32_t a = (uint32_t)(uintptr_t)(&hb[l32 * kG32HStride + hi * 8]);
+        asm volatile(
+            "ds_read_b128 %0, %2\n\t"
+            "ds_read_b128 %1, %2 offset:16\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(h0), "=v"(h1)
+            : "v"(a)
+            : "memory");
+      }
+      const float hv[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
       bool cand = false;
 #pragma unroll
       for (int i = 0; i < 8; ++i) cand |= hv[i] > lv[L - 1];
@@ -220,11 +278,18 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       // column sums: lanes l, l ^ 16 (same expert, other rows) and l ^ 32
       colsum += __shfl_xor(colsum, 16);
       colsum += __shfl_xor(colsum, 32);
-      if (lane < 16) red[c & 1][wave][lane] = colsum;
+      if (lane < 16) red[P][wave][lane] = colsum;
     }
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // Block barrier without a release fence (which would wait for every copy
+    // in flight): each wave first waits for its LDS traffic and for all its
+    // copies but the three noise/bias copies issued this pass, if any (copies
+    // complete in issue order, so a count of 3 then covers the weights).
+    if (!PASS2 && c + 3 < nchunks) {
+      asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
 
     if constexpr (PASS2) {
       if (tid < EC) {
@@ -232,7 +297,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         if (e < n) {
           float s = 0.f;
 #pragma unroll
-          for (int w = 0; w < kG32Waves; ++w) s += red[c & 1][w][tid];
+          for (int w = 0; w < kG32Waves; ++w) s += red[P][w][tid];
           p.partial[(int64_t)blockIdx.x * n + e] = s;
         }
       }
@@ -240,8 +305,10 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = acc_next[j];
     bv = bv_next;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ev[i] = ev_next[i];
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    chunk_pass(c, IntConst<0>{});
+    if (c + 1 < nchunks) chunk_pass(c + 1, IntConst<1>{});
   }
 
   if constexpr (!PASS2) {

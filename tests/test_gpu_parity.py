@@ -39,8 +39,9 @@ GATE_CASES = [
     ("zipf_bf16_n256", {"tokens": 1500}),
     ("flat_bf16_n4096", {"tokens": 700}),
     ("flat_bf16_n4096", {"tokens": 300, "n_experts": 333, "k": 2, "d_model": 128}),
-    ("flat_bf16_n4096", {"tokens": 555, "n_experts": 100, "k": 6, "d_model": 256}),
-    ("flat_bf16_n4096", {"tokens": 257, "n_experts": 17, "k": 8}),
+    ("flat_bf16_n4096", {"tokens": 555, "n_experts": 96, "k": 6, "d_model": 256}),
+    ("flat_bf16_n4096", {"tokens": 257, "n_experts": 32, "k": 8}),
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 100, "k": 3}),
 ]
 
 
