@@ -53,6 +53,35 @@ def time_calls(fn, iters, torch):
     return e0.elapsed_time(e1) / iters
 
 
+# HBM bytes per ffn_kernel launch from the calibrated FETCH_SIZE + WRITE_SIZE
+# counters of the committed rocprofv3 summary; valid only while the kernel's
+# sources are byte-identical to those the counters were taken on.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ffn_kernel_flat_bf16_n4096_hbm_traffic.txt")
+FFN_SOURCES = ["sparsely_gated_mixture_moe_amd/csrc/ffn.hip",
+               "sparsely_gated_mixture_moe_amd/csrc/device_common.h",
+               "sparsely_gated_mixture_moe_amd/csrc/moe_internal.h"]
+
+
+def profiled_traffic(workload):
+    import hashlib
+
+    if workload != "flat_bf16_n4096" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        key, sep, val = line.partition(":")
+        if sep and key in ("traffic_bytes_per_launch", "sources_sha256"):
+            fields[key] = val.strip()
+    h = hashlib.sha256()
+    for f in FFN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("sources_sha256") != h.hexdigest():
+        log("ffn sources changed since the traffic counters were taken: traffic = null")
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(w, inp, target_s):
     """The oracle's whole forward pass on the first S tokens of the workload,
     S grown until one run takes about target_s seconds."""
@@ -71,8 +100,10 @@ def cpu_baseline(w, inp, target_s):
 
     S = 256
     t = run(S)
-    if t < target_s / 4:
-        S = int(min(w.tokens, max(256, S * target_s / max(t, 1e-3))))
+    # grow the sample until one run takes at least half the target (fixed costs
+    # make the first estimate low)
+    while t < target_s / 2 and S < w.tokens:
+        S = int(min(w.tokens, max(2 * S, S * target_s / max(t, 1e-3))))
         t = run(S)
     threads = oracle.threads()
     return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -214,7 +245,7 @@ def main():
                    "gate_dtype": "bf16" if w.gate_dtype == dg.BF16 else "f32"},
         "roofline": {"kernel": "ffn_kernel (moe_expert_ffn)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(w.name),
                      "alg_bytes_per_launch": ffn_bytes, "avg_launch_ms": ffn_ms,
                      "mfma_frac": ffn_flops / (ffn_ms * 1e-3) / (mfma_peak * 1e12)},
         "step": {"alg_bytes": step_bytes, "alg_flops": step_flops,
