@@ -62,8 +62,14 @@ def _load():
         lib.oracle_route.argtypes = [_I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
         lib.oracle_forward.argtypes = [_I64, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D,
                                        _I, _P, _P, _P, _P, _I, _D, _D, _P, _P, _P, _P, _P, _P, _P]
+        lib.oracle_hier_gate.argtypes = [_I64, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P,
+                                         _I, _P, _P, _I, _D, _I, _P, _P,
+                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+        lib.oracle_hier_forward.argtypes = [_I64, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P,
+                                            _I, _P, _P, _I, _D, _I, _P, _P, _P, _P, _P, _P, _I,
+                                            _D, _D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         for f in ("oracle_gate", "oracle_load", "oracle_y_rows", "oracle_expert_pairs",
-                  "oracle_route", "oracle_forward"):
+                  "oracle_route", "oracle_forward", "oracle_hier_gate", "oracle_hier_forward"):
             getattr(lib, f).restype = _I
         _lib = lib
     return _lib
@@ -243,4 +249,105 @@ def forward(inp: Dict[str, np.ndarray], k: int, train: bool = True, noise_floor:
                                                                    "thresh", "importance", "load",
                                                                    "losses")])
     _check(rc, "forward")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Hierarchical MoE (section "Hierarchical MoE"; eq 12 read from its prose)
+# ---------------------------------------------------------------------------
+
+class _HierGate:
+    """Arguments of both gate levels: ``w_gate``/``w_noise`` [a, d], ``eps`` [B, a],
+    ``w_gate2``/``w_noise2`` [a, b, d], ``eps2`` [B, k1, b]."""
+
+    def __init__(self, inp: Dict[str, np.ndarray], k1: int, k2: int, train: bool):
+        self.x, self.x_dt = _arr(inp["x"])
+        self.wg1, self.w_dt = _arr(inp["w_gate"])
+        self.wn1, _ = _arr(inp["w_noise"])
+        self.wg2, w2_dt = _arr(inp["w_gate2"])
+        self.wn2, _ = _arr(inp["w_noise2"])
+        if w2_dt != self.w_dt:
+            raise ValueError("both gate levels must share a dtype")
+        self.B, self.d = self.x.shape
+        self.a, self.b = self.wg2.shape[0], self.wg2.shape[1]
+        if self.wg1.shape != (self.a, self.d) or self.wg2.shape != (self.a, self.b, self.d):
+            raise ValueError("gate weights must be [a, d] and [a, b, d]")
+        self.k1, self.k2 = k1, k2
+        self.eps1 = np.ascontiguousarray(inp["eps"], dtype=np.float32) if train else None
+        self.eps2 = np.ascontiguousarray(inp["eps2"], dtype=np.float32) if train else None
+        if train and (self.eps1.shape != (self.B, self.a) or
+                      self.eps2.shape != (self.B, k1, self.b)):
+            raise ValueError("eps must be [B, a] and eps2 [B, k1, b]")
+
+    def args(self):
+        return (_ptr(self.x), self.x_dt, _ptr(self.wg1), _ptr(self.wn1), _ptr(self.wg2),
+                _ptr(self.wn2), self.w_dt, _ptr(self.eps1), _ptr(self.eps2))
+
+
+def _forced(f, shape):
+    if f is None:
+        return None
+    f = np.ascontiguousarray(f, dtype=np.int32)
+    if f.shape != shape:
+        raise ValueError(f"forced selection must have shape {shape}")
+    return f
+
+
+def hier_gate(inp: Dict[str, np.ndarray], k1: int, k2: int, rows: Optional[Sequence[int]] = None,
+              train: bool = True, noise_floor: float = 1e-2, decide_fp32: bool = True,
+              force1=None, force2=None, want_logits: bool = False) -> Dict[str, np.ndarray]:
+    """Both gate levels on token rows ``rows`` (default all).
+
+    Returns sel1/gate1 [R, k1], thr1 [R, 2]; sel2/gate2 [R, k1, k2] (expert index within
+    the group), thr2 [R, k1, 2]; leaf_idx/leaf_gate [R, k1*k2] in slot order (r, j);
+    with ``want_logits`` also H1 [R, a] and H2 [R, k1, b]. ``force1`` [R, k1] and
+    ``force2`` [R, k1, k2] replace the selections (e.g. another valid choice on a near-tie row).
+    """
+    g = _HierGate(inp, k1, k2, train)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    R = g.B if rows_a is None else rows_a.size
+    K = k1 * k2
+    f1 = _forced(force1, (R, k1))
+    f2 = _forced(force2, (R, k1, k2))
+    out = {"sel1": np.empty((R, k1), np.int32), "gate1": np.empty((R, k1)),
+           "thr1": np.empty((R, 2)), "sel2": np.empty((R, k1, k2), np.int32),
+           "gate2": np.empty((R, k1, k2)), "thr2": np.empty((R, k1, 2)),
+           "leaf_idx": np.empty((R, K), np.int32), "leaf_gate": np.empty((R, K))}
+    if want_logits:
+        out["H1"] = np.empty((R, g.a))
+        out["H2"] = np.empty((R, k1, g.b))
+    rc = _load().oracle_hier_gate(
+        R, _ptr(rows_a), g.d, g.a, g.b, k1, k2, *g.args(), int(train), float(noise_floor),
+        int(decide_fp32), _ptr(f1), _ptr(f2), *[_ptr(out.get(key)) for key in (
+            "sel1", "gate1", "thr1", "H1", "sel2", "gate2", "thr2", "H2", "leaf_idx",
+            "leaf_gate")])
+    _check(rc, "hier_gate")
+    return out
+
+
+def hier_forward(inp: Dict[str, np.ndarray], k1: int, k2: int, train: bool = True,
+                 noise_floor: float = 1e-2, w_importance: float = 0.1, w_load: float = 0.1,
+                 decide_fp32: bool = True, force1=None, force2=None) -> Dict[str, np.ndarray]:
+    """The hierarchical layer's forward pass on the whole batch.
+
+    Returns y [B, d], leaf_idx/leaf_gate [B, k1*k2], imp1/load1/rows1 [a], load2 [a*b],
+    importance/load [a*b] (leaf) and losses [3].
+    """
+    g = _HierGate(inp, k1, k2, train)
+    w1, b1, w2, b2, e_dt, h = _experts(inp)
+    n = g.a * g.b
+    K = k1 * k2
+    f1 = _forced(force1, (g.B, k1))
+    f2 = _forced(force2, (g.B, k1, k2))
+    out = {"y": np.empty((g.B, g.d)), "leaf_idx": np.empty((g.B, K), np.int32),
+           "leaf_gate": np.empty((g.B, K)), "imp1": np.empty(g.a), "load1": np.empty(g.a),
+           "rows1": np.empty(g.a), "load2": np.empty(n), "importance": np.empty(n),
+           "load": np.empty(n), "losses": np.empty(3)}
+    rc = _load().oracle_hier_forward(
+        g.B, g.d, h, g.a, g.b, k1, k2, *g.args(), int(train), float(noise_floor),
+        int(decide_fp32), _ptr(f1), _ptr(f2), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), e_dt,
+        float(w_importance), float(w_load),
+        *[out[key].ctypes.data for key in ("y", "leaf_idx", "leaf_gate", "imp1", "load1",
+                                            "rows1", "load2", "importance", "load", "losses")])
+    _check(rc, "hier_forward")
     return out

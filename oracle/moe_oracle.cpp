@@ -35,9 +35,20 @@
 //  * An optional gate bias is added to the clean logit (so it enters H and the
 //    numerator of eq 9 alike).
 //  * Experts: E_i(x) = ReLU(x.W1_i + b1_i).W2_i + b2_i with optional biases.
+//  * Hierarchical MoE (eq 12 is missing from the page; its prose is followed):
+//    the primary gate picks k1 of a groups; for the r-th picked group i the
+//    secondary gate of group i picks k2 of its b experts, with noise row
+//    eps2[t][r][:]; leaf i*b + j gets gate G1_i * G2_ij, so each token uses
+//    k1*k2 leaves. The pages give no balancing losses for the hierarchy; the
+//    ones here are: leaf Importance = sum over tokens of the leaf gates; leaf
+//    Load = Load1_i * Load2_ij / |X_i| (0 when |X_i| = 0), where Load1 is the
+//    primary gate's Load over the batch, Load2_i the secondary gate's Load
+//    over the rows X_i routed to group i; both reduce to the flat losses
+//    when a = 1 or b = 1. PARITY UNPINNED beyond those reductions.
 //
 // Weight layouts: w_gate/w_noise [n][d] (row i = expert i), w1 [n][h][d]
-// (row j = hidden unit j), w2 [n][d][h] (row c = output unit c).
+// (row j = hidden unit j), w2 [n][d][h] (row c = output unit c). Hierarchical:
+// primary gate [a][d], secondary gates [a][b][d], leaves as experts [a*b].
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -200,6 +211,82 @@ GateArgs make_args(int d, int n, int k, const void* x, int x_dt, const void* wg,
 
 bool bad_args(int64_t B, int d, int n, int k, int train, const void* eps) {
   return B < 0 || d < 1 || n < 1 || k < 1 || k > n || (train && !eps);
+}
+
+// Replaces the row's selection by a given set of k experts (in the given slot
+// order) -- used to evaluate everything downstream of a selection another
+// implementation made on a near-tie row. The order statistics v_k, v_{k+1} of
+// the row's logits do not depend on the selection and are kept.
+bool force_selection(RowGate& r, const int32_t* sel, int k, int n) {
+  std::fill(r.in_top.begin(), r.in_top.end(), 0);
+  for (int j = 0; j < k; ++j) {
+    if (sel[j] < 0 || sel[j] >= n || r.in_top[sel[j]]) return false;
+    r.in_top[sel[j]] = 1;
+  }
+  double top = r.H[sel[0]];
+  for (int j = 1; j < k; ++j) top = std::max(top, r.H[sel[j]]);
+  double z = 0.0;
+  for (int j = 0; j < k; ++j) {
+    r.order[j] = sel[j];
+    r.gate[j] = std::exp(r.H[sel[j]] - top);
+    z += r.gate[j];
+  }
+  for (int j = 0; j < k; ++j) r.gate[j] /= z;
+  return true;
+}
+
+size_t dt_size(int dt) { return dt == kF32 ? 4 : 2; }
+
+// Hierarchical MoE: both gate levels of one token.
+struct HierArgs {
+  GateArgs g1;         // primary gate over the a groups
+  GateArgs g2;         // secondary gate template (weights of group 0, eps rank 0)
+  int a, b, k1, k2;
+  size_t w2_group;     // bytes of one group's [b][d] secondary gate weights
+};
+
+struct HierRow {
+  RowGate r1;
+  std::vector<RowGate> r2;  // [k1], the secondary gate of the r-th picked group
+  HierRow(int a, int b, int k1) : r1(a), r2(k1, RowGate(b)) {}
+};
+
+HierArgs make_hier(int d, int a, int b, int k1, int k2, const void* x, int x_dt,
+                   const void* wg1, const void* wn1, const void* wg2, const void* wn2, int w_dt,
+                   const float* eps1, const float* eps2, int train, double floor,
+                   int decide_fp32) {
+  HierArgs h;
+  h.g1 = make_args(d, a, k1, x, x_dt, wg1, wn1, w_dt, nullptr, eps1, train, floor, decide_fp32);
+  h.g2 = make_args(d, b, k2, x, x_dt, wg2, wn2, w_dt, nullptr, eps2, train, floor, decide_fp32);
+  h.g2.eps_row_stride = (int64_t)k1 * b;  // eps2 is [B][k1][b]
+  h.a = a; h.b = b; h.k1 = k1; h.k2 = k2;
+  h.w2_group = (size_t)b * d * dt_size(w_dt);
+  return h;
+}
+
+// Primary gate of token t, then for each picked group (slot order r) the
+// group's own gate with noise row eps2[t][r]. force1 [k1] / force2 [k1][k2]
+// (either may be null) replace the selections.
+bool hier_gate_row(const HierArgs& h, int64_t t, const int32_t* force1, const int32_t* force2,
+                   HierRow& hr, std::vector<double>& xrow, std::vector<double>& wrow) {
+  gate_row(h.g1, t, hr.r1, xrow, wrow);
+  if (force1 && !force_selection(hr.r1, force1, h.k1, h.a)) return false;
+  for (int r = 0; r < h.k1; ++r) {
+    const int grp = hr.r1.order[r];
+    GateArgs g2 = h.g2;
+    g2.wg = (const char*)h.g2.wg + grp * h.w2_group;
+    g2.wn = (const char*)h.g2.wn + grp * h.w2_group;
+    if (g2.eps) g2.eps = h.g2.eps + (int64_t)r * h.b;
+    gate_row(g2, t, hr.r2[r], xrow, wrow);
+    if (force2 && !force_selection(hr.r2[r], force2 + r * h.k2, h.k2, h.b)) return false;
+  }
+  return true;
+}
+
+bool bad_hier(int64_t B, int d, int a, int b, int k1, int k2, int train, const void* eps1,
+              const void* eps2) {
+  return B < 0 || d < 1 || a < 1 || b < 1 || k1 < 1 || k1 > a || k2 < 1 || k2 > b ||
+         (train && (!eps1 || !eps2));
 }
 
 }  // namespace
@@ -444,6 +531,173 @@ int oracle_forward(int64_t B, int d, int h, int n, int k, const void* x, int x_d
     losses[0] = cv_imp;
     losses[1] = cv_load;
     losses[2] = w_imp * cv_imp + w_load * cv_load;  // eqs 7 and 11
+  }
+  return 0;
+}
+
+// Hierarchical gating ("Hierarchical MoE") for a list of token rows (rows ==
+// null: 0..nrows-1). force1 [nrows][k1] / force2 [nrows][k1][k2] may be null.
+// Outputs per listed row q (any may be null):
+//   sel1/gate1 [k1], thr1 [2], H1 [a]; sel2/gate2 [k1][k2] (expert index within
+//   the group), thr2 [k1][2], H2 [k1][b]; leaf_idx/leaf_gate [k1*k2] in slot
+//   order (r, j): leaf sel1[r]*b + sel2[r][j], gate gate1[r]*gate2[r][j].
+int oracle_hier_gate(int64_t nrows, const int64_t* rows, int d, int a, int b, int k1, int k2,
+                     const void* x, int x_dt, const void* wg1, const void* wn1, const void* wg2,
+                     const void* wn2, int w_dt, const float* eps1, const float* eps2, int train,
+                     double floor, int decide_fp32, const int32_t* force1, const int32_t* force2,
+                     int32_t* sel1, double* gate1, double* thr1, double* H1, int32_t* sel2,
+                     double* gate2, double* thr2, double* H2, int32_t* leaf_idx,
+                     double* leaf_gate) {
+  if (nrows < 0 || bad_hier(nrows, d, a, b, k1, k2, train, eps1, eps2)) return 1;
+  const HierArgs h = make_hier(d, a, b, k1, k2, x, x_dt, wg1, wn1, wg2, wn2, w_dt, eps1, eps2,
+                               train, floor, decide_fp32);
+  const int K = k1 * k2;
+  int bad = 0;
+#pragma omp parallel
+  {
+    HierRow hr(a, b, k1);
+    std::vector<double> xrow(d), wrow(d);
+#pragma omp for schedule(dynamic, 16) reduction(| : bad)
+    for (int64_t q = 0; q < nrows; ++q) {
+      const int64_t t = rows ? rows[q] : q;
+      if (!hier_gate_row(h, t, force1 ? force1 + q * k1 : nullptr,
+                         force2 ? force2 + q * K : nullptr, hr, xrow, wrow)) {
+        bad = 1;
+        continue;
+      }
+      for (int r = 0; r < k1; ++r) {
+        if (sel1) sel1[q * k1 + r] = hr.r1.order[r];
+        if (gate1) gate1[q * k1 + r] = hr.r1.gate[r];
+        const RowGate& g2 = hr.r2[r];
+        for (int j = 0; j < k2; ++j) {
+          const int64_t o = q * K + r * k2 + j;
+          if (sel2) sel2[o] = g2.order[j];
+          if (gate2) gate2[o] = g2.gate[j];
+          if (leaf_idx) leaf_idx[o] = hr.r1.order[r] * b + g2.order[j];
+          if (leaf_gate) leaf_gate[o] = hr.r1.gate[r] * g2.gate[j];
+        }
+        if (thr2) {
+          thr2[(q * k1 + r) * 2] = g2.vk;
+          thr2[(q * k1 + r) * 2 + 1] = g2.vk1;
+        }
+        if (H2) std::copy(g2.H.begin(), g2.H.end(), H2 + (q * k1 + r) * b);
+      }
+      if (thr1) {
+        thr1[q * 2] = hr.r1.vk;
+        thr1[q * 2 + 1] = hr.r1.vk1;
+      }
+      if (H1) std::copy(hr.r1.H.begin(), hr.r1.H.end(), H1 + q * a);
+    }
+  }
+  return bad ? 3 : 0;
+}
+
+// The hierarchical layer's forward pass on a batch of B tokens (eq 12 read
+// from the prose; losses as in the header). force1/force2 as in
+// oracle_hier_gate (null: the oracle's own selections). Outputs (any may be
+// null except y), n = a*b leaves:
+//   y [B][d]; leaf_idx/leaf_gate [B][k1*k2];
+//   imp1/load1 [a] (primary gate's Importance and Load), rows1 [a] = |X_i|;
+//   load2 [a*b] (secondary Load of group i over X_i, at i*b + j);
+//   importance/load [n] (leaf); losses[3] = {CV^2(Imp), CV^2(Load), weighted sum}.
+int oracle_hier_forward(int64_t B, int d, int h, int a, int b, int k1, int k2, const void* x,
+                        int x_dt, const void* wg1, const void* wn1, const void* wg2,
+                        const void* wn2, int w_dt, const float* eps1, const float* eps2,
+                        int train, double floor, int decide_fp32, const int32_t* force1,
+                        const int32_t* force2, const void* w1, const void* b1, const void* w2,
+                        const void* b2, int e_dt, double w_imp, double w_load, double* y,
+                        int32_t* leaf_idx, double* leaf_gate, double* imp1, double* load1,
+                        double* rows1, double* load2, double* importance, double* load,
+                        double* losses) {
+  if (bad_hier(B, d, a, b, k1, k2, train, eps1, eps2) || h < 1 || !y) return 1;
+  const HierArgs ha = make_hier(d, a, b, k1, k2, x, x_dt, wg1, wn1, wg2, wn2, w_dt, eps1, eps2,
+                                train, floor, decide_fp32);
+  const int K = k1 * k2;
+  const int n = a * b;
+  std::vector<int32_t> idx((size_t)B * K);
+  std::vector<double> gate((size_t)B * K), g1((size_t)B * k1);
+  std::vector<int32_t> s1((size_t)B * k1);
+  const int64_t nblk = (B + kRowBlock - 1) / kRowBlock;
+  std::vector<double> l1_part((size_t)nblk * a, 0.0), l2_part((size_t)nblk * n, 0.0);
+  int bad = 0;
+#pragma omp parallel
+  {
+    HierRow hr(a, b, k1);
+    std::vector<double> xrow(d), wrow(d);
+#pragma omp for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+      double* acc1 = l1_part.data() + blk * a;
+      double* acc2 = l2_part.data() + blk * n;
+      for (int64_t t = blk * kRowBlock; t < std::min(B, (blk + 1) * kRowBlock); ++t) {
+        if (!hier_gate_row(ha, t, force1 ? force1 + t * k1 : nullptr,
+                           force2 ? force2 + t * K : nullptr, hr, xrow, wrow)) {
+          bad = 1;
+          continue;
+        }
+        for (int i = 0; i < a; ++i) acc1[i] += prob_in_top_k(ha.g1, hr.r1, i);
+        for (int r = 0; r < k1; ++r) {
+          const int grp = hr.r1.order[r];
+          s1[t * k1 + r] = grp;
+          g1[t * k1 + r] = hr.r1.gate[r];
+          // the secondary gate of group grp sees this token as one of X_grp
+          for (int j = 0; j < b; ++j) acc2[grp * b + j] += prob_in_top_k(ha.g2, hr.r2[r], j);
+          for (int j = 0; j < k2; ++j) {
+            idx[t * K + r * k2 + j] = grp * b + hr.r2[r].order[j];
+            gate[t * K + r * k2 + j] = hr.r1.gate[r] * hr.r2[r].gate[j];
+          }
+        }
+      }
+    }
+  }
+  if (bad) return 3;
+  // eq 12: y_t = sum over the token's leaves, ascending leaf id, of gate * E_leaf(x_t)
+#pragma omp parallel
+  {
+    std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h), eo(d);
+    std::vector<std::pair<int32_t, double>> lv(K);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t t = 0; t < B; ++t) {
+      for (int j = 0; j < K; ++j) lv[j] = {idx[t * K + j], gate[t * K + j]};
+      std::sort(lv.begin(), lv.end());
+      widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+      double* yr = y + t * d;
+      for (int c = 0; c < d; ++c) yr[c] = 0.0;
+      for (int j = 0; j < K; ++j) {
+        expert_apply(d, h, xrow.data(), w1, b1, w2, b2, e_dt, lv[j].first, eo.data(), hid, wrow);
+        for (int c = 0; c < d; ++c) yr[c] += lv[j].second * eo[c];
+      }
+    }
+  }
+  // batch sums in ascending token / block order
+  std::vector<double> i1(a, 0.0), l1(a, 0.0), r1(a, 0.0), l2(n, 0.0), imp(n, 0.0), ld(n, 0.0);
+  for (int64_t t = 0; t < B; ++t) {
+    for (int r = 0; r < k1; ++r) {
+      i1[s1[t * k1 + r]] += g1[t * k1 + r];
+      r1[s1[t * k1 + r]] += 1.0;
+    }
+    for (int j = 0; j < K; ++j) imp[idx[t * K + j]] += gate[t * K + j];
+  }
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    for (int i = 0; i < a; ++i) l1[i] += l1_part[blk * a + i];
+    for (int e = 0; e < n; ++e) l2[e] += l2_part[blk * n + e];
+  }
+  for (int i = 0; i < a; ++i)
+    for (int j = 0; j < b; ++j)
+      ld[i * b + j] = r1[i] > 0.0 ? l1[i] * l2[i * b + j] / r1[i] : 0.0;
+  const double cv_imp = cv_squared(n, imp.data());
+  const double cv_load = cv_squared(n, ld.data());
+  if (leaf_idx) std::copy(idx.begin(), idx.end(), leaf_idx);
+  if (leaf_gate) std::copy(gate.begin(), gate.end(), leaf_gate);
+  if (imp1) std::copy(i1.begin(), i1.end(), imp1);
+  if (load1) std::copy(l1.begin(), l1.end(), load1);
+  if (rows1) std::copy(r1.begin(), r1.end(), rows1);
+  if (load2) std::copy(l2.begin(), l2.end(), load2);
+  if (importance) std::copy(imp.begin(), imp.end(), importance);
+  if (load) std::copy(ld.begin(), ld.end(), load);
+  if (losses) {
+    losses[0] = cv_imp;
+    losses[1] = cv_load;
+    losses[2] = w_imp * cv_imp + w_load * cv_load;
   }
   return 0;
 }
