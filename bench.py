@@ -58,8 +58,7 @@ def time_calls(fn, iters, torch):
 # sources are byte-identical to those the counters were taken on.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ffn_kernel_flat_bf16_n4096_hbm_traffic.txt")
 FFN_SOURCES = ["sparsely_gated_mixture_moe_amd/csrc/ffn.hip",
-               "sparsely_gated_mixture_moe_amd/csrc/device_common.h",
-               "sparsely_gated_mixture_moe_amd/csrc/moe_internal.h"]
+               "sparsely_gated_mixture_moe_amd/csrc/device_common.h"]
 
 
 def profiled_traffic(workload):

@@ -37,6 +37,23 @@ class MoeGateOpts(ctypes.Structure):
                 ("w_importance", ctypes.c_float), ("w_load", ctypes.c_float)]
 
 
+class MoeHierDims(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("d_model", ctypes.c_int32),
+                ("d_hidden", ctypes.c_int32), ("groups", ctypes.c_int32),
+                ("group_experts", ctypes.c_int32), ("k1", ctypes.c_int32), ("k2", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int), ("expert_dtype", ctypes.c_int),
+                ("gate_dtype", ctypes.c_int)]
+
+
+_HIER_OUT_FIELDS = ("topk_idx", "topk_gate", "counts", "group_idx", "group_gate", "group_thresh",
+                    "group_rows", "group_importance", "group_load", "sub_idx", "sub_gate",
+                    "sub_thresh", "sub_load")
+
+
+class MoeHierOutputs(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in _HIER_OUT_FIELDS]
+
+
 _P = ctypes.c_void_p
 _lib = None
 
@@ -63,8 +80,13 @@ def lib():
         L.moe_combine.argtypes = [D, _P, _P, _P, _P, _P]
         L.moe_aux_losses.argtypes = [D, O, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
         L.moe_forward.argtypes = [D, O] + [_P] * 19 + [S, _P]
+        HD = ctypes.POINTER(MoeHierDims)
+        L.moe_hier_workspace_size.argtypes = [HD, O]
+        L.moe_hier_workspace_size.restype = ctypes.c_size_t
+        L.moe_hier_forward.argtypes = ([HD, O] + [_P] * 15 + [ctypes.POINTER(MoeHierOutputs), _P, S,
+                                                              _P])
         for f in ("moe_gate", "moe_route", "moe_expert_ffn", "moe_combine", "moe_aux_losses",
-                  "moe_forward"):
+                  "moe_forward", "moe_hier_forward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -332,6 +354,100 @@ def moe_forward(x, w_gate, w_noise, eps, w1, w2, k: int, *, b1=None, b2=None, ga
                  "counts": torch.empty(n, dtype=torch.int32, device=dev),
                  "perm_token": torch.empty(B * k, dtype=torch.int32, device=dev)}
     y = f(x, eps, **extra, stream=stream)
+    out = {"y": y, "importance": f.importance, "load": f.load, "losses": f.losses}
+    out.update(extra)
+    return out
+
+
+class MoeHierForward:
+    """Holds a hierarchical layer's weights, options and workspace for repeated
+    ``moe_hier_forward`` calls (section "Hierarchical MoE"): primary gate
+    ``w_gate1``/``w_noise1`` [a, d], secondary gates ``w_gate2``/``w_noise2``
+    [a, b, d], leaves ``w1`` [a*b, h, d] and ``w2`` [a*b, d, h]."""
+
+    def __init__(self, x_shape, w_gate1, w_noise1, w_gate2, w_noise2, w1, w2, k1: int, k2: int, *,
+                 b1=None, b2=None, train: bool = True, noise_floor: float = 1e-2,
+                 w_importance: float = 0.1, w_load: float = 0.1):
+        B, d = x_shape
+        a, b, _ = w_gate2.shape
+        n, h, _ = w1.shape
+        if n != a * b:
+            raise MoeError(f"w1 has {n} leaves, expected groups * group_experts = {a * b}")
+        _dev(w_gate1, "w_gate1", shape=(a, d))
+        _dev(w_noise1, "w_noise1", w_gate1.dtype, (a, d))
+        _dev(w_gate2, "w_gate2", w_gate1.dtype, (a, b, d))
+        _dev(w_noise2, "w_noise2", w_gate1.dtype, (a, b, d))
+        _dev(w1, "w1")
+        _dev(w2, "w2", w1.dtype, (n, d, h))
+        _dev(b1, "b1", w1.dtype, (n, h))
+        _dev(b2, "b2", w1.dtype, (n, d))
+        self.w = (w_gate1, w_noise1, w_gate2, w_noise2, w1, b1, w2, b2)
+        self.dims = MoeHierDims(B, d, h, a, b, k1, k2, _dt(w1), _dt(w1), _dt(w_gate1))
+        self.opts = make_opts(train, noise_floor, w_importance, w_load)
+        dev = w1.device
+        nbytes = int(lib().moe_hier_workspace_size(ctypes.byref(self.dims), ctypes.byref(self.opts)))
+        if nbytes == 0:
+            _check(1, "moe_hier_workspace_size")
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.importance = torch.empty(n, dtype=torch.float32, device=dev)
+        self.load = torch.empty(n, dtype=torch.float32, device=dev)
+        self.losses = torch.empty(3, dtype=torch.float32, device=dev)
+
+    def output_shapes(self) -> Dict[str, Tuple[Tuple[int, ...], torch.dtype]]:
+        """Shape and dtype of every optional output."""
+        d = self.dims
+        B, a, b, k1, k2 = d.tokens, d.groups, d.group_experts, d.k1, d.k2
+        i32, f32 = torch.int32, torch.float32
+        return {"topk_idx": ((B, k1 * k2), i32), "topk_gate": ((B, k1 * k2), f32),
+                "counts": ((a * b,), i32), "group_idx": ((B, k1), i32),
+                "group_gate": ((B, k1), f32), "group_thresh": ((B, 2), f32),
+                "group_rows": ((a,), i32), "group_importance": ((a,), f32),
+                "group_load": ((a,), f32), "sub_idx": ((B, k1, k2), i32),
+                "sub_gate": ((B, k1, k2), f32), "sub_thresh": ((B, k1, 2), f32),
+                "sub_load": ((a * b,), f32)}
+
+    def __call__(self, x, eps1, eps2, y=None, *, stream=None, **extra):
+        d = self.dims
+        w_gate1, w_noise1, w_gate2, w_noise2, w1, b1, w2, b2 = self.w
+        _dev(x, "x", w1.dtype, (d.tokens, d.d_model))
+        train = bool(self.opts.train)
+        _dev(eps1 if train else None, "eps1", torch.float32, (d.tokens, d.groups))
+        _dev(eps2 if train else None, "eps2", torch.float32, (d.tokens, d.k1, d.group_experts))
+        if y is None:
+            y = torch.empty((d.tokens, d.d_model), dtype=x.dtype, device=x.device)
+        _dev(y, "y", x.dtype, (d.tokens, d.d_model))
+        shapes = self.output_shapes()
+        outs = MoeHierOutputs()
+        for name, t in extra.items():
+            if name not in shapes:
+                raise MoeError(f"unknown output {name}")
+            shp, dt = shapes[name]
+            _dev(t, name, dt, shp)
+            setattr(outs, name, t.data_ptr() if t is not None else None)
+        st = lib().moe_hier_forward(
+            ctypes.byref(self.dims), ctypes.byref(self.opts), _ptr(x), _ptr(w_gate1),
+            _ptr(w_noise1), _ptr(eps1 if train else None), _ptr(w_gate2), _ptr(w_noise2),
+            _ptr(eps2 if train else None), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(y),
+            _ptr(self.importance), _ptr(self.load), _ptr(self.losses), ctypes.byref(outs),
+            _ptr(self.ws), self.ws.numel(), _stream(stream))
+        _check(st, "moe_hier_forward")
+        return y
+
+
+def moe_hier_forward(x, w_gate1, w_noise1, eps1, w_gate2, w_noise2, eps2, w1, w2, k1: int, k2: int,
+                     *, b1=None, b2=None, train: bool = True, noise_floor: float = 1e-2,
+                     w_importance: float = 0.1, w_load: float = 0.1, return_all: bool = False,
+                     stream=None):
+    """One call of the hierarchical forward pass; returns a dict of device tensors
+    (with ``return_all`` also every optional output of the C call)."""
+    f = MoeHierForward(tuple(x.shape), w_gate1, w_noise1, w_gate2, w_noise2, w1, w2, k1, k2,
+                       b1=b1, b2=b2, train=train, noise_floor=noise_floor,
+                       w_importance=w_importance, w_load=w_load)
+    extra = {}
+    if return_all:
+        extra = {name: torch.empty(shp, dtype=dt, device=x.device)
+                 for name, (shp, dt) in f.output_shapes().items()}
+    y = f(x, eps1, eps2, **extra, stream=stream)
     out = {"y": y, "importance": f.importance, "load": f.load, "losses": f.losses}
     out.update(extra)
     return out

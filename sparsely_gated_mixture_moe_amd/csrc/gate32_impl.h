@@ -35,6 +35,7 @@ namespace gate_detail {
 constexpr int kG32Waves = 8;
 constexpr int kG32Threads = kG32Waves * 64;
 constexpr int kG32Rows = kG32Waves * 32;
+static_assert(kG32Rows == kGate32Rows, "rows per block of the 32x32 gate kernel");
 constexpr int kG32Chunk = 16;
 constexpr int kG32HStride = 20;  // padded row stride (floats) of the transpose tile
 
@@ -45,6 +46,8 @@ struct IntConst {
 
 template <int D, int L, bool PASS2>
 __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
+  RowTile tile;
+  if (!resolve_tile<kG32Rows, bf16, D>(p, tile)) return;
   constexpr int UE = 8;          // bf16 per 16-byte unit
   constexpr int NKB = D / 16;    // 32x32x16 K-blocks
   static_assert(NKB % kG32Waves == 0, "each wave copies whole fragments");
@@ -70,21 +73,19 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const bool clean_lane = l32 < 16;
-  const int64_t B = p.B;
   const int n = p.n;
-  const int64_t blk_row0 = (int64_t)blockIdx.x * kG32Rows;
-  const int64_t row0 = blk_row0 + wave * 32;
+  const int wrow0 = wave * 32;  // first local row of this wave
   const bf16* wg = reinterpret_cast<const bf16*>(p.wg);
   const bf16* wn = reinterpret_cast<const bf16*>(p.wn);
 
   // x rows of this wave as A operands: lane supplies row l32, unit 2 kb + hi.
   U16 xa[NKB];
   {
-    const int64_t r = row0 + l32;
+    const int64_t r = tile_xrow(p, tile, wrow0 + l32);
     const bf16* x = reinterpret_cast<const bf16*>(p.x);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
-      xa[kb] = (r < B) ? ld_unit(x + r * D + (kb * 2 + hi) * UE) : zero_unit();
+      xa[kb] = (r >= 0) ? ld_unit(x + r * D + (kb * 2 + hi) * UE) : zero_unit();
   }
 
   // Rows of this lane's (clean, noise) pairs after the exchange: element i is
@@ -94,13 +95,13 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     rr[i] = (clean_lane ? 0 : 16) + 8 * (i / 4) + 4 * hi + (i % 4);
-    row_ok[i] = row0 + rr[i] < B;
+    row_ok[i] = tile.first + wrow0 + rr[i] < tile.end;
   }
 
   if constexpr (PASS2) {
     for (int t = tid; t < kG32Rows; t += kG32Threads) {
-      const int64_t row = blk_row0 + t;
-      const bool ok = row < B;
+      const int64_t row = tile_iorow(p, tile, t);
+      const bool ok = row >= 0;
 #pragma unroll
       for (int j = 0; j < L - 1; ++j) selbuf[t][j] = (ok && j < p.k) ? p.sel_idx[row * p.k + j] : -1;
       thrbuf[t][0] = ok ? p.sel_thr[row * 2] : 0.f;
@@ -139,16 +140,22 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) Mfma<bf16>::k32(acc, xa[kb], src[kb * 64 + lane]);
   };
-  // Noise draws of chunk c -> ring slot b (pass 1): wave w copies rows
+  // Noise draws of chunk c -> ring slot b (pass 1): wave w copies local rows
   // 32 w + 16 i + (l / 4), experts 4 (l % 4) .. + 3 of the chunk, so the slot
   // holds the block's [256][16] tile row-major. This kernel runs only when n is
   // a multiple of 16, so every 16-byte group is aligned and inside its row;
-  // rows past B read row B - 1 and are masked in the epilogue.
+  // rows past the tile's end read the tile's first row and are masked in the
+  // epilogue.
+  int64_t erow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t r = tile_iorow(p, tile, wrow0 + 16 * i + (lane >> 2));
+    erow[i] = r >= 0 ? r : tile_iorow(p, tile, 0);
+  }
   auto dma_eps = [&](int c, int b) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int64_t row = min(row0 + 16 * i + (lane >> 2), B - 1);
-      const float* src = p.eps + row * n + c * EC + 4 * (lane & 3);
+      const float* src = p.eps + erow[i] * n + c * EC + 4 * (lane & 3);
       copy16_to_lds(src, &ebuf[b][(wave * 32 + 16 * i) * EC]);
     }
     // lanes 0-3 copy the chunk's biases (or, without a bias, any in-bounds
@@ -322,8 +329,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
 #pragma unroll
     for (int j = 0; j < L; ++j) insert_any<L>(lv, li, ov[j], oi[j]);
-    const int64_t row = row0 + l32;
-    if (hi == 0 && row < B) {
+    const int64_t row = tile_iorow(p, tile, wrow0 + l32);
+    if (hi == 0 && row >= 0) {
       const int k = p.k;
       const float top = lv[0];
       float ex[L - 1];

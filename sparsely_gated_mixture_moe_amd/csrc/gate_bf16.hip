@@ -7,7 +7,7 @@ hipError_t gate_dispatch_bf16(const GateLaunch& g, const gate_detail::GateParams
                               hipStream_t s) {
   using namespace gate_detail;
   if (g.train && gate_uses_g32(g)) {
-    const dim3 grid((unsigned)((g.tokens + kG32Rows - 1) / kG32Rows));
+    const dim3 grid = gate_grid(g, kG32Rows);
     const dim3 block(kG32Threads);
     const bool k4 = g.k <= 4;
 #define MOE_G32(DD)                                                                        \

@@ -48,7 +48,64 @@ struct GateParams {
   const int32_t* sel_idx;
   const float* sel_thr;
   float* partial;
+  // Secondary gating of a hierarchical layer ("Hierarchical MoE"); all null
+  // for a flat gate. The rows are those a primary route sent to each group:
+  // workgroup u covers the rows seg_off[g] + first, ... of group g, with
+  // (g, first) = (units[1 + 2u], units[2 + 2u]) and units[0] the number of
+  // units. Routed row r reads x row row_token[r] and owns row row_slot[r] of
+  // eps, of the outputs and of sel_idx / sel_thr; group g's gate weights are
+  // rows g*n .. g*n + n - 1 of wg / wn, its biases entries g*n .. of bias.
+  const int32_t* units;
+  const int32_t* seg_off;
+  const int32_t* row_token;
+  const int32_t* row_slot;
 };
+
+// The rows of one workgroup: flat gating takes batch rows first .. first +
+// ROWS - 1 (those below B); secondary gating takes routed rows first .. of one
+// group (those below the group's segment end).
+struct RowTile {
+  int64_t first, end;
+  bool grouped;
+};
+
+// Resolves this workgroup's rows; for secondary gating also moves the weight
+// and bias pointers to the group's block. Returns false when a secondary
+// gating workgroup has no unit (the grid covers the largest possible count).
+template <int ROWS, typename WT, int D>
+__device__ __forceinline__ bool resolve_tile(GateParams& p, RowTile& t) {
+  if (p.units == nullptr) {
+    t.first = (int64_t)blockIdx.x * ROWS;
+    t.end = p.B;
+    t.grouped = false;
+    return true;
+  }
+  const int u = blockIdx.x;
+  if (u >= p.units[0]) return false;
+  const int g = p.units[1 + 2 * u];
+  t.first = (int64_t)p.seg_off[g] + p.units[2 + 2 * u];
+  t.end = p.seg_off[g + 1];
+  t.grouped = true;
+  const int64_t woff = (int64_t)g * p.n * D;
+  p.wg = reinterpret_cast<const WT*>(p.wg) + woff;
+  p.wn = reinterpret_cast<const WT*>(p.wn) + woff;
+  if (p.bias) p.bias += (int64_t)g * p.n;
+  return true;
+}
+
+// x row of local row i of the tile, or -1 past its end.
+__device__ __forceinline__ int64_t tile_xrow(const GateParams& p, const RowTile& t, int i) {
+  const int64_t r = t.first + i;
+  if (r >= t.end) return -1;
+  return t.grouped ? (int64_t)p.row_token[r] : r;
+}
+
+// Row of eps, of the outputs and of the selections owned by local row i, or -1.
+__device__ __forceinline__ int64_t tile_iorow(const GateParams& p, const RowTile& t, int i) {
+  const int64_t r = t.first + i;
+  if (r >= t.end) return -1;
+  return t.grouped ? (int64_t)p.row_slot[r] : r;
+}
 
 template <typename CT>
 struct GateShape;
@@ -112,6 +169,8 @@ __device__ __forceinline__ void insert_any(float (&lv)[L], int (&li)[L], float v
 
 template <typename XS, typename CT, int D, int L, bool TRAIN, bool PASS2>
 __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
+  RowTile tile;
+  if (!resolve_tile<kGateRows, CT, D>(p, tile)) return;
   constexpr int UE = Elem<CT>::kPerUnit;
   constexpr int KB = 4 * UE;  // K-block of the 16x16 tiles
   static_assert(D % KB == 0, "d must be a multiple of the K-block");
@@ -132,23 +191,29 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   const int wave = tid >> 6;
   const int lr = lane & 15;  // A-operand row / C column within a 16x16 tile
   const int q = lane >> 4;   // K unit of the A/B operands; C row group
-  const int64_t B = p.B;
   const int n = p.n;
-  const int64_t row0 = (int64_t)blockIdx.x * kGateRows + wave * 16;
+  const int wrow0 = wave * 16;  // first local row of this wave
 
   // x rows of this wave as A operands for every K-block.
   U16 xa[NKB];
   {
-    const int64_t r = row0 + lr;
+    const int64_t r = tile_xrow(p, tile, wrow0 + lr);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
-      xa[kb] = (r < B) ? load_x_unit<XS, CT>(p.x, r * D + kb * KB + q * UE) : zero_unit();
+      xa[kb] = (r >= 0) ? load_x_unit<XS, CT>(p.x, r * D + kb * KB + q * UE) : zero_unit();
   }
 
-  // Per-lane state for the C rows row0 + 4q + r, r < 4.
+  // Per-lane state for the C rows wrow0 + 4q + r, r < 4: validity and the row
+  // of eps / outputs they own (invalid rows read the tile's first row's noise,
+  // which is masked).
   bool row_ok[4];
+  int64_t iorow[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) row_ok[r] = row0 + 4 * q + r < B;
+  for (int r = 0; r < 4; ++r) {
+    iorow[r] = tile_iorow(p, tile, wrow0 + 4 * q + r);
+    row_ok[r] = iorow[r] >= 0;
+  }
+  const int64_t iorow_any = tile_iorow(p, tile, 0);
   float lv[4][L];
   int li[4][L];
   float shared_thr[4];  // max over the row's 16 lanes of their L-th best: a lower
@@ -168,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t row = row0 + 4 * q + r;
+      const int64_t row = iorow[r];
 #pragma unroll
       for (int j = 0; j < L - 1; ++j)
         sel[r][j] = (row_ok[r] && j < p.k) ? p.sel_idx[row * p.k + j] : -1;
@@ -233,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
       if constexpr (TRAIN && !PASS2) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int64_t row = min(row0 + 4 * q + r, B - 1);
+          const int64_t row = row_ok[r] ? iorow[r] : iorow_any;
           ev[nt][r] = p.eps[row * n + e];
         }
       }
@@ -393,8 +458,8 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
       const int k = p.k;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t row = row0 + 4 * q + r;
-        if (row < B) {
+        const int64_t row = iorow[r];
+        if (row_ok[r]) {
           // softmax over the k kept logits (the rest are -inf, gate 0)
           const float top = lv[r][0];
           float ex[L - 1];
@@ -426,9 +491,15 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   }
 }
 
+// Workgroups of a launch: one per tile of `rows` batch rows, or for secondary
+// gating one per possible work unit (those past the unit count exit at once).
+inline dim3 gate_grid(const GateLaunch& g, int rows) {
+  return dim3((unsigned)(g.units ? g.max_units : (g.tokens + rows - 1) / rows));
+}
+
 template <typename XS, typename CT, int D, int L>
 hipError_t gate_dispatch_train(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
-  const dim3 grid((unsigned)gate_blocks(g.tokens));
+  const dim3 grid = gate_grid(g, kGateRows);
   if (pass2) {
     hipLaunchKernelGGL((gate_kernel<XS, CT, D, L, true, true>), grid, dim3(kThreads), 0, s, p);
   } else if (g.train) {

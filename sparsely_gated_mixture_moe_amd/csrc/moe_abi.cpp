@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -191,6 +192,109 @@ moe_status check_gate_args(const moe_dims* d, const moe_gate_opts* o, const void
   if (!moe::gate_supported(d->d_model, to_dt(d->act_dtype), to_dt(d->gate_dtype), d->k))
     return fail(MOE_ERR_UNSUPPORTED, "gate: unsupported shape or dtype combination");
   return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Hierarchical layer
+// ---------------------------------------------------------------------------
+
+moe_status check_hier_dims(const moe_hier_dims* h) {
+  if (!h) return fail(MOE_ERR_INVALID, "dims is NULL");
+  if (h->groups < 1 || h->group_experts < 1)
+    return fail(MOE_ERR_INVALID, "groups = %d and group_experts = %d must be positive",
+                h->groups, h->group_experts);
+  if ((int64_t)h->groups * h->group_experts > 32768)
+    return fail(MOE_ERR_INVALID, "groups * group_experts = %lld > 32768",
+                (long long)h->groups * h->group_experts);
+  if (h->k1 < 1 || h->k1 > h->groups)
+    return fail(MOE_ERR_INVALID, "k1 = %d outside [1, groups = %d]", h->k1, h->groups);
+  if (h->k2 < 1 || h->k2 > h->group_experts)
+    return fail(MOE_ERR_INVALID, "k2 = %d outside [1, group_experts = %d]", h->k2,
+                h->group_experts);
+  if (h->k1 * h->k2 > 8) return fail(MOE_ERR_UNSUPPORTED, "k1 * k2 = %d > 8", h->k1 * h->k2);
+  // the leaf layer: the same limits as a flat layer with k = k1 * k2
+  moe_dims leaf{h->tokens, h->d_model, h->d_hidden, h->groups * h->group_experts,
+                h->k1 * h->k2, h->act_dtype, h->expert_dtype, h->gate_dtype};
+  return check_dims(&leaf);
+}
+
+struct HierLayout {
+  size_t sel1, gate1, thr1, counts1, offsets1, perm_token1, perm_gate1, slot_pos1, perm_slot1,
+      imp1, blockcnt1, units, unit_start, sel2, gate2, thr2, topk_idx, topk_gate, counts, offsets,
+      perm_token, perm_gate, slot_pos, blockcnt, ffn_blocks, expert_out, load1, partial1, load2,
+      partial2, total;
+  int64_t max_units;
+};
+
+moe::GateLaunch hier_gate_launch(const moe_hier_dims* h, const moe_gate_opts* o, int level,
+                                 const void* x, const void* wg, const void* wn, const float* eps) {
+  moe::GateLaunch g;
+  g.x = x;
+  g.w_gate = wg;
+  g.w_noise = wn;
+  g.bias = nullptr;
+  g.eps = o->train ? eps : nullptr;
+  g.tokens = level == 1 ? h->tokens : h->tokens * h->k1;
+  g.d = h->d_model;
+  g.n = level == 1 ? h->groups : h->group_experts;
+  g.k = level == 1 ? h->k1 : h->k2;
+  g.x_dt = to_dt(h->act_dtype);
+  g.w_dt = to_dt(h->gate_dtype);
+  g.train = o->train;
+  g.noise_floor = o->noise_floor;
+  return g;
+}
+
+HierLayout hier_layout(const moe_hier_dims* h, const moe_gate_opts* o) {
+  const int64_t B = h->tokens, a = h->groups, b = h->group_experts, k1 = h->k1;
+  const int64_t n = a * b, K = k1 * h->k2;
+  const int64_t rows2 = B * k1, pairs = B * K;
+  const bool train = o && o->train;
+  moe_gate_opts tmp{train ? 1 : 0, 0.01f, 0.f, 0.f};
+  const int tile = moe::gate_tile_rows(hier_gate_launch(h, &tmp, 2, nullptr, nullptr, nullptr,
+                                                        nullptr));
+  HierLayout L{};
+  L.max_units = moe::gate_max_units(rows2, (int)a, tile);
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t off = at;
+    at += align_up(bytes);
+    return off;
+  };
+  L.sel1 = take(rows2 * sizeof(int32_t));
+  L.gate1 = take(rows2 * sizeof(float));
+  L.thr1 = take(B * 2 * sizeof(float));
+  L.counts1 = take(a * sizeof(int32_t));
+  L.offsets1 = take((a + 1) * sizeof(int32_t));
+  L.perm_token1 = take(rows2 * sizeof(int32_t));
+  L.perm_gate1 = take(rows2 * sizeof(float));
+  L.slot_pos1 = take(rows2 * sizeof(int32_t));
+  L.perm_slot1 = take(rows2 * sizeof(int32_t));
+  L.imp1 = take(a * sizeof(float));
+  L.blockcnt1 = take((size_t)a * moe::route_blocks(B) * sizeof(int32_t));
+  L.units = take((size_t)(1 + 2 * L.max_units) * sizeof(int32_t));
+  L.unit_start = take((a + 1) * sizeof(int32_t));
+  L.sel2 = take(pairs * sizeof(int32_t));
+  L.gate2 = take(pairs * sizeof(float));
+  L.thr2 = take(rows2 * 2 * sizeof(float));
+  L.topk_idx = take(pairs * sizeof(int32_t));
+  L.topk_gate = take(pairs * sizeof(float));
+  L.counts = take(n * sizeof(int32_t));
+  L.offsets = take((n + 1) * sizeof(int32_t));
+  L.perm_token = take(pairs * sizeof(int32_t));
+  L.perm_gate = take(pairs * sizeof(float));
+  L.slot_pos = take(pairs * sizeof(int32_t));
+  L.blockcnt = take((size_t)n * moe::route_blocks(B) * sizeof(int32_t));
+  L.ffn_blocks = take((size_t)(1 + 2 * moe::ffn_max_blocks(pairs, (int)n, h->d_model,
+                                                            to_dt(h->act_dtype))) *
+                      sizeof(int32_t));
+  L.expert_out = take((size_t)pairs * h->d_model * dt_size(h->act_dtype));
+  L.load1 = take(a * sizeof(float));
+  L.partial1 = take(train ? (size_t)moe::gate_blocks(B) * a * sizeof(float) : 0);
+  L.load2 = take(n * sizeof(float));
+  L.partial2 = take(train ? (size_t)L.max_units * b * sizeof(float) : 0);
+  L.total = at;
+  return L;
 }
 
 }  // namespace
@@ -390,6 +494,145 @@ moe_status moe_forward(const moe_dims* dims, const moe_gate_opts* opts, const vo
   e = moe::launch_cv2_losses(importance, load, dims->n_experts, opts->w_importance, opts->w_load,
                              losses, st);
   return device_status(e, "moe_forward (losses)");
+}
+
+size_t moe_hier_workspace_size(const moe_hier_dims* dims, const moe_gate_opts* opts) {
+  if (check_hier_dims(dims) != MOE_OK) return 0;
+  if (opts && check_opts(opts) != MOE_OK) return 0;
+  return hier_layout(dims, opts).total;
+}
+
+moe_status moe_hier_forward(const moe_hier_dims* dims, const moe_gate_opts* opts, const void* x,
+                            const void* w_gate1, const void* w_noise1, const float* eps1,
+                            const void* w_gate2, const void* w_noise2, const float* eps2,
+                            const void* w1, const void* b1, const void* w2, const void* b2,
+                            void* y, float* importance, float* load, float* losses,
+                            const moe_hier_outputs* extra, void* ws, size_t ws_bytes,
+                            void* stream) {
+  moe_status s;
+  if ((s = check_hier_dims(dims)) != MOE_OK || (s = check_opts(opts)) != MOE_OK) return s;
+  const int64_t B = dims->tokens;
+  REQN(x, 16, B);
+  REQ(w_gate1, 16);
+  REQ(w_gate2, 16);
+  if (opts->train) {
+    REQ(w_noise1, 16);
+    REQ(w_noise2, 16);
+    REQN(eps1, 4, B);
+    REQN(eps2, 4, B);
+  } else {
+    OPT(w_noise1, 16);
+    OPT(w_noise2, 16);
+  }
+  REQ(w1, 16);
+  REQ(w2, 16);
+  OPT(b1, 4);
+  OPT(b2, 4);
+  REQN(y, 16, B);
+  REQ(importance, 4);
+  REQ(load, 4);
+  REQ(losses, 4);
+  moe_hier_outputs none{};
+  const moe_hier_outputs* ex = extra ? extra : &none;
+  OPT(ex->topk_idx, 4);
+  OPT(ex->topk_gate, 4);
+  OPT(ex->counts, 4);
+  OPT(ex->group_idx, 4);
+  OPT(ex->group_gate, 4);
+  OPT(ex->group_thresh, 4);
+  OPT(ex->group_rows, 4);
+  OPT(ex->group_importance, 4);
+  OPT(ex->group_load, 4);
+  OPT(ex->sub_idx, 4);
+  OPT(ex->sub_gate, 4);
+  OPT(ex->sub_thresh, 4);
+  OPT(ex->sub_load, 4);
+  const moe::Dt x_dt = to_dt(dims->act_dtype), w_dt = to_dt(dims->gate_dtype);
+  if (!moe::gate_supported(dims->d_model, x_dt, w_dt, dims->k1) ||
+      !moe::gate_supported(dims->d_model, x_dt, w_dt, dims->k2))
+    return fail(MOE_ERR_UNSUPPORTED, "gate: unsupported shape or dtype combination");
+  if (!moe::ffn_supported(dims->d_model, dims->d_hidden, x_dt))
+    return fail(MOE_ERR_UNSUPPORTED, "expert_ffn: unsupported shape");
+  const HierLayout L = hier_layout(dims, opts);
+  if ((s = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return s;
+
+  const hipStream_t st = (hipStream_t)stream;
+  const int a = dims->groups, b = dims->group_experts, k1 = dims->k1, k2 = dims->k2;
+  const int n = a * b, K = k1 * k2;
+  auto pick = [&](auto* given, size_t off) {
+    using T = std::remove_pointer_t<decltype(given)>;
+    return given ? given : at<T>(ws, off);
+  };
+  int32_t* sel1 = pick(ex->group_idx, L.sel1);
+  float* gate1 = pick(ex->group_gate, L.gate1);
+  float* thr1 = pick(ex->group_thresh, L.thr1);
+  int32_t* counts1 = pick(ex->group_rows, L.counts1);
+  float* imp1 = pick(ex->group_importance, L.imp1);
+  float* load1 = pick(ex->group_load, L.load1);
+  int32_t* sel2 = pick(ex->sub_idx, L.sel2);
+  float* gate2 = pick(ex->sub_gate, L.gate2);
+  float* thr2 = pick(ex->sub_thresh, L.thr2);
+  float* load2 = pick(ex->sub_load, L.load2);
+  int32_t* topk_idx = pick(ex->topk_idx, L.topk_idx);
+  float* topk_gate = pick(ex->topk_gate, L.topk_gate);
+  int32_t* counts = pick(ex->counts, L.counts);
+  int32_t* offsets1 = at<int32_t>(ws, L.offsets1);
+  int32_t* perm_token1 = at<int32_t>(ws, L.perm_token1);
+  int32_t* perm_slot1 = at<int32_t>(ws, L.perm_slot1);
+  int32_t* unit_start = at<int32_t>(ws, L.unit_start);
+  int32_t* units = at<int32_t>(ws, L.units);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm_token = at<int32_t>(ws, L.perm_token);
+  int32_t* slot_pos = at<int32_t>(ws, L.slot_pos);
+  void* expert_out = at<char>(ws, L.expert_out);
+
+  // primary gate and the routing of each token's k1 slots to their groups
+  const moe::GateLaunch g1 = hier_gate_launch(dims, opts, 1, x, w_gate1, w_noise1, eps1);
+  hipError_t e = moe::launch_gate(g1, sel1, gate1, thr1, st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (primary gate)");
+  e = moe::launch_route(B, k1, a, sel1, gate1, at<int32_t>(ws, L.blockcnt1), counts1, offsets1,
+                        perm_token1, at<float>(ws, L.perm_gate1), at<int32_t>(ws, L.slot_pos1),
+                        imp1, st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (primary route)");
+  e = moe::launch_invert_slots(at<int32_t>(ws, L.slot_pos1), B * k1, perm_slot1, st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (slots)");
+  // secondary gates over each group's routed rows
+  moe::GateLaunch g2 = hier_gate_launch(dims, opts, 2, x, w_gate2, w_noise2, eps2);
+  g2.units = units;
+  g2.seg_off = offsets1;
+  g2.row_token = perm_token1;
+  g2.row_slot = perm_slot1;
+  g2.max_units = L.max_units;
+  e = moe::launch_group_plan(offsets1, a, moe::gate_tile_rows(g2), units, unit_start, st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (plan)");
+  e = moe::launch_gate(g2, sel2, gate2, thr2, st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (secondary gate)");
+  // leaves, then the flat path over them
+  e = moe::launch_hier_leaves(B, k1, k2, b, sel1, gate1, sel2, gate2, topk_idx, topk_gate, st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (leaves)");
+  e = moe::launch_route(B, K, n, topk_idx, topk_gate, at<int32_t>(ws, L.blockcnt), counts, offsets,
+                        perm_token, at<float>(ws, L.perm_gate), slot_pos, importance, st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (route)");
+  e = moe::launch_ffn(B, K, dims->d_model, dims->d_hidden, n, x_dt, x, offsets, perm_token, w1, b1,
+                      w2, b2, expert_out, at<int32_t>(ws, L.ffn_blocks), st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (expert_ffn)");
+  e = moe::launch_combine(B, K, dims->d_model, x_dt, expert_out, slot_pos, topk_gate, y, st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (combine)");
+  // both levels' Load, then the leaf Load and the losses
+  if (opts->train) {
+    e = moe::launch_load(g1, sel1, thr1, at<float>(ws, L.partial1), load1, st);
+    if (e == hipSuccess)
+      e = moe::launch_load_grouped(g2, a, unit_start, sel2, thr2, at<float>(ws, L.partial2),
+                                   load2, st);
+  } else {
+    e = moe::launch_counts_to_load(counts1, a, load1, st);
+    if (e == hipSuccess) e = moe::launch_counts_to_load(counts, n, load2, st);
+  }
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (load)");
+  e = moe::launch_hier_leaf_load(a, b, load1, load2, counts1, load, st);
+  if (e != hipSuccess) return device_status(e, "moe_hier_forward (leaf load)");
+  e = moe::launch_cv2_losses(importance, load, n, opts->w_importance, opts->w_load, losses, st);
+  return device_status(e, "moe_hier_forward (losses)");
 }
 
 }  // extern "C"

@@ -11,8 +11,10 @@ namespace moe {
 
 enum Dt { kF32 = 0, kBF16 = 1 };
 
-// Gate kernel geometry: 8 waves of 16 token rows each.
+// Gate kernel geometry: 8 waves of 16 token rows each; the 32x32-tile kernel
+// for bf16 gates runs 8 waves of 32 rows.
 constexpr int kGateRows = 128;
+constexpr int kGate32Rows = 256;
 // Routing: tokens per block of the counting sort.
 constexpr int kRouteTokens = 1024;
 
@@ -27,6 +29,15 @@ struct GateLaunch {
   Dt x_dt, w_dt;
   int train;
   float noise_floor;
+  // Secondary gating of a hierarchical layer (all null for a flat gate): the
+  // rows are the routed rows of a primary route, tiled per group by
+  // launch_group_plan; `tokens` is then the number of routed rows, `n` the
+  // experts per group, and w_gate / w_noise / bias hold every group's block.
+  const int32_t* units = nullptr;      // [1 + 2 * max_units]
+  const int32_t* seg_off = nullptr;    // [groups + 1] primary route offsets
+  const int32_t* row_token = nullptr;  // [tokens] x row of each routed row
+  const int32_t* row_slot = nullptr;   // [tokens] eps / output row of each routed row
+  int64_t max_units = 0;
 };
 
 // Noisy top-k gating: writes topk_idx [B,k], topk_gate [B,k], thresh [B,2].
@@ -40,6 +51,19 @@ int gate_blocks(int64_t tokens);
 hipError_t launch_load(const GateLaunch& g, const int32_t* topk_idx, const float* thresh,
                        float* partial, float* load, hipStream_t s);
 bool gate_supported(int d, Dt x_dt, Dt w_dt, int k);
+
+// Secondary (grouped) gating. Rows per work unit of the kernel that `g` runs
+// on; the largest unit count for `rows` routed rows over `groups` groups;
+// the unit list (units [1 + 2 * max_units], unit_start [groups + 1]) from the
+// primary route's offsets; the Load pass, whose per-unit partial sums
+// ([max_units][n]) are reduced per group into load [groups * n].
+int gate_tile_rows(const GateLaunch& g);
+int64_t gate_max_units(int64_t rows, int groups, int tile_rows);
+hipError_t launch_group_plan(const int32_t* offsets, int groups, int tile_rows, int32_t* units,
+                             int32_t* unit_start, hipStream_t s);
+hipError_t launch_load_grouped(const GateLaunch& g, int groups, const int32_t* unit_start,
+                               const int32_t* topk_idx, const float* thresh, float* partial,
+                               float* load, hipStream_t s);
 
 // Routing.
 int route_blocks(int64_t tokens);
@@ -61,6 +85,17 @@ hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const v
 hipError_t launch_combine(int64_t tokens, int k, int d, Dt dt, const void* expert_out,
                           const int32_t* slot_pos, const float* topk_gate, void* y,
                           hipStream_t s);
+
+// Hierarchical layer: inverse of a route's slot_pos (perm_slot[slot_pos[q]] = q);
+// leaves of each token from both levels (leaf r*k2 + j = sel1[r]*b + sel2[r][j],
+// gate gate1[r]*gate2[r][j]); leaf Load = load1[i] * load2[i*b + j] / rows1[i].
+hipError_t launch_invert_slots(const int32_t* slot_pos, int64_t npairs, int32_t* perm_slot,
+                               hipStream_t s);
+hipError_t launch_hier_leaves(int64_t tokens, int k1, int k2, int b, const int32_t* sel1,
+                              const float* gate1, const int32_t* sel2, const float* gate2,
+                              int32_t* leaf_idx, float* leaf_gate, hipStream_t s);
+hipError_t launch_hier_leaf_load(int a, int b, const float* load1, const float* load2,
+                                 const int32_t* rows1, float* load, hipStream_t s);
 
 // Load as the hard count (train = 0) and the CV^2 losses.
 hipError_t launch_counts_to_load(const int32_t* counts, int n, float* load, hipStream_t s);

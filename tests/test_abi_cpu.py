@@ -129,3 +129,51 @@ def test_status_strings():
     assert L.moe_status_string(0) == b"MOE_OK"
     assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+def hdims(**kw):
+    base = dict(tokens=1024, d_model=512, d_hidden=1024, groups=16, group_experts=32, k1=2, k2=2,
+                act_dtype=1, expert_dtype=1, gate_dtype=1)
+    base.update(kw)
+    return B.MoeHierDims(*[base[f] for f, _ in B.MoeHierDims._fields_])
+
+
+def call_hier(d, o, ws=FAKE, ws_bytes=1 << 40, eps2=FAKE, extra=None):
+    L = B.lib()
+    return L.moe_hier_forward(ctypes.byref(d), ctypes.byref(o), P(), P(), P(), P(), P(), P(),
+                              P(eps2), P(), None, P(), None, P(), P(), P(), P(),
+                              ctypes.byref(extra) if extra is not None else None, P(ws), ws_bytes,
+                              None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    ({"groups": 0}, INVALID, "groups"),
+    ({"k1": 0}, INVALID, "k1"),
+    ({"k1": 17}, INVALID, "k1"),
+    ({"k2": 33}, INVALID, "k2"),
+    ({"k1": 3, "k2": 3}, UNSUPPORTED, "k1 * k2"),
+    ({"groups": 256, "group_experts": 256}, INVALID, "32768"),
+    ({"d_model": 96}, UNSUPPORTED, "d_model"),
+    ({"tokens": -5}, INVALID, "tokens"),
+])
+def test_hier_invalid_dims(kw, status, msg):
+    assert call_hier(hdims(**kw), opts()) == status
+    assert msg in last_error()
+    assert B.lib().moe_hier_workspace_size(ctypes.byref(hdims(**kw)), ctypes.byref(opts())) == 0
+
+
+def test_hier_pointer_and_workspace_checks():
+    L = B.lib()
+    d, o = hdims(), opts()
+    need = L.moe_hier_workspace_size(ctypes.byref(d), ctypes.byref(o))
+    # the leaf layer's expert outputs alone take B * k1 * k2 bf16 rows
+    assert need >= 1024 * 4 * 512 * 2
+    assert call_hier(d, o, eps2=0) == INVALID and "eps2" in last_error()
+    assert call_hier(d, opts(train=0), eps2=0, ws_bytes=0) == WORKSPACE
+    assert call_hier(d, o, ws_bytes=need - 256) == WORKSPACE and "needed" in last_error()
+    assert call_hier(d, o, ws=FAKE + 16, ws_bytes=need) == INVALID
+    bad = B.MoeHierOutputs()
+    bad.sub_load = FAKE + 2
+    assert call_hier(d, o, extra=bad) == INVALID and "sub_load" in last_error()
+    infer = L.moe_hier_workspace_size(ctypes.byref(d), ctypes.byref(opts(train=0)))
+    assert 0 < infer < need
