@@ -111,6 +111,116 @@ def cpu_baseline(w, inp, target_s):
                       f"expert FFNs, weighted sum, Importance/Load and losses; {t:.1f} s"}
 
 
+def upload(w, name, shape, torch, dg, chunk=1 << 27):
+    """Tensor `name` of workload `w` generated in chunks straight into device memory."""
+    import numpy as np
+
+    probe = dg.gen(w, name, 0, 1)
+    bf16 = probe.dtype == np.uint16
+    total = int(np.prod(shape))
+    t = torch.empty(total, dtype=torch.bfloat16 if bf16 else torch.float32, device="cuda")
+    for i, off in enumerate(range(0, total, chunk)):
+        cnt = min(chunk, total - off)
+        if i % 16 == 15:
+            log(f"  {name}: {off / total:.0%}")
+        a = dg.gen(w, name, off, cnt)
+        src = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+        t[off:off + cnt].copy_(src)
+    return t.view(*shape)
+
+
+def bench_hier(a, w):
+    """The hierarchical layer ("Hierarchical MoE"): one step = one moe_hier_forward
+    call (both gate levels, leaf routing, expert FFNs, weighted sum, both levels'
+    Load and the losses, training mode)."""
+    import numpy as np
+    import torch
+
+    import datagen as dg
+    import sparsely_gated_mixture_moe_amd as moe
+
+    B, d, h = w.tokens, w.d_model, w.d_hidden
+    ga, gb, k1, k2 = w.groups, w.group_experts, w.k1, w.k2
+    n, K = ga * gb, k1 * k2
+    log(f"generating {w.name} on the device: {w.description}")
+    t0 = time.time()
+    g = {"x": upload(w, "x", (B, d), torch, dg), "w_gate": upload(w, "w_gate", (ga, d), torch, dg),
+         "w_noise": upload(w, "w_noise", (ga, d), torch, dg),
+         "eps": upload(w, "eps", (B, ga), torch, dg),
+         "w_gate2": upload(w, "w_gate2", (ga, gb, d), torch, dg),
+         "w_noise2": upload(w, "w_noise2", (ga, gb, d), torch, dg),
+         "eps2": upload(w, "eps2", (B, k1, gb), torch, dg),
+         "w1": upload(w, "w1", (n, h, d), torch, dg), "w2": upload(w, "w2", (n, d, h), torch, dg)}
+    torch.cuda.synchronize()
+    log(f"inputs resident after {time.time() - t0:.1f} s")
+    f = moe.MoeHierForward((B, d), g["w_gate"], g["w_noise"], g["w_gate2"], g["w_noise2"],
+                           g["w1"], g["w2"], k1, k2, train=True)
+    dev = g["x"].device
+    y = torch.empty((B, d), dtype=g["x"].dtype, device=dev)
+    leaf_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    leaf_gate = torch.empty((B, K), dtype=torch.float32, device=dev)
+
+    def step():
+        f(g["x"], g["eps"], g["eps2"], y, topk_idx=leaf_idx, topk_gate=leaf_gate)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(a.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / a.steps
+    log(f"{ms_step:.3f} ms/step")
+    # the leaf FFN on its own, on the step's routing
+    dims = moe.make_dims(B, d, h, n, K, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_BF16)
+    ws = moe.workspace(dims, moe.make_opts(), dev)
+    route = moe.moe_route(leaf_idx, leaf_gate, n, d_model=d, ws=ws)
+    eo = torch.empty((B * K, d), dtype=g["x"].dtype, device=dev)
+    it = a.stage_iters
+    stages = {
+        "route_leaves": time_calls(lambda: moe.moe_route(leaf_idx, leaf_gate, n, d_model=d, ws=ws),
+                                   it, torch),
+        "expert_ffn": time_calls(lambda: moe.moe_expert_ffn(
+            g["x"], route["offsets"], route["perm_token"], g["w1"], g["w2"], K, ws=ws, out=eo),
+            it, torch),
+    }
+    log("stages (ms): " + ", ".join(f"{k_}={v:.3f}" for k_, v in stages.items()))
+    cnt = route["counts"].cpu().numpy()
+    used, rows = int((cnt > 0).sum()), int(cnt.sum())
+    ffn_bytes = used * 2 * d * h * 2 + 2 * rows * d * 2
+    ffn_ms = stages["expert_ffn"]
+    achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+    gate_flops = 2.0 * B * d * 2 * ga + 2.0 * B * k1 * d * 2 * gb
+    step_flops = 2 * gate_flops + 4.0 * rows * d * h  # both gates twice (selection, Load) + FFN
+    step_bytes = (B * d * 2 + B * ga * 4 + B * k1 * gb * 4 + 2 * ga * d * 2 + 2 * n * d * 2
+                  + used * 2 * d * h * 2 + B * d * 2)
+    result = {
+        "metric": "hierarchical MoE-layer forward tokens/sec (128 x 128 = 16384 leaves, k1 = k2 = 2)",
+        "value": B / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "groups": ga,
+                   "group_experts": gb, "k1": k1, "k2": k2, "train": 1},
+        "roofline": {"kernel": "ffn_kernel (moe_expert_ffn over the leaves)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": ffn_bytes, "avg_launch_ms": ffn_ms,
+                     "mfma_frac": 4.0 * rows * d * h / (ffn_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
+        "step": {"alg_bytes": step_bytes, "alg_flops": step_flops,
+                 "hbm_frac": step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                 "mfma_frac": step_flops / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
+        "stages_ms": stages, "wall_ms_per_step": 1000 * wall / a.steps,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,7 +257,8 @@ def main():
 
     w = dg.WORKLOADS[a.workload]
     if w.hierarchical:
-        raise SystemExit("the hierarchical workload is not part of this benchmark")
+        bench_hier(a, w)
+        return
     B, d, h, n, k = w.tokens, w.d_model, w.d_hidden, w.n_experts, w.k
     log(f"generating {w.name}: {w.description}")
     t0 = time.time()

@@ -291,6 +291,38 @@ def test_forward_parity(case, train):
     print(w.name, kw, train, res)
 
 
+def test_forward_full_size_sampled():
+    """The benchmark's workload in the benchmark's launch configuration
+    (MoeForward, training mode, default options): 65536 tokens, 4096 experts
+    512-1024-512, k 4, bf16. Gating and y are checked on sampled rows (both
+    ends, tile edges and random rows), routing and Importance on the whole
+    batch through properties, and Load and the losses against the oracle's
+    full-batch Load."""
+    w = wl("flat_bf16_n4096")
+    B, d, n, k = w.tokens, w.d_model, w.n_experts, w.k
+    announce(f"moe_forward full size {w.name}: generating inputs")
+    inp = dg.make_inputs(w)
+    g = gpu_inputs(inp)
+    f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,
+                       gate_bias=g.get("gate_bias"), train=True)
+    dev = g["x"].device
+    out = {"topk_idx": torch.empty((B, k), dtype=torch.int32, device=dev),
+           "topk_gate": torch.empty((B, k), dtype=torch.float32, device=dev),
+           "thresh": torch.empty((B, 2), dtype=torch.float32, device=dev),
+           "counts": torch.empty(n, dtype=torch.int32, device=dev),
+           "perm_token": torch.empty(B * k, dtype=torch.int32, device=dev)}
+    announce("moe_forward full size: GPU call")
+    y = f(g["x"], g["eps"], **out)
+    torch.cuda.synchronize()
+    out.update(y=y, importance=f.importance, load=f.load, losses=f.losses)
+    rng = np.random.default_rng(7)
+    edges = [0, 1, 127, 128, 255, 256, 257, B // 2, B - 257, B - 256, B - 2, B - 1]
+    rows = np.unique(np.concatenate([edges, rng.choice(B, 400, replace=False)]))
+    announce("moe_forward full size: oracle on sampled rows and full-batch Load")
+    res = check_forward(w, inp, out, True, rows=rows, full_load=True)
+    print(w.name, "full size", len(rows), "rows", res)
+
+
 def test_forward_is_deterministic():
     w = wl("zipf_bf16_n256", tokens=2048)
     announce("moe_forward determinism")
