@@ -106,19 +106,6 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Gather the unit's rows of x.
-  for (int u = tid; u < S::BM * S::XU; u += NT) {
-    const int r = u / S::XU;
-    const int c = u - r * S::XU;
-    U16 v = zero_unit();
-    if (r < rows) {
-      const int64_t tok = p.perm_token[seg + r];
-      v = ld_unit(reinterpret_cast<const T*>(p.x) + tok * D + c * UE);
-    }
-    xs[r * S::XU + (c ^ (r & (S::XSW - 1)))] = v;
-  }
-  __syncthreads();
-
   const T* w1e = reinterpret_cast<const T*>(p.w1) + (int64_t)e * h * D;
   const T* w2e = reinterpret_cast<const T*>(p.w2) + (int64_t)e * D * h;
 
@@ -154,8 +141,23 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   };
   U16 pa[PF1];
   U16 pb[PF2][S::CT2];
+  // The first W1 fragments are requested before the gather, so the weight
+  // stream is already in flight while the rows of x arrive.
 #pragma unroll
   for (int j = 0; j < PF1; ++j) pa[j] = ld_unit(w1_at(0, j));
+
+  // Gather the unit's rows of x.
+  for (int u = tid; u < S::BM * S::XU; u += NT) {
+    const int r = u / S::XU;
+    const int c = u - r * S::XU;
+    U16 v = zero_unit();
+    if (r < rows) {
+      const int64_t tok = p.perm_token[seg + r];
+      v = ld_unit(reinterpret_cast<const T*>(p.x) + tok * D + c * UE);
+    }
+    xs[r * S::XU + (c ^ (r & (S::XSW - 1)))] = v;
+  }
+  __syncthreads();
 
   for (int ch = 0; ch < nch; ++ch) {
     const int hc = ch * S::HC;

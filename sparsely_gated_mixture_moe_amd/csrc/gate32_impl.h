@@ -1,7 +1,7 @@
 // Noisy top-k gating and the Load pass on 32x32x16 bf16 matrix-core tiles,
 // for bf16 x and gate weights with d_model >= 128, n a multiple of 16, in
-// training mode (the configuration of the large workloads). Same mathematics as gate_impl.h
-// (sections "Noisy top-k gating", eqs 3-5, and "A differentiable count of
+// training mode (the configuration of the large workloads). Same mathematics
+// as gate_impl.h (sections "Noisy top-k gating", eqs 3-5, and "A differentiable count of
 // examples", eqs 8-10); different data movement:
 //
 //  * a workgroup owns 256 token rows, 32 per wave; each wave keeps its rows of
@@ -11,20 +11,21 @@
 //    is copied HBM/L2 -> LDS with global_load_lds_dwordx4 (no staging
 //    registers) into a double buffer, each 1 KB fragment in lane order;
 //  * every fragment read from LDS feeds one 32x32x16 MFMA (32 flop per LDS byte);
-//  * the two waves that share a SIMD run each chunk's halves (next chunk's
-//    products, this chunk's epilogue) in opposite order so the matrix cores
-//    and the vector ALUs overlap.
+//  * each pass issues the next chunk's matrix products before this chunk's
+//    epilogue, so the matrix cores and the vector ALUs overlap.
 //
 // Epilogue. In the 32x32 C layout lane l holds column l % 32 for 16 rows: the
 // clean logit (columns 0-15) or the noise pre-activation (16-31) of one expert.
-// Lanes l and l ^ 16 swap half of their rows so each holds (clean, noise) pairs
-// for 8 rows of one expert. Pass 1 forms H = clean + eps * (Softplus(u) +
-// floor), transposes it through LDS and lets each lane own one row's half of
-// the chunk: a lane sees every 8th-block of its row's experts in increasing
-// order, keeps the row's L best (H, expert), and rarely needs to insert once
-// its list is warm. Lanes l and l ^ 32 (the two halves of a row) merge at the
-// end. Pass 2 evaluates P = Phi((clean - thr) / sigma) in place and sums each
-// expert's column over the block's rows in a fixed order.
+// Lanes l and l ^ 16 swap half of their rows (v_permlane16_swap) so each holds
+// (clean, noise) pairs for 8 rows of one expert. Pass 1 forms H = clean + eps *
+// (Softplus(u) + floor), transposes it through LDS (one chunk behind, into a
+// double-buffered tile) and lets each lane own one row's half of the chunk: a
+// lane sees its row's experts in increasing order, keeps the row's L best
+// (H, expert), and rarely needs to insert once its list is warm. Lanes l and
+// l ^ 32 (the two halves of a row) merge at the end. The noise draws and
+// biases ride a three-slot LDS ring two chunks ahead. Pass 2 evaluates
+// P = Phi((clean - thr) / sigma) in place and sums each expert's column over
+// the block's rows in a fixed order.
 #pragma once
 
 #include "gate_impl.h"
@@ -61,15 +62,16 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // pass 1: noise draws of a chunk, [256 rows][16 experts] fp32, then one copy
   // of the chunk's 16 biases per wave; four chunks in flight
   constexpr int ESLOT = kG32Rows * kG32Chunk + kG32Waves * kG32Chunk;
-  __shared__ float ebuf[PASS2 ? 1 : 4][PASS2 ? 1 : ESLOT];
-  __shared__ float hbuf[PASS2 ? 1 : kG32Waves][32 * kG32HStride];
+  __shared__ float ebuf[PASS2 ? 1 : 3][PASS2 ? 1 : ESLOT];
+  // pass 1: each wave's transpose tile, double-buffered by chunk parity
+  __shared__ float hbuf[PASS2 ? 1 : 2][PASS2 ? 1 : kG32Waves][32 * kG32HStride];
   __shared__ int selbuf[PASS2 ? kG32Rows : 1][L - 1];
   __shared__ float thrbuf[PASS2 ? kG32Rows : 1][2];
   __shared__ float red[PASS2 ? 2 : 1][kG32Waves][EC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const bool clean_lane = l32 < 16;
@@ -89,14 +91,13 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   }
 
   // Rows of this lane's (clean, noise) pairs after the exchange: element i is
-  // C-layout register j = i (clean lanes) or 8 + i (noise lanes).
+  // C-layout register j = i (clean lanes) or 8 + i (noise lanes). Rows past
+  // the tile's end compute finite garbage (zero x, the first row's noise):
+  // pass 1 never writes them out, pass 2 gives them thresholds of +inf, so
+  // their P is exactly 0. n is a multiple of 16, so every expert is valid.
   int rr[8];
-  bool row_ok[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    rr[i] = (clean_lane ? 0 : 16) + 8 * (i / 4) + 4 * hi + (i % 4);
-    row_ok[i] = tile.first + wrow0 + rr[i] < tile.end;
-  }
+  for (int i = 0; i < 8; ++i) rr[i] = (clean_lane ? 0 : 16) + 8 * (i / 4) + 4 * hi + (i % 4);
 
   if constexpr (PASS2) {
     for (int t = tid; t < kG32Rows; t += kG32Threads) {
@@ -104,8 +105,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       const bool ok = row >= 0;
 #pragma unroll
       for (int j = 0; j < L - 1; ++j) selbuf[t][j] = (ok && j < p.k) ? p.sel_idx[row * p.k + j] : -1;
-      thrbuf[t][0] = ok ? p.sel_thr[row * 2] : 0.f;
-      thrbuf[t][1] = ok ? p.sel_thr[row * 2 + 1] : 0.f;
+      thrbuf[t][0] = ok ? p.sel_thr[row * 2] : INFINITY;
+      thrbuf[t][1] = ok ? p.sel_thr[row * 2 + 1] : INFINITY;
     }
   }
 
@@ -120,25 +121,55 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
 
   // Chunk c -> LDS buffer dst. Wave w copies fragments kb = w + 8 i; lane l's
   // 16 bytes are B column l32 (clean row of expert 16 c + l32, or the noise row
-  // of expert 16 c + l32 - 16), K unit 2 kb + hi. Experts past n read row n - 1
-  // and are masked in the epilogue.
+  // of expert 16 c + l32 - 16), K unit 2 kb + hi: a fixed per-lane source plus
+  // a chunk offset common to the wave.
+  const bf16* wlane = (clean_lane ? wg : wn) + (int64_t)(l32 & 15) * D + hi * UE;
   auto dma = [&](int c, U16* dst) {
-    const int e = min(c * EC + (l32 & 15), n - 1);
-    const bf16* w = clean_lane ? wg : wn;
+    const bf16* src = wlane + (int64_t)c * EC * D;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
       const int kb = wave + kG32Waves * i;
-      copy16_to_lds(w + (int64_t)e * D + (kb * 2 + hi) * UE, &dst[kb * 64]);
+      copy16_to_lds(src + kb * 2 * UE, &dst[kb * 64]);
     }
   };
   const bool has_bias = p.bias != nullptr;
   const float* bias_src = has_bias ? p.bias : reinterpret_cast<const float*>(p.wg);
-  auto load_bias = [&](int c, float& bv) { bv = bias_src[min(c * EC + (l32 & 15), n - 1)]; };
+  auto load_bias = [&](int c, float& bv) {
+    if (has_bias) bv = bias_src[c * EC + (l32 & 15)];
+  };
+  // One chunk's products: 32 x 32 tile of (rows, clean|noise columns) over
+  // the K-blocks. Fragments are read four ahead of their matrix product; the
+  // base address is kept in a register so each read's offset within the
+  // buffer fits the instruction's immediate field.
+  constexpr int FPF = NKB < 4 ? NKB : 4;
   auto mfma_chunk = [&](const U16* src, f32x16& acc) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(3))) u32x4* LdsPtr;
+    uint32_t base = (uint32_t)(uintptr_t)(src + lane);
+    asm("" : "+v"(base));
+    const LdsPtr bl = (LdsPtr)base;
+    u32x4 f[FPF];
+#pragma unroll
+    for (int j = 0; j < FPF; ++j) f[j] = bl[j * 64];
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) Mfma<bf16>::k32(acc, xa[kb], src[kb * 64 + lane]);
+    for (int kb = 0; kb < NKB; ++kb) {
+      U16 cur;
+      __builtin_memcpy(&cur, &f[kb % FPF], 16);
+      if (kb + FPF < NKB) f[kb % FPF] = bl[(kb + FPF) * 64];
+      Mfma<bf16>::k32(acc, xa[kb], cur);
+    }
+    // Keep that order (the scheduler would otherwise pull the reads down next
+    // to their use): FPF reads, then matrix product / read pairs, then the
+    // last FPF products.
+    __builtin_amdgcn_sched_group_barrier(0x100, FPF, 0);
+#pragma unroll
+    for (int kb = 0; kb + FPF < NKB; ++kb) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FPF, 0);
   };
   // Noise draws of chunk c -> ring slot b (pass 1): wave w copies local rows
   // 32 w + 16 i + (l / 4), experts 4 (l % 4) .. + 3 of the chunk, so the slot
@@ -146,16 +177,17 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // a multiple of 16, so every 16-byte group is aligned and inside its row;
   // rows past the tile's end read the tile's first row and are masked in the
   // epilogue.
-  int64_t erow[2];
+  const float* elane[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int64_t r = tile_iorow(p, tile, wrow0 + 16 * i + (lane >> 2));
-    erow[i] = r >= 0 ? r : tile_iorow(p, tile, 0);
+    int64_t r = tile_iorow(p, tile, wrow0 + 16 * i + (lane >> 2));
+    if (r < 0) r = tile_iorow(p, tile, 0);
+    elane[i] = p.eps + r * n + 4 * (lane & 3);
   }
   auto dma_eps = [&](int c, int b) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const float* src = p.eps + erow[i] * n + c * EC + 4 * (lane & 3);
+      const float* src = elane[i] + c * EC;
       copy16_to_lds(src, &ebuf[b][(wave * 32 + 16 * i) * EC]);
     }
     // lanes 0-3 copy the chunk's biases (or, without a bias, any in-bounds
@@ -165,134 +197,144 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
   };
 
+  // Pass 1: lane (l32, hi) owns row l32's experts hi * 8 .. hi * 8 + 7 of a
+  // chunk; it keeps the row's L best, which rarely change once warm.
+  auto insert_row = [&](const f32x4 (&h)[2], int chunk) {
+    const float hv[8] = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    bool cand = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cand |= hv[i] > lv[L - 1];
+    if (__any(cand)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) insert_new<L>(lv, li, hv[i], chunk * EC + hi * 8 + i);
+    }
+  };
+
   const int nchunks = (n + EC - 1) / EC;
-  f32x16 acc, acc_next;
-  float bv, bv_next;
+  // Accumulators of two consecutive chunks: pass P reads accs[P] (its own
+  // chunk's products) and fills accs[P ^ 1] (the next chunk's); the same for
+  // pass 2's biases.
+  f32x16 accs[2];
+  float bvs[2] = {0.f, 0.f};
   dma(0, wbuf0);
   if (nchunks > 1) dma(1, wbuf1);
   if constexpr (!PASS2) {
-    for (int c = 0; c < 3 && c < nchunks; ++c) dma_eps(c, c);
+    for (int c = 0; c < 2 && c < nchunks; ++c) dma_eps(c, c);
   }
-  if constexpr (PASS2) load_bias(0, bv);
+  if constexpr (PASS2) load_bias(0, bvs[0]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  mfma_chunk(wbuf0, acc);
+  mfma_chunk(wbuf0, accs[0]);
   __syncthreads();  // every wave has read chunk 0 before buffer 0 is refilled
 
   // One pass per chunk; P = c & 1 is a compile-time constant (the loop below
-  // is unrolled by two) so each pass names its weight buffers statically.
+  // is unrolled by two) so each pass names its buffers statically.
   auto chunk_pass = [&](const int c, auto parity) {
     constexpr int P = decltype(parity)::value;
     U16* const wfill = P ? wbuf1 : wbuf0;       // buffer c & 1: chunk c + 2 goes here
     const U16* const wnext = P ? wbuf0 : wbuf1;  // buffer (c + 1) & 1: chunk c + 1
+    f32x16& acc = accs[P];
     // Copies issued this pass, oldest first: (pass 2) chunk c + 1's bias into
     // registers, chunk c + 2's weights into buffer c & 1 (whose chunk c every
-    // wave used before the last barrier), and (pass 1) chunk c + 3's noise
-    // draws and biases into ring slot (c + 3) & 3. The weights must land by
-    // the end of this pass; the noise draws have two more passes.
-    if constexpr (PASS2) load_bias(c + 1 < nchunks ? c + 1 : c, bv_next);
+    // wave used before the last barrier), and (pass 1) chunk c + 2's noise
+    // draws and biases into ring slot (c + 2) % 3 (chunk c - 1's, used in the
+    // last pass). The weights must land by the end of this pass; the noise
+    // draws have one more pass.
+    if constexpr (PASS2) load_bias(c + 1 < nchunks ? c + 1 : c, bvs[P ^ 1]);
     if (c + 2 < nchunks) dma(c + 2, wfill);
     asm volatile("" ::: "memory");
     if constexpr (!PASS2) {
-      if (c + 3 < nchunks) dma_eps(c + 3, (c + 3) & 3);
+      if (c + 2 < nchunks) dma_eps(c + 2, (c + 2) % 3);
     }
 
     float colsum = 0.f;
     float hpair[8];
-    auto products = [&]() { mfma_chunk(wnext, acc_next); };
+    auto products = [&]() { mfma_chunk(wnext, accs[P ^ 1]); };
     auto epilogue = [&]() {
-      // exchange: clean lanes send clean rows j = 8..15, noise lanes send noise rows j = 0..7
-      float recv[8];
+      // Exchange within each pair of 16-lane rows: the odd row's (noise
+      // lanes') registers acc[i] trade places with the even row's (clean
+      // lanes') registers acc[8 + i]. Afterwards every lane holds, for its
+      // rows rr[i], the clean logit in the first result and the noise
+      // pre-activation in the second.
+      float cl[8], un[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        // two static extracts and one select (kept apart so they are not
-        // folded into a per-lane dynamic index of the accumulator)
-        float hi8 = acc[8 + i], lo8 = acc[i];
-        asm("" : "+v"(hi8));
-        asm("" : "+v"(lo8));
-        recv[i] = __shfl_xor(clean_lane ? hi8 : lo8, 16);
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i]),
+                                                          __float_as_uint(acc[8 + i]), false, false);
+        cl[i] = __uint_as_float(sw[0]);
+        un[i] = __uint_as_float(sw[1]);
       }
-      const int e = c * EC + (l32 & 15);
-      const bool e_ok = e < n;
       float bias;
       if constexpr (PASS2) {
-        bias = has_bias ? bv : 0.f;
+        bias = has_bias ? bvs[P] : 0.f;
       } else {
-        bias = has_bias ? ebuf[c & 3][kG32Rows * EC + wave * EC + (l32 & 15)] : 0.f;
+        bias = has_bias ? ebuf[c % 3][kG32Rows * EC + wave * EC + (l32 & 15)] : 0.f;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float clean = (clean_lane ? acc[i] : recv[i]) + bias;
-        const float u = clean_lane ? recv[i] : acc[8 + i];
-        const bool ok = e_ok && row_ok[i];
+        const float clean = cl[i] + bias;
         if constexpr (!PASS2) {
-          const float eps = ebuf[c & 3][(wave * 32 + rr[i]) * EC + (l32 & 15)];
-          const float H = fmaf(eps, softplus_f(u) + p.floor, clean);
-          hpair[i] = ok ? H : -INFINITY;
+          const float eps = ebuf[c % 3][(wave * 32 + rr[i]) * EC + (l32 & 15)];
+          hpair[i] = fmaf(eps, softplus_f(un[i]) + p.floor, clean);
         } else {
-          const float sigma = softplus_f(u) + p.floor;
+          const int e = c * EC + (l32 & 15);
+          const float sigma = softplus_f(un[i]) + p.floor;
           const int row = wave * 32 + rr[i];
           bool member = false;
 #pragma unroll
           for (int j = 0; j < L - 1; ++j) member |= (selbuf[row][j] == e);
           const float thr = member ? thrbuf[row][1] : thrbuf[row][0];
-          const float P = phi_f((clean - thr) * rcp_f(sigma));
-          colsum += ok ? P : 0.f;
+          colsum += phi_f((clean - thr) * rcp_f(sigma));
         }
       }
     };
-    if (wave & 4) {
-      epilogue();
-      __builtin_amdgcn_sched_barrier(0);
-      products();
-    } else {
-      products();
-      __builtin_amdgcn_sched_barrier(0);
-      epilogue();
-    }
-
-    if constexpr (!PASS2) {
-      // Transpose H through this wave's LDS tile, then each lane scans its row.
-      float* hb = hbuf[wave];
-      const int ecol = l32 & 15;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) hb[rr[i] * kG32HStride + ecol] = hpair[i];
-      // A wave's LDS instructions execute in order, so its own writes are
-      // visible to the reads below without a fence. The reads are issued (and
-      // waited for) in one asm block: the compiler would otherwise also wait
-      // for every global->LDS copy still in flight before an LDS read.
-      f32x4 h0, h1;
-      {
-        const uint32_t a = (uint32_t)(uintptr_t)(&hb[l32 * kG32HStride + hi * 8]);
-        asm volatile(
-            "ds_read_b128 %0, %2\n\t"
-            "ds_read_b128 %1, %2 offset:16\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=v"(h0), "=v"(h1)
-            : "v"(a)
-            : "memory");
+    // Pass 1 transposes H through this wave's LDS tile and lets each lane scan
+    // its row, one chunk behind: chunk c's values are written in this pass
+    // and read back in the next, so the reads never wait for fresh writes
+    // (a wave's LDS operations complete in order, so no fence is needed).
+    f32x4 hprev[2];
+    auto read_prev = [&]() {
+      if constexpr (!PASS2) {
+        if (c > 0) {
+          const float* hb = &hbuf[P ^ 1][wave][l32 * kG32HStride + hi * 8];
+          hprev[0] = *reinterpret_cast<const f32x4*>(hb);
+          hprev[1] = *reinterpret_cast<const f32x4*>(hb + 4);
+        }
       }
-      const float hv[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-      bool cand = false;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) cand |= hv[i] > lv[L - 1];
-      if (__any(cand)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) insert_new<L>(lv, li, hv[i], c * EC + hi * 8 + i);
+    };
+    auto insert_prev = [&]() {
+      if constexpr (!PASS2) {
+        if (c > 0) insert_row(hprev, c - 1);
       }
-      __builtin_amdgcn_wave_barrier();
-    } else {
-      // column sums: lanes l, l ^ 16 (same expert, other rows) and l ^ 32
-      colsum += __shfl_xor(colsum, 16);
-      colsum += __shfl_xor(colsum, 32);
-      if (lane < 16) red[P][wave][lane] = colsum;
-    }
+    };
+    // Pass 1: write this chunk's H to the tile. Pass 2: the column sums of the chunk.
+    auto finish = [&]() {
+      if constexpr (!PASS2) {
+        float* hb = hbuf[P][wave];
+        const int ecol = l32 & 15;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hb[rr[i] * kG32HStride + ecol] = hpair[i];
+      } else {
+        // column sums: lanes l, l ^ 16 (same expert, other rows) and l ^ 32
+        colsum += __shfl_xor(colsum, 16);
+        colsum += __shfl_xor(colsum, 32);
+        if (lane < 16) red[P][wave][lane] = colsum;
+      }
+    };
+    // The next chunk's products go first: their matrix operations run while
+    // this chunk's epilogue occupies the vector ALUs.
+    products();
+    __builtin_amdgcn_sched_barrier(0);
+    read_prev();
+    epilogue();
+    insert_prev();
+    finish();
 
     // Block barrier without a release fence (which would wait for every copy
     // in flight): each wave first waits for its LDS traffic and for all its
     // copies but the three noise/bias copies issued this pass, if any (copies
     // complete in issue order, so a count of 3 then covers the weights).
-    if (!PASS2 && c + 3 < nchunks) {
+    if (!PASS2 && c + 2 < nchunks) {
       asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -300,22 +342,24 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
 
     if constexpr (PASS2) {
       if (tid < EC) {
-        const int e = c * EC + tid;
-        if (e < n) {
-          float s = 0.f;
+        float s = 0.f;
 #pragma unroll
-          for (int w = 0; w < kG32Waves; ++w) s += red[P][w][tid];
-          p.partial[(int64_t)blockIdx.x * n + e] = s;
-        }
+        for (int w = 0; w < kG32Waves; ++w) s += red[P][w][tid];
+        p.partial[(int64_t)blockIdx.x * n + c * EC + tid] = s;
       }
     }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = acc_next[j];
-    bv = bv_next;
   };
   for (int c = 0; c < nchunks; c += 2) {
     chunk_pass(c, IntConst<0>{});
     if (c + 1 < nchunks) chunk_pass(c + 1, IntConst<1>{});
+  }
+  if constexpr (!PASS2) {
+    // the last chunk's values, written in the last pass
+    f32x4 h[2];
+    const float* hb = &hbuf[(nchunks - 1) & 1][wave][l32 * kG32HStride + hi * 8];
+    h[0] = *reinterpret_cast<const f32x4*>(hb);
+    h[1] = *reinterpret_cast<const f32x4*>(hb + 4);
+    insert_row(h, nchunks - 1);
   }
 
   if constexpr (!PASS2) {
