@@ -314,8 +314,8 @@ def main():
         "combine": time_calls(lambda: moe.moe_combine(eo, route["slot_pos"], topk_gate,
                                                       n_experts=n, out=y), it, torch),
         "aux_losses": time_calls(lambda: moe.moe_aux_losses(
-            g["x"], g["w_gate"], g["w_noise"], topk_idx, thresh, counts, route["importance"],
-            gate_bias=g.get("gate_bias"), ws=ws), it, torch),
+            g["x"], g["w_gate"], g["w_noise"], thresh, route["offsets"], route["perm_token"],
+            route["importance"], k, gate_bias=g.get("gate_bias"), ws=ws), it, torch),
     }
     torch.cuda.synchronize()
     log("stages (ms): " + ", ".join(f"{k_}={v:.3f}" for k_, v in stages.items()))

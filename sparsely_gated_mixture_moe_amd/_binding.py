@@ -256,21 +256,21 @@ def moe_combine(expert_out, slot_pos, topk_gate, *, n_experts: int = 1, out=None
     return out
 
 
-def moe_aux_losses(x, w_gate, w_noise, topk_idx, thresh, counts, importance, *, train: bool = True,
-                   noise_floor: float = 1e-2, w_importance: float = 0.1, w_load: float = 0.1,
-                   gate_bias=None, ws: Optional[torch.Tensor] = None,
+def moe_aux_losses(x, w_gate, w_noise, thresh, offsets, perm_token, importance, k: int, *,
+                   train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
+                   w_load: float = 0.1, gate_bias=None, ws: Optional[torch.Tensor] = None,
                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """(load [n], losses [3] = CV2(imp), CV2(load), weighted sum)."""
+    """(load [n], losses [3] = CV2(imp), CV2(load), weighted sum). ``thresh`` comes from
+    moe_gate; ``offsets``, ``perm_token`` and ``importance`` from moe_route of its selection."""
     _dev(x, "x")
     B, d = x.shape
     _dev(w_gate, "w_gate")
     n = w_gate.shape[0]
     _dev(w_noise, "w_noise", w_gate.dtype, (n, d))
     _dev(gate_bias, "gate_bias", torch.float32, (n,))
-    _dev(topk_idx, "topk_idx", torch.int32)
-    k = topk_idx.shape[1]
     _dev(thresh, "thresh", torch.float32, (B, 2))
-    _dev(counts, "counts", torch.int32, (n,))
+    _dev(offsets, "offsets", torch.int32, (n + 1,))
+    _dev(perm_token, "perm_token", torch.int32, (B * k,))
     _dev(importance, "importance", torch.float32, (n,))
     dims = _gate_dims(x, w_gate, k)
     opts = make_opts(train, noise_floor, w_importance, w_load)
@@ -279,9 +279,9 @@ def moe_aux_losses(x, w_gate, w_noise, topk_idx, thresh, counts, importance, *, 
     load = torch.empty(n, dtype=torch.float32, device=x.device)
     losses = torch.empty(3, dtype=torch.float32, device=x.device)
     st = lib().moe_aux_losses(ctypes.byref(dims), ctypes.byref(opts), _ptr(x), _ptr(w_gate),
-                              _ptr(w_noise), _ptr(gate_bias), _ptr(topk_idx), _ptr(thresh),
-                              _ptr(counts), _ptr(importance), _ptr(load), _ptr(losses), _ptr(ws),
-                              ws.numel(), _stream(stream))
+                              _ptr(w_noise), _ptr(gate_bias), _ptr(thresh), _ptr(offsets),
+                              _ptr(perm_token), _ptr(importance), _ptr(load), _ptr(losses),
+                              _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_aux_losses")
     return load, losses
 

@@ -59,6 +59,13 @@ __global__ void counts_to_load_kernel(const int32_t* __restrict__ counts, int n,
   if (e < n) load[e] = (float)counts[e];
 }
 
+// The same from a route's offsets: load[e] = offsets[e + 1] - offsets[e].
+__global__ void offsets_to_load_kernel(const int32_t* __restrict__ offsets, int n,
+                                       float* __restrict__ load) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n) load[e] = (float)(offsets[e + 1] - offsets[e]);
+}
+
 // CV^2 = population variance / mean^2 of importance and of load, in fp64 with a
 // fixed reduction order; losses = {CV2(imp), CV2(load), w_imp CV2(imp) + w_load CV2(load)}.
 __global__ __launch_bounds__(256) void cv2_losses_kernel(const float* __restrict__ imp,
@@ -124,6 +131,12 @@ hipError_t launch_combine(int64_t tokens, int k, int d, Dt dt, const void* exper
 
 hipError_t launch_counts_to_load(const int32_t* counts, int n, float* load, hipStream_t s) {
   hipLaunchKernelGGL(counts_to_load_kernel, dim3((n + 255) / 256), dim3(256), 0, s, counts, n, load);
+  return hipGetLastError();
+}
+
+hipError_t launch_offsets_to_load(const int32_t* offsets, int n, float* load, hipStream_t s) {
+  hipLaunchKernelGGL(offsets_to_load_kernel, dim3((n + 255) / 256), dim3(256), 0, s, offsets, n,
+                     load);
   return hipGetLastError();
 }
 

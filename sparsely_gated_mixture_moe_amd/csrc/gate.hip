@@ -9,9 +9,11 @@ using gate_detail::GateParams;
 
 // load[e] = sum over gate blocks b of partial[b][e], in a fixed order: 32
 // experts per workgroup, 8 threads per expert each summing a strided subset
-// of the blocks, then the 8 partial sums in thread order.
+// of the blocks, then the 8 partial sums in thread order; plus the selected
+// pairs' correction corr[e].
 __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restrict__ partial,
                                                           int nblocks, int n,
+                                                          const float* __restrict__ corr,
                                                           float* __restrict__ load) {
   __shared__ float red[8][32];
   const int col = threadIdx.x & 31;
@@ -26,7 +28,7 @@ __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restric
     float t = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) t += red[i][col];
-    load[e] = t;
+    load[e] = t + corr[e];
   }
 }
 
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restric
 // order as above; a group without rows gets 0.
 __global__ __launch_bounds__(256) void load_reduce_grouped_kernel(
     const float* __restrict__ partial, const int32_t* __restrict__ unit_start, int n,
-    float* __restrict__ load) {
+    const float* __restrict__ corr, float* __restrict__ load) {
   __shared__ float red[8][32];
   const int col = threadIdx.x & 31;
   const int part = threadIdx.x >> 5;
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void load_reduce_grouped_kernel(
     float t = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) t += red[i][col];
-    load[(int64_t)grp * n + e] = t;
+    load[(int64_t)grp * n + e] = t + corr[(int64_t)grp * n + e];
   }
 }
 
@@ -90,6 +92,112 @@ __global__ __launch_bounds__(1024) void group_plan_kernel(const int32_t* __restr
     units[0] = part[t];
     unit_start[groups] = part[t];
   }
+}
+
+// Eight consecutive elements (storage type T) widened to fp32; 16 bytes for
+// bf16, 32 for fp32.
+template <typename T>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const U16 u = ld_unit(reinterpret_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u.w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u.w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float* f = reinterpret_cast<const float*>(base) + off;
+    const U16 a = ld_unit(f), b = ld_unit(f + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(a.w[i]);
+      v[4 + i] = __uint_as_float(b.w[i]);
+    }
+  }
+}
+
+// The selected pairs of eq 8: the Load pass evaluates every (token, expert)
+// pair against the row's k-th largest logit v_k, while a selected expert's
+// threshold is the (k+1)-th, v_{k+1}. For expert e this kernel takes the rows
+// routed to it (positions offsets[e] .. offsets[e+1] - 1, tokens perm_token[p])
+// and sums Phi((clean - v_{k+1}) / sigma) - Phi((clean - v_k) / sigma), with
+// clean = x . W_g[e] (+ bias) and sigma = Softplus(x . W_noise[e]) + floor
+// recomputed by a dot product over d in fp32. One workgroup of four waves per
+// expert: lane l holds elements 8 l .. 8 l + 7 of both weight rows (d <= 512);
+// wave w takes the rows' groups of eight with index w mod 4, all eight in
+// flight at once; the four waves' sums are added in wave order.
+// Secondary gates of a hierarchical layer: expert e is leaf (g, j) = (e / b,
+// e % b), its weights are row e of the [a * b, d] secondary weights, and token
+// t's thresholds are row t * k1 + r, where r is g's rank in sel1[t].
+template <typename XS, typename WS>
+__global__ __launch_bounds__(256) void load_correction_kernel(
+    const void* __restrict__ x, const void* __restrict__ wg, const void* __restrict__ wn,
+    const float* __restrict__ bias, int d, int n, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ perm_token, const float* __restrict__ thresh, float noise_floor,
+    const int32_t* __restrict__ sel1, int k1, int b, float* __restrict__ corr) {
+  constexpr int R = 8;
+  __shared__ float part[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int e = blockIdx.x;
+  const bool active = lane * 8 < d;
+  float wgv[8], wnv[8];
+  if (active) {
+    load8<WS>(wg, (int64_t)e * d + lane * 8, wgv);
+    load8<WS>(wn, (int64_t)e * d + lane * 8, wnv);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wgv[i] = wnv[i] = 0.f;
+  }
+  const float be = bias ? bias[e] : 0.f;
+  const int grp = e / b;
+  const int p0 = offsets[e], p1 = offsets[e + 1];
+  float acc = 0.f;
+  for (int p = p0 + wave * R; p < p1; p += 4 * R) {
+    int64_t t[R];
+    float c[R], u[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) t[r] = perm_token[min(p + r, p1 - 1)];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      c[r] = u[r] = 0.f;
+      if (active) {
+        float xv[8];
+        load8<XS>(x, t[r] * d + lane * 8, xv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          c[r] = fmaf(xv[i], wgv[i], c[r]);
+          u[r] = fmaf(xv[i], wnv[i], u[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        c[r] += __shfl_xor(c[r], o);
+        u[r] += __shfl_xor(u[r], o);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (p + r < p1) {  // uniform across the wave
+        int64_t row = t[r];
+        if (sel1) {
+          int rank = 0;
+          for (int j = 0; j < k1; ++j)
+            if (sel1[t[r] * k1 + j] == grp) rank = j;
+          row = t[r] * k1 + rank;
+        }
+        const float inv = rcp_f(softplus_f(u[r]) + noise_floor);
+        const float cl = c[r] + be;
+        acc += phi_f((cl - thresh[row * 2 + 1]) * inv) - phi_f((cl - thresh[row * 2]) * inv);
+      }
+    }
+  }
+  if (lane == 0) part[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) corr[e] = ((part[0] + part[1]) + part[2]) + part[3];
 }
 
 hipError_t gate_dispatch(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
@@ -151,37 +259,61 @@ hipError_t launch_group_plan(const int32_t* offsets, int groups, int tile_rows, 
   return hipGetLastError();
 }
 
+hipError_t launch_load_correction(const GateLaunch& g, int n, const int32_t* offsets,
+                                  const int32_t* perm_token, const float* thresh,
+                                  const int32_t* sel1, int k1, int b, float* corr, hipStream_t s) {
+  const dim3 grid((unsigned)n), block(256);
+  const void* bias = g.units ? nullptr : g.bias;
+  const float* bp = reinterpret_cast<const float*>(bias);
+#define MOE_CORR(XS, WS)                                                                      \
+  hipLaunchKernelGGL((load_correction_kernel<XS, WS>), grid, block, 0, s, g.x, g.w_gate,      \
+                     g.w_noise, bp, g.d, n, offsets, perm_token, thresh, g.noise_floor, sel1, \
+                     k1, b, corr)
+  if (g.x_dt == kBF16 && g.w_dt == kBF16) MOE_CORR(bf16, bf16);
+  else if (g.x_dt == kBF16) MOE_CORR(bf16, float);
+  else MOE_CORR(float, float);
+#undef MOE_CORR
+  return hipGetLastError();
+}
+
 hipError_t launch_load_grouped(const GateLaunch& g, int groups, const int32_t* unit_start,
-                               const int32_t* topk_idx, const float* thresh, float* partial,
-                               float* load, hipStream_t s) {
+                               const float* thresh, const int32_t* leaf_offsets,
+                               const int32_t* leaf_perm_token, const int32_t* sel1, int k1,
+                               float* partial, float* corr, float* load, hipStream_t s) {
   if (g.tokens > 0) {
     GateParams p = make_params(g);
-    p.sel_idx = topk_idx;
     p.sel_thr = thresh;
     p.partial = partial;
     hipError_t e = gate_dispatch(g, p, true, s);
     if (e != hipSuccess) return e;
   }
+  const int nleaves = groups * g.n;
+  hipError_t e = launch_load_correction(g, nleaves, leaf_offsets, leaf_perm_token, thresh, sel1,
+                                        k1, g.n, corr, s);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(load_reduce_grouped_kernel, dim3((g.n + 31) / 32, groups), dim3(256), 0, s,
-                     partial, unit_start, g.n, load);
+                     partial, unit_start, g.n, corr, load);
   return hipGetLastError();
 }
 
-hipError_t launch_load(const GateLaunch& g, const int32_t* topk_idx, const float* thresh,
-                       float* partial, float* load, hipStream_t s) {
+hipError_t launch_load(const GateLaunch& g, const float* thresh, const int32_t* offsets,
+                       const int32_t* perm_token, float* partial, float* corr, float* load,
+                       hipStream_t s) {
   // partial has room for gate_blocks() rows: the 32x32 kernel's 256-row blocks need fewer
   const int rows = gate_tile_rows(g);
   const int nb = (int)((g.tokens + rows - 1) / rows);
   if (nb > 0) {
     GateParams p = make_params(g);
-    p.sel_idx = topk_idx;
     p.sel_thr = thresh;
     p.partial = partial;
     hipError_t e = gate_dispatch(g, p, true, s);
     if (e != hipSuccess) return e;
   }
+  hipError_t e = launch_load_correction(g, g.n, offsets, perm_token, thresh, nullptr, 1, 1, corr,
+                                        s);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(load_reduce_kernel, dim3((g.n + 31) / 32), dim3(256), 0, s, partial, nb,
-                     g.n, load);
+                     g.n, corr, load);
   return hipGetLastError();
 }
 

@@ -24,8 +24,9 @@
 // (H, expert), and rarely needs to insert once its list is warm. Lanes l and
 // l ^ 32 (the two halves of a row) merge at the end. The noise draws and
 // biases ride a three-slot LDS ring two chunks ahead. Pass 2 evaluates
-// P = Phi((clean - thr) / sigma) in place and sums each expert's column over
-// the block's rows in a fixed order.
+// P = Phi((clean - v_k) / sigma) in place and sums each expert's column over
+// the block's rows in a fixed order (the selected pairs are corrected to the
+// (k+1)-th threshold separately).
 #pragma once
 
 #include "gate_impl.h"
@@ -65,8 +66,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   __shared__ float ebuf[PASS2 ? 1 : 3][PASS2 ? 1 : ESLOT];
   // pass 1: each wave's transpose tile, double-buffered by chunk parity
   __shared__ float hbuf[PASS2 ? 1 : 2][PASS2 ? 1 : kG32Waves][32 * kG32HStride];
-  __shared__ int selbuf[PASS2 ? kG32Rows : 1][L - 1];
-  __shared__ float thrbuf[PASS2 ? kG32Rows : 1][2];
+  __shared__ float thrbuf[PASS2 ? kG32Rows : 1];  // pass 2: each row's k-th logit
   __shared__ float red[PASS2 ? 2 : 1][kG32Waves][EC];
 
   const int tid = threadIdx.x;
@@ -102,11 +102,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   if constexpr (PASS2) {
     for (int t = tid; t < kG32Rows; t += kG32Threads) {
       const int64_t row = tile_iorow(p, tile, t);
-      const bool ok = row >= 0;
-#pragma unroll
-      for (int j = 0; j < L - 1; ++j) selbuf[t][j] = (ok && j < p.k) ? p.sel_idx[row * p.k + j] : -1;
-      thrbuf[t][0] = ok ? p.sel_thr[row * 2] : INFINITY;
-      thrbuf[t][1] = ok ? p.sel_thr[row * 2 + 1] : INFINITY;
+      thrbuf[t] = row >= 0 ? p.sel_thr[row * 2] : INFINITY;
     }
   }
 
@@ -227,6 +223,15 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   mfma_chunk(wbuf0, accs[0]);
   __syncthreads();  // every wave has read chunk 0 before buffer 0 is refilled
 
+  // Pass 2 evaluates every pair against its row's k-th largest logit (+inf
+  // for rows past the tile's end, so their P is 0); the selected pairs'
+  // difference (threshold (k+1)-th) is added by a separate kernel.
+  float thrk[8];
+  if constexpr (PASS2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) thrk[i] = thrbuf[wave * 32 + rr[i]];
+  }
+
   // One pass per chunk; P = c & 1 is a compile-time constant (the loop below
   // is unrolled by two) so each pass names its buffers statically.
   auto chunk_pass = [&](const int c, auto parity) {
@@ -277,14 +282,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
           const float eps = ebuf[c % 3][(wave * 32 + rr[i]) * EC + (l32 & 15)];
           hpair[i] = fmaf(eps, softplus_f(un[i]) + p.floor, clean);
         } else {
-          const int e = c * EC + (l32 & 15);
           const float sigma = softplus_f(un[i]) + p.floor;
-          const int row = wave * 32 + rr[i];
-          bool member = false;
-#pragma unroll
-          for (int j = 0; j < L - 1; ++j) member |= (selbuf[row][j] == e);
-          const float thr = member ? thrbuf[row][1] : thrbuf[row][0];
-          colsum += phi_f((clean - thr) * rcp_f(sigma));
+          colsum += phi_f((clean - thrk[i]) * rcp_f(sigma));
         }
       }
     };

@@ -18,10 +18,12 @@
 // 16 lanes of a row merge their lists (butterfly over lane bits 0-3), and the
 // row's top k, their softmax gates and the k-th/(k+1)-th logits are written.
 //
-// Pass 2 epilogue: P = Phi((clean - thr) / sigma) with thr the (k+1)-th logit
-// for selected experts and the k-th otherwise; column sums over the block's
-// rows in a fixed order go to a per-block partial, reduced afterwards in block
-// order. Pass 2 recomputes the matrix products instead of storing B x n logits.
+// Pass 2 epilogue: P = Phi((clean - v_k) / sigma) with v_k the row's k-th
+// largest logit; column sums over the block's rows in a fixed order go to a
+// per-block partial, reduced afterwards in block order. The selected pairs,
+// whose threshold is the (k+1)-th logit instead, are corrected by a separate
+// kernel over the routed rows. Pass 2 recomputes the matrix products instead
+// of storing B x n logits.
 
 #include "device_common.h"
 #include "moe_internal.h"
@@ -45,15 +47,14 @@ struct GateParams {
   int32_t* topk_idx;
   float* topk_gate;
   float* thresh;
-  const int32_t* sel_idx;
-  const float* sel_thr;
+  const float* sel_thr;  // pass 2: (k-th, (k+1)-th) logit of each row
   float* partial;
   // Secondary gating of a hierarchical layer ("Hierarchical MoE"); all null
   // for a flat gate. The rows are those a primary route sent to each group:
   // workgroup u covers the rows seg_off[g] + first, ... of group g, with
   // (g, first) = (units[1 + 2u], units[2 + 2u]) and units[0] the number of
   // units. Routed row r reads x row row_token[r] and owns row row_slot[r] of
-  // eps, of the outputs and of sel_idx / sel_thr; group g's gate weights are
+  // eps, of the outputs and of sel_thr; group g's gate weights are
   // rows g*n .. g*n + n - 1 of wg / wn, its biases entries g*n .. of bias.
   const int32_t* units;
   const int32_t* seg_off;
@@ -218,8 +219,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   int li[4][L];
   float shared_thr[4];  // max over the row's 16 lanes of their L-th best: a lower
                         // bound of the row's L-th best logit
-  int sel[4][L - 1];
-  float thr_k[4], thr_k1[4];
+  float thr_k[4];
   if constexpr (!PASS2) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -231,15 +231,10 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
       }
     }
   } else {
+    // Every pair is evaluated against the row's k-th largest logit; the
+    // selected pairs' difference (threshold (k+1)-th) is added separately.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = iorow[r];
-#pragma unroll
-      for (int j = 0; j < L - 1; ++j)
-        sel[r][j] = (row_ok[r] && j < p.k) ? p.sel_idx[row * p.k + j] : -1;
-      thr_k[r] = row_ok[r] ? p.sel_thr[row * 2] : 0.f;
-      thr_k1[r] = row_ok[r] ? p.sel_thr[row * 2 + 1] : 0.f;
-    }
+    for (int r = 0; r < 4; ++r) thr_k[r] = row_ok[r] ? p.sel_thr[iorow[r] * 2] : 0.f;
   }
 
   // Chunk staging. Unit u of a chunk is stored at LDS unit u in fragment order
@@ -355,11 +350,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
             cand_any |= (H > lv[r][L - 1]) && (H >= shared_thr[r]);
           } else {
             const float sigma = softplus_f(acc[NM - 1][nt][r]) + p.floor;
-            bool member = false;
-#pragma unroll
-            for (int j = 0; j < L - 1; ++j) member |= (sel[r][j] == e);
-            const float thr = member ? thr_k1[r] : thr_k[r];
-            const float P = phi_f((clean - thr) * rcp_f(sigma));
+            const float P = phi_f((clean - thr_k[r]) * rcp_f(sigma));
             colsum[nt] += ok ? P : 0.f;
           }
         }

@@ -104,7 +104,7 @@ moe_status check_opts(const moe_gate_opts* o) {
 // Workspace regions. Each call uses a prefix-free subset; moe_forward uses all.
 struct Layout {
   size_t topk_idx, topk_gate, thresh, counts, offsets, perm_token, perm_gate, slot_pos,
-      importance, blockcnt, ffn_blocks, expert_out, load_partial, total;
+      importance, blockcnt, ffn_blocks, expert_out, load_partial, load_corr, total;
   size_t route_bytes, ffn_bytes, aux_bytes;  // standalone needs (from offset 0)
 };
 
@@ -123,7 +123,10 @@ Layout layout(const moe_dims* d, const moe_gate_opts* o) {
   L.ffn_bytes = align_up((size_t)(1 + 2 * moe::ffn_max_blocks(pairs, (int)n, d->d_model,
                                                              to_dt(d->act_dtype))) *
                          sizeof(int32_t));
-  L.aux_bytes = (o && o->train) ? align_up((size_t)moe::gate_blocks(B) * n * sizeof(float)) : 0;
+  // the Load pass: per-block partial sums, then the selected pairs' corrections
+  L.aux_bytes = (o && o->train) ? align_up((size_t)moe::gate_blocks(B) * n * sizeof(float)) +
+                                      align_up((size_t)n * sizeof(float))
+                                : 0;
   // moe_forward
   L.topk_idx = take(pairs * sizeof(int32_t));
   L.topk_gate = take(pairs * sizeof(float));
@@ -138,6 +141,9 @@ Layout layout(const moe_dims* d, const moe_gate_opts* o) {
   L.ffn_blocks = take(L.ffn_bytes);
   L.expert_out = take((size_t)pairs * d->d_model * dt_size(d->act_dtype));
   L.load_partial = take(L.aux_bytes);
+  L.load_corr = L.load_partial + (L.aux_bytes ? align_up((size_t)moe::gate_blocks(B) * n *
+                                                         sizeof(float))
+                                              : 0);
   L.total = at;
   return L;
 }
@@ -221,8 +227,8 @@ moe_status check_hier_dims(const moe_hier_dims* h) {
 struct HierLayout {
   size_t sel1, gate1, thr1, counts1, offsets1, perm_token1, perm_gate1, slot_pos1, perm_slot1,
       imp1, blockcnt1, units, unit_start, sel2, gate2, thr2, topk_idx, topk_gate, counts, offsets,
-      perm_token, perm_gate, slot_pos, blockcnt, ffn_blocks, expert_out, load1, partial1, load2,
-      partial2, total;
+      perm_token, perm_gate, slot_pos, blockcnt, ffn_blocks, expert_out, load1, partial1, corr1,
+      load2, partial2, corr2, total;
   int64_t max_units;
 };
 
@@ -291,8 +297,10 @@ HierLayout hier_layout(const moe_hier_dims* h, const moe_gate_opts* o) {
   L.expert_out = take((size_t)pairs * h->d_model * dt_size(h->act_dtype));
   L.load1 = take(a * sizeof(float));
   L.partial1 = take(train ? (size_t)moe::gate_blocks(B) * a * sizeof(float) : 0);
+  L.corr1 = take(a * sizeof(float));
   L.load2 = take(n * sizeof(float));
   L.partial2 = take(train ? (size_t)L.max_units * b * sizeof(float) : 0);
+  L.corr2 = take(n * sizeof(float));
   L.total = at;
   return L;
 }
@@ -403,7 +411,7 @@ moe_status moe_combine(const moe_dims* dims, const void* expert_out, const int32
 
 moe_status moe_aux_losses(const moe_dims* dims, const moe_gate_opts* opts, const void* x,
                           const void* w_gate, const void* w_noise, const float* gate_bias,
-                          const int32_t* topk_idx, const float* thresh, const int32_t* counts,
+                          const float* thresh, const int32_t* offsets, const int32_t* perm_token,
                           const float* importance, float* load, float* losses, void* ws,
                           size_t ws_bytes, void* stream) {
   moe_status s;
@@ -411,21 +419,22 @@ moe_status moe_aux_losses(const moe_dims* dims, const moe_gate_opts* opts, const
   REQ(importance, 4);
   REQ(load, 4);
   REQ(losses, 4);
+  REQ(offsets, 4);
   const hipStream_t st = (hipStream_t)stream;
   if (opts->train) {
     if ((s = check_gate_args(dims, opts, x, w_gate, w_noise, gate_bias, nullptr, false)) !=
         MOE_OK)
       return s;
-    REQN(topk_idx, 4, dims->tokens);
     REQN(thresh, 4, dims->tokens);
+    REQN(perm_token, 4, dims->tokens);
     const Layout L = layout(dims, opts);
     if ((s = check_ws(ws, ws_bytes, L.aux_bytes)) != MOE_OK) return s;
     const moe::GateLaunch g = gate_launch(dims, opts, x, w_gate, w_noise, gate_bias, nullptr);
-    hipError_t e = moe::launch_load(g, topk_idx, thresh, at<float>(ws, 0), load, st);
+    hipError_t e = moe::launch_load(g, thresh, offsets, perm_token, at<float>(ws, 0),
+                                    at<float>(ws, L.load_corr - L.load_partial), load, st);
     if (e != hipSuccess) return device_status(e, "moe_aux_losses (load)");
   } else {
-    REQ(counts, 4);
-    hipError_t e = moe::launch_counts_to_load(counts, dims->n_experts, load, st);
+    hipError_t e = moe::launch_offsets_to_load(offsets, dims->n_experts, load, st);
     if (e != hipSuccess) return device_status(e, "moe_aux_losses (counts)");
   }
   return device_status(moe::launch_cv2_losses(importance, load, dims->n_experts,
@@ -487,7 +496,8 @@ moe_status moe_forward(const moe_dims* dims, const moe_gate_opts* opts, const vo
                           slot_pos, topk_gate, y, st);
   if (e != hipSuccess) return device_status(e, "moe_forward (combine)");
   if (opts->train)
-    e = moe::launch_load(g, topk_idx, thresh, at<float>(ws, L.load_partial), load, st);
+    e = moe::launch_load(g, thresh, offsets, perm_token, at<float>(ws, L.load_partial),
+                         at<float>(ws, L.load_corr), load, st);
   else
     e = moe::launch_counts_to_load(counts, dims->n_experts, load, st);
   if (e != hipSuccess) return device_status(e, "moe_forward (load)");
@@ -620,10 +630,11 @@ moe_status moe_hier_forward(const moe_hier_dims* dims, const moe_gate_opts* opts
   if (e != hipSuccess) return device_status(e, "moe_hier_forward (combine)");
   // both levels' Load, then the leaf Load and the losses
   if (opts->train) {
-    e = moe::launch_load(g1, sel1, thr1, at<float>(ws, L.partial1), load1, st);
+    e = moe::launch_load(g1, thr1, offsets1, perm_token1, at<float>(ws, L.partial1),
+                         at<float>(ws, L.corr1), load1, st);
     if (e == hipSuccess)
-      e = moe::launch_load_grouped(g2, a, unit_start, sel2, thr2, at<float>(ws, L.partial2),
-                                   load2, st);
+      e = moe::launch_load_grouped(g2, a, unit_start, thr2, offsets, perm_token, sel1, k1,
+                                   at<float>(ws, L.partial2), at<float>(ws, L.corr2), load2, st);
   } else {
     e = moe::launch_counts_to_load(counts1, a, load1, st);
     if (e == hipSuccess) e = moe::launch_counts_to_load(counts, n, load2, st);

@@ -45,25 +45,32 @@ hipError_t launch_gate(const GateLaunch& g, int32_t* topk_idx, float* topk_gate,
                        hipStream_t s);
 
 // Load (eq 10) with train = 1: recomputes the logits, evaluates P for every
-// (token, expert) and writes per-block column sums partial [blocks][n]; then
-// reduces them into load [n].
+// (token, expert) against the row's k-th logit and writes per-block column sums
+// partial [blocks][n]; corrects the selected pairs to the (k+1)-th threshold
+// from the routed rows (offsets / perm_token of the route of this selection)
+// into corr [n]; then reduces both into load [n].
 int gate_blocks(int64_t tokens);
-hipError_t launch_load(const GateLaunch& g, const int32_t* topk_idx, const float* thresh,
-                       float* partial, float* load, hipStream_t s);
+hipError_t launch_load(const GateLaunch& g, const float* thresh, const int32_t* offsets,
+                       const int32_t* perm_token, float* partial, float* corr, float* load,
+                       hipStream_t s);
 bool gate_supported(int d, Dt x_dt, Dt w_dt, int k);
 
 // Secondary (grouped) gating. Rows per work unit of the kernel that `g` runs
 // on; the largest unit count for `rows` routed rows over `groups` groups;
 // the unit list (units [1 + 2 * max_units], unit_start [groups + 1]) from the
 // primary route's offsets; the Load pass, whose per-unit partial sums
-// ([max_units][n]) are reduced per group into load [groups * n].
+// ([max_units][n]) plus the selected pairs' corrections (from the route of the
+// leaves, leaf = group * n + expert, and the primary selection sel1
+// that gives each token's rank of the group) are reduced per group into
+// load [groups * n].
 int gate_tile_rows(const GateLaunch& g);
 int64_t gate_max_units(int64_t rows, int groups, int tile_rows);
 hipError_t launch_group_plan(const int32_t* offsets, int groups, int tile_rows, int32_t* units,
                              int32_t* unit_start, hipStream_t s);
 hipError_t launch_load_grouped(const GateLaunch& g, int groups, const int32_t* unit_start,
-                               const int32_t* topk_idx, const float* thresh, float* partial,
-                               float* load, hipStream_t s);
+                               const float* thresh, const int32_t* leaf_offsets,
+                               const int32_t* leaf_perm_token, const int32_t* sel1, int k1,
+                               float* partial, float* corr, float* load, hipStream_t s);
 
 // Routing.
 int route_blocks(int64_t tokens);
@@ -99,6 +106,7 @@ hipError_t launch_hier_leaf_load(int a, int b, const float* load1, const float* 
 
 // Load as the hard count (train = 0) and the CV^2 losses.
 hipError_t launch_counts_to_load(const int32_t* counts, int n, float* load, hipStream_t s);
+hipError_t launch_offsets_to_load(const int32_t* offsets, int n, float* load, hipStream_t s);
 hipError_t launch_cv2_losses(const float* importance, const float* load, int n, float w_imp,
                              float w_load, float* losses, hipStream_t s);
 

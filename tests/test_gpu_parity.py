@@ -194,9 +194,9 @@ def test_aux_losses_parity(case, train):
     load_ref = oracle.load(inp, w.k, train=train, noise_floor=FLOOR)
     g = gpu_inputs(inp)
     load, losses = moe.moe_aux_losses(
-        g["x"], g["w_gate"], g["w_noise"], to_device(ref["topk_idx"]),
-        to_device(ref["thresh"].astype(np.float32)), to_device(rt["counts"]),
-        to_device(rt["importance"].astype(np.float32)), train=train, noise_floor=FLOOR,
+        g["x"], g["w_gate"], g["w_noise"], to_device(ref["thresh"].astype(np.float32)),
+        to_device(rt["offsets"]), to_device(rt["perm_token"]),
+        to_device(rt["importance"].astype(np.float32)), w.k, train=train, noise_floor=FLOOR,
         w_importance=0.1, w_load=0.3, gate_bias=g.get("gate_bias"))
     torch.cuda.synchronize()
     err = rel_err(to_host(load), load_ref)
