@@ -168,6 +168,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
     for (int kb = 0; kb < NKB1; ++kb) {
       const U16 a = pa[kb % PF1];
       if (kb + PF1 < NKB1) pa[kb % PF1] = ld_unit(w1_at(hc, kb + PF1));
+      // keep the prefetches where they are issued (the scheduler would
+      // otherwise sink them next to their use under register pressure)
+      __builtin_amdgcn_sched_barrier(0);
       if (kb == (NKB1 > PF1 ? NKB1 - PF1 : 0)) {
 #pragma unroll
         for (int j = 0; j < PF2; ++j)
@@ -232,6 +235,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 #pragma unroll
         for (int j = 0; j < PF1; ++j) pa[j] = ld_unit(w1_at(hc + S::HC, j));
       }
+      __builtin_amdgcn_sched_barrier(0);
       const int c = kb * 2 + hi;
       U16 a[S::TT];
 #pragma unroll

@@ -67,6 +67,34 @@ def test_gate_parity(case, train):
           "swapped", len(stats["swapped"]))
 
 
+@pytest.mark.parametrize("case", [("flat_bf16_n4096", {"tokens": 1000, "n_experts": 512}),
+                                  ("tiny_fp32", {"tokens": 300, "n_experts": 37, "k": 3})],
+                         ids=["bf16-n512", "fp32-n37"])
+def test_gate_and_load_with_noise_floor_zero(case):
+    """sigma = Softplus(u) with no floor (eq 4 as written): sigma can be tiny, which
+    stresses the relative accuracy of Softplus and of the Phi argument."""
+    name, kw = case
+    w = wl(name, **kw)
+    announce(f"moe_gate / moe_aux_losses {w.name} {kw} noise_floor=0")
+    inp = dg.make_inputs(w, experts=False)
+    ref = oracle.gate(inp, w.k, noise_floor=0.0, want_logits=True)
+    g = gpu_inputs(inp)
+    idx, gate, thr = moe.moe_gate(g["x"], g["w_gate"], g["w_noise"], g["eps"], w.k,
+                                  noise_floor=0.0)
+    torch.cuda.synchronize()
+    check_gating(ref, ref["H"], to_host(idx), to_host(gate), to_host(thr))
+    rt = oracle.route(ref["topk_idx"], ref["topk_gate"], w.n_experts)
+    load, losses = moe.moe_aux_losses(
+        g["x"], g["w_gate"], g["w_noise"], to_device(ref["thresh"].astype(np.float32)),
+        to_device(rt["offsets"]), to_device(rt["perm_token"]),
+        to_device(rt["importance"].astype(np.float32)), w.k, noise_floor=0.0)
+    torch.cuda.synchronize()
+    load_ref = oracle.load(inp, w.k, noise_floor=0.0)
+    err = rel_err(to_host(load), load_ref)
+    print(w.name, kw, "floor 0 load err", err)
+    assert err <= GATE_TOL
+
+
 def _random_topk(B, n, k, seed, skew=0.0):
     rng = np.random.default_rng(seed)
     if skew == 0.0:
