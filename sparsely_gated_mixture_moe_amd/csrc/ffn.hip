@@ -14,7 +14,8 @@
 //                                      lane), X^T comes from LDS;
 //       bias + ReLU, round to the storage type, stage Hc in LDS;
 //       GEMM2  Out += Hc . W2[:, chunk]^T  W2 rows stream from HBM into the B
-//                                         operands; Out stays in registers;
+//                                         operands (64 contiguous bytes per lane
+//                                         per load); Out stays in registers;
 //   * add b2 and write the rows to expert_out in segment order.
 // Every expert weight is read from HBM once per work unit; with ~64 rows per
 // expert (4096 experts, k = 4, 65536 tokens) the kernel is bound by streaming
@@ -34,8 +35,7 @@ struct FfnShape {
   // weights once; fp32 keeps its x tile within 64 KB of LDS
   static constexpr int BM = sizeof(T) == 2 ? 96 : (D >= 512 ? 32 : 64);
   static constexpr int T16 = BM / 16;                    // 16-row token tiles (GEMM1)
-  static constexpr int TT = BM / 32;                     // 32-row token tiles (GEMM2)
-  static constexpr int CT2 = D / 32 / NW;                // 32-col output tiles per wave
+  static constexpr int CT2 = D / 16 / NW;                // 16-col output tiles per wave
   static constexpr int UE = Elem<T>::kPerUnit;
   static constexpr int XU = D / UE;                      // 16-byte units per x row
   static constexpr int HU = HC / UE;                     // units per hidden-chunk row
@@ -102,20 +102,16 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const T* w1e = reinterpret_cast<const T*>(p.w1) + (int64_t)e * h * D;
   const T* w2e = reinterpret_cast<const T*>(p.w2) + (int64_t)e * D * h;
 
-  f32x16 acc2[S::TT][S::CT2];
+  f32x4 acc2[S::T16][S::CT2];
 #pragma unroll
-  for (int tt = 0; tt < S::TT; ++tt)
+  for (int tt = 0; tt < S::T16; ++tt)
 #pragma unroll
-    for (int i = 0; i < S::CT2; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc2[tt][i][j] = 0.f;
+    for (int i = 0; i < S::CT2; ++i) acc2[tt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Weight streaming: W1/W2 fragments go from HBM straight into registers
   // through two prefetch rings (PF1 K-blocks of W1, PF2 K-blocks of W2 ahead
@@ -124,27 +120,59 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   //
   // GEMM1 runs on 16x16 tiles: wave w owns hidden units hc + 16 w + (0..15)
   // (A operand, a row of W1 per lane) against all BM tokens (B operand from the
-  // x tile); GEMM2 runs on 32x32 tiles: wave w owns output columns
-  // [32 CT2 w, 32 CT2 (w + 1)) for all tokens.
+  // x tile); GEMM2 runs on 16x16 tiles too: wave w owns output columns
+  // [16 CT2 w, 16 CT2 (w + 1)) for all tokens (B operand: a W2 row per lane,
+  // 64 contiguous bytes of it per load), Hc tiles from LDS as A operands.
   constexpr int NKB1 = D / (4 * UE);
-  constexpr int NKB2 = S::HC / (2 * UE);
+  constexpr int NKB2 = S::HC / (4 * UE);
   constexpr int PF1 = NKB1 < 7 ? NKB1 : 7;
-  constexpr int PF2 = NKB2 < 3 ? NKB2 : 3;
+  constexpr int PF2 = NKB2 < 2 ? NKB2 : 2;
   const int l16 = lane & 15;
   const int q = lane >> 4;
   const int nch = h / S::HC;
+  // Addresses: a wave-uniform base (scalar registers) plus one 32-bit byte
+  // offset per lane and stream, so the prefetch rings cost no 64-bit vector
+  // address registers.
+  const char* w1w = reinterpret_cast<const char*>(w1e + (int64_t)16 * wave * D);
+  const char* w2w = reinterpret_cast<const char*>(w2e + (int64_t)16 * S::CT2 * wave * h);
+  const uint32_t o1 = (uint32_t)((l16 * D + q * UE) * (int)sizeof(T));
+  const uint32_t o2 = (uint32_t)((l16 * h + q * UE) * (int)sizeof(T));
   auto w1_at = [&](int hc, int kb) {
-    return w1e + (int64_t)(hc + 16 * wave + l16) * D + (kb * 4 + q) * UE;
+    return ld_unit(w1w + ((int64_t)hc * D + kb * 4 * UE) * (int64_t)sizeof(T) + o1);
   };
   auto w2_at = [&](int hc, int kb, int i) {
-    return w2e + (int64_t)((wave * S::CT2 + i) * 32 + l32) * h + hc + kb * 2 * UE + hi * UE;
+    return ld_unit(w2w + ((int64_t)i * 16 * h + hc + kb * 4 * UE) * (int64_t)sizeof(T) + o2);
   };
+  // b1 of the lane's 4 hidden units of a chunk travels with the chunk's first
+  // W1 fragments, so the bias never waits on a load issued next to its use.
+  constexpr int BW = sizeof(T) == 2 ? 2 : 4;
+  struct B1 { uint32_t w[BW]; };
+  const bool has_b1 = p.b1 != nullptr;
+  const char* b1w = has_b1 ? reinterpret_cast<const char*>(p.b1) +
+                                ((int64_t)e * h + 16 * wave) * (int64_t)sizeof(T)
+                          : nullptr;
+  const uint32_t ob = (uint32_t)(4 * q * (int)sizeof(T));
+  auto b1_at = [&](int hc) {
+    B1 v;
+    if constexpr (BW == 2) {
+      const uint2 u = *reinterpret_cast<const uint2*>(b1w + (int64_t)hc * sizeof(T) + ob);
+      v.w[0] = u.x;
+      v.w[1] = u.y;
+    } else {
+      const U16 u = ld_unit(b1w + (int64_t)hc * sizeof(T) + ob);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v.w[i] = u.w[i];
+    }
+    return v;
+  };
+  B1 b1r{};
   U16 pa[PF1];
   U16 pb[PF2][S::CT2];
   // The first W1 fragments are requested before the gather, so the weight
   // stream is already in flight while the rows of x arrive.
 #pragma unroll
-  for (int j = 0; j < PF1; ++j) pa[j] = ld_unit(w1_at(0, j));
+  for (int j = 0; j < PF1; ++j) pa[j] = w1_at(0, j);
+  if (has_b1) b1r = b1_at(0);
 
   // Gather the unit's rows of x.
   for (int u = tid; u < S::BM * S::XU; u += NT) {
@@ -167,7 +195,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 #pragma unroll
     for (int kb = 0; kb < NKB1; ++kb) {
       const U16 a = pa[kb % PF1];
-      if (kb + PF1 < NKB1) pa[kb % PF1] = ld_unit(w1_at(hc, kb + PF1));
+      if (kb + PF1 < NKB1) pa[kb % PF1] = w1_at(hc, kb + PF1);
       // keep the prefetches where they are issued (the scheduler would
       // otherwise sink them next to their use under register pressure)
       __builtin_amdgcn_sched_barrier(0);
@@ -175,7 +203,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 #pragma unroll
         for (int j = 0; j < PF2; ++j)
 #pragma unroll
-          for (int i = 0; i < S::CT2; ++i) pb[j][i] = ld_unit(w2_at(hc, j, i));
+          for (int i = 0; i < S::CT2; ++i) pb[j][i] = w2_at(hc, j, i);
       }
       const int c = kb * 4 + q;
 #pragma unroll
@@ -190,10 +218,13 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
     // 16 tt + l % 16 and the 4 consecutive hidden units 16 w + 4 (l / 16) + r.
     {
       const int hl = 16 * wave + 4 * q;
-      float bias[4] = {0.f, 0.f, 0.f, 0.f};
-      if (p.b1) {
+      float bias[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bias[i] = load_scalar<T>(p.b1, (int64_t)e * h + hc + hl + i);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (BW == 2)
+          bias[i] = bf16_bits_to_f32((b1r.w[i / 2] >> (16 * (i % 2))) & 0xffffu);
+        else
+          bias[i] = __uint_as_float(b1r.w[i]);
       }
       const int cu = hl / UE;
 #pragma unroll
@@ -229,37 +260,36 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
       for (int i = 0; i < S::CT2; ++i) b[i] = pb[kb % PF2][i];
       if (kb + PF2 < NKB2) {
 #pragma unroll
-        for (int i = 0; i < S::CT2; ++i) pb[kb % PF2][i] = ld_unit(w2_at(hc, kb + PF2, i));
+        for (int i = 0; i < S::CT2; ++i) pb[kb % PF2][i] = w2_at(hc, kb + PF2, i);
       }
       if (kb == (NKB2 > PF2 ? NKB2 - PF2 : 0) && ch + 1 < nch) {
 #pragma unroll
-        for (int j = 0; j < PF1; ++j) pa[j] = ld_unit(w1_at(hc + S::HC, j));
+        for (int j = 0; j < PF1; ++j) pa[j] = w1_at(hc + S::HC, j);
+        if (has_b1) b1r = b1_at(hc + S::HC);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const int c = kb * 2 + hi;
-      U16 a[S::TT];
+      const int c = kb * 4 + q;
 #pragma unroll
-      for (int tt = 0; tt < S::TT; ++tt) {
-        const int r = tt * 32 + l32;
-        a[tt] = hs[r * S::HU + (c ^ (r & (S::HSW - 1)))];
+      for (int tt = 0; tt < S::T16; ++tt) {
+        const int r = tt * 16 + l16;
+        const U16 a = hs[r * S::HU + (c ^ (r & (S::HSW - 1)))];
+#pragma unroll
+        for (int i = 0; i < S::CT2; ++i) Mfma<T>::k16(acc2[tt][i], a, b[i]);
       }
-#pragma unroll
-      for (int i = 0; i < S::CT2; ++i)
-#pragma unroll
-        for (int tt = 0; tt < S::TT; ++tt) Mfma<T>::k32(acc2[tt][i], a[tt], b[i]);
     }
   }
 
-  // b2, then write the rows in segment order.
+  // b2, then write the rows in segment order (lane: column l % 16 of each tile,
+  // token rows 4 (l / 16) + j).
 #pragma unroll
   for (int i = 0; i < S::CT2; ++i) {
-    const int col = (wave * S::CT2 + i) * 32 + l32;
+    const int col = (wave * S::CT2 + i) * 16 + l16;
     const float bias = p.b2 ? load_scalar<T>(p.b2, (int64_t)e * D + col) : 0.f;
 #pragma unroll
-    for (int tt = 0; tt < S::TT; ++tt)
+    for (int tt = 0; tt < S::T16; ++tt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int tok = tt * 32 + 8 * (j / 4) + 4 * hi + (j % 4);
+      for (int j = 0; j < 4; ++j) {
+        const int tok = tt * 16 + 4 * q + j;
         if (tok < rows) store_scalar<T>(p.out, (seg + tok) * D + col, acc2[tt][i][j] + bias);
       }
   }
