@@ -128,14 +128,16 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds_b
 // Fast reciprocal (v_rcp_f32, about 1 ulp).
 __device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// log(1 + t) for t in [0, 1] to a few ulp with one native log: with
-// w = 1 + t rounded, log(w) * t / (w - 1) cancels the rounding error of w
-// (Kahan's method; Goldberg, "What every computer scientist should know about
-// floating-point arithmetic", 1991, Theorem 4).
+// log(1 + t) for t in [0, 1] with one native log2: w = 1 + t is rounded, but
+// w - 1 is exact (Sterbenz), so the rounding error d = t - (w - 1) is known
+// exactly and log(1 + t) = log(w) + log(1 + d / w). Taking d for the last term
+// errs by |d| (w - 1) / w <= 2^-24 t, a relative error below 2^-23 (the
+// compensated-summation idea of Kahan; Goldberg, "What every computer
+// scientist should know about floating-point arithmetic", 1991).
 __device__ __forceinline__ float log1p_small(float t) {
-  const float w = 1.0f + t;  // in [1, 2]: the native log2 needs no range reduction
-  const float lw = __builtin_amdgcn_logf(w) * 0.69314718055994531f;
-  return (w == 1.0f) ? t : lw * t * rcp_f(w - 1.0f);
+  const float w = 1.0f + t;
+  const float d = t - (w - 1.0f);
+  return fmaf(__builtin_amdgcn_logf(w), 0.69314718055994531f, d);
 }
 
 // e^x through the native 2^x (v_exp_f32); arguments are <= 0 here.
@@ -143,33 +145,34 @@ __device__ __forceinline__ float exp_native(float x) {
   return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
 }
 
-// Softplus(u) = log(1 + e^u) = max(u, 0) + log(1 + e^-|u|), which cannot overflow.
+// Softplus(u) = log(1 + e^u) = max(u, 0) + log(1 + e^-|u|), which cannot
+// overflow; max(u, 0) = (u + |u|) / 2 rides on the final multiply-add. u must
+// be finite.
 __device__ __forceinline__ float softplus_f(float u) {
-  return fmaxf(u, 0.0f) + log1p_small(exp_native(-fabsf(u)));
+  return fmaf(u + fabsf(u), 0.5f, log1p_small(exp_native(-fabsf(u))));
 }
 
-// erfc(x) for x >= 0 by the Chebyshev fit of Numerical Recipes (Press et al.,
-// 2nd ed., section 6.2, "erfcc"): fractional error below 1.2e-7 everywhere.
-__device__ __forceinline__ float erfc_nonneg(float x) {
-  const float t = rcp_f(1.0f + 0.5f * x);
-  float p = 0.17087277f;
-  p = fmaf(t, p, -0.82215223f);
-  p = fmaf(t, p, 1.48851587f);
-  p = fmaf(t, p, -1.13520398f);
-  p = fmaf(t, p, 0.27886807f);
-  p = fmaf(t, p, -0.18628806f);
-  p = fmaf(t, p, 0.09678418f);
-  p = fmaf(t, p, 0.37409196f);
-  p = fmaf(t, p, 1.00002368f);
-  p = fmaf(t, p, -1.26551223f);
-  return t * exp_native(fmaf(-x, x, p));
-}
-
-// Standard normal CDF: Phi(z) = erfc(-z / sqrt 2) / 2, using
-// erfc(-a) = 2 - erfc(a) for the upper half.
+// Standard normal CDF from the Chebyshev fit of erfc in Numerical Recipes
+// (Press et al., 2nd ed., section 6.2, "erfcc"; fractional error below 1.2e-7
+// everywhere): with a = |z| / sqrt 2 and t = 1 / (1 + a / 2),
+// erfc(a) = t exp(-a^2 + P(t)). Here h = erfc(a) / 2 is evaluated as
+// t 2^(Q(t) - z^2 log2(e) / 2) with Q = log2(e) P - 1 (the fit's coefficients
+// times log2 e, the constant term lowered by one for the halving), and
+// Phi(z) = h for z < 0, 1 - h otherwise (erfc(-a) = 2 - erfc(a)).
 __device__ __forceinline__ float phi_f(float z) {
-  const float a = fabsf(z) * 0.70710678118654752f;
-  const float h = 0.5f * erfc_nonneg(a);
+  constexpr float L2E = 1.44269504088896341f;
+  const float t = rcp_f(fmaf(fabsf(z), 0.35355339059327376f, 1.0f));
+  float q = 0.17087277f * L2E;
+  q = fmaf(t, q, -0.82215223f * L2E);
+  q = fmaf(t, q, 1.48851587f * L2E);
+  q = fmaf(t, q, -1.13520398f * L2E);
+  q = fmaf(t, q, 0.27886807f * L2E);
+  q = fmaf(t, q, -0.18628806f * L2E);
+  q = fmaf(t, q, 0.09678418f * L2E);
+  q = fmaf(t, q, 0.37409196f * L2E);
+  q = fmaf(t, q, 1.00002368f * L2E);
+  q = fmaf(t, q, -1.26551223f * L2E - 1.0f);
+  const float h = t * __builtin_amdgcn_exp2f(fmaf(z * (-0.5f * L2E), z, q));
   return z < 0.0f ? h : 1.0f - h;
 }
 

@@ -67,6 +67,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // pass 1: each wave's transpose tile, double-buffered by chunk parity
   __shared__ float hbuf[PASS2 ? 1 : 2][PASS2 ? 1 : kG32Waves][32 * kG32HStride];
   __shared__ float thrbuf[PASS2 ? kG32Rows : 1];  // pass 2: each row's k-th logit
+  // pass 2: each wave's copy of a chunk's 16 biases, double-buffered by chunk parity
+  __shared__ float bbuf[PASS2 ? 2 : 1][PASS2 ? kG32Waves * kG32Chunk : 1];
   __shared__ float red[PASS2 ? 2 : 1][kG32Waves][EC];
 
   const int tid = threadIdx.x;
@@ -130,8 +132,12 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   };
   const bool has_bias = p.bias != nullptr;
   const float* bias_src = has_bias ? p.bias : reinterpret_cast<const float*>(p.wg);
-  auto load_bias = [&](int c, float& bv) {
-    if (has_bias) bv = bias_src[c * EC + (l32 & 15)];
+  // Pass 2: lanes 0-3 copy chunk c's biases (or, without a bias, any
+  // in-bounds floats, which are never read) into this wave's slot. A copy, not
+  // a register load, so that no compiler-inserted wait on the memory counter
+  // stalls the epilogue behind the weight copies in flight.
+  auto dma_bias = [&](int c, int slot) {
+    if (lane < 4) copy16_to_lds(bias_src + c * EC + 4 * lane, &bbuf[slot][wave * EC]);
   };
   // One chunk's products: 32 x 32 tile of (rows, clean|noise columns) over
   // the K-blocks. Fragments are read four ahead of their matrix product; the
@@ -209,15 +215,14 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   const int nchunks = (n + EC - 1) / EC;
   // Accumulators of two consecutive chunks: pass P reads accs[P] (its own
   // chunk's products) and fills accs[P ^ 1] (the next chunk's); the same for
-  // pass 2's biases.
+  // pass 2's bias slots.
   f32x16 accs[2];
-  float bvs[2] = {0.f, 0.f};
   dma(0, wbuf0);
   if (nchunks > 1) dma(1, wbuf1);
   if constexpr (!PASS2) {
     for (int c = 0; c < 2 && c < nchunks; ++c) dma_eps(c, c);
   }
-  if constexpr (PASS2) load_bias(0, bvs[0]);
+  if constexpr (PASS2) dma_bias(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   mfma_chunk(wbuf0, accs[0]);
@@ -239,13 +244,15 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     U16* const wfill = P ? wbuf1 : wbuf0;       // buffer c & 1: chunk c + 2 goes here
     const U16* const wnext = P ? wbuf0 : wbuf1;  // buffer (c + 1) & 1: chunk c + 1
     f32x16& acc = accs[P];
-    // Copies issued this pass, oldest first: (pass 2) chunk c + 1's bias into
-    // registers, chunk c + 2's weights into buffer c & 1 (whose chunk c every
+    // Copies issued this pass, oldest first: (pass 2) chunk c + 1's biases into
+    // bias slot P ^ 1, chunk c + 2's weights into buffer c & 1 (whose chunk c every
     // wave used before the last barrier), and (pass 1) chunk c + 2's noise
     // draws and biases into ring slot (c + 2) % 3 (chunk c - 1's, used in the
     // last pass). The weights must land by the end of this pass; the noise
     // draws have one more pass.
-    if constexpr (PASS2) load_bias(c + 1 < nchunks ? c + 1 : c, bvs[P ^ 1]);
+    if constexpr (PASS2) {
+      if (c + 1 < nchunks) dma_bias(c + 1, P ^ 1);
+    }
     if (c + 2 < nchunks) dma(c + 2, wfill);
     asm volatile("" ::: "memory");
     if constexpr (!PASS2) {
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       }
       float bias;
       if constexpr (PASS2) {
-        bias = has_bias ? bvs[P] : 0.f;
+        bias = has_bias ? bbuf[P][wave * EC + (l32 & 15)] : 0.f;
       } else {
         bias = has_bias ? ebuf[c % 3][kG32Rows * EC + wave * EC + (l32 & 15)] : 0.f;
       }
