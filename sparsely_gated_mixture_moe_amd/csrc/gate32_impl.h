@@ -11,8 +11,10 @@
 //    is copied HBM/L2 -> LDS with global_load_lds_dwordx4 (no staging
 //    registers) into a double buffer, each 1 KB fragment in lane order;
 //  * every fragment read from LDS feeds one 32x32x16 MFMA (32 flop per LDS byte);
-//  * each pass issues the next chunk's matrix products before this chunk's
-//    epilogue, so the matrix cores and the vector ALUs overlap.
+//  * each pass computes the next chunk's matrix products while this chunk's
+//    epilogue runs on the vector ALUs: pass 1 issues the products first, pass
+//    2 weaves its per-pair work between them (measured faster for pass 2's
+//    longer per-pair work; pass 1's epilogue reads LDS and branches).
 //
 // Epilogue. In the 32x32 C layout lane l holds column l % 32 for 16 rows: the
 // clean logit (columns 0-15) or the noise pre-activation (16-31) of one expert.
@@ -24,7 +26,7 @@
 // (H, expert), and rarely needs to insert once its list is warm. Lanes l and
 // l ^ 32 (the two halves of a row) merge at the end. The noise draws and
 // biases ride a three-slot LDS ring two chunks ahead. Pass 2 evaluates
-// P = Phi((clean - v_k) / sigma) in place and sums each expert's column over
+// P = Phi((clean - v_k) / sigma) in place (after the exchange) and sums each expert's column over
 // the block's rows in a fixed order (the selected pairs are corrected to the
 // (k+1)-th threshold separately).
 #pragma once
@@ -45,6 +47,10 @@ template <int V>
 struct IntConst {
   static constexpr int value = V;
 };
+
+// Vector instructions of one Load-pass pair (exchange, Softplus, Phi, sum):
+// the scheduler spreads this many over the matrix products that precede it.
+constexpr int kG32PhiValu = 30;
 
 template <int D, int L, bool PASS2>
 __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
@@ -261,6 +267,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
 
     float colsum = 0.f;
     float hpair[8];
+    // Selection pass: the next chunk's products, then this chunk's epilogue.
     auto products = [&]() { mfma_chunk(wnext, accs[P ^ 1]); };
     auto epilogue = [&]() {
       // Exchange within each pair of 16-lane rows: the odd row's (noise
@@ -276,22 +283,11 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         cl[i] = __uint_as_float(sw[0]);
         un[i] = __uint_as_float(sw[1]);
       }
-      float bias;
-      if constexpr (PASS2) {
-        bias = has_bias ? bbuf[P][wave * EC + (l32 & 15)] : 0.f;
-      } else {
-        bias = has_bias ? ebuf[c % 3][kG32Rows * EC + wave * EC + (l32 & 15)] : 0.f;
-      }
+      const float bias = has_bias ? ebuf[c % 3][kG32Rows * EC + wave * EC + (l32 & 15)] : 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float clean = cl[i] + bias;
-        if constexpr (!PASS2) {
-          const float eps = ebuf[c % 3][(wave * 32 + rr[i]) * EC + (l32 & 15)];
-          hpair[i] = fmaf(eps, softplus_f(un[i]) + p.floor, clean);
-        } else {
-          const float sigma = softplus_f(un[i]) + p.floor;
-          colsum += phi_f((clean - thrk[i]) * rcp_f(sigma));
-        }
+        const float eps = ebuf[c % 3][(wave * 32 + rr[i]) * EC + (l32 & 15)];
+        hpair[i] = fmaf(eps, softplus_f(un[i]) + p.floor, cl[i] + bias);
       }
     };
     // Pass 1 transposes H through this wave's LDS tile and lets each lane scan
@@ -327,14 +323,62 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         if (lane < 16) red[P][wave][lane] = colsum;
       }
     };
-    // The next chunk's products go first: their matrix operations run while
-    // this chunk's epilogue occupies the vector ALUs.
-    products();
-    __builtin_amdgcn_sched_barrier(0);
-    read_prev();
-    epilogue();
-    insert_prev();
-    finish();
+    if constexpr (PASS2) {
+      // Load pass: the next chunk's products with this chunk's pairs woven
+      // in, one pair after every eighth of the products, so that each pair's
+      // vector work issues while the matrix core is busy.
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      typedef const __attribute__((address_space(3))) u32x4* LdsPtr;
+      uint32_t base = (uint32_t)(uintptr_t)(wnext + lane);
+      asm("" : "+v"(base));
+      const LdsPtr bl = (LdsPtr)base;
+      u32x4 f[FPF];
+#pragma unroll
+      for (int j = 0; j < FPF; ++j) f[j] = bl[j * 64];
+      f32x16& an = accs[P ^ 1];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) an[j] = 0.f;
+      const float bias = has_bias ? bbuf[P][wave * EC + (l32 & 15)] : 0.f;
+      constexpr int MPE = NKB / 8;
+      static_assert(NKB % 8 == 0, "whole K-blocks per pair");
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < MPE; ++j) {
+          const int kb = i * MPE + j;
+          U16 cur;
+          __builtin_memcpy(&cur, &f[kb % FPF], 16);
+          if (kb + FPF < NKB) f[kb % FPF] = bl[(kb + FPF) * 64];
+          Mfma<bf16>::k32(an, xa[kb], cur);
+        }
+        // the exchange of the selection epilogue, then P of pair i
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i]),
+                                                          __float_as_uint(acc[8 + i]), false, false);
+        const float clean = __uint_as_float(sw[0]) + bias;
+        const float sigma = softplus_f(__uint_as_float(sw[1])) + p.floor;
+        colsum += phi_f((clean - thrk[i]) * rcp_f(sigma));
+      }
+      // reads ahead, then (product, read, vector work) triples
+      constexpr int V = (kG32PhiValu + MPE - 1) / MPE;
+      __builtin_amdgcn_sched_group_barrier(0x100, FPF, 0);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (kb + FPF < NKB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      finish();
+    } else {
+      // Selection pass: the next chunk's products go first; their matrix
+      // operations run while this chunk's epilogue occupies the vector ALUs.
+      products();
+      __builtin_amdgcn_sched_barrier(0);
+      read_prev();
+      epilogue();
+      insert_prev();
+      finish();
+    }
 
     // Block barrier without a release fence (which would wait for every copy
     // in flight): each wave first waits for its LDS traffic and for all its
