@@ -99,10 +99,10 @@ def cpu_baseline(w, inp, target_s):
 
     S = 256
     t = run(S)
-    # grow the sample until one run takes at least half the target (fixed costs
-    # make the first estimate low)
-    while t < target_s / 2 and S < w.tokens:
-        S = int(min(w.tokens, max(2 * S, S * target_s / max(t, 1e-3))))
+    # grow the sample until one run takes at least 80 % of the target (fixed
+    # costs make the small-sample estimates low)
+    while t < 0.8 * target_s and S < w.tokens:
+        S = int(min(w.tokens, max(2 * S, S * 1.05 * target_s / max(t, 1e-3))))
         t = run(S)
     threads = oracle.threads()
     return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -227,7 +227,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="flat_bf16_n4096")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target length of the oracle CPU-baseline run (0 skips it)")
     ap.add_argument("--stage-iters", type=int, default=10)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -125,6 +125,18 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds_b
       : "memory");
 }
 
+// The same with 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes
+// land at lds_base + 4 l.
+__device__ __forceinline__ void copy4_to_lds(const void* src, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(src), "{m0}"(m0)
+      : "memory");
+}
+
 // Fast reciprocal (v_rcp_f32, about 1 ulp).
 __device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x); }
 

@@ -21,6 +21,8 @@
 // expert (4096 experts, k = 4, 65536 tokens) the kernel is bound by streaming
 // the expert weights, the shrinking-batch regime of "Keeping each expert's
 // batch large".
+#include <algorithm>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -54,9 +56,22 @@ struct FfnParams {
   const void* w2;
   const void* b2;
   void* out;
-  const int32_t* blocks;  // [0] = count, then (expert, first row) pairs
+  const int32_t* blocks;  // [0] = count; from [4] on, 16 bytes per unit (FfnUnit)
   int h;
 };
+
+// Global-memory byte pointer: loads through it are global (not flat) loads
+// even after the pointer has passed through an asm statement.
+typedef const __attribute__((address_space(1))) char* GPtr;
+__device__ __forceinline__ GPtr gptr(const void* p) { return (GPtr)(p); }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ U16 ld_unit_g(GPtr p) {
+  const u32x4 v = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(p);
+  U16 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
 
 template <typename T>
 __device__ __forceinline__ float load_scalar(const void* p, int64_t i) {
@@ -76,47 +91,84 @@ __device__ __forceinline__ void store_scalar(void* p, int64_t i, float v) {
   }
 }
 
+// DPP quad permutation (lanes 4m..4m+3 exchange values): xor 1 and xor 2.
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// 4x4 transpose within each quad of lanes: lane c of the quad holds x[j] =
+// M[c][j] before and M[j][c] after.
+__device__ __forceinline__ void quad_transpose(f32x4& x, int c) {
+  const bool odd = c & 1, hi = c & 2;
+  const float r0 = quad_xor1(odd ? x[0] : x[1]);
+  const float r2 = quad_xor1(odd ? x[2] : x[3]);
+  if (odd) {
+    x[0] = r0;
+    x[2] = r2;
+  } else {
+    x[1] = r0;
+    x[3] = r2;
+  }
+  const float s0 = quad_xor2(hi ? x[0] : x[2]);
+  const float s1 = quad_xor2(hi ? x[1] : x[3]);
+  if (hi) {
+    x[0] = s0;
+    x[1] = s1;
+  } else {
+    x[2] = s0;
+    x[3] = s1;
+  }
+}
+
+// A work unit as the planning kernel lists it (16 bytes).
+struct FfnUnit {
+  int32_t e, seg, rows, pad;
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__((FfnShape<T, D>::NW * 64))
 __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   using S = FfnShape<T, D>;
-  constexpr int NT = S::NW * 64;
   constexpr int UE = S::UE;
   __shared__ U16 xs[S::BM * S::XU];
   __shared__ U16 hs[S::BM * S::HU];
+  __shared__ int32_t tokbuf[S::BM];  // token of each row of the unit whose rows come next
 
-  // XCD-aware placement: workgroups are dealt to the 8 XCDs round-robin, so
-  // XCD x = blockIdx % 8 takes the x-th eighth of the unit list in order and
-  // the units of one expert run back to back on one L2.
+  // Persistent workgroups. Workgroups are dealt to the 8 XCDs round-robin, so
+  // workgroup b runs on XCD b % 8; it takes every (G / 8)-th unit of that
+  // XCD's eighth of the unit list, starting at b / 8. The units of one expert
+  // are adjacent in the list, so they run at the same time on one L2.
   const int count = p.blocks[0];
   const int per_xcd = (count + 7) / 8;
-  const int slot = blockIdx.x / 8;
-  const int blk = (blockIdx.x % 8) * per_xcd + slot;
-  if (slot >= per_xcd || blk >= count) return;
-  const int e = p.blocks[1 + 2 * blk];
-  const int row0 = p.blocks[2 + 2 * blk];
-  const int seg0 = p.offsets[e];
-  const int rows = min(S::BM, p.offsets[e + 1] - seg0 - row0);
-  const int64_t seg = (int64_t)seg0 + row0;
+  const int xcd = blockIdx.x % 8;
+  const int nslot = gridDim.x / 8;
+  auto valid = [&](int j) { return j < per_xcd && xcd * per_xcd + j < count; };
+  const FfnUnit* units = reinterpret_cast<const FfnUnit*>(p.blocks + 4);
+  // a unit's description, loaded by every lane, moved to scalar registers
+  auto uniform_unit = [&](const FfnUnit& v) {
+    FfnUnit u;
+    u.e = __builtin_amdgcn_readfirstlane(v.e);
+    u.seg = __builtin_amdgcn_readfirstlane(v.seg);
+    u.rows = __builtin_amdgcn_readfirstlane(v.rows);
+    u.pad = 0;
+    return u;
+  };
+  int j = blockIdx.x / 8;
+  if (!valid(j)) return;
   const int h = p.h;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const T* w1e = reinterpret_cast<const T*>(p.w1) + (int64_t)e * h * D;
-  const T* w2e = reinterpret_cast<const T*>(p.w2) + (int64_t)e * D * h;
-
-  f32x4 acc2[S::T16][S::CT2];
-#pragma unroll
-  for (int tt = 0; tt < S::T16; ++tt)
-#pragma unroll
-    for (int i = 0; i < S::CT2; ++i) acc2[tt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   // Weight streaming: W1/W2 fragments go from HBM straight into registers
   // through two prefetch rings (PF1 K-blocks of W1, PF2 K-blocks of W2 ahead
-  // of use). The next phase's first fragments are requested before each
-  // barrier, so the loads stay in flight across the barriers.
+  // of use). The next phase's first fragments (across units too) are
+  // requested before each barrier, so the loads stay in flight across the
+  // barriers.
   //
   // GEMM1 runs on 16x16 tiles: wave w owns hidden units hc + 16 w + (0..15)
   // (A operand, a row of W1 per lane) against all BM tokens (B operand from the
@@ -125,7 +177,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   // 64 contiguous bytes of it per load), Hc tiles from LDS as A operands.
   constexpr int NKB1 = D / (4 * UE);
   constexpr int NKB2 = S::HC / (4 * UE);
-  constexpr int PF1 = NKB1 < 7 ? NKB1 : 7;
+  constexpr int PF1 = NKB1 < 5 ? NKB1 : 5;
   constexpr int PF2 = NKB2 < 2 ? NKB2 : 2;
   const int l16 = lane & 15;
   const int q = lane >> 4;
@@ -133,169 +185,292 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   // Addresses: a wave-uniform base (scalar registers) plus one 32-bit byte
   // offset per lane and stream, so the prefetch rings cost no 64-bit vector
   // address registers.
-  const char* w1w = reinterpret_cast<const char*>(w1e + (int64_t)16 * wave * D);
-  const char* w2w = reinterpret_cast<const char*>(w2e + (int64_t)16 * S::CT2 * wave * h);
+  auto w1_base = [&](int e) {
+    return gptr(reinterpret_cast<const T*>(p.w1) + ((int64_t)e * h + 16 * wave) * D);
+  };
+  auto w2_base = [&](int e) {
+    return gptr(reinterpret_cast<const T*>(p.w2) + ((int64_t)e * D + 16 * S::CT2 * wave) * h);
+  };
   const uint32_t o1 = (uint32_t)((l16 * D + q * UE) * (int)sizeof(T));
   const uint32_t o2 = (uint32_t)((l16 * h + q * UE) * (int)sizeof(T));
-  auto w1_at = [&](int hc, int kb) {
-    return ld_unit(w1w + ((int64_t)hc * D + kb * 4 * UE) * (int64_t)sizeof(T) + o1);
+  auto w1_at = [&](GPtr w1w, int hc, int kb) {
+    return ld_unit_g(w1w + ((int64_t)hc * D + kb * 4 * UE) * (int64_t)sizeof(T) + o1);
   };
-  auto w2_at = [&](int hc, int kb, int i) {
-    return ld_unit(w2w + ((int64_t)i * 16 * h + hc + kb * 4 * UE) * (int64_t)sizeof(T) + o2);
+  auto w2_at = [&](GPtr w2w, int hc, int kb, int i) {
+    return ld_unit_g(w2w + ((int64_t)i * 16 * h + hc + kb * 4 * UE) * (int64_t)sizeof(T) + o2);
   };
   // b1 of the lane's 4 hidden units of a chunk travels with the chunk's first
   // W1 fragments, so the bias never waits on a load issued next to its use.
+  // Without b1 the same loads read the start of W1 (always there) and the
+  // values are not used, so that no branch separates the prefetches.
   constexpr int BW = sizeof(T) == 2 ? 2 : 4;
-  struct B1 { uint32_t w[BW]; };
+  struct B1 {
+    uint32_t w[BW];
+  };
   const bool has_b1 = p.b1 != nullptr;
-  const char* b1w = has_b1 ? reinterpret_cast<const char*>(p.b1) +
-                                ((int64_t)e * h + 16 * wave) * (int64_t)sizeof(T)
-                          : nullptr;
-  const uint32_t ob = (uint32_t)(4 * q * (int)sizeof(T));
-  auto b1_at = [&](int hc) {
+  const uint32_t ob1 = (uint32_t)(4 * q * (int)sizeof(T));
+  auto b1_at = [&](int e, int hc) {
+    const GPtr b1w = has_b1 ? gptr(reinterpret_cast<const T*>(p.b1) + (int64_t)e * h + 16 * wave + hc)
+                            : gptr(p.w1);
     B1 v;
     if constexpr (BW == 2) {
-      const uint2 u = *reinterpret_cast<const uint2*>(b1w + (int64_t)hc * sizeof(T) + ob);
-      v.w[0] = u.x;
-      v.w[1] = u.y;
+      const u32x2 u = *reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(b1w + ob1);
+      v.w[0] = u[0];
+      v.w[1] = u[1];
     } else {
-      const U16 u = ld_unit(b1w + (int64_t)hc * sizeof(T) + ob);
+      const U16 u = ld_unit_g(b1w + ob1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) v.w[i] = u.w[i];
     }
     return v;
   };
+  // Rows of x of a unit -> the x tile, by global -> LDS copies (no staging
+  // registers): copy g (of BM XU / 64) fills tile units [64 g, 64 g + 64);
+  // lane l's unit is row r = (64 g + l) / XU, slot (64 g + l) % XU, which
+  // holds column slot ^ (r % XSW) of the row (the swizzle of the operand
+  // reads). Rows past the unit's end are not copied: they keep finite values
+  // of an earlier unit (or whatever the tile held), which only reach output
+  // rows that are never written.
+  constexpr int NG = S::BM * S::XU / 64 / S::NW;
+  static_assert(S::BM * S::XU % (64 * S::NW) == 0, "whole copies per wave");
+  auto gather = [&](int rows) {
+    // lane index made opaque, so that the per-copy indexes are recomputed
+    // here rather than kept in registers across units
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int g = wave + S::NW * i;
+      const int u = 64 * g + ln;
+      const int r = u / S::XU;
+      const int slot = u - r * S::XU;
+      if (r < rows) {
+        const int64_t tok = tokbuf[r];
+        copy16_to_lds(reinterpret_cast<const T*>(p.x) + tok * D + (slot ^ (r & (S::XSW - 1))) * UE,
+                      &xs[64 * g]);
+      }
+    }
+  };
+  // Token ids of a unit's rows -> tokbuf, by 4-byte global -> LDS copies
+  // issued by the first (BM + 63) / 64 waves.
+  auto copy_tokens = [&](const FfnUnit& u) {
+    if (wave * 64 < S::BM) {
+      int ln = lane;  // opaque, as in gather()
+      asm volatile("" : "+v"(ln));
+      const int r = wave * 64 + ln;
+      if (r < u.rows) copy4_to_lds(p.perm_token + u.seg + r, &tokbuf[wave * 64]);
+    }
+  };
+  // Waits for this wave's copies: everything older than the last PF1 + 1
+  // loads (the next unit's first W1 fragments and b1), which complete in
+  // issue order.
+  auto wait_copies = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PF1 + 1) : "memory"); };
+
+  FfnUnit u = uniform_unit(units[xcd * per_xcd + j]);
+  GPtr w1w = w1_base(u.e);
   B1 b1r{};
   U16 pa[PF1];
   U16 pb[PF2][S::CT2];
-  // The first W1 fragments are requested before the gather, so the weight
-  // stream is already in flight while the rows of x arrive.
+  // first unit: its tokens, then its rows of x and its first W1 fragments
+  if (tid < u.rows) tokbuf[tid] = p.perm_token[u.seg + tid];
+  __syncthreads();
+  gather(u.rows);
 #pragma unroll
-  for (int j = 0; j < PF1; ++j) pa[j] = w1_at(0, j);
-  if (has_b1) b1r = b1_at(0);
-
-  // Gather the unit's rows of x.
-  for (int u = tid; u < S::BM * S::XU; u += NT) {
-    const int r = u / S::XU;
-    const int c = u - r * S::XU;
-    U16 v = zero_unit();
-    if (r < rows) {
-      const int64_t tok = p.perm_token[seg + r];
-      v = ld_unit(reinterpret_cast<const T*>(p.x) + tok * D + c * UE);
-    }
-    xs[r * S::XU + (c ^ (r & (S::XSW - 1)))] = v;
-  }
+  for (int jj = 0; jj < PF1; ++jj) pa[jj] = w1_at(w1w, 0, jj);
+  b1r = b1_at(u.e, 0);
+  wait_copies();
   __syncthreads();
 
-  for (int ch = 0; ch < nch; ++ch) {
-    const int hc = ch * S::HC;
-    f32x4 acc1[S::T16];
-#pragma unroll
-    for (int tt = 0; tt < S::T16; ++tt) acc1[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKB1; ++kb) {
-      const U16 a = pa[kb % PF1];
-      if (kb + PF1 < NKB1) pa[kb % PF1] = w1_at(hc, kb + PF1);
-      // keep the prefetches where they are issued (the scheduler would
-      // otherwise sink them next to their use under register pressure)
-      __builtin_amdgcn_sched_barrier(0);
-      if (kb == (NKB1 > PF1 ? NKB1 - PF1 : 0)) {
-#pragma unroll
-        for (int j = 0; j < PF2; ++j)
-#pragma unroll
-          for (int i = 0; i < S::CT2; ++i) pb[j][i] = w2_at(hc, j, i);
-      }
-      const int c = kb * 4 + q;
-#pragma unroll
-      for (int tt = 0; tt < S::T16; ++tt) {
-        const int r = tt * 16 + l16;
-        Mfma<T>::k16(acc1[tt], a, xs[r * S::XU + (c ^ (r & (S::XSW - 1)))]);
-      }
-    }
-    __syncthreads();  // the previous chunk's GEMM2 has finished reading hs
+  for (;;) {
+    const bool has_next = valid(j + nslot);
+    const int jn = has_next ? j + nslot : j;
+    // the next unit's description: requested now, used after chunk 0's GEMM1
+    const FfnUnit un_raw = units[xcd * per_xcd + jn];
+    FfnUnit un = u;
+    const GPtr w2w = w2_base(u.e);
+    GPtr w1n = w1w;
 
-    // bias + ReLU, round, stage Hc[token][hidden] in LDS: lane l holds token
-    // 16 tt + l % 16 and the 4 consecutive hidden units 16 w + 4 (l / 16) + r.
-    {
-      const int hl = 16 * wave + 4 * q;
-      float bias[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (BW == 2)
-          bias[i] = bf16_bits_to_f32((b1r.w[i / 2] >> (16 * (i % 2))) & 0xffffu);
-        else
-          bias[i] = __uint_as_float(b1r.w[i]);
-      }
-      const int cu = hl / UE;
-#pragma unroll
-      for (int tt = 0; tt < S::T16; ++tt) {
-        const int tok = tt * 16 + l16;
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = acc1[tt][i] + bias[i];
-          v[i] = a > 0.f ? a : 0.f;
-        }
-        char* dst = reinterpret_cast<char*>(&hs[tok * S::HU + (cu ^ (tok & (S::HSW - 1)))]);
-        if constexpr (sizeof(T) == 2) {
-          uint2 pk;
-          pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-          pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-          *reinterpret_cast<uint2*>(dst + (hl % UE) * 2) = pk;
-        } else {
-          U16 pk;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pk.w[i] = __float_as_uint(v[i]);
-          *reinterpret_cast<U16*>(dst) = pk;
-        }
-      }
-    }
-    __syncthreads();
-
-    // GEMM2: Out[token][col] += Hc[token][:] . W2[col][hc:hc+HC].
-#pragma unroll
-    for (int kb = 0; kb < NKB2; ++kb) {
-      U16 b[S::CT2];
-#pragma unroll
-      for (int i = 0; i < S::CT2; ++i) b[i] = pb[kb % PF2][i];
-      if (kb + PF2 < NKB2) {
-#pragma unroll
-        for (int i = 0; i < S::CT2; ++i) pb[kb % PF2][i] = w2_at(hc, kb + PF2, i);
-      }
-      if (kb == (NKB2 > PF2 ? NKB2 - PF2 : 0) && ch + 1 < nch) {
-#pragma unroll
-        for (int j = 0; j < PF1; ++j) pa[j] = w1_at(hc + S::HC, j);
-        if (has_b1) b1r = b1_at(hc + S::HC);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const int c = kb * 4 + q;
-#pragma unroll
-      for (int tt = 0; tt < S::T16; ++tt) {
-        const int r = tt * 16 + l16;
-        const U16 a = hs[r * S::HU + (c ^ (r & (S::HSW - 1)))];
-#pragma unroll
-        for (int i = 0; i < S::CT2; ++i) Mfma<T>::k16(acc2[tt][i], a, b[i]);
-      }
-    }
-  }
-
-  // b2, then write the rows in segment order (lane: column l % 16 of each tile,
-  // token rows 4 (l / 16) + j).
-#pragma unroll
-  for (int i = 0; i < S::CT2; ++i) {
-    const int col = (wave * S::CT2 + i) * 16 + l16;
-    const float bias = p.b2 ? load_scalar<T>(p.b2, (int64_t)e * D + col) : 0.f;
+    f32x4 acc2[S::T16][S::CT2];
 #pragma unroll
     for (int tt = 0; tt < S::T16; ++tt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok = tt * 16 + 4 * q + j;
-        if (tok < rows) store_scalar<T>(p.out, (seg + tok) * D + col, acc2[tt][i][j] + bias);
+      for (int i = 0; i < S::CT2; ++i) acc2[tt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int ch = 0; ch < nch; ++ch) {
+      const int hc = ch * S::HC;
+      const bool last = ch + 1 == nch;
+      // this chunk's weight bases, opaque to the compiler so that it forms
+      // each load's address from one base and an immediate offset instead of
+      // keeping a pointer per K-block live across chunks and units
+      GPtr w1c = w1w + (int64_t)hc * D * (int64_t)sizeof(T);
+      GPtr w2c = w2w + (int64_t)hc * (int64_t)sizeof(T);
+      asm volatile("" : "+s"(w1c), "+s"(w2c));
+      f32x4 acc1[S::T16];
+#pragma unroll
+      for (int tt = 0; tt < S::T16; ++tt) acc1[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB1; ++kb) {
+        const U16 a = pa[kb % PF1];
+        if (kb + PF1 < NKB1) pa[kb % PF1] = w1_at(w1c, 0, kb + PF1);
+        // keep the prefetches where they are issued (the scheduler would
+        // otherwise sink them next to their use under register pressure)
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb == (NKB1 > PF1 ? NKB1 - PF1 : 0)) {
+#pragma unroll
+          for (int jj = 0; jj < PF2; ++jj)
+#pragma unroll
+            for (int i = 0; i < S::CT2; ++i) pb[jj][i] = w2_at(w2c, 0, jj, i);
+        }
+        const int c = kb * 4 + q;
+#pragma unroll
+        for (int tt = 0; tt < S::T16; ++tt) {
+          const int r = tt * 16 + l16;
+          Mfma<T>::k16(acc1[tt], a, xs[r * S::XU + (c ^ (r & (S::XSW - 1)))]);
+        }
       }
+      if (ch == 0) {
+        // the next unit: its description, and its tokens on their way to
+        // tokbuf (read by its row copies at the end of this unit)
+        un = uniform_unit(un_raw);
+        w1n = w1_base(un.e);
+        if (has_next) copy_tokens(un);
+        if (nch == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();  // the previous chunk's GEMM2 has finished reading hs;
+                        // after the last chunk, every wave is done with xs
+      if (last && has_next) gather(un.rows);
+
+      // bias + ReLU, round, stage Hc[token][hidden] in LDS: lane l holds token
+      // 16 tt + l % 16 and the 4 consecutive hidden units 16 w + 4 (l / 16) + r.
+      {
+        const int hl = 16 * wave + 4 * q;
+        float bias[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float b;
+          if constexpr (BW == 2)
+            b = bf16_bits_to_f32((b1r.w[i / 2] >> (16 * (i % 2))) & 0xffffu);
+          else
+            b = __uint_as_float(b1r.w[i]);
+          bias[i] = has_b1 ? b : 0.f;
+        }
+        const int cu = hl / UE;
+#pragma unroll
+        for (int tt = 0; tt < S::T16; ++tt) {
+          const int tok = tt * 16 + l16;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = acc1[tt][i] + bias[i];
+            v[i] = a > 0.f ? a : 0.f;
+          }
+          char* dst = reinterpret_cast<char*>(&hs[tok * S::HU + (cu ^ (tok & (S::HSW - 1)))]);
+          if constexpr (sizeof(T) == 2) {
+            uint2 pk;
+            pk.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+            pk.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+            *reinterpret_cast<uint2*>(dst + (hl % UE) * 2) = pk;
+          } else {
+            U16 pk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pk.w[i] = __float_as_uint(v[i]);
+            *reinterpret_cast<U16*>(dst) = pk;
+          }
+        }
+      }
+      __syncthreads();
+
+      // GEMM2: Out[token][col] += Hc[token][:] . W2[col][hc:hc+HC]. Its last
+      // K-blocks request the first W1 fragments and b1 of the next chunk, of
+      // the next unit's first chunk, or (after the last unit) of this unit's
+      // first chunk again, unused.
+      const GPtr w1p = !last ? w1c + (int64_t)S::HC * D * (int64_t)sizeof(T) : w1n;
+      const int e_p = last ? un.e : u.e;
+      const int hc_p = last ? 0 : hc + S::HC;
+#pragma unroll
+      for (int kb = 0; kb < NKB2; ++kb) {
+        U16 b[S::CT2];
+#pragma unroll
+        for (int i = 0; i < S::CT2; ++i) b[i] = pb[kb % PF2][i];
+        if (kb + PF2 < NKB2) {
+#pragma unroll
+          for (int i = 0; i < S::CT2; ++i) pb[kb % PF2][i] = w2_at(w2c, 0, kb + PF2, i);
+        }
+        if (kb == (NKB2 > PF2 ? NKB2 - PF2 : 0)) {
+#pragma unroll
+          for (int jj = 0; jj < PF1; ++jj) pa[jj] = w1_at(w1p, 0, jj);
+          b1r = b1_at(e_p, hc_p);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int c = kb * 4 + q;
+#pragma unroll
+        for (int tt = 0; tt < S::T16; ++tt) {
+          const int r = tt * 16 + l16;
+          const U16 a = hs[r * S::HU + (c ^ (r & (S::HSW - 1)))];
+#pragma unroll
+          for (int i = 0; i < S::CT2; ++i) Mfma<T>::k16(acc2[tt][i], a, b[i]);
+        }
+      }
+    }
+
+    // the next unit's rows have landed in this wave's part of the tile (the
+    // wait comes before the stores, so that the last loads issued are the
+    // next unit's first W1 fragments and b1, which it leaves in flight)
+    if (has_next) wait_copies();
+
+    // Output rows in segment order. A 4x4 transpose inside each quad of lanes
+    // turns the C layout (lane: one column, 4 consecutive rows) into one row
+    // and 4 consecutive columns per lane, written with one 8-byte (bf16) or
+    // 16-byte (fp32) store; b2 is added on the way.
+    {
+      int ln = lane;  // opaque, as in gather()
+      asm volatile("" : "+v"(ln));
+      const int cq = ln & 3;
+      const int col0 = wave * S::CT2 * 16 + (ln & 12);
+      const int row0 = 4 * (ln >> 4) + cq;
+      // this unit's output from the lane's first element on, opaque (as for
+      // the weights) so that no per-element address outlives the unit
+      __attribute__((address_space(1))) T* orow =
+          (__attribute__((address_space(1))) T*)(reinterpret_cast<T*>(p.out)) +
+          (u.seg + row0) * D + col0;
+      asm volatile("" : "+v"(orow));
+      const int rleft = u.rows - row0;
+#pragma unroll
+      for (int i = 0; i < S::CT2; ++i) {
+        float b2v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.b2) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) b2v[k] = load_scalar<T>(p.b2, (int64_t)u.e * D + col0 + i * 16 + k);
+        }
+#pragma unroll
+        for (int tt = 0; tt < S::T16; ++tt) {
+          f32x4 v = acc2[tt][i];
+          quad_transpose(v, cq);
+          if (tt * 16 < rleft) {
+            __attribute__((address_space(1))) T* dst = orow + (int64_t)tt * 16 * D + i * 16;
+            if constexpr (sizeof(T) == 2) {
+              u32x2 pk;
+              pk[0] = f32_to_bf16_bits(v[0] + b2v[0]) | (f32_to_bf16_bits(v[1] + b2v[1]) << 16);
+              pk[1] = f32_to_bf16_bits(v[2] + b2v[2]) | (f32_to_bf16_bits(v[3] + b2v[3]) << 16);
+              *reinterpret_cast<__attribute__((address_space(1))) u32x2*>(dst) = pk;
+            } else {
+              f32x4 o = {v[0] + b2v[0], v[1] + b2v[1], v[2] + b2v[2], v[3] + b2v[3]};
+              *reinterpret_cast<__attribute__((address_space(1))) f32x4*>(dst) = o;
+            }
+          }
+        }
+      }
+    }
+    if (!has_next) break;
+    __syncthreads();  // ... and in every wave's part
+    u = un;
+    w1w = w1n;
+    j = jn;
   }
 }
 
-// Lists the work units: expert e gets ceil(count_e / BM) units. One workgroup;
+// Lists the work units: expert e gets ceil(count_e / BM) units, each written
+// as (expert, first pair of its rows, rows) after the count. One workgroup;
 // thread t owns a contiguous span of experts.
 __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ offsets, int n, int bm,
                                                  int32_t* __restrict__ blocks) {
@@ -314,15 +489,33 @@ __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ off
     __syncthreads();
   }
   int pos = part[t] - s;
+  FfnUnit* units = reinterpret_cast<FfnUnit*>(blocks + 4);
   for (int e = e0; e < e1; ++e) {
-    const int cnt = offsets[e + 1] - offsets[e];
+    const int seg = offsets[e];
+    const int cnt = offsets[e + 1] - seg;
     for (int r = 0; r < cnt; r += bm) {
-      blocks[1 + 2 * pos] = e;
-      blocks[2 + 2 * pos] = r;
+      units[pos] = FfnUnit{e, seg + r, min(bm, cnt - r), 0};
       ++pos;
     }
   }
   if (t == 1023) blocks[0] = part[t];
+}
+
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* cus) {
+  static int cache[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cache[dev] == 0) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cache[dev] = v > 0 ? v : 1;
+  }
+  *cus = cache[dev];
+  return hipSuccess;
 }
 
 template <typename T, int D>
@@ -331,10 +524,16 @@ hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* o
   using S = FfnShape<T, D>;
   hipLaunchKernelGGL(ffn_plan, dim3(1), dim3(1024), 0, s, offsets, n, S::BM,
                      const_cast<int32_t*>(p.blocks));
-  // every XCD gets ceil(count / 8) slots; the grid covers the largest possible count
-  const int64_t grid = (max_blocks + 7) / 8 * 8;
-  if (max_blocks > 0)
-    hipLaunchKernelGGL((ffn_kernel<T, D>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
+  if (max_blocks <= 0) return hipGetLastError();
+  // one persistent workgroup per compute unit (the LDS tile allows one), a
+  // multiple of 8 so that every XCD gets the same number of slots, and no
+  // more than the largest possible unit count needs
+  int cus = 0;
+  const hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const int64_t want = (max_blocks + 7) / 8 * 8;
+  const int64_t grid = std::min<int64_t>(want, std::max(8, cus / 8 * 8));
+  hipLaunchKernelGGL((ffn_kernel<T, D>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -357,6 +556,10 @@ int64_t ffn_max_blocks(int64_t rows, int n, int d, Dt dt) {
   const int bm = ffn_rows_per_block(d, dt);
   if (bm <= 0) return 0;
   return (rows + bm - 1) / bm + n;
+}
+
+size_t ffn_plan_bytes(int64_t rows, int n, int d, Dt dt) {
+  return (size_t)(4 + 4 * ffn_max_blocks(rows, n, d, dt)) * sizeof(int32_t);
 }
 
 bool ffn_supported(int d, int h, Dt dt) {

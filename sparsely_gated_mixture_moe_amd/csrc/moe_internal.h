@@ -82,6 +82,8 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
 // Expert FFN.
 int ffn_rows_per_block(int d, Dt dt);
 int64_t ffn_max_blocks(int64_t rows, int n, int d, Dt dt);
+// Bytes of the expert-FFN work-unit list (the count, then 16 bytes per unit).
+size_t ffn_plan_bytes(int64_t rows, int n, int d, Dt dt);
 bool ffn_supported(int d, int h, Dt dt);
 hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const void* x,
                       const int32_t* offsets, const int32_t* perm_token, const void* w1,
