@@ -16,18 +16,22 @@
 //    2 weaves its per-pair work between them (measured faster for pass 2's
 //    longer per-pair work; pass 1's epilogue reads LDS and branches).
 //
-// Epilogue. In the 32x32 C layout lane l holds column l % 32 for 16 rows: the
-// clean logit (columns 0-15) or the noise pre-activation (16-31) of one expert.
-// Lanes l and l ^ 16 swap half of their rows (v_permlane16_swap) so each holds
-// (clean, noise) pairs for 8 rows of one expert. Pass 1 forms H = clean + eps *
-// (Softplus(u) + floor), transposes it through LDS (one chunk behind, into a
-// double-buffered tile) and lets each lane own one row's half of the chunk: a
-// lane sees its row's experts in increasing order, keeps the row's L best
-// (H, expert), and rarely needs to insert once its list is warm. Lanes l and
-// l ^ 32 (the two halves of a row) merge at the end. The noise draws and
-// biases ride a three-slot LDS ring two chunks ahead. Pass 2 evaluates
-// P = Phi((clean - v_k) / sigma) in place (after the exchange) and sums each expert's column over
-// the block's rows in a fixed order (the selected pairs are corrected to the
+// Epilogue. Pass 1 multiplies weights (A operand, from LDS) by x (B operand,
+// in registers), so in the 32x32 C layout lane l holds token l % 32 and rows
+// 8 (j / 4) + 4 (l / 32) + j % 4 of the weight tile: registers j < 8 are the
+// clean logits of experts 4 (l / 32) + (0..3) and 8 + 4 (l / 32) + (0..3) of
+// the chunk, registers 8 + j the noise pre-activations of the same experts.
+// Each lane forms H = clean + eps * (Softplus(u) + floor) for its token and 8
+// experts and keeps the token's L best (H, expert) of the experts it sees (in
+// increasing order, so it rarely needs to insert once its list is warm); lanes
+// l and l ^ 32 (the two halves of a token's experts) merge at the end. The
+// noise draws and biases ride a three-slot LDS ring two chunks ahead.
+// Pass 2 multiplies x (A) by the weights (B): lane l holds expert column l % 32
+// for 16 rows, the clean logit (columns 0-15) or the noise pre-activation
+// (16-31); lanes l and l ^ 16 swap half of their rows (v_permlane16_swap) so
+// each holds (clean, noise) pairs for 8 rows of one expert, evaluates
+// P = Phi((clean - v_k) / sigma) and sums each expert's column over the
+// block's rows in a fixed order (the selected pairs are corrected to the
 // (k+1)-th threshold separately).
 #pragma once
 
@@ -41,7 +45,6 @@ constexpr int kG32Threads = kG32Waves * 64;
 constexpr int kG32Rows = kG32Waves * 32;
 static_assert(kG32Rows == kGate32Rows, "rows per block of the 32x32 gate kernel");
 constexpr int kG32Chunk = 16;
-constexpr int kG32HStride = 20;  // padded row stride (floats) of the transpose tile
 
 template <int V>
 struct IntConst {
@@ -70,8 +73,6 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // of the chunk's 16 biases per wave; four chunks in flight
   constexpr int ESLOT = kG32Rows * kG32Chunk + kG32Waves * kG32Chunk;
   __shared__ float ebuf[PASS2 ? 1 : 3][PASS2 ? 1 : ESLOT];
-  // pass 1: each wave's transpose tile, double-buffered by chunk parity
-  __shared__ float hbuf[PASS2 ? 1 : 2][PASS2 ? 1 : kG32Waves][32 * kG32HStride];
   __shared__ float thrbuf[PASS2 ? kG32Rows : 1];  // pass 2: each row's k-th logit
   // pass 2: each wave's copy of a chunk's 16 biases, double-buffered by chunk parity
   __shared__ float bbuf[PASS2 ? 2 : 1][PASS2 ? kG32Waves * kG32Chunk : 1];
@@ -88,7 +89,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   const bf16* wg = reinterpret_cast<const bf16*>(p.wg);
   const bf16* wn = reinterpret_cast<const bf16*>(p.wn);
 
-  // x rows of this wave as A operands: lane supplies row l32, unit 2 kb + hi.
+  // x rows of this wave as MFMA operands (B in pass 1, A in pass 2): lane
+  // supplies row l32, unit 2 kb + hi.
   U16 xa[NKB];
   {
     const int64_t r = tile_xrow(p, tile, wrow0 + l32);
@@ -98,11 +100,12 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       xa[kb] = (r >= 0) ? ld_unit(x + r * D + (kb * 2 + hi) * UE) : zero_unit();
   }
 
-  // Rows of this lane's (clean, noise) pairs after the exchange: element i is
-  // C-layout register j = i (clean lanes) or 8 + i (noise lanes). Rows past
-  // the tile's end compute finite garbage (zero x, the first row's noise):
-  // pass 1 never writes them out, pass 2 gives them thresholds of +inf, so
-  // their P is exactly 0. n is a multiple of 16, so every expert is valid.
+  // Pass 2: rows of this lane's (clean, noise) pairs after the exchange:
+  // element i is C-layout register j = i (clean lanes) or 8 + i (noise
+  // lanes). Rows past the tile's end compute finite garbage (zero x, the
+  // first row's noise): pass 1 never writes them out, pass 2 gives them
+  // thresholds of +inf, so their P is exactly 0. n is a multiple of 16, so
+  // every expert is valid.
   int rr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) rr[i] = (clean_lane ? 0 : 16) + 8 * (i / 4) + 4 * hi + (i % 4);
@@ -114,7 +117,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
   }
 
-  // Row-owner state (pass 1): lane owns row l32 of the wave, half hi of each chunk.
+  // Pass 1: lane (l32, hi) owns token l32 of the wave and experts 4 hi + (0..3)
+  // and 8 + 4 hi + (0..3) of every chunk.
   float lv[L];
   int li[L];
 #pragma unroll
@@ -166,7 +170,10 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       U16 cur;
       __builtin_memcpy(&cur, &f[kb % FPF], 16);
       if (kb + FPF < NKB) f[kb % FPF] = bl[(kb + FPF) * 64];
-      Mfma<bf16>::k32(acc, xa[kb], cur);
+      if constexpr (PASS2)
+        Mfma<bf16>::k32(acc, xa[kb], cur);  // rows: tokens, columns: weights
+      else
+        Mfma<bf16>::k32(acc, cur, xa[kb]);  // rows: weights, columns: tokens
     }
     // Keep that order (the scheduler would otherwise pull the reads down next
     // to their use): FPF reads, then matrix product / read pairs, then the
@@ -205,16 +212,17 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
   };
 
-  // Pass 1: lane (l32, hi) owns row l32's experts hi * 8 .. hi * 8 + 7 of a
-  // chunk; it keeps the row's L best, which rarely change once warm.
-  auto insert_row = [&](const f32x4 (&h)[2], int chunk) {
-    const float hv[8] = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+  // Pass 1: insert the lane's 8 values of chunk `chunk` (experts in
+  // increasing order) into its token's list; any lane with a candidate makes
+  // the wave run the insertions, which become rare once the lists are warm.
+  auto insert_pairs = [&](const float (&hv)[8], int chunk) {
     bool cand = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) cand |= hv[i] > lv[L - 1];
     if (__any(cand)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) insert_new<L>(lv, li, hv[i], chunk * EC + hi * 8 + i);
+      for (int i = 0; i < 8; ++i)
+        insert_new<L>(lv, li, hv[i], chunk * EC + 8 * (i / 4) + 4 * hi + (i % 4));
     }
   };
 
@@ -266,62 +274,15 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
 
     float colsum = 0.f;
-    float hpair[8];
-    // Selection pass: the next chunk's products, then this chunk's epilogue.
-    auto products = [&]() { mfma_chunk(wnext, accs[P ^ 1]); };
-    auto epilogue = [&]() {
-      // Exchange within each pair of 16-lane rows: the odd row's (noise
-      // lanes') registers acc[i] trade places with the even row's (clean
-      // lanes') registers acc[8 + i]. Afterwards every lane holds, for its
-      // rows rr[i], the clean logit in the first result and the noise
-      // pre-activation in the second.
-      float cl[8], un[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i]),
-                                                          __float_as_uint(acc[8 + i]), false, false);
-        cl[i] = __uint_as_float(sw[0]);
-        un[i] = __uint_as_float(sw[1]);
-      }
-      const float bias = has_bias ? ebuf[c % 3][kG32Rows * EC + wave * EC + (l32 & 15)] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float eps = ebuf[c % 3][(wave * 32 + rr[i]) * EC + (l32 & 15)];
-        hpair[i] = fmaf(eps, softplus_f(un[i]) + p.floor, cl[i] + bias);
-      }
-    };
-    // Pass 1 transposes H through this wave's LDS tile and lets each lane scan
-    // its row, one chunk behind: chunk c's values are written in this pass
-    // and read back in the next, so the reads never wait for fresh writes
-    // (a wave's LDS operations complete in order, so no fence is needed).
-    f32x4 hprev[2];
-    auto read_prev = [&]() {
-      if constexpr (!PASS2) {
-        if (c > 0) {
-          const float* hb = &hbuf[P ^ 1][wave][l32 * kG32HStride + hi * 8];
-          hprev[0] = *reinterpret_cast<const f32x4*>(hb);
-          hprev[1] = *reinterpret_cast<const f32x4*>(hb + 4);
-        }
-      }
-    };
-    auto insert_prev = [&]() {
-      if constexpr (!PASS2) {
-        if (c > 0) insert_row(hprev, c - 1);
-      }
-    };
-    // Pass 1: write this chunk's H to the tile. Pass 2: the column sums of the chunk.
+    // Pass 2's exchange within each pair of 16-lane rows: the odd row's
+    // (noise lanes') register acc[i] trades places with the even row's (clean
+    // lanes') register acc[8 + i]; afterwards the lane holds, for its row
+    // rr[i], the clean logit (first) and the noise pre-activation (second).
     auto finish = [&]() {
-      if constexpr (!PASS2) {
-        float* hb = hbuf[P][wave];
-        const int ecol = l32 & 15;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hb[rr[i] * kG32HStride + ecol] = hpair[i];
-      } else {
-        // column sums: lanes l, l ^ 16 (same expert, other rows) and l ^ 32
-        colsum += __shfl_xor(colsum, 16);
-        colsum += __shfl_xor(colsum, 32);
-        if (lane < 16) red[P][wave][lane] = colsum;
-      }
+      // column sums: lanes l, l ^ 16 (same expert, other rows) and l ^ 32
+      colsum += __shfl_xor(colsum, 16);
+      colsum += __shfl_xor(colsum, 32);
+      if (lane < 16) red[P][wave][lane] = colsum;
     };
     if constexpr (PASS2) {
       // Load pass: the next chunk's products with this chunk's pairs woven
@@ -351,7 +312,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
           if (kb + FPF < NKB) f[kb % FPF] = bl[(kb + FPF) * 64];
           Mfma<bf16>::k32(an, xa[kb], cur);
         }
-        // the exchange of the selection epilogue, then P of pair i
+        // the exchange (see finish), then P of pair i
         const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i]),
                                                           __float_as_uint(acc[8 + i]), false, false);
         const float clean = __uint_as_float(sw[0]) + bias;
@@ -372,12 +333,25 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     } else {
       // Selection pass: the next chunk's products go first; their matrix
       // operations run while this chunk's epilogue occupies the vector ALUs.
-      products();
+      mfma_chunk(wnext, accs[P ^ 1]);
       __builtin_amdgcn_sched_barrier(0);
-      read_prev();
-      epilogue();
-      insert_prev();
-      finish();
+      const float* er = &ebuf[c % 3][(wave * 32 + l32) * EC + 4 * hi];
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(er);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(er + 8);
+      f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
+      if (has_bias) {
+        const float* br = &ebuf[c % 3][kG32Rows * EC + wave * EC + 4 * hi];
+        b0 = *reinterpret_cast<const f32x4*>(br);
+        b1 = *reinterpret_cast<const f32x4*>(br + 8);
+      }
+      float hv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float eps = i < 4 ? e0[i] : e1[i - 4];
+        const float bias = i < 4 ? b0[i] : b1[i - 4];
+        hv[i] = fmaf(eps, softplus_f(acc[8 + i]) + p.floor, acc[i] + bias);
+      }
+      insert_pairs(hv, c);
     }
 
     // Block barrier without a release fence (which would wait for every copy
@@ -404,16 +378,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     if (c + 1 < nchunks) chunk_pass(c + 1, IntConst<1>{});
   }
   if constexpr (!PASS2) {
-    // the last chunk's values, written in the last pass
-    f32x4 h[2];
-    const float* hb = &hbuf[(nchunks - 1) & 1][wave][l32 * kG32HStride + hi * 8];
-    h[0] = *reinterpret_cast<const f32x4*>(hb);
-    h[1] = *reinterpret_cast<const f32x4*>(hb + 4);
-    insert_row(h, nchunks - 1);
-  }
-
-  if constexpr (!PASS2) {
-    // The two halves of a row (lanes l and l ^ 32) merge, then lanes 0-31 write.
+    // The two halves of a token's experts (lanes l and l ^ 32) merge, then
+    // lanes 0-31 write.
     float ov[L];
     int oi[L];
 #pragma unroll
