@@ -1,5 +1,7 @@
 // Host glue of the gating kernels (the kernel template is in gate_impl.h) and
 // the block-order reduction of the Load partial sums.
+#include <algorithm>
+
 #include "gate_impl.h"
 
 namespace moe {
@@ -14,6 +16,7 @@ using gate_detail::GateParams;
 __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restrict__ partial,
                                                           int nblocks, int n,
                                                           const float* __restrict__ corr,
+                                                          int splits,
                                                           float* __restrict__ load) {
   __shared__ float red[8][32];
   const int col = threadIdx.x & 31;
@@ -28,7 +31,9 @@ __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restric
     float t = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) t += red[i][col];
-    load[e] = t + corr[e];
+    float c = 0.f;
+    for (int i = 0; i < splits; ++i) c += corr[(int64_t)e * splits + i];
+    load[e] = t + c;
   }
 }
 
@@ -37,7 +42,7 @@ __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restric
 // order as above; a group without rows gets 0.
 __global__ __launch_bounds__(256) void load_reduce_grouped_kernel(
     const float* __restrict__ partial, const int32_t* __restrict__ unit_start, int n,
-    const float* __restrict__ corr, float* __restrict__ load) {
+    const float* __restrict__ corr, int splits, float* __restrict__ load) {
   __shared__ float red[8][32];
   const int col = threadIdx.x & 31;
   const int part = threadIdx.x >> 5;
@@ -53,7 +58,9 @@ __global__ __launch_bounds__(256) void load_reduce_grouped_kernel(
     float t = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) t += red[i][col];
-    load[(int64_t)grp * n + e] = t + corr[(int64_t)grp * n + e];
+    float c = 0.f;
+    for (int i = 0; i < splits; ++i) c += corr[((int64_t)grp * n + e) * splits + i];
+    load[(int64_t)grp * n + e] = t + c;
   }
 }
 
@@ -122,10 +129,13 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float (&v)[
 // routed to it (positions offsets[e] .. offsets[e+1] - 1, tokens perm_token[p])
 // and sums Phi((clean - v_{k+1}) / sigma) - Phi((clean - v_k) / sigma), with
 // clean = x . W_g[e] (+ bias) and sigma = Softplus(x . W_noise[e]) + floor
-// recomputed by a dot product over d in fp32. One workgroup of four waves per
-// expert: lane l holds elements 8 l .. 8 l + 7 of both weight rows (d <= 512);
-// wave w takes the rows' groups of eight with index w mod 4, all eight in
-// flight at once; the four waves' sums are added in wave order.
+// recomputed by a dot product over d in fp32. Workgroup (e, s), four waves,
+// takes split s of `splits` equal, consecutive slices of expert e's rows (so
+// a large segment is spread over several workgroups): lane l holds elements
+// 8 l .. 8 l + 7 of both weight rows (d <= 512); wave w takes the slice's
+// groups of eight with index w mod 4, all eight in flight at once; the four
+// waves' sums are added in wave order into corr[e * splits + s] (0 for an
+// empty slice), and the reductions add the splits in order.
 // Secondary gates of a hierarchical layer: expert e is leaf (g, j) = (e / b,
 // e % b), its weights are row e of the [a * b, d] secondary weights, and token
 // t's thresholds are row t * k1 + r, where r is g's rank in sel1[t].
@@ -134,12 +144,21 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
     const void* __restrict__ x, const void* __restrict__ wg, const void* __restrict__ wn,
     const float* __restrict__ bias, int d, int n, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm_token, const float* __restrict__ thresh, float noise_floor,
-    const int32_t* __restrict__ sel1, int k1, int b, float* __restrict__ corr) {
+    const int32_t* __restrict__ sel1, int k1, int b, int splits, float* __restrict__ corr) {
   constexpr int R = 8;
   __shared__ float part[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int e = blockIdx.x;
+  const int split = blockIdx.y;
+  const int q0 = offsets[e], q1 = offsets[e + 1];
+  // slice length: an equal share, rounded up to whole passes of the 4 x R rows
+  const int chunk = ((q1 - q0 + splits - 1) / splits + 4 * R - 1) / (4 * R) * (4 * R);
+  const int p0 = q0 + split * chunk, p1 = min(q1, p0 + chunk);
+  if (p0 >= p1) {
+    if (threadIdx.x == 0) corr[(int64_t)e * splits + split] = 0.f;
+    return;
+  }
   const bool active = lane * 8 < d;
   float wgv[8], wnv[8];
   if (active) {
@@ -151,7 +170,6 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
   }
   const float be = bias ? bias[e] : 0.f;
   const int grp = e / b;
-  const int p0 = offsets[e], p1 = offsets[e + 1];
   float acc = 0.f;
   for (int p = p0 + wave * R; p < p1; p += 4 * R) {
     int64_t t[R];
@@ -197,7 +215,8 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
   }
   if (lane == 0) part[wave] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) corr[e] = ((part[0] + part[1]) + part[2]) + part[3];
+  if (threadIdx.x == 0)
+    corr[(int64_t)e * splits + split] = ((part[0] + part[1]) + part[2]) + part[3];
 }
 
 hipError_t gate_dispatch(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
@@ -259,16 +278,24 @@ hipError_t launch_group_plan(const int32_t* offsets, int groups, int tile_rows, 
   return hipGetLastError();
 }
 
+int corr_splits(int64_t pairs, int n) {
+  if (n <= 0) return 1;
+  const int64_t avg = pairs / n;
+  const int64_t sp = (2 * avg + 255) / 256;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kCorrSplitsMax, sp));
+}
+
 hipError_t launch_load_correction(const GateLaunch& g, int n, const int32_t* offsets,
                                   const int32_t* perm_token, const float* thresh,
-                                  const int32_t* sel1, int k1, int b, float* corr, hipStream_t s) {
-  const dim3 grid((unsigned)n), block(256);
+                                  const int32_t* sel1, int k1, int b, int splits, float* corr,
+                                  hipStream_t s) {
+  const dim3 grid((unsigned)n, (unsigned)splits), block(256);
   const void* bias = g.units ? nullptr : g.bias;
   const float* bp = reinterpret_cast<const float*>(bias);
 #define MOE_CORR(XS, WS)                                                                      \
   hipLaunchKernelGGL((load_correction_kernel<XS, WS>), grid, block, 0, s, g.x, g.w_gate,      \
                      g.w_noise, bp, g.d, n, offsets, perm_token, thresh, g.noise_floor, sel1, \
-                     k1, b, corr)
+                     k1, b, splits, corr)
   if (g.x_dt == kBF16 && g.w_dt == kBF16) MOE_CORR(bf16, bf16);
   else if (g.x_dt == kBF16) MOE_CORR(bf16, float);
   else MOE_CORR(float, float);
@@ -288,11 +315,12 @@ hipError_t launch_load_grouped(const GateLaunch& g, int groups, const int32_t* u
     if (e != hipSuccess) return e;
   }
   const int nleaves = groups * g.n;
+  const int splits = corr_splits(g.tokens * g.k, nleaves);
   hipError_t e = launch_load_correction(g, nleaves, leaf_offsets, leaf_perm_token, thresh, sel1,
-                                        k1, g.n, corr, s);
+                                        k1, g.n, splits, corr, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(load_reduce_grouped_kernel, dim3((g.n + 31) / 32, groups), dim3(256), 0, s,
-                     partial, unit_start, g.n, corr, load);
+                     partial, unit_start, g.n, corr, splits, load);
   return hipGetLastError();
 }
 
@@ -309,11 +337,12 @@ hipError_t launch_load(const GateLaunch& g, const float* thresh, const int32_t* 
     hipError_t e = gate_dispatch(g, p, true, s);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_load_correction(g, g.n, offsets, perm_token, thresh, nullptr, 1, 1, corr,
-                                        s);
+  const int splits = corr_splits(g.tokens * g.k, g.n);
+  hipError_t e = launch_load_correction(g, g.n, offsets, perm_token, thresh, nullptr, 1, 1, splits,
+                                        corr, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(load_reduce_kernel, dim3((g.n + 31) / 32), dim3(256), 0, s, partial, nb,
-                     g.n, corr, load);
+                     g.n, corr, splits, load);
   return hipGetLastError();
 }
 

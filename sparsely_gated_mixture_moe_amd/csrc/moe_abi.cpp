@@ -123,7 +123,7 @@ Layout layout(const moe_dims* d, const moe_gate_opts* o) {
   L.ffn_bytes = align_up(moe::ffn_plan_bytes(pairs, (int)n, d->d_model, to_dt(d->act_dtype)));
   // the Load pass: per-block partial sums, then the selected pairs' corrections
   L.aux_bytes = (o && o->train) ? align_up((size_t)moe::gate_blocks(B) * n * sizeof(float)) +
-                                      align_up((size_t)n * sizeof(float))
+                                      align_up((size_t)n * moe::kCorrSplitsMax * sizeof(float))
                                 : 0;
   // moe_forward
   L.topk_idx = take(pairs * sizeof(int32_t));
@@ -293,10 +293,10 @@ HierLayout hier_layout(const moe_hier_dims* h, const moe_gate_opts* o) {
   L.expert_out = take((size_t)pairs * h->d_model * dt_size(h->act_dtype));
   L.load1 = take(a * sizeof(float));
   L.partial1 = take(train ? (size_t)moe::gate_blocks(B) * a * sizeof(float) : 0);
-  L.corr1 = take(a * sizeof(float));
+  L.corr1 = take(a * moe::kCorrSplitsMax * sizeof(float));
   L.load2 = take(n * sizeof(float));
   L.partial2 = take(train ? (size_t)L.max_units * b * sizeof(float) : 0);
-  L.corr2 = take(n * sizeof(float));
+  L.corr2 = take(n * moe::kCorrSplitsMax * sizeof(float));
   L.total = at;
   return L;
 }

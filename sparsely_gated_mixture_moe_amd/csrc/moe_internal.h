@@ -50,6 +50,11 @@ hipError_t launch_gate(const GateLaunch& g, int32_t* topk_idx, float* topk_gate,
 // from the routed rows (offsets / perm_token of the route of this selection)
 // into corr [n]; then reduces both into load [n].
 int gate_blocks(int64_t tokens);
+// The selected pairs' corrections are summed in up to kCorrSplitsMax slices
+// per expert (corr holds [n][kCorrSplitsMax] floats); corr_splits gives the
+// count used for `pairs` routed rows over n experts.
+constexpr int kCorrSplitsMax = 16;
+int corr_splits(int64_t pairs, int n);
 hipError_t launch_load(const GateLaunch& g, const float* thresh, const int32_t* offsets,
                        const int32_t* perm_token, float* partial, float* corr, float* load,
                        hipStream_t s);
