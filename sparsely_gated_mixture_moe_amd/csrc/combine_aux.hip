@@ -25,20 +25,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ eo,
   float acc[UE];
 #pragma unroll
   for (int i = 0; i < UE; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int sp = slot_pos[t * k + j];
-    if (sp < 0 || sp >= eo_rows) continue;
-    const float g = gate[t * k + j];
-    const U16 v = ld_unit(eo + (int64_t)sp * d + u * UE);
-    if constexpr (sizeof(T) == 2) {
+  // slots in groups of four: the group's positions, gates and rows are all
+  // requested before the first is added, then added in slot order
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    int sp[4];
+    float g[4];
+    U16 v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += g * __uint_as_float(v.w[i] << 16);
-        acc[2 * i + 1] += g * __uint_as_float(v.w[i] & 0xFFFF0000u);
+    for (int jj = 0; jj < 4; ++jj) {
+      const bool in = j0 + jj < k;
+      sp[jj] = in ? slot_pos[t * k + j0 + jj] : -1;
+      g[jj] = in ? gate[t * k + j0 + jj] : 0.f;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      v[jj] = (sp[jj] >= 0 && sp[jj] < eo_rows) ? ld_unit(eo + (int64_t)sp[jj] * d + u * UE)
+                                                : zero_unit();
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (sp[jj] < 0 || sp[jj] >= eo_rows) continue;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += g[jj] * __uint_as_float(v[jj].w[i] << 16);
+          acc[2 * i + 1] += g[jj] * __uint_as_float(v[jj].w[i] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += g[jj] * __uint_as_float(v[jj].w[i]);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += g * __uint_as_float(v.w[i]);
     }
   }
   U16 o;

@@ -172,10 +172,24 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
   const int grp = e / b;
   float acc = 0.f;
   for (int p = p0 + wave * R; p < p1; p += 4 * R) {
-    int64_t t[R];
-    float c[R], u[R];
+    int64_t t[R], row[R];
+    float c[R], u[R], th0[R], th1[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) t[r] = perm_token[min(p + r, p1 - 1)];
+    // each row's thresholds (row of the secondary gate: the token's rank of
+    // the group), requested together with the rows of x
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      row[r] = t[r];
+      if (sel1) {
+        int rank = 0;
+        for (int j = 0; j < k1; ++j)
+          if (sel1[t[r] * k1 + j] == grp) rank = j;
+        row[r] = t[r] * k1 + rank;
+      }
+      th0[r] = thresh[row[r] * 2];
+      th1[r] = thresh[row[r] * 2 + 1];
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       c[r] = u[r] = 0.f;
@@ -200,16 +214,9 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (p + r < p1) {  // uniform across the wave
-        int64_t row = t[r];
-        if (sel1) {
-          int rank = 0;
-          for (int j = 0; j < k1; ++j)
-            if (sel1[t[r] * k1 + j] == grp) rank = j;
-          row = t[r] * k1 + rank;
-        }
         const float inv = rcp_f(softplus_f(u[r]) + noise_floor);
         const float cl = c[r] + be;
-        acc += phi_f((cl - thresh[row * 2 + 1]) * inv) - phi_f((cl - thresh[row * 2]) * inv);
+        acc += phi_f((cl - th1[r]) * inv) - phi_f((cl - th0[r]) * inv);
       }
     }
   }

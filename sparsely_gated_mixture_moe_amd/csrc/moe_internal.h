@@ -16,7 +16,7 @@ enum Dt { kF32 = 0, kBF16 = 1 };
 constexpr int kGateRows = 128;
 constexpr int kGate32Rows = 256;
 // Routing: tokens per block of the counting sort.
-constexpr int kRouteTokens = 1024;
+constexpr int kRouteTokens = 256;
 
 struct GateLaunch {
   const void* x;

@@ -5,9 +5,9 @@
 // large"). It is a stable counting sort of the B*k (token, slot) pairs by
 // expert, plus Importance (eq 6) as a segmented sum.
 //
-//   1. count:   per block of 1024 tokens, an LDS histogram over experts,
+//   1. count:   per block of 256 tokens, an LDS histogram over experts,
 //               written expert-major as blockcnt[e][b].
-//   2. scan_b:  per expert, exclusive prefix over blocks -> counts[e].
+//   2. scan_b:  per expert (one wave), exclusive prefix over blocks -> counts[e].
 //   3. scan_e:  one workgroup: exclusive prefix of counts -> offsets.
 //   4. scatter: per block, stable ranks. Each wave matches equal experts in its
 //               64 pairs with 16 ballots; the waves of a block then claim
@@ -42,18 +42,29 @@ __global__ __launch_bounds__(kThreads) void route_count(const int32_t* __restric
   for (int e = threadIdx.x; e < n; e += kThreads) blockcnt[(int64_t)e * nblk + blockIdx.x] = hist[e];
 }
 
-__global__ void route_scan_blocks(int32_t* __restrict__ blockcnt, int n, int nblk,
-                                  int32_t* __restrict__ counts) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per expert: lane b takes block b of each group of 64 blocks, an
+// inclusive wave scan (shuffles) plus the running total of earlier groups
+// gives the exclusive prefix.
+__global__ __launch_bounds__(256) void route_scan_blocks(int32_t* __restrict__ blockcnt, int n,
+                                                         int nblk, int32_t* __restrict__ counts) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= n) return;
   int32_t* c = blockcnt + (int64_t)e * nblk;
-  int s = 0;
-  for (int b = 0; b < nblk; ++b) {
-    const int v = c[b];
-    c[b] = s;
-    s += v;
+  int carry = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 64) {
+    const int b = b0 + lane;
+    const int v = b < nblk ? c[b] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    if (b < nblk) c[b] = carry + incl - v;
+    carry += __shfl(incl, 63);
   }
-  counts[e] = s;
+  if (lane == 0) counts[e] = carry;
 }
 
 // Exclusive scan of n counts by one workgroup; thread t owns a contiguous span.
@@ -177,7 +188,7 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
   if (nblk > 0) {
     hipLaunchKernelGGL(route_count, dim3(nblk), dim3(kThreads), lds, s, topk_idx, npairs, ppb, n,
                        nblk, blockcnt);
-    hipLaunchKernelGGL(route_scan_blocks, dim3((n + 255) / 256), dim3(256), 0, s, blockcnt, n, nblk,
+    hipLaunchKernelGGL(route_scan_blocks, dim3((n + 3) / 4), dim3(256), 0, s, blockcnt, n, nblk,
                        counts);
   } else {
     hipLaunchKernelGGL(fill_zero_i32, dim3((n + 255) / 256), dim3(256), 0, s, counts, n);
