@@ -83,43 +83,65 @@ __global__ void offsets_to_load_kernel(const int32_t* __restrict__ offsets, int 
 
 // CV^2 = population variance / mean^2 of importance and of load, in fp64 with a
 // fixed reduction order; losses = {CV2(imp), CV2(load), w_imp CV2(imp) + w_load CV2(load)}.
-__global__ __launch_bounds__(256) void cv2_losses_kernel(const float* __restrict__ imp,
-                                                         const float* __restrict__ load, int n,
-                                                         float w_imp, float w_load,
-                                                         float* __restrict__ losses) {
-  __shared__ double red[256];
-  double cv[2];
-  for (int v = 0; v < 2; ++v) {
-    const float* x = v ? load : imp;
-    double s = 0.0;
-    for (int i = threadIdx.x; i < n; i += 256) s += (double)x[i];
-    red[threadIdx.x] = s;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-      __syncthreads();
-    }
-    const double mean = red[0] / n;
-    __syncthreads();
-    double q = 0.0;
-    for (int i = threadIdx.x; i < n; i += 256) {
-      const double dv = (double)x[i] - mean;
-      q += dv * dv;
-    }
-    red[threadIdx.x] = q;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-      __syncthreads();
-    }
-    const double var = red[0] / n;
-    __syncthreads();
-    cv[v] = (n <= 1 || mean == 0.0) ? 0.0 : var / (mean * mean);
+// One workgroup of 1024 threads; thread t holds elements t, t + 1024, ... of
+// both vectors in registers (n <= 32768), sums them in that order, then a tree
+// over the threads; the squared deviations are formed from the same registers.
+constexpr int kCvThreads = 1024;
+constexpr int kCvPer = 32;  // 32768 / 1024
+__global__ __launch_bounds__(kCvThreads) void cv2_losses_kernel(const float* __restrict__ imp,
+                                                                const float* __restrict__ load,
+                                                                int n, float w_imp, float w_load,
+                                                                float* __restrict__ losses) {
+  __shared__ double red[2][kCvThreads];
+  const int t = threadIdx.x;
+  float xi[kCvPer], xl[kCvPer];
+#pragma unroll
+  for (int j = 0; j < kCvPer; ++j) {
+    const int i = t + j * kCvThreads;
+    xi[j] = i < n ? imp[i] : 0.f;
+    xl[j] = i < n ? load[i] : 0.f;
   }
-  if (threadIdx.x == 0) {
-    losses[0] = (float)cv[0];
-    losses[1] = (float)cv[1];
-    losses[2] = (float)((double)w_imp * cv[0] + (double)w_load * cv[1]);
+  auto tree = [&](double a, double b, double (&out)[2]) {
+    red[0][t] = a;
+    red[1][t] = b;
+    __syncthreads();
+    for (int o = kCvThreads / 2; o > 0; o >>= 1) {
+      if (t < o) {
+        red[0][t] += red[0][t + o];
+        red[1][t] += red[1][t + o];
+      }
+      __syncthreads();
+    }
+    out[0] = red[0][0];
+    out[1] = red[1][0];
+    __syncthreads();
+  };
+  double si = 0.0, sl = 0.0;
+#pragma unroll
+  for (int j = 0; j < kCvPer; ++j) {
+    si += (double)xi[j];
+    sl += (double)xl[j];
+  }
+  double sum[2];
+  tree(si, sl, sum);
+  const double mi = sum[0] / n, ml = sum[1] / n;
+  double qi = 0.0, ql = 0.0;
+#pragma unroll
+  for (int j = 0; j < kCvPer; ++j) {
+    if (t + j * kCvThreads < n) {
+      const double di = (double)xi[j] - mi, dl = (double)xl[j] - ml;
+      qi += di * di;
+      ql += dl * dl;
+    }
+  }
+  double q[2];
+  tree(qi, ql, q);
+  if (t == 0) {
+    const double cvi = (n <= 1 || mi == 0.0) ? 0.0 : (q[0] / n) / (mi * mi);
+    const double cvl = (n <= 1 || ml == 0.0) ? 0.0 : (q[1] / n) / (ml * ml);
+    losses[0] = (float)cvi;
+    losses[1] = (float)cvl;
+    losses[2] = (float)((double)w_imp * cvi + (double)w_load * cvl);
   }
 }
 
@@ -157,7 +179,8 @@ hipError_t launch_offsets_to_load(const int32_t* offsets, int n, float* load, hi
 
 hipError_t launch_cv2_losses(const float* importance, const float* load, int n, float w_imp,
                              float w_load, float* losses, hipStream_t s) {
-  hipLaunchKernelGGL(cv2_losses_kernel, dim3(1), dim3(256), 0, s, importance, load, n, w_imp,
+  if (n > kCvThreads * kCvPer) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(cv2_losses_kernel, dim3(1), dim3(kCvThreads), 0, s, importance, load, n, w_imp,
                      w_load, losses);
   return hipGetLastError();
 }

@@ -23,8 +23,19 @@ __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restric
   const int part = threadIdx.x >> 5;
   const int e = blockIdx.x * 32 + col;
   float s = 0.f;
-  if (e < n)
-    for (int b = part; b < nblocks; b += 8) s += partial[(int64_t)b * n + e];
+  if (e < n) {
+    // four loads in flight, added in block order
+    int b = part;
+    for (; b + 24 < nblocks; b += 32) {
+      const float v0 = partial[(int64_t)b * n + e], v1 = partial[(int64_t)(b + 8) * n + e];
+      const float v2 = partial[(int64_t)(b + 16) * n + e], v3 = partial[(int64_t)(b + 24) * n + e];
+      s += v0;
+      s += v1;
+      s += v2;
+      s += v3;
+    }
+    for (; b < nblocks; b += 8) s += partial[(int64_t)b * n + e];
+  }
   red[part][col] = s;
   __syncthreads();
   if (part == 0 && e < n) {

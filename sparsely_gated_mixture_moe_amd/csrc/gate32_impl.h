@@ -25,7 +25,8 @@
 // experts and keeps the token's L best (H, expert) of the experts it sees (in
 // increasing order, so it rarely needs to insert once its list is warm); lanes
 // l and l ^ 32 (the two halves of a token's experts) merge at the end. The
-// noise draws and biases ride a three-slot LDS ring two chunks ahead.
+// noise draws and biases ride a five-slot LDS ring four chunks ahead, copied
+// by waves 4-7 while waves 0-3 copy the weights.
 // Pass 2 multiplies x (A) by the weights (B): lane l holds expert column l % 32
 // for 16 rows, the clean logit (columns 0-15) or the noise pre-activation
 // (16-31); lanes l and l ^ 16 swap half of their rows (v_permlane16_swap) so
@@ -70,9 +71,10 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   __shared__ U16 wbuf0[NKB * 64];
   __shared__ U16 wbuf1[NKB * 64];
   // pass 1: noise draws of a chunk, [256 rows][16 experts] fp32, then one copy
-  // of the chunk's 16 biases per wave; four chunks in flight
+  // of the chunk's 16 biases per wave; a ring of NE slots, NE - 1 chunks ahead
   constexpr int ESLOT = kG32Rows * kG32Chunk + kG32Waves * kG32Chunk;
-  __shared__ float ebuf[PASS2 ? 1 : 3][PASS2 ? 1 : ESLOT];
+  constexpr int NE = 5;
+  __shared__ float ebuf[PASS2 ? 1 : NE][PASS2 ? 1 : ESLOT];
   __shared__ float thrbuf[PASS2 ? kG32Rows : 1];  // pass 2: each row's k-th logit
   // pass 2: each wave's copy of a chunk's 16 biases, double-buffered by chunk parity
   __shared__ float bbuf[PASS2 ? 2 : 1][PASS2 ? kG32Waves * kG32Chunk : 1];
@@ -127,17 +129,28 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     li[j] = 0x7FFFFFFF;
   }
 
-  // Chunk c -> LDS buffer dst. Wave w copies fragments kb = w + 8 i; lane l's
-  // 16 bytes are B column l32 (clean row of expert 16 c + l32, or the noise row
-  // of expert 16 c + l32 - 16), K unit 2 kb + hi: a fixed per-lane source plus
-  // a chunk offset common to the wave.
+  // Chunk c -> LDS buffer dst: lane l's 16 bytes are column l32 (clean row of
+  // expert 16 c + l32, or the noise row of expert 16 c + l32 - 16), K unit
+  // 2 kb + hi, a fixed per-lane source plus a chunk offset common to the
+  // wave. Pass 2: wave w copies fragments kb = w + 8 i. Pass 1: waves 0-3 copy
+  // all fragments (kb = w + 4 i) and waves 4-7 all noise draws, so that each
+  // wave's in-order copy counter waits on one stream only: the weights must
+  // land within a pass, the noise draws have NE - 2 more.
   const bf16* wlane = (clean_lane ? wg : wn) + (int64_t)(l32 & 15) * D + hi * UE;
   auto dma = [&](int c, U16* dst) {
     const bf16* src = wlane + (int64_t)c * EC * D;
+    if constexpr (PASS2) {
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int kb = wave + kG32Waves * i;
-      copy16_to_lds(src + kb * 2 * UE, &dst[kb * 64]);
+      for (int i = 0; i < DMA_PER_WAVE; ++i) {
+        const int kb = wave + kG32Waves * i;
+        copy16_to_lds(src + kb * 2 * UE, &dst[kb * 64]);
+      }
+    } else if (wave < 4) {
+#pragma unroll
+      for (int i = 0; i < 2 * DMA_PER_WAVE; ++i) {
+        const int kb = wave + 4 * i;
+        copy16_to_lds(src + kb * 2 * UE, &dst[kb * 64]);
+      }
     }
   };
   const bool has_bias = p.bias != nullptr;
@@ -186,29 +199,32 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, FPF, 0);
   };
-  // Noise draws of chunk c -> ring slot b (pass 1): wave w copies local rows
-  // 32 w + 16 i + (l / 4), experts 4 (l % 4) .. + 3 of the chunk, so the slot
-  // holds the block's [256][16] tile row-major. This kernel runs only when n is
-  // a multiple of 16, so every 16-byte group is aligned and inside its row;
-  // rows past the tile's end read the tile's first row and are masked in the
-  // epilogue.
-  const float* elane[2];
+  // Noise draws of chunk c -> ring slot b (pass 1, waves 4-7): wave 4 + v
+  // copies local rows 64 v + 16 i + (l / 4), experts 4 (l % 4) .. + 3 of the
+  // chunk, so the slot holds the block's [256][16] tile row-major. This kernel
+  // runs only when n is a multiple of 16, so every 16-byte group is aligned
+  // and inside its row; rows past the tile's end read the tile's first row and
+  // are masked in the epilogue.
+  const int ev = wave & 3;
+  const float* elane[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int64_t r = tile_iorow(p, tile, wrow0 + 16 * i + (lane >> 2));
+  for (int i = 0; i < 4; ++i) {
+    int64_t r = tile_iorow(p, tile, 64 * ev + 16 * i + (lane >> 2));
     if (r < 0) r = tile_iorow(p, tile, 0);
     elane[i] = p.eps + r * n + 4 * (lane & 3);
   }
+  constexpr int EPS_COPIES = 5;  // per wave and chunk: 4 row groups, 1 bias copy
   auto dma_eps = [&](int c, int b) {
+    if (wave >= 4) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float* src = elane[i] + c * EC;
-      copy16_to_lds(src, &ebuf[b][(wave * 32 + 16 * i) * EC]);
-    }
-    // lanes 0-3 copy the chunk's biases (or, without a bias, any in-bounds
-    // floats, which are never read) into this wave's slot
-    if (lane < 4) {
-      copy16_to_lds(bias_src + c * EC + 4 * lane, &ebuf[b][kG32Rows * EC + wave * EC]);
+      for (int i = 0; i < 4; ++i) {
+        const float* src = elane[i] + c * EC;
+        copy16_to_lds(src, &ebuf[b][(64 * ev + 16 * i) * EC]);
+      }
+      // lanes 0-7 copy the chunk's biases (or, without a bias, any in-bounds
+      // floats, which are never read) into the slots of waves 2 v and 2 v + 1
+      if (lane < 8)
+        copy16_to_lds(bias_src + c * EC + 4 * (lane & 3), &ebuf[b][kG32Rows * EC + 2 * ev * EC]);
     }
   };
 
@@ -234,7 +250,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   dma(0, wbuf0);
   if (nchunks > 1) dma(1, wbuf1);
   if constexpr (!PASS2) {
-    for (int c = 0; c < 2 && c < nchunks; ++c) dma_eps(c, c);
+    for (int c = 0; c < NE - 1 && c < nchunks; ++c) dma_eps(c, c);
   }
   if constexpr (PASS2) dma_bias(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -258,19 +274,19 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     U16* const wfill = P ? wbuf1 : wbuf0;       // buffer c & 1: chunk c + 2 goes here
     const U16* const wnext = P ? wbuf0 : wbuf1;  // buffer (c + 1) & 1: chunk c + 1
     f32x16& acc = accs[P];
-    // Copies issued this pass, oldest first: (pass 2) chunk c + 1's biases into
-    // bias slot P ^ 1, chunk c + 2's weights into buffer c & 1 (whose chunk c every
-    // wave used before the last barrier), and (pass 1) chunk c + 2's noise
-    // draws and biases into ring slot (c + 2) % 3 (chunk c - 1's, used in the
-    // last pass). The weights must land by the end of this pass; the noise
-    // draws have one more pass.
+    // Copies issued this pass: (pass 2) chunk c + 1's biases into bias slot
+    // P ^ 1, chunk c + 2's weights into buffer c & 1 (whose chunk c every wave
+    // used before the last barrier), and (pass 1) chunk c + NE - 1's noise
+    // draws and biases into ring slot (c + NE - 1) % NE (chunk c - 1's, used
+    // in the last pass). The weights must land by the end of this pass; the
+    // noise draws of chunk c + 1 too, those of later chunks may stay in flight.
     if constexpr (PASS2) {
       if (c + 1 < nchunks) dma_bias(c + 1, P ^ 1);
     }
     if (c + 2 < nchunks) dma(c + 2, wfill);
     asm volatile("" ::: "memory");
     if constexpr (!PASS2) {
-      if (c + 2 < nchunks) dma_eps(c + 2, (c + 2) % 3);
+      if (c + NE - 1 < nchunks) dma_eps(c + NE - 1, (c + NE - 1) % NE);
     }
 
     float colsum = 0.f;
@@ -335,12 +351,12 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       // operations run while this chunk's epilogue occupies the vector ALUs.
       mfma_chunk(wnext, accs[P ^ 1]);
       __builtin_amdgcn_sched_barrier(0);
-      const float* er = &ebuf[c % 3][(wave * 32 + l32) * EC + 4 * hi];
+      const float* er = &ebuf[c % NE][(wave * 32 + l32) * EC + 4 * hi];
       const f32x4 e0 = *reinterpret_cast<const f32x4*>(er);
       const f32x4 e1 = *reinterpret_cast<const f32x4*>(er + 8);
       f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
       if (has_bias) {
-        const float* br = &ebuf[c % 3][kG32Rows * EC + wave * EC + 4 * hi];
+        const float* br = &ebuf[c % NE][kG32Rows * EC + wave * EC + 4 * hi];
         b0 = *reinterpret_cast<const f32x4*>(br);
         b1 = *reinterpret_cast<const f32x4*>(br + 8);
       }
@@ -355,11 +371,17 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
 
     // Block barrier without a release fence (which would wait for every copy
-    // in flight): each wave first waits for its LDS traffic and for all its
-    // copies but the three noise/bias copies issued this pass, if any (copies
-    // complete in issue order, so a count of 3 then covers the weights).
-    if (!PASS2 && c + 2 < nchunks) {
-      asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // in flight): each wave first waits for its LDS traffic and for its
+    // copies; in pass 1 the noise waves leave the copies of chunks c + 2 ..
+    // c + NE - 1 in flight (copies complete in issue order, so the count
+    // covers everything older).
+    static_assert(NE == 5, "the waits below count NE - 2 chunks of noise copies");
+    if (!PASS2 && wave >= 4 && c + 4 < nchunks) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * EPS_COPIES) : "memory");
+    } else if (!PASS2 && wave >= 4 && c + 3 < nchunks) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * EPS_COPIES) : "memory");
+    } else if (!PASS2 && wave >= 4 && c + 2 < nchunks) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(EPS_COPIES) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
