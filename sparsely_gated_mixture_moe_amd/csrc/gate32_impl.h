@@ -298,7 +298,9 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       // column sums: lanes l, l ^ 16 (same expert, other rows) and l ^ 32
       colsum += __shfl_xor(colsum, 16);
       colsum += __shfl_xor(colsum, 32);
-      if (lane < 16) red[P][wave][lane] = colsum;
+      if constexpr (PASS2) {
+        if (lane < 16) red[P][wave][lane] = colsum;
+      }
     };
     if constexpr (PASS2) {
       // Load pass: the next chunk's products with this chunk's pairs woven

@@ -208,7 +208,12 @@ def test_combine_parity(case):
     assert err <= out_tol(w.act_dtype == dg.BF16)
 
 
-AUX_CASES = GATE_CASES[:4] + GATE_CASES[6:]
+# plus segments long enough for the Load correction to split them over 8 and
+# 16 workgroups per expert (uniform and Zipf-skewed routing)
+AUX_CASES = GATE_CASES[:4] + GATE_CASES[6:] + [
+    ("flat_bf16_n4096", {"tokens": 16384, "n_experts": 8, "k": 2}),
+    ("zipf_bf16_n256", {"tokens": 16384, "n_experts": 64}),
+]
 
 
 @pytest.mark.parametrize("case", AUX_CASES, ids=[_gate_ids(c) for c in AUX_CASES])
