@@ -16,8 +16,8 @@
 //    2 weaves its per-pair work between them (measured faster for pass 2's
 //    longer per-pair work; pass 1's epilogue reads LDS and branches).
 //
-// Epilogue. Pass 1 multiplies weights (A operand, from LDS) by x (B operand,
-// in registers), so in the 32x32 C layout lane l holds token l % 32 and rows
+// Epilogue. Both passes multiply weights (A operand, from LDS) by x (B
+// operand, in registers), so in the 32x32 C layout lane l holds token l % 32 and rows
 // 8 (j / 4) + 4 (l / 32) + j % 4 of the weight tile: registers j < 8 are the
 // clean logits of experts 4 (l / 32) + (0..3) and 8 + 4 (l / 32) + (0..3) of
 // the chunk, registers 8 + j the noise pre-activations of the same experts.
@@ -27,13 +27,12 @@
 // l and l ^ 32 (the two halves of a token's experts) merge at the end. The
 // noise draws and biases ride a five-slot LDS ring four chunks ahead, copied
 // by waves 4-7 while waves 0-3 copy the weights.
-// Pass 2 multiplies x (A) by the weights (B): lane l holds expert column l % 32
-// for 16 rows, the clean logit (columns 0-15) or the noise pre-activation
-// (16-31); lanes l and l ^ 16 swap half of their rows (v_permlane16_swap) so
-// each holds (clean, noise) pairs for 8 rows of one expert, evaluates
-// P = Phi((clean - v_k) / sigma) and sums each expert's column over the
-// block's rows in a fixed order (the selected pairs are corrected to the
-// (k+1)-th threshold separately).
+// Pass 2 evaluates P = Phi((clean - v_k) / sigma) for the same 8 (token,
+// expert) pairs of each lane and sums every expert's column over the wave's
+// 32 tokens with a transposing reduction across lanes (lane swaps and DPP
+// moves, each step halving the values a lane holds), then over the block's
+// waves, in a fixed order (the selected pairs are corrected to the (k+1)-th
+// threshold separately).
 #pragma once
 
 #include "gate_impl.h"
@@ -77,7 +76,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   __shared__ float ebuf[PASS2 ? 1 : NE][PASS2 ? 1 : ESLOT];
   __shared__ float thrbuf[PASS2 ? kG32Rows : 1];  // pass 2: each row's k-th logit
   // pass 2: each wave's copy of a chunk's 16 biases, double-buffered by chunk parity
-  __shared__ float bbuf[PASS2 ? 2 : 1][PASS2 ? kG32Waves * kG32Chunk : 1];
+  __shared__ __attribute__((aligned(16))) float bbuf[PASS2 ? 2 : 1][PASS2 ? kG32Waves * kG32Chunk : 1];
   __shared__ float red[PASS2 ? 2 : 1][kG32Waves][EC];
 
   const int tid = threadIdx.x;
@@ -91,7 +90,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   const bf16* wg = reinterpret_cast<const bf16*>(p.wg);
   const bf16* wn = reinterpret_cast<const bf16*>(p.wn);
 
-  // x rows of this wave as MFMA operands (B in pass 1, A in pass 2): lane
+  // x rows of this wave as the B operands of the matrix products: lane
   // supplies row l32, unit 2 kb + hi.
   U16 xa[NKB];
   {
@@ -102,16 +101,10 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       xa[kb] = (r >= 0) ? ld_unit(x + r * D + (kb * 2 + hi) * UE) : zero_unit();
   }
 
-  // Pass 2: rows of this lane's (clean, noise) pairs after the exchange:
-  // element i is C-layout register j = i (clean lanes) or 8 + i (noise
-  // lanes). Rows past the tile's end compute finite garbage (zero x, the
-  // first row's noise): pass 1 never writes them out, pass 2 gives them
-  // thresholds of +inf, so their P is exactly 0. n is a multiple of 16, so
-  // every expert is valid.
-  int rr[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) rr[i] = (clean_lane ? 0 : 16) + 8 * (i / 4) + 4 * hi + (i % 4);
-
+  // Rows past the tile's end compute finite garbage (zero x, the first row's
+  // noise): pass 1 never writes them out, pass 2 gives them thresholds of
+  // +inf, so their P is exactly 0. n is a multiple of 16, so every expert is
+  // valid.
   if constexpr (PASS2) {
     for (int t = tid; t < kG32Rows; t += kG32Threads) {
       const int64_t row = tile_iorow(p, tile, t);
@@ -155,12 +148,12 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   };
   const bool has_bias = p.bias != nullptr;
   const float* bias_src = has_bias ? p.bias : reinterpret_cast<const float*>(p.wg);
-  // Pass 2: lanes 0-3 copy chunk c's biases (or, without a bias, any
-  // in-bounds floats, which are never read) into this wave's slot. A copy, not
-  // a register load, so that no compiler-inserted wait on the memory counter
-  // stalls the epilogue behind the weight copies in flight.
+  // Pass 2: lanes 0-3 copy chunk c's 16 biases into this wave's slot (which
+  // holds zeros when the gate has no bias). A copy, not a register load, so
+  // that no compiler-inserted wait on the memory counter stalls the epilogue
+  // behind the weight copies in flight.
   auto dma_bias = [&](int c, int slot) {
-    if (lane < 4) copy16_to_lds(bias_src + c * EC + 4 * lane, &bbuf[slot][wave * EC]);
+    if (has_bias && lane < 4) copy16_to_lds(bias_src + c * EC + 4 * lane, &bbuf[slot][wave * EC]);
   };
   // One chunk's products: 32 x 32 tile of (rows, clean|noise columns) over
   // the K-blocks. Fragments are read four ahead of their matrix product; the
@@ -183,10 +176,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       U16 cur;
       __builtin_memcpy(&cur, &f[kb % FPF], 16);
       if (kb + FPF < NKB) f[kb % FPF] = bl[(kb + FPF) * 64];
-      if constexpr (PASS2)
-        Mfma<bf16>::k32(acc, xa[kb], cur);  // rows: tokens, columns: weights
-      else
-        Mfma<bf16>::k32(acc, cur, xa[kb]);  // rows: weights, columns: tokens
+      Mfma<bf16>::k32(acc, cur, xa[kb]);  // rows: weights, columns: tokens
     }
     // Keep that order (the scheduler would otherwise pull the reads down next
     // to their use): FPF reads, then matrix product / read pairs, then the
@@ -252,7 +242,12 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   if constexpr (!PASS2) {
     for (int c = 0; c < NE - 1 && c < nchunks; ++c) dma_eps(c, c);
   }
-  if constexpr (PASS2) dma_bias(0, 0);
+  if constexpr (PASS2) {
+    if (!has_bias) {
+      for (int t = tid; t < 2 * kG32Waves * EC; t += kG32Threads) (&bbuf[0][0])[t] = 0.f;
+    }
+    dma_bias(0, 0);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   mfma_chunk(wbuf0, accs[0]);
@@ -261,11 +256,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // Pass 2 evaluates every pair against its row's k-th largest logit (+inf
   // for rows past the tile's end, so their P is 0); the selected pairs'
   // difference (threshold (k+1)-th) is added by a separate kernel.
-  float thrk[8];
-  if constexpr (PASS2) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) thrk[i] = thrbuf[wave * 32 + rr[i]];
-  }
+  float thrk = 0.f;
+  if constexpr (PASS2) thrk = thrbuf[wave * 32 + l32];
 
   // One pass per chunk; P = c & 1 is a compile-time constant (the loop below
   // is unrolled by two) so each pass names its buffers statically.
@@ -289,23 +281,16 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       if (c + NE - 1 < nchunks) dma_eps(c + NE - 1, (c + NE - 1) % NE);
     }
 
-    float colsum = 0.f;
-    // Pass 2's exchange within each pair of 16-lane rows: the odd row's
-    // (noise lanes') register acc[i] trades places with the even row's (clean
-    // lanes') register acc[8 + i]; afterwards the lane holds, for its row
-    // rr[i], the clean logit (first) and the noise pre-activation (second).
-    auto finish = [&]() {
-      // column sums: lanes l, l ^ 16 (same expert, other rows) and l ^ 32
-      colsum += __shfl_xor(colsum, 16);
-      colsum += __shfl_xor(colsum, 32);
-      if constexpr (PASS2) {
-        if (lane < 16) red[P][wave][lane] = colsum;
-      }
-    };
     if constexpr (PASS2) {
       // Load pass: the next chunk's products with this chunk's pairs woven
       // in, one pair after every eighth of the products, so that each pair's
       // vector work issues while the matrix core is busy.
+      // This lane's 8 biases and the first reads ahead are issued before the
+      // woven region below: the scheduler keeps the weave's pattern only
+      // when that region starts with the products and reads of K-blocks.
+      const float* br = &bbuf[P][wave * EC + 4 * hi];
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(br);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(br + 8);
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       typedef const __attribute__((address_space(3))) u32x4* LdsPtr;
       uint32_t base = (uint32_t)(uintptr_t)(wnext + lane);
@@ -314,12 +299,13 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       u32x4 f[FPF];
 #pragma unroll
       for (int j = 0; j < FPF; ++j) f[j] = bl[j * 64];
+      __builtin_amdgcn_sched_barrier(0);
       f32x16& an = accs[P ^ 1];
 #pragma unroll
       for (int j = 0; j < 16; ++j) an[j] = 0.f;
-      const float bias = has_bias ? bbuf[P][wave * EC + (l32 & 15)] : 0.f;
       constexpr int MPE = NKB / 8;
       static_assert(NKB % 8 == 0, "whole K-blocks per pair");
+      float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -328,14 +314,14 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
           U16 cur;
           __builtin_memcpy(&cur, &f[kb % FPF], 16);
           if (kb + FPF < NKB) f[kb % FPF] = bl[(kb + FPF) * 64];
-          Mfma<bf16>::k32(an, xa[kb], cur);
+          Mfma<bf16>::k32(an, cur, xa[kb]);
         }
-        // the exchange (see finish), then P of pair i
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i]),
-                                                          __float_as_uint(acc[8 + i]), false, false);
-        const float clean = __uint_as_float(sw[0]) + bias;
-        const float sigma = softplus_f(__uint_as_float(sw[1])) + p.floor;
-        colsum += phi_f((clean - thrk[i]) * rcp_f(sigma));
+        // pairs in the order 0, 4, 1, 5, ...: the reduction's first step
+        // pairs values i and i + 4, so it can start inside the weave
+        const int e = (i >> 1) + 4 * (i & 1);
+        const float clean = acc[e] + (e < 4 ? b0[e] : b1[e - 4]);
+        const float sigma = softplus_f(acc[8 + e]) + p.floor;
+        pv[e] = phi_f((clean - thrk) * rcp_f(sigma));
       }
       // reads ahead, then (product, read, vector work) triples
       constexpr int V = (kG32PhiValu + MPE - 1) / MPE;
@@ -347,7 +333,41 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      finish();
+      // Column sums over the wave's 32 tokens (lanes of equal hi). Lane l
+      // holds value j for expert 8 (j / 4) + 4 hi + j % 4. Each step pairs
+      // lanes that hold the same values, keeps half of them and adds the
+      // partner's copy of that half: lanes l, l ^ 16 (v_permlane16_swap
+      // exchanges the upper row's j with the lower row's j + 4), then l, l ^ 8
+      // (DPP row rotation by 8), then the lanes mirrored within each 8-lane
+      // half-row (which differ in bit 2), then the quad. Afterwards lane l
+      // holds the total of value j = (l / 4) % 8 for its half.
+      float s4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(pv[i]),
+                                                          __float_as_uint(pv[i + 4]), false, false);
+        s4[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+      float s2[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float keep = b3 ? s4[i + 2] : s4[i];
+        const float send = b3 ? s4[i] : s4[i + 2];
+        s2[i] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x128, 0xF, 0xF, true));
+      }
+      float s1;
+      {
+        const float keep = b2 ? s2[1] : s2[0];
+        const float send = b2 ? s2[0] : s2[1];
+        s1 = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x141, 0xF, 0xF, true));
+      }
+      s1 += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0xB1, 0xF, 0xF, true));
+      s1 += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0x4E, 0xF, 0xF, true));
+      if ((lane & 3) == 0) {
+        const int j = (lane >> 2) & 7;
+        red[P][wave][8 * (j >> 2) + 4 * hi + (j & 3)] = s1;
+      }
     } else {
       // Selection pass: the next chunk's products go first; their matrix
       // operations run while this chunk's epilogue occupies the vector ALUs.
