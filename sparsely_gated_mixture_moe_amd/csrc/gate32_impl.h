@@ -51,9 +51,14 @@ struct IntConst {
   static constexpr int value = V;
 };
 
-// Vector instructions of one Load-pass pair (exchange, Softplus, Phi, sum):
-// the scheduler spreads this many over the matrix products that precede it.
+// Biases of a gate without one: every chunk copies these 16 zeros.
+__device__ const float kZeroBias[kG32Chunk] = {};
+
+// Vector instructions of one Load-pass pair (Softplus, Phi) and of one noisy
+// logit of the selection pass (Softplus, noise, bias): the scheduler spreads
+// this many over the matrix products that precede it.
 constexpr int kG32PhiValu = 30;
+constexpr int kG32HValu = 12;
 
 template <int D, int L, bool PASS2>
 __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
@@ -147,13 +152,15 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
   };
   const bool has_bias = p.bias != nullptr;
-  const float* bias_src = has_bias ? p.bias : reinterpret_cast<const float*>(p.wg);
-  // Pass 2: lanes 0-3 copy chunk c's 16 biases into this wave's slot (which
-  // holds zeros when the gate has no bias). A copy, not a register load, so
+  // chunk c's biases: bias_src + c * bias_step
+  const float* bias_src = has_bias ? p.bias : kZeroBias;
+  const int bias_step = has_bias ? EC : 0;
+  // Pass 2: lanes 0-3 copy chunk c's 16 biases into this wave's slot. A
+  // copy, not a register load, so
   // that no compiler-inserted wait on the memory counter stalls the epilogue
   // behind the weight copies in flight.
   auto dma_bias = [&](int c, int slot) {
-    if (has_bias && lane < 4) copy16_to_lds(bias_src + c * EC + 4 * lane, &bbuf[slot][wave * EC]);
+    if (lane < 4) copy16_to_lds(bias_src + c * bias_step + 4 * lane, &bbuf[slot][wave * EC]);
   };
   // One chunk's products: 32 x 32 tile of (rows, clean|noise columns) over
   // the K-blocks. Fragments are read four ahead of their matrix product; the
@@ -190,18 +197,20 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     __builtin_amdgcn_sched_group_barrier(0x008, FPF, 0);
   };
   // Noise draws of chunk c -> ring slot b (pass 1, waves 4-7): wave 4 + v
-  // copies local rows 64 v + 16 i + (l / 4), experts 4 (l % 4) .. + 3 of the
-  // chunk, so the slot holds the block's [256][16] tile row-major. This kernel
-  // runs only when n is a multiple of 16, so every 16-byte group is aligned
-  // and inside its row; rows past the tile's end read the tile's first row and
-  // are masked in the epilogue.
+  // copies local rows 64 v + 16 i + (l / 4), so the slot holds the block's
+  // [256][16] tile with each row's four 16-byte groups swizzled: group g of
+  // row R sits at position g ^ ((R / 2) % 4), so that the reads of eight
+  // consecutive rows' group fall in distinct banks. This kernel runs only when
+  // n is a multiple of 16, so every 16-byte group is aligned and inside its
+  // row; rows past the tile's end read the tile's first row and are masked in
+  // the epilogue.
   const int ev = wave & 3;
   const float* elane[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int64_t r = tile_iorow(p, tile, 64 * ev + 16 * i + (lane >> 2));
     if (r < 0) r = tile_iorow(p, tile, 0);
-    elane[i] = p.eps + r * n + 4 * (lane & 3);
+    elane[i] = p.eps + r * n + 4 * ((lane & 3) ^ ((lane >> 3) & 3));
   }
   constexpr int EPS_COPIES = 5;  // per wave and chunk: 4 row groups, 1 bias copy
   auto dma_eps = [&](int c, int b) {
@@ -211,10 +220,10 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         const float* src = elane[i] + c * EC;
         copy16_to_lds(src, &ebuf[b][(64 * ev + 16 * i) * EC]);
       }
-      // lanes 0-7 copy the chunk's biases (or, without a bias, any in-bounds
-      // floats, which are never read) into the slots of waves 2 v and 2 v + 1
+      // lanes 0-7 copy the chunk's biases into the slots of waves 2 v and 2 v + 1
       if (lane < 8)
-        copy16_to_lds(bias_src + c * EC + 4 * (lane & 3), &ebuf[b][kG32Rows * EC + 2 * ev * EC]);
+        copy16_to_lds(bias_src + c * bias_step + 4 * (lane & 3),
+                      &ebuf[b][kG32Rows * EC + 2 * ev * EC]);
     }
   };
 
@@ -242,12 +251,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   if constexpr (!PASS2) {
     for (int c = 0; c < NE - 1 && c < nchunks; ++c) dma_eps(c, c);
   }
-  if constexpr (PASS2) {
-    if (!has_bias) {
-      for (int t = tid; t < 2 * kG32Waves * EC; t += kG32Threads) (&bbuf[0][0])[t] = 0.f;
-    }
-    dma_bias(0, 0);
-  }
+  if constexpr (PASS2) dma_bias(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   mfma_chunk(wbuf0, accs[0]);
@@ -369,26 +373,55 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         red[P][wave][8 * (j >> 2) + 4 * hi + (j & 3)] = s1;
       }
     } else {
-      // Selection pass: the next chunk's products go first; their matrix
-      // operations run while this chunk's epilogue occupies the vector ALUs.
-      mfma_chunk(wnext, accs[P ^ 1]);
+      // Selection pass: this chunk's noise draws and biases are read first,
+      // then the next chunk's products with this chunk's noisy logits woven
+      // in (one after every eighth of the products); the insertions, which
+      // branch, follow the products.
+      const float* er = &ebuf[c % NE][(wave * 32 + l32) * EC];
+      const int sw = (l32 >> 1) & 3;  // the row's group swizzle
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(er + 4 * (hi ^ sw));
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(er + 4 * ((2 + hi) ^ sw));
+      const float* bp = &ebuf[c % NE][kG32Rows * EC + wave * EC + 4 * hi];
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 8);
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      typedef const __attribute__((address_space(3))) u32x4* LdsPtr;
+      uint32_t base = (uint32_t)(uintptr_t)(wnext + lane);
+      asm("" : "+v"(base));
+      const LdsPtr bl = (LdsPtr)base;
+      u32x4 f[FPF];
+#pragma unroll
+      for (int j = 0; j < FPF; ++j) f[j] = bl[j * 64];
       __builtin_amdgcn_sched_barrier(0);
-      const float* er = &ebuf[c % NE][(wave * 32 + l32) * EC + 4 * hi];
-      const f32x4 e0 = *reinterpret_cast<const f32x4*>(er);
-      const f32x4 e1 = *reinterpret_cast<const f32x4*>(er + 8);
-      f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
-      if (has_bias) {
-        const float* br = &ebuf[c % NE][kG32Rows * EC + wave * EC + 4 * hi];
-        b0 = *reinterpret_cast<const f32x4*>(br);
-        b1 = *reinterpret_cast<const f32x4*>(br + 8);
-      }
+      f32x16& an = accs[P ^ 1];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) an[j] = 0.f;
+      constexpr int MPE = NKB / 8;
+      static_assert(NKB % 8 == 0, "whole K-blocks per noisy logit");
       float hv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < MPE; ++j) {
+          const int kb = i * MPE + j;
+          U16 cur;
+          __builtin_memcpy(&cur, &f[kb % FPF], 16);
+          if (kb + FPF < NKB) f[kb % FPF] = bl[(kb + FPF) * 64];
+          Mfma<bf16>::k32(an, cur, xa[kb]);
+        }
         const float eps = i < 4 ? e0[i] : e1[i - 4];
         const float bias = i < 4 ? b0[i] : b1[i - 4];
         hv[i] = fmaf(eps, softplus_f(acc[8 + i]) + p.floor, acc[i] + bias);
       }
+      constexpr int V = (kG32HValu + MPE - 1) / MPE;
+      __builtin_amdgcn_sched_group_barrier(0x100, FPF, 0);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (kb + FPF < NKB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       insert_pairs(hv, c);
     }
 
