@@ -9,6 +9,6 @@ PyTorch is used only for device memory and streams.
 from ._binding import (  # noqa: F401
     LIB_PATH, MOE_BF16, MOE_F32, MoeDims, MoeError, MoeForward, MoeGateOpts, MoeHierDims,
     MoeHierForward, MoeHierOutputs, lib, make_dims, make_opts, moe_aux_losses, moe_combine,
-    moe_expert_ffn, moe_forward, moe_gate, moe_hier_forward, moe_route, moe_workspace_size,
-    workspace,
+    moe_expert_ffn, moe_ffn_timing, moe_ffn_timing_read, moe_forward, moe_gate, moe_hier_forward,
+    moe_route, moe_workspace_size, workspace,
 )

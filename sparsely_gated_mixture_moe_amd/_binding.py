@@ -85,8 +85,12 @@ def lib():
         L.moe_hier_workspace_size.restype = ctypes.c_size_t
         L.moe_hier_forward.argtypes = ([HD, O] + [_P] * 15 + [ctypes.POINTER(MoeHierOutputs), _P, S,
                                                               _P])
+        L.moe_ffn_timing.argtypes = [ctypes.c_int]
+        L.moe_ffn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_double)]
         for f in ("moe_gate", "moe_route", "moe_expert_ffn", "moe_combine", "moe_aux_losses",
-                  "moe_forward", "moe_hier_forward"):
+                  "moe_forward", "moe_hier_forward", "moe_ffn_timing",
+                  "moe_ffn_timing_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -130,6 +134,19 @@ def _ptr(t: Optional[torch.Tensor]):
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def moe_ffn_timing(enable: bool) -> None:
+    """Start (clearing the record) or stop timing the expert-FFN kernel of
+    forward calls on the current device."""
+    _check(lib().moe_ffn_timing(1 if enable else 0), "moe_ffn_timing")
+
+
+def moe_ffn_timing_read() -> Tuple[int, float]:
+    """(timed expert-FFN kernels, their summed duration in ms); waits for them."""
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(lib().moe_ffn_timing_read(ctypes.byref(n), ctypes.byref(ms)), "moe_ffn_timing_read")
+    return int(n.value), float(ms.value)
 
 
 def make_dims(tokens: int, d_model: int, d_hidden: int, n_experts: int, k: int,

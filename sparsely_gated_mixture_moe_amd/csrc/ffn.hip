@@ -520,11 +520,16 @@ hipError_t device_cus(int* cus) {
 
 template <typename T, int D>
 hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* offsets, int n,
-                        hipStream_t s) {
+                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   using S = FfnShape<T, D>;
   hipLaunchKernelGGL(ffn_plan, dim3(1), dim3(1024), 0, s, offsets, n, S::BM,
                      const_cast<int32_t*>(p.blocks));
-  if (max_blocks <= 0) return hipGetLastError();
+  if (max_blocks <= 0) {  // no rows: an empty timed interval
+    hipError_t er = hipGetLastError();
+    if (er == hipSuccess && ev0) er = hipEventRecord(ev0, s);
+    if (er == hipSuccess && ev1) er = hipEventRecord(ev1, s);
+    return er;
+  }
   // one persistent workgroup per compute unit (the LDS tile allows one), a
   // multiple of 8 so that every XCD gets the same number of slots, and no
   // more than the largest possible unit count needs
@@ -533,8 +538,14 @@ hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* o
   if (e != hipSuccess) return e;
   const int64_t want = (max_blocks + 7) / 8 * 8;
   const int64_t grid = std::min<int64_t>(want, std::max(8, cus / 8 * 8));
+  if (ev0) {
+    const hipError_t er = hipEventRecord(ev0, s);
+    if (er != hipSuccess) return er;
+  }
   hipLaunchKernelGGL((ffn_kernel<T, D>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
-  return hipGetLastError();
+  const hipError_t el = hipGetLastError();
+  if (el != hipSuccess || !ev1) return el;
+  return hipEventRecord(ev1, s);
 }
 
 template <typename T>
@@ -570,22 +581,22 @@ bool ffn_supported(int d, int h, Dt dt) {
 hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const void* x,
                       const int32_t* offsets, const int32_t* perm_token, const void* w1,
                       const void* b1, const void* w2, const void* b2, void* expert_out,
-                      int32_t* blocks, hipStream_t s) {
+                      int32_t* blocks, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   FfnParams p{x, offsets, perm_token, w1, b1, w2, b2, expert_out, blocks, h};
   const int64_t mb = ffn_max_blocks(tokens * k, n, d, dt);
   if (dt == kBF16) {
     switch (d) {
-      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, s);
-      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, s);
-      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, s);
-      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, s);
+      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, s, ev0, ev1);
+      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, s, ev0, ev1);
+      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, s, ev0, ev1);
+      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, s, ev0, ev1);
     }
   } else {
     switch (d) {
-      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, s);
-      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, s);
-      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, s);
-      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, s);
+      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, s, ev0, ev1);
+      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, s, ev0, ev1);
+      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, s, ev0, ev1);
+      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, s, ev0, ev1);
     }
   }
   return hipErrorInvalidValue;

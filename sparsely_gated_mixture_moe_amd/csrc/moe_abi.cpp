@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -301,11 +302,82 @@ HierLayout hier_layout(const moe_hier_dims* h, const moe_gate_opts* o) {
   return L;
 }
 
+// Timing events around the expert-FFN kernel of forward calls (moe_ffn_timing).
+constexpr int kTimedMax = 1024;
+struct FfnTiming {
+  bool on = false;
+  int dev = -1;
+  int used = 0;
+  hipEvent_t ev[kTimedMax][2] = {};
+};
+std::mutex g_timing_mu;
+FfnTiming g_timing;
+
+// The next pair of events for a forward call on the current device, or
+// nulls when timing is off, on another device or full.
+void timing_pair(hipEvent_t* e0, hipEvent_t* e1) {
+  *e0 = *e1 = nullptr;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  int dev = -1;
+  if (!g_timing.on || hipGetDevice(&dev) != hipSuccess || dev != g_timing.dev ||
+      g_timing.used >= kTimedMax)
+    return;
+  *e0 = g_timing.ev[g_timing.used][0];
+  *e1 = g_timing.ev[g_timing.used][1];
+  ++g_timing.used;
+}
+
 }  // namespace
 
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+moe_status moe_ffn_timing(int enable) {
+  if (enable != 0 && enable != 1) return fail(MOE_ERR_INVALID, "enable = %d is not 0 or 1", enable);
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!enable) {
+    g_timing.on = false;
+    return ok();
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && dev != g_timing.dev) {  // events belong to the device they were made on
+    for (auto& pr : g_timing.ev)
+      for (auto& ev : pr)
+        if (ev) {
+          (void)hipEventDestroy(ev);
+          ev = nullptr;
+        }
+    for (int i = 0; i < kTimedMax && e == hipSuccess; ++i)
+      for (int j = 0; j < 2 && e == hipSuccess; ++j) e = hipEventCreate(&g_timing.ev[i][j]);
+  }
+  if (e != hipSuccess) {
+    g_timing.dev = -1;
+    g_timing.on = false;
+    return device_status(e, "moe_ffn_timing");
+  }
+  g_timing.dev = dev;
+  g_timing.used = 0;
+  g_timing.on = true;
+  return ok();
+}
+
+moe_status moe_ffn_timing_read(int64_t* launches, double* total_ms) {
+  if (!launches || !total_ms) return fail(MOE_ERR_INVALID, "NULL output");
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  double sum = 0.0;
+  for (int i = 0; i < g_timing.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_timing.ev[i][1]);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timing.ev[i][0], g_timing.ev[i][1]);
+    if (e != hipSuccess) return device_status(e, "moe_ffn_timing_read");
+    sum += ms;
+  }
+  *launches = g_timing.used;
+  *total_ms = sum;
+  return ok();
+}
 
 const char* moe_status_string(int s) {
   switch (s) {
@@ -484,9 +556,11 @@ moe_status moe_forward(const moe_dims* dims, const moe_gate_opts* opts, const vo
                         at<int32_t>(ws, L.blockcnt), counts, offsets, perm_token, perm_gate,
                         slot_pos, importance, st);
   if (e != hipSuccess) return device_status(e, "moe_forward (route)");
+  hipEvent_t t0, t1;
+  timing_pair(&t0, &t1);
   e = moe::launch_ffn(dims->tokens, dims->k, dims->d_model, dims->d_hidden, dims->n_experts,
                       to_dt(dims->act_dtype), x, offsets, perm_token, w1, b1, w2, b2, expert_out,
-                      at<int32_t>(ws, L.ffn_blocks), st);
+                      at<int32_t>(ws, L.ffn_blocks), st, t0, t1);
   if (e != hipSuccess) return device_status(e, "moe_forward (expert_ffn)");
   e = moe::launch_combine(dims->tokens, dims->k, dims->d_model, to_dt(dims->act_dtype), expert_out,
                           slot_pos, topk_gate, y, st);
@@ -619,8 +693,10 @@ moe_status moe_hier_forward(const moe_hier_dims* dims, const moe_gate_opts* opts
   e = moe::launch_route(B, K, n, topk_idx, topk_gate, at<int32_t>(ws, L.blockcnt), counts, offsets,
                         perm_token, at<float>(ws, L.perm_gate), slot_pos, importance, st);
   if (e != hipSuccess) return device_status(e, "moe_hier_forward (route)");
+  hipEvent_t t0, t1;
+  timing_pair(&t0, &t1);
   e = moe::launch_ffn(B, K, dims->d_model, dims->d_hidden, n, x_dt, x, offsets, perm_token, w1, b1,
-                      w2, b2, expert_out, at<int32_t>(ws, L.ffn_blocks), st);
+                      w2, b2, expert_out, at<int32_t>(ws, L.ffn_blocks), st, t0, t1);
   if (e != hipSuccess) return device_status(e, "moe_hier_forward (expert_ffn)");
   e = moe::launch_combine(B, K, dims->d_model, x_dt, expert_out, slot_pos, topk_gate, y, st);
   if (e != hipSuccess) return device_status(e, "moe_hier_forward (combine)");

@@ -90,10 +90,13 @@ int64_t ffn_max_blocks(int64_t rows, int n, int d, Dt dt);
 // Bytes of the expert-FFN work-unit list (the count, then 16 bytes per unit).
 size_t ffn_plan_bytes(int64_t rows, int n, int d, Dt dt);
 bool ffn_supported(int d, int h, Dt dt);
+// ev0 / ev1, when given, are recorded on s right before and after the FFN
+// kernel (after its plan kernel).
 hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const void* x,
                       const int32_t* offsets, const int32_t* perm_token, const void* w1,
                       const void* b1, const void* w2, const void* b2, void* expert_out,
-                      int32_t* blocks /* [2*max_blocks + 1] */, hipStream_t s);
+                      int32_t* blocks /* [2*max_blocks + 1] */, hipStream_t s,
+                      hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Weighted sum.
 hipError_t launch_combine(int64_t tokens, int k, int d, Dt dt, const void* expert_out,

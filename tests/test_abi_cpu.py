@@ -124,6 +124,12 @@ def test_workspace_size_scales_with_workload():
     assert L.moe_workspace_size(ctypes.byref(dims(tokens=0)), ctypes.byref(opts())) > 0
 
 
+def test_timing_argument_checks():
+    L = B.lib()
+    assert L.moe_ffn_timing(2) == 1 and L.moe_ffn_timing(-1) == 1  # MOE_ERR_INVALID
+    assert L.moe_ffn_timing_read(None, None) == 1
+
+
 def test_status_strings():
     L = B.lib()
     assert L.moe_status_string(0) == b"MOE_OK"

@@ -372,6 +372,24 @@ def test_forward_is_deterministic():
         assert torch.equal(a, b)
 
 
+def test_ffn_timing_counts_forward_calls():
+    w = wl("flat_bf16_n4096", tokens=4096, n_experts=256)
+    announce("moe_ffn_timing")
+    inp = dg.make_inputs(w)
+    g = gpu_inputs(inp)
+    f = moe.MoeForward(tuple(g["x"].shape), g["w_gate"], g["w_noise"], g["w1"], g["w2"], w.k)
+    f(g["x"], g["eps"])
+    moe.moe_ffn_timing(True)
+    try:
+        for _ in range(3):
+            f(g["x"], g["eps"])
+    finally:
+        moe.moe_ffn_timing(False)
+    f(g["x"], g["eps"])  # not timed
+    n, ms = moe.moe_ffn_timing_read()
+    assert n == 3 and ms > 0
+
+
 def test_empty_batch():
     w = wl("tiny_fp32", tokens=0)
     announce("moe_forward empty batch")
