@@ -181,8 +181,10 @@ def _gate_dims(x, w_gate, k, d_hidden=128, w1=None) -> MoeDims:
 
 
 def moe_gate(x, w_gate, w_noise, eps, k: int, *, train: bool = True, noise_floor: float = 1e-2,
-             gate_bias=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Noisy top-k gating -> (topk_idx [B,k] int32, topk_gate [B,k] fp32, thresh [B,2] fp32)."""
+             gate_bias=None, ws: Optional[torch.Tensor] = None,
+             stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Noisy top-k gating -> (topk_idx [B,k] int32, topk_gate [B,k] fp32, thresh [B,2] fp32).
+    ws (optional, moe_workspace_size bytes) lets a small batch split its expert sweep."""
     _dev(x, "x")
     B, d = x.shape
     _dev(w_gate, "w_gate")
@@ -198,7 +200,7 @@ def moe_gate(x, w_gate, w_noise, eps, k: int, *, train: bool = True, noise_floor
     thr = torch.empty((B, 2), dtype=torch.float32, device=dev)
     st = lib().moe_gate(ctypes.byref(dims), ctypes.byref(opts), _ptr(x), _ptr(w_gate),
                         _ptr(w_noise), _ptr(gate_bias), _ptr(eps), _ptr(idx), _ptr(gate), _ptr(thr),
-                        None, 0, _stream(stream))
+                        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "moe_gate")
     return idx, gate, thr
 

@@ -8,6 +8,9 @@ namespace moe {
 namespace {
 
 using gate_detail::GateParams;
+using gate_detail::GateShape;
+using gate_detail::insert_any;
+using gate_detail::write_selection;
 
 // load[e] = sum over gate blocks b of partial[b][e], in a fixed order: 32
 // experts per workgroup, 8 threads per expert each summing a strided subset
@@ -237,6 +240,31 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
     corr[(int64_t)e * splits + split] = ((part[0] + part[1]) + part[2]) + part[3];
 }
 
+// Merges the candidate lists of a split selection: row t's `ranges` lists of
+// L (value, expert) into its best L under the same order (value descending,
+// ties to the lower expert), then the row's outputs.
+template <int L>
+__global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p, int ranges) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= p.B) return;
+  float lv[L];
+  int li[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    lv[j] = -INFINITY;
+    li[j] = 0x7FFFFFFF;
+  }
+  for (int r = 0; r < ranges; ++r) {
+    const int64_t o = (row * ranges + r) * L;
+#pragma unroll
+    for (int j = 0; j < L; ++j) insert_any<L>(lv, li, p.cand_v[o + j], p.cand_i[o + j]);
+  }
+  GateParams q = p;
+  q.cand_v = nullptr;
+  q.cand_i = nullptr;
+  write_selection<L>(q, row, lv, li);
+}
+
 hipError_t gate_dispatch(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
   if (g.x_dt == kBF16 && g.w_dt == kBF16) return gate_dispatch_bf16(g, p, pass2, s);
   if (g.x_dt == kBF16 && g.w_dt == kF32) return gate_dispatch_bf16x_f32w(g, p, pass2, s);
@@ -273,14 +301,50 @@ bool gate_supported(int d, Dt x_dt, Dt w_dt, int k) {
   return true;
 }
 
-hipError_t launch_gate(const GateLaunch& g, int32_t* topk_idx, float* topk_gate, float* thresh,
-                       hipStream_t s) {
-  if (g.tokens == 0) return hipSuccess;
+int gate_ranges(const GateLaunch& g) {
+  if (g.units || g.tokens <= 0) return 1;
+  const int rows = gate_tile_rows(g);
+  const int64_t tiles = (g.tokens + rows - 1) / rows;
+  constexpr int kTarget = 256;  // workgroups to aim for
+  if (2 * tiles > kTarget) return 1;
+  const int w = gate_uses_g32(g) ? kGate32Chunk
+                                 : (g.x_dt == kBF16 && g.w_dt == kBF16 ? GateShape<bf16>::kChunk
+                                                                        : GateShape<float>::kChunk);
+  const int nch = (g.n + w - 1) / w;
+  const int64_t want = std::min<int64_t>((kTarget + tiles - 1) / tiles, nch / 2);
+  if (want <= 1) return 1;
+  // equal ranges of `per` chunks, none empty
+  const int per = (int)((nch + want - 1) / want);
+  return (nch + per - 1) / per;
+}
+
+size_t gate_cand_bytes(const GateLaunch& g) {
+  const int r = gate_ranges(g);
+  if (r <= 1) return 0;
+  return (size_t)g.tokens * r * (g.k <= 4 ? 5 : 9) * 8;
+}
+
+hipError_t launch_gate(const GateLaunch& g0, int32_t* topk_idx, float* topk_gate, float* thresh,
+                       hipStream_t s, void* cand) {
+  if (g0.tokens == 0) return hipSuccess;
+  GateLaunch g = g0;
+  g.ranges = cand ? gate_ranges(g) : 1;
   GateParams p = make_params(g);
   p.topk_idx = topk_idx;
   p.topk_gate = topk_gate;
   p.thresh = thresh;
-  return gate_dispatch(g, p, false, s);
+  if (g.ranges <= 1) return gate_dispatch(g, p, false, s);
+  // split sweep: each range's candidates, then one thread per row merges them
+  const int L = g.k <= 4 ? 5 : 9;
+  p.cand_v = static_cast<float*>(cand);
+  p.cand_i = reinterpret_cast<int32_t*>(static_cast<char*>(cand) +
+                                        (size_t)g.tokens * g.ranges * L * sizeof(float));
+  hipError_t e = gate_dispatch(g, p, false, s);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((g.tokens + 255) / 256));
+  if (L == 5) hipLaunchKernelGGL((gate_merge_kernel<5>), grid, dim3(256), 0, s, p, g.ranges);
+  else hipLaunchKernelGGL((gate_merge_kernel<9>), grid, dim3(256), 0, s, p, g.ranges);
+  return hipGetLastError();
 }
 
 int gate_tile_rows(const GateLaunch& g) { return gate_uses_g32(g) ? kGate32Rows : kGateRows; }
@@ -349,10 +413,14 @@ hipError_t launch_load(const GateLaunch& g, const float* thresh, const int32_t* 
   const int rows = gate_tile_rows(g);
   const int nb = (int)((g.tokens + rows - 1) / rows);
   if (nb > 0) {
-    GateParams p = make_params(g);
+    // a small batch splits each tile's sweep over the experts as the
+    // selection does; every (tile, expert) column sum is still written once
+    GateLaunch gs = g;
+    gs.ranges = gate_ranges(g);
+    GateParams p = make_params(gs);
     p.sel_thr = thresh;
     p.partial = partial;
-    hipError_t e = gate_dispatch(g, p, true, s);
+    hipError_t e = gate_dispatch(gs, p, true, s);
     if (e != hipSuccess) return e;
   }
   const int splits = corr_splits(g.tokens * g.k, g.n);

@@ -44,7 +44,7 @@ constexpr int kG32Waves = 8;
 constexpr int kG32Threads = kG32Waves * 64;
 constexpr int kG32Rows = kG32Waves * 32;
 static_assert(kG32Rows == kGate32Rows, "rows per block of the 32x32 gate kernel");
-constexpr int kG32Chunk = 16;
+constexpr int kG32Chunk = kGate32Chunk;
 
 template <int V>
 struct IntConst {
@@ -134,7 +134,12 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // all fragments (kb = w + 4 i) and waves 4-7 all noise draws, so that each
   // wave's in-order copy counter waits on one stream only: the weights must
   // land within a pass, the noise draws have NE - 2 more.
-  const bf16* wlane = (clean_lane ? wg : wn) + (int64_t)(l32 & 15) * D + hi * UE;
+  // this workgroup's range of expert chunks (all of them unless split); the
+  // copy sources below start at its first chunk, c counts from there
+  const ChunkRange cr = chunk_range((n + EC - 1) / EC);
+  const int nchunks = cr.count;
+  const bf16* wlane =
+      (clean_lane ? wg : wn) + ((int64_t)cr.c0 * EC + (l32 & 15)) * D + hi * UE;
   auto dma = [&](int c, U16* dst) {
     const bf16* src = wlane + (int64_t)c * EC * D;
     if constexpr (PASS2) {
@@ -153,8 +158,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   };
   const bool has_bias = p.bias != nullptr;
   // chunk c's biases: bias_src + c * bias_step
-  const float* bias_src = has_bias ? p.bias : kZeroBias;
   const int bias_step = has_bias ? EC : 0;
+  const float* bias_src = has_bias ? p.bias + cr.c0 * bias_step : kZeroBias;
   // Pass 2: lanes 0-3 copy chunk c's 16 biases into this wave's slot. A
   // copy, not a register load, so
   // that no compiler-inserted wait on the memory counter stalls the epilogue
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   for (int i = 0; i < 4; ++i) {
     int64_t r = tile_iorow(p, tile, 64 * ev + 16 * i + (lane >> 2));
     if (r < 0) r = tile_iorow(p, tile, 0);
-    elane[i] = p.eps + r * n + 4 * ((lane & 3) ^ ((lane >> 3) & 3));
+    elane[i] = p.eps + r * n + cr.c0 * EC + 4 * ((lane & 3) ^ ((lane >> 3) & 3));
   }
   constexpr int EPS_COPIES = 5;  // per wave and chunk: 4 row groups, 1 bias copy
   auto dma_eps = [&](int c, int b) {
@@ -237,11 +242,10 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     if (__any(cand)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        insert_new<L>(lv, li, hv[i], chunk * EC + 8 * (i / 4) + 4 * hi + (i % 4));
+        insert_new<L>(lv, li, hv[i], (cr.c0 + chunk) * EC + 8 * (i / 4) + 4 * hi + (i % 4));
     }
   };
 
-  const int nchunks = (n + EC - 1) / EC;
   // Accumulators of two consecutive chunks: pass P reads accs[P] (its own
   // chunk's products) and fills accs[P ^ 1] (the next chunk's); the same for
   // pass 2's bias slots.
@@ -446,7 +450,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kG32Waves; ++w) s += red[P][w][tid];
-        p.partial[(int64_t)blockIdx.x * n + c * EC + tid] = s;
+        p.partial[(int64_t)blockIdx.x * n + (cr.c0 + c) * EC + tid] = s;
       }
     }
   };
@@ -467,33 +471,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
 #pragma unroll
     for (int j = 0; j < L; ++j) insert_any<L>(lv, li, ov[j], oi[j]);
     const int64_t row = tile_iorow(p, tile, wrow0 + l32);
-    if (hi == 0 && row >= 0) {
-      const int k = p.k;
-      const float top = lv[0];
-      float ex[L - 1];
-      float z = 0.f;
-#pragma unroll
-      for (int j = 0; j < L - 1; ++j) {
-        ex[j] = (j < k) ? expf(lv[j] - top) : 0.f;
-        z += ex[j];
-      }
-      const float inv = 1.0f / z;
-#pragma unroll
-      for (int j = 0; j < L - 1; ++j) {
-        if (j < k) {
-          p.topk_idx[row * k + j] = li[j];
-          p.topk_gate[row * k + j] = ex[j] * inv;
-        }
-      }
-      float vk = lv[0], vk1 = lv[1];
-#pragma unroll
-      for (int j = 1; j < L; ++j) {
-        if (j == k - 1) vk = lv[j];
-        if (j == k) vk1 = lv[j];
-      }
-      p.thresh[row * 2] = vk;
-      p.thresh[row * 2 + 1] = vk1;
-    }
+    if (hi == 0 && row >= 0) write_selection<L>(p, row, lv, li);
   }
 }
 

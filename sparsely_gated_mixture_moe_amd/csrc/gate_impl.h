@@ -49,6 +49,11 @@ struct GateParams {
   float* thresh;
   const float* sel_thr;  // pass 2: (k-th, (k+1)-th) logit of each row
   float* partial;
+  // Selection of one expert range (gridDim.y ranges): each row's best L
+  // (value, expert) go to [(row * gridDim.y + blockIdx.y) * L + j] instead of
+  // the outputs above; null when every workgroup sweeps all experts.
+  float* cand_v;
+  int32_t* cand_i;
   // Secondary gating of a hierarchical layer ("Hierarchical MoE"); all null
   // for a flat gate. The rows are those a primary route sent to each group:
   // workgroup u covers the rows seg_off[g] + first, ... of group g, with
@@ -168,6 +173,61 @@ __device__ __forceinline__ void insert_any(float (&lv)[L], int (&li)[L], float v
   }
 }
 
+// Chunks [c0, c0 + count) of the nch chunks of n experts that workgroup
+// (x, y) sweeps: gridDim.y consecutive ranges of ceil(nch / gridDim.y) chunks
+// (the launcher picks gridDim.y so that none is empty).
+struct ChunkRange {
+  int c0, count;
+};
+__device__ __forceinline__ ChunkRange chunk_range(int nch) {
+  const int per = (nch + (int)gridDim.y - 1) / (int)gridDim.y;
+  const int c0 = (int)blockIdx.y * per;
+  return ChunkRange{c0, min(per, nch - c0)};
+}
+
+// A row's outputs from its best L (value, expert) in rank order: the first
+// k experts, the softmax of their logits, and the k-th and (k+1)-th logits;
+// or, for a split sweep, the list itself as this range's candidates.
+template <int L>
+__device__ __forceinline__ void write_selection(const GateParams& p, int64_t row,
+                                                const float (&lv)[L], const int (&li)[L]) {
+  if (p.cand_v) {
+    const int64_t o = (row * gridDim.y + blockIdx.y) * L;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      p.cand_v[o + j] = lv[j];
+      p.cand_i[o + j] = li[j];
+    }
+    return;
+  }
+  const int k = p.k;
+  // softmax over the k kept logits (the rest are -inf, gate 0)
+  const float top = lv[0];
+  float ex[L - 1];
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) {
+    ex[j] = (j < k) ? expf(lv[j] - top) : 0.f;
+    z += ex[j];
+  }
+  const float inv = 1.0f / z;
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) {
+    if (j < k) {
+      p.topk_idx[row * k + j] = li[j];
+      p.topk_gate[row * k + j] = ex[j] * inv;
+    }
+  }
+  float vk = lv[0], vk1 = lv[1];
+#pragma unroll
+  for (int j = 1; j < L; ++j) {
+    if (j == k - 1) vk = lv[j];
+    if (j == k) vk1 = lv[j];
+  }
+  p.thresh[row * 2] = vk;
+  p.thresh[row * 2 + 1] = vk1;
+}
+
 template <typename XS, typename CT, int D, int L, bool TRAIN, bool PASS2>
 __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   RowTile tile;
@@ -194,6 +254,10 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   const int q = lane >> 4;   // K unit of the A/B operands; C row group
   const int n = p.n;
   const int wrow0 = wave * 16;  // first local row of this wave
+  // this workgroup's range of expert chunks (all of them unless split)
+  const ChunkRange cr = chunk_range((n + EC - 1) / EC);
+  const int cbase = cr.c0 * EC;
+  const int nchunks = cr.count;
 
   // x rows of this wave as A operands for every K-block.
   U16 xa[NKB];
@@ -254,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
         const int m = (rest / NT) % NM;
         const int kb = rest / (NT * NM);
         // experts past n read row n - 1; their logits are masked in the epilogue
-        const int e = min(c * EC + nt * 16 + (fl & 15), n - 1);
+        const int e = min(cbase + c * EC + nt * 16 + (fl & 15), n - 1);
         const CT* w = reinterpret_cast<const CT*>(m ? p.wn : p.wg);
         stage[it] = ld_unit(w + (int64_t)e * D + (kb * 4 + (fl >> 4)) * UE);
       }
@@ -288,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   auto load_eps = [&](int c, float (&ev)[NT][4], float (&bv)[NT]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int e = min(c * EC + nt * 16 + lr, n - 1);
+      const int e = min(cbase + c * EC + nt * 16 + lr, n - 1);
       bv[nt] = bias_src[e];
       if constexpr (TRAIN && !PASS2) {
 #pragma unroll
@@ -303,7 +367,6 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   // Software pipeline over expert chunks: the matrix products of chunk c + 1
   // and the epilogue of chunk c sit in one straight-line block, so the matrix
   // cores and the vector ALUs overlap; weights are staged two chunks ahead.
-  const int nchunks = (n + EC - 1) / EC;
   f32x4 acc[NM][NT], acc_next[NM][NT];
   float ev[NT][4], ev_next[NT][4], bv[NT], bv_next[NT];
   gload(0);
@@ -335,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         colsum[nt] = 0.f;
-        const int e = c * EC + nt * 16 + lr;
+        const int e = cbase + c * EC + nt * 16 + lr;
         const bool e_ok = e < n;
         const float bias = has_bias ? bv[nt] : 0.f;
 #pragma unroll
@@ -383,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (hv[nt][r] >= shared_thr[r])
-              insert_new<L>(lv[r], li[r], hv[nt][r], c * EC + nt * 16 + lr);
+              insert_new<L>(lv[r], li[r], hv[nt][r], cbase + c * EC + nt * 16 + lr);
       }
     }
 
@@ -406,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
       }
     } else {
       if (tid < EC) {
-        const int e = c * EC + tid;
+        const int e = cbase + c * EC + tid;
         if (e < n) {
           float s = 0.f;
 #pragma unroll
@@ -446,38 +509,9 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
       }
     }
     if (lr == 0) {
-      const int k = p.k;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = iorow[r];
-        if (row_ok[r]) {
-          // softmax over the k kept logits (the rest are -inf, gate 0)
-          const float top = lv[r][0];
-          float ex[L - 1];
-          float z = 0.f;
-#pragma unroll
-          for (int j = 0; j < L - 1; ++j) {
-            ex[j] = (j < k) ? expf(lv[r][j] - top) : 0.f;
-            z += ex[j];
-          }
-          const float inv = 1.0f / z;
-#pragma unroll
-          for (int j = 0; j < L - 1; ++j) {
-            if (j < k) {
-              p.topk_idx[row * k + j] = li[r][j];
-              p.topk_gate[row * k + j] = ex[j] * inv;
-            }
-          }
-          float vk = lv[r][0], vk1 = lv[r][1];
-#pragma unroll
-          for (int j = 1; j < L; ++j) {
-            if (j == k - 1) vk = lv[r][j];
-            if (j == k) vk1 = lv[r][j];
-          }
-          p.thresh[row * 2] = vk;
-          p.thresh[row * 2 + 1] = vk1;
-        }
-      }
+      for (int r = 0; r < 4; ++r)
+        if (row_ok[r]) write_selection<L>(p, iorow[r], lv[r], li[r]);
     }
   }
 }
@@ -485,7 +519,8 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
 // Workgroups of a launch: one per tile of `rows` batch rows, or for secondary
 // gating one per possible work unit (those past the unit count exit at once).
 inline dim3 gate_grid(const GateLaunch& g, int rows) {
-  return dim3((unsigned)(g.units ? g.max_units : (g.tokens + rows - 1) / rows));
+  return dim3((unsigned)(g.units ? g.max_units : (g.tokens + rows - 1) / rows),
+              (unsigned)(g.units ? 1 : g.ranges));
 }
 
 template <typename XS, typename CT, int D, int L>

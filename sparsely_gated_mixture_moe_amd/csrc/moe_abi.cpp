@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -105,8 +106,8 @@ moe_status check_opts(const moe_gate_opts* o) {
 // Workspace regions. Each call uses a prefix-free subset; moe_forward uses all.
 struct Layout {
   size_t topk_idx, topk_gate, thresh, counts, offsets, perm_token, perm_gate, slot_pos,
-      importance, blockcnt, ffn_blocks, expert_out, load_partial, load_corr, total;
-  size_t route_bytes, ffn_bytes, aux_bytes;  // standalone needs (from offset 0)
+      importance, blockcnt, ffn_blocks, expert_out, load_partial, load_corr, gate_cand, total;
+  size_t route_bytes, ffn_bytes, aux_bytes, gate_bytes;  // standalone needs (from offset 0)
 };
 
 Layout layout(const moe_dims* d, const moe_gate_opts* o) {
@@ -126,6 +127,19 @@ Layout layout(const moe_dims* d, const moe_gate_opts* o) {
   L.aux_bytes = (o && o->train) ? align_up((size_t)moe::gate_blocks(B) * n * sizeof(float)) +
                                       align_up((size_t)n * moe::kCorrSplitsMax * sizeof(float))
                                 : 0;
+  // a small batch's split selection: each expert range's candidates
+  auto cand = [&](int train) {
+    moe::GateLaunch g{};
+    g.tokens = B;
+    g.d = d->d_model;
+    g.n = (int)n;
+    g.k = (int)k;
+    g.x_dt = to_dt(d->act_dtype);
+    g.w_dt = to_dt(d->gate_dtype);
+    g.train = train;
+    return moe::gate_cand_bytes(g);
+  };
+  L.gate_bytes = align_up(o ? cand(o->train) : std::max(cand(0), cand(1)));
   // moe_forward
   L.topk_idx = take(pairs * sizeof(int32_t));
   L.topk_gate = take(pairs * sizeof(float));
@@ -143,6 +157,7 @@ Layout layout(const moe_dims* d, const moe_gate_opts* o) {
   L.load_corr = L.load_partial + (L.aux_bytes ? align_up((size_t)moe::gate_blocks(B) * n *
                                                          sizeof(float))
                                               : 0);
+  L.gate_cand = take(L.gate_bytes);
   L.total = at;
   return L;
 }
@@ -402,16 +417,18 @@ moe_status moe_gate(const moe_dims* dims, const moe_gate_opts* opts, const void*
                     const void* w_gate, const void* w_noise, const float* gate_bias,
                     const float* eps, int32_t* topk_idx, float* topk_gate, float* thresh, void* ws,
                     size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   moe_status s;
   if ((s = check_dims(dims)) != MOE_OK || (s = check_opts(opts)) != MOE_OK) return s;
   if ((s = check_gate_args(dims, opts, x, w_gate, w_noise, gate_bias, eps, true)) != MOE_OK) return s;
   REQN(topk_idx, 4, dims->tokens);
   REQN(topk_gate, 4, dims->tokens);
   REQN(thresh, 4, dims->tokens);
+  // the workspace is optional here: it only lets a small batch split its sweep
+  const size_t need = ws ? layout(dims, opts).gate_bytes : 0;
+  if ((s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
   const moe::GateLaunch g = gate_launch(dims, opts, x, w_gate, w_noise, gate_bias, eps);
-  return device_status(moe::launch_gate(g, topk_idx, topk_gate, thresh, (hipStream_t)stream),
+  return device_status(moe::launch_gate(g, topk_idx, topk_gate, thresh, (hipStream_t)stream,
+                                        need ? ws : nullptr),
                        "moe_gate");
 }
 
@@ -550,7 +567,8 @@ moe_status moe_forward(const moe_dims* dims, const moe_gate_opts* opts, const vo
   void* expert_out = at<char>(ws, L.expert_out);
 
   const moe::GateLaunch g = gate_launch(dims, opts, x, w_gate, w_noise, gate_bias, eps);
-  hipError_t e = moe::launch_gate(g, topk_idx, topk_gate, thresh, st);
+  hipError_t e = moe::launch_gate(g, topk_idx, topk_gate, thresh, st,
+                                  L.gate_bytes ? at<char>(ws, L.gate_cand) : nullptr);
   if (e != hipSuccess) return device_status(e, "moe_forward (gate)");
   e = moe::launch_route(dims->tokens, dims->k, dims->n_experts, topk_idx, topk_gate,
                         at<int32_t>(ws, L.blockcnt), counts, offsets, perm_token, perm_gate,

@@ -15,6 +15,7 @@ enum Dt { kF32 = 0, kBF16 = 1 };
 // for bf16 gates runs 8 waves of 32 rows.
 constexpr int kGateRows = 128;
 constexpr int kGate32Rows = 256;
+constexpr int kGate32Chunk = 16;  // experts per chunk of the 32x32-tile kernel
 // Routing: tokens per block of the counting sort.
 constexpr int kRouteTokens = 256;
 
@@ -38,11 +39,17 @@ struct GateLaunch {
   const int32_t* row_token = nullptr;  // [tokens] x row of each routed row
   const int32_t* row_slot = nullptr;   // [tokens] eps / output row of each routed row
   int64_t max_units = 0;
+  // Flat gating of a small batch: each row tile's expert sweep split into
+  // `ranges` consecutive ranges of chunks, one workgroup each (set by the
+  // launchers from gate_ranges).
+  int ranges = 1;
 };
 
 // Noisy top-k gating: writes topk_idx [B,k], topk_gate [B,k], thresh [B,2].
+// cand (gate_cand_bytes(g) bytes, or null) lets a small flat batch split
+// its expert sweep.
 hipError_t launch_gate(const GateLaunch& g, int32_t* topk_idx, float* topk_gate, float* thresh,
-                       hipStream_t s);
+                       hipStream_t s, void* cand = nullptr);
 
 // Load (eq 10) with train = 1: recomputes the logits, evaluates P for every
 // (token, expert) against the row's k-th logit and writes per-block column sums
@@ -59,6 +66,14 @@ hipError_t launch_load(const GateLaunch& g, const float* thresh, const int32_t* 
                        const int32_t* perm_token, float* partial, float* corr, float* load,
                        hipStream_t s);
 bool gate_supported(int d, Dt x_dt, Dt w_dt, int k);
+// Expert ranges per row tile for flat gating of `g` (1: no split): a batch of
+// fewer row tiles than half of 256 workgroups splits each tile's sweep over
+// the experts into up to 256 / tiles ranges of at least two chunks. A
+// selection split this way leaves each range's best k+1 (value, expert) of
+// every row in a candidate buffer of gate_cand_bytes(g) bytes, merged by a
+// second kernel; without that buffer launch_gate does not split.
+int gate_ranges(const GateLaunch& g);
+size_t gate_cand_bytes(const GateLaunch& g);
 
 // Secondary (grouped) gating. Rows per work unit of the kernel that `g` runs
 // on; the largest unit count for `rows` routed rows over `groups` groups;

@@ -67,6 +67,47 @@ def test_gate_parity(case, train):
           "swapped", len(stats["swapped"]))
 
 
+# Batches of fewer than 128 row tiles split each tile's sweep over the experts
+# when moe_gate has a workspace: one row, a few rows, a ragged tile, and the
+# kernels of every dtype (chunks of 16 and 32 experts, tails in the last range).
+SPLIT_CASES = [
+    ("flat_bf16_n4096", {"tokens": 1}),
+    ("flat_bf16_n4096", {"tokens": 7}),
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 512}),
+    ("flat_bf16_n4096", {"tokens": 40, "n_experts": 100, "k": 3}),
+    ("flat_bf16_n4096", {"tokens": 33, "n_experts": 96, "k": 6, "d_model": 256}),
+    ("zipf_bf16_n256", {"tokens": 5}),
+    ("tiny_fp32", {"tokens": 3}),
+    ("tiny_fp32", {"tokens": 129, "n_experts": 37, "k": 3, "d_model": 128}),
+    ("flat_fp32_n32", {"tokens": 64}),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[_gate_ids(c) for c in SPLIT_CASES])
+@pytest.mark.parametrize("train", [True, False])
+def test_gate_split_sweep(case, train):
+    """The split sweep against the oracle, and bit-identical to one workgroup
+    per row tile sweeping every expert (moe_gate without a workspace)."""
+    name, kw = case
+    w = wl(name, **kw)
+    announce(f"moe_gate split {w.name} {kw} train={train}")
+    inp = dg.make_inputs(w, experts=False, with_bias=(name == "zipf_bf16_n256"))
+    ref = oracle.gate(inp, w.k, train=train, noise_floor=FLOOR, want_logits=True)
+    g = gpu_inputs(inp)
+    act = moe.MOE_F32 if g["x"].dtype == torch.float32 else moe.MOE_BF16
+    dims = moe.make_dims(w.tokens, w.d_model, 128, w.n_experts, w.k, act, act,
+                         moe.MOE_F32 if g["w_gate"].dtype == torch.float32 else moe.MOE_BF16)
+    ws = moe.workspace(dims, moe.make_opts(train, FLOOR), g["x"].device)
+    args = (g["x"], g["w_gate"], g["w_noise"], g["eps"] if train else None, w.k)
+    kw2 = dict(train=train, noise_floor=FLOOR, gate_bias=g.get("gate_bias"))
+    split = moe.moe_gate(*args, ws=ws, **kw2)
+    whole = moe.moe_gate(*args, **kw2)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(split, whole):
+        assert np.array_equal(to_host(a_), to_host(b_))
+    check_gating(ref, ref["H"], *[to_host(t) for t in split])
+
+
 @pytest.mark.parametrize("case", [("flat_bf16_n4096", {"tokens": 1000, "n_experts": 512}),
                                   ("tiny_fp32", {"tokens": 300, "n_experts": 37, "k": 3})],
                          ids=["bf16-n512", "fp32-n37"])
@@ -299,6 +340,8 @@ def check_forward(w, inp, out, train, rows=None, full_load=True, w_imp=0.1, w_lo
 
 
 FWD_CASES = [
+    ("flat_bf16_n4096", {"tokens": 3, "n_experts": 512, "d_hidden": 256}, False),
+    ("flat_bf16_n4096", {"tokens": 200, "n_experts": 1024, "d_hidden": 128}, True),
     ("tiny_fp32", {}, True),
     ("tiny_fp32", {"tokens": 333, "n_experts": 37, "k": 3, "d_model": 128}, False),
     ("tiny_fp32", {"tokens": 100, "n_experts": 4, "k": 4}, False),
