@@ -58,6 +58,10 @@ struct FfnParams {
   void* out;
   const int32_t* blocks;  // [0] = count; from [4] on, 16 bytes per unit (FfnUnit)
   int h;
+  // split over the hidden units: unit u writes its fp32 partial output rows
+  // (no b2) to part + u * part_rows * D; null when units are whole
+  float* part;
+  int part_rows;
 };
 
 // Global-memory byte pointer: loads through it are global (not flat) loads
@@ -123,9 +127,11 @@ __device__ __forceinline__ void quad_transpose(f32x4& x, int c) {
   }
 }
 
-// A work unit as the planning kernel lists it (16 bytes).
+// A work unit as the planning kernel lists it (16 bytes). hr = 0: every
+// hidden chunk; otherwise chunks [hr & 0xFFFF, + (hr >> 16)) only, the unit's
+// output then being a partial sum (a small batch split over the hidden units).
 struct FfnUnit {
-  int32_t e, seg, rows, pad;
+  int32_t e, seg, rows, hr;
 };
 
 template <typename T, int D>
@@ -153,7 +159,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
     u.e = __builtin_amdgcn_readfirstlane(v.e);
     u.seg = __builtin_amdgcn_readfirstlane(v.seg);
     u.rows = __builtin_amdgcn_readfirstlane(v.rows);
-    u.pad = 0;
+    u.hr = __builtin_amdgcn_readfirstlane(v.hr);
     return u;
   };
   int j = blockIdx.x / 8;
@@ -182,6 +188,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   const int l16 = lane & 15;
   const int q = lane >> 4;
   const int nch = h / S::HC;
+  // a unit's first hidden chunk and chunk count
+  auto chunk0 = [&](const FfnUnit& v) { return v.hr & 0xFFFF; };
+  auto nchunks = [&](const FfnUnit& v) { return (v.hr >> 16) ? (v.hr >> 16) : nch; };
   // Addresses: a wave-uniform base (scalar registers) plus one 32-bit byte
   // offset per lane and stream, so the prefetch rings cost no 64-bit vector
   // address registers.
@@ -276,8 +285,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   __syncthreads();
   gather(u.rows);
 #pragma unroll
-  for (int jj = 0; jj < PF1; ++jj) pa[jj] = w1_at(w1w, 0, jj);
-  b1r = b1_at(u.e, 0);
+  for (int jj = 0; jj < PF1; ++jj) pa[jj] = w1_at(w1w, chunk0(u) * S::HC, jj);
+  b1r = b1_at(u.e, chunk0(u) * S::HC);
   wait_copies();
   __syncthreads();
 
@@ -296,9 +305,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 #pragma unroll
       for (int i = 0; i < S::CT2; ++i) acc2[tt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int ch = 0; ch < nch; ++ch) {
-      const int hc = ch * S::HC;
-      const bool last = ch + 1 == nch;
+    const int nchu = nchunks(u);
+    for (int ch = 0; ch < nchu; ++ch) {
+      const int hc = (chunk0(u) + ch) * S::HC;
+      const bool last = ch + 1 == nchu;
       // this chunk's weight bases, opaque to the compiler so that it forms
       // each load's address from one base and an immediate offset instead of
       // keeping a pointer per K-block live across chunks and units
@@ -334,7 +344,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
         un = uniform_unit(un_raw);
         w1n = w1_base(un.e);
         if (has_next) copy_tokens(un);
-        if (nch == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (nchu == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       __syncthreads();  // the previous chunk's GEMM2 has finished reading hs;
                         // after the last chunk, every wave is done with xs
@@ -384,9 +394,10 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
       // K-blocks request the first W1 fragments and b1 of the next chunk, of
       // the next unit's first chunk, or (after the last unit) of this unit's
       // first chunk again, unused.
-      const GPtr w1p = !last ? w1c + (int64_t)S::HC * D * (int64_t)sizeof(T) : w1n;
+      const int hc_p = last ? chunk0(un) * S::HC : hc + S::HC;
+      const GPtr w1p = !last ? w1c + (int64_t)S::HC * D * (int64_t)sizeof(T)
+                             : w1n + (int64_t)hc_p * D * (int64_t)sizeof(T);
       const int e_p = last ? un.e : u.e;
-      const int hc_p = last ? 0 : hc + S::HC;
 #pragma unroll
       for (int kb = 0; kb < NKB2; ++kb) {
         U16 b[S::CT2];
@@ -421,8 +432,24 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
     // Output rows in segment order. A 4x4 transpose inside each quad of lanes
     // turns the C layout (lane: one column, 4 consecutive rows) into one row
     // and 4 consecutive columns per lane, written with one 8-byte (bf16) or
-    // 16-byte (fp32) store; b2 is added on the way.
-    {
+    // 16-byte (fp32) store; b2 is added on the way. A unit of a split batch
+    // writes its fp32 partial sums instead.
+    if (p.part) {
+      const int cq = lane & 3;
+      const int col0 = wave * S::CT2 * 16 + (lane & 12);
+      const int row0 = 4 * (lane >> 4) + cq;
+      float* prow = p.part + ((int64_t)(xcd * per_xcd + j) * p.part_rows + row0) * D + col0;
+      const int rleft = u.rows - row0;
+#pragma unroll
+      for (int i = 0; i < S::CT2; ++i) {
+#pragma unroll
+        for (int tt = 0; tt < S::T16; ++tt) {
+          f32x4 v = acc2[tt][i];
+          quad_transpose(v, cq);
+          if (tt * 16 < rleft) *reinterpret_cast<f32x4*>(prow + (int64_t)tt * 16 * D + i * 16) = v;
+        }
+      }
+    } else {
       int ln = lane;  // opaque, as in gather()
       asm volatile("" : "+v"(ln));
       const int cq = ln & 3;
@@ -473,13 +500,17 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 // as (expert, first pair of its rows, rows) after the count. One workgroup;
 // thread t owns a contiguous span of experts.
 __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ offsets, int n, int bm,
+                                                 int hsplit, int nch,
                                                  int32_t* __restrict__ blocks) {
   __shared__ int part[1024];
   const int t = threadIdx.x;
   const int per = (n + 1023) / 1024;
   const int e0 = min(n, t * per), e1 = min(n, e0 + per);
+  // hsplit > 1: each unit becomes hsplit consecutive units over hidden-chunk
+  // ranges of hper chunks (the launcher picks hsplit so that none is empty)
+  const int hper = (nch + hsplit - 1) / hsplit;
   int s = 0;
-  for (int e = e0; e < e1; ++e) s += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  for (int e = e0; e < e1; ++e) s += (offsets[e + 1] - offsets[e] + bm - 1) / bm * hsplit;
   part[t] = s;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
@@ -494,11 +525,47 @@ __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ off
     const int seg = offsets[e];
     const int cnt = offsets[e + 1] - seg;
     for (int r = 0; r < cnt; r += bm) {
-      units[pos] = FfnUnit{e, seg + r, min(bm, cnt - r), 0};
-      ++pos;
+      for (int q = 0; q < hsplit; ++q) {
+        const int hr = hsplit > 1 ? (q * hper) | (min(hper, nch - q * hper) << 16) : 0;
+        units[pos] = FfnUnit{e, seg + r, min(bm, cnt - r), hr};
+        ++pos;
+      }
     }
   }
   if (t == 1023) blocks[0] = part[t];
+}
+
+// Sum of a split batch's partial outputs: workgroup b owns the b-th group of
+// hsplit consecutive units (one row block of one expert) and writes its rows
+// of expert_out = b2 + the hsplit partials in order, 4 columns per thread.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void ffn_split_reduce(FfnParams p, int hsplit) {
+  const int count = p.blocks[0];
+  const int b = blockIdx.x;
+  if (b * hsplit >= count) return;
+  const FfnUnit u = reinterpret_cast<const FfnUnit*>(p.blocks + 4)[b * hsplit];
+  for (int idx = threadIdx.x; idx < u.rows * (D / 4); idx += 256) {
+    const int r = idx / (D / 4), c = (idx % (D / 4)) * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (p.b2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = load_scalar<T>(p.b2, (int64_t)u.e * D + c + i);
+    }
+    for (int q = 0; q < hsplit; ++q) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(
+          p.part + ((int64_t)(b * hsplit + q) * p.part_rows + r) * D + c);
+      acc += v;
+    }
+    T* dst = reinterpret_cast<T*>(p.out) + (int64_t)(u.seg + r) * D + c;
+    if constexpr (sizeof(T) == 2) {
+      uint2 pk;
+      pk.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+      pk.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+      *reinterpret_cast<uint2*>(dst) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>(dst) = acc;
+    }
+  }
 }
 
 // Compute units of the current device (cached per device).
@@ -520,10 +587,11 @@ hipError_t device_cus(int* cus) {
 
 template <typename T, int D>
 hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* offsets, int n,
-                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                        int hsplit, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   using S = FfnShape<T, D>;
-  hipLaunchKernelGGL(ffn_plan, dim3(1), dim3(1024), 0, s, offsets, n, S::BM,
-                     const_cast<int32_t*>(p.blocks));
+  hipLaunchKernelGGL(ffn_plan, dim3(1), dim3(1024), 0, s, offsets, n, S::BM, hsplit,
+                     p.h / S::HC, const_cast<int32_t*>(p.blocks));
+  max_blocks *= hsplit;
   if (max_blocks <= 0) {  // no rows: an empty timed interval
     hipError_t er = hipGetLastError();
     if (er == hipSuccess && ev0) er = hipEventRecord(ev0, s);
@@ -543,6 +611,9 @@ hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* o
     if (er != hipSuccess) return er;
   }
   hipLaunchKernelGGL((ffn_kernel<T, D>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
+  if (hsplit > 1)
+    hipLaunchKernelGGL((ffn_split_reduce<T, D>), dim3((unsigned)(max_blocks / hsplit)), dim3(256),
+                       0, s, p, hsplit);
   const hipError_t el = hipGetLastError();
   if (el != hipSuccess || !ev1) return el;
   return hipEventRecord(ev1, s);
@@ -569,8 +640,38 @@ int64_t ffn_max_blocks(int64_t rows, int n, int d, Dt dt) {
   return (rows + bm - 1) / bm + n;
 }
 
-size_t ffn_plan_bytes(int64_t rows, int n, int d, Dt dt) {
-  return (size_t)(4 + 4 * ffn_max_blocks(rows, n, d, dt)) * sizeof(int32_t);
+int ffn_hsplit(int64_t rows, int n, int d, int h, Dt dt) {
+  // units are at most the rows and at most ffn_max_blocks; a batch of fewer
+  // than 128 units splits each over up to 256 / units hidden-chunk ranges
+  const int64_t ub = std::min<int64_t>(ffn_max_blocks(rows, n, d, dt), rows);
+  const int hc = 16 * std::max(2, std::min(8, d / 64));  // hidden units per chunk
+  const int nch = h / hc;
+  if (ub <= 0 || ub >= 128 || nch < 2) return 1;
+  const int want = (int)std::min<int64_t>(nch, 256 / ub);
+  if (want <= 1) return 1;
+  const int per = (nch + want - 1) / want;
+  return (nch + per - 1) / per;  // no empty range
+}
+
+// Rows of a split unit's partial-output slot: a unit holds at most BM rows,
+// and at most all rows of the batch.
+static int ffn_part_rows(int64_t rows, int d, Dt dt) {
+  return (int)std::min<int64_t>(ffn_rows_per_block(d, dt), rows);
+}
+
+static size_t ffn_list_bytes(int64_t rows, int n, int d, int h, Dt dt) {
+  const size_t b = (size_t)(4 + 4 * ffn_max_blocks(rows, n, d, dt) * ffn_hsplit(rows, n, d, h, dt)) *
+                   sizeof(int32_t);
+  return (b + 255) / 256 * 256;
+}
+
+size_t ffn_plan_bytes(int64_t rows, int n, int d, int h, Dt dt) {
+  const int hs = ffn_hsplit(rows, n, d, h, dt);
+  size_t b = ffn_list_bytes(rows, n, d, h, dt);
+  if (hs > 1)
+    b += (size_t)ffn_max_blocks(rows, n, d, dt) * hs * ffn_part_rows(rows, d, dt) * d *
+         sizeof(float);
+  return b;
 }
 
 bool ffn_supported(int d, int h, Dt dt) {
@@ -582,21 +683,27 @@ hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const v
                       const int32_t* offsets, const int32_t* perm_token, const void* w1,
                       const void* b1, const void* w2, const void* b2, void* expert_out,
                       int32_t* blocks, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  FfnParams p{x, offsets, perm_token, w1, b1, w2, b2, expert_out, blocks, h};
   const int64_t mb = ffn_max_blocks(tokens * k, n, d, dt);
+  const int hs = ffn_hsplit(tokens * k, n, d, h, dt);
+  FfnParams p{x, offsets, perm_token, w1, b1, w2, b2, expert_out, blocks, h, nullptr, 0};
+  if (hs > 1) {
+    p.part = reinterpret_cast<float*>(reinterpret_cast<char*>(blocks) +
+                                      ffn_list_bytes(tokens * k, n, d, h, dt));
+    p.part_rows = ffn_part_rows(tokens * k, d, dt);
+  }
   if (dt == kBF16) {
     switch (d) {
-      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, s, ev0, ev1);
-      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, s, ev0, ev1);
-      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, s, ev0, ev1);
-      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, s, ev0, ev1);
+      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, hs, s, ev0, ev1);
+      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, hs, s, ev0, ev1);
+      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, hs, s, ev0, ev1);
+      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, hs, s, ev0, ev1);
     }
   } else {
     switch (d) {
-      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, s, ev0, ev1);
-      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, s, ev0, ev1);
-      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, s, ev0, ev1);
-      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, s, ev0, ev1);
+      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, hs, s, ev0, ev1);
+      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, hs, s, ev0, ev1);
+      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, hs, s, ev0, ev1);
+      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, hs, s, ev0, ev1);
     }
   }
   return hipErrorInvalidValue;

@@ -242,11 +242,15 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
 
 // Merges the candidate lists of a split selection: row t's `ranges` lists of
 // L (value, expert) into its best L under the same order (value descending,
-// ties to the lower expert), then the row's outputs.
+// ties to the lower expert), then the row's outputs. One wave per row: lane j
+// takes candidates j, j + 64, ..., then the lanes' lists merge pairwise over
+// six shuffle steps (the result does not depend on the merge order: the
+// order is total and every expert appears in one range only).
 template <int L>
 __global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p, int ranges) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= p.B) return;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= p.B) return;  // wave-uniform
   float lv[L];
   int li[L];
 #pragma unroll
@@ -254,15 +258,27 @@ __global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p, int range
     lv[j] = -INFINITY;
     li[j] = 0x7FFFFFFF;
   }
-  for (int r = 0; r < ranges; ++r) {
-    const int64_t o = (row * ranges + r) * L;
+  const int total = ranges * L;
+  const int64_t o = row * total;
+  for (int c = lane; c < total; c += 64) insert_any<L>(lv, li, p.cand_v[o + c], p.cand_i[o + c]);
 #pragma unroll
-    for (int j = 0; j < L; ++j) insert_any<L>(lv, li, p.cand_v[o + j], p.cand_i[o + j]);
+  for (int s = 32; s >= 1; s >>= 1) {
+    float ov[L];
+    int oi[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      ov[j] = __shfl_xor(lv[j], s);
+      oi[j] = __shfl_xor(li[j], s);
+    }
+#pragma unroll
+    for (int j = 0; j < L; ++j) insert_any<L>(lv, li, ov[j], oi[j]);
   }
-  GateParams q = p;
-  q.cand_v = nullptr;
-  q.cand_i = nullptr;
-  write_selection<L>(q, row, lv, li);
+  if (lane == 0) {
+    GateParams q = p;
+    q.cand_v = nullptr;
+    q.cand_i = nullptr;
+    write_selection<L>(q, row, lv, li);
+  }
 }
 
 hipError_t gate_dispatch(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
@@ -341,7 +357,7 @@ hipError_t launch_gate(const GateLaunch& g0, int32_t* topk_idx, float* topk_gate
                                         (size_t)g.tokens * g.ranges * L * sizeof(float));
   hipError_t e = gate_dispatch(g, p, false, s);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((g.tokens + 255) / 256));
+  const dim3 grid((unsigned)((g.tokens + 3) / 4));
   if (L == 5) hipLaunchKernelGGL((gate_merge_kernel<5>), grid, dim3(256), 0, s, p, g.ranges);
   else hipLaunchKernelGGL((gate_merge_kernel<9>), grid, dim3(256), 0, s, p, g.ranges);
   return hipGetLastError();

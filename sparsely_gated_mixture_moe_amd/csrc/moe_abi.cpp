@@ -122,7 +122,7 @@ Layout layout(const moe_dims* d, const moe_gate_opts* o) {
   };
   // standalone requirements (each placed at offset 0)
   L.route_bytes = align_up((size_t)n * moe::route_blocks(B) * sizeof(int32_t));
-  L.ffn_bytes = align_up(moe::ffn_plan_bytes(pairs, (int)n, d->d_model, to_dt(d->act_dtype)));
+  L.ffn_bytes = align_up(moe::ffn_plan_bytes(pairs, (int)n, d->d_model, d->d_hidden, to_dt(d->act_dtype)));
   // the Load pass: per-block partial sums, then the selected pairs' corrections
   L.aux_bytes = (o && o->train) ? align_up((size_t)moe::gate_blocks(B) * n * sizeof(float)) +
                                       align_up((size_t)n * moe::kCorrSplitsMax * sizeof(float))
@@ -305,7 +305,7 @@ HierLayout hier_layout(const moe_hier_dims* h, const moe_gate_opts* o) {
   L.perm_gate = take(pairs * sizeof(float));
   L.slot_pos = take(pairs * sizeof(int32_t));
   L.blockcnt = take((size_t)n * moe::route_blocks(B) * sizeof(int32_t));
-  L.ffn_blocks = take(moe::ffn_plan_bytes(pairs, (int)n, h->d_model, to_dt(h->act_dtype)));
+  L.ffn_blocks = take(moe::ffn_plan_bytes(pairs, (int)n, h->d_model, h->d_hidden, to_dt(h->act_dtype)));
   L.expert_out = take((size_t)pairs * h->d_model * dt_size(h->act_dtype));
   L.load1 = take(a * sizeof(float));
   L.partial1 = take(train ? (size_t)moe::gate_blocks(B) * a * sizeof(float) : 0);

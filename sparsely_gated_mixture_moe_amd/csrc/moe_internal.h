@@ -102,8 +102,11 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
 // Expert FFN.
 int ffn_rows_per_block(int d, Dt dt);
 int64_t ffn_max_blocks(int64_t rows, int n, int d, Dt dt);
-// Bytes of the expert-FFN work-unit list (the count, then 16 bytes per unit).
-size_t ffn_plan_bytes(int64_t rows, int n, int d, Dt dt);
+// Bytes of the expert-FFN workspace: the work-unit list (the count, then 16
+// bytes per unit) and, for a batch of few units split over the hidden units
+// (ffn_hsplit > 1 ranges), each unit's fp32 partial output rows.
+size_t ffn_plan_bytes(int64_t rows, int n, int d, int h, Dt dt);
+int ffn_hsplit(int64_t rows, int n, int d, int h, Dt dt);
 bool ffn_supported(int d, int h, Dt dt);
 // ev0 / ev1, when given, are recorded on s right before and after the FFN
 // kernel (after its plan kernel).

@@ -203,6 +203,10 @@ FFN_CASES = [
     ("zipf_bf16_n256", {"tokens": 1200}, True),
     ("flat_bf16_n4096", {"tokens": 300, "n_experts": 40, "d_model": 64, "d_hidden": 128}, True),
     ("flat_bf16_n4096", {"tokens": 600, "n_experts": 64}, False),
+    # batches of few units, split over hidden-chunk ranges (partial sums + reduction)
+    ("flat_bf16_n4096", {"tokens": 2, "n_experts": 64}, True),
+    ("tiny_fp32", {"tokens": 5}, True),
+    ("flat_bf16_n4096", {"tokens": 20, "n_experts": 16, "d_model": 256, "d_hidden": 384}, False),
 ]
 
 
