@@ -235,7 +235,13 @@ def main():
     ap.add_argument("--workload", default="flat_bf16_n4096")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target length of the oracle CPU-baseline run (0 skips it)")
-    ap.add_argument("--stage-iters", type=int, default=10)
+    ap.add_argument("--stage-iters", type=int, default=10,
+                    help="calls of each entry point on its own for the stage times (0 skips them)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="batch size instead of the workload's (same model), e.g. 1 for the "
+                         "latency of a single token")
+    ap.add_argument("--train", type=int, default=1, choices=(0, 1),
+                    help="1: noisy gating with the Load pass (the headline step); 0: inference")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes three times "
                          "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -262,6 +268,8 @@ def main():
     import sparsely_gated_mixture_moe_amd as moe
 
     w = dg.WORKLOADS[a.workload]
+    if a.tokens > 0:
+        w = dg.workload(a.workload, tokens=a.tokens)
     if w.hierarchical:
         bench_hier(a, w)
         return
@@ -274,7 +282,7 @@ def main():
     torch.cuda.synchronize()
 
     f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,
-                       gate_bias=g.get("gate_bias"), train=True)
+                       gate_bias=g.get("gate_bias"), train=bool(a.train))
     dev = g["x"].device
     y = torch.empty((B, d), dtype=g["x"].dtype, device=dev)
     topk_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
@@ -312,9 +320,11 @@ def main():
     route = moe.moe_route(topk_idx, topk_gate, n, d_model=d)
     ws = moe.workspace(f.dims, f.opts, dev)
     eo = torch.empty((B * k, d), dtype=g["x"].dtype, device=dev)
-    stages = {
-        "gate": time_calls(lambda: moe.moe_gate(g["x"], g["w_gate"], g["w_noise"], g["eps"], k,
-                                                gate_bias=g.get("gate_bias")), it, torch),
+    stages = {} if it <= 0 else {
+        "gate": time_calls(lambda: moe.moe_gate(g["x"], g["w_gate"], g["w_noise"],
+                                                g["eps"] if a.train else None, k,
+                                                train=bool(a.train), gate_bias=g.get("gate_bias"),
+                                                ws=ws), it, torch),
         "route": time_calls(lambda: moe.moe_route(topk_idx, topk_gate, n, d_model=d, ws=ws),
                             it, torch),
         "expert_ffn": time_calls(lambda: moe.moe_expert_ffn(
@@ -322,10 +332,11 @@ def main():
             it, torch),
         "combine": time_calls(lambda: moe.moe_combine(eo, route["slot_pos"], topk_gate,
                                                       n_experts=n, out=y), it, torch),
-        "aux_losses": time_calls(lambda: moe.moe_aux_losses(
-            g["x"], g["w_gate"], g["w_noise"], thresh, route["offsets"], route["perm_token"],
-            route["importance"], k, gate_bias=g.get("gate_bias"), ws=ws), it, torch),
     }
+    if it > 0 and a.train:
+        stages["aux_losses"] = time_calls(lambda: moe.moe_aux_losses(
+            g["x"], g["w_gate"], g["w_noise"], thresh, route["offsets"], route["perm_token"],
+            route["importance"], k, gate_bias=g.get("gate_bias"), ws=ws), it, torch)
     torch.cuda.synchronize()
     log("stages (ms): " + ", ".join(f"{k_}={v:.3f}" for k_, v in stages.items()))
 
@@ -341,9 +352,14 @@ def main():
     ffn_flops = 4.0 * rows * d * h
     ffn_ms = ffn_total / ffn_n  # the FFN kernel inside the timed steps
     achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
-    step_bytes = (B * d * asize + B * n * 4 + 2 * n * d * (2 if w.gate_dtype == dg.BF16 else 4)
-                  + used * 2 * d * h * esize + B * d * asize)
-    step_flops = 2.0 * B * d * 2 * n * 2 + ffn_flops  # gate GEMM twice (selection, load) + FFN
+    gsize = 2 if w.gate_dtype == dg.BF16 else 4
+    if a.train:  # x, eps, both gate matrices, the used experts, y; gate GEMM twice + FFN
+        step_bytes = (B * d * asize + B * n * 4 + 2 * n * d * gsize + used * 2 * d * h * esize
+                      + B * d * asize)
+        step_flops = 2.0 * B * d * 2 * n * 2 + ffn_flops
+    else:  # no noise: x, W_g, the used experts, y; one clean-logit GEMM + FFN
+        step_bytes = B * d * asize + n * d * gsize + used * 2 * d * h * esize + B * d * asize
+        step_flops = 2.0 * B * d * n + ffn_flops
     mfma_peak = BF16_PEAK_TFLOPS if w.expert_dtype == dg.BF16 else FP32_PEAK_TFLOPS
 
     result = {
@@ -360,7 +376,7 @@ def main():
         "dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "n_experts": n,
-                   "k": k, "train": 1, "act_dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
+                   "k": k, "train": a.train, "act_dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
                    "gate_dtype": "bf16" if w.gate_dtype == dg.BF16 else "f32"},
         "roofline": {"kernel": "ffn_kernel (expert FFN)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
