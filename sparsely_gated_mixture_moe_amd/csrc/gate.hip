@@ -243,9 +243,10 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
 // Merges the candidate lists of a split selection: row t's `ranges` lists of
 // L (value, expert) into its best L under the same order (value descending,
 // ties to the lower expert), then the row's outputs. One wave per row: lane j
-// takes candidates j, j + 64, ..., then the lanes' lists merge pairwise over
-// six shuffle steps (the result does not depend on the merge order: the
-// order is total and every expert appears in one range only).
+// takes candidates j, j + 64, ... (eight loads at a time), then the lanes'
+// lists merge pairwise over six shuffle steps (the result does not depend on
+// the merge order: the order is total and every expert appears in one range
+// only).
 template <int L>
 __global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p, int ranges) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -260,7 +261,19 @@ __global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p, int range
   }
   const int total = ranges * L;
   const int64_t o = row * total;
-  for (int c = lane; c < total; c += 64) insert_any<L>(lv, li, p.cand_v[o + c], p.cand_i[o + c]);
+  // eight candidates per lane loaded at once, then inserted
+  for (int base = 0; base < total; base += 64 * 8) {
+    float cv[8];
+    int ci[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int c = base + lane + 64 * m;
+      cv[m] = c < total ? p.cand_v[o + c] : -INFINITY;
+      ci[m] = c < total ? p.cand_i[o + c] : 0x7FFFFFFF;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) insert_any<L>(lv, li, cv[m], ci[m]);
+  }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) {
     float ov[L];

@@ -157,6 +157,94 @@ __global__ void route_importance(const float* __restrict__ perm_gate,
   if (lane == 0) importance[e] = s;
 }
 
+// Routing of a small batch in one workgroup and one launch instead of five:
+// the same outputs as the multi-kernel path. Counts by LDS atomics (integers),
+// offsets by the same span scan as route_scan_experts, each pair's position
+// = its expert's offset + the pairs before it with the same expert (stable),
+// and each Importance summed in the same order as route_importance (lane l
+// takes positions l, l + 64, ... of the segment, then a butterfly), from an
+// LDS copy of the permuted gates.
+constexpr int kSmallPairs = 1024;
+constexpr int kSmallExperts = 16384;
+constexpr size_t kSmallLds = (2 * (size_t)kSmallExperts + 1 + 3 * kSmallPairs) * sizeof(int);
+__global__ __launch_bounds__(kThreads) void route_small(
+    const int32_t* __restrict__ idx, const float* __restrict__ gate, int npairs, int k, int n,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+    float* __restrict__ perm_gate, int32_t* __restrict__ slot_pos, float* __restrict__ importance) {
+  extern __shared__ int sm[];
+  int* cnt = sm;                                    // [n]
+  int* off = cnt + n;                               // [n + 1]
+  int* se = off + n + 1;                            // [npairs] expert of each pair, -1 dropped
+  int* lst = se + kSmallPairs;                      // experts with rows
+  float* pg = reinterpret_cast<float*>(lst + kSmallPairs);  // gates in perm order
+  __shared__ int part[kThreads];
+  __shared__ int nlst;
+  const int t = threadIdx.x;
+  for (int e = t; e < n; e += kThreads) cnt[e] = 0;
+  if (t == 0) nlst = 0;
+  __syncthreads();
+  if (t < npairs) {
+    const int e = idx[t];
+    const bool live = e >= 0 && e < n;
+    se[t] = live ? e : -1;
+    if (live) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  const int per = (n + kThreads - 1) / kThreads;
+  const int e0 = min(n, t * per), e1 = min(n, e0 + per);
+  int s = 0;
+  for (int e = e0; e < e1; ++e) s += cnt[e];
+  part[t] = s;
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const int v = (t >= o) ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - s;
+  for (int e = e0; e < e1; ++e) {
+    off[e] = run;
+    offsets[e] = run;
+    counts[e] = cnt[e];
+    if (importance) importance[e] = 0.f;
+    run += cnt[e];
+  }
+  if (t == kThreads - 1) {
+    off[n] = part[t];
+    offsets[n] = part[t];
+  }
+  __syncthreads();
+  if (t < npairs) {
+    const int e = se[t];
+    if (e >= 0) {
+      int rank = 0;
+      for (int q = 0; q < t; ++q) rank += se[q] == e;
+      const int pos = off[e] + rank;
+      const float gv = gate[t];
+      perm_token[pos] = t / k;
+      perm_gate[pos] = gv;
+      pg[pos] = gv;
+      slot_pos[t] = pos;
+      if (rank == 0) lst[atomicAdd(&nlst, 1)] = e;
+    } else {
+      slot_pos[t] = -1;
+    }
+  }
+  __syncthreads();
+  if (importance) {
+    const int lane = t & 63;
+    for (int i = t >> 6; i < nlst; i += kWaves) {
+      const int e = lst[i];
+      float v = 0.f;
+      for (int j = off[e] + lane; j < off[e + 1]; j += 64) v += pg[j];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0) importance[e] = v;
+    }
+  }
+}
+
 __global__ void fill_zero_i32(int32_t* __restrict__ p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -182,9 +270,18 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
                         hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * (int)sizeof(int));
     hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter),
                         hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * (int)sizeof(int));
+    hipFuncSetAttribute(reinterpret_cast<const void*>(route_small),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallLds);
     return true;
   }();
   (void)lds_attr_set;
+  if (npairs > 0 && npairs <= kSmallPairs && n <= kSmallExperts) {
+    const size_t small_lds = (2 * (size_t)n + 1 + 3 * kSmallPairs) * sizeof(int);
+    hipLaunchKernelGGL(route_small, dim3(1), dim3(kThreads), small_lds, s, topk_idx, topk_gate,
+                       (int)npairs, k, n, counts, offsets, perm_token, perm_gate, slot_pos,
+                       importance);
+    return hipGetLastError();
+  }
   if (nblk > 0) {
     hipLaunchKernelGGL(route_count, dim3(nblk), dim3(kThreads), lds, s, topk_idx, npairs, ppb, n,
                        nblk, blockcnt);
