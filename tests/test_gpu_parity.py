@@ -437,6 +437,38 @@ def test_ffn_timing_counts_forward_calls():
     assert n == 3 and ms > 0
 
 
+@pytest.mark.parametrize("tokens,train", [(3, False), (5, True), (3000, True)])
+def test_forward_graph_replays(tokens, train):
+    """moe_forward captured in a HIP graph (it allocates nothing, makes no
+    copies or fills and never synchronizes): every replay, with eager calls
+    of the same MoeForward on other inputs and synchronizations in between,
+    gives exactly the eager outputs. Small batches take the split gate and
+    FFN and the one-workgroup route."""
+    w = wl("flat_bf16_n4096", tokens=tokens, n_experts=256, d_hidden=256)
+    announce(f"moe_forward graph replay tokens={tokens} train={train}")
+    inp = dg.make_inputs(w)
+    g = gpu_inputs(inp)
+    f = moe.MoeForward(tuple(g["x"].shape), g["w_gate"], g["w_noise"], g["w1"], g["w2"], w.k,
+                       train=train)
+    x, eps = g["x"].clone(), g["eps"].clone()
+    y = torch.empty_like(x)
+    idx = torch.empty((w.tokens, w.k), dtype=torch.int32, device=x.device)
+    f(x, eps, y, topk_idx=idx)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (y, idx, f.importance, f.load, f.losses)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        f(x, eps, y, topk_idx=idx)
+    other_x, other_eps = torch.flip(x, [0]).contiguous(), torch.flip(eps, [0]).contiguous()
+    for _ in range(3):
+        f(other_x, other_eps)  # eager work on the same workspace and loss buffers
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a_, b_ in zip(ref, (y, idx, f.importance, f.load, f.losses)):
+            assert torch.equal(a_, b_)
+
+
 def test_empty_batch():
     w = wl("tiny_fp32", tokens=0)
     announce("moe_forward empty batch")
