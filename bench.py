@@ -240,6 +240,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=0,
                     help="batch size instead of the workload's (same model), e.g. 1 for the "
                          "latency of a single token")
+    ap.add_argument("--capacity-factor", type=float, default=0.0, metavar="F",
+                    help="fixed expert capacity ceil(F * tokens * k / n) rows (GShard variant; "
+                         "0: no limit, the pages' layer)")
     ap.add_argument("--train", type=int, default=1, choices=(0, 1),
                     help="1: noisy gating with the Load pass (the headline step); 0: inference")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -281,8 +284,9 @@ def main():
     g = {key: to_device(v, torch, np) for key, v in inp.items()}
     torch.cuda.synchronize()
 
+    cap = int(np.ceil(a.capacity_factor * B * k / n)) if a.capacity_factor > 0 else 0
     f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,
-                       gate_bias=g.get("gate_bias"), train=bool(a.train))
+                       gate_bias=g.get("gate_bias"), train=bool(a.train), capacity=cap)
     dev = g["x"].device
     y = torch.empty((B, d), dtype=g["x"].dtype, device=dev)
     topk_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
@@ -325,11 +329,11 @@ def main():
                                                 g["eps"] if a.train else None, k,
                                                 train=bool(a.train), gate_bias=g.get("gate_bias"),
                                                 ws=ws), it, torch),
-        "route": time_calls(lambda: moe.moe_route(topk_idx, topk_gate, n, d_model=d, ws=ws),
-                            it, torch),
+        "route": time_calls(lambda: moe.moe_route(topk_idx, topk_gate, n, d_model=d, ws=ws,
+                                                  capacity=cap), it, torch),
         "expert_ffn": time_calls(lambda: moe.moe_expert_ffn(
-            g["x"], route["offsets"], route["perm_token"], g["w1"], g["w2"], k, ws=ws, out=eo),
-            it, torch),
+            g["x"], route["offsets"], route["perm_token"], g["w1"], g["w2"], k, ws=ws, out=eo,
+            capacity=cap), it, torch),
         "combine": time_calls(lambda: moe.moe_combine(eo, route["slot_pos"], topk_gate,
                                                       n_experts=n, out=y), it, torch),
     }
@@ -346,6 +350,8 @@ def main():
     cnt = counts.cpu().numpy()
     esize = 2 if w.expert_dtype == dg.BF16 else 4
     asize = 2 if w.act_dtype == dg.BF16 else 4
+    if cap:  # the rows the experts serve
+        cnt = np.minimum(cnt, cap)
     used = int((cnt > 0).sum())
     rows = int(cnt.sum())
     ffn_bytes = used * 2 * d * h * esize + 2 * rows * d * asize
@@ -376,7 +382,7 @@ def main():
         "dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "n_experts": n,
-                   "k": k, "train": a.train, "act_dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
+                   "k": k, "train": a.train, "capacity": cap, "act_dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
                    "gate_dtype": "bf16" if w.gate_dtype == dg.BF16 else "f32"},
         "roofline": {"kernel": "ffn_kernel (expert FFN)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

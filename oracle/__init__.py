@@ -215,8 +215,16 @@ def expert_pairs(inp: Dict[str, np.ndarray], tokens: Sequence[int], experts: Seq
     return out
 
 
-def route(topk_idx: np.ndarray, topk_gate: np.ndarray, n: int) -> Dict[str, np.ndarray]:
-    """Stable expert-major routing of the (token, slot) pairs, plus Importance."""
+def route(topk_idx: np.ndarray, topk_gate: np.ndarray, n: int,
+          capacity: int = 0) -> Dict[str, np.ndarray]:
+    """Stable expert-major routing of the (token, slot) pairs, plus Importance.
+
+    capacity > 0 is the fixed per-expert capacity of the GShard variant that
+    [MoE-explainer] "From LSTMs to Switch and Mixtral" contrasts with this
+    layer: an expert serves only its first `capacity` routed rows (in (token,
+    slot) order, i.e. the first positions of its segment); the other pairs keep
+    their place in the segments, counts and Importance but get slot_pos -1, so
+    they add nothing to y."""
     idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
     gates = np.ascontiguousarray(topk_gate, dtype=np.float64)
     B, k = idx.shape
@@ -228,6 +236,11 @@ def route(topk_idx: np.ndarray, topk_gate: np.ndarray, n: int) -> Dict[str, np.n
                                                                  "perm_gate", "slot_pos",
                                                                  "importance")])
     _check(rc, "route")
+    if capacity > 0:
+        sp = out["slot_pos"]
+        for p in range(B * k):
+            if sp[p] >= 0 and sp[p] - out["offsets"][idx.flat[p]] >= capacity:
+                sp[p] = -1
     return out
 
 

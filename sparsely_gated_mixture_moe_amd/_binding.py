@@ -29,7 +29,7 @@ class MoeDims(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("d_model", ctypes.c_int32),
                 ("d_hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int), ("expert_dtype", ctypes.c_int),
-                ("gate_dtype", ctypes.c_int)]
+                ("gate_dtype", ctypes.c_int), ("capacity", ctypes.c_int32)]
 
 
 class MoeGateOpts(ctypes.Structure):
@@ -150,8 +150,9 @@ def moe_ffn_timing_read() -> Tuple[int, float]:
 
 
 def make_dims(tokens: int, d_model: int, d_hidden: int, n_experts: int, k: int,
-              act_dtype: int, expert_dtype: int, gate_dtype: int) -> MoeDims:
-    return MoeDims(tokens, d_model, d_hidden, n_experts, k, act_dtype, expert_dtype, gate_dtype)
+              act_dtype: int, expert_dtype: int, gate_dtype: int, capacity: int = 0) -> MoeDims:
+    return MoeDims(tokens, d_model, d_hidden, n_experts, k, act_dtype, expert_dtype, gate_dtype,
+                   capacity)
 
 
 def make_opts(train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
@@ -206,13 +207,14 @@ def moe_gate(x, w_gate, w_noise, eps, k: int, *, train: bool = True, noise_floor
 
 
 def moe_route(topk_idx, topk_gate, n_experts: int, *, d_model: int = 64,
-              ws: Optional[torch.Tensor] = None, with_importance: bool = True,
+              ws: Optional[torch.Tensor] = None, with_importance: bool = True, capacity: int = 0,
               stream=None) -> Dict[str, torch.Tensor]:
-    """Stable expert-major routing: counts, offsets, perm_token, perm_gate, slot_pos, importance."""
+    """Stable expert-major routing: counts, offsets, perm_token, perm_gate, slot_pos, importance.
+    capacity > 0: slots past the first `capacity` rows of their expert get slot_pos -1."""
     _dev(topk_idx, "topk_idx", torch.int32)
     B, k = topk_idx.shape
     _dev(topk_gate, "topk_gate", torch.float32, (B, k))
-    dims = make_dims(B, d_model, 128, n_experts, k, MOE_F32, MOE_F32, MOE_F32)
+    dims = make_dims(B, d_model, 128, n_experts, k, MOE_F32, MOE_F32, MOE_F32, capacity)
     dev = topk_idx.device
     if ws is None:
         ws = workspace(dims, None, dev)
@@ -232,8 +234,10 @@ def moe_route(topk_idx, topk_gate, n_experts: int, *, d_model: int = 64,
 
 
 def moe_expert_ffn(x, offsets, perm_token, w1, w2, k: int, *, b1=None, b2=None,
-                   ws: Optional[torch.Tensor] = None, out=None, stream=None) -> torch.Tensor:
-    """expert_out [B*k, d] in permutation order: E_e(x[perm_token[p]]) per segment."""
+                   ws: Optional[torch.Tensor] = None, out=None, capacity: int = 0,
+                   stream=None) -> torch.Tensor:
+    """expert_out [B*k, d] in permutation order: E_e(x[perm_token[p]]) per segment (with
+    capacity > 0 only the first `capacity` rows of each segment are computed)."""
     _dev(x, "x")
     B, d = x.shape
     _dev(w1, "w1", x.dtype)
@@ -243,7 +247,7 @@ def moe_expert_ffn(x, offsets, perm_token, w1, w2, k: int, *, b1=None, b2=None,
     _dev(b2, "b2", x.dtype, (n, d))
     _dev(offsets, "offsets", torch.int32, (n + 1,))
     _dev(perm_token, "perm_token", torch.int32, (B * k,))
-    dims = make_dims(B, d, h, n, k, _dt(x), _dt(w1), _dt(x))
+    dims = make_dims(B, d, h, n, k, _dt(x), _dt(w1), _dt(x), capacity)
     if ws is None:
         ws = workspace(dims, None, x.device)
     if out is None:
@@ -311,7 +315,8 @@ class MoeForward:
 
     def __init__(self, x_shape, w_gate, w_noise, w1, w2, k: int, *, b1=None, b2=None,
                  gate_bias=None, train: bool = True, noise_floor: float = 1e-2,
-                 w_importance: float = 0.1, w_load: float = 0.1, act_dtype=None):
+                 w_importance: float = 0.1, w_load: float = 0.1, act_dtype=None,
+                 capacity: int = 0):
         B, d = x_shape
         n, h, _ = w1.shape
         self.w_gate, self.w_noise, self.w1, self.w2, self.b1, self.b2 = w_gate, w_noise, w1, w2, b1, b2
@@ -324,7 +329,7 @@ class MoeForward:
         _dev(b2, "b2", w1.dtype, (n, d))
         _dev(gate_bias, "gate_bias", torch.float32, (n,))
         adt = _dt(w1) if act_dtype is None else act_dtype
-        self.dims = make_dims(B, d, h, n, k, adt, _dt(w1), _dt(w_gate))
+        self.dims = make_dims(B, d, h, n, k, adt, _dt(w1), _dt(w_gate), capacity)
         self.opts = make_opts(train, noise_floor, w_importance, w_load)
         dev = w1.device
         self.ws = workspace(self.dims, self.opts, dev)
@@ -359,10 +364,12 @@ class MoeForward:
 
 def moe_forward(x, w_gate, w_noise, eps, w1, w2, k: int, *, b1=None, b2=None, gate_bias=None,
                 train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
-                w_load: float = 0.1, return_routing: bool = False, stream=None):
+                w_load: float = 0.1, return_routing: bool = False, capacity: int = 0,
+                stream=None):
     """One call of the whole forward pass; returns a dict of device tensors."""
     f = MoeForward(tuple(x.shape), w_gate, w_noise, w1, w2, k, b1=b1, b2=b2, gate_bias=gate_bias,
-                   train=train, noise_floor=noise_floor, w_importance=w_importance, w_load=w_load)
+                   train=train, noise_floor=noise_floor, w_importance=w_importance, w_load=w_load,
+                   capacity=capacity)
     B, n = x.shape[0], w1.shape[0]
     extra = {}
     if return_routing:

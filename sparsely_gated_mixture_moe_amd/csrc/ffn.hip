@@ -500,8 +500,13 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 // as (expert, first pair of its rows, rows) after the count. One workgroup;
 // thread t owns a contiguous span of experts.
 __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ offsets, int n, int bm,
-                                                 int hsplit, int nch,
+                                                 int hsplit, int nch, int capacity,
                                                  int32_t* __restrict__ blocks) {
+  // rows of expert e that are served: all, or the first `capacity`
+  auto served = [&](int e) {
+    const int c = offsets[e + 1] - offsets[e];
+    return capacity > 0 ? min(c, capacity) : c;
+  };
   __shared__ int part[1024];
   const int t = threadIdx.x;
   const int per = (n + 1023) / 1024;
@@ -510,7 +515,7 @@ __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ off
   // ranges of hper chunks (the launcher picks hsplit so that none is empty)
   const int hper = (nch + hsplit - 1) / hsplit;
   int s = 0;
-  for (int e = e0; e < e1; ++e) s += (offsets[e + 1] - offsets[e] + bm - 1) / bm * hsplit;
+  for (int e = e0; e < e1; ++e) s += (served(e) + bm - 1) / bm * hsplit;
   part[t] = s;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
@@ -523,7 +528,7 @@ __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ off
   FfnUnit* units = reinterpret_cast<FfnUnit*>(blocks + 4);
   for (int e = e0; e < e1; ++e) {
     const int seg = offsets[e];
-    const int cnt = offsets[e + 1] - seg;
+    const int cnt = served(e);
     for (int r = 0; r < cnt; r += bm) {
       for (int q = 0; q < hsplit; ++q) {
         const int hr = hsplit > 1 ? (q * hper) | (min(hper, nch - q * hper) << 16) : 0;
@@ -587,10 +592,11 @@ hipError_t device_cus(int* cus) {
 
 template <typename T, int D>
 hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* offsets, int n,
-                        int hsplit, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                        int hsplit, int capacity, hipStream_t s, hipEvent_t ev0,
+                        hipEvent_t ev1) {
   using S = FfnShape<T, D>;
   hipLaunchKernelGGL(ffn_plan, dim3(1), dim3(1024), 0, s, offsets, n, S::BM, hsplit,
-                     p.h / S::HC, const_cast<int32_t*>(p.blocks));
+                     p.h / S::HC, capacity, const_cast<int32_t*>(p.blocks));
   max_blocks *= hsplit;
   if (max_blocks <= 0) {  // no rows: an empty timed interval
     hipError_t er = hipGetLastError();
@@ -682,7 +688,8 @@ bool ffn_supported(int d, int h, Dt dt) {
 hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const void* x,
                       const int32_t* offsets, const int32_t* perm_token, const void* w1,
                       const void* b1, const void* w2, const void* b2, void* expert_out,
-                      int32_t* blocks, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                      int32_t* blocks, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                      int capacity) {
   const int64_t mb = ffn_max_blocks(tokens * k, n, d, dt);
   const int hs = ffn_hsplit(tokens * k, n, d, h, dt);
   FfnParams p{x, offsets, perm_token, w1, b1, w2, b2, expert_out, blocks, h, nullptr, 0};
@@ -693,17 +700,17 @@ hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const v
   }
   if (dt == kBF16) {
     switch (d) {
-      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, hs, s, ev0, ev1);
-      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, hs, s, ev0, ev1);
-      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, hs, s, ev0, ev1);
-      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, hs, s, ev0, ev1);
+      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
+      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
+      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
+      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
     }
   } else {
     switch (d) {
-      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, hs, s, ev0, ev1);
-      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, hs, s, ev0, ev1);
-      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, hs, s, ev0, ev1);
-      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, hs, s, ev0, ev1);
+      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
+      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
+      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
+      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
     }
   }
   return hipErrorInvalidValue;

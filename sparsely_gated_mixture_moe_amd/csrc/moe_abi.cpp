@@ -50,6 +50,7 @@ moe_status check_dims(const moe_dims* d) {
   if (d->k < 1 || d->k > d->n_experts)
     return fail(MOE_ERR_INVALID, "k = %d outside [1, n_experts = %d]", d->k, d->n_experts);
   if (d->k > 8) return fail(MOE_ERR_UNSUPPORTED, "k = %d > 8", d->k);
+  if (d->capacity < 0) return fail(MOE_ERR_INVALID, "capacity = %d < 0", d->capacity);
   if (d->tokens * (int64_t)d->k > (int64_t)0x7FFFFFFE)
     return fail(MOE_ERR_INVALID, "tokens * k = %lld does not fit int32 indices",
                 (long long)(d->tokens * d->k));
@@ -234,7 +235,7 @@ moe_status check_hier_dims(const moe_hier_dims* h) {
   if (h->k1 * h->k2 > 8) return fail(MOE_ERR_UNSUPPORTED, "k1 * k2 = %d > 8", h->k1 * h->k2);
   // the leaf layer: the same limits as a flat layer with k = k1 * k2
   moe_dims leaf{h->tokens, h->d_model, h->d_hidden, h->groups * h->group_experts,
-                h->k1 * h->k2, h->act_dtype, h->expert_dtype, h->gate_dtype};
+                h->k1 * h->k2, h->act_dtype, h->expert_dtype, h->gate_dtype, 0};
   return check_dims(&leaf);
 }
 
@@ -451,7 +452,7 @@ moe_status moe_route(const moe_dims* dims, const int32_t* topk_idx, const float*
   return device_status(
       moe::launch_route(dims->tokens, dims->k, dims->n_experts, topk_idx, topk_gate,
                         at<int32_t>(ws, 0), counts, offsets, perm_token, perm_gate, slot_pos,
-                        importance, (hipStream_t)stream),
+                        importance, (hipStream_t)stream, dims->capacity),
       "moe_route");
 }
 
@@ -476,7 +477,7 @@ moe_status moe_expert_ffn(const moe_dims* dims, const void* x, const int32_t* of
   return device_status(
       moe::launch_ffn(dims->tokens, dims->k, dims->d_model, dims->d_hidden, dims->n_experts,
                       to_dt(dims->act_dtype), x, offsets, perm_token, w1, b1, w2, b2, expert_out,
-                      at<int32_t>(ws, 0), (hipStream_t)stream),
+                      at<int32_t>(ws, 0), (hipStream_t)stream, nullptr, nullptr, dims->capacity),
       "moe_expert_ffn");
 }
 
@@ -572,13 +573,13 @@ moe_status moe_forward(const moe_dims* dims, const moe_gate_opts* opts, const vo
   if (e != hipSuccess) return device_status(e, "moe_forward (gate)");
   e = moe::launch_route(dims->tokens, dims->k, dims->n_experts, topk_idx, topk_gate,
                         at<int32_t>(ws, L.blockcnt), counts, offsets, perm_token, perm_gate,
-                        slot_pos, importance, st);
+                        slot_pos, importance, st, dims->capacity);
   if (e != hipSuccess) return device_status(e, "moe_forward (route)");
   hipEvent_t t0, t1;
   timing_pair(&t0, &t1);
   e = moe::launch_ffn(dims->tokens, dims->k, dims->d_model, dims->d_hidden, dims->n_experts,
                       to_dt(dims->act_dtype), x, offsets, perm_token, w1, b1, w2, b2, expert_out,
-                      at<int32_t>(ws, L.ffn_blocks), st, t0, t1);
+                      at<int32_t>(ws, L.ffn_blocks), st, t0, t1, dims->capacity);
   if (e != hipSuccess) return device_status(e, "moe_forward (expert_ffn)");
   e = moe::launch_combine(dims->tokens, dims->k, dims->d_model, to_dt(dims->act_dtype), expert_out,
                           slot_pos, topk_gate, y, st);

@@ -94,10 +94,12 @@ hipError_t launch_load_grouped(const GateLaunch& g, int groups, const int32_t* u
 
 // Routing.
 int route_blocks(int64_t tokens);
+// capacity > 0: pairs past the first `capacity` of their expert's segment
+// get slot_pos -1 (the segments and counts are unchanged).
 hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
                         const float* topk_gate, int32_t* blockcnt /* [n][route_blocks] */,
                         int32_t* counts, int32_t* offsets, int32_t* perm_token, float* perm_gate,
-                        int32_t* slot_pos, float* importance, hipStream_t s);
+                        int32_t* slot_pos, float* importance, hipStream_t s, int capacity = 0);
 
 // Expert FFN.
 int ffn_rows_per_block(int d, Dt dt);
@@ -109,12 +111,13 @@ size_t ffn_plan_bytes(int64_t rows, int n, int d, int h, Dt dt);
 int ffn_hsplit(int64_t rows, int n, int d, int h, Dt dt);
 bool ffn_supported(int d, int h, Dt dt);
 // ev0 / ev1, when given, are recorded on s right before and after the FFN
-// kernel (after its plan kernel).
+// kernel (after its plan kernel); capacity > 0 computes only the first
+// `capacity` rows of each segment.
 hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const void* x,
                       const int32_t* offsets, const int32_t* perm_token, const void* w1,
                       const void* b1, const void* w2, const void* b2, void* expert_out,
                       int32_t* blocks /* [2*max_blocks + 1] */, hipStream_t s,
-                      hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                      hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, int capacity = 0);
 
 // Weighted sum.
 hipError_t launch_combine(int64_t tokens, int k, int d, Dt dt, const void* expert_out,

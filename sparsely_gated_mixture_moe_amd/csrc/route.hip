@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     const int32_t* __restrict__ idx, const float* __restrict__ gate, int64_t npairs, int k,
     int pairs_per_block, int n, int nbits, int nblk, const int32_t* __restrict__ blockoff,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
-    float* __restrict__ perm_gate, int32_t* __restrict__ slot_pos) {
+    float* __restrict__ perm_gate, int32_t* __restrict__ slot_pos, int capacity) {
   extern __shared__ int ctr[];
   for (int e = threadIdx.x; e < n; e += kThreads)
     ctr[e] = offsets[e] + blockoff[(int64_t)e * nblk + blockIdx.x];
@@ -137,7 +137,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
       const int pos = start + rank;
       perm_token[pos] = (int32_t)(p / k);
       perm_gate[pos] = gate[p];
-      slot_pos[p] = pos;
+      // past the expert's capacity: routed, but not served
+      slot_pos[p] = (capacity > 0 && pos - offsets[e] >= capacity) ? -1 : pos;
     } else if (valid) {
       slot_pos[p] = -1;
     }
@@ -170,7 +171,8 @@ constexpr size_t kSmallLds = (2 * (size_t)kSmallExperts + 1 + 3 * kSmallPairs) *
 __global__ __launch_bounds__(kThreads) void route_small(
     const int32_t* __restrict__ idx, const float* __restrict__ gate, int npairs, int k, int n,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
-    float* __restrict__ perm_gate, int32_t* __restrict__ slot_pos, float* __restrict__ importance) {
+    float* __restrict__ perm_gate, int32_t* __restrict__ slot_pos, float* __restrict__ importance,
+    int capacity) {
   extern __shared__ int sm[];
   int* cnt = sm;                                    // [n]
   int* off = cnt + n;                               // [n + 1]
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void route_small(
       perm_token[pos] = t / k;
       perm_gate[pos] = gv;
       pg[pos] = gv;
-      slot_pos[t] = pos;
+      slot_pos[t] = (capacity > 0 && rank >= capacity) ? -1 : pos;
       if (rank == 0) lst[atomicAdd(&nlst, 1)] = e;
     } else {
       slot_pos[t] = -1;
@@ -257,7 +259,7 @@ int route_blocks(int64_t tokens) { return (int)((tokens + kRouteTokens - 1) / kR
 hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
                         const float* topk_gate, int32_t* blockcnt, int32_t* counts,
                         int32_t* offsets, int32_t* perm_token, float* perm_gate, int32_t* slot_pos,
-                        float* importance, hipStream_t s) {
+                        float* importance, hipStream_t s, int capacity) {
   const int nblk = route_blocks(tokens);
   const int64_t npairs = tokens * k;
   const int ppb = kRouteTokens * k;
@@ -279,7 +281,7 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
     const size_t small_lds = (2 * (size_t)n + 1 + 3 * kSmallPairs) * sizeof(int);
     hipLaunchKernelGGL(route_small, dim3(1), dim3(kThreads), small_lds, s, topk_idx, topk_gate,
                        (int)npairs, k, n, counts, offsets, perm_token, perm_gate, slot_pos,
-                       importance);
+                       importance, capacity);
     return hipGetLastError();
   }
   if (nblk > 0) {
@@ -294,7 +296,7 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
   if (nblk > 0)
     hipLaunchKernelGGL(route_scatter, dim3(nblk), dim3(kThreads), lds, s, topk_idx, topk_gate,
                        npairs, k, ppb, n, nbits, nblk, blockcnt, offsets, perm_token, perm_gate,
-                       slot_pos);
+                       slot_pos, capacity);
   if (importance)
     hipLaunchKernelGGL(route_importance, dim3((n + 3) / 4), dim3(256), 0, s, perm_gate, offsets, n,
                        importance);

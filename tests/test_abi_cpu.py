@@ -30,12 +30,12 @@ def test_header_symbols_are_exported():
     assert "moe_forward" in names and len(names) >= 10
     for name in names:
         assert hasattr(L, name), f"{name} declared in moe.h but not exported"
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def dims(**kw):
     base = dict(tokens=1024, d_model=512, d_hidden=1024, n_experts=64, k=4, act_dtype=1,
-                expert_dtype=1, gate_dtype=1)
+                expert_dtype=1, gate_dtype=1, capacity=0)
     base.update(kw)
     return B.MoeDims(*[base[f] for f, _ in B.MoeDims._fields_])
 
@@ -75,6 +75,7 @@ def last_error():
     ({"expert_dtype": 0}, UNSUPPORTED, "expert_dtype"),
     ({"act_dtype": 7}, INVALID, "dtype"),
     ({"tokens": 600_000_000}, INVALID, "int32"),
+    ({"capacity": -1}, INVALID, "capacity"),
 ])
 def test_invalid_dims(kw, status, msg):
     assert call_gate(dims(**kw), opts()) == status

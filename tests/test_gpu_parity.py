@@ -181,6 +181,59 @@ def test_route_full_size_against_stable_sort(B, n, k):
     assert rel_err(to_host(out["importance"]), imp) <= 1e-5
 
 
+# capacity < the largest count: dropped pairs in both route paths (one workgroup for
+# at most 1024 pairs, five kernels above), skewed so that popular experts overflow
+CAPACITY_ROUTE_CASES = [(200, 16, 2, 1.0, 20), (3, 8, 8, 0.0, 1), (3000, 64, 4, 1.0, 150),
+                        (65536, 4096, 4, 0.0, 70)]
+
+
+@pytest.mark.parametrize("B,n,k,skew,cap", CAPACITY_ROUTE_CASES)
+def test_route_capacity_parity(B, n, k, skew, cap):
+    announce(f"moe_route capacity B={B} n={n} k={k} cap={cap}")
+    idx, gate = _random_topk(B, n, k, seed=B + 3 * n, skew=skew)
+    ref = oracle.route(idx, gate, n, capacity=cap)
+    assert (ref["slot_pos"] < 0).any()  # the case drops pairs
+    out = moe.moe_route(to_device(idx), to_device(gate), n, capacity=cap)
+    torch.cuda.synchronize()
+    for key in ("counts", "offsets", "perm_token", "slot_pos"):
+        assert np.array_equal(to_host(out[key]), ref[key]), key
+    assert rel_err(to_host(out["importance"]), ref["importance"]) <= 1e-5
+
+
+@pytest.mark.parametrize("case,cap", [(("zipf_bf16_n256", {"tokens": 2000}), 40),
+                                      (("flat_bf16_n4096", {"tokens": 700, "n_experts": 64}), 30),
+                                      (("tiny_fp32", {"tokens": 200}), 20)])
+def test_forward_capacity_parity(case, cap):
+    """The whole forward with a fixed expert capacity: gating against the
+    oracle as everywhere; y against the oracle's routing of the GPU's own
+    selection with the same capacity (so a near tie elsewhere cannot move the
+    ranks), summing only the served slots of each token."""
+    name, kw = case
+    w = wl(name, **kw)
+    announce(f"moe_forward capacity {w.name} {kw} cap={cap}")
+    inp = dg.make_inputs(w, with_bias=(name == "zipf_bf16_n256"))
+    g = gpu_inputs(inp)
+    out = moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], w.k,
+                          b1=g.get("b1"), b2=g.get("b2"), gate_bias=g.get("gate_bias"),
+                          noise_floor=FLOOR, capacity=cap, return_routing=True)
+    torch.cuda.synchronize()
+    ref_g = oracle.gate(inp, w.k, noise_floor=FLOOR, want_logits=True)
+    check_gating(ref_g, ref_g["H"], to_host(out["topk_idx"]), to_host(out["topk_gate"]),
+                 to_host(out["thresh"]))
+    idx, gate = to_host(out["topk_idx"]), to_host(out["topk_gate"]).astype(np.float64)
+    rt = oracle.route(idx, gate, w.n_experts, capacity=cap)
+    served = rt["slot_pos"] >= 0
+    assert not served.all()
+    tok = np.repeat(np.arange(w.tokens), w.k)[served]
+    eo = oracle.expert_pairs(inp, tok, idx.ravel()[served])
+    y_ref = np.zeros((w.tokens, w.d_model))
+    np.add.at(y_ref, tok, gate.ravel()[served][:, None] * eo)
+    err = rel_err(to_host(out["y"]), y_ref)
+    print(w.name, kw, "cap", cap, "served", served.mean(), "y err", err)
+    assert err <= out_tol(w.act_dtype == dg.BF16)
+    assert np.array_equal(to_host(out["counts"]), rt["counts"])
+
+
 def test_route_drops_out_of_range_entries():
     announce("moe_route out-of-range entries")
     idx = np.array([[0, 3], [-1, 2], [3, 9], [2, 0]], np.int32)

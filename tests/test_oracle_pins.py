@@ -489,6 +489,43 @@ def test_route_handles_empty_experts():
     assert r["perm_token"].tolist() == [0, 1, 2, 0, 1, 2]
 
 
+def test_route_capacity_hand_example():
+    """Fixed expert capacity (the GShard variant named beside the layer): each
+    expert serves its first C pairs in (token, slot) order. Worked by hand for
+    B = 5, k = 2, n = 3, C = 2: expert 0 is picked by (0,0) (1,0) (2,1) (3,0)
+    (4,1) at positions 0-4 and serves the first two; expert 1 by (0,1) (2,0)
+    (3,1) at 5-7, serving two; expert 2 by (1,1) (4,0) at 8-9, serving both."""
+    idx = np.array([[0, 1], [0, 2], [1, 0], [0, 1], [2, 0]], np.int32)
+    gates = np.full((5, 2), 0.5)
+    full = oracle.route(idx, gates, 3)
+    assert full["slot_pos"].tolist() == [0, 5, 1, 8, 6, 2, 3, 7, 9, 4]
+    capped = oracle.route(idx, gates, 3, capacity=2)
+    assert capped["slot_pos"].tolist() == [0, 5, 1, 8, 6, -1, -1, -1, 9, -1]
+    # the demand is unchanged: segments, counts and Importance list every pair
+    for key in ("counts", "offsets", "perm_token", "perm_gate", "importance"):
+        assert np.array_equal(full[key], capped[key])
+
+
+def test_route_capacity_properties():
+    rng = np.random.default_rng(19)
+    B, n, k = 400, 13, 3
+    idx = np.stack([rng.permutation(n)[:k] for _ in range(B)]).astype(np.int32)
+    gates = rng.uniform(size=(B, k))
+    full = oracle.route(idx, gates, n)
+    for cap in (1, 5, 50, int(full["counts"].max())):
+        r = oracle.route(idx, gates, n, capacity=cap)
+        kept = r["slot_pos"] >= 0
+        served = np.bincount(idx.ravel()[kept], minlength=n)
+        assert np.array_equal(served, np.minimum(full["counts"], cap))
+        # a served pair keeps its position; it precedes every dropped pair of its expert
+        assert np.array_equal(r["slot_pos"][kept], full["slot_pos"][kept])
+        for e in range(n):
+            pe = np.flatnonzero(idx.ravel() == e)
+            assert kept[pe].tolist() == sorted(kept[pe].tolist(), reverse=True)
+    r = oracle.route(idx, gates, n, capacity=int(full["counts"].max()))
+    assert np.array_equal(r["slot_pos"], full["slot_pos"])
+
+
 # --------------------------------------------------------------------------
 # bf16 inputs are read by exact widening
 # --------------------------------------------------------------------------
