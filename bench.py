@@ -243,6 +243,9 @@ def main():
     ap.add_argument("--capacity-factor", type=float, default=0.0, metavar="F",
                     help="fixed expert capacity ceil(F * tokens * k / n) rows (GShard variant; "
                          "0: no limit, the pages' layer)")
+    ap.add_argument("--gate-order", type=int, default=0, choices=(0, 1),
+                    help="0: softmax over the kept k (the pages); 1: softmax over all n, then "
+                         "the kept k (Switch's order)")
     ap.add_argument("--train", type=int, default=1, choices=(0, 1),
                     help="1: noisy gating with the Load pass (the headline step); 0: inference")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -286,7 +289,8 @@ def main():
 
     cap = int(np.ceil(a.capacity_factor * B * k / n)) if a.capacity_factor > 0 else 0
     f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,
-                       gate_bias=g.get("gate_bias"), train=bool(a.train), capacity=cap)
+                       gate_bias=g.get("gate_bias"), train=bool(a.train), capacity=cap,
+                       gate_order=a.gate_order)
     dev = g["x"].device
     y = torch.empty((B, d), dtype=g["x"].dtype, device=dev)
     topk_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
@@ -328,7 +332,7 @@ def main():
         "gate": time_calls(lambda: moe.moe_gate(g["x"], g["w_gate"], g["w_noise"],
                                                 g["eps"] if a.train else None, k,
                                                 train=bool(a.train), gate_bias=g.get("gate_bias"),
-                                                ws=ws), it, torch),
+                                                ws=ws, gate_order=a.gate_order), it, torch),
         "route": time_calls(lambda: moe.moe_route(topk_idx, topk_gate, n, d_model=d, ws=ws,
                                                   capacity=cap), it, torch),
         "expert_ffn": time_calls(lambda: moe.moe_expert_ffn(
@@ -382,7 +386,8 @@ def main():
         "dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "n_experts": n,
-                   "k": k, "train": a.train, "capacity": cap, "act_dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
+                   "k": k, "train": a.train, "capacity": cap, "gate_order": a.gate_order,
+                   "act_dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
                    "gate_dtype": "bf16" if w.gate_dtype == dg.BF16 else "f32"},
         "roofline": {"kernel": "ffn_kernel (expert FFN)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -140,14 +140,20 @@ class _Gate:
 
 def gate(inp: Dict[str, np.ndarray], k: int, train: bool = True, noise_floor: float = 1e-2,
          rows: Optional[Sequence[int]] = None, decide_fp32: bool = True,
-         want_logits: bool = False) -> Dict[str, np.ndarray]:
-    """Noisy top-k gating for all rows or a list of rows."""
+         want_logits: bool = False, gate_order: int = 0) -> Dict[str, np.ndarray]:
+    """Noisy top-k gating for all rows or a list of rows.
+
+    gate_order 1 keeps the same selection but takes the gates from the softmax
+    over all n logits, the order of operations [MoE-explainer] "From LSTMs to
+    Switch and Mixtral" attributes to Switch: G_i = exp(H_i) / sum_j exp(H_j)
+    for the kept i (so a row's gates sum to at most 1)."""
     g = _Gate(inp, train)
     n = g.n
     rws = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     nr = g.B if rws is None else rws.size
     out = {"topk_idx": np.empty((nr, k), np.int32), "topk_gate": np.empty((nr, k), np.float64),
            "thresh": np.empty((nr, 2), np.float64)}
+    want_logits = want_logits or gate_order == 1
     if want_logits:
         for key in ("clean", "sigma", "H"):
             out[key] = np.empty((nr, n), np.float64)
@@ -156,6 +162,11 @@ def gate(inp: Dict[str, np.ndarray], k: int, train: bool = True, noise_floor: fl
                              _ptr(out.get("H")), _ptr(out["topk_idx"]), _ptr(out["topk_gate"]),
                              _ptr(out["thresh"]))
     _check(rc, "gate")
+    if gate_order == 1 and nr > 0:
+        H = out["H"]
+        top = H.max(axis=1, keepdims=True)
+        z = np.exp(H - top).sum(axis=1, keepdims=True)
+        out["topk_gate"] = np.exp(np.take_along_axis(H, out["topk_idx"].astype(np.int64), 1) - top) / z
     return out
 
 

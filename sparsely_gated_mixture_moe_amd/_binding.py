@@ -34,7 +34,8 @@ class MoeDims(ctypes.Structure):
 
 class MoeGateOpts(ctypes.Structure):
     _fields_ = [("train", ctypes.c_int32), ("noise_floor", ctypes.c_float),
-                ("w_importance", ctypes.c_float), ("w_load", ctypes.c_float)]
+                ("w_importance", ctypes.c_float), ("w_load", ctypes.c_float),
+                ("gate_order", ctypes.c_int32)]
 
 
 class MoeHierDims(ctypes.Structure):
@@ -156,8 +157,8 @@ def make_dims(tokens: int, d_model: int, d_hidden: int, n_experts: int, k: int,
 
 
 def make_opts(train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
-              w_load: float = 0.1) -> MoeGateOpts:
-    return MoeGateOpts(int(bool(train)), noise_floor, w_importance, w_load)
+              w_load: float = 0.1, gate_order: int = 0) -> MoeGateOpts:
+    return MoeGateOpts(int(bool(train)), noise_floor, w_importance, w_load, int(gate_order))
 
 
 def moe_workspace_size(dims: MoeDims, opts: Optional[MoeGateOpts] = None) -> int:
@@ -182,7 +183,7 @@ def _gate_dims(x, w_gate, k, d_hidden=128, w1=None) -> MoeDims:
 
 
 def moe_gate(x, w_gate, w_noise, eps, k: int, *, train: bool = True, noise_floor: float = 1e-2,
-             gate_bias=None, ws: Optional[torch.Tensor] = None,
+             gate_bias=None, ws: Optional[torch.Tensor] = None, gate_order: int = 0,
              stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Noisy top-k gating -> (topk_idx [B,k] int32, topk_gate [B,k] fp32, thresh [B,2] fp32).
     ws (optional, moe_workspace_size bytes) lets a small batch split its expert sweep."""
@@ -194,7 +195,7 @@ def moe_gate(x, w_gate, w_noise, eps, k: int, *, train: bool = True, noise_floor
     _dev(gate_bias, "gate_bias", torch.float32, (n,))
     _dev(eps, "eps", torch.float32, (B, n))
     dims = _gate_dims(x, w_gate, k)
-    opts = make_opts(train, noise_floor)
+    opts = make_opts(train, noise_floor, gate_order=gate_order)
     dev = x.device
     idx = torch.empty((B, k), dtype=torch.int32, device=dev)
     gate = torch.empty((B, k), dtype=torch.float32, device=dev)
@@ -316,7 +317,7 @@ class MoeForward:
     def __init__(self, x_shape, w_gate, w_noise, w1, w2, k: int, *, b1=None, b2=None,
                  gate_bias=None, train: bool = True, noise_floor: float = 1e-2,
                  w_importance: float = 0.1, w_load: float = 0.1, act_dtype=None,
-                 capacity: int = 0):
+                 capacity: int = 0, gate_order: int = 0):
         B, d = x_shape
         n, h, _ = w1.shape
         self.w_gate, self.w_noise, self.w1, self.w2, self.b1, self.b2 = w_gate, w_noise, w1, w2, b1, b2
@@ -330,7 +331,7 @@ class MoeForward:
         _dev(gate_bias, "gate_bias", torch.float32, (n,))
         adt = _dt(w1) if act_dtype is None else act_dtype
         self.dims = make_dims(B, d, h, n, k, adt, _dt(w1), _dt(w_gate), capacity)
-        self.opts = make_opts(train, noise_floor, w_importance, w_load)
+        self.opts = make_opts(train, noise_floor, w_importance, w_load, gate_order)
         dev = w1.device
         self.ws = workspace(self.dims, self.opts, dev)
         self.importance = torch.empty(n, dtype=torch.float32, device=dev)
@@ -365,11 +366,11 @@ class MoeForward:
 def moe_forward(x, w_gate, w_noise, eps, w1, w2, k: int, *, b1=None, b2=None, gate_bias=None,
                 train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
                 w_load: float = 0.1, return_routing: bool = False, capacity: int = 0,
-                stream=None):
+                gate_order: int = 0, stream=None):
     """One call of the whole forward pass; returns a dict of device tensors."""
     f = MoeForward(tuple(x.shape), w_gate, w_noise, w1, w2, k, b1=b1, b2=b2, gate_bias=gate_bias,
                    train=train, noise_floor=noise_floor, w_importance=w_importance, w_load=w_load,
-                   capacity=capacity)
+                   capacity=capacity, gate_order=gate_order)
     B, n = x.shape[0], w1.shape[0]
     extra = {}
     if return_routing:

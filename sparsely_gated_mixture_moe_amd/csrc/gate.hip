@@ -11,6 +11,8 @@ using gate_detail::GateParams;
 using gate_detail::GateShape;
 using gate_detail::insert_any;
 using gate_detail::write_selection;
+using gate_detail::ExpSum;
+using gate_detail::expsum_merge;
 
 // load[e] = sum over gate blocks b of partial[b][e], in a fixed order: 32
 // experts per workgroup, 8 threads per expert each summing a strided subset
@@ -286,11 +288,23 @@ __global__ __launch_bounds__(256) void gate_merge_kernel(GateParams p, int range
 #pragma unroll
     for (int j = 0; j < L; ++j) insert_any<L>(lv, li, ov[j], oi[j]);
   }
+  // gate_order 1: the ranges' (max, sum) pairs, strided over the lanes, then
+  // the same pairwise merge
+  ExpSum es{-INFINITY, 0.f};
+  if (p.cand_ms) {
+    for (int r = lane; r < ranges; r += 64)
+      es = expsum_merge(es, ExpSum{p.cand_ms[(row * ranges + r) * 2],
+                                   p.cand_ms[(row * ranges + r) * 2 + 1]});
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1)
+      es = expsum_merge(es, ExpSum{__shfl_xor(es.m, s), __shfl_xor(es.s, s)});
+  }
   if (lane == 0) {
     GateParams q = p;
     q.cand_v = nullptr;
     q.cand_i = nullptr;
-    write_selection<L>(q, row, lv, li);
+    q.cand_ms = nullptr;
+    write_selection<L>(q, row, lv, li, es);
   }
 }
 
@@ -350,7 +364,8 @@ int gate_ranges(const GateLaunch& g) {
 size_t gate_cand_bytes(const GateLaunch& g) {
   const int r = gate_ranges(g);
   if (r <= 1) return 0;
-  return (size_t)g.tokens * r * (g.k <= 4 ? 5 : 9) * 8;
+  // (value, expert) candidates, then a (max, sum) pair per row and range
+  return (size_t)g.tokens * r * ((g.k <= 4 ? 5 : 9) * 8 + 8);
 }
 
 hipError_t launch_gate(const GateLaunch& g0, int32_t* topk_idx, float* topk_gate, float* thresh,
@@ -368,6 +383,9 @@ hipError_t launch_gate(const GateLaunch& g0, int32_t* topk_idx, float* topk_gate
   p.cand_v = static_cast<float*>(cand);
   p.cand_i = reinterpret_cast<int32_t*>(static_cast<char*>(cand) +
                                         (size_t)g.tokens * g.ranges * L * sizeof(float));
+  if (g.gate_order)
+    p.cand_ms = reinterpret_cast<float*>(static_cast<char*>(cand) +
+                                         (size_t)g.tokens * g.ranges * L * 8);
   hipError_t e = gate_dispatch(g, p, false, s);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((g.tokens + 3) / 4));

@@ -60,7 +60,7 @@ __device__ const float kZeroBias[kG32Chunk] = {};
 constexpr int kG32PhiValu = 30;
 constexpr int kG32HValu = 12;
 
-template <int D, int L, bool PASS2>
+template <int D, int L, bool PASS2, bool SMX = false>
 __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   RowTile tile;
   if (!resolve_tile<kG32Rows, bf16, D>(p, tile)) return;
@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     lv[j] = -INFINITY;
     li[j] = 0x7FFFFFFF;
   }
+  ExpSum es{-INFINITY, 0.f};  // SMX: this lane's part of the softmax over all n
 
   // Chunk c -> LDS buffer dst: lane l's 16 bytes are column l32 (clean row of
   // expert 16 c + l32, or the noise row of expert 16 c + l32 - 16), K unit
@@ -426,6 +427,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SMX) es = expsum_add(es, hv);
       insert_pairs(hv, c);
     }
 
@@ -470,8 +472,9 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
 #pragma unroll
     for (int j = 0; j < L; ++j) insert_any<L>(lv, li, ov[j], oi[j]);
+    if constexpr (SMX) es = expsum_merge(es, ExpSum{__shfl_xor(es.m, 32), __shfl_xor(es.s, 32)});
     const int64_t row = tile_iorow(p, tile, wrow0 + l32);
-    if (hi == 0 && row >= 0) write_selection<L>(p, row, lv, li);
+    if (hi == 0 && row >= 0) write_selection<L>(p, row, lv, li, es);
   }
 }
 

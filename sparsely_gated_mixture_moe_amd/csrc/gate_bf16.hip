@@ -15,6 +15,9 @@ hipError_t gate_dispatch_bf16(const GateLaunch& g, const gate_detail::GateParams
     if (pass2) {                                                                           \
       if (k4) hipLaunchKernelGGL((gate32_kernel<DD, 5, true>), grid, block, 0, s, p);      \
       else hipLaunchKernelGGL((gate32_kernel<DD, 9, true>), grid, block, 0, s, p);         \
+    } else if (g.gate_order) {                                                             \
+      if (k4) hipLaunchKernelGGL((gate32_kernel<DD, 5, false, true>), grid, block, 0, s, p); \
+      else hipLaunchKernelGGL((gate32_kernel<DD, 9, false, true>), grid, block, 0, s, p);    \
     } else {                                                                               \
       if (k4) hipLaunchKernelGGL((gate32_kernel<DD, 5, false>), grid, block, 0, s, p);     \
       else hipLaunchKernelGGL((gate32_kernel<DD, 9, false>), grid, block, 0, s, p);        \

@@ -54,6 +54,9 @@ struct GateParams {
   // the outputs above; null when every workgroup sweeps all experts.
   float* cand_v;
   int32_t* cand_i;
+  // with gate_order 1 each range also writes its rows' (max, sum of exp(H -
+  // max)) pair to cand_ms [(row * gridDim.y + blockIdx.y) * 2]
+  float* cand_ms;
   // Secondary gating of a hierarchical layer ("Hierarchical MoE"); all null
   // for a flat gate. The rows are those a primary route sent to each group:
   // workgroup u covers the rows seg_off[g] + first, ... of group g, with
@@ -185,12 +188,40 @@ __device__ __forceinline__ ChunkRange chunk_range(int nch) {
   return ChunkRange{c0, min(per, nch - c0)};
 }
 
+// Softmax over all n logits (gate_order 1): each lane keeps the running
+// maximum m of the logits it has seen and s = sum of exp(H - m) over them,
+// rescaled when m grows; two such pairs combine the same way. A lane that
+// has seen only -inf keeps (m, s) = (-inf, 0).
+struct ExpSum {
+  float m, s;
+};
+__device__ __forceinline__ ExpSum expsum_merge(ExpSum a, ExpSum b) {
+  const float m = fmaxf(a.m, b.m);
+  const float ref = m == -INFINITY ? 0.f : m;
+  return ExpSum{m, a.s * expf(a.m - ref) + b.s * expf(b.m - ref)};
+}
+template <int N>
+__device__ __forceinline__ ExpSum expsum_add(ExpSum a, const float (&h)[N]) {
+  float mx = h[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) mx = fmaxf(mx, h[i]);
+  const float m = fmaxf(a.m, mx);
+  const float ref = m == -INFINITY ? 0.f : m;
+  float add = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) add += expf(h[i] - ref);
+  return ExpSum{m, fmaf(a.s, expf(a.m - ref), add)};
+}
+
 // A row's outputs from its best L (value, expert) in rank order: the first
-// k experts, the softmax of their logits, and the k-th and (k+1)-th logits;
-// or, for a split sweep, the list itself as this range's candidates.
+// k experts, the softmax of their logits (over the kept k, or with gate_order
+// 1 over all n, whose (max, sum) is `es`), and the k-th and (k+1)-th logits;
+// or, for a split sweep, the list itself (and `es`) as this range's
+// candidates.
 template <int L>
 __device__ __forceinline__ void write_selection(const GateParams& p, int64_t row,
-                                                const float (&lv)[L], const int (&li)[L]) {
+                                                const float (&lv)[L], const int (&li)[L],
+                                                ExpSum es = ExpSum{-INFINITY, 0.f}) {
   if (p.cand_v) {
     const int64_t o = (row * gridDim.y + blockIdx.y) * L;
 #pragma unroll
@@ -198,11 +229,17 @@ __device__ __forceinline__ void write_selection(const GateParams& p, int64_t row
       p.cand_v[o + j] = lv[j];
       p.cand_i[o + j] = li[j];
     }
+    if (p.cand_ms) {
+      p.cand_ms[(row * gridDim.y + blockIdx.y) * 2] = es.m;
+      p.cand_ms[(row * gridDim.y + blockIdx.y) * 2 + 1] = es.s;
+    }
     return;
   }
   const int k = p.k;
-  // softmax over the k kept logits (the rest are -inf, gate 0)
-  const float top = lv[0];
+  // softmax over the k kept logits (the rest are -inf, gate 0), or their
+  // share of the softmax over all n
+  const bool all_n = es.s > 0.f;
+  const float top = all_n ? es.m : lv[0];
   float ex[L - 1];
   float z = 0.f;
 #pragma unroll
@@ -210,7 +247,7 @@ __device__ __forceinline__ void write_selection(const GateParams& p, int64_t row
     ex[j] = (j < k) ? expf(lv[j] - top) : 0.f;
     z += ex[j];
   }
-  const float inv = 1.0f / z;
+  const float inv = 1.0f / (all_n ? es.s : z);
 #pragma unroll
   for (int j = 0; j < L - 1; ++j) {
     if (j < k) {
@@ -228,7 +265,7 @@ __device__ __forceinline__ void write_selection(const GateParams& p, int64_t row
   p.thresh[row * 2 + 1] = vk1;
 }
 
-template <typename XS, typename CT, int D, int L, bool TRAIN, bool PASS2>
+template <typename XS, typename CT, int D, int L, bool TRAIN, bool PASS2, bool SMX = false>
 __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   RowTile tile;
   if (!resolve_tile<kGateRows, CT, D>(p, tile)) return;
@@ -281,6 +318,9 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   const int64_t iorow_any = tile_iorow(p, tile, 0);
   float lv[4][L];
   int li[4][L];
+  ExpSum es[4];  // SMX: this lane's part of each row's softmax over all n
+#pragma unroll
+  for (int r = 0; r < 4; ++r) es[r] = ExpSum{-INFINITY, 0.f};
   float shared_thr[4];  // max over the row's 16 lanes of their L-th best: a lower
                         // bound of the row's L-th best logit
   float thr_k[4];
@@ -438,6 +478,15 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
         if (q == 0) red[c & 1][wave][nt * 16 + lr] = s;
       }
     } else {
+      if constexpr (SMX) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float h[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) h[nt] = hv[nt][r];
+          es[r] = expsum_add(es[r], h);
+        }
+      }
       // Rare path: candidates above both the lane's own L-th best and the
       // row's shared bound. Experts reach a lane in increasing index order.
       if (__any(cand_any)) {
@@ -508,10 +557,17 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
         for (int j = 0; j < L; ++j) insert_any<L>(lv[r], li[r], ov[j], oi[j]);
       }
     }
+    if constexpr (SMX) {
+#pragma unroll
+      for (int s = 1; s < 16; s <<= 1)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          es[r] = expsum_merge(es[r], ExpSum{__shfl_xor(es[r].m, s), __shfl_xor(es[r].s, s)});
+    }
     if (lr == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (row_ok[r]) write_selection<L>(p, iorow[r], lv[r], li[r]);
+        if (row_ok[r]) write_selection<L>(p, iorow[r], lv[r], li[r], es[r]);
     }
   }
 }
@@ -528,6 +584,13 @@ hipError_t gate_dispatch_train(const GateLaunch& g, const GateParams& p, bool pa
   const dim3 grid = gate_grid(g, kGateRows);
   if (pass2) {
     hipLaunchKernelGGL((gate_kernel<XS, CT, D, L, true, true>), grid, dim3(kThreads), 0, s, p);
+  } else if (g.gate_order) {
+    if (g.train)
+      hipLaunchKernelGGL((gate_kernel<XS, CT, D, L, true, false, true>), grid, dim3(kThreads), 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((gate_kernel<XS, CT, D, L, false, false, true>), grid, dim3(kThreads), 0,
+                         s, p);
   } else if (g.train) {
     hipLaunchKernelGGL((gate_kernel<XS, CT, D, L, true, false>), grid, dim3(kThreads), 0, s, p);
   } else {

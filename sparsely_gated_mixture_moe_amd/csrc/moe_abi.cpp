@@ -81,6 +81,8 @@ moe_status check_opts(const moe_gate_opts* o) {
     return fail(MOE_ERR_INVALID, "noise_floor must be finite and >= 0");
   if (!std::isfinite(o->w_importance) || !std::isfinite(o->w_load))
     return fail(MOE_ERR_INVALID, "loss weights must be finite");
+  if (o->gate_order != 0 && o->gate_order != 1)
+    return fail(MOE_ERR_INVALID, "gate_order must be 0 or 1");
   return MOE_OK;
 }
 
@@ -198,6 +200,7 @@ moe::GateLaunch gate_launch(const moe_dims* d, const moe_gate_opts* o, const voi
   g.w_dt = to_dt(d->gate_dtype);
   g.train = o->train;
   g.noise_floor = o->noise_floor;
+  g.gate_order = o->gate_order;
   return g;
 }
 
@@ -610,6 +613,8 @@ moe_status moe_hier_forward(const moe_hier_dims* dims, const moe_gate_opts* opts
                             void* stream) {
   moe_status s;
   if ((s = check_hier_dims(dims)) != MOE_OK || (s = check_opts(opts)) != MOE_OK) return s;
+  if (opts->gate_order != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_hier_forward: gate_order 1 applies to the flat layer");
   const int64_t B = dims->tokens;
   REQN(x, 16, B);
   REQ(w_gate1, 16);

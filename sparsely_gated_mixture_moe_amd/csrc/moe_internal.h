@@ -43,6 +43,9 @@ struct GateLaunch {
   // `ranges` consecutive ranges of chunks, one workgroup each (set by the
   // launchers from gate_ranges).
   int ranges = 1;
+  // 1: the gates are the softmax over all n logits at the selected experts
+  // (the selection is the same); 0: the softmax over the kept k.
+  int gate_order = 0;
 };
 
 // Noisy top-k gating: writes topk_idx [B,k], topk_gate [B,k], thresh [B,2].

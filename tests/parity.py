@@ -69,7 +69,8 @@ def softmax_at(H_row: np.ndarray, idx: np.ndarray) -> np.ndarray:
 
 
 def check_gating(ref: Dict[str, np.ndarray], H: np.ndarray, g_idx: np.ndarray,
-                 g_gate: np.ndarray, g_thr: np.ndarray, rows=None) -> Dict[str, object]:
+                 g_gate: np.ndarray, g_thr: np.ndarray, rows=None,
+                 gate_order: int = 0) -> Dict[str, object]:
     """Compare GPU gating on rows `rows` (default all) with the oracle's.
 
     ``ref`` holds the oracle's topk_idx/topk_gate/thresh for those rows and
@@ -101,6 +102,9 @@ def check_gating(ref: Dict[str, np.ndarray], H: np.ndarray, g_idx: np.ndarray,
         if same_set[r]:
             m = {int(e): gv for e, gv in zip(r_idx[r], r_gate[r])}
             ref_gate_by_set[r] = [m[int(e)] for e in g_idx[r]]
+        elif gate_order == 1:  # the softmax over all n at the GPU's set
+            e = np.exp(H[r] - H[r].max())
+            ref_gate_by_set[r] = e[g_idx[r]] / e.sum()
         else:
             ref_gate_by_set[r] = softmax_at(H[r], g_idx[r])
     gerr = rel_err(g_gate, ref_gate_by_set)

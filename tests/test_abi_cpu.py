@@ -41,7 +41,7 @@ def dims(**kw):
 
 
 def opts(**kw):
-    base = dict(train=1, noise_floor=0.01, w_importance=0.1, w_load=0.1)
+    base = dict(train=1, noise_floor=0.01, w_importance=0.1, w_load=0.1, gate_order=0)
     base.update(kw)
     return B.MoeGateOpts(*[base[f] for f, _ in B.MoeGateOpts._fields_])
 
@@ -92,6 +92,7 @@ def test_null_and_misaligned_pointers():
     assert call_gate(dims(), opts(train=2)) == INVALID
     assert call_gate(dims(), opts(noise_floor=-1.0)) == INVALID
     assert call_gate(dims(), opts(noise_floor=float("nan"))) == INVALID
+    assert call_gate(dims(), opts(gate_order=2)) == INVALID
 
 
 def test_workspace_checks():

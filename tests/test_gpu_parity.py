@@ -108,6 +108,66 @@ def test_gate_split_sweep(case, train):
     check_gating(ref, ref["H"], *[to_host(t) for t in split])
 
 
+SWITCH_CASES = [
+    ("flat_bf16_n4096", {"tokens": 700}, True),            # 32x32 kernel (bf16, training)
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 333, "k": 2, "d_model": 128}, False),
+    ("zipf_bf16_n256", {"tokens": 1500, "k": 1}, True),    # Switch proper: k = 1
+    ("tiny_fp32", {"tokens": 333, "n_experts": 37, "k": 3, "d_model": 128}, True),
+    ("flat_bf16_n4096", {"tokens": 5}, True),               # split sweep
+    ("flat_bf16_n4096", {"tokens": 3, "n_experts": 512}, False),
+]
+
+
+@pytest.mark.parametrize("case", SWITCH_CASES, ids=[_gate_ids(c[:2]) + f"-train{c[2]}" for c in SWITCH_CASES])
+def test_gate_switch_order(case):
+    """gate_order 1: the same selection and thresholds as the pages' order,
+    the gates from the softmax over all n logits (running max and sum of
+    exponentials over the sweep, merged across lanes and expert ranges)."""
+    name, kw, train = case
+    w = wl(name, **kw)
+    announce(f"moe_gate switch order {w.name} {kw} train={train}")
+    inp = dg.make_inputs(w, experts=False, with_bias=(name == "zipf_bf16_n256"))
+    ref = oracle.gate(inp, w.k, train=train, noise_floor=FLOOR, want_logits=True, gate_order=1)
+    g = gpu_inputs(inp)
+    act = moe.MOE_F32 if g["x"].dtype == torch.float32 else moe.MOE_BF16
+    dims = moe.make_dims(w.tokens, w.d_model, 128, w.n_experts, w.k, act, act,
+                         moe.MOE_F32 if g["w_gate"].dtype == torch.float32 else moe.MOE_BF16)
+    ws = moe.workspace(dims, moe.make_opts(train, FLOOR, gate_order=1), g["x"].device)
+    for w_s in (ws, None):
+        idx, gate, thr = moe.moe_gate(g["x"], g["w_gate"], g["w_noise"], g["eps"] if train else None,
+                                      w.k, train=train, noise_floor=FLOOR,
+                                      gate_bias=g.get("gate_bias"), gate_order=1, ws=w_s)
+        torch.cuda.synchronize()
+        check_gating(ref, ref["H"], to_host(idx), to_host(gate), to_host(thr), gate_order=1)
+        assert np.all(to_host(gate).sum(1) <= 1.0 + 1e-6)
+
+
+def test_forward_switch_order():
+    """The whole forward with gate_order 1 and k = 1 (Switch), fp32 so that y
+    is held to the fp32 bar: y against the oracle's expert outputs weighted by
+    the oracle's all-n softmax gates on the GPU's selection. (The bf16 gate
+    kernels' gate_order 1 is covered by test_gate_switch_order.)"""
+    w = wl("flat_fp32_n32", tokens=1500, k=1)
+    announce("moe_forward switch order")
+    inp = dg.make_inputs(w, with_bias=True)
+    g = gpu_inputs(inp)
+    out = moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], w.k,
+                          b1=g.get("b1"), b2=g.get("b2"), gate_bias=g.get("gate_bias"),
+                          noise_floor=FLOOR, gate_order=1, return_routing=True)
+    torch.cuda.synchronize()
+    ref = oracle.gate(inp, w.k, noise_floor=FLOOR, want_logits=True, gate_order=1)
+    idx = to_host(out["topk_idx"])
+    check_gating(ref, ref["H"], idx, to_host(out["topk_gate"]), to_host(out["thresh"]),
+                 gate_order=1)
+    same = np.all(idx == ref["topk_idx"], axis=1)
+    tok = np.repeat(np.arange(w.tokens), w.k)
+    eo = oracle.expert_pairs(inp, tok, idx.ravel()).reshape(w.tokens, w.k, w.d_model)
+    y_ref = (ref["topk_gate"][:, :, None] * eo).sum(1)
+    err = rel_err(to_host(out["y"])[same], y_ref[same])
+    print("switch forward y err", err, "rows", int(same.sum()))
+    assert err <= out_tol(False)
+
+
 @pytest.mark.parametrize("case", [("flat_bf16_n4096", {"tokens": 1000, "n_experts": 512}),
                                   ("tiny_fp32", {"tokens": 300, "n_experts": 37, "k": 3})],
                          ids=["bf16-n512", "fp32-n37"])

@@ -489,6 +489,45 @@ def test_route_handles_empty_experts():
     assert r["perm_token"].tolist() == [0, 1, 2, 0, 1, 2]
 
 
+def _exact_logits_input(h, d=64):
+    """x = e_0 and W_g row i = h_i e_0, so that clean_i = h_i exactly (fp32)."""
+    n = len(h)
+    x = np.zeros((1, d), np.float32)
+    x[0, 0] = 1.0
+    wg = np.zeros((n, d), np.float32)
+    wg[:, 0] = h
+    return {"x": x, "w_gate": wg, "w_noise": np.zeros((n, d), np.float32),
+            "eps": np.zeros((1, n), np.float32)}
+
+
+def test_switch_order_hand_example():
+    """Logits 0, ln 2, ln 3: the softmax over all three is 1/6, 2/6, 3/6. The
+    Switch order keeps the largest with gate 1/2 (k = 1) or 1/2, 1/3 (k = 2);
+    the pages' order renormalises the kept: 1 (k = 1), 3/5, 2/5 (k = 2)."""
+    h = np.array([0.0, np.log(2.0), np.log(3.0)], np.float32)
+    inp = _exact_logits_input(h)
+    for k, switch, kept in ((1, [0.5], [1.0]), (2, [1 / 2, 1 / 3], [3 / 5, 2 / 5])):
+        s = oracle.gate(inp, k, train=False, gate_order=1)
+        p = oracle.gate(inp, k, train=False, gate_order=0)
+        assert s["topk_idx"].tolist() == p["topk_idx"].tolist() == [[2, 1][:k]]
+        assert np.allclose(s["topk_gate"][0], switch, rtol=1e-6)
+        assert np.allclose(p["topk_gate"][0], kept, rtol=1e-6)
+
+
+def test_switch_order_k_equals_n_is_the_dense_softmax():
+    rng = np.random.default_rng(21)
+    inp = {"x": rng.normal(size=(40, 64)).astype(np.float32),
+           "w_gate": (rng.normal(size=(6, 64)) / 8).astype(np.float32),
+           "w_noise": (rng.normal(size=(6, 64)) / 8).astype(np.float32),
+           "eps": rng.normal(size=(40, 6)).astype(np.float32)}
+    a = oracle.gate(inp, 6, train=True, gate_order=1)
+    b = oracle.gate(inp, 6, train=True, gate_order=0)
+    assert np.array_equal(a["topk_idx"], b["topk_idx"])
+    assert np.allclose(a["topk_gate"], b["topk_gate"], rtol=1e-12)
+    c = oracle.gate(inp, 2, train=True, gate_order=1)
+    assert np.all(c["topk_gate"].sum(1) < 1.0) and np.all(c["topk_gate"] > 0)
+
+
 def test_route_capacity_hand_example():
     """Fixed expert capacity (the GShard variant named beside the layer): each
     expert serves its first C pairs in (token, slot) order. Worked by hand for
