@@ -84,19 +84,16 @@ __global__ void offsets_to_load_kernel(const int32_t* __restrict__ offsets, int 
 // CV^2 = population variance / mean^2 of importance and of load, in fp64 with a
 // fixed reduction order; losses = {CV2(imp), CV2(load), w_imp CV2(imp) + w_load CV2(load)}.
 // One workgroup of 1024 threads; thread t holds elements t, t + 1024, ... of
-// both vectors in registers (n <= 32768), sums them in that order, then
-// across the block (a butterfly within each wave, the waves in order); the
-// squared deviations are formed from the same registers.
+// both vectors in registers (n <= 32768), sums them in that order, then a tree
+// over the threads; the squared deviations are formed from the same registers.
 constexpr int kCvThreads = 1024;
 constexpr int kCvPer = 32;  // 32768 / 1024
 __global__ __launch_bounds__(kCvThreads) void cv2_losses_kernel(const float* __restrict__ imp,
                                                                 const float* __restrict__ load,
                                                                 int n, float w_imp, float w_load,
                                                                 float* __restrict__ losses) {
-  constexpr int kWaves = kCvThreads / 64;
-  __shared__ double red[2][kWaves];
+  __shared__ double red[2][kCvThreads];
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
   float xi[kCvPer], xl[kCvPer];
 #pragma unroll
   for (int j = 0; j < kCvPer; ++j) {
@@ -104,28 +101,19 @@ __global__ __launch_bounds__(kCvThreads) void cv2_losses_kernel(const float* __r
     xi[j] = i < n ? imp[i] : 0.f;
     xl[j] = i < n ? load[i] : 0.f;
   }
-  // Two sums over the block in a fixed order: a butterfly over each wave's
-  // lanes (partners add the same two values, so every lane holds the same
-  // total), then the waves' totals in wave order.
   auto tree = [&](double a, double b, double (&out)[2]) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      a += __shfl_xor(a, o);
-      b += __shfl_xor(b, o);
-    }
-    if (lane == 0) {
-      red[0][wave] = a;
-      red[1][wave] = b;
-    }
+    red[0][t] = a;
+    red[1][t] = b;
     __syncthreads();
-    double s0 = 0.0, s1 = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      s0 += red[0][w];
-      s1 += red[1][w];
+    for (int o = kCvThreads / 2; o > 0; o >>= 1) {
+      if (t < o) {
+        red[0][t] += red[0][t + o];
+        red[1][t] += red[1][t + o];
+      }
+      __syncthreads();
     }
-    out[0] = s0;
-    out[1] = s1;
+    out[0] = red[0][0];
+    out[1] = red[1][0];
     __syncthreads();
   };
   double si = 0.0, sl = 0.0;
