@@ -375,3 +375,83 @@ def hier_forward(inp: Dict[str, np.ndarray], k1: int, k2: int, train: bool = Tru
                                             "rows1", "load2", "importance", "load", "losses")])
     _check(rc, "hier_forward")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Batchwise gating ([MoE-explainer] "What the paper measured": the gate of the
+# single-pair translation models, the paper's Appendix F)
+# ---------------------------------------------------------------------------
+
+def batchwise_select(S, m: int, threshold=None):
+    """Column-wise choice of batchwise gating on a score matrix S [B, n].
+
+    Expert i takes the rows t with S[t, i] > threshold[i] (every row when
+    ``threshold`` is None), at most m of them: the m largest scores, ties to
+    the lower row. The pages' training rule is threshold None with
+    m = k B / n (each expert gets the same batch size); their inference rule
+    is a learned per-expert threshold, here with m as a cap (m = B: none).
+    Returns (counts [n] int32, keep [B, n] bool)."""
+    S = np.asarray(S, dtype=np.float64)
+    B, n = S.shape
+    thr = np.full(n, -np.inf) if threshold is None else np.asarray(threshold, np.float64)
+    keep = np.zeros((B, n), bool)
+    for i in range(n):
+        col = S[:, i]
+        cand = np.flatnonzero(col > thr[i])
+        if cand.size > m:
+            # descending score; the stable sort keeps equal scores in row order
+            order = np.argsort(-col[cand], kind="stable")
+            cand = cand[order[:m]]
+        keep[cand, i] = True
+    return keep.sum(axis=0).astype(np.int32), keep
+
+
+def batchwise_gates(S, keep) -> np.ndarray:
+    """Gates of batchwise gating: each row's softmax over its kept scores (the
+    softmax eq 3 applies to the kept logits), 0 elsewhere; a row that no
+    expert took has no gates."""
+    S = np.asarray(S, dtype=np.float64)
+    G = np.zeros(S.shape)
+    for t in range(S.shape[0]):
+        idx = np.flatnonzero(keep[t])
+        if idx.size:
+            v = S[t, idx]
+            e = np.exp(v - v.max())
+            G[t, idx] = e / e.sum()
+    return G
+
+
+def batchwise_forward(inp: Dict[str, np.ndarray], m: int, train: bool = True,
+                      noise_floor: float = 1e-2, threshold=None, decide_fp32: bool = True,
+                      keep=None) -> Dict[str, np.ndarray]:
+    """Forward pass with batchwise gating on the whole batch.
+
+    The scores are H of eq 4 (noise included when ``train``), computed by
+    ``gate``; the choice is ``batchwise_select`` on the scores rounded to fp32
+    when ``decide_fp32`` (the precision the kernels decide in); the gates use
+    the fp64 scores. y[t] = sum_i G[t, i] E_i(x[t]) (eq 1). ``keep`` [B, n]
+    replaces the choice (e.g. another valid one on a near-tie column).
+    Returns y, H, keep, counts, G, importance (= G.sum(0)), load (= counts)
+    and losses [CV^2(importance), CV^2(load)]."""
+    g = gate(inp, 1, train=train, noise_floor=noise_floor, want_logits=True)
+    H = g["H"]
+    if keep is None:
+        Sd = H.astype(np.float32).astype(np.float64) if decide_fp32 else H
+        thr = None if threshold is None else np.asarray(threshold, np.float32).astype(np.float64)
+        counts, keep = batchwise_select(Sd, m, thr)
+    else:
+        keep = np.asarray(keep, bool)
+        counts = keep.sum(axis=0).astype(np.int32)
+    G = batchwise_gates(H, keep)
+    B = H.shape[0]
+    d = np.asarray(inp["x"]).shape[1]
+    y = np.zeros((B, d))
+    tok, exp_ = np.nonzero(keep)
+    if tok.size:
+        E = expert_pairs(inp, tok, exp_.astype(np.int32))
+        for r in range(tok.size):
+            y[tok[r]] += G[tok[r], exp_[r]] * E[r]
+    imp = G.sum(axis=0)
+    load = counts.astype(np.float64)
+    return {"y": y, "H": H, "keep": keep, "counts": counts, "G": G, "importance": imp,
+            "load": load, "losses": np.array([cv_squared(imp), cv_squared(load)])}
