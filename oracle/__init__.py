@@ -455,3 +455,28 @@ def batchwise_forward(inp: Dict[str, np.ndarray], m: int, train: bool = True,
     load = counts.astype(np.float64)
     return {"y": y, "H": H, "keep": keep, "counts": counts, "G": G, "importance": imp,
             "load": load, "losses": np.array([cv_squared(imp), cv_squared(load)])}
+
+
+def _widen(a) -> np.ndarray:
+    """Storage arrays (float32, or bf16 as uint16 bit patterns) as float64."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def score_columns(inp: Dict[str, np.ndarray], experts: Sequence[int], train: bool = True,
+                  noise_floor: float = 1e-2) -> np.ndarray:
+    """H of eq 4 for every row of the batch and the listed experts only
+    ([B, len(experts)], fp64): clean = x . W_g[e] + b_e, sigma =
+    Softplus(x . W_noise[e]) + floor, H = clean + eps[:, e] * sigma (train)."""
+    e = np.asarray(experts, dtype=np.int64)
+    x = _widen(inp["x"])
+    clean = x @ _widen(inp["w_gate"])[e].T
+    if inp.get("gate_bias") is not None:
+        clean = clean + np.asarray(inp["gate_bias"], np.float64)[e]
+    if not train:
+        return clean
+    u = x @ _widen(inp["w_noise"])[e].T
+    sigma = np.maximum(u, 0.0) + np.log1p(np.exp(-np.abs(u))) + noise_floor
+    return clean + np.asarray(inp["eps"], np.float64)[:, e] * sigma

@@ -86,11 +86,14 @@ def lib():
         L.moe_hier_workspace_size.restype = ctypes.c_size_t
         L.moe_hier_forward.argtypes = ([HD, O] + [_P] * 15 + [ctypes.POINTER(MoeHierOutputs), _P, S,
                                                               _P])
+        L.moe_batchwise_workspace_size.argtypes = [D, O, ctypes.c_int32]
+        L.moe_batchwise_workspace_size.restype = ctypes.c_size_t
+        L.moe_batchwise_forward.argtypes = [D, O, ctypes.c_int32] + [_P] * 19 + [S, _P]
         L.moe_ffn_timing.argtypes = [ctypes.c_int]
         L.moe_ffn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_double)]
         for f in ("moe_gate", "moe_route", "moe_expert_ffn", "moe_combine", "moe_aux_losses",
-                  "moe_forward", "moe_hier_forward", "moe_ffn_timing",
+                  "moe_forward", "moe_hier_forward", "moe_batchwise_forward", "moe_ffn_timing",
                   "moe_ffn_timing_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -384,6 +387,81 @@ def moe_forward(x, w_gate, w_noise, eps, w1, w2, k: int, *, b1=None, b2=None, ga
     out = {"y": y, "importance": f.importance, "load": f.load, "losses": f.losses}
     out.update(extra)
     return out
+
+
+class MoeBatchwiseForward:
+    """Holds the weights, options and workspace for repeated
+    ``moe_batchwise_forward`` calls: batchwise gating, where every expert takes
+    its ``rows_per_expert`` best rows of the batch (above ``expert_threshold``
+    [n] fp32 if given). Tensors stay owned by the caller."""
+
+    def __init__(self, x_shape, w_gate, w_noise, w1, w2, rows_per_expert: int, *, b1=None,
+                 b2=None, gate_bias=None, expert_threshold=None, train: bool = True,
+                 noise_floor: float = 1e-2, w_importance: float = 0.1, w_load: float = 0.1,
+                 act_dtype=None):
+        B, d = x_shape
+        n, h, _ = w1.shape
+        self.w_gate, self.w_noise, self.w1, self.w2, self.b1, self.b2 = w_gate, w_noise, w1, w2, b1, b2
+        self.gate_bias, self.threshold = gate_bias, expert_threshold
+        _dev(w_gate, "w_gate", shape=(n, d))
+        _dev(w_noise, "w_noise", w_gate.dtype, (n, d))
+        _dev(w1, "w1")
+        _dev(w2, "w2", w1.dtype, (n, d, h))
+        _dev(b1, "b1", w1.dtype, (n, h))
+        _dev(b2, "b2", w1.dtype, (n, d))
+        _dev(gate_bias, "gate_bias", torch.float32, (n,))
+        _dev(expert_threshold, "expert_threshold", torch.float32, (n,))
+        adt = _dt(w1) if act_dtype is None else act_dtype
+        self.m = int(rows_per_expert)
+        self.dims = make_dims(B, d, h, n, 1, adt, _dt(w1), _dt(w_gate))
+        self.opts = make_opts(train, noise_floor, w_importance, w_load)
+        size = lib().moe_batchwise_workspace_size(ctypes.byref(self.dims), ctypes.byref(self.opts),
+                                                  self.m)
+        if size == 0:
+            raise MoeError(f"moe_batchwise_workspace_size: invalid shape or options "
+                           f"(B={B}, n={n}, m={self.m})")
+        dev = w1.device
+        self.ws = torch.empty(size, dtype=torch.uint8, device=dev)
+        self.counts = torch.empty(n, dtype=torch.int32, device=dev)
+        self.sel_token = torch.empty(n * self.m, dtype=torch.int32, device=dev)
+        self.sel_score = torch.empty(n * self.m, dtype=torch.float32, device=dev)
+        self.sel_gate = torch.empty(n * self.m, dtype=torch.float32, device=dev)
+        self.importance = torch.empty(n, dtype=torch.float32, device=dev)
+        self.load = torch.empty(n, dtype=torch.float32, device=dev)
+        self.losses = torch.empty(3, dtype=torch.float32, device=dev)
+
+    def __call__(self, x, eps, y=None, *, stream=None):
+        d = self.dims
+        _dev(x, "x", self.w1.dtype, (d.tokens, d.d_model))
+        _dev(eps, "eps", torch.float32, (d.tokens, d.n_experts))
+        if y is None:
+            y = torch.empty((d.tokens, d.d_model), dtype=x.dtype, device=x.device)
+        _dev(y, "y", x.dtype, (d.tokens, d.d_model))
+        st = lib().moe_batchwise_forward(
+            ctypes.byref(self.dims), ctypes.byref(self.opts), self.m, _ptr(self.threshold),
+            _ptr(x), _ptr(self.w_gate), _ptr(self.w_noise), _ptr(self.gate_bias), _ptr(eps),
+            _ptr(self.w1), _ptr(self.b1), _ptr(self.w2), _ptr(self.b2), _ptr(y),
+            _ptr(self.counts), _ptr(self.sel_token), _ptr(self.sel_score), _ptr(self.sel_gate),
+            _ptr(self.importance), _ptr(self.load), _ptr(self.losses), _ptr(self.ws),
+            self.ws.numel(), _stream(stream))
+        _check(st, "moe_batchwise_forward")
+        return y
+
+
+def moe_batchwise_forward(x, w_gate, w_noise, eps, w1, w2, rows_per_expert: int, *, b1=None,
+                          b2=None, gate_bias=None, expert_threshold=None, train: bool = True,
+                          noise_floor: float = 1e-2, w_importance: float = 0.1,
+                          w_load: float = 0.1, stream=None):
+    """One call of the batchwise-gated forward pass; returns a dict of device
+    tensors (y, counts, sel_token, sel_score, sel_gate [n * m], importance,
+    load, losses)."""
+    f = MoeBatchwiseForward(tuple(x.shape), w_gate, w_noise, w1, w2, rows_per_expert, b1=b1, b2=b2,
+                            gate_bias=gate_bias, expert_threshold=expert_threshold, train=train,
+                            noise_floor=noise_floor, w_importance=w_importance, w_load=w_load)
+    y = f(x, eps, stream=stream)
+    return {"y": y, "counts": f.counts, "sel_token": f.sel_token, "sel_score": f.sel_score,
+            "sel_gate": f.sel_gate, "importance": f.importance, "load": f.load,
+            "losses": f.losses}
 
 
 class MoeHierForward:

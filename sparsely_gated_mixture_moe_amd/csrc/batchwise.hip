@@ -1,0 +1,533 @@
+// Batchwise gating (section "What the paper measured" of the MoE explainer:
+// the gate of the single-pair translation models, the paper's Appendix F).
+// Instead of every token choosing its k best experts, every expert chooses
+// rows of the batch: in training the m rows with the largest score H (m =
+// k B / n gives every expert the same batch size); at inference the rows whose
+// score exceeds the expert's threshold, here at most m of them (the largest).
+// A token's gates are the softmax of the scores of the experts that took it
+// (the softmax that eq 3 applies to the kept logits); y is eq 1.
+//
+//   1. scores     H of every (token, expert), written expert-major by the gate
+//                 kernels (launch_scores): scores[e][t].
+//   2. select     one workgroup per expert. Its B scores stay in registers as
+//                 order-preserving integer keys (up to 64 per thread). The
+//                 m-th largest key is found from a lower bound (the m-th
+//                 largest of the threads' maxima, by a 2-bit-per-step search)
+//                 and the few keys at or above it, ranked in LDS; then the
+//                 chosen rows are compacted in token order (one scan over the
+//                 (tile, wave) cells), ties to the lower token. Expert e's rows
+//                 go to slots [e m, e m + count_e).
+//   3. token lists  each token's slots: integer-atomic counts, a prefix sum,
+//                 an atomic fill, then each list put in slot order by ranks
+//                 (slot order is expert order, so every later sum over a
+//                 token's experts has a fixed order).
+//   4. expert FFNs  the grouped FFN kernel over the fixed-stride segments.
+//   5. gates + combine  one wave per token: the softmax of its scores, then
+//                 y = sum of gate * expert output, both in slot order.
+//   6. importance per expert, the sum of its rows' gates in slot order; the
+//                 load is the count (no noise estimate: the counts are fixed).
+#include <climits>
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kCandCap = 2048;  // keys at or above the lower bound kept in LDS
+
+// Order-preserving map of floats to unsigned keys (-0 is read as +0, so that
+// equal numbers get equal keys); key_value is its inverse.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = __float_as_uint(v == 0.f ? 0.f : v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Workgroup-wide sums of up to three per-thread integers (sum) or flags
+// (count). The LDS array is used by parity, so one barrier per call
+// suffices: a wave writes slot p again only after every wave has passed the
+// next call's barrier, i.e. has read slot p.
+struct BlockSum {
+  int (*red)[3][kSelWaves];
+  int parity = 0;
+  template <int N>
+  __device__ __forceinline__ void finish(int (&v)[N]) {
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) red[parity][i][wave] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int t = 0;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) t += red[parity][i][w];
+      v[i] = t;
+    }
+    parity ^= 1;
+  }
+  template <int N>
+  __device__ __forceinline__ void sum(int (&v)[N]) {
+    static_assert(N <= 3, "three sums per call");
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = wave_sum_i(v[i]);
+    finish(v);
+  }
+  template <int N>
+  __device__ __forceinline__ void count(const bool (&f)[N], int (&v)[N]) {
+    static_assert(N <= 3, "three counts per call");
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = (int)__popcll(__ballot(f[i]));
+    finish(v);
+  }
+};
+
+// One workgroup per expert e: chooses its rows among scores[e][0 .. B) and
+// writes them in token order to sel_token / sel_score [e m ...], their number
+// to counts[e]. B <= 64 * 1024. Row r = j * 1024 + tid is read by thread tid
+// (tile j); the column is read once from HBM, the later passes mostly hit
+// the caches.
+__global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
+    const float* __restrict__ scores, int B, int m, const float* __restrict__ thr,
+    int32_t* __restrict__ counts, int32_t* __restrict__ sel_token, float* __restrict__ sel_score) {
+  constexpr int kMaxTiles = 64;
+  __shared__ int red[2][3][kSelWaves];
+  __shared__ uint32_t cand_k[kCandCap];
+  __shared__ int32_t cand_r[kCandCap];
+  __shared__ uint8_t cand_sel[kCandCap];
+  __shared__ int cell_g[kMaxTiles * kSelWaves], cell_e[kMaxTiles * kSelWaves];
+  __shared__ int wtot[2][kSelWaves];
+  __shared__ int ncand;
+  __shared__ uint32_t tsh;
+  BlockSum bs{red};
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int tiles = (B + kSelThreads - 1) / kSelThreads;
+  const float* col = scores + (int64_t)e * B;
+  auto key_at = [&](int j) {
+    const int r = j * kSelThreads + tid;
+    return r < B ? order_key(col[r]) : 0u;  // 0: below every score's key
+  };
+  const float tv = thr ? thr[e] : -INFINITY;
+  // a NaN threshold passes nothing (no number exceeds it)
+  const uint32_t tkey = tv != tv ? 0xFFFFFFFFu : order_key(tv);
+  const int64_t base = (int64_t)e * m;
+
+  uint32_t mx = 0;
+  int above = 0;
+  for (int j = 0; j < tiles; ++j) {
+    const uint32_t k = key_at(j);
+    above += k > tkey;
+    mx = max(mx, k);
+  }
+  int cv[1] = {above};
+  bs.sum(cv);
+  const int c = cv[0];  // rows above the threshold
+  if (tid == 0) counts[e] = c < m ? c : m;
+
+  // Rows with key > t are taken, and of those with key == t the first need_eq
+  // in token order. With at most m rows above the threshold: all of them.
+  // Compaction over every row: each (tile, wave) cell's counts of rows above
+  // t and of tied rows, an exclusive scan over the cells, then every taken
+  // row's slot.
+  auto compact_rows = [&](uint32_t t, int need_eq) {
+    for (int j = 0; j < tiles; ++j) {
+      const uint32_t k = key_at(j);
+      const uint64_t bg = __ballot(k > t);
+      const uint64_t be = __ballot(need_eq > 0 && k == t);
+      if (lane == 0) {
+        cell_g[j * kSelWaves + wave] = (int)__popcll(bg);
+        cell_e[j * kSelWaves + wave] = (int)__popcll(be);
+      }
+    }
+    __syncthreads();
+    {
+      const int nc = tiles * kSelWaves;
+      int vg = tid < nc ? cell_g[tid] : 0;
+      int ve = tid < nc ? cell_e[tid] : 0;
+      const int og = vg, oe = ve;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int ug = __shfl_up(vg, o), ue = __shfl_up(ve, o);
+        if (lane >= o) {
+          vg += ug;
+          ve += ue;
+        }
+      }
+      if (lane == 63) {
+        wtot[0][wave] = vg;
+        wtot[1][wave] = ve;
+      }
+      __syncthreads();
+      for (int w = 0; w < wave; ++w) {
+        vg += wtot[0][w];
+        ve += wtot[1][w];
+      }
+      if (tid < nc) {
+        cell_g[tid] = vg - og;
+        cell_e[tid] = ve - oe;
+      }
+    }
+    __syncthreads();
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    for (int j = 0; j < tiles; ++j) {
+      const uint32_t k = key_at(j);
+      const bool gt = k > t;
+      const bool eq = need_eq > 0 && k == t;
+      const uint64_t bg = __ballot(gt);
+      const uint64_t be = __ballot(eq);
+      const int gb = cell_g[j * kSelWaves + wave] + (int)__popcll(bg & below);
+      const int eb = cell_e[j * kSelWaves + wave] + (int)__popcll(be & below);
+      const int pos = gb + min(eb, need_eq);
+      if ((gt || (eq && eb < need_eq)) && pos < m) {
+        sel_token[base + pos] = j * kSelThreads + tid;
+        sel_score[base + pos] = key_value(k);
+      }
+    }
+  };
+
+  if (c <= m) {
+    compact_rows(tkey, 0);
+    return;
+  }
+  if (m <= kSelThreads) {
+    // lower bound lb <= t: the m-th largest of the threads' maxima (m
+    // distinct keys are >= it), two bits per step
+    uint32_t lb = 0;
+    for (int b = 30; b >= 0; b -= 2) {
+      const bool f[3] = {mx >= (lb | (1u << b)), mx >= (lb | (2u << b)), mx >= (lb | (3u << b))};
+      int v[3];
+      bs.count(f, v);
+      if (v[2] >= m) lb |= 3u << b;
+      else if (v[1] >= m) lb |= 2u << b;
+      else if (v[0] >= m) lb |= 1u << b;
+    }
+    // the rows with keys >= lb (at least m of them, and every row with a key
+    // >= t) to LDS, in any order
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    for (int j = 0; j < tiles; ++j) {
+      const uint32_t k = key_at(j);
+      if (k >= lb) {
+        const int at = atomicAdd(&ncand, 1);
+        if (at < kCandCap) {
+          cand_k[at] = k;
+          cand_r[at] = j * kSelThreads + tid;
+        }
+      }
+    }
+    __syncthreads();
+    const int nc = ncand;
+    if (nc <= kCandCap) {
+      // t: the candidate with fewer than m candidates above it and at least m
+      // at or above it (all such candidates hold the same key)
+      for (int q = tid; q < nc; q += kSelThreads) {
+        const uint32_t v = cand_k[q];
+        int gt = 0, ge = 0;
+        for (int r = 0; r < nc; ++r) {
+          const uint32_t w = cand_k[r];
+          gt += w > v;
+          ge += w >= v;
+        }
+        if (gt < m && ge >= m) tsh = v;
+      }
+      __syncthreads();
+      const uint32_t t = tsh;
+      int gtc[1] = {0};
+      for (int q = tid; q < nc; q += kSelThreads) gtc[0] += cand_k[q] > t;
+      bs.sum(gtc);
+      const int need_eq = m - gtc[0];
+      // taken: above t, or tied and among the first need_eq tied rows
+      for (int q = tid; q < nc; q += kSelThreads) {
+        const uint32_t v = cand_k[q];
+        bool sel = v > t;
+        if (v == t) {
+          const int r = cand_r[q];
+          int er = 0;
+          for (int p = 0; p < nc; ++p) er += cand_k[p] == t && cand_r[p] < r;
+          sel = er < need_eq;
+        }
+        cand_sel[q] = sel;
+      }
+      __syncthreads();
+      // slot: the taken candidates on lower rows
+      for (int q = tid; q < nc; q += kSelThreads) {
+        if (!cand_sel[q]) continue;
+        const int r = cand_r[q];
+        int pos = 0;
+        for (int p = 0; p < nc; ++p) pos += cand_sel[p] && cand_r[p] < r;
+        if (pos < m) {
+          sel_token[base + pos] = r;
+          sel_score[base + pos] = key_value(cand_k[q]);
+        }
+      }
+      return;
+    }
+  }
+  // general case: a bitwise search for the largest t with at least m keys >= t
+  uint32_t t = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cb = t | (1u << b);
+    int cnt[1] = {0};
+    for (int j = 0; j < tiles; ++j) cnt[0] += key_at(j) >= cb;
+    bs.sum(cnt);
+    if (cnt[0] >= m) t = cb;
+  }
+  int gt[1] = {0};
+  for (int j = 0; j < tiles; ++j) gt[0] += key_at(j) > t;
+  bs.sum(gt);
+  compact_rows(t, m - gt[0]);
+}
+
+__global__ void batch_zero_kernel(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// Rows each token was taken for (integer atomics: the counts do not depend on
+// the order of the additions).
+__global__ void batch_tok_count_kernel(const int32_t* __restrict__ counts,
+                                       const int32_t* __restrict__ sel_token, int64_t slots, int m,
+                                       int B, int32_t* __restrict__ tok_cnt) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= slots) return;
+  const int e = (int)(q / m);
+  if (q - (int64_t)e * m >= counts[e]) return;
+  const int tok = sel_token[q];
+  if (tok >= 0 && tok < B) atomicAdd(&tok_cnt[tok], 1);
+}
+
+// Each taken slot into its token's list (in any order; counted down from the
+// token's count, which ends at 0).
+__global__ void batch_tok_fill_kernel(const int32_t* __restrict__ counts,
+                                      const int32_t* __restrict__ sel_token, int64_t slots, int m,
+                                      int B,
+                                      const int32_t* __restrict__ tok_off,
+                                      int32_t* __restrict__ tok_cnt,
+                                      int32_t* __restrict__ tok_list) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= slots) return;
+  const int e = (int)(q / m);
+  if (q - (int64_t)e * m >= counts[e]) return;
+  const int tok = sel_token[q];
+  if (tok < 0 || tok >= B) return;
+  const int pos = atomicSub(&tok_cnt[tok], 1) - 1;
+  if (pos >= 0) tok_list[tok_off[tok] + pos] = (int32_t)q;
+}
+
+// One wave per token: its list in slot order (ranks; the slots are distinct).
+__global__ __launch_bounds__(256) void batch_tok_sort_kernel(const int32_t* __restrict__ tok_off,
+                                                             const int32_t* __restrict__ tok_list,
+                                                             int B, int32_t* __restrict__ tok_sorted) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= B) return;
+  const int o = tok_off[tok];
+  const int c = tok_off[tok + 1] - o;
+  for (int a0 = 0; a0 < c; a0 += 64) {
+    const int a = a0 + lane;
+    const int va = a < c ? tok_list[o + a] : INT_MAX;
+    int rank = 0;
+    for (int b0 = 0; b0 < c; b0 += 64) {
+      const int vb = b0 + lane < c ? tok_list[o + b0 + lane] : INT_MAX;
+      const int nb = min(64, c - b0);
+      for (int s = 0; s < nb; ++s) rank += __shfl(vb, s) < va;
+    }
+    if (a < c) tok_sorted[o + rank] = va;
+  }
+}
+
+// One wave per token: its gates (softmax of its scores, slot order) to
+// sel_gate, and y[tok] = sum over its slots, in slot order, of gate * expert
+// output (fp32 accumulation), one 16-byte unit of the row per lane and step.
+template <typename T>
+__global__ __launch_bounds__(256) void batch_combine_kernel(
+    const T* __restrict__ eo, const int32_t* __restrict__ tok_off,
+    const int32_t* __restrict__ tok_sorted, const float* __restrict__ sel_score,
+    float* __restrict__ sel_gate, int B, int d, T* __restrict__ y) {
+  constexpr int UE = Elem<T>::kPerUnit;
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= B) return;
+  const int o = tok_off[tok];
+  const int c = tok_off[tok + 1] - o;
+  float mx = -INFINITY;
+  for (int a = lane; a < c; a += 64) mx = fmaxf(mx, sel_score[tok_sorted[o + a]]);
+  mx = wave_max_f(mx);
+  float den = 0.f;
+  for (int a = lane; a < c; a += 64) den += expf(sel_score[tok_sorted[o + a]] - mx);
+  den = wave_sum_f(den);
+  for (int a = lane; a < c; a += 64) {
+    const int q = tok_sorted[o + a];
+    sel_gate[q] = expf(sel_score[q] - mx) / den;
+  }
+  const int units = d / UE;
+  for (int u = lane; u < units; u += 64) {
+    float acc[UE];
+#pragma unroll
+    for (int i = 0; i < UE; ++i) acc[i] = 0.f;
+    // slots in groups of four: positions, gates and rows requested first,
+    // then added in slot order
+    for (int a0 = 0; a0 < c; a0 += 4) {
+      int q[4];
+      float g[4];
+      U16 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = a0 + i < c ? tok_sorted[o + a0 + i] : -1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        g[i] = q[i] >= 0 ? expf(sel_score[q[i]] - mx) / den : 0.f;
+        v[i] = q[i] >= 0 ? ld_unit(eo + (int64_t)q[i] * d + u * UE) : zero_unit();
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (q[i] < 0) continue;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            acc[2 * w] += g[i] * __uint_as_float(v[i].w[w] << 16);
+            acc[2 * w + 1] += g[i] * __uint_as_float(v[i].w[w] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[w] += g[i] * __uint_as_float(v[i].w[w]);
+        }
+      }
+    }
+    U16 out;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        out.w[w] = f32_to_bf16_bits(acc[2 * w]) | (f32_to_bf16_bits(acc[2 * w + 1]) << 16);
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) out.w[w] = __float_as_uint(acc[w]);
+    }
+    st_unit(y + (int64_t)tok * d + u * UE, out);
+  }
+}
+
+// One wave per expert: Importance (eq 6) = the sum of its rows' gates,
+// lane-strided in slot order, then a fixed butterfly.
+__global__ __launch_bounds__(256) void batch_importance_kernel(const int32_t* __restrict__ counts,
+                                                               const float* __restrict__ sel_gate,
+                                                               int n, int m,
+                                                               float* __restrict__ importance) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= n) return;
+  const int c = counts[e];
+  const float* g = sel_gate + (int64_t)e * m;
+  float s = 0.f;
+  for (int r = lane; r < c; r += 64) s += g[r];
+  s = wave_sum_f(s);
+  if (lane == 0) importance[e] = s;
+}
+
+}  // namespace
+
+size_t batchwise_ws_bytes(int64_t tokens, int n, int m, int d, int h, Dt act_dt) {
+  const int64_t slots = (int64_t)n * m;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  return al((size_t)tokens * n * sizeof(float)) +          // scores
+         al((size_t)tokens * sizeof(int32_t)) +            // tok_cnt
+         al((size_t)(tokens + 1) * sizeof(int32_t)) +      // tok_off
+         2 * al((size_t)slots * sizeof(int32_t)) +         // tok_list, tok_sorted
+         al(ffn_plan_bytes(slots, n, d, h, act_dt)) +      // FFN work units
+         al((size_t)slots * d * (act_dt == kBF16 ? 2 : 4)); // expert outputs
+}
+
+void batchwise_carve(BatchwiseLaunch& b, void* ws, int d, int h, Dt act_dt) {
+  const int64_t B = b.gate.tokens;
+  const int n = b.gate.n;
+  const int64_t slots = (int64_t)n * b.m;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  char* p = static_cast<char*>(ws);
+  b.scores = reinterpret_cast<float*>(p);
+  p += al((size_t)B * n * sizeof(float));
+  b.tok_cnt = reinterpret_cast<int32_t*>(p);
+  p += al((size_t)B * sizeof(int32_t));
+  b.tok_off = reinterpret_cast<int32_t*>(p);
+  p += al((size_t)(B + 1) * sizeof(int32_t));
+  b.tok_list = reinterpret_cast<int32_t*>(p);
+  p += al((size_t)slots * sizeof(int32_t));
+  b.tok_sorted = reinterpret_cast<int32_t*>(p);
+  p += al((size_t)slots * sizeof(int32_t));
+  b.ffn_blocks = reinterpret_cast<int32_t*>(p);
+  p += al(ffn_plan_bytes(slots, n, d, h, act_dt));
+  b.expert_out = p;
+}
+
+hipError_t launch_batchwise(const BatchwiseLaunch& b, hipStream_t s, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+  const int64_t B = b.gate.tokens;
+  const int n = b.gate.n;
+  const int m = b.m;
+  const int64_t slots = (int64_t)n * m;
+  if (B > 65536 || m < 1 || slots >= INT_MAX) return hipErrorInvalidValue;
+  hipError_t e = launch_scores(b.gate, b.scores, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(batch_select_kernel, dim3((unsigned)n), dim3(kSelThreads), 0, s, b.scores,
+                     (int)B, m, b.threshold, b.counts, b.sel_token, b.sel_score);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned slot_blocks = (unsigned)((slots + 255) / 256);
+  if (B > 0) {
+    hipLaunchKernelGGL(batch_zero_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s,
+                       b.tok_cnt, (int)B);
+    hipLaunchKernelGGL(batch_tok_count_kernel, dim3(slot_blocks), dim3(256), 0, s, b.counts,
+                       b.sel_token, slots, m, (int)B, b.tok_cnt);
+  }
+  if ((e = launch_scan_counts(b.tok_cnt, (int)B, b.tok_off, s)) != hipSuccess) return e;
+  if (B > 0) {
+    hipLaunchKernelGGL(batch_tok_fill_kernel, dim3(slot_blocks), dim3(256), 0, s, b.counts,
+                       b.sel_token, slots, m, (int)B, b.tok_off, b.tok_cnt, b.tok_list);
+    hipLaunchKernelGGL(batch_tok_sort_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, s,
+                       b.tok_off, b.tok_list, (int)B, b.tok_sorted);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = launch_ffn(slots, 1, b.gate.d, b.h, n, b.act_dt, b.gate.x, nullptr, b.sel_token, b.w1, b.b1,
+                 b.w2, b.b2, b.expert_out, b.ffn_blocks, s, ev0, ev1, 0, b.counts, m);
+  if (e != hipSuccess) return e;
+  if (B > 0) {
+    const dim3 grid((unsigned)((B + 3) / 4));
+    if (b.act_dt == kBF16)
+      hipLaunchKernelGGL(batch_combine_kernel<bf16>, grid, dim3(256), 0, s,
+                         reinterpret_cast<const bf16*>(b.expert_out), b.tok_off, b.tok_sorted,
+                         b.sel_score, b.sel_gate, (int)B, b.gate.d, reinterpret_cast<bf16*>(b.y));
+    else
+      hipLaunchKernelGGL(batch_combine_kernel<float>, grid, dim3(256), 0, s,
+                         reinterpret_cast<const float*>(b.expert_out), b.tok_off, b.tok_sorted,
+                         b.sel_score, b.sel_gate, (int)B, b.gate.d, reinterpret_cast<float*>(b.y));
+  }
+  hipLaunchKernelGGL(batch_importance_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s,
+                     b.counts, b.sel_gate, n, m, b.importance);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_counts_to_load(b.counts, n, b.load, s)) != hipSuccess) return e;
+  return launch_cv2_losses(b.importance, b.load, n, b.w_importance, b.w_load, b.losses, s);
+}
+
+}  // namespace moe

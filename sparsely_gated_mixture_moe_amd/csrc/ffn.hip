@@ -499,14 +499,20 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
 // Lists the work units: expert e gets ceil(count_e / BM) units, each written
 // as (expert, first pair of its rows, rows) after the count. One workgroup;
 // thread t owns a contiguous span of experts.
+// Segments: expert e's rows start at offsets[e] and number offsets[e + 1] -
+// offsets[e]; or, with seg_counts, start at e * seg_stride and number
+// seg_counts[e] (fixed-stride segments with gaps, as batchwise gating lays
+// them out).
 __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ offsets, int n, int bm,
                                                  int hsplit, int nch, int capacity,
-                                                 int32_t* __restrict__ blocks) {
+                                                 const int32_t* __restrict__ seg_counts,
+                                                 int seg_stride, int32_t* __restrict__ blocks) {
   // rows of expert e that are served: all, or the first `capacity`
   auto served = [&](int e) {
-    const int c = offsets[e + 1] - offsets[e];
+    const int c = seg_counts ? seg_counts[e] : offsets[e + 1] - offsets[e];
     return capacity > 0 ? min(c, capacity) : c;
   };
+  auto seg_start = [&](int e) { return seg_counts ? e * seg_stride : offsets[e]; };
   __shared__ int part[1024];
   const int t = threadIdx.x;
   const int per = (n + 1023) / 1024;
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ off
   int pos = part[t] - s;
   FfnUnit* units = reinterpret_cast<FfnUnit*>(blocks + 4);
   for (int e = e0; e < e1; ++e) {
-    const int seg = offsets[e];
+    const int seg = seg_start(e);
     const int cnt = served(e);
     for (int r = 0; r < cnt; r += bm) {
       for (int q = 0; q < hsplit; ++q) {
@@ -592,11 +598,12 @@ hipError_t device_cus(int* cus) {
 
 template <typename T, int D>
 hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* offsets, int n,
-                        int hsplit, int capacity, hipStream_t s, hipEvent_t ev0,
-                        hipEvent_t ev1) {
+                        int hsplit, int capacity, const int32_t* seg_counts, int seg_stride,
+                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   using S = FfnShape<T, D>;
   hipLaunchKernelGGL(ffn_plan, dim3(1), dim3(1024), 0, s, offsets, n, S::BM, hsplit,
-                     p.h / S::HC, capacity, const_cast<int32_t*>(p.blocks));
+                     p.h / S::HC, capacity, seg_counts, seg_stride,
+                     const_cast<int32_t*>(p.blocks));
   max_blocks *= hsplit;
   if (max_blocks <= 0) {  // no rows: an empty timed interval
     hipError_t er = hipGetLastError();
@@ -689,7 +696,7 @@ hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const v
                       const int32_t* offsets, const int32_t* perm_token, const void* w1,
                       const void* b1, const void* w2, const void* b2, void* expert_out,
                       int32_t* blocks, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
-                      int capacity) {
+                      int capacity, const int32_t* seg_counts, int seg_stride) {
   const int64_t mb = ffn_max_blocks(tokens * k, n, d, dt);
   const int hs = ffn_hsplit(tokens * k, n, d, h, dt);
   FfnParams p{x, offsets, perm_token, w1, b1, w2, b2, expert_out, blocks, h, nullptr, 0};
@@ -700,17 +707,17 @@ hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const v
   }
   if (dt == kBF16) {
     switch (d) {
-      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
-      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
-      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
-      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
+      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
+      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
+      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
+      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
     }
   } else {
     switch (d) {
-      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
-      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
-      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
-      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, hs, capacity, s, ev0, ev1);
+      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
+      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
+      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
+      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
     }
   }
   return hipErrorInvalidValue;

@@ -394,6 +394,15 @@ hipError_t launch_gate(const GateLaunch& g0, int32_t* topk_idx, float* topk_gate
   return hipGetLastError();
 }
 
+hipError_t launch_scores(const GateLaunch& g0, float* scores, hipStream_t s) {
+  if (g0.tokens == 0) return hipSuccess;
+  GateLaunch g = g0;
+  g.ranges = gate_ranges(g);  // each range writes its own experts' rows: no merge
+  GateParams p = make_params(g);
+  p.scores = scores;
+  return gate_dispatch(g, p, false, s);
+}
+
 int gate_tile_rows(const GateLaunch& g) { return gate_uses_g32(g) ? kGate32Rows : kGateRows; }
 
 int64_t gate_max_units(int64_t rows, int groups, int tile_rows) {

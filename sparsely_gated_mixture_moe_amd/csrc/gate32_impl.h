@@ -60,7 +60,7 @@ __device__ const float kZeroBias[kG32Chunk] = {};
 constexpr int kG32PhiValu = 30;
 constexpr int kG32HValu = 12;
 
-template <int D, int L, bool PASS2, bool SMX = false>
+template <int D, int L, bool PASS2, bool SMX = false, bool SCORES = false>
 __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   RowTile tile;
   if (!resolve_tile<kG32Rows, bf16, D>(p, tile)) return;
@@ -127,6 +127,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     li[j] = 0x7FFFFFFF;
   }
   ExpSum es{-INFINITY, 0.f};  // SMX: this lane's part of the softmax over all n
+  // SCORES: the batch row of this lane's token (-1 past the tile's end)
+  const int64_t srow = SCORES ? tile_iorow(p, tile, wrow0 + l32) : -1;
 
   // Chunk c -> LDS buffer dst: lane l's 16 bytes are column l32 (clean row of
   // expert 16 c + l32, or the noise row of expert 16 c + l32 - 16), K unit
@@ -427,8 +429,18 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (SMX) es = expsum_add(es, hv);
-      insert_pairs(hv, c);
+      if constexpr (SCORES) {
+        // batchwise gating: the 8 scores to their experts' rows; the 32 lanes
+        // of each half write 128 contiguous bytes per expert
+        if (srow >= 0) {
+          float* dst = p.scores + (int64_t)((cr.c0 + c) * EC + 4 * hi) * p.B + srow;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dst[(int64_t)(8 * (i / 4) + (i % 4)) * p.B] = hv[i];
+        }
+      } else {
+        if constexpr (SMX) es = expsum_add(es, hv);
+        insert_pairs(hv, c);
+      }
     }
 
     // Block barrier without a release fence (which would wait for every copy
@@ -460,7 +472,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     chunk_pass(c, IntConst<0>{});
     if (c + 1 < nchunks) chunk_pass(c + 1, IntConst<1>{});
   }
-  if constexpr (!PASS2) {
+  if constexpr (!PASS2 && !SCORES) {
     // The two halves of a token's experts (lanes l and l ^ 32) merge, then
     // lanes 0-31 write.
     float ov[L];

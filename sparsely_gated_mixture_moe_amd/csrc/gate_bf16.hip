@@ -12,7 +12,9 @@ hipError_t gate_dispatch_bf16(const GateLaunch& g, const gate_detail::GateParams
     const bool k4 = g.k <= 4;
 #define MOE_G32(DD)                                                                        \
   if (g.d == DD) {                                                                         \
-    if (pass2) {                                                                           \
+    if (p.scores) {                                                                        \
+      hipLaunchKernelGGL((gate32_kernel<DD, 5, false, false, true>), grid, block, 0, s, p);  \
+    } else if (pass2) {                                                                    \
       if (k4) hipLaunchKernelGGL((gate32_kernel<DD, 5, true>), grid, block, 0, s, p);      \
       else hipLaunchKernelGGL((gate32_kernel<DD, 9, true>), grid, block, 0, s, p);         \
     } else if (g.gate_order) {                                                             \

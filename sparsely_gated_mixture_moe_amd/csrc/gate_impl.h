@@ -57,6 +57,9 @@ struct GateParams {
   // with gate_order 1 each range also writes its rows' (max, sum of exp(H -
   // max)) pair to cand_ms [(row * gridDim.y + blockIdx.y) * 2]
   float* cand_ms;
+  // Batchwise gating: every H goes to scores[e * B + row] (expert-major, one
+  // row of B per expert) instead of a selection; null otherwise.
+  float* scores;
   // Secondary gating of a hierarchical layer ("Hierarchical MoE"); all null
   // for a flat gate. The rows are those a primary route sent to each group:
   // workgroup u covers the rows seg_off[g] + first, ... of group g, with
@@ -265,7 +268,8 @@ __device__ __forceinline__ void write_selection(const GateParams& p, int64_t row
   p.thresh[row * 2 + 1] = vk1;
 }
 
-template <typename XS, typename CT, int D, int L, bool TRAIN, bool PASS2, bool SMX = false>
+template <typename XS, typename CT, int D, int L, bool TRAIN, bool PASS2, bool SMX = false,
+          bool SCORES = false>
 __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   RowTile tile;
   if (!resolve_tile<kGateRows, CT, D>(p, tile)) return;
@@ -477,6 +481,14 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
         s += __shfl_xor(s, 32);
         if (q == 0) red[c & 1][wave][nt * 16 + lr] = s;
       }
+    } else if constexpr (SCORES) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int e = cbase + c * EC + nt * 16 + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (e < n && row_ok[r]) p.scores[(int64_t)e * p.B + iorow[r]] = hv[nt][r];
+      }
     } else {
       if constexpr (SMX) {
 #pragma unroll
@@ -540,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
     }
   }
 
-  if constexpr (!PASS2) {
+  if constexpr (!PASS2 && !SCORES) {
     // Merge the 16 lanes that share each row.
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1) {
@@ -582,7 +594,14 @@ inline dim3 gate_grid(const GateLaunch& g, int rows) {
 template <typename XS, typename CT, int D, int L>
 hipError_t gate_dispatch_train(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
   const dim3 grid = gate_grid(g, kGateRows);
-  if (pass2) {
+  if (p.scores) {
+    if (g.train)
+      hipLaunchKernelGGL((gate_kernel<XS, CT, D, 5, true, false, false, true>), grid,
+                         dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((gate_kernel<XS, CT, D, 5, false, false, false, true>), grid,
+                         dim3(kThreads), 0, s, p);
+  } else if (pass2) {
     hipLaunchKernelGGL((gate_kernel<XS, CT, D, L, true, true>), grid, dim3(kThreads), 0, s, p);
   } else if (g.gate_order) {
     if (g.train)
@@ -601,7 +620,7 @@ hipError_t gate_dispatch_train(const GateLaunch& g, const GateParams& p, bool pa
 
 template <typename XS, typename CT, int D>
 hipError_t gate_dispatch_l(const GateLaunch& g, const GateParams& p, bool pass2, hipStream_t s) {
-  if (g.k <= 4) return gate_dispatch_train<XS, CT, D, 5>(g, p, pass2, s);
+  if (g.k <= 4 || p.scores) return gate_dispatch_train<XS, CT, D, 5>(g, p, pass2, s);
   return gate_dispatch_train<XS, CT, D, 9>(g, p, pass2, s);
 }
 

@@ -598,6 +598,90 @@ moe_status moe_forward(const moe_dims* dims, const moe_gate_opts* opts, const vo
   return device_status(e, "moe_forward (losses)");
 }
 
+namespace {
+
+moe_status check_batchwise(const moe_dims* d, const moe_gate_opts* o, int32_t m) {
+  moe_status s;
+  if ((s = check_dims(d)) != MOE_OK || (s = check_opts(o)) != MOE_OK) return s;
+  if (d->capacity != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "batchwise gating: capacity must be 0 (m bounds each expert)");
+  if (o->gate_order != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "batchwise gating: gate_order must be 0");
+  if (d->tokens > 65536)
+    return fail(MOE_ERR_UNSUPPORTED, "batchwise gating: tokens = %lld > 65536",
+                (long long)d->tokens);
+  if (m < 1) return fail(MOE_ERR_INVALID, "rows_per_expert = %d < 1", m);
+  if ((int64_t)m * d->n_experts > (int64_t)0x7FFFFFFE)
+    return fail(MOE_ERR_INVALID, "n_experts * rows_per_expert does not fit int32 indices");
+  if (!moe::ffn_supported(d->d_model, d->d_hidden, to_dt(d->act_dtype)))
+    return fail(MOE_ERR_UNSUPPORTED, "expert_ffn: unsupported shape");
+  return MOE_OK;
+}
+
+}  // namespace
+
+size_t moe_batchwise_workspace_size(const moe_dims* dims, const moe_gate_opts* opts,
+                                    int32_t rows_per_expert) {
+  if (check_batchwise(dims, opts, rows_per_expert) != MOE_OK) return 0;
+  return moe::batchwise_ws_bytes(dims->tokens, dims->n_experts, rows_per_expert, dims->d_model,
+                                 dims->d_hidden, to_dt(dims->act_dtype));
+}
+
+moe_status moe_batchwise_forward(const moe_dims* dims, const moe_gate_opts* opts,
+                                 int32_t rows_per_expert, const float* expert_threshold,
+                                 const void* x, const void* w_gate, const void* w_noise,
+                                 const float* gate_bias, const float* eps, const void* w1,
+                                 const void* b1, const void* w2, const void* b2, void* y,
+                                 int32_t* counts, int32_t* sel_token, float* sel_score,
+                                 float* sel_gate, float* importance, float* load, float* losses,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  moe_status s;
+  if ((s = check_batchwise(dims, opts, rows_per_expert)) != MOE_OK) return s;
+  if ((s = check_gate_args(dims, opts, x, w_gate, w_noise, gate_bias, eps, true)) != MOE_OK) return s;
+  OPT(expert_threshold, 4);
+  REQ(w1, 16);
+  REQ(w2, 16);
+  OPT(b1, 4);
+  OPT(b2, 4);
+  REQN(y, 16, dims->tokens);
+  REQ(counts, 4);
+  REQ(sel_token, 4);
+  REQ(sel_score, 4);
+  REQ(sel_gate, 4);
+  REQ(importance, 4);
+  REQ(load, 4);
+  REQ(losses, 4);
+  const moe::Dt adt = to_dt(dims->act_dtype);
+  const size_t need = moe::batchwise_ws_bytes(dims->tokens, dims->n_experts, rows_per_expert,
+                                              dims->d_model, dims->d_hidden, adt);
+  if ((s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
+  moe::BatchwiseLaunch b;
+  b.gate = gate_launch(dims, opts, x, w_gate, w_noise, gate_bias, eps);
+  b.m = rows_per_expert;
+  b.threshold = expert_threshold;
+  b.h = dims->d_hidden;
+  b.act_dt = adt;
+  b.w1 = w1;
+  b.b1 = b1;
+  b.w2 = w2;
+  b.b2 = b2;
+  b.w_importance = opts->w_importance;
+  b.w_load = opts->w_load;
+  b.y = y;
+  b.counts = counts;
+  b.sel_token = sel_token;
+  b.sel_score = sel_score;
+  b.sel_gate = sel_gate;
+  b.importance = importance;
+  b.load = load;
+  b.losses = losses;
+  moe::batchwise_carve(b, ws, dims->d_model, dims->d_hidden, adt);
+  hipEvent_t t0, t1;
+  timing_pair(&t0, &t1);
+  return device_status(moe::launch_batchwise(b, (hipStream_t)stream, t0, t1),
+                       "moe_batchwise_forward");
+}
+
 size_t moe_hier_workspace_size(const moe_hier_dims* dims, const moe_gate_opts* opts) {
   if (check_hier_dims(dims) != MOE_OK) return 0;
   if (opts && check_opts(opts) != MOE_OK) return 0;

@@ -48,6 +48,10 @@ struct GateLaunch {
   int gate_order = 0;
 };
 
+// Batchwise gating's scores: H of every (token, expert) pair, written
+// expert-major to scores [n][B] (same arithmetic as launch_gate's H).
+hipError_t launch_scores(const GateLaunch& g, float* scores, hipStream_t s);
+
 // Noisy top-k gating: writes topk_idx [B,k], topk_gate [B,k], thresh [B,2].
 // cand (gate_cand_bytes(g) bytes, or null) lets a small flat batch split
 // its expert sweep.
@@ -104,6 +108,9 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
                         int32_t* counts, int32_t* offsets, int32_t* perm_token, float* perm_gate,
                         int32_t* slot_pos, float* importance, hipStream_t s, int capacity = 0);
 
+// Exclusive prefix sum of n counts into offsets [n + 1] (one workgroup).
+hipError_t launch_scan_counts(const int32_t* counts, int n, int32_t* offsets, hipStream_t s);
+
 // Expert FFN.
 int ffn_rows_per_block(int d, Dt dt);
 int64_t ffn_max_blocks(int64_t rows, int n, int d, Dt dt);
@@ -115,12 +122,15 @@ int ffn_hsplit(int64_t rows, int n, int d, int h, Dt dt);
 bool ffn_supported(int d, int h, Dt dt);
 // ev0 / ev1, when given, are recorded on s right before and after the FFN
 // kernel (after its plan kernel); capacity > 0 computes only the first
-// `capacity` rows of each segment.
+// `capacity` rows of each segment. With seg_counts, expert e's segment is
+// rows [e * seg_stride, e * seg_stride + seg_counts[e]) and offsets is unused;
+// tokens * k is then the row count the workspace was sized for.
 hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const void* x,
                       const int32_t* offsets, const int32_t* perm_token, const void* w1,
                       const void* b1, const void* w2, const void* b2, void* expert_out,
                       int32_t* blocks /* [2*max_blocks + 1] */, hipStream_t s,
-                      hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, int capacity = 0);
+                      hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, int capacity = 0,
+                      const int32_t* seg_counts = nullptr, int seg_stride = 0);
 
 // Weighted sum.
 hipError_t launch_combine(int64_t tokens, int k, int d, Dt dt, const void* expert_out,
@@ -137,6 +147,41 @@ hipError_t launch_hier_leaves(int64_t tokens, int k1, int k2, int b, const int32
                               int32_t* leaf_idx, float* leaf_gate, hipStream_t s);
 hipError_t launch_hier_leaf_load(int a, int b, const float* load1, const float* load2,
                                  const int32_t* rows1, float* load, hipStream_t s);
+
+// Batchwise gating: every expert takes the rows of the batch with the largest
+// scores H (above its threshold, if given), at most m; each token's gates are
+// the softmax of the scores of the experts that took it. Slots e*m .. e*m +
+// counts[e] - 1 hold expert e's rows in token order. B <= 65536.
+struct BatchwiseLaunch {
+  GateLaunch gate;           // x, gate weights, noise; k unused
+  int m = 0;
+  const float* threshold = nullptr;  // [n] or null (no threshold)
+  int h = 0;
+  Dt act_dt = kBF16;
+  const void *w1 = nullptr, *b1 = nullptr, *w2 = nullptr, *b2 = nullptr;
+  float w_importance = 0.f, w_load = 0.f;
+  // outputs
+  void* y = nullptr;
+  int32_t* counts = nullptr;     // [n]
+  int32_t* sel_token = nullptr;  // [n*m]
+  float* sel_score = nullptr;    // [n*m]
+  float* sel_gate = nullptr;     // [n*m]
+  float* importance = nullptr;   // [n]
+  float* load = nullptr;         // [n]
+  float* losses = nullptr;       // [3]
+  // workspace (batchwise_carve)
+  float* scores = nullptr;       // [n][B]
+  int32_t* tok_cnt = nullptr;    // [B]
+  int32_t* tok_off = nullptr;    // [B + 1]
+  int32_t* tok_list = nullptr;   // [n*m]
+  int32_t* tok_sorted = nullptr; // [n*m]
+  int32_t* ffn_blocks = nullptr;
+  void* expert_out = nullptr;    // [n*m][d]
+};
+size_t batchwise_ws_bytes(int64_t tokens, int n, int m, int d, int h, Dt act_dt);
+void batchwise_carve(BatchwiseLaunch& b, void* ws, int d, int h, Dt act_dt);
+hipError_t launch_batchwise(const BatchwiseLaunch& b, hipStream_t s, hipEvent_t ev0 = nullptr,
+                            hipEvent_t ev1 = nullptr);
 
 // Load as the hard count (train = 0) and the CV^2 losses.
 hipError_t launch_counts_to_load(const int32_t* counts, int n, float* load, hipStream_t s);

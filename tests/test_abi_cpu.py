@@ -30,7 +30,7 @@ def test_header_symbols_are_exported():
     assert "moe_forward" in names and len(names) >= 10
     for name in names:
         assert hasattr(L, name), f"{name} declared in moe.h but not exported"
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def dims(**kw):
@@ -185,3 +185,37 @@ def test_hier_pointer_and_workspace_checks():
     assert call_hier(d, o, extra=bad) == INVALID and "sub_load" in last_error()
     infer = L.moe_hier_workspace_size(ctypes.byref(d), ctypes.byref(opts(train=0)))
     assert 0 < infer < need
+
+
+def call_batchwise(d, o, m, ws=FAKE, ws_bytes=1 << 40, y=FAKE, counts=FAKE):
+    L = B.lib()
+    return L.moe_batchwise_forward(ctypes.byref(d), ctypes.byref(o), m, None, P(), P(), P(), None,
+                                   P(), P(), None, P(), None, P(y), P(counts), P(), P(), P(), P(),
+                                   P(), P(), P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,okw,m,status,msg", [
+    ({}, {}, 0, INVALID, "rows_per_expert"),
+    ({"tokens": 70000}, {}, 64, UNSUPPORTED, "65536"),
+    ({"capacity": 8}, {}, 64, UNSUPPORTED, "capacity"),
+    ({}, {"gate_order": 1}, 64, UNSUPPORTED, "gate_order"),
+    ({"n_experts": 32768, "tokens": 65536}, {}, 65536, INVALID, "int32"),
+    ({"d_hidden": 100}, {}, 64, UNSUPPORTED, "d_hidden"),
+])
+def test_batchwise_invalid_arguments(kw, okw, m, status, msg):
+    d, o = dims(**kw), opts(**okw)
+    assert call_batchwise(d, o, m) == status
+    assert msg in last_error()
+    assert B.lib().moe_batchwise_workspace_size(ctypes.byref(d), ctypes.byref(o), m) == 0
+
+
+def test_batchwise_pointer_and_workspace_checks():
+    L = B.lib()
+    d, o = dims(tokens=65536, n_experts=4096), opts()
+    need = L.moe_batchwise_workspace_size(ctypes.byref(d), ctypes.byref(o), 64)
+    # the fp32 score matrix [n, B] and one bf16 expert output row per slot
+    assert need >= 4096 * 65536 * 4 + 4096 * 64 * 512 * 2
+    assert call_batchwise(d, o, 64, counts=0) == INVALID and "counts is NULL" in last_error()
+    assert call_batchwise(d, o, 64, y=FAKE + 2) == INVALID and "aligned" in last_error()
+    assert call_batchwise(d, o, 64, ws_bytes=need - 1) == WORKSPACE
+    assert call_batchwise(d, o, 64, ws=FAKE + 16, ws_bytes=need) == INVALID

@@ -151,3 +151,18 @@ def test_infinite_thresholds():
     a = oracle.batchwise_forward(inp, B, train=False, threshold=np.full(n, -np.inf))
     b = oracle.batchwise_forward(inp, B, train=False)
     assert np.array_equal(a["y"], b["y"])
+
+
+def test_score_columns_match_the_gate_logits():
+    """The column helper and the row-wise gate give the same H (two code
+    paths: numpy over columns, the C oracle over rows)."""
+    rng = np.random.default_rng(14)
+    B, d, n = 20, 8, 6
+    inp = inputs(rng.normal(size=(B, d)), rng.normal(size=(n, d)), rng.normal(size=(n, d)),
+                 eps=rng.normal(size=(B, n)), bg=rng.normal(size=n))
+    H = oracle.gate(inp, 1, want_logits=True)["H"]
+    cols = [4, 0, 5]
+    assert np.allclose(oracle.score_columns(inp, cols), H[:, cols], rtol=1e-12, atol=1e-12)
+    Hc = oracle.gate(inp, 1, train=False, want_logits=True)["H"]
+    assert np.allclose(oracle.score_columns(inp, cols, train=False), Hc[:, cols], rtol=1e-12,
+                       atol=1e-12)
