@@ -227,6 +227,69 @@ def bench_hier(a, w):
     print(json.dumps(result), flush=True)
 
 
+def bench_batchwise(a, w, g, moe, torch):
+    """Batchwise gating (section "What the paper measured"): one step = one
+    moe_batchwise_forward call (expert-major scores, each expert's top m =
+    k B / n rows, token lists, expert FFNs, softmax and weighted sum,
+    Importance and the losses)."""
+    B, d, h, n, k = w.tokens, w.d_model, w.d_hidden, w.n_experts, w.k
+    m = max(1, k * B // n)
+    f = moe.MoeBatchwiseForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], m,
+                                gate_bias=g.get("gate_bias"), train=bool(a.train))
+    y = torch.empty((B, d), dtype=g["x"].dtype, device=g["x"].device)
+
+    def step():
+        f(g["x"], g["eps"], y)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    moe.moe_ffn_timing(True)
+    w0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(a.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    moe.moe_ffn_timing(False)
+    ffn_n, ffn_total = moe.moe_ffn_timing_read()
+    ms_step = e0.elapsed_time(e1) / a.steps
+    log(f"{ms_step:.3f} ms/step")
+    cnt = f.counts.cpu().numpy()
+    used, rows = int((cnt > 0).sum()), int(cnt.sum())
+    ffn_bytes = used * 2 * d * h * 2 + 2 * rows * d * 2
+    ffn_ms = ffn_total / ffn_n
+    achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+    gate_flops = 2.0 * B * d * n * (2 if a.train else 1)
+    step_flops = gate_flops + 4.0 * rows * d * h
+    # x, eps, gate weights, the fp32 score matrix written and read back, the
+    # expert weights, the rows in and out, y
+    step_bytes = (B * d * 2 + (B * n * 4 if a.train else 0) + 2 * n * d * 2 + 2 * B * n * 4
+                  + used * 2 * d * h * 2 + 2 * rows * d * 2 + B * d * 2)
+    result = {
+        "metric": "batchwise-gated MoE-layer forward tokens/sec (4096 experts, m = k B / n rows each)",
+        "value": B / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.act_dtype == 1 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "n_experts": n,
+                   "k": k, "gating": "batchwise", "rows_per_expert": m, "train": a.train},
+        "roofline": {"kernel": "ffn_kernel (expert FFN)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": ffn_bytes, "avg_launch_ms": ffn_ms,
+                     "timed_launches": ffn_n},
+        "step": {"alg_bytes": step_bytes, "alg_flops": step_flops,
+                 "hbm_frac": step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                 "mfma_frac": step_flops / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
+        "wall_ms_per_step": 1000 * wall / a.steps,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +309,9 @@ def main():
     ap.add_argument("--gate-order", type=int, default=0, choices=(0, 1),
                     help="0: softmax over the kept k (the pages); 1: softmax over all n, then "
                          "the kept k (Switch's order)")
+    ap.add_argument("--gating", default="topk", choices=("topk", "batchwise"),
+                    help="batchwise: every expert takes its k B / n best rows of the batch "
+                         "(moe_batchwise_forward) instead of every token its k best experts")
     ap.add_argument("--train", type=int, default=1, choices=(0, 1),
                     help="1: noisy gating with the Load pass (the headline step); 0: inference")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -287,6 +353,9 @@ def main():
     g = {key: to_device(v, torch, np) for key, v in inp.items()}
     torch.cuda.synchronize()
 
+    if a.gating == "batchwise":
+        bench_batchwise(a, w, g, moe, torch)
+        return
     cap = int(np.ceil(a.capacity_factor * B * k / n)) if a.capacity_factor > 0 else 0
     f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,
                        gate_bias=g.get("gate_bias"), train=bool(a.train), capacity=cap,

@@ -34,9 +34,12 @@
 namespace moe {
 namespace {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kCandCap = 2048;  // keys at or above the lower bound kept in LDS
+constexpr int kTileRows = 4 * kSelThreads;  // rows per pass step: 4 per thread
+constexpr int kMaxTiles = 65536 / kTileRows;
+constexpr int kCandCap = 2048;  // rows at or above the lower bound kept in LDS
+constexpr int kTop = 4;         // largest keys each thread remembers from its first pass
 
 // Order-preserving map of floats to unsigned keys (-0 is read as +0, so that
 // equal numbers get equal keys); key_value is its inverse.
@@ -104,15 +107,24 @@ struct BlockSum {
   }
 };
 
-// One workgroup per expert e: chooses its rows among scores[e][0 .. B) and
-// writes them in token order to sel_token / sel_score [e m ...], their number
-// to counts[e]. B <= 64 * 1024. Row r = j * 1024 + tid is read by thread tid
-// (tile j); the column is read once from HBM, the later passes mostly hit
-// the caches.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// One workgroup per expert e: chooses its rows among scores[e * ld + 0 .. B)
+// and writes them in token order to sel_token / sel_score [e m ...], their
+// number to counts[e]. B <= 65536, ld a multiple of 4. Thread tid reads rows
+// j * 2048 + 4 tid + (0..3) with one 16-byte load per step j; the first pass
+// reads the column from HBM, later passes (only when needed) mostly hit the
+// caches.
 __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
-    const float* __restrict__ scores, int B, int m, const float* __restrict__ thr,
+    const float* __restrict__ scores, int B, int64_t ld, int m, const float* __restrict__ thr,
     int32_t* __restrict__ counts, int32_t* __restrict__ sel_token, float* __restrict__ sel_score) {
-  constexpr int kMaxTiles = 64;
   __shared__ int red[2][3][kSelWaves];
   __shared__ uint32_t cand_k[kCandCap];
   __shared__ int32_t cand_r[kCandCap];
@@ -126,23 +138,57 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int tiles = (B + kSelThreads - 1) / kSelThreads;
-  const float* col = scores + (int64_t)e * B;
-  auto key_at = [&](int j) {
-    const int r = j * kSelThreads + tid;
-    return r < B ? order_key(col[r]) : 0u;  // 0: below every score's key
+  const int tiles = (B + kTileRows - 1) / kTileRows;
+  const float* col = scores + (int64_t)e * ld;
+  // the 4 keys of step j (0 for rows past B: below every score's key)
+  auto keys_at = [&](int j, uint32_t (&k)[4]) {
+    const int r0 = j * kTileRows + 4 * tid;
+    if (r0 < B) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(col + r0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k[i] = r0 + i < B ? order_key(v[i]) : 0u;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k[i] = 0u;
+    }
   };
   const float tv = thr ? thr[e] : -INFINITY;
   // a NaN threshold passes nothing (no number exceeds it)
   const uint32_t tkey = tv != tv ? 0xFFFFFFFFu : order_key(tv);
   const int64_t base = (int64_t)e * m;
 
-  uint32_t mx = 0;
+  // First pass: rows above the threshold, and this thread's kTop largest keys
+  // (descending; an equal key does not displace an earlier row).
+  uint32_t tk[kTop];
+  int tr[kTop];
+#pragma unroll
+  for (int i = 0; i < kTop; ++i) {
+    tk[i] = 0u;
+    tr[i] = -1;
+  }
   int above = 0;
   for (int j = 0; j < tiles; ++j) {
-    const uint32_t k = key_at(j);
-    above += k > tkey;
-    mx = max(mx, k);
+    uint32_t k[4];
+    keys_at(j, k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      above += k[i] > tkey;
+      if (k[i] > tk[kTop - 1]) {
+        uint32_t ck = k[i];
+        int cr = j * kTileRows + 4 * tid + i;
+#pragma unroll
+        for (int q = 0; q < kTop; ++q) {
+          if (ck > tk[q]) {
+            const uint32_t sk = tk[q];
+            const int sr = tr[q];
+            tk[q] = ck;
+            tr[q] = cr;
+            ck = sk;
+            cr = sr;
+          }
+        }
+      }
+    }
   }
   int cv[1] = {above};
   bs.sum(cv);
@@ -150,18 +196,25 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   if (tid == 0) counts[e] = c < m ? c : m;
 
   // Rows with key > t are taken, and of those with key == t the first need_eq
-  // in token order. With at most m rows above the threshold: all of them.
-  // Compaction over every row: each (tile, wave) cell's counts of rows above
+  // in token order (with at most m rows above the threshold: all of them).
+  // Compaction over every row: each (step, wave) cell's counts of rows above
   // t and of tied rows, an exclusive scan over the cells, then every taken
   // row's slot.
   auto compact_rows = [&](uint32_t t, int need_eq) {
     for (int j = 0; j < tiles; ++j) {
-      const uint32_t k = key_at(j);
-      const uint64_t bg = __ballot(k > t);
-      const uint64_t be = __ballot(need_eq > 0 && k == t);
-      if (lane == 0) {
-        cell_g[j * kSelWaves + wave] = (int)__popcll(bg);
-        cell_e[j * kSelWaves + wave] = (int)__popcll(be);
+      uint32_t k[4];
+      keys_at(j, k);
+      int g = 0, q = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        g += k[i] > t;
+        q += need_eq > 0 && k[i] == t;
+      }
+      g = wave_incl_scan(g, lane);
+      q = wave_incl_scan(q, lane);
+      if (lane == 63) {
+        cell_g[j * kSelWaves + wave] = g;
+        cell_e[j * kSelWaves + wave] = q;
       }
     }
     __syncthreads();
@@ -170,14 +223,8 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
       int vg = tid < nc ? cell_g[tid] : 0;
       int ve = tid < nc ? cell_e[tid] : 0;
       const int og = vg, oe = ve;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int ug = __shfl_up(vg, o), ue = __shfl_up(ve, o);
-        if (lane >= o) {
-          vg += ug;
-          ve += ue;
-        }
-      }
+      vg = wave_incl_scan(vg, lane);
+      ve = wave_incl_scan(ve, lane);
       if (lane == 63) {
         wtot[0][wave] = vg;
         wtot[1][wave] = ve;
@@ -193,19 +240,28 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
       }
     }
     __syncthreads();
-    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     for (int j = 0; j < tiles; ++j) {
-      const uint32_t k = key_at(j);
-      const bool gt = k > t;
-      const bool eq = need_eq > 0 && k == t;
-      const uint64_t bg = __ballot(gt);
-      const uint64_t be = __ballot(eq);
-      const int gb = cell_g[j * kSelWaves + wave] + (int)__popcll(bg & below);
-      const int eb = cell_e[j * kSelWaves + wave] + (int)__popcll(be & below);
-      const int pos = gb + min(eb, need_eq);
-      if ((gt || (eq && eb < need_eq)) && pos < m) {
-        sel_token[base + pos] = j * kSelThreads + tid;
-        sel_score[base + pos] = key_value(k);
+      uint32_t k[4];
+      keys_at(j, k);
+      int g = 0, q = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        g += k[i] > t;
+        q += need_eq > 0 && k[i] == t;
+      }
+      int gb = cell_g[j * kSelWaves + wave] + wave_incl_scan(g, lane) - g;
+      int eb = cell_e[j * kSelWaves + wave] + wave_incl_scan(q, lane) - q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool gt = k[i] > t;
+        const bool eq = need_eq > 0 && k[i] == t;
+        const int pos = gb + min(eb, need_eq);
+        if ((gt || (eq && eb < need_eq)) && pos < m) {
+          sel_token[base + pos] = j * kTileRows + 4 * tid + i;
+          sel_score[base + pos] = key_value(k[i]);
+        }
+        gb += gt;
+        eb += eq;
       }
     }
   };
@@ -217,6 +273,7 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   if (m <= kSelThreads) {
     // lower bound lb <= t: the m-th largest of the threads' maxima (m
     // distinct keys are >= it), two bits per step
+    const uint32_t mx = tk[0];
     uint32_t lb = 0;
     for (int b = 30; b >= 0; b -= 2) {
       const bool f[3] = {mx >= (lb | (1u << b)), mx >= (lb | (2u << b)), mx >= (lb | (3u << b))};
@@ -227,16 +284,36 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
       else if (v[0] >= m) lb |= 1u << b;
     }
     // the rows with keys >= lb (at least m of them, and every row with a key
-    // >= t) to LDS, in any order
+    // >= t) to LDS, in any order: from the remembered keys, unless a thread's
+    // kTop-th key reaches lb (it may have more), then from another pass
     if (tid == 0) ncand = 0;
-    __syncthreads();
-    for (int j = 0; j < tiles; ++j) {
-      const uint32_t k = key_at(j);
-      if (k >= lb) {
-        const int at = atomicAdd(&ncand, 1);
-        if (at < kCandCap) {
-          cand_k[at] = k;
-          cand_r[at] = j * kSelThreads + tid;
+    const bool more[1] = {tk[kTop - 1] >= lb};
+    int anym[1];
+    bs.count(more, anym);  // its barrier also orders the reset of ncand
+    if (anym[0] == 0) {
+#pragma unroll
+      for (int i = 0; i < kTop; ++i) {
+        if (tk[i] >= lb) {
+          const int at = atomicAdd(&ncand, 1);
+          if (at < kCandCap) {
+            cand_k[at] = tk[i];
+            cand_r[at] = tr[i];
+          }
+        }
+      }
+    } else {
+      for (int j = 0; j < tiles; ++j) {
+        uint32_t k[4];
+        keys_at(j, k);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (k[i] >= lb) {
+            const int at = atomicAdd(&ncand, 1);
+            if (at < kCandCap) {
+              cand_k[at] = k[i];
+              cand_r[at] = j * kTileRows + 4 * tid + i;
+            }
+          }
         }
       }
     }
@@ -293,14 +370,57 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   for (int b = 31; b >= 0; --b) {
     const uint32_t cb = t | (1u << b);
     int cnt[1] = {0};
-    for (int j = 0; j < tiles; ++j) cnt[0] += key_at(j) >= cb;
+    for (int j = 0; j < tiles; ++j) {
+      uint32_t k[4];
+      keys_at(j, k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cnt[0] += k[i] >= cb;
+    }
     bs.sum(cnt);
     if (cnt[0] >= m) t = cb;
   }
   int gt[1] = {0};
-  for (int j = 0; j < tiles; ++j) gt[0] += key_at(j) > t;
+  for (int j = 0; j < tiles; ++j) {
+    uint32_t k[4];
+    keys_at(j, k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gt[0] += k[i] > t;
+  }
   bs.sum(gt);
   compact_rows(t, m - gt[0]);
+}
+
+// Exclusive prefix sum of n counts into offsets [n + 1], one workgroup of
+// 1024 threads: steps of 4096 counts, 4 consecutive per thread, a wave scan
+// and the waves' totals, plus the running total of earlier steps.
+__global__ __launch_bounds__(1024) void batch_scan_kernel(const int32_t* __restrict__ in, int n,
+                                                          int32_t* __restrict__ out) {
+  __shared__ int wsum[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int s0 = 0, it = 0; s0 < n; s0 += 4096, ++it) {
+    const int i0 = s0 + 4 * tid;
+    int v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = i0 + i < n ? in[i0 + i] : 0;
+    const int own = v[0] + v[1] + v[2] + v[3];
+    const int incl = wave_incl_scan(own, lane);
+    if (lane == 63) wsum[it & 1][wave] = incl;
+    __syncthreads();
+    int before = carry + incl - own, total = carry;
+    for (int w = 0; w < 16; ++w) {
+      const int x = wsum[it & 1][w];
+      if (w < wave) before += x;
+      total += x;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i0 + i < n) out[i0 + i] = before;
+      before += v[i];
+    }
+    carry = total;
+  }
+  if (tid == 0) out[n] = carry;
 }
 
 __global__ void batch_zero_kernel(int32_t* __restrict__ p, int n) {
@@ -448,12 +568,16 @@ __global__ __launch_bounds__(256) void batch_importance_kernel(const int32_t* __
   if (lane == 0) importance[e] = s;
 }
 
+// Row stride of the score matrix: B rounded up to 4 floats, so that every
+// row starts 16-byte aligned.
+int64_t score_ld(int64_t B) { return (B + 3) / 4 * 4; }
+
 }  // namespace
 
 size_t batchwise_ws_bytes(int64_t tokens, int n, int m, int d, int h, Dt act_dt) {
   const int64_t slots = (int64_t)n * m;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  return al((size_t)tokens * n * sizeof(float)) +          // scores
+  return al((size_t)score_ld(tokens) * n * sizeof(float)) +  // scores
          al((size_t)tokens * sizeof(int32_t)) +            // tok_cnt
          al((size_t)(tokens + 1) * sizeof(int32_t)) +      // tok_off
          2 * al((size_t)slots * sizeof(int32_t)) +         // tok_list, tok_sorted
@@ -468,7 +592,7 @@ void batchwise_carve(BatchwiseLaunch& b, void* ws, int d, int h, Dt act_dt) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   char* p = static_cast<char*>(ws);
   b.scores = reinterpret_cast<float*>(p);
-  p += al((size_t)B * n * sizeof(float));
+  p += al((size_t)score_ld(B) * n * sizeof(float));
   b.tok_cnt = reinterpret_cast<int32_t*>(p);
   p += al((size_t)B * sizeof(int32_t));
   b.tok_off = reinterpret_cast<int32_t*>(p);
@@ -489,10 +613,11 @@ hipError_t launch_batchwise(const BatchwiseLaunch& b, hipStream_t s, hipEvent_t 
   const int m = b.m;
   const int64_t slots = (int64_t)n * m;
   if (B > 65536 || m < 1 || slots >= INT_MAX) return hipErrorInvalidValue;
-  hipError_t e = launch_scores(b.gate, b.scores, s);
+  const int64_t ld = score_ld(B);
+  hipError_t e = launch_scores(b.gate, b.scores, ld, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(batch_select_kernel, dim3((unsigned)n), dim3(kSelThreads), 0, s, b.scores,
-                     (int)B, m, b.threshold, b.counts, b.sel_token, b.sel_score);
+                     (int)B, ld, m, b.threshold, b.counts, b.sel_token, b.sel_score);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned slot_blocks = (unsigned)((slots + 255) / 256);
   if (B > 0) {
@@ -501,7 +626,7 @@ hipError_t launch_batchwise(const BatchwiseLaunch& b, hipStream_t s, hipEvent_t 
     hipLaunchKernelGGL(batch_tok_count_kernel, dim3(slot_blocks), dim3(256), 0, s, b.counts,
                        b.sel_token, slots, m, (int)B, b.tok_cnt);
   }
-  if ((e = launch_scan_counts(b.tok_cnt, (int)B, b.tok_off, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(batch_scan_kernel, dim3(1), dim3(1024), 0, s, b.tok_cnt, (int)B, b.tok_off);
   if (B > 0) {
     hipLaunchKernelGGL(batch_tok_fill_kernel, dim3(slot_blocks), dim3(256), 0, s, b.counts,
                        b.sel_token, slots, m, (int)B, b.tok_off, b.tok_cnt, b.tok_list);

@@ -394,12 +394,13 @@ hipError_t launch_gate(const GateLaunch& g0, int32_t* topk_idx, float* topk_gate
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const GateLaunch& g0, float* scores, hipStream_t s) {
+hipError_t launch_scores(const GateLaunch& g0, float* scores, int64_t sld, hipStream_t s) {
   if (g0.tokens == 0) return hipSuccess;
   GateLaunch g = g0;
   g.ranges = gate_ranges(g);  // each range writes its own experts' rows: no merge
   GateParams p = make_params(g);
   p.scores = scores;
+  p.sld = sld;
   return gate_dispatch(g, p, false, s);
 }
 

@@ -433,9 +433,9 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         // batchwise gating: the 8 scores to their experts' rows; the 32 lanes
         // of each half write 128 contiguous bytes per expert
         if (srow >= 0) {
-          float* dst = p.scores + (int64_t)((cr.c0 + c) * EC + 4 * hi) * p.B + srow;
+          float* dst = p.scores + (int64_t)((cr.c0 + c) * EC + 4 * hi) * p.sld + srow;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) dst[(int64_t)(8 * (i / 4) + (i % 4)) * p.B] = hv[i];
+          for (int i = 0; i < 8; ++i) dst[(int64_t)(8 * (i / 4) + (i % 4)) * p.sld] = hv[i];
         }
       } else {
         if constexpr (SMX) es = expsum_add(es, hv);

@@ -57,9 +57,10 @@ struct GateParams {
   // with gate_order 1 each range also writes its rows' (max, sum of exp(H -
   // max)) pair to cand_ms [(row * gridDim.y + blockIdx.y) * 2]
   float* cand_ms;
-  // Batchwise gating: every H goes to scores[e * B + row] (expert-major, one
-  // row of B per expert) instead of a selection; null otherwise.
+  // Batchwise gating: every H goes to scores[e * sld + row] (expert-major,
+  // one row of sld >= B per expert) instead of a selection; null otherwise.
   float* scores;
+  int64_t sld;
   // Secondary gating of a hierarchical layer ("Hierarchical MoE"); all null
   // for a flat gate. The rows are those a primary route sent to each group:
   // workgroup u covers the rows seg_off[g] + first, ... of group g, with
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
         const int e = cbase + c * EC + nt * 16 + lr;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (e < n && row_ok[r]) p.scores[(int64_t)e * p.B + iorow[r]] = hv[nt][r];
+          if (e < n && row_ok[r]) p.scores[(int64_t)e * p.sld + iorow[r]] = hv[nt][r];
       }
     } else {
       if constexpr (SMX) {

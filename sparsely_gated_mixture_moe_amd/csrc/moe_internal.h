@@ -49,8 +49,8 @@ struct GateLaunch {
 };
 
 // Batchwise gating's scores: H of every (token, expert) pair, written
-// expert-major to scores [n][B] (same arithmetic as launch_gate's H).
-hipError_t launch_scores(const GateLaunch& g, float* scores, hipStream_t s);
+// expert-major to scores [n][sld], sld >= B (same arithmetic as launch_gate's H).
+hipError_t launch_scores(const GateLaunch& g, float* scores, int64_t sld, hipStream_t s);
 
 // Noisy top-k gating: writes topk_idx [B,k], topk_gate [B,k], thresh [B,2].
 // cand (gate_cand_bytes(g) bytes, or null) lets a small flat batch split
@@ -170,7 +170,7 @@ struct BatchwiseLaunch {
   float* load = nullptr;         // [n]
   float* losses = nullptr;       // [3]
   // workspace (batchwise_carve)
-  float* scores = nullptr;       // [n][B]
+  float* scores = nullptr;       // [n][score_ld], score_ld = B rounded up to 4
   int32_t* tok_cnt = nullptr;    // [B]
   int32_t* tok_off = nullptr;    // [B + 1]
   int32_t* tok_list = nullptr;   // [n*m]

@@ -268,11 +268,11 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
   while ((1u << nbits) <= (uint32_t)n) ++nbits;  // keys 0..n need nbits bits
   // Up to 32768 experts: 128 KB of LDS counters (set once per process).
   static const bool lds_attr_set = [] {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(route_count),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(route_count),
                         hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * (int)sizeof(int));
-    hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter),
                         hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * (int)sizeof(int));
-    hipFuncSetAttribute(reinterpret_cast<const void*>(route_small),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(route_small),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmallLds);
     return true;
   }();
