@@ -167,24 +167,39 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
     tr[i] = -1;
   }
   int above = 0;
-  for (int j = 0; j < tiles; ++j) {
-    uint32_t k[4];
-    keys_at(j, k);
+  // eight steps' loads are issued before any is used, so that each thread
+  // keeps 128 bytes in flight
+  constexpr int kBatch = 8;
+  for (int j0 = 0; j0 < tiles; j0 += kBatch) {
+    f32x4 raw[kBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      above += k[i] > tkey;
-      if (k[i] > tk[kTop - 1]) {
-        uint32_t ck = k[i];
-        int cr = j * kTileRows + 4 * tid + i;
+    for (int q = 0; q < kBatch; ++q) {
+      const int r0 = (j0 + q) * kTileRows + 4 * tid;
+      raw[q] = r0 < B ? *reinterpret_cast<const f32x4*>(col + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-        for (int q = 0; q < kTop; ++q) {
-          if (ck > tk[q]) {
-            const uint32_t sk = tk[q];
-            const int sr = tr[q];
-            tk[q] = ck;
-            tr[q] = cr;
-            ck = sk;
-            cr = sr;
+    for (int q = 0; q < kBatch; ++q) {
+      const int j = j0 + q;
+      const int r0 = j * kTileRows + 4 * tid;
+      uint32_t k[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k[i] = r0 + i < B ? order_key(raw[q][i]) : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        above += k[i] > tkey;
+        if (k[i] > tk[kTop - 1]) {
+          uint32_t ck = k[i];
+          int cr = j * kTileRows + 4 * tid + i;
+#pragma unroll
+          for (int t = 0; t < kTop; ++t) {
+            if (ck > tk[t]) {
+              const uint32_t sk = tk[t];
+              const int sr = tr[t];
+              tk[t] = ck;
+              tr[t] = cr;
+              ck = sk;
+              cr = sr;
+            }
           }
         }
       }

@@ -271,3 +271,56 @@ def test_batchwise_full_size_sampled():
         yerr = max(yerr, rel_err(yg[t], (gr[:, None] * eo).sum(0)))
     assert yerr <= out_tol(True), f"y error {yerr}"
     print("batchwise full size", len(rows), "rows, y err", yerr)
+
+
+def test_batchwise_is_deterministic():
+    """Every sum over a token's experts or an expert's rows runs in a fixed
+    order, so two calls give bitwise-equal outputs (the token lists are filled
+    with atomics and then sorted)."""
+    w = dg.workload("flat_bf16_n4096", tokens=4096, n_experts=256, d_hidden=256)
+    announce("moe_batchwise_forward determinism")
+    inp = dg.make_inputs(w, with_bias=True)
+    g = gpu_inputs(inp)
+    m = w.k * w.tokens // w.n_experts
+    f = moe.MoeBatchwiseForward(tuple(g["x"].shape), g["w_gate"], g["w_noise"], g["w1"], g["w2"],
+                                m, b1=g.get("b1"), b2=g.get("b2"), gate_bias=g.get("gate_bias"))
+    y1 = f(g["x"], g["eps"]).clone()
+    first = [t.clone() for t in (f.counts, f.sel_token, f.sel_score, f.sel_gate, f.importance,
+                                 f.losses)]
+    y2 = f(g["x"], g["eps"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    for a_, b_ in zip(first, (f.counts, f.sel_token, f.sel_score, f.sel_gate, f.importance,
+                              f.losses)):
+        assert torch.equal(a_, b_)
+
+
+@pytest.mark.parametrize("tokens,train", [(5, True), (3000, False)])
+def test_batchwise_graph_replays(tokens, train):
+    """moe_batchwise_forward captured in a HIP graph (no allocations, copies,
+    fills or synchronizations inside): each replay, with eager calls on other
+    inputs and synchronizations in between, gives exactly the eager outputs."""
+    w = dg.workload("flat_bf16_n4096", tokens=tokens, n_experts=256, d_hidden=256)
+    announce(f"moe_batchwise_forward graph replay tokens={tokens} train={train}")
+    inp = dg.make_inputs(w)
+    g = gpu_inputs(inp)
+    m = max(1, w.k * w.tokens // w.n_experts)
+    f = moe.MoeBatchwiseForward(tuple(g["x"].shape), g["w_gate"], g["w_noise"], g["w1"], g["w2"],
+                                m, train=train)
+    x, eps = g["x"].clone(), g["eps"].clone()
+    y = torch.empty_like(x)
+    f(x, eps, y)
+    torch.cuda.synchronize()
+    outs = lambda: (y, f.counts, f.sel_token, f.sel_gate, f.importance, f.losses)  # noqa: E731
+    ref = [t.clone() for t in outs()]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        f(x, eps, y)
+    other_x, other_eps = torch.flip(x, [0]).contiguous(), torch.flip(eps, [0]).contiguous()
+    for _ in range(3):
+        f(other_x, other_eps)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a_, b_ in zip(ref, outs()):
+            assert torch.equal(a_, b_)
