@@ -108,9 +108,6 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
                         int32_t* counts, int32_t* offsets, int32_t* perm_token, float* perm_gate,
                         int32_t* slot_pos, float* importance, hipStream_t s, int capacity = 0);
 
-// Exclusive prefix sum of n counts into offsets [n + 1] (one workgroup).
-hipError_t launch_scan_counts(const int32_t* counts, int n, int32_t* offsets, hipStream_t s);
-
 // Expert FFN.
 int ffn_rows_per_block(int d, Dt dt);
 int64_t ffn_max_blocks(int64_t rows, int n, int d, Dt dt);

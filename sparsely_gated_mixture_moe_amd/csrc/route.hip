@@ -303,9 +303,4 @@ hipError_t launch_route(int64_t tokens, int k, int n, const int32_t* topk_idx,
   return hipGetLastError();
 }
 
-hipError_t launch_scan_counts(const int32_t* counts, int n, int32_t* offsets, hipStream_t s) {
-  hipLaunchKernelGGL(route_scan_experts, dim3(1), dim3(kThreads), 0, s, counts, n, offsets);
-  return hipGetLastError();
-}
-
 }  // namespace moe
