@@ -9,14 +9,16 @@
 //
 //   1. scores     H of every (token, expert), written expert-major by the gate
 //                 kernels (launch_scores): scores[e][t].
-//   2. select     one workgroup per expert. Its B scores stay in registers as
-//                 order-preserving integer keys (up to 64 per thread). The
-//                 m-th largest key is found from a lower bound (the m-th
-//                 largest of the threads' maxima, by a 2-bit-per-step search)
-//                 and the few keys at or above it, ranked in LDS; then the
-//                 chosen rows are compacted in token order (one scan over the
-//                 (tile, wave) cells), ties to the lower token. Expert e's rows
-//                 go to slots [e m, e m + count_e).
+//   2. select     one workgroup per expert; its scores are read as
+//                 order-preserving integer keys with 16-byte loads. The m-th
+//                 largest of the threads' maxima is a lower bound of the cut (m
+//                 distinct keys reach it); the few rows at or above it (about
+//                 m) are gathered into LDS by a second pass, which mostly hits
+//                 the caches, and ranked there: the cut, the ties (to the lower
+//                 token) and each taken row's slot in token order. Expert e's
+//                 rows go to slots [e m, e m + count_e). (When every row above
+//                 the threshold is taken, or the candidates do not fit, a scan
+//                 over all rows compacts.)
 //   3. token lists  each token's slots: integer-atomic counts, a prefix sum,
 //                 an atomic fill, then each list put in slot order by ranks
 //                 (slot order is expert order, so every later sum over a
@@ -39,7 +41,6 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kTileRows = 4 * kSelThreads;  // rows per pass step: 4 per thread
 constexpr int kMaxTiles = 65536 / kTileRows;
 constexpr int kCandCap = 2048;  // rows at or above the lower bound kept in LDS
-constexpr int kTop = 4;         // largest keys each thread remembers from its first pass
 
 // Order-preserving map of floats to unsigned keys (-0 is read as +0, so that
 // equal numbers get equal keys); key_value is its inverse.
@@ -67,8 +68,7 @@ __device__ __forceinline__ float wave_max_f(float v) {
   return v;
 }
 
-// Workgroup-wide sums of up to three per-thread integers (sum) or flags
-// (count). The LDS array is used by parity, so one barrier per call
+// Workgroup-wide sums of up to three per-thread integers. The LDS array is used by parity, so one barrier per call
 // suffices: a wave writes slot p again only after every wave has passed the
 // next call's barrier, i.e. has read slot p.
 struct BlockSum {
@@ -98,13 +98,6 @@ struct BlockSum {
     for (int i = 0; i < N; ++i) v[i] = wave_sum_i(v[i]);
     finish(v);
   }
-  template <int N>
-  __device__ __forceinline__ void count(const bool (&f)[N], int (&v)[N]) {
-    static_assert(N <= 3, "three counts per call");
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = (int)__popcll(__ballot(f[i]));
-    finish(v);
-  }
 };
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -120,8 +113,7 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // and writes them in token order to sel_token / sel_score [e m ...], their
 // number to counts[e]. B <= 65536, ld a multiple of 4. Thread tid reads rows
 // j * 2048 + 4 tid + (0..3) with one 16-byte load per step j; the first pass
-// reads the column from HBM, later passes (only when needed) mostly hit the
-// caches.
+// reads the column from HBM, later passes mostly hit the caches.
 __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
     const float* __restrict__ scores, int B, int64_t ld, int m, const float* __restrict__ thr,
     int32_t* __restrict__ counts, int32_t* __restrict__ sel_token, float* __restrict__ sel_score) {
@@ -131,6 +123,7 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   __shared__ uint8_t cand_sel[kCandCap];
   __shared__ int cell_g[kMaxTiles * kSelWaves], cell_e[kMaxTiles * kSelWaves];
   __shared__ int wtot[2][kSelWaves];
+  __shared__ uint32_t mxs[kSelThreads];
   __shared__ int ncand;
   __shared__ uint32_t tsh;
   BlockSum bs{red};
@@ -140,16 +133,26 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   const int wave = tid >> 6;
   const int tiles = (B + kTileRows - 1) / kTileRows;
   const float* col = scores + (int64_t)e * ld;
-  // the 4 keys of step j (0 for rows past B: below every score's key)
-  auto keys_at = [&](int j, uint32_t (&k)[4]) {
-    const int r0 = j * kTileRows + 4 * tid;
-    if (r0 < B) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(col + r0);
+  // every step's keys, eight steps' loads issued before any is used
+  auto each_step = [&](auto&& fn) {
+    constexpr int kB = 8;
+    for (int j0 = 0; j0 < tiles; j0 += kB) {
+      f32x4 raw[kB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) k[i] = r0 + i < B ? order_key(v[i]) : 0u;
-    } else {
+      for (int q = 0; q < kB; ++q) {
+        const int r0 = (j0 + q) * kTileRows + 4 * tid;
+        raw[q] = r0 < B ? *reinterpret_cast<const f32x4*>(col + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) k[i] = 0u;
+      for (int q = 0; q < kB; ++q) {
+        const int j = j0 + q;
+        if (j >= tiles) break;
+        const int r0 = j * kTileRows + 4 * tid;
+        uint32_t k[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k[i] = r0 + i < B ? order_key(raw[q][i]) : 0u;
+        fn(j, k);
+      }
     }
   };
   const float tv = thr ? thr[e] : -INFINITY;
@@ -157,54 +160,16 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   const uint32_t tkey = tv != tv ? 0xFFFFFFFFu : order_key(tv);
   const int64_t base = (int64_t)e * m;
 
-  // First pass: rows above the threshold, and this thread's kTop largest keys
-  // (descending; an equal key does not displace an earlier row).
-  uint32_t tk[kTop];
-  int tr[kTop];
-#pragma unroll
-  for (int i = 0; i < kTop; ++i) {
-    tk[i] = 0u;
-    tr[i] = -1;
-  }
+  // First pass: the rows above the threshold and this thread's largest key.
+  uint32_t mx = 0;
   int above = 0;
-  // eight steps' loads are issued before any is used, so that each thread
-  // keeps 128 bytes in flight
-  constexpr int kBatch = 8;
-  for (int j0 = 0; j0 < tiles; j0 += kBatch) {
-    f32x4 raw[kBatch];
+  each_step([&](int, const uint32_t (&k)[4]) {
 #pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      const int r0 = (j0 + q) * kTileRows + 4 * tid;
-      raw[q] = r0 < B ? *reinterpret_cast<const f32x4*>(col + r0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) {
+      above += k[i] > tkey;
+      mx = max(mx, k[i]);
     }
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      const int j = j0 + q;
-      const int r0 = j * kTileRows + 4 * tid;
-      uint32_t k[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) k[i] = r0 + i < B ? order_key(raw[q][i]) : 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        above += k[i] > tkey;
-        if (k[i] > tk[kTop - 1]) {
-          uint32_t ck = k[i];
-          int cr = j * kTileRows + 4 * tid + i;
-#pragma unroll
-          for (int t = 0; t < kTop; ++t) {
-            if (ck > tk[t]) {
-              const uint32_t sk = tk[t];
-              const int sr = tr[t];
-              tk[t] = ck;
-              tr[t] = cr;
-              ck = sk;
-              cr = sr;
-            }
-          }
-        }
-      }
-    }
-  }
+  });
   int cv[1] = {above};
   bs.sum(cv);
   const int c = cv[0];  // rows above the threshold
@@ -216,9 +181,7 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   // t and of tied rows, an exclusive scan over the cells, then every taken
   // row's slot.
   auto compact_rows = [&](uint32_t t, int need_eq) {
-    for (int j = 0; j < tiles; ++j) {
-      uint32_t k[4];
-      keys_at(j, k);
+    each_step([&](int j, const uint32_t (&k)[4]) {
       int g = 0, q = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -231,7 +194,7 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
         cell_g[j * kSelWaves + wave] = g;
         cell_e[j * kSelWaves + wave] = q;
       }
-    }
+    });
     __syncthreads();
     {
       const int nc = tiles * kSelWaves;
@@ -255,9 +218,7 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
       }
     }
     __syncthreads();
-    for (int j = 0; j < tiles; ++j) {
-      uint32_t k[4];
-      keys_at(j, k);
+    each_step([&](int j, const uint32_t (&k)[4]) {
       int g = 0, q = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -278,7 +239,7 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
         gb += gt;
         eb += eq;
       }
-    }
+    });
   };
 
   if (c <= m) {
@@ -287,51 +248,44 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   }
   if (m <= kSelThreads) {
     // lower bound lb <= t: the m-th largest of the threads' maxima (m
-    // distinct keys are >= it), two bits per step
-    const uint32_t mx = tk[0];
-    uint32_t lb = 0;
-    for (int b = 30; b >= 0; b -= 2) {
-      const bool f[3] = {mx >= (lb | (1u << b)), mx >= (lb | (2u << b)), mx >= (lb | (3u << b))};
-      int v[3];
-      bs.count(f, v);
-      if (v[2] >= m) lb |= 3u << b;
-      else if (v[1] >= m) lb |= 2u << b;
-      else if (v[0] >= m) lb |= 1u << b;
-    }
-    // the rows with keys >= lb (at least m of them, and every row with a key
-    // >= t) to LDS, in any order: from the remembered keys, unless a thread's
-    // kTop-th key reaches lb (it may have more), then from another pass
-    if (tid == 0) ncand = 0;
-    const bool more[1] = {tk[kTop - 1] >= lb};
-    int anym[1];
-    bs.count(more, anym);  // its barrier also orders the reset of ncand
-    if (anym[0] == 0) {
+    // distinct keys are >= it), by a bitwise search that one wave runs alone
+    // over the maxima in LDS (no workgroup barrier per step)
+    mxs[tid] = mx;
+    __syncthreads();
+    if (wave == 0) {
+      constexpr int PER = kSelThreads / 64;
+      uint32_t v[PER];
 #pragma unroll
-      for (int i = 0; i < kTop; ++i) {
-        if (tk[i] >= lb) {
+      for (int i = 0; i < PER; ++i) v[i] = mxs[lane * PER + i];
+      uint32_t l = 0;
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t cb = l | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) cnt += v[i] >= cb;
+        if (wave_sum_i(cnt) >= m) l = cb;
+      }
+      if (lane == 0) tsh = l;
+    }
+    __syncthreads();
+    const uint32_t lb = tsh;
+    // the rows with keys >= lb (at least m of them, and every row with a key
+    // >= t) to LDS, in any order, from a second pass over the column (it
+    // mostly hits the caches)
+    if (tid == 0) ncand = 0;
+    __syncthreads();
+    each_step([&](int j, const uint32_t (&k)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (k[i] >= lb) {
           const int at = atomicAdd(&ncand, 1);
           if (at < kCandCap) {
-            cand_k[at] = tk[i];
-            cand_r[at] = tr[i];
+            cand_k[at] = k[i];
+            cand_r[at] = j * kTileRows + 4 * tid + i;
           }
         }
       }
-    } else {
-      for (int j = 0; j < tiles; ++j) {
-        uint32_t k[4];
-        keys_at(j, k);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (k[i] >= lb) {
-            const int at = atomicAdd(&ncand, 1);
-            if (at < kCandCap) {
-              cand_k[at] = k[i];
-              cand_r[at] = j * kTileRows + 4 * tid + i;
-            }
-          }
-        }
-      }
-    }
+    });
     __syncthreads();
     const int nc = ncand;
     if (nc <= kCandCap) {
@@ -385,22 +339,18 @@ __global__ __launch_bounds__(kSelThreads) void batch_select_kernel(
   for (int b = 31; b >= 0; --b) {
     const uint32_t cb = t | (1u << b);
     int cnt[1] = {0};
-    for (int j = 0; j < tiles; ++j) {
-      uint32_t k[4];
-      keys_at(j, k);
+    each_step([&](int, const uint32_t (&k)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) cnt[0] += k[i] >= cb;
-    }
+    });
     bs.sum(cnt);
     if (cnt[0] >= m) t = cb;
   }
   int gt[1] = {0};
-  for (int j = 0; j < tiles; ++j) {
-    uint32_t k[4];
-    keys_at(j, k);
+  each_step([&](int, const uint32_t (&k)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) gt[0] += k[i] > t;
-  }
+  });
   bs.sum(gt);
   compact_rows(t, m - gt[0]);
 }
