@@ -350,7 +350,7 @@ int gate_ranges(const GateLaunch& g) {
   const int64_t tiles = (g.tokens + rows - 1) / rows;
   constexpr int kTarget = 256;  // workgroups to aim for
   if (2 * tiles > kTarget) return 1;
-  const int w = gate_uses_g32(g) ? kGate32Chunk
+  const int w = gate_uses_g32(g) ? (g.train ? kGate32Chunk : 2 * kGate32Chunk)
                                  : (g.x_dt == kBF16 && g.w_dt == kBF16 ? GateShape<bf16>::kChunk
                                                                         : GateShape<float>::kChunk);
   const int nch = (g.n + w - 1) / w;

@@ -60,7 +60,7 @@ __device__ const float kZeroBias[kG32Chunk] = {};
 constexpr int kG32PhiValu = 30;
 constexpr int kG32HValu = 12;
 
-template <int D, int L, bool PASS2, bool SMX = false, bool SCORES = false>
+template <int D, int L, bool PASS2, bool SMX = false, bool SCORES = false, bool CL = false>
 __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   RowTile tile;
   if (!resolve_tile<kG32Rows, bf16, D>(p, tile)) return;
@@ -69,6 +69,10 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   static_assert(NKB % kG32Waves == 0, "each wave copies whole fragments");
   constexpr int DMA_PER_WAVE = NKB / kG32Waves;
   constexpr int EC = kG32Chunk;
+  // CL (noise-free selection pass without gate bias): a chunk's 32 tile
+  // columns are 32 experts' clean rows instead of 16 clean and 16 noise rows
+  static_assert(!(CL && PASS2), "the Load pass needs the noise rows");
+  constexpr int EX = CL ? 2 * EC : EC;  // experts per chunk
 
   // weight double buffer as two objects, so that the compiler can tell a read
   // of one from a copy in flight into the other
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // of the chunk's 16 biases per wave; a ring of NE slots, NE - 1 chunks ahead
   constexpr int ESLOT = kG32Rows * kG32Chunk + kG32Waves * kG32Chunk;
   constexpr int NE = 5;
-  __shared__ float ebuf[PASS2 ? 1 : NE][PASS2 ? 1 : ESLOT];
+  __shared__ float ebuf[PASS2 || CL ? 1 : NE][PASS2 || CL ? 1 : ESLOT];
   __shared__ float thrbuf[PASS2 ? kG32Rows : 1];  // pass 2: each row's k-th logit
   // pass 2: each wave's copy of a chunk's 16 biases, double-buffered by chunk parity
   __shared__ __attribute__((aligned(16))) float bbuf[PASS2 ? 2 : 1][PASS2 ? kG32Waves * kG32Chunk : 1];
@@ -139,13 +143,14 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // land within a pass, the noise draws have NE - 2 more.
   // this workgroup's range of expert chunks (all of them unless split); the
   // copy sources below start at its first chunk, c counts from there
-  const ChunkRange cr = chunk_range((n + EC - 1) / EC);
+  const ChunkRange cr = chunk_range((n + EX - 1) / EX);
   const int nchunks = cr.count;
   const bf16* wlane =
-      (clean_lane ? wg : wn) + ((int64_t)cr.c0 * EC + (l32 & 15)) * D + hi * UE;
+      CL ? wg + ((int64_t)cr.c0 * EX + l32) * D + hi * UE
+         : (clean_lane ? wg : wn) + ((int64_t)cr.c0 * EC + (l32 & 15)) * D + hi * UE;
   auto dma = [&](int c, U16* dst) {
-    const bf16* src = wlane + (int64_t)c * EC * D;
-    if constexpr (PASS2) {
+    const bf16* src = wlane + (int64_t)c * EX * D;
+    if constexpr (PASS2 || CL) {
 #pragma unroll
       for (int i = 0; i < DMA_PER_WAVE; ++i) {
         const int kb = wave + kG32Waves * i;
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   }
   constexpr int EPS_COPIES = 5;  // per wave and chunk: 4 row groups, 1 bias copy
   auto dma_eps = [&](int c, int b) {
-    if (wave >= 4) {
+    if (!CL && wave >= 4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float* src = elane[i] + c * EC;
@@ -238,14 +243,15 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // Pass 1: insert the lane's 8 values of chunk `chunk` (experts in
   // increasing order) into its token's list; any lane with a candidate makes
   // the wave run the insertions, which become rare once the lists are warm.
-  auto insert_pairs = [&](const float (&hv)[8], int chunk) {
+  auto insert_pairs = [&](const auto& hv, int chunk) {
+    constexpr int NV = CL ? 16 : 8;
     bool cand = false;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) cand |= hv[i] > lv[L - 1];
+    for (int i = 0; i < NV; ++i) cand |= hv[i] > lv[L - 1];
     if (__any(cand)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        insert_new<L>(lv, li, hv[i], (cr.c0 + chunk) * EC + 8 * (i / 4) + 4 * hi + (i % 4));
+      for (int i = 0; i < NV; ++i)
+        insert_new<L>(lv, li, hv[i], (cr.c0 + chunk) * EX + 8 * (i / 4) + 4 * hi + (i % 4));
     }
   };
 
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   f32x16 accs[2];
   dma(0, wbuf0);
   if (nchunks > 1) dma(1, wbuf1);
-  if constexpr (!PASS2) {
+  if constexpr (!PASS2 && !CL) {
     for (int c = 0; c < NE - 1 && c < nchunks; ++c) dma_eps(c, c);
   }
   if constexpr (PASS2) dma_bias(0, 0);
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
     if (c + 2 < nchunks) dma(c + 2, wfill);
     asm volatile("" ::: "memory");
-    if constexpr (!PASS2) {
+    if constexpr (!PASS2 && !CL) {
       if (c + NE - 1 < nchunks) dma_eps(c + NE - 1, (c + NE - 1) % NE);
     }
 
@@ -384,13 +390,16 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       // then the next chunk's products with this chunk's noisy logits woven
       // in (one after every eighth of the products); the insertions, which
       // branch, follow the products.
-      const float* er = &ebuf[c % NE][(wave * 32 + l32) * EC];
-      const int sw = (l32 >> 1) & 3;  // the row's group swizzle
-      const f32x4 e0 = *reinterpret_cast<const f32x4*>(er + 4 * (hi ^ sw));
-      const f32x4 e1 = *reinterpret_cast<const f32x4*>(er + 4 * ((2 + hi) ^ sw));
-      const float* bp = &ebuf[c % NE][kG32Rows * EC + wave * EC + 4 * hi];
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(bp + 8);
+      f32x4 e0{}, e1{}, b0{}, b1{};
+      if constexpr (!CL) {
+        const float* er = &ebuf[c % NE][(wave * 32 + l32) * EC];
+        const int sw = (l32 >> 1) & 3;  // the row's group swizzle
+        e0 = *reinterpret_cast<const f32x4*>(er + 4 * (hi ^ sw));
+        e1 = *reinterpret_cast<const f32x4*>(er + 4 * ((2 + hi) ^ sw));
+        const float* bp = &ebuf[c % NE][kG32Rows * EC + wave * EC + 4 * hi];
+        b0 = *reinterpret_cast<const f32x4*>(bp);
+        b1 = *reinterpret_cast<const f32x4*>(bp + 8);
+      }
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       typedef const __attribute__((address_space(3))) u32x4* LdsPtr;
       uint32_t base = (uint32_t)(uintptr_t)(wnext + lane);
@@ -405,7 +414,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       for (int j = 0; j < 16; ++j) an[j] = 0.f;
       constexpr int MPE = NKB / 8;
       static_assert(NKB % 8 == 0, "whole K-blocks per noisy logit");
-      float hv[8];
+      float hv[CL ? 16 : 8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -416,26 +425,41 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
           if (kb + FPF < NKB) f[kb % FPF] = bl[(kb + FPF) * 64];
           Mfma<bf16>::k32(an, cur, xa[kb]);
         }
-        const float eps = i < 4 ? e0[i] : e1[i - 4];
-        const float bias = i < 4 ? b0[i] : b1[i - 4];
-        hv[i] = fmaf(eps, softplus_f(acc[8 + i]) + p.floor, acc[i] + bias);
+        if constexpr (!CL) {
+          const float eps = i < 4 ? e0[i] : e1[i - 4];
+          const float bias = i < 4 ? b0[i] : b1[i - 4];
+          hv[i] = fmaf(eps, softplus_f(acc[8 + i]) + p.floor, acc[i] + bias);
+        }
       }
-      constexpr int V = (kG32HValu + MPE - 1) / MPE;
-      __builtin_amdgcn_sched_group_barrier(0x100, FPF, 0);
+      if constexpr (CL) {
+        // noise-free, no bias: H is the clean logit
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (kb + FPF < NKB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+        for (int i = 0; i < 16; ++i) hv[i] = acc[i];
+        __builtin_amdgcn_sched_group_barrier(0x100, FPF, 0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (kb + FPF < NKB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        constexpr int V = (kG32HValu + MPE - 1) / MPE;
+        __builtin_amdgcn_sched_group_barrier(0x100, FPF, 0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (kb + FPF < NKB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (SCORES) {
         // batchwise gating: the 8 scores to their experts' rows; the 32 lanes
         // of each half write 128 contiguous bytes per expert
         if (srow >= 0) {
-          float* dst = p.scores + (int64_t)((cr.c0 + c) * EC + 4 * hi) * p.sld + srow;
+          float* dst = p.scores + (int64_t)((cr.c0 + c) * EX + 4 * hi) * p.sld + srow;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) dst[(int64_t)(8 * (i / 4) + (i % 4)) * p.sld] = hv[i];
+          for (int i = 0; i < (CL ? 16 : 8); ++i)
+            dst[(int64_t)(8 * (i / 4) + (i % 4)) * p.sld] = hv[i];
         }
       } else {
         if constexpr (SMX) es = expsum_add(es, hv);
@@ -449,11 +473,11 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     // c + NE - 1 in flight (copies complete in issue order, so the count
     // covers everything older).
     static_assert(NE == 5, "the waits below count NE - 2 chunks of noise copies");
-    if (!PASS2 && wave >= 4 && c + 4 < nchunks) {
+    if (!PASS2 && !CL && wave >= 4 && c + 4 < nchunks) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * EPS_COPIES) : "memory");
-    } else if (!PASS2 && wave >= 4 && c + 3 < nchunks) {
+    } else if (!PASS2 && !CL && wave >= 4 && c + 3 < nchunks) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * EPS_COPIES) : "memory");
-    } else if (!PASS2 && wave >= 4 && c + 2 < nchunks) {
+    } else if (!PASS2 && !CL && wave >= 4 && c + 2 < nchunks) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(EPS_COPIES) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
