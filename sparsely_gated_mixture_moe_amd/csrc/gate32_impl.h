@@ -51,8 +51,9 @@ struct IntConst {
   static constexpr int value = V;
 };
 
-// Biases of a gate without one: every chunk copies these 16 zeros.
-__device__ const float kZeroBias[kG32Chunk] = {};
+// Biases of a gate without one: every chunk copies these zeros (16, or 32 in
+// the clean-only mode).
+__device__ const float kZeroBias[2 * kG32Chunk] = {};
 
 // Vector instructions of one Load-pass pair (Softplus, Phi) and of one noisy
 // logit of the selection pass (Softplus, noise, bias): the scheduler spreads
@@ -85,7 +86,8 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   __shared__ float ebuf[PASS2 || CL ? 1 : NE][PASS2 || CL ? 1 : ESLOT];
   __shared__ float thrbuf[PASS2 ? kG32Rows : 1];  // pass 2: each row's k-th logit
   // pass 2: each wave's copy of a chunk's 16 biases, double-buffered by chunk parity
-  __shared__ __attribute__((aligned(16))) float bbuf[PASS2 ? 2 : 1][PASS2 ? kG32Waves * kG32Chunk : 1];
+  // (CL: the same for a chunk's 32 biases)
+  __shared__ __attribute__((aligned(16))) float bbuf[PASS2 || CL ? 2 : 1][PASS2 || CL ? kG32Waves * EX : 1];
   __shared__ float red[PASS2 ? 2 : 1][kG32Waves][EC];
 
   const int tid = threadIdx.x;
@@ -166,14 +168,14 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   };
   const bool has_bias = p.bias != nullptr;
   // chunk c's biases: bias_src + c * bias_step
-  const int bias_step = has_bias ? EC : 0;
+  const int bias_step = has_bias ? EX : 0;
   const float* bias_src = has_bias ? p.bias + cr.c0 * bias_step : kZeroBias;
   // Pass 2: lanes 0-3 copy chunk c's 16 biases into this wave's slot. A
   // copy, not a register load, so
   // that no compiler-inserted wait on the memory counter stalls the epilogue
   // behind the weight copies in flight.
   auto dma_bias = [&](int c, int slot) {
-    if (lane < 4) copy16_to_lds(bias_src + c * bias_step + 4 * lane, &bbuf[slot][wave * EC]);
+    if (lane < EX / 4) copy16_to_lds(bias_src + c * bias_step + 4 * lane, &bbuf[slot][wave * EX]);
   };
   // One chunk's products: 32 x 32 tile of (rows, clean|noise columns) over
   // the K-blocks. Fragments are read four ahead of their matrix product; the
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   if constexpr (!PASS2 && !CL) {
     for (int c = 0; c < NE - 1 && c < nchunks; ++c) dma_eps(c, c);
   }
-  if constexpr (PASS2) dma_bias(0, 0);
+  if constexpr (PASS2 || CL) dma_bias(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   mfma_chunk(wbuf0, accs[0]);
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     // draws and biases into ring slot (c + NE - 1) % NE (chunk c - 1's, used
     // in the last pass). The weights must land by the end of this pass; the
     // noise draws of chunk c + 1 too, those of later chunks may stay in flight.
-    if constexpr (PASS2) {
+    if constexpr (PASS2 || CL) {
       if (c + 1 < nchunks) dma_bias(c + 1, P ^ 1);
     }
     if (c + 2 < nchunks) dma(c + 2, wfill);
@@ -390,8 +392,15 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       // then the next chunk's products with this chunk's noisy logits woven
       // in (one after every eighth of the products); the insertions, which
       // branch, follow the products.
-      f32x4 e0{}, e1{}, b0{}, b1{};
-      if constexpr (!CL) {
+      f32x4 e0{}, e1{}, b0{}, b1{}, b2{}, b3{};
+      if constexpr (CL) {
+        // this lane's 16 biases: experts 4 hi + (0..3) of each group of 8
+        const float* br = &bbuf[P][wave * EX + 4 * hi];
+        b0 = *reinterpret_cast<const f32x4*>(br);
+        b1 = *reinterpret_cast<const f32x4*>(br + 8);
+        b2 = *reinterpret_cast<const f32x4*>(br + 16);
+        b3 = *reinterpret_cast<const f32x4*>(br + 24);
+      } else {
         const float* er = &ebuf[c % NE][(wave * 32 + l32) * EC];
         const int sw = (l32 >> 1) & 3;  // the row's group swizzle
         e0 = *reinterpret_cast<const f32x4*>(er + 4 * (hi ^ sw));
@@ -432,9 +441,12 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         }
       }
       if constexpr (CL) {
-        // noise-free, no bias: H is the clean logit
+        // noise-free: H is the clean logit plus the bias
 #pragma unroll
-        for (int i = 0; i < 16; ++i) hv[i] = acc[i];
+        for (int i = 0; i < 16; ++i) {
+          const f32x4& bq = i < 4 ? b0 : (i < 8 ? b1 : (i < 12 ? b2 : b3));
+          hv[i] = acc[i] + bq[i % 4];
+        }
         __builtin_amdgcn_sched_group_barrier(0x100, FPF, 0);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {

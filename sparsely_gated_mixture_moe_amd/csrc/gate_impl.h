@@ -639,12 +639,11 @@ hipError_t gate_dispatch_d(const GateLaunch& g, const GateParams& p, bool pass2,
 }  // namespace gate_detail
 
 // The 32x32 kernel (gate32_impl.h) takes bf16 x and weights, d in {128, 256,
-// 512}, and either training mode with n a multiple of 16, or inference
-// without a gate bias with n a multiple of 32 (chunks of 32 experts' clean
-// rows); it uses 256-row blocks instead of 128.
+// 512}, and n a multiple of 16 in training mode or of 32 in inference (chunks
+// of 32 experts' clean rows); it uses 256-row blocks instead of 128.
 inline bool gate_uses_g32(const GateLaunch& g) {
   return g.x_dt == kBF16 && g.w_dt == kBF16 && (g.d == 128 || g.d == 256 || g.d == 512) &&
-         (g.train ? g.n % 16 == 0 : (g.bias == nullptr && g.n % 32 == 0));
+         g.n % (g.train ? 16 : 32) == 0;
 }
 
 hipError_t gate_dispatch_bf16(const GateLaunch& g, const gate_detail::GateParams& p, bool pass2, hipStream_t s);

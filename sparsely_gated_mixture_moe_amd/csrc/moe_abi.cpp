@@ -140,10 +140,7 @@ Layout layout(const moe_dims* d, const moe_gate_opts* o) {
     g.x_dt = to_dt(d->act_dtype);
     g.w_dt = to_dt(d->gate_dtype);
     g.train = train;
-    const size_t plain = moe::gate_cand_bytes(g);
-    // a gate with a bias may run the other kernel (another tile and chunk size)
-    g.bias = reinterpret_cast<const float*>(alignof(float));
-    return std::max(plain, moe::gate_cand_bytes(g));
+    return moe::gate_cand_bytes(g);
   };
   L.gate_bytes = align_up(o ? cand(o->train) : std::max(cand(0), cand(1)));
   // moe_forward
