@@ -1,6 +1,7 @@
 // Noisy top-k gating and the Load pass on 32x32x16 bf16 matrix-core tiles,
-// for bf16 x and gate weights with d_model >= 128, n a multiple of 16, in
-// training mode (the configuration of the large workloads). Same mathematics
+// for bf16 x and gate weights with d_model >= 128: training mode with n a
+// multiple of 16, or the noise-free selection (inference) with n a multiple
+// of 32, where a chunk is 32 experts' clean rows (template flag CL). Same mathematics
 // as gate_impl.h (sections "Noisy top-k gating", eqs 3-5, and "A differentiable count of
 // examples", eqs 8-10); different data movement:
 //
