@@ -142,6 +142,40 @@ def test_gate_switch_order(case):
         assert np.all(to_host(gate).sum(1) <= 1.0 + 1e-6)
 
 
+# Inference on the 32x32 kernel (n a multiple of 32: chunks of 32 experts'
+# clean rows), with and without a gate bias, both gate orders, whole and split
+# sweeps.
+CLEAN32_CASES = [
+    ("zipf_bf16_n256", {"tokens": 1500}, 0),
+    ("zipf_bf16_n256", {"tokens": 1500}, 1),
+    ("zipf_bf16_n256", {"tokens": 3}, 0),
+    ("flat_bf16_n4096", {"tokens": 3, "n_experts": 512}, 1),
+    ("flat_bf16_n4096", {"tokens": 257, "n_experts": 96, "k": 8, "d_model": 256}, 0),
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 32, "k": 1, "d_model": 128}, 1),
+]
+
+
+@pytest.mark.parametrize("case", CLEAN32_CASES,
+                         ids=[_gate_ids(c[:2]) + f"-order{c[2]}" for c in CLEAN32_CASES])
+def test_gate_clean32(case):
+    name, kw, order = case
+    w = wl(name, **kw)
+    announce(f"moe_gate clean-only 32x32 {w.name} {kw} gate_order={order}")
+    inp = dg.make_inputs(w, experts=False, with_bias=True)
+    ref = oracle.gate(inp, w.k, train=False, noise_floor=FLOOR, want_logits=True,
+                      gate_order=order)
+    g = gpu_inputs(inp)
+    dims = moe.make_dims(w.tokens, w.d_model, 128, w.n_experts, w.k, moe.MOE_BF16, moe.MOE_BF16,
+                         moe.MOE_BF16)
+    ws = moe.workspace(dims, moe.make_opts(False, FLOOR, gate_order=order), g["x"].device)
+    for w_s in (ws, None):
+        idx, gate, thr = moe.moe_gate(g["x"], g["w_gate"], g["w_noise"], None, w.k, train=False,
+                                      noise_floor=FLOOR, gate_bias=g.get("gate_bias"),
+                                      gate_order=order, ws=w_s)
+        torch.cuda.synchronize()
+        check_gating(ref, ref["H"], to_host(idx), to_host(gate), to_host(thr), gate_order=order)
+
+
 def test_forward_switch_order():
     """The whole forward with gate_order 1 and k = 1 (Switch), fp32 so that y
     is held to the fp32 bar: y against the oracle's expert outputs weighted by
