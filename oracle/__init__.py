@@ -47,12 +47,14 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_threads.restype = _I
+        lib.oracle_set_threads.argtypes = [_I]
+        lib.oracle_set_threads.restype = None
         lib.oracle_softplus.argtypes = [_D]
         lib.oracle_softplus.restype = _D
         lib.oracle_phi.argtypes = [_D]
         lib.oracle_phi.restype = _D
-        lib.oracle_cv_squared.argtypes = [_I, _P]
-        lib.oracle_cv_squared.restype = _D
+        lib.oracle_cv2.argtypes = [_I, _P]
+        lib.oracle_cv2.restype = _D
         lib.oracle_gate.argtypes = [_I64, _P, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D, _I,
                                     _P, _P, _P, _P, _P, _P]
         lib.oracle_load.argtypes = [_I64, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D, _I, _P]
@@ -100,6 +102,11 @@ def threads() -> int:
     return _load().oracle_threads()
 
 
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's later calls from this thread."""
+    _load().oracle_set_threads(int(n))
+
+
 def softplus(u: float) -> float:
     return _load().oracle_softplus(float(u))
 
@@ -108,9 +115,10 @@ def phi(z: float) -> float:
     return _load().oracle_phi(float(z))
 
 
-def cv_squared(v) -> float:
+def cv2(v) -> float:
+    """CV^2 of a vector with the population variance (eqs 7 and 11)."""
     v = np.ascontiguousarray(v, dtype=np.float64)
-    return _load().oracle_cv_squared(v.size, v.ctypes.data)
+    return _load().oracle_cv2(v.size, v.ctypes.data)
 
 
 class _Gate:
@@ -258,7 +266,7 @@ def route(topk_idx: np.ndarray, topk_gate: np.ndarray, n: int,
 def forward(inp: Dict[str, np.ndarray], k: int, train: bool = True, noise_floor: float = 1e-2,
             w_importance: float = 0.1, w_load: float = 0.1,
             decide_fp32: bool = True) -> Dict[str, np.ndarray]:
-    """The whole forward pass of the implementation notes on the batch."""
+    """The layer's forward pass on the batch: eqs 1 and 3-11."""
     g = _Gate(inp, train)
     w1, b1, w2, b2, e_dt, h = _experts(inp)
     B, d, n = g.B, g.d, g.n
@@ -351,19 +359,26 @@ def hier_gate(inp: Dict[str, np.ndarray], k1: int, k2: int, rows: Optional[Seque
 
 def hier_forward(inp: Dict[str, np.ndarray], k1: int, k2: int, train: bool = True,
                  noise_floor: float = 1e-2, w_importance: float = 0.1, w_load: float = 0.1,
-                 decide_fp32: bool = True, force1=None, force2=None) -> Dict[str, np.ndarray]:
+                 decide_fp32: bool = True, force1=None, force2=None,
+                 with_y: bool = True) -> Dict[str, np.ndarray]:
     """The hierarchical layer's forward pass on the whole batch.
 
     Returns y [B, d], leaf_idx/leaf_gate [B, k1*k2], imp1/load1/rows1 [a], load2 [a*b],
-    importance/load [a*b] (leaf) and losses [3].
+    importance/load [a*b] (leaf) and losses [3]. ``with_y=False`` skips the
+    experts (no y; ``inp`` then needs no expert weights).
     """
     g = _HierGate(inp, k1, k2, train)
-    w1, b1, w2, b2, e_dt, h = _experts(inp)
+    if with_y:
+        w1, b1, w2, b2, e_dt, h = _experts(inp)
+    else:
+        w1 = b1 = w2 = b2 = None
+        e_dt, h = 0, 0
     n = g.a * g.b
     K = k1 * k2
     f1 = _forced(force1, (g.B, k1))
     f2 = _forced(force2, (g.B, k1, k2))
-    out = {"y": np.empty((g.B, g.d)), "leaf_idx": np.empty((g.B, K), np.int32),
+    out = {"y": np.empty((g.B, g.d)) if with_y else None,
+           "leaf_idx": np.empty((g.B, K), np.int32),
            "leaf_gate": np.empty((g.B, K)), "imp1": np.empty(g.a), "load1": np.empty(g.a),
            "rows1": np.empty(g.a), "load2": np.empty(n), "importance": np.empty(n),
            "load": np.empty(n), "losses": np.empty(3)}
@@ -371,9 +386,11 @@ def hier_forward(inp: Dict[str, np.ndarray], k1: int, k2: int, train: bool = Tru
         g.B, g.d, h, g.a, g.b, k1, k2, *g.args(), int(train), float(noise_floor),
         int(decide_fp32), _ptr(f1), _ptr(f2), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), e_dt,
         float(w_importance), float(w_load),
-        *[out[key].ctypes.data for key in ("y", "leaf_idx", "leaf_gate", "imp1", "load1",
-                                            "rows1", "load2", "importance", "load", "losses")])
+        *[_ptr(out[key]) for key in ("y", "leaf_idx", "leaf_gate", "imp1", "load1",
+                                     "rows1", "load2", "importance", "load", "losses")])
     _check(rc, "hier_forward")
+    if not with_y:
+        del out["y"]
     return out
 
 
@@ -454,7 +471,7 @@ def batchwise_forward(inp: Dict[str, np.ndarray], m: int, train: bool = True,
     imp = G.sum(axis=0)
     load = counts.astype(np.float64)
     return {"y": y, "H": H, "keep": keep, "counts": counts, "G": G, "importance": imp,
-            "load": load, "losses": np.array([cv_squared(imp), cv_squared(load)])}
+            "load": load, "losses": np.array([cv2(imp), cv2(load)])}
 
 
 def _widen(a) -> np.ndarray:

@@ -8,9 +8,11 @@
 // Networks" (intuitivepapers.ai explainer of Shazeer et al., 2017), sections
 // "How a mixture-of-experts layer works" (eq 1), "Noisy top-k gating"
 // (eqs 2-5), "Why experts collapse, and the balancing losses" (eqs 6-7 and the
-// coefficient of variation), "A differentiable count of examples" (eqs 8-11),
-// "Hierarchical MoE" (eq 12) and "Implementation notes" (the forward-pass
-// pseudo-code, whose step order is followed here).
+// coefficient of variation), "A differentiable count of examples" (eqs 8-11)
+// and "Hierarchical MoE" (eq 12). Each function below evaluates one of those
+// definitions directly: per token, the logits of eq 4, the kept set and
+// softmax of eqs 3 and 5, the weighted expert sum of eq 1, P of eq 9; per
+// batch, the sums of eqs 6 and 10 and the CV^2 of eqs 7 and 11.
 //
 // Arithmetic: every sum and transcendental in double precision. Inputs are the
 // same rounded fp32 or bf16 values the GPU reads, widened exactly. Loops are
@@ -19,8 +21,8 @@
 // thread count.
 //
 // Readings where the pages are open (each also listed in the design notes):
-//  * noise std = Softplus(x.W_noise) + noise_floor; the implementation notes
-//    add a floor of 0.01, eq 4 has none, so the floor is a parameter.
+//  * noise std = Softplus(x.W_noise) + noise_floor; the explainer's code
+//    adds a floor of 0.01, eq 4 has none, so the floor is a parameter.
 //  * Selection order: larger noisy logit first, equal logits -> lower expert
 //    index first. The selection is decided on the logits rounded to fp32 (the
 //    precision the GPU decides in) when decide_fp32 != 0; every value that is
@@ -134,7 +136,7 @@ void gate_row(const GateArgs& g, int64_t t, RowGate& r, std::vector<double>& xro
       r.H[i] = c;
     }
   }
-  // top_k(H, k+1): rank experts by logit, larger first, ties to the lower index.
+  // Rank the experts by noisy logit, larger first, ties to the lower index.
   std::iota(r.order.begin(), r.order.end(), 0);
   if (g.decide_fp32) {
     std::vector<float> key(n);
@@ -158,12 +160,14 @@ void gate_row(const GateArgs& g, int64_t t, RowGate& r, std::vector<double>& xro
   for (int j = 0; j < k; ++j) r.gate[j] /= z;
 }
 
-// Eqs 8-9: probability that expert i stays in the top k under a fresh draw of
-// its own noise, the other experts' noise held fixed.
-inline double prob_in_top_k(const GateArgs& g, const RowGate& r, int i) {
+// P(x, i) of eq 9: the probability that expert i is among the k largest
+// logits under a fresh draw of its own noise, the other experts' noise held
+// fixed (eq 8). The logit it has to beat is the k-th largest of the other
+// experts' logits: v_{k+1} when i itself is one of the k kept, v_k otherwise.
+inline double p_eq9(const GateArgs& g, const RowGate& r, int i) {
   if (!g.train) return r.in_top[i] ? 1.0 : 0.0;
-  const double thr = r.in_top[i] ? r.vk1 : r.vk;  // kth_excluding(H, k, i)
-  return Phi((r.clean[i] - thr) / r.sigma[i]);
+  const double to_beat = r.in_top[i] ? r.vk1 : r.vk;
+  return Phi((r.clean[i] - to_beat) / r.sigma[i]);
 }
 
 // E_i(x) for one token row: ReLU(W1_i x + b1_i), then W2_i . hidden + b2_i.
@@ -187,7 +191,7 @@ void expert_apply(int d, int h, const double* xrow, const void* w1, const void* 
 }
 
 // Squared coefficient of variation with the population variance.
-double cv_squared(int n, const double* v) {
+double cv2(int n, const double* v) {
   if (n <= 1) return 0.0;
   double mean = 0.0;
   for (int i = 0; i < n; ++i) mean += v[i];
@@ -295,10 +299,13 @@ extern "C" {
 
 int oracle_version(void) { return 1; }
 int oracle_threads(void) { return omp_get_max_threads(); }
+// Threads of the oracle's later parallel regions on the calling thread (the
+// CPU baseline times it on one thread and on all host threads).
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 double oracle_softplus(double u) { return softplus(u); }
 double oracle_phi(double z) { return Phi(z); }
-double oracle_cv_squared(int n, const double* v) { return cv_squared(n, v); }
+double oracle_cv2(int n, const double* v) { return cv2(n, v); }
 
 // Gating for a list of token rows (rows == null: rows 0..nrows-1).
 // Outputs per listed row r (any may be null):
@@ -354,7 +361,7 @@ int oracle_load(int64_t B, int d, int n, int k, const void* x, int x_dt, const v
       double* acc = part.data() + b * n;
       for (int64_t t = b * kRowBlock; t < std::min(B, (b + 1) * kRowBlock); ++t) {
         gate_row(g, t, r, xrow, wrow);
-        for (int i = 0; i < n; ++i) acc[i] += prob_in_top_k(g, r, i);
+        for (int i = 0; i < n; ++i) acc[i] += p_eq9(g, r, i);
       }
     }
   }
@@ -413,8 +420,9 @@ int oracle_expert_pairs(int64_t npairs, const int64_t* tokens, const int32_t* ex
   return 0;
 }
 
-// The per-expert row sets nonzero(G[:, e]) of the implementation notes, made
-// stable: segment e lists the tokens routed to expert e in ascending order.
+// Each expert's batch (eq 1 evaluates expert e only on the tokens whose gate
+// for e is nonzero), in a fixed order: segment e lists the tokens that kept
+// expert e, in ascending token order.
 // Also Importance (eq 6): imp[e] = sum over those tokens of their gate.
 //   counts [n], offsets [n+1], perm_token [B*k], perm_gate [B*k],
 //   slot_pos [B*k] (slot_pos[t*k + j] = position of (t, j) in the permutation).
@@ -458,7 +466,8 @@ int oracle_route(int64_t B, int n, int k, const int32_t* topk_idx, const double*
   return 0;
 }
 
-// The whole forward pass of the implementation notes on a batch of B tokens.
+// The layer's forward pass on a batch of B tokens: eqs 3-5 per token, eq 1
+// per token, eqs 6-7 and 9-11 over the batch.
 // Outputs (any may be null except y):
 //   y [B][d]; topk_idx/topk_gate [B][k]; thresh [B][2]; importance/load [n];
 //   losses[3] = {CV^2(Importance), CV^2(Load), w_imp*CV^2(Imp) + w_load*CV^2(Load)}.
@@ -470,7 +479,7 @@ int oracle_forward(int64_t B, int d, int h, int n, int k, const void* x, int x_d
                    double* importance, double* load, double* losses) {
   if (bad_args(B, d, n, k, train, eps) || h < 1 || !y) return 1;
   const GateArgs g = make_args(d, n, k, x, x_dt, wg, wn, w_dt, bg, eps, train, floor, decide_fp32);
-  // Gating: clean logits, noise std, noisy logits, top_k(H, k+1), softmax, G.
+  // Gating of every token (eqs 3-5) and its P(x_t, i) terms (eq 9).
   std::vector<int32_t> idx((size_t)B * k);
   std::vector<double> gate((size_t)B * k), thr((size_t)B * 2);
   std::vector<double> G((size_t)B * n, 0.0);
@@ -493,23 +502,25 @@ int oracle_forward(int64_t B, int d, int h, int n, int k, const void* x, int x_d
         thr[t * 2 + 1] = r.vk1;
         // P(x_t, i) of eq 9, accumulated for eq 10 in this row block
         double* acc = load_part.data() + b * n;
-        for (int i = 0; i < n; ++i) acc[i] += prob_in_top_k(g, r, i);
+        for (int i = 0; i < n; ++i) acc[i] += p_eq9(g, r, i);
       }
     }
   }
-  // Expert loop: y[rows] += G[rows, i] * E_i(X[rows]) for each expert in turn.
-  for (int64_t q = 0; q < B * d; ++q) y[q] = 0.0;
-  for (int i = 0; i < n; ++i) {
+  // Eq 1 per token: y_t = sum of G(x_t)_i * E_i(x_t) over the experts with a
+  // nonzero gate, in ascending expert index.
 #pragma omp parallel
-    {
-      std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h), eo(d);
+  {
+    std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h), eo(d);
 #pragma omp for schedule(dynamic, 8)
-      for (int64_t t = 0; t < B; ++t) {
+    for (int64_t t = 0; t < B; ++t) {
+      double* yr = y + t * d;
+      for (int c = 0; c < d; ++c) yr[c] = 0.0;
+      widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+      for (int i = 0; i < n; ++i) {
         const double gi = G[t * n + i];
         if (gi == 0.0) continue;
-        widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
         expert_apply(d, h, xrow.data(), w1, b1, w2, b2, e_dt, i, eo.data(), hid, wrow);
-        for (int c = 0; c < d; ++c) y[t * d + c] += gi * eo[c];
+        for (int c = 0; c < d; ++c) yr[c] += gi * eo[c];
       }
     }
   }
@@ -520,8 +531,8 @@ int oracle_forward(int64_t B, int d, int h, int n, int k, const void* x, int x_d
   // Load (eq 10): block partials in ascending block order.
   for (int64_t b = 0; b < nblk; ++b)
     for (int i = 0; i < n; ++i) ld[i] += load_part[b * n + i];
-  const double cv_imp = cv_squared(n, imp.data());
-  const double cv_load = cv_squared(n, ld.data());
+  const double cv_imp = cv2(n, imp.data());
+  const double cv_load = cv2(n, ld.data());
   if (topk_idx_out) std::copy(idx.begin(), idx.end(), topk_idx_out);
   if (topk_gate_out) std::copy(gate.begin(), gate.end(), topk_gate_out);
   if (thresh_out) std::copy(thr.begin(), thr.end(), thresh_out);
@@ -595,7 +606,8 @@ int oracle_hier_gate(int64_t nrows, const int64_t* rows, int d, int a, int b, in
 // The hierarchical layer's forward pass on a batch of B tokens (eq 12 read
 // from the prose; losses as in the header). force1/force2 as in
 // oracle_hier_gate (null: the oracle's own selections). Outputs (any may be
-// null except y), n = a*b leaves:
+// null; with y null the experts are not evaluated and w1/w2 may be null),
+// n = a*b leaves:
 //   y [B][d]; leaf_idx/leaf_gate [B][k1*k2];
 //   imp1/load1 [a] (primary gate's Importance and Load), rows1 [a] = |X_i|;
 //   load2 [a*b] (secondary Load of group i over X_i, at i*b + j);
@@ -609,7 +621,7 @@ int oracle_hier_forward(int64_t B, int d, int h, int a, int b, int k1, int k2, c
                         int32_t* leaf_idx, double* leaf_gate, double* imp1, double* load1,
                         double* rows1, double* load2, double* importance, double* load,
                         double* losses) {
-  if (bad_hier(B, d, a, b, k1, k2, train, eps1, eps2) || h < 1 || !y) return 1;
+  if (bad_hier(B, d, a, b, k1, k2, train, eps1, eps2) || (y && (h < 1 || !w1 || !w2))) return 1;
   const HierArgs ha = make_hier(d, a, b, k1, k2, x, x_dt, wg1, wn1, wg2, wn2, w_dt, eps1, eps2,
                                 train, floor, decide_fp32);
   const int K = k1 * k2;
@@ -634,13 +646,13 @@ int oracle_hier_forward(int64_t B, int d, int h, int a, int b, int k1, int k2, c
           bad = 1;
           continue;
         }
-        for (int i = 0; i < a; ++i) acc1[i] += prob_in_top_k(ha.g1, hr.r1, i);
+        for (int i = 0; i < a; ++i) acc1[i] += p_eq9(ha.g1, hr.r1, i);
         for (int r = 0; r < k1; ++r) {
           const int grp = hr.r1.order[r];
           s1[t * k1 + r] = grp;
           g1[t * k1 + r] = hr.r1.gate[r];
           // the secondary gate of group grp sees this token as one of X_grp
-          for (int j = 0; j < b; ++j) acc2[grp * b + j] += prob_in_top_k(ha.g2, hr.r2[r], j);
+          for (int j = 0; j < b; ++j) acc2[grp * b + j] += p_eq9(ha.g2, hr.r2[r], j);
           for (int j = 0; j < k2; ++j) {
             idx[t * K + r * k2 + j] = grp * b + hr.r2[r].order[j];
             gate[t * K + r * k2 + j] = hr.r1.gate[r] * hr.r2[r].gate[j];
@@ -651,8 +663,8 @@ int oracle_hier_forward(int64_t B, int d, int h, int a, int b, int k1, int k2, c
   }
   if (bad) return 3;
   // eq 12: y_t = sum over the token's leaves, ascending leaf id, of gate * E_leaf(x_t)
-#pragma omp parallel
-  {
+#pragma omp parallel if (y != nullptr)
+  if (y) {
     std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h), eo(d);
     std::vector<std::pair<int32_t, double>> lv(K);
 #pragma omp for schedule(dynamic, 4)
@@ -684,8 +696,8 @@ int oracle_hier_forward(int64_t B, int d, int h, int a, int b, int k1, int k2, c
   for (int i = 0; i < a; ++i)
     for (int j = 0; j < b; ++j)
       ld[i * b + j] = r1[i] > 0.0 ? l1[i] * l2[i * b + j] / r1[i] : 0.0;
-  const double cv_imp = cv_squared(n, imp.data());
-  const double cv_load = cv_squared(n, ld.data());
+  const double cv_imp = cv2(n, imp.data());
+  const double cv_load = cv2(n, ld.data());
   if (leaf_idx) std::copy(idx.begin(), idx.end(), leaf_idx);
   if (leaf_gate) std::copy(gate.begin(), gate.end(), leaf_gate);
   if (imp1) std::copy(i1.begin(), i1.end(), imp1);

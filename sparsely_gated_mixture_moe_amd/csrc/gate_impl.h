@@ -2,8 +2,8 @@
 // gate_bf16.hip, gate_bf16x_f32w.hip and gate_f32.hip.
 #pragma once
 
-// Noisy top-k gating on gfx950 (section "Noisy top-k gating", eqs 3-5, and the
-// forward-pass listing of "Implementation notes"), and the Load pass of
+// Noisy top-k gating on gfx950 (section "Noisy top-k gating", eqs 3-5, with the
+// noise floor of the explainer's code as a parameter), and the Load pass of
 // "A differentiable count of examples" (eqs 8-10), which shares its main loop.
 //
 // One workgroup owns 128 token rows (8 waves x 16 rows) and sweeps all n

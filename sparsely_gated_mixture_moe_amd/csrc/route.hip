@@ -1,5 +1,5 @@
-// Routing on gfx950: the per-expert row sets of the forward-pass listing
-// ("Implementation notes": rows = nonzero(G[:, i])) laid out as one contiguous
+// Routing on gfx950: each expert's batch (the tokens whose gate for it is
+// nonzero, the only ones eq 1 evaluates it on) laid out as one contiguous
 // block per expert, which is how a single GPU keeps each expert's matrix
 // products as large as the batch allows (section "Keeping each expert's batch
 // large"). It is a stable counting sort of the B*k (token, slot) pairs by

@@ -95,7 +95,7 @@ def test_importance_worked_example():
     assert out["losses"][0] == pytest.approx(g["printed_cv2"], abs=g["printed_precision"])
     assert out["losses"][0] == pytest.approx(g["printed_mean_sq_dev"] / g["printed_mean"] ** 2, rel=1e-5)
     assert out["losses"][2] == pytest.approx(g["printed_loss"], abs=g["printed_precision"])
-    assert oracle.cv_squared(g["importance"]) == pytest.approx(0.30, rel=1e-12)
+    assert oracle.cv2(g["importance"]) == pytest.approx(0.30, rel=1e-12)
 
 
 def _load_case(clean, u, eps, k, floor=0.0):
@@ -394,7 +394,7 @@ def test_load_probability_matches_monte_carlo():
 
 def test_load_in_and_out_thresholds():
     """The selected expert is measured against the (k+1)-th logit, the others
-    against the k-th (eq 8 with kth_excluding)."""
+    against the k-th (eq 8: the k-th largest of the other logits)."""
     u = math.log(math.expm1(0.5))
     inp, floor = _load_case([2.0, 1.3, 0.2], [u, u, u], [0.0, 0.0, 0.0], 1)
     load = oracle.load(inp, 1, noise_floor=floor)
@@ -424,16 +424,16 @@ def test_inference_load_is_the_hard_count():
 # Importance, CV^2 and the losses
 # --------------------------------------------------------------------------
 
-def test_cv_squared_closed_forms():
+def test_cv2_closed_forms():
     v = np.array([3.0, 1.0])
-    assert oracle.cv_squared(v) == pytest.approx(((3 - 1) / (3 + 1)) ** 2, rel=1e-15)
+    assert oracle.cv2(v) == pytest.approx(((3 - 1) / (3 + 1)) ** 2, rel=1e-15)
     rng = np.random.default_rng(15)
     w = rng.uniform(0.1, 5, 37)
-    assert oracle.cv_squared(2 * w) == pytest.approx(oracle.cv_squared(w), rel=1e-13)
-    assert oracle.cv_squared(np.full(9, 4.2)) == pytest.approx(0.0, abs=1e-28)
-    assert oracle.cv_squared([5.0]) == 0.0
-    assert oracle.cv_squared([0.0, 0.0]) == 0.0
-    assert oracle.cv_squared(w) == pytest.approx(np.var(w) / np.mean(w) ** 2, rel=1e-12)
+    assert oracle.cv2(2 * w) == pytest.approx(oracle.cv2(w), rel=1e-13)
+    assert oracle.cv2(np.full(9, 4.2)) == pytest.approx(0.0, abs=1e-28)
+    assert oracle.cv2([5.0]) == 0.0
+    assert oracle.cv2([0.0, 0.0]) == 0.0
+    assert oracle.cv2(w) == pytest.approx(np.var(w) / np.mean(w) ** 2, rel=1e-12)
 
 
 def test_importance_sums_to_batch_and_k1_is_counts():
