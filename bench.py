@@ -7,11 +7,16 @@ weighted sum, Importance/Load and both losses, training mode) over a batch of
 fp32 accumulation and fp32 gate math. Inputs are synthetic (seeded Philox
 normals, weights ~ N(0, 1/fan_in)) and resident in HBM before timing starts.
 
-Prints one JSON line: tokens/s, the expert-FFN kernel's achieved HBM bandwidth
-against the 8 TB/s peak (its duration from timing events the library records
-around that kernel inside the timed steps, on the step's stream), per-stage
-times of each entry point called on its own, and the oracle's CPU throughput
-on a bounded sample of the same workload.
+Prints one JSON line: tokens/s from the median of the timed steps (HIP events
+around each step on the stream the library launches on); the expert-FFN
+kernel against its own roof (HBM bandwidth where streaming the experts'
+weights bounds it, the MFMA peak of its dtype where its arithmetic does; its
+duration from timing events the library records around that kernel inside
+the timed steps); every stage, each entry point called on its own, against
+its own roof (gate and Load passes: MFMA; expert FFN: the larger of its two
+ideal times; combine: HBM; route: latency, in microseconds); and the oracle's
+CPU throughput on a bounded sample of the same workload (all host threads),
+plus on one thread for the two fp32 workloads.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 """
@@ -42,6 +47,58 @@ def to_device(a, torch, np):
     return torch.from_numpy(a).cuda()
 
 
+def time_steps(step, steps, torch):
+    """Times `steps` calls of step() with a pair of HIP events around each one
+    on the current stream (the stream the library launches on), the events of
+    consecutive steps back to back. Returns (per-step ms list, total ms from
+    the first event to the last)."""
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(st)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(st)
+    ev[-1].synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return per, ev[0].elapsed_time(ev[-1])
+
+
+def median(v):
+    v = sorted(v)
+    m = len(v) // 2
+    return v[m] if len(v) % 2 else 0.5 * (v[m - 1] + v[m])
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def roof(name, ms, flops=0.0, nbytes=0.0, flops_peak=None, bound=None):
+    """A stage's time against its own roof: achieved TFLOP/s over the MFMA
+    peak of its dtype and achieved GB/s over the HBM peak; `bound` names the
+    roof that limits it (by default the larger of the two ideal times)."""
+    r = {"ms": ms}
+    t_mfma = flops / (flops_peak * 1e12) * 1e3 if flops and flops_peak else 0.0
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3 if nbytes else 0.0
+    if flops:
+        r.update(alg_flops=flops, tflops=flops / (ms * 1e-3) / 1e12, mfma_peak_tflops=flops_peak,
+                 mfma_frac=flops / (ms * 1e-3) / (flops_peak * 1e12))
+    if nbytes:
+        r.update(alg_bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+                 hbm_frac=nbytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9))
+    r["bound"] = bound or ("latency" if not (flops or nbytes) else
+                           "mfma" if t_mfma >= t_hbm else "hbm")
+    r["roof_ms"] = max(t_mfma, t_hbm)
+    r["frac"] = r["roof_ms"] / ms if r["roof_ms"] else None
+    return r
+
+
 def time_calls(fn, iters, torch):
     """Average device time of fn() over iters calls, bracketed by HIP events on
     the current stream (the stream the library launches on)."""
@@ -56,9 +113,9 @@ def time_calls(fn, iters, torch):
 
 
 # HBM bytes per ffn_kernel launch from the calibrated FETCH_SIZE + WRITE_SIZE
-# counters of the committed rocprofv3 summary; valid only while the kernel's
-# sources are byte-identical to those the counters were taken on.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ffn_kernel_flat_bf16_n4096_hbm_traffic.txt")
+# counters of the committed rocprofv3 summary of that workload; valid only
+# while the kernel's sources are byte-identical to those the counters were
+# taken on.
 FFN_SOURCES = ["sparsely_gated_mixture_moe_amd/csrc/ffn.hip",
                "sparsely_gated_mixture_moe_amd/csrc/device_common.h"]
 
@@ -66,7 +123,8 @@ FFN_SOURCES = ["sparsely_gated_mixture_moe_amd/csrc/ffn.hip",
 def profiled_traffic(workload):
     import hashlib
 
-    if workload != "flat_bf16_n4096" or not os.path.exists(TRAFFIC_PROFILE):
+    TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", f"ffn_kernel_{workload}_hbm_traffic.txt")
+    if not os.path.exists(TRAFFIC_PROFILE):
         return None
     fields = {}
     for line in open(TRAFFIC_PROFILE):
@@ -108,9 +166,45 @@ def cpu_baseline(w, inp, target_s):
         t = run(S)
     threads = oracle.threads()
     return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"oracle forward pass (fp64, {threads} OpenMP threads) on the first {S} "
                       f"tokens of the same workload: gating over all {w.n_experts} experts, "
                       f"expert FFNs, weighted sum, Importance/Load and losses; {t:.1f} s"}
+
+
+def cpu_single_thread(target_s):
+    """The oracle's forward pass on one host thread for the two fp32
+    workloads (256 tokens over 16 experts; 8192 tokens over 32 experts),
+    median of three runs on the whole batch or on its first S tokens, S grown
+    until one run takes about target_s seconds."""
+    import datagen as dg
+    import oracle
+
+    all_threads = oracle.threads()
+    oracle.set_threads(1)
+    res = {}
+    try:
+        for name in ("tiny_fp32", "flat_fp32_n32"):
+            w = dg.WORKLOADS[name]
+            inp = dg.make_inputs(w)
+
+            def run(S):
+                sub = dict(inp, x=inp["x"][:S], eps=inp["eps"][:S])
+                t0 = time.perf_counter()
+                oracle.forward(sub, w.k)
+                return time.perf_counter() - t0
+
+            S = min(w.tokens, 64)
+            t = run(S)
+            while t < 0.8 * target_s and S < w.tokens:
+                S = int(min(w.tokens, max(2 * S, S * 1.05 * target_s / max(t, 1e-3))))
+                t = run(S)
+            ts = sorted([t, run(S), run(S)])
+            res[name] = {"value": S / ts[1], "unit": "tokens/s", "cores": 1, "tokens": S,
+                         "median_of": 3, "seconds": ts[1]}
+    finally:
+        oracle.set_threads(all_threads)
+    return res
 
 
 def upload(w, name, shape, torch, dg, chunk=1 << 27):
@@ -168,20 +262,15 @@ def bench_hier(a, w):
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     moe.moe_ffn_timing(True)
     w0 = time.perf_counter()
-    e0.record(st)
-    for _ in range(a.steps):
-        step()
-    e1.record(st)
+    per_step, total_ms = time_steps(step, a.steps, torch)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     moe.moe_ffn_timing(False)
     ffn_n, ffn_total = moe.moe_ffn_timing_read()
-    ms_step = e0.elapsed_time(e1) / a.steps
-    log(f"{ms_step:.3f} ms/step")
+    ms_step = median(per_step)
+    log(f"{ms_step:.3f} ms/step median, {total_ms / a.steps:.3f} mean")
     # the leaf FFN on its own, on the step's routing
     dims = moe.make_dims(B, d, h, n, K, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_BF16)
     ws = moe.workspace(dims, moe.make_opts(), dev)
@@ -202,7 +291,7 @@ def bench_hier(a, w):
     ffn_ms = ffn_total / ffn_n  # the FFN kernel inside the timed steps
     achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
     gate_flops = 2.0 * B * d * 2 * ga + 2.0 * B * k1 * d * 2 * gb
-    step_flops = 2 * gate_flops + 4.0 * rows * d * h  # both gates twice (selection, Load) + FFN
+    step_flops = gate_flops + 4.0 * rows * d * h  # both gate levels once + FFN
     step_bytes = (B * d * 2 + B * ga * 4 + B * k1 * gb * 4 + 2 * ga * d * 2 + 2 * n * d * 2
                   + used * 2 * d * h * 2 + B * d * 2)
     result = {
@@ -220,7 +309,8 @@ def bench_hier(a, w):
                      "mfma_frac": 4.0 * rows * d * h / (ffn_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
         "step": {"alg_bytes": step_bytes, "alg_flops": step_flops,
                  "hbm_frac": step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
-                 "mfma_frac": step_flops / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
+                 "mfma_frac": step_flops / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                 "mean_ms": total_ms / a.steps},
         "stages_ms": stages, "wall_ms_per_step": 1000 * wall / a.steps,
         "cpu_baseline": None,
     }
@@ -244,20 +334,15 @@ def bench_batchwise(a, w, g, moe, torch):
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     moe.moe_ffn_timing(True)
     w0 = time.perf_counter()
-    e0.record(st)
-    for _ in range(a.steps):
-        step()
-    e1.record(st)
+    per_step, total_ms = time_steps(step, a.steps, torch)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     moe.moe_ffn_timing(False)
     ffn_n, ffn_total = moe.moe_ffn_timing_read()
-    ms_step = e0.elapsed_time(e1) / a.steps
-    log(f"{ms_step:.3f} ms/step")
+    ms_step = median(per_step)
+    log(f"{ms_step:.3f} ms/step median, {total_ms / a.steps:.3f} mean")
     cnt = f.counts.cpu().numpy()
     used, rows = int((cnt > 0).sum()), int(cnt.sum())
     ffn_bytes = used * 2 * d * h * 2 + 2 * rows * d * 2
@@ -283,7 +368,8 @@ def bench_batchwise(a, w, g, moe, torch):
                      "timed_launches": ffn_n},
         "step": {"alg_bytes": step_bytes, "alg_flops": step_flops,
                  "hbm_frac": step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
-                 "mfma_frac": step_flops / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
+                 "mfma_frac": step_flops / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                 "mean_ms": total_ms / a.steps},
         "wall_ms_per_step": 1000 * wall / a.steps,
         "cpu_baseline": None,
     }
@@ -376,28 +462,24 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"timing {a.steps} steps")
-    st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     moe.moe_ffn_timing(True)
     w0 = time.perf_counter()
-    e0.record(st)
-    for _ in range(a.steps):
-        step()
-    e1.record(st)
+    per_step, total_ms = time_steps(step, a.steps, torch)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     moe.moe_ffn_timing(False)
     ffn_n, ffn_total = moe.moe_ffn_timing_read()
-    ms_step = e0.elapsed_time(e1) / a.steps
-    log(f"{ms_step:.3f} ms/step (wall {1000 * wall / a.steps:.3f} ms/step)")
+    ms_step = median(per_step)
+    log(f"{ms_step:.3f} ms/step median, {total_ms / a.steps:.3f} mean "
+        f"(wall {1000 * wall / a.steps:.3f} ms/step)")
 
     # Stage times: each entry point on its own, on the routing of the step above.
     it = a.stage_iters
     route = moe.moe_route(topk_idx, topk_gate, n, d_model=d)
     ws = moe.workspace(f.dims, f.opts, dev)
     eo = torch.empty((B * k, d), dtype=g["x"].dtype, device=dev)
-    stages = {} if it <= 0 else {
+    stage_ms = {} if it <= 0 else {
         "gate": time_calls(lambda: moe.moe_gate(g["x"], g["w_gate"], g["w_noise"],
                                                 g["eps"] if a.train else None, k,
                                                 train=bool(a.train), gate_bias=g.get("gate_bias"),
@@ -411,35 +493,73 @@ def main():
                                                       n_experts=n, out=y), it, torch),
     }
     if it > 0 and a.train:
-        stages["aux_losses"] = time_calls(lambda: moe.moe_aux_losses(
+        stage_ms["aux_losses"] = time_calls(lambda: moe.moe_aux_losses(
             g["x"], g["w_gate"], g["w_noise"], thresh, route["offsets"], route["perm_token"],
             route["importance"], k, gate_bias=g.get("gate_bias"), ws=ws), it, torch)
     torch.cuda.synchronize()
-    log("stages (ms): " + ", ".join(f"{k_}={v:.3f}" for k_, v in stages.items()))
+    log("stages (ms): " + ", ".join(f"{k_}={v:.3f}" for k_, v in stage_ms.items()))
 
-    # Roofline of the dominant kernel, the expert FFN: algorithmic bytes per launch =
-    # the weights of every expert that received rows (2 d h elements each) + the
-    # gathered input rows + the written output rows.
+    # Algorithmic work (the selected experts only; the gate GEMM once for the
+    # step, and once more for the Load pass as a stage of its own).
     cnt = counts.cpu().numpy()
     esize = 2 if w.expert_dtype == dg.BF16 else 4
     asize = 2 if w.act_dtype == dg.BF16 else 4
+    gsize = 2 if w.gate_dtype == dg.BF16 else 4
     if cap:  # the rows the experts serve
         cnt = np.minimum(cnt, cap)
     used = int((cnt > 0).sum())
     rows = int(cnt.sum())
+    expert_peak = BF16_PEAK_TFLOPS if w.expert_dtype == dg.BF16 else FP32_PEAK_TFLOPS
+    gate_peak = BF16_PEAK_TFLOPS if w.gate_dtype == dg.BF16 else FP32_PEAK_TFLOPS
+    gate_mats = 2 if a.train else 1  # W_g and W_noise, or W_g alone without noise
+    gate_flops = 2.0 * B * d * n * gate_mats
+    gate_bytes = B * d * asize + (B * n * 4 if a.train else 0) + gate_mats * n * d * gsize \
+        + B * k * 8 + B * 8
     ffn_bytes = used * 2 * d * h * esize + 2 * rows * d * asize
     ffn_flops = 4.0 * rows * d * h
+    comb_bytes = B * k * d * asize + B * d * asize + B * k * 8
+    load_flops = 2.0 * B * d * n * 2
+    load_bytes = B * d * asize + 2 * n * d * gsize + B * 8
     ffn_ms = ffn_total / ffn_n  # the FFN kernel inside the timed steps
-    achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
-    gsize = 2 if w.gate_dtype == dg.BF16 else 4
-    if a.train:  # x, eps, both gate matrices, the used experts, y; gate GEMM twice + FFN
-        step_bytes = (B * d * asize + B * n * 4 + 2 * n * d * gsize + used * 2 * d * h * esize
-                      + B * d * asize)
-        step_flops = 2.0 * B * d * 2 * n * 2 + ffn_flops
-    else:  # no noise: x, W_g, the used experts, y; one clean-logit GEMM + FFN
-        step_bytes = B * d * asize + n * d * gsize + used * 2 * d * h * esize + B * d * asize
-        step_flops = 2.0 * B * d * n + ffn_flops
-    mfma_peak = BF16_PEAK_TFLOPS if w.expert_dtype == dg.BF16 else FP32_PEAK_TFLOPS
+    stages = {}
+    if stage_ms:
+        stages = {
+            "gate": roof("gate", stage_ms["gate"], gate_flops, gate_bytes, gate_peak, "mfma"),
+            "route": roof("route", stage_ms["route"]),
+            "expert_ffn": roof("expert_ffn", stage_ms["expert_ffn"], ffn_flops, ffn_bytes,
+                               expert_peak),
+            "combine": roof("combine", stage_ms["combine"], 0.0, comb_bytes, None, "hbm"),
+        }
+        stages["route"]["us"] = stage_ms["route"] * 1e3
+        if "aux_losses" in stage_ms:
+            stages["aux_losses"] = roof("aux_losses", stage_ms["aux_losses"], load_flops,
+                                        load_bytes, gate_peak, "mfma")
+    ffn_roof = roof("ffn", ffn_ms, ffn_flops, ffn_bytes, expert_peak)
+    if ffn_roof["bound"] == "mfma":
+        rl = {"kernel": "ffn_kernel (expert FFN)", "bound": "mfma",
+              "achieved": ffn_roof["tflops"], "peak": expert_peak, "unit": "TFLOP/s",
+              "frac": ffn_roof["mfma_frac"], "hbm_frac": ffn_roof["hbm_frac"]}
+    else:
+        rl = {"kernel": "ffn_kernel (expert FFN)", "bound": "hbm",
+              "achieved": ffn_roof["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "frac": ffn_roof["hbm_frac"], "mfma_frac": ffn_roof["mfma_frac"]}
+    rl.update(traffic=profiled_traffic(w.name), alg_bytes_per_launch=ffn_bytes,
+              alg_flops_per_launch=ffn_flops, avg_launch_ms=ffn_ms, timed_launches=ffn_n)
+    # x, eps, the gate matrices, the used experts' weights, y; gate GEMM once + FFN
+    step_bytes = B * d * asize + (B * n * 4 if a.train else 0) + gate_mats * n * d * gsize \
+        + used * 2 * d * h * esize + B * d * asize
+    step_flops = gate_flops + ffn_flops
+    step_gate_ms = gate_flops / (gate_peak * 1e12) * 1e3
+    step_ffn_ms = ffn_flops / (expert_peak * 1e12) * 1e3
+    alg_roof_ms = max(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, step_gate_ms + step_ffn_ms)
+    step = {"alg_bytes": step_bytes, "alg_flops": step_flops,
+            "hbm_frac": step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "mfma_frac": (step_gate_ms + step_ffn_ms) / ms_step,
+            "alg_roofline_ms": alg_roof_ms, "alg_roofline_frac": alg_roof_ms / ms_step,
+            "mean_ms": total_ms / a.steps, "min_ms": min(per_step), "max_ms": max(per_step)}
+    if stages:
+        serial = sum(v["roof_ms"] for v in stages.values())
+        step.update(stage_roofs_ms=serial, stage_roofs_frac=serial / ms_step)
 
     result = {
         "metric": METRIC,
@@ -457,23 +577,20 @@ def main():
         "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "n_experts": n,
                    "k": k, "train": a.train, "capacity": cap, "gate_order": a.gate_order,
                    "act_dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
+                   "expert_dtype": "bf16" if w.expert_dtype == dg.BF16 else "f32",
                    "gate_dtype": "bf16" if w.gate_dtype == dg.BF16 else "f32"},
-        "roofline": {"kernel": "ffn_kernel (expert FFN)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(w.name),
-                     "alg_bytes_per_launch": ffn_bytes, "avg_launch_ms": ffn_ms,
-                     "timed_launches": ffn_n,
-                     "mfma_frac": ffn_flops / (ffn_ms * 1e-3) / (mfma_peak * 1e12)},
-        "step": {"alg_bytes": step_bytes, "alg_flops": step_flops,
-                 "hbm_frac": step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
-                 "mfma_frac": step_flops / (ms_step * 1e-3) / (mfma_peak * 1e12)},
-        "stages_ms": stages,
+        "roofline": rl,
+        "step": step,
+        "stages": stages,
         "wall_ms_per_step": 1000 * wall / a.steps,
         "cpu_baseline": None,
     }
     if a.cpu_seconds > 0:
         log("timing the oracle on the host cores")
-        result["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
+        cb = cpu_baseline(w, inp, a.cpu_seconds)
+        log("timing the oracle on one host thread (256-token and 8192-token fp32 workloads)")
+        cb["single_thread"] = cpu_single_thread(min(4.0, a.cpu_seconds / 3))
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 

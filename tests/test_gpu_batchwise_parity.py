@@ -128,7 +128,9 @@ CASES = [
     ("tiny_fp32", {"tokens": 20000}, 1000, True, False),                    # too many candidates
     ("tiny_fp32", {"tokens": 1, "n_experts": 8}, 1, False, False),         # every expert, one row
     ("flat_bf16_n4096", {"tokens": 700, "n_experts": 32, "d_hidden": 128}, 700, True, False),
-    ("zipf_bf16_n256", {"tokens": 2048, "d_hidden": 128}, None, False, False),  # gate bias, 32x32
+    ("zipf_bf16_n256", {"tokens": 2048, "d_hidden": 128}, None, False, False),  # gate bias, 16x16
+    ("zipf_bf16_n256", {"tokens": 2048, "d_hidden": 128, "gate_dtype": dg.BF16}, None, False,
+     False),                                                                # gate bias, 32x32
 ]
 
 

@@ -1,0 +1,268 @@
+"""GPU gating with exact ties, and with a gate bias on the 32x32 kernel.
+
+Exact ties. [MoE-explainer] "Noisy top-k gating" keeps the k largest noisy
+logits; which of two equal logits is kept is this library's reading (larger
+first, equal logits to the lower expert index; slot j is the rank). Random
+inputs almost never tie exactly, so these cases build ties on purpose: the
+gate weights are zero, the noisy logit of expert e is then
+H = b_e + eps_te * (Softplus(0) + f) exactly, and experts e and e + n/2 share
+their bias and their noise column. Biases come from {0, 0.5, 1} and noise
+draws from {-1, 0, 1, 2}, so distinct logits differ by at least 0.2 and every
+tie is exact on both sides. The selection (in rank order), the thresholds and
+the gates are then compared bit-exactly or at the fp32 bar with no near-tie
+allowance, on every gate kernel (16x16 fp32 and bf16, 32x32 bf16 in training
+and clean-only mode, the split sweep and its merge), and the Load and the
+whole forward pass are checked against the oracle on the same ties.
+
+Gate bias on the 32x32 kernel. The Zipf-skewed workload's bias with bf16 gate
+weights (so the 32x32 kernel runs, not the fp32-gate 16x16 one), in training
+and inference, both gate orders, whole and split sweeps, and the Load pass
+(batchwise inference with it: tests/test_gpu_batchwise_parity.py).
+"""
+import numpy as np
+import pytest
+
+import datagen as dg
+import oracle
+from parity import (GATE_TOL, LOSS_TOL, announce, check_gating, gpu_inputs, out_tol, rel_err,
+                    scalar_rel, to_device, to_host)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import sparsely_gated_mixture_moe_amd as moe  # noqa: E402
+
+FLOOR = 1e-2
+
+
+def tie_inputs(w, seed, experts=False):
+    """Inputs of workload ``w`` with zero gate weights and tied (bias, noise)
+    pairs: expert e and e + n/2 (n even) are the same expert for the gate."""
+    n = w.n_experts
+    assert n % 2 == 0
+    inp = dg.make_inputs(w, experts=experts)
+    rng = np.random.default_rng(seed)
+    zero = np.zeros((n, w.d_model), np.float32)
+    inp["w_gate"] = dg.f32_to_bf16(zero) if w.gate_dtype == dg.BF16 else zero
+    inp["w_noise"] = inp["w_gate"].copy()
+    half = n // 2
+    b = rng.choice([0.0, 0.5, 1.0], size=half).astype(np.float32)
+    inp["gate_bias"] = np.concatenate([b, b])
+    e = rng.choice([-1.0, 0.0, 1.0, 2.0], size=(w.tokens, half)).astype(np.float32)
+    inp["eps"] = np.ascontiguousarray(np.concatenate([e, e], axis=1))
+    return inp
+
+
+def expected_selection(H, k):
+    """The k largest of each row, larger first, equal values to the lower
+    index: a stable sort of the negated logits (numpy's, not the oracle's)."""
+    return np.argsort(-H, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def dims_for(g, w, train, gate_order=0):
+    act = moe.MOE_F32 if g["x"].dtype == torch.float32 else moe.MOE_BF16
+    gdt = moe.MOE_F32 if g["w_gate"].dtype == torch.float32 else moe.MOE_BF16
+    dims = moe.make_dims(w.tokens, w.d_model, 128, w.n_experts, w.k, act, act, gdt)
+    return dims, moe.make_opts(train, FLOOR, gate_order=gate_order)
+
+
+def check_exact(ref, idx, gate, thr, k):
+    exp = expected_selection(ref["H"], k)
+    assert np.array_equal(ref["topk_idx"], exp), "oracle selection is not the stable order"
+    bad = np.nonzero(np.any(idx != exp, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, e.g. row {bad[0]}: gpu {idx[bad[0]]} " \
+                          f"expected {exp[bad[0]]} (H {ref['H'][bad[0]][exp[bad[0]]]})"
+    # thresholds are the k-th and (k+1)-th largest logits, exact fp32 roundings
+    # of values that both sides form from the same few inputs
+    assert rel_err(np.where(np.isfinite(thr), thr, 0),
+                   np.where(np.isfinite(ref["thresh"]), ref["thresh"], 0)) <= GATE_TOL
+    assert rel_err(gate, ref["topk_gate"]) <= GATE_TOL
+    ties = np.sum(ref["thresh"][:, 0] == ref["thresh"][:, 1])
+    return int(ties)
+
+
+# (workload, overrides, kernel): every gate kernel and the split sweep
+TIE_CASES = [
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 64}, "32x32"),
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 48, "k": 3}, "32x32 train, 16x16 infer"),
+    ("flat_bf16_n4096", {"tokens": 257, "n_experts": 40, "k": 2, "d_model": 128}, "16x16 bf16"),
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 96, "k": 8, "d_model": 256}, "32x32 k8"),
+    ("tiny_fp32", {"tokens": 300, "n_experts": 64, "k": 4}, "16x16 fp32"),
+    ("zipf_bf16_n256", {"tokens": 300, "zipf": False}, "16x16 bf16 x, fp32 weights"),
+    ("flat_bf16_n4096", {"tokens": 5, "n_experts": 512}, "32x32 split"),
+    ("tiny_fp32", {"tokens": 3, "n_experts": 96, "k": 3, "d_model": 128}, "16x16 split"),
+]
+
+
+def _tid(c):
+    name, kw, kern = c
+    return name + "".join(f"-{k}{v}" for k, v in kw.items()) + "-" + kern.replace(" ", "_")
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=[_tid(c) for c in TIE_CASES])
+@pytest.mark.parametrize("train", [True, False])
+def test_gate_exact_ties_lower_index(case, train):
+    name, kw, kern = case
+    w = dg.workload(name, **kw)
+    announce(f"moe_gate exact ties {w.name} {kw} ({kern}) train={train}")
+    inp = tie_inputs(w, seed=w.tokens + w.n_experts)
+    ref = oracle.gate(inp, w.k, train=train, noise_floor=FLOOR, want_logits=True)
+    g = gpu_inputs(inp)
+    dims, opts = dims_for(g, w, train)
+    ws = moe.workspace(dims, opts, g["x"].device)
+    res = []
+    for w_s in (ws, None):
+        idx, gate, thr = moe.moe_gate(g["x"], g["w_gate"], g["w_noise"],
+                                      g["eps"] if train else None, w.k, train=train,
+                                      noise_floor=FLOOR, gate_bias=g["gate_bias"], ws=w_s)
+        torch.cuda.synchronize()
+        res.append(check_exact(ref, to_host(idx), to_host(gate), to_host(thr), w.k))
+    assert res[0] > 0, "the case built no tie at the k-th / (k+1)-th logit"
+    print(w.name, kw, kern, train, "rows with v_k == v_k+1:", res[0])
+
+
+@pytest.mark.parametrize("case", TIE_CASES[:6], ids=[_tid(c) for c in TIE_CASES[:6]])
+def test_load_with_exact_ties(case):
+    """Eq 9 on tied rows: the selected experts are compared against the
+    (k+1)-th logit, the others against the k-th, by index membership; with
+    v_k == v_k+1 both thresholds are the same value."""
+    name, kw, kern = case
+    w = dg.workload(name, **kw)
+    announce(f"moe_aux_losses exact ties {w.name} {kw} ({kern})")
+    inp = tie_inputs(w, seed=3 * w.tokens + w.n_experts)
+    ref = oracle.gate(inp, w.k, noise_floor=FLOOR)
+    rt = oracle.route(ref["topk_idx"], ref["topk_gate"], w.n_experts)
+    g = gpu_inputs(inp)
+    load, losses = moe.moe_aux_losses(
+        g["x"], g["w_gate"], g["w_noise"], to_device(ref["thresh"].astype(np.float32)),
+        to_device(rt["offsets"]), to_device(rt["perm_token"]),
+        to_device(rt["importance"].astype(np.float32)), w.k, noise_floor=FLOOR,
+        gate_bias=g["gate_bias"])
+    torch.cuda.synchronize()
+    load_ref = oracle.load(inp, w.k, noise_floor=FLOOR)
+    err = rel_err(to_host(load), load_ref)
+    assert err <= GATE_TOL, f"load error {err}"
+    lo = to_host(losses)
+    assert scalar_rel(lo[1], oracle.cv2(load_ref)) <= LOSS_TOL
+    print(w.name, kw, "load err", err)
+
+
+@pytest.mark.parametrize("case", [TIE_CASES[0], TIE_CASES[4], TIE_CASES[6]],
+                         ids=[_tid(c) for c in (TIE_CASES[0], TIE_CASES[4], TIE_CASES[6])])
+@pytest.mark.parametrize("train", [True, False])
+def test_forward_exact_ties(case, train):
+    """The whole forward on tied rows: selection bit-exact in rank order,
+    routing of that selection, y, Importance, Load and losses against the
+    oracle (which decides the same ties the same way)."""
+    name, kw, kern = case
+    w = dg.workload(name, **kw)
+    announce(f"moe_forward exact ties {w.name} {kw} ({kern}) train={train}")
+    inp = tie_inputs(w, seed=7 * w.tokens + w.n_experts, experts=True)
+    g = gpu_inputs(inp)
+    out = moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], w.k,
+                          gate_bias=g["gate_bias"], train=train, noise_floor=FLOOR,
+                          return_routing=True)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp, w.k, train=train, noise_floor=FLOOR)
+    idx = to_host(out["topk_idx"])
+    assert np.array_equal(idx, ref["topk_idx"])
+    rt = oracle.route(ref["topk_idx"], ref["topk_gate"], w.n_experts)
+    assert np.array_equal(to_host(out["counts"]), rt["counts"])
+    assert np.array_equal(to_host(out["perm_token"]), rt["perm_token"])
+    yerr = rel_err(to_host(out["y"]), ref["y"])
+    assert yerr <= out_tol(w.act_dtype == dg.BF16), f"y error {yerr}"
+    for key in ("importance", "load"):
+        e = rel_err(to_host(out[key]), ref[key])
+        assert e <= GATE_TOL, f"{key} error {e}"
+    lo = to_host(out["losses"])
+    for i in range(3):
+        assert scalar_rel(lo[i], ref["losses"][i]) <= LOSS_TOL, (i, lo, ref["losses"])
+    print(w.name, kw, train, "y err", yerr)
+
+
+# ---------------------------------------------------------------------------
+# Gate bias through the 32x32 kernel (bf16 gate weights)
+# ---------------------------------------------------------------------------
+
+def zipf_bf16_gate(**kw):
+    """The Zipf-skewed workload with bf16 gate weights: its gate bias then
+    goes through the 32x32 kernel."""
+    return dg.workload("zipf_bf16_n256", gate_dtype=dg.BF16, **kw)
+
+
+BIAS32_CASES = [
+    ({"tokens": 1500}, True, 0),
+    ({"tokens": 1500}, False, 0),
+    ({"tokens": 1500}, True, 1),
+    ({"tokens": 1500}, False, 1),
+    ({"tokens": 3}, True, 0),     # split sweep
+    ({"tokens": 3}, False, 1),    # split sweep, clean-only mode
+    ({"tokens": 700, "n_experts": 96, "k": 8, "d_model": 256}, False, 0),
+    ({"tokens": 700, "n_experts": 48, "k": 2, "d_model": 128}, True, 0),
+]
+
+
+@pytest.mark.parametrize("kw,train,order", BIAS32_CASES,
+                         ids=["".join(f"{k}{v}-" for k, v in c[0].items()) + f"train{int(c[1])}-order{c[2]}"
+                              for c in BIAS32_CASES])
+def test_gate_bias_32x32(kw, train, order):
+    w = zipf_bf16_gate(**kw)
+    announce(f"moe_gate bias 32x32 {kw} train={train} order={order}")
+    inp = dg.make_inputs(w, experts=False)
+    assert inp["w_gate"].dtype == np.uint16 and "gate_bias" in inp
+    ref = oracle.gate(inp, w.k, train=train, noise_floor=FLOOR, want_logits=True,
+                      gate_order=order)
+    g = gpu_inputs(inp)
+    dims, opts = dims_for(g, w, train, order)
+    ws = moe.workspace(dims, opts, g["x"].device)
+    for w_s in (ws, None):
+        idx, gate, thr = moe.moe_gate(g["x"], g["w_gate"], g["w_noise"],
+                                      g["eps"] if train else None, w.k, train=train,
+                                      noise_floor=FLOOR, gate_bias=g["gate_bias"],
+                                      gate_order=order, ws=w_s)
+        torch.cuda.synchronize()
+        st = check_gating(ref, ref["H"], to_host(idx), to_host(gate), to_host(thr),
+                          gate_order=order)
+    print(kw, train, order, {k: v for k, v in st.items() if k != "swapped"})
+
+
+@pytest.mark.parametrize("kw", [{"tokens": 1500}, {"tokens": 16384, "n_experts": 64}])
+def test_load_bias_32x32(kw):
+    """The Load pass (pass 2 of the 32x32 kernel) with a gate bias, and the
+    selected pairs' correction, against the oracle's Load."""
+    w = zipf_bf16_gate(**kw)
+    announce(f"moe_aux_losses bias 32x32 {kw}")
+    inp = dg.make_inputs(w, experts=False)
+    ref = oracle.gate(inp, w.k, noise_floor=FLOOR)
+    rt = oracle.route(ref["topk_idx"], ref["topk_gate"], w.n_experts)
+    g = gpu_inputs(inp)
+    load, losses = moe.moe_aux_losses(
+        g["x"], g["w_gate"], g["w_noise"], to_device(ref["thresh"].astype(np.float32)),
+        to_device(rt["offsets"]), to_device(rt["perm_token"]),
+        to_device(rt["importance"].astype(np.float32)), w.k, noise_floor=FLOOR,
+        gate_bias=g["gate_bias"])
+    torch.cuda.synchronize()
+    load_ref = oracle.load(inp, w.k, noise_floor=FLOOR)
+    err = rel_err(to_host(load), load_ref)
+    assert err <= GATE_TOL, f"load error {err}"
+    lo = to_host(losses)
+    cv_imp, cv_load = oracle.cv2(rt["importance"]), oracle.cv2(load_ref)
+    assert scalar_rel(lo[0], cv_imp) <= LOSS_TOL
+    assert scalar_rel(lo[1], cv_load) <= LOSS_TOL
+    print(kw, "load err", err)
+
+
+@pytest.mark.parametrize("train", [True, False])
+def test_forward_bias_32x32(train):
+    """The fused forward with the bias through the 32x32 kernel (both passes
+    in training), end to end against the oracle."""
+    from test_gpu_parity import check_forward
+    w = zipf_bf16_gate(tokens=3000, d_hidden=256)
+    announce(f"moe_forward bias 32x32 train={train}")
+    inp = dg.make_inputs(w)
+    g = gpu_inputs(inp)
+    out = moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], w.k,
+                          gate_bias=g["gate_bias"], train=train, noise_floor=FLOOR,
+                          return_routing=True)
+    torch.cuda.synchronize()
+    print(train, check_forward(w, inp, out, train))

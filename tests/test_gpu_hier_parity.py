@@ -16,8 +16,8 @@ import pytest
 
 import datagen as dg
 import oracle
-from parity import (GATE_TOL, LOSS_TOL, announce, check_gating, gpu_inputs, out_tol, rel_err,
-                    scalar_rel, to_host)
+from parity import (GATE_TOL, LOSS_TOL, announce, check_gating, device_tensor, gpu_inputs,
+                    out_tol, rel_err, scalar_rel, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,3 +151,90 @@ def test_hier_empty_batch():
     assert out["y"].shape == (0, 128)
     assert np.all(out["importance"] == 0) and np.all(out["load"] == 0)
     assert np.all(out["losses"] == 0)
+
+
+@pytest.mark.timeout(900)
+def test_hier_full_size_sampled():
+    """The hierarchical workload at its full size in the benchmark's launch
+    configuration (MoeHierForward, training mode): 131072 tokens, 128 groups
+    x 128 experts 512-1024-512 (16384 leaves, 34.4 GB of bf16 expert weights
+    generated on the device), k1 = k2 = 2. Both gate levels are checked on
+    every row against the oracle (the secondary gates on the GPU's groups);
+    the oracle, forced to the GPU's selections at both levels, then gives the
+    leaves (bit-exact), their gates, the leaf counts, both levels' Importance
+    and Load, the leaf Load and the losses over the whole batch; y is checked
+    on sampled rows, each from its four leaves' weights regenerated on the
+    host."""
+    w = dg.WORKLOADS["hier_bf16_16384"]
+    B, d, h = w.tokens, w.d_model, w.d_hidden
+    a, b, k1, k2 = w.groups, w.group_experts, w.k1, w.k2
+    n, K = a * b, k1 * k2
+    announce("moe_hier_forward full size: gate inputs")
+    inp = dg.make_hier_inputs(w, experts=False)
+    g = gpu_inputs(inp)
+    announce("moe_hier_forward full size: expert weights on the device")
+    w1 = device_tensor(w, "w1", (n, h, d))
+    w2 = device_tensor(w, "w2", (n, d, h))
+    f = moe.MoeHierForward((B, d), g["w_gate"], g["w_noise"], g["w_gate2"], g["w_noise2"], w1, w2,
+                           k1, k2, train=True)
+    extra = {name: torch.empty(shp, dtype=dt, device=w1.device)
+             for name, (shp, dt) in f.output_shapes().items()}
+    announce("moe_hier_forward full size: GPU call")
+    y = f(g["x"], g["eps"], g["eps2"], **extra)
+    torch.cuda.synchronize()
+    out = {key: to_host(v) for key, v in extra.items()}
+    out.update(y=to_host(y), importance=to_host(f.importance), load=to_host(f.load),
+               losses=to_host(f.losses))
+    del w1, w2, f, extra
+    torch.cuda.empty_cache()
+    announce("moe_hier_forward full size: oracle gating, level 1")
+    ref = oracle.hier_gate(inp, k1, k2, want_logits=True)
+    s1 = check_gating({"topk_idx": ref["sel1"], "topk_gate": ref["gate1"], "thresh": ref["thr1"]},
+                      ref["H1"], out["group_idx"], out["group_gate"], out["group_thresh"])
+    f1 = out["group_idx"]
+    del ref
+    announce("moe_hier_forward full size: oracle gating, level 2 on the GPU's groups")
+    ref2 = oracle.hier_gate(inp, k1, k2, want_logits=True, force1=f1)
+    s2 = check_gating({"topk_idx": ref2["sel2"].reshape(B * k1, k2),
+                       "topk_gate": ref2["gate2"].reshape(B * k1, k2),
+                       "thresh": ref2["thr2"].reshape(B * k1, 2)},
+                      ref2["H2"].reshape(B * k1, b), out["sub_idx"].reshape(B * k1, k2),
+                      out["sub_gate"].reshape(B * k1, k2), out["sub_thresh"].reshape(B * k1, 2))
+    del ref2
+    announce("moe_hier_forward full size: oracle batch sums on the GPU's selections")
+    fo = oracle.hier_forward(inp, k1, k2, force1=f1, force2=out["sub_idx"], with_y=False)
+    assert np.array_equal(out["topk_idx"], fo["leaf_idx"])
+    assert rel_err(out["topk_gate"], fo["leaf_gate"]) <= GATE_TOL
+    assert np.array_equal(out["counts"], np.bincount(out["topk_idx"].ravel(), minlength=n))
+    assert np.array_equal(out["group_rows"], fo["rows1"].astype(np.int32))
+    errs = {}
+    for key, rkey in (("importance", "importance"), ("group_importance", "imp1"),
+                      ("group_load", "load1"), ("sub_load", "load2"), ("load", "load")):
+        e = rel_err(out[key], fo[rkey])
+        assert e <= GATE_TOL, f"{key} error {e}"
+        errs[key] = e
+    for i in range(3):
+        assert scalar_rel(out["losses"][i], fo["losses"][i]) <= LOSS_TOL, \
+            f"loss {i}: {out['losses'][i]} vs {fo['losses'][i]}"
+    # y on sampled rows from the leaves' weights regenerated on the host
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, B // 2, B - 2, B - 1],
+                                     rng.choice(B, 150, replace=False)]))
+    leaves = np.unique(out["topk_idx"][rows])
+    announce(f"moe_hier_forward full size: y on {len(rows)} rows ({len(leaves)} leaves)")
+    where = {int(e): i for i, e in enumerate(leaves)}
+    sub = {"x": inp["x"],
+           "w1": np.stack([dg.gen(w, "w1", int(e) * h * d, h * d) for e in leaves]).reshape(-1, h, d),
+           "w2": np.stack([dg.gen(w, "w2", int(e) * d * h, d * h) for e in leaves]).reshape(-1, d, h)}
+    tok = np.repeat(rows, K)
+    lv = out["topk_idx"][rows].ravel()
+    eo = oracle.expert_pairs(sub, tok, [where[int(e)] for e in lv]).reshape(len(rows), K, d)
+    order = np.argsort(out["topk_idx"][rows], axis=1, kind="stable")
+    gates = np.take_along_axis(fo["leaf_gate"][rows], order, 1)
+    eo = np.take_along_axis(eo, order[:, :, None], 1)
+    y_ref = (gates[:, :, None] * eo).sum(1)
+    yerr = rel_err(out["y"][rows], y_ref)
+    assert yerr <= out_tol(True), f"y error {yerr}"
+    errs.update(y=yerr, near_tie1=int(s1["near_tie"]), swapped1=len(s1["swapped"]),
+                near_tie2=int(s2["near_tie"]), swapped2=len(s2["swapped"]))
+    print("hier full size", errs)

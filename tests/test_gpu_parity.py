@@ -143,8 +143,8 @@ def test_gate_switch_order(case):
 
 
 # Inference on the 32x32 kernel (n a multiple of 32: chunks of 32 experts'
-# clean rows), with and without a gate bias, both gate orders, whole and split
-# sweeps.
+# clean rows): bf16 gate weights with the Zipf gate bias, both gate orders,
+# whole and split sweeps.
 CLEAN32_CASES = [
     ("zipf_bf16_n256", {"tokens": 1500}, 0),
     ("zipf_bf16_n256", {"tokens": 1500}, 1),
@@ -159,9 +159,10 @@ CLEAN32_CASES = [
                          ids=[_gate_ids(c[:2]) + f"-order{c[2]}" for c in CLEAN32_CASES])
 def test_gate_clean32(case):
     name, kw, order = case
-    w = wl(name, **kw)
+    w = wl(name, gate_dtype=dg.BF16, zipf=True, **kw)
     announce(f"moe_gate clean-only 32x32 {w.name} {kw} gate_order={order}")
-    inp = dg.make_inputs(w, experts=False, with_bias=True)
+    inp = dg.make_inputs(w, experts=False)
+    assert inp["w_gate"].dtype == np.uint16 and "gate_bias" in inp
     ref = oracle.gate(inp, w.k, train=False, noise_floor=FLOOR, want_logits=True,
                       gate_order=order)
     g = gpu_inputs(inp)
@@ -428,15 +429,17 @@ def test_aux_losses_parity(case, train):
     print(w.name, kw, train, "load err", err)
     assert err <= GATE_TOL
     lo = to_host(losses)
-    cv_imp = oracle.cv_squared(rt["importance"].astype(np.float32))
-    cv_load = oracle.cv_squared(load_ref)
+    cv_imp = oracle.cv2(rt["importance"].astype(np.float32))
+    cv_load = oracle.cv2(load_ref)
     assert scalar_rel(lo[0], cv_imp) <= LOSS_TOL
     assert scalar_rel(lo[1], cv_load) <= LOSS_TOL
     assert scalar_rel(lo[2], 0.1 * cv_imp + 0.3 * cv_load) <= LOSS_TOL
 
 
-def check_forward(w, inp, out, train, rows=None, full_load=True, w_imp=0.1, w_load=0.1):
-    """End-to-end check of moe_forward's outputs against the oracle."""
+def check_forward(w, inp, out, train, rows=None, full_load=True, w_imp=0.1, w_load=0.1,
+                  y_rows=None):
+    """End-to-end check of moe_forward's outputs against the oracle: gating on
+    ``rows`` (default all), y on ``y_rows`` (default the same rows)."""
     B, n, k = w.tokens, w.n_experts, w.k
     sel_rows = np.arange(B) if rows is None else np.asarray(rows)
     g_idx = to_host(out["topk_idx"])
@@ -450,14 +453,18 @@ def check_forward(w, inp, out, train, rows=None, full_load=True, w_imp=0.1, w_lo
     assert np.array_equal(counts, np.bincount(g_idx.ravel(), minlength=n))
     assert np.array_equal(to_host(out["perm_token"]), (order // k).astype(np.int32))
     # y on the checked rows; rows whose near-tie selection differs are checked on the GPU's set
-    y = to_host(out["y"])[sel_rows]
-    y_ref = oracle.y_rows(inp, k, rows=sel_rows, train=train, noise_floor=FLOOR)
+    yr = sel_rows if y_rows is None else np.asarray(y_rows)
+    y = to_host(out["y"])[yr]
+    y_ref = oracle.y_rows(inp, k, rows=yr, train=train, noise_floor=FLOOR)
+    at = {int(t): i for i, t in enumerate(yr)}
     for r in stats["swapped"]:
         t = int(sel_rows[r])
+        if t not in at:
+            continue
         sel = g_idx[t]
         gates = softmax_at(ref["H"][r], sel)
         eo = oracle.expert_pairs(inp, [t] * k, sel)
-        y_ref[r] = (gates[:, None] * eo).sum(0)
+        y_ref[at[t]] = (gates[:, None] * eo).sum(0)
     yerr = rel_err(y, y_ref)
     assert yerr <= out_tol(w.act_dtype == dg.BF16), f"y error {yerr}"
     # Importance: the gate sums of the GPU's selection; on full-batch checks
@@ -483,7 +490,7 @@ def check_forward(w, inp, out, train, rows=None, full_load=True, w_imp=0.1, w_lo
         lerr = rel_err(load, load_ref)
         assert lerr <= GATE_TOL, f"load error {lerr}"
         res["load_err"] = lerr
-        cv_imp, cv_load = oracle.cv_squared(full), oracle.cv_squared(load_ref)
+        cv_imp, cv_load = oracle.cv2(full), oracle.cv2(load_ref)
         assert scalar_rel(lo[0], cv_imp) <= LOSS_TOL
         assert scalar_rel(lo[1], cv_load) <= LOSS_TOL
         assert scalar_rel(lo[2], w_imp * cv_imp + w_load * cv_load) <= LOSS_TOL
@@ -548,6 +555,56 @@ def test_forward_full_size_sampled():
     announce("moe_forward full size: oracle on sampled rows and full-batch Load")
     res = check_forward(w, inp, out, True, rows=rows, full_load=True)
     print(w.name, "full size", len(rows), "rows", res)
+
+
+def test_forward_zipf_full_size_sampled():
+    """The Zipf-skewed workload at its full size in the benchmark's launch
+    configuration (MoeForward, training mode): 32768 tokens, 256 experts
+    512-1024-512, k 4, bf16 activations and experts, fp32 gate weights with
+    the calibrated Zipf gate bias (about 21K rows on expert 0, over 200 FFN
+    work units of that one expert). Gating, routing, Importance, Load and the
+    losses are checked on the whole batch against the oracle; y on sampled
+    rows: both ends, every FFN unit edge of the most popular expert's first
+    and last units and a few in between, the whole segment of the least
+    popular expert, and random rows."""
+    w = wl("zipf_bf16_n256")
+    B, d, n, k = w.tokens, w.d_model, w.n_experts, w.k
+    announce(f"moe_forward full size {w.name}: generating inputs")
+    inp = dg.make_inputs(w)
+    g = gpu_inputs(inp)
+    f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,
+                       gate_bias=g["gate_bias"], train=True)
+    dev = g["x"].device
+    out = {"topk_idx": torch.empty((B, k), dtype=torch.int32, device=dev),
+           "topk_gate": torch.empty((B, k), dtype=torch.float32, device=dev),
+           "thresh": torch.empty((B, 2), dtype=torch.float32, device=dev),
+           "counts": torch.empty(n, dtype=torch.int32, device=dev),
+           "perm_token": torch.empty(B * k, dtype=torch.int32, device=dev)}
+    announce("moe_forward zipf full size: GPU call")
+    y = f(g["x"], g["eps"], **out)
+    torch.cuda.synchronize()
+    out.update(y=y, importance=f.importance, load=f.load, losses=f.losses)
+    counts = to_host(out["counts"])
+    perm = to_host(out["perm_token"])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    top, last = int(np.argmax(counts)), int(np.argmin(counts))
+    assert counts[top] > 10000, f"the skew is gone: top expert has {counts[top]} rows"
+    unit = 96  # rows per FFN work unit of the bf16 kernel at d = 512
+    seg = perm[off[top]:off[top + 1]]
+    pos = []
+    for u in list(range(3)) + list(range(len(seg) // unit - 2, (len(seg) + unit - 1) // unit)) + \
+            [len(seg) // (2 * unit)]:
+        for p in (u * unit, u * unit + 1, u * unit + unit - 1):
+            if 0 <= p < len(seg):
+                pos.append(p)
+    rng = np.random.default_rng(3)
+    edges = [0, 1, 255, 256, 257, B // 2, B - 257, B - 256, B - 2, B - 1]
+    y_rows = np.unique(np.concatenate([edges, seg[pos], perm[off[last]:off[last + 1]],
+                                       rng.choice(B, 200, replace=False)]))
+    announce(f"moe_forward zipf full size: oracle, gating on all rows, y on {len(y_rows)} rows")
+    res = check_forward(w, inp, out, True, rows=None, full_load=True, y_rows=y_rows)
+    print(w.name, "full size: top expert", top, counts[top], "rows; least", last, counts[last],
+          "; y rows", len(y_rows), res)
 
 
 def test_forward_is_deterministic():

@@ -174,3 +174,16 @@ def test_forced_selection():
         bad = g["sel1"].copy()
         bad[0] = [1, 1]
         oracle.hier_gate(inp, 2, 2, force1=bad)
+
+
+def test_batch_sums_without_the_experts():
+    """hier_forward(with_y=False) skips only the experts: every batch sum and
+    the selection equal the full call's, bit for bit."""
+    w = hier_wl(tokens=300, a=5, b=7, k1=2, k2=2)
+    inp = dg.make_hier_inputs(w)
+    full = oracle.hier_forward(inp, 2, 2, noise_floor=FLOOR)
+    gates_only = {k: v for k, v in inp.items() if k not in ("w1", "w2")}
+    part = oracle.hier_forward(gates_only, 2, 2, noise_floor=FLOOR, with_y=False)
+    assert "y" not in part
+    for key, v in part.items():
+        np.testing.assert_array_equal(v, full[key], err_msg=key)
