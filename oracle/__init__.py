@@ -70,6 +70,18 @@ def _load():
         lib.oracle_hier_forward.argtypes = [_I64, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P,
                                             _I, _P, _P, _I, _D, _I, _P, _P, _P, _P, _P, _P, _I,
                                             _D, _D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+        lib.oracle_objective.argtypes = [_I64, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D,
+                                         _P, _P, _P, _P, _I, _D, _D, _P, _D, _P, _P, _P]
+        lib.oracle_backward.argtypes = [_I64, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D,
+                                        _I, _P, _P, _P, _P, _I, _D, _D, _P, _D, _P] + [_P] * 8
+        lib.oracle_cv2_grad.argtypes = [_I, _P, _P]
+        lib.oracle_cv2_grad.restype = None
+        lib.oracle_kept_softmax_grad.argtypes = [_I, _P, _P, _P]
+        lib.oracle_kept_softmax_grad.restype = None
+        lib.oracle_p_eq9_grad.argtypes = [_D, _D, _D, _P, _P]
+        lib.oracle_p_eq9_grad.restype = None
+        for f in ("oracle_objective", "oracle_backward"):
+            getattr(lib, f).restype = _I
         for f in ("oracle_gate", "oracle_load", "oracle_y_rows", "oracle_expert_pairs",
                   "oracle_route", "oracle_forward", "oracle_hier_gate", "oracle_hier_forward"):
             getattr(lib, f).restype = _I
@@ -281,6 +293,89 @@ def forward(inp: Dict[str, np.ndarray], k: int, train: bool = True, noise_floor:
                                                                    "thresh", "importance", "load",
                                                                    "losses")])
     _check(rc, "forward")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Backward pass ("Implementation notes": which parameters receive gradients;
+# the selection and eq 9's thresholds pass none)
+# ---------------------------------------------------------------------------
+
+def cv2_grad(v) -> np.ndarray:
+    """d CV^2(v) / d v_i (population variance)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    g = np.empty_like(v)
+    _load().oracle_cv2_grad(v.size, v.ctypes.data, g.ctypes.data)
+    return g
+
+
+def kept_softmax_grad(gates, dgates) -> np.ndarray:
+    """Gradient on the kept logits from the gradient on their softmax gates."""
+    g = np.ascontiguousarray(gates, dtype=np.float64)
+    dg = np.ascontiguousarray(dgates, dtype=np.float64)
+    dH = np.empty_like(g)
+    _load().oracle_kept_softmax_grad(g.size, g.ctypes.data, dg.ctypes.data, dH.ctypes.data)
+    return dH
+
+
+def p_eq9_grad(c: float, thr: float, sigma: float):
+    """(dP/dc, dP/dsigma) of eq 9's P = Phi((c - thr) / sigma), thr fixed."""
+    dc, ds = ctypes.c_double(), ctypes.c_double()
+    _load().oracle_p_eq9_grad(float(c), float(thr), float(sigma), ctypes.byref(dc),
+                              ctypes.byref(ds))
+    return dc.value, ds.value
+
+
+def _dy(dy, B, d):
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    if dy.shape != (B, d):
+        raise ValueError("dy must be [B, d]")
+    return dy
+
+
+def objective(inp: Dict[str, np.ndarray], k: int, dy, force_idx, thresh, aux_scale: float = 1.0,
+              train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
+              w_load: float = 0.1) -> float:
+    """J = sum dy . y + aux_scale (w_imp CV^2(Imp) + w_load CV^2(Load)) with the
+    selection fixed to force_idx [B, k] and eq 9's thresholds to thresh [B, 2]."""
+    g = _Gate(inp, train)
+    w1, b1, w2, b2, e_dt, h = _experts(inp)
+    dy = _dy(dy, g.B, g.d)
+    f = _forced(force_idx, (g.B, k))
+    th = np.ascontiguousarray(thresh, dtype=np.float64)
+    J = ctypes.c_double()
+    rc = _load().oracle_objective(g.B, g.d, h, g.n, k, *g.args(), int(train), float(noise_floor),
+                                  _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), e_dt,
+                                  float(w_importance), float(w_load), dy.ctypes.data,
+                                  float(aux_scale), _ptr(f), th.ctypes.data, ctypes.byref(J))
+    _check(rc, "objective")
+    return J.value
+
+
+def backward(inp: Dict[str, np.ndarray], k: int, dy, aux_scale: float = 1.0, train: bool = True,
+             noise_floor: float = 1e-2, w_importance: float = 0.1, w_load: float = 0.1,
+             force_idx=None, decide_fp32: bool = True) -> Dict[str, np.ndarray]:
+    """Gradients of sum dy . y + aux_scale * (weighted losses) with respect to
+    x, the gate parameters and the expert parameters (fp64), the selection
+    (the oracle's own, or force_idx [B, k]) and eq 9's thresholds held fixed.
+    Returns dx [B, d], dw_gate / dw_noise [n, d], dgate_bias [n], dw1 [n, h, d],
+    db1 [n, h], dw2 [n, d, h], db2 [n, d]."""
+    g = _Gate(inp, train)
+    w1, b1, w2, b2, e_dt, h = _experts(inp)
+    B, d, n = g.B, g.d, g.n
+    dy = _dy(dy, B, d)
+    f = _forced(force_idx, (B, k))
+    out = {"dx": np.empty((B, d)), "dw_gate": np.empty((n, d)), "dw_noise": np.empty((n, d)),
+           "dgate_bias": np.empty(n), "dw1": np.empty((n, h, d)), "db1": np.empty((n, h)),
+           "dw2": np.empty((n, d, h)), "db2": np.empty((n, d))}
+    rc = _load().oracle_backward(B, d, h, n, k, *g.args(), int(train), float(noise_floor),
+                                 int(decide_fp32), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), e_dt,
+                                 float(w_importance), float(w_load), dy.ctypes.data,
+                                 float(aux_scale), _ptr(f),
+                                 *[out[key].ctypes.data for key in (
+                                     "dx", "dw_gate", "dw_noise", "dgate_bias", "dw1", "db1",
+                                     "dw2", "db2")])
+    _check(rc, "backward")
     return out
 
 

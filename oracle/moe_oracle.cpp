@@ -203,6 +203,68 @@ double cv2(int n, const double* v) {
   return var / (mean * mean);
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass ("Implementation notes", the paragraph on which parameters
+// receive gradients; "Noisy top-k gating", the k >= 2 paragraph; "Why experts
+// collapse, and the balancing losses"; "A differentiable count of examples").
+// Reading: the selection (which experts are kept) and the thresholds of eq 9
+// (the k-th / (k+1)-th largest noisy logits, values the selection produces)
+// are constants; gradients flow through the kept gates' softmax into their
+// noisy logits, through the numerator (clean logit) and the denominator
+// (noise scale) of eq 9, and through each kept expert's output.
+// ---------------------------------------------------------------------------
+
+// d CV^2(v) / d v_i for the population-variance CV^2: with mean m and
+// variance V, (2 / (n m^2)) ((v_i - m) - V / m); 0 when n == 1 or m == 0
+// (where CV^2 is defined as 0).
+void cv2_grad(int n, const double* v, double* g) {
+  if (n <= 1) {
+    for (int i = 0; i < n; ++i) g[i] = 0.0;
+    return;
+  }
+  double m = 0.0;
+  for (int i = 0; i < n; ++i) m += v[i];
+  m /= n;
+  if (m == 0.0) {
+    for (int i = 0; i < n; ++i) g[i] = 0.0;
+    return;
+  }
+  double V = 0.0;
+  for (int i = 0; i < n; ++i) V += (v[i] - m) * (v[i] - m);
+  V /= n;
+  for (int i = 0; i < n; ++i) g[i] = 2.0 / (n * m * m) * ((v[i] - m) - V / m);
+}
+
+// Backward of the softmax over the kept logits: gates g (k of them, summing
+// to 1) and the gradient dg with respect to each gate give the gradient with
+// respect to each kept logit, g_j (dg_j - sum_l g_l dg_l). Its diagonal is
+// g_j (1 - g_j), the derivative of a gate by its own logit.
+void kept_softmax_grad(int k, const double* g, const double* dg, double* dH) {
+  double s = 0.0;
+  for (int l = 0; l < k; ++l) s += g[l] * dg[l];
+  for (int j = 0; j < k; ++j) dH[j] = g[j] * (dg[j] - s);
+}
+
+// Derivatives of eq 9's P = Phi((c - thr) / sigma) by the clean logit c and by
+// the noise scale sigma (thr fixed): phi(z) / sigma and -phi(z) z / sigma,
+// z = (c - thr) / sigma. With no threshold (thr = -inf, k == n) P is 1 and
+// both are 0.
+void p_eq9_grad(double c, double thr, double sigma, double* dc, double* dsigma) {
+  if (std::isinf(thr)) {
+    *dc = *dsigma = 0.0;
+    return;
+  }
+  const double z = (c - thr) / sigma;
+  const double ph = std::exp(-0.5 * z * z) / std::sqrt(2.0 * M_PI);
+  *dc = ph / sigma;
+  *dsigma = -ph * z / sigma;
+}
+
+// d Softplus(u) / du, the logistic function, in a form that cannot overflow.
+inline double softplus_grad(double u) {
+  return u >= 0.0 ? 1.0 / (1.0 + std::exp(-u)) : std::exp(u) / (1.0 + std::exp(u));
+}
+
 GateArgs make_args(int d, int n, int k, const void* x, int x_dt, const void* wg, const void* wn,
                    int w_dt, const float* bg, const float* eps, int train, double floor,
                    int decide_fp32) {
@@ -544,6 +606,272 @@ int oracle_forward(int64_t B, int d, int h, int n, int k, const void* x, int x_d
     losses[2] = w_imp * cv_imp + w_load * cv_load;  // eqs 7 and 11
   }
   return 0;
+}
+
+// Scalar objective of the backward pass's finite-difference check: with the
+// selection fixed to force_idx [B][k] (rank order) and the thresholds of eq 9
+// fixed to thresh_in [B][2] (the constants of the backward's reading), J =
+// sum over t, c of dy[t][c] y[t][c] + aux_scale (w_imp CV^2(Importance) +
+// w_load CV^2(Load)), y from eq 1 with the kept gates' softmax, Importance from
+// eq 6 and Load from eqs 9-10 (hard counts when train == 0).
+int oracle_objective(int64_t B, int d, int h, int n, int k, const void* x, int x_dt,
+                     const void* wg, const void* wn, int w_dt, const float* bg, const float* eps,
+                     int train, double floor, const void* w1, const void* b1, const void* w2,
+                     const void* b2, int e_dt, double w_imp, double w_load, const double* dy,
+                     double aux_scale, const int32_t* force_idx, const double* thresh_in,
+                     double* J) {
+  if (bad_args(B, d, n, k, train, eps) || h < 1 || !force_idx || !thresh_in || !dy || !J) return 1;
+  const GateArgs g = make_args(d, n, k, x, x_dt, wg, wn, w_dt, bg, eps, train, floor, 1);
+  std::vector<double> imp(n, 0.0), ld(n, 0.0);
+  double task = 0.0;
+  RowGate r(n);
+  std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h), eo(d);
+  for (int64_t t = 0; t < B; ++t) {
+    gate_row(g, t, r, xrow, wrow);
+    if (!force_selection(r, force_idx + t * k, k, n)) return 3;
+    r.vk = thresh_in[t * 2];
+    r.vk1 = thresh_in[t * 2 + 1];
+    for (int j = 0; j < k; ++j) {
+      const int e = r.order[j];
+      imp[e] += r.gate[j];
+      expert_apply(d, h, xrow.data(), w1, b1, w2, b2, e_dt, e, eo.data(), hid, wrow);
+      for (int c = 0; c < d; ++c) task += dy[t * d + c] * r.gate[j] * eo[c];
+    }
+    for (int i = 0; i < n; ++i) ld[i] += p_eq9(g, r, i);
+  }
+  *J = task + aux_scale * (w_imp * cv2(n, imp.data()) + w_load * cv2(n, ld.data()));
+  return 0;
+}
+
+// Backward pass of the layer (reading in the comment above cv2_grad): the
+// gradient of J = sum dy . y + aux_scale (w_imp CV^2(Importance) + w_load
+// CV^2(Load)) with respect to the layer's input and parameters, the selection
+// and the thresholds held fixed. force_idx [B][k] (null: the oracle's own
+// selection) replaces the selection, as in oracle_gate's callers. Outputs
+// (any may be null): dx [B][d]; dwg, dwn [n][d]; dbg [n]; dw1 [n][h][d];
+// db1 [n][h]; dw2 [n][d][h]; db2 [n][d]. Sums over tokens run in ascending
+// token order.
+int oracle_backward(int64_t B, int d, int h, int n, int k, const void* x, int x_dt,
+                    const void* wg, const void* wn, int w_dt, const float* bg, const float* eps,
+                    int train, double floor, int decide_fp32, const void* w1, const void* b1,
+                    const void* w2, const void* b2, int e_dt, double w_imp, double w_load,
+                    const double* dy, double aux_scale, const int32_t* force_idx, double* dx,
+                    double* dwg, double* dwn, double* dbg, double* dw1, double* db1, double* dw2,
+                    double* db2) {
+  if (bad_args(B, d, n, k, train, eps) || h < 1 || !dy) return 1;
+  const GateArgs g = make_args(d, n, k, x, x_dt, wg, wn, w_dt, bg, eps, train, floor, decide_fp32);
+  // Per token: the selection, gates and P terms (forward), then Importance and Load.
+  std::vector<int32_t> sel((size_t)B * k);
+  std::vector<double> gate((size_t)B * k), dgate((size_t)B * k), thr((size_t)B * 2);
+  int bad = 0;
+#pragma omp parallel
+  {
+    RowGate r(n);
+    std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h), eo(d);
+#pragma omp for schedule(dynamic, 8) reduction(| : bad)
+    for (int64_t t = 0; t < B; ++t) {
+      gate_row(g, t, r, xrow, wrow);
+      if (force_idx && !force_selection(r, force_idx + t * k, k, n)) {
+        bad = 1;
+        continue;
+      }
+      thr[t * 2] = r.vk;
+      thr[t * 2 + 1] = r.vk1;
+      for (int j = 0; j < k; ++j) {
+        sel[t * k + j] = r.order[j];
+        gate[t * k + j] = r.gate[j];
+        // task part of dJ/dgate: dy_t . E_e(x_t)
+        expert_apply(d, h, xrow.data(), w1, b1, w2, b2, e_dt, r.order[j], eo.data(), hid, wrow);
+        double s = 0.0;
+        for (int c = 0; c < d; ++c) s += dy[t * d + c] * eo[c];
+        dgate[t * k + j] = s;
+      }
+    }
+  }
+  if (bad) return 3;
+  std::vector<double> imp(n, 0.0), ld(n, 0.0), dimp(n), dld(n);
+  for (int64_t t = 0; t < B; ++t)
+    for (int j = 0; j < k; ++j) imp[sel[t * k + j]] += gate[t * k + j];
+  if (train) {
+    // Load (eq 10) with the same selection and thresholds, tokens in order
+    RowGate r(n);
+    std::vector<double> xrow(d), wrow(d);
+    for (int64_t t = 0; t < B; ++t) {
+      gate_row(g, t, r, xrow, wrow);
+      force_selection(r, sel.data() + t * k, k, n);
+      r.vk = thr[t * 2];
+      r.vk1 = thr[t * 2 + 1];
+      for (int i = 0; i < n; ++i) ld[i] += p_eq9(g, r, i);
+    }
+  }
+  cv2_grad(n, imp.data(), dimp.data());
+  cv2_grad(n, ld.data(), dld.data());
+  for (int i = 0; i < n; ++i) {
+    dimp[i] *= aux_scale * w_imp;
+    dld[i] = train ? dld[i] * aux_scale * w_load : 0.0;  // hard counts carry no gradient
+  }
+  // Per (token, expert): gradients of the clean logit and of u = x . W_noise.
+  std::vector<double> dC((size_t)B * n), dU((size_t)B * n);
+#pragma omp parallel
+  {
+    RowGate r(n);
+    std::vector<double> xrow(d), wrow(d), dg(k), dH(k);
+#pragma omp for schedule(dynamic, 8)
+    for (int64_t t = 0; t < B; ++t) {
+      gate_row(g, t, r, xrow, wrow);
+      force_selection(r, sel.data() + t * k, k, n);
+      r.vk = thr[t * 2];
+      r.vk1 = thr[t * 2 + 1];
+      for (int j = 0; j < k; ++j) dg[j] = dgate[t * k + j] + dimp[sel[t * k + j]];
+      kept_softmax_grad(k, gate.data() + t * k, dg.data(), dH.data());
+      std::vector<double> dh_full(n, 0.0);
+      for (int j = 0; j < k; ++j) dh_full[sel[t * k + j]] = dH[j];
+      for (int i = 0; i < n; ++i) {
+        double dc = dh_full[i];             // H = clean + eps * sigma: dH/dclean = 1
+        double dsig = 0.0;
+        if (train) {
+          dsig = dh_full[i] * (double)g.eps[t * g.eps_row_stride + i];  // dH/dsigma = eps
+          double pc, ps;
+          p_eq9_grad(r.clean[i], r.in_top[i] ? r.vk1 : r.vk, r.sigma[i], &pc, &ps);
+          dc += dld[i] * pc;
+          dsig += dld[i] * ps;
+        }
+        dC[t * n + i] = dc;
+        if (train) {
+          // sigma = Softplus(u) + floor
+          widen_run(g.wn, (int64_t)i * d, d, g.w_dt, wrow.data());
+          double u = 0.0;
+          for (int c = 0; c < d; ++c) u += xrow[c] * wrow[c];
+          dU[t * n + i] = dsig * softplus_grad(u);
+        } else {
+          dU[t * n + i] = 0.0;
+        }
+      }
+    }
+  }
+  // Gate parameters: dW_g[i] = sum_t dC[t][i] x_t, dW_noise likewise, db_g = sum_t dC.
+#pragma omp parallel
+  {
+    std::vector<double> xrow(d);
+#pragma omp for schedule(static)
+    for (int i = 0; i < n; ++i) {
+      std::vector<double> ag(d, 0.0), an(d, 0.0);
+      double ab = 0.0;
+      for (int64_t t = 0; t < B; ++t) {
+        widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+        const double dc = dC[t * n + i], du = dU[t * n + i];
+        for (int c = 0; c < d; ++c) {
+          ag[c] += dc * xrow[c];
+          an[c] += du * xrow[c];
+        }
+        ab += dc;
+      }
+      for (int c = 0; c < d; ++c) {
+        if (dwg) dwg[(int64_t)i * d + c] = ag[c];
+        if (dwn) dwn[(int64_t)i * d + c] = an[c];
+      }
+      if (dbg) dbg[i] = ab;
+    }
+  }
+  // Experts: each from its routed rows only, scaled by their gates.
+  // E(x) = ReLU(x.W1 + b1).W2 + b2 with dE = gate * dy_t.
+  if (dw1 || db1 || dw2 || db2) {
+#pragma omp parallel
+    {
+      std::vector<double> xrow(d), wrow(std::max(d, h)), pre(h), hid(h), dO(d), dA(h);
+#pragma omp for schedule(dynamic, 1)
+      for (int e = 0; e < n; ++e) {
+        std::vector<double> gw1((size_t)h * d, 0.0), gb1(h, 0.0), gw2((size_t)d * h, 0.0),
+            gb2(d, 0.0);
+        for (int64_t t = 0; t < B; ++t) {
+          int j = -1;
+          for (int q = 0; q < k; ++q)
+            if (sel[t * k + q] == e) j = q;
+          if (j < 0) continue;
+          widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+          for (int a = 0; a < h; ++a) {
+            widen_run(w1, ((int64_t)e * h + a) * d, d, e_dt, wrow.data());
+            double v = 0.0;
+            for (int c = 0; c < d; ++c) v += xrow[c] * wrow[c];
+            if (b1) v += widen(b1, (int64_t)e * h + a, e_dt);
+            pre[a] = v;
+            hid[a] = v > 0.0 ? v : 0.0;
+          }
+          for (int c = 0; c < d; ++c) dO[c] = gate[t * k + j] * dy[t * d + c];
+          for (int a = 0; a < h; ++a) dA[a] = 0.0;
+          for (int c = 0; c < d; ++c) {
+            widen_run(w2, ((int64_t)e * d + c) * h, h, e_dt, wrow.data());
+            for (int a = 0; a < h; ++a) {
+              gw2[(size_t)c * h + a] += dO[c] * hid[a];
+              dA[a] += dO[c] * wrow[a];
+            }
+            gb2[c] += dO[c];
+          }
+          for (int a = 0; a < h; ++a) {
+            const double da = pre[a] > 0.0 ? dA[a] : 0.0;
+            gb1[a] += da;
+            for (int c = 0; c < d; ++c) gw1[(size_t)a * d + c] += da * xrow[c];
+          }
+        }
+        if (dw1) std::copy(gw1.begin(), gw1.end(), dw1 + (int64_t)e * h * d);
+        if (db1) std::copy(gb1.begin(), gb1.end(), db1 + (int64_t)e * h);
+        if (dw2) std::copy(gw2.begin(), gw2.end(), dw2 + (int64_t)e * d * h);
+        if (db2) std::copy(gb2.begin(), gb2.end(), db2 + (int64_t)e * d);
+      }
+    }
+  }
+  // The input: through the gate logits and through each kept expert.
+  if (dx) {
+#pragma omp parallel
+    {
+      std::vector<double> xrow(d), wrow(std::max(d, h)), pre(h), dA(h), acc(d);
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t t = 0; t < B; ++t) {
+        widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+        for (int c = 0; c < d; ++c) acc[c] = 0.0;
+        for (int i = 0; i < n; ++i) {
+          widen_run(g.wg, (int64_t)i * d, d, g.w_dt, wrow.data());
+          for (int c = 0; c < d; ++c) acc[c] += dC[t * n + i] * wrow[c];
+          if (train) {
+            widen_run(g.wn, (int64_t)i * d, d, g.w_dt, wrow.data());
+            for (int c = 0; c < d; ++c) acc[c] += dU[t * n + i] * wrow[c];
+          }
+        }
+        for (int j = 0; j < k; ++j) {
+          const int e = sel[t * k + j];
+          for (int a = 0; a < h; ++a) {
+            widen_run(w1, ((int64_t)e * h + a) * d, d, e_dt, wrow.data());
+            double v = 0.0;
+            for (int c = 0; c < d; ++c) v += xrow[c] * wrow[c];
+            if (b1) v += widen(b1, (int64_t)e * h + a, e_dt);
+            pre[a] = v;
+            dA[a] = 0.0;
+          }
+          for (int c = 0; c < d; ++c) {
+            widen_run(w2, ((int64_t)e * d + c) * h, h, e_dt, wrow.data());
+            const double dO = gate[t * k + j] * dy[t * d + c];
+            for (int a = 0; a < h; ++a) dA[a] += dO * wrow[a];
+          }
+          for (int a = 0; a < h; ++a) {
+            if (pre[a] <= 0.0) continue;
+            widen_run(w1, ((int64_t)e * h + a) * d, d, e_dt, wrow.data());
+            for (int c = 0; c < d; ++c) acc[c] += dA[a] * wrow[c];
+          }
+        }
+        for (int c = 0; c < d; ++c) dx[t * d + c] = acc[c];
+      }
+    }
+  }
+  return 0;
+}
+
+// The backward's pieces on their own, for their pins.
+void oracle_cv2_grad(int n, const double* v, double* g) { cv2_grad(n, v, g); }
+void oracle_kept_softmax_grad(int k, const double* g, const double* dg, double* dH) {
+  kept_softmax_grad(k, g, dg, dH);
+}
+void oracle_p_eq9_grad(double c, double thr, double sigma, double* dc, double* dsigma) {
+  p_eq9_grad(c, thr, sigma, dc, dsigma);
 }
 
 // Hierarchical gating ("Hierarchical MoE") for a list of token rows (rows ==
