@@ -17,11 +17,12 @@ using gate_detail::expsum_merge;
 // load[e] = sum over gate blocks b of partial[b][e], in a fixed order: 32
 // experts per workgroup, 8 threads per expert each summing a strided subset
 // of the blocks, then the 8 partial sums in thread order; plus the selected
-// pairs' correction corr[e].
+// pairs' corrections of expert e's slices (slice_start[e] ..
+// slice_start[e + 1] - 1), in slice order.
 __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restrict__ partial,
                                                           int nblocks, int n,
                                                           const float* __restrict__ corr,
-                                                          int splits,
+                                                          const int32_t* __restrict__ slice_start,
                                                           float* __restrict__ load) {
   __shared__ float red[8][32];
   const int col = threadIdx.x & 31;
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restric
 #pragma unroll
     for (int i = 0; i < 8; ++i) t += red[i][col];
     float c = 0.f;
-    for (int i = 0; i < splits; ++i) c += corr[(int64_t)e * splits + i];
+    for (int i = slice_start[e]; i < slice_start[e + 1]; ++i) c += corr[i];
     load[e] = t + c;
   }
 }
@@ -58,7 +59,8 @@ __global__ __launch_bounds__(256) void load_reduce_kernel(const float* __restric
 // order as above; a group without rows gets 0.
 __global__ __launch_bounds__(256) void load_reduce_grouped_kernel(
     const float* __restrict__ partial, const int32_t* __restrict__ unit_start, int n,
-    const float* __restrict__ corr, int splits, float* __restrict__ load) {
+    const float* __restrict__ corr, const int32_t* __restrict__ slice_start,
+    float* __restrict__ load) {
   __shared__ float red[8][32];
   const int col = threadIdx.x & 31;
   const int part = threadIdx.x >> 5;
@@ -74,9 +76,10 @@ __global__ __launch_bounds__(256) void load_reduce_grouped_kernel(
     float t = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) t += red[i][col];
+    const int64_t leaf = (int64_t)grp * n + e;
     float c = 0.f;
-    for (int i = 0; i < splits; ++i) c += corr[((int64_t)grp * n + e) * splits + i];
-    load[(int64_t)grp * n + e] = t + c;
+    for (int i = slice_start[leaf]; i < slice_start[leaf + 1]; ++i) c += corr[i];
+    load[leaf] = t + c;
   }
 }
 
@@ -117,6 +120,36 @@ __global__ __launch_bounds__(1024) void group_plan_kernel(const int32_t* __restr
   }
 }
 
+// Slices of the selected pairs' correction: expert e's routed rows (offsets[e]
+// .. offsets[e + 1] - 1) in slices of kCorrSliceRows; slice_start[e] is the
+// index of e's first slice and slice_start[n] the number of slices. One
+// workgroup; thread t owns a contiguous span of experts.
+__global__ __launch_bounds__(1024) void corr_slice_scan_kernel(const int32_t* __restrict__ offsets,
+                                                               int n,
+                                                               int32_t* __restrict__ slice_start) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int e0 = min(n, t * per), e1 = min(n, e0 + per);
+  int s = 0;
+  for (int e = e0; e < e1; ++e)
+    s += (offsets[e + 1] - offsets[e] + kCorrSliceRows - 1) / kCorrSliceRows;
+  part[t] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = (t >= o) ? part[t - o] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int pos = part[t] - s;
+  for (int e = e0; e < e1; ++e) {
+    slice_start[e] = pos;
+    pos += (offsets[e + 1] - offsets[e] + kCorrSliceRows - 1) / kCorrSliceRows;
+  }
+  if (t == 1023) slice_start[n] = part[t];
+}
+
 // Eight consecutive elements (storage type T) widened to fp32; 16 bytes for
 // bf16, 32 for fp32.
 template <typename T>
@@ -145,13 +178,15 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float (&v)[
 // routed to it (positions offsets[e] .. offsets[e+1] - 1, tokens perm_token[p])
 // and sums Phi((clean - v_{k+1}) / sigma) - Phi((clean - v_k) / sigma), with
 // clean = x . W_g[e] (+ bias) and sigma = Softplus(x . W_noise[e]) + floor
-// recomputed by a dot product over d in fp32. Workgroup (e, s), four waves,
-// takes split s of `splits` equal, consecutive slices of expert e's rows (so
-// a large segment is spread over several workgroups): lane l holds elements
-// 8 l .. 8 l + 7 of both weight rows (d <= 512); wave w takes the slice's
-// groups of eight with index w mod 4, all eight in flight at once; the four
-// waves' sums are added in wave order into corr[e * splits + s] (0 for an
-// empty slice), and the reductions add the splits in order.
+// recomputed by a dot product over d in fp32. Workgroup i, four waves, takes
+// slice i of the slices corr_slice_scan_kernel lists: the slice's expert e
+// is found by a binary search of slice_start, its rows are kCorrSliceRows
+// consecutive routed rows of e (fewer in e's last slice); lane l holds
+// elements 8 l .. 8 l + 7 of both weight rows (d <= 512); wave w takes the
+// slice's groups of eight with index w mod 4, all eight in flight at once;
+// the four waves' sums are added in wave order into corr[i], and the
+// reductions add an expert's slices in order. Workgroups past the number of
+// slices (the grid covers the largest possible count) exit at once.
 // Secondary gates of a hierarchical layer: expert e is leaf (g, j) = (e / b,
 // e % b), its weights are row e of the [a * b, d] secondary weights, and token
 // t's thresholds are row t * k1 + r, where r is g's rank in sel1[t].
@@ -160,21 +195,26 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
     const void* __restrict__ x, const void* __restrict__ wg, const void* __restrict__ wn,
     const float* __restrict__ bias, int d, int n, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm_token, const float* __restrict__ thresh, float noise_floor,
-    const int32_t* __restrict__ sel1, int k1, int b, int splits, float* __restrict__ corr) {
+    const int32_t* __restrict__ sel1, int k1, int b, const int32_t* __restrict__ slice_start,
+    float* __restrict__ corr) {
   constexpr int R = 8;
+  static_assert(kCorrSliceRows % (4 * R) == 0, "slices are whole passes of the 4 x R rows");
   __shared__ float part[4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int e = blockIdx.x;
-  const int split = blockIdx.y;
-  const int q0 = offsets[e], q1 = offsets[e + 1];
-  // slice length: an equal share, rounded up to whole passes of the 4 x R rows
-  const int chunk = ((q1 - q0 + splits - 1) / splits + 4 * R - 1) / (4 * R) * (4 * R);
-  const int p0 = q0 + split * chunk, p1 = min(q1, p0 + chunk);
-  if (p0 >= p1) {
-    if (threadIdx.x == 0) corr[(int64_t)e * splits + split] = 0.f;
-    return;
+  const int slice = blockIdx.x;
+  if (slice >= slice_start[n]) return;  // uniform: past the number of slices
+  // the expert of this slice: the last e with slice_start[e] <= slice (experts
+  // without rows have no slice, so e is never one of them)
+  int lo = 0, hi = n;  // slice_start[lo] <= slice < slice_start[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (slice_start[mid] <= slice) lo = mid;
+    else hi = mid;
   }
+  const int e = lo;
+  const int p0 = offsets[e] + (slice - slice_start[e]) * kCorrSliceRows;
+  const int p1 = min(offsets[e + 1], p0 + kCorrSliceRows);
   const bool active = lane * 8 < d;
   float wgv[8], wnv[8];
   if (active) {
@@ -238,8 +278,7 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
   }
   if (lane == 0) part[wave] = acc;
   __syncthreads();
-  if (threadIdx.x == 0)
-    corr[(int64_t)e * splits + split] = ((part[0] + part[1]) + part[2]) + part[3];
+  if (threadIdx.x == 0) corr[slice] = ((part[0] + part[1]) + part[2]) + part[3];
 }
 
 // Merges the candidate lists of a split selection: row t's `ranges` lists of
@@ -417,24 +456,35 @@ hipError_t launch_group_plan(const int32_t* offsets, int groups, int tile_rows, 
   return hipGetLastError();
 }
 
-int corr_splits(int64_t pairs, int n) {
-  if (n <= 0) return 1;
-  const int64_t avg = pairs / n;
-  const int64_t sp = (2 * avg + 255) / 256;
-  return (int)std::max<int64_t>(1, std::min<int64_t>(kCorrSplitsMax, sp));
+int64_t corr_slices_max(int64_t pairs, int n) {
+  // each expert has at most one partly filled slice
+  return (int64_t)n + (pairs + kCorrSliceRows - 1) / kCorrSliceRows;
 }
 
-hipError_t launch_load_correction(const GateLaunch& g, int n, const int32_t* offsets,
-                                  const int32_t* perm_token, const float* thresh,
-                                  const int32_t* sel1, int k1, int b, int splits, float* corr,
-                                  hipStream_t s) {
-  const dim3 grid((unsigned)n, (unsigned)splits), block(256);
+size_t corr_bytes(int64_t pairs, int n) {
+  const size_t f = ((size_t)corr_slices_max(pairs, n) * sizeof(float) + 255) / 256 * 256;
+  return f + ((size_t)(n + 1) * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+// The slice list of the corr region: after the slice sums.
+int32_t* corr_slice_start(float* corr, int64_t pairs, int n) {
+  const size_t f = ((size_t)corr_slices_max(pairs, n) * sizeof(float) + 255) / 256 * 256;
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(corr) + f);
+}
+
+hipError_t launch_load_correction(const GateLaunch& g, int n, int64_t pairs,
+                                  const int32_t* offsets, const int32_t* perm_token,
+                                  const float* thresh, const int32_t* sel1, int k1, int b,
+                                  float* corr, hipStream_t s) {
+  int32_t* slice_start = corr_slice_start(corr, pairs, n);
+  hipLaunchKernelGGL(corr_slice_scan_kernel, dim3(1), dim3(1024), 0, s, offsets, n, slice_start);
+  const dim3 grid((unsigned)corr_slices_max(pairs, n)), block(256);
   const void* bias = g.units ? nullptr : g.bias;
   const float* bp = reinterpret_cast<const float*>(bias);
 #define MOE_CORR(XS, WS)                                                                      \
   hipLaunchKernelGGL((load_correction_kernel<XS, WS>), grid, block, 0, s, g.x, g.w_gate,      \
                      g.w_noise, bp, g.d, n, offsets, perm_token, thresh, g.noise_floor, sel1, \
-                     k1, b, splits, corr)
+                     k1, b, slice_start, corr)
   if (g.x_dt == kBF16 && g.w_dt == kBF16) MOE_CORR(bf16, bf16);
   else if (g.x_dt == kBF16) MOE_CORR(bf16, float);
   else MOE_CORR(float, float);
@@ -454,12 +504,12 @@ hipError_t launch_load_grouped(const GateLaunch& g, int groups, const int32_t* u
     if (e != hipSuccess) return e;
   }
   const int nleaves = groups * g.n;
-  const int splits = corr_splits(g.tokens * g.k, nleaves);
-  hipError_t e = launch_load_correction(g, nleaves, leaf_offsets, leaf_perm_token, thresh, sel1,
-                                        k1, g.n, splits, corr, s);
+  const int64_t pairs = g.tokens * g.k;
+  hipError_t e = launch_load_correction(g, nleaves, pairs, leaf_offsets, leaf_perm_token, thresh,
+                                        sel1, k1, g.n, corr, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(load_reduce_grouped_kernel, dim3((g.n + 31) / 32, groups), dim3(256), 0, s,
-                     partial, unit_start, g.n, corr, splits, load);
+                     partial, unit_start, g.n, corr, corr_slice_start(corr, pairs, nleaves), load);
   return hipGetLastError();
 }
 
@@ -480,12 +530,12 @@ hipError_t launch_load(const GateLaunch& g, const float* thresh, const int32_t* 
     hipError_t e = gate_dispatch(gs, p, true, s);
     if (e != hipSuccess) return e;
   }
-  const int splits = corr_splits(g.tokens * g.k, g.n);
-  hipError_t e = launch_load_correction(g, g.n, offsets, perm_token, thresh, nullptr, 1, 1, splits,
+  const int64_t pairs = g.tokens * g.k;
+  hipError_t e = launch_load_correction(g, g.n, pairs, offsets, perm_token, thresh, nullptr, 1, 1,
                                         corr, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(load_reduce_kernel, dim3((g.n + 31) / 32), dim3(256), 0, s, partial, nb,
-                     g.n, corr, splits, load);
+                     g.n, corr, corr_slice_start(corr, pairs, g.n), load);
   return hipGetLastError();
 }
 

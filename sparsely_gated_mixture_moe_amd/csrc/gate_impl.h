@@ -278,6 +278,15 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   constexpr int KB = 4 * UE;  // K-block of the 16x16 tiles
   static_assert(D % KB == 0, "d must be a multiple of the K-block");
   constexpr int NKB = D / KB;
+  // bf16 x with fp32 weights: x stays packed as bf16 in registers (half the
+  // registers of fp32, which would not fit beside the rest with two waves per
+  // SIMD) and each value is widened exactly as it feeds its fp32 product. A
+  // lane then holds 8 consecutive K values per 16-byte unit, so K-block kb
+  // takes K values (kb / 2) * 32 + 8 q + 4 (kb % 2) + s at product step s (the
+  // weight fragments are staged in the same order).
+  constexpr bool XPACK = sizeof(XS) == 2 && sizeof(CT) == 4;
+  static_assert(!XPACK || NKB % 2 == 0, "packed x takes K-blocks in pairs");
+  constexpr int NXU = XPACK ? NKB / 2 : NKB;  // x units per lane
   constexpr int EC = GateShape<CT>::kChunk;
   constexpr int NT = EC / 16;
   constexpr int NM = TRAIN ? 2 : 1;
@@ -302,13 +311,35 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   const int nchunks = cr.count;
 
   // x rows of this wave as A operands for every K-block.
-  U16 xa[NKB];
+  U16 xa[NXU];
   {
     const int64_t r = tile_xrow(p, tile, wrow0 + lr);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      xa[kb] = (r >= 0) ? load_x_unit<XS, CT>(p.x, r * D + kb * KB + q * UE) : zero_unit();
+    for (int u = 0; u < NXU; ++u) {
+      if constexpr (XPACK)
+        xa[u] = (r >= 0) ? ld_unit(reinterpret_cast<const XS*>(p.x) + r * D + u * 32 + q * 8)
+                         : zero_unit();
+      else
+        xa[u] = (r >= 0) ? load_x_unit<XS, CT>(p.x, r * D + u * KB + q * UE) : zero_unit();
+    }
   }
+  // The A operand of K-block kb.
+  auto x_operand = [&](int kb) __attribute__((always_inline)) -> U16 {
+    if constexpr (XPACK) {
+      // opaque copies: the widened values are loop-invariant, and hoisting
+      // them out of the chunk loop would rebuild the fp32 copy of x
+      uint32_t lo = xa[kb >> 1].w[(kb & 1) * 2], hi = xa[kb >> 1].w[(kb & 1) * 2 + 1];
+      asm volatile("" : "+v"(lo), "+v"(hi));
+      U16 a;
+      a.w[0] = lo << 16;
+      a.w[1] = lo & 0xFFFF0000u;
+      a.w[2] = hi << 16;
+      a.w[3] = hi & 0xFFFF0000u;
+      return a;
+    } else {
+      return xa[kb];
+    }
+  };
 
   // Per-lane state for the C rows wrow0 + 4q + r, r < 4: validity and the row
   // of eps / outputs they own (invalid rows read the tile's first row's noise,
@@ -352,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
   // contiguous too. Fragment lane fl holds expert column nt * 16 + (fl & 15),
   // K unit kb * 4 + (fl >> 4).
   U16 stage[LOAD_ITERS];
-  auto gload = [&](int c) {
+  auto gload = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < LOAD_ITERS; ++it) {
       const int u = tid + it * kThreads;
@@ -365,18 +396,20 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
         // experts past n read row n - 1; their logits are masked in the epilogue
         const int e = min(cbase + c * EC + nt * 16 + (fl & 15), n - 1);
         const CT* w = reinterpret_cast<const CT*>(m ? p.wn : p.wg);
-        stage[it] = ld_unit(w + (int64_t)e * D + (kb * 4 + (fl >> 4)) * UE);
+        const int koff = XPACK ? (kb >> 1) * 32 + (fl >> 4) * 8 + (kb & 1) * 4
+                               : (kb * 4 + (fl >> 4)) * UE;
+        stage[it] = ld_unit(w + (int64_t)e * D + koff);
       }
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < LOAD_ITERS; ++it) {
       const int u = tid + it * kThreads;
       if (CHUNK_UNITS % kThreads == 0 || u < CHUNK_UNITS) wbuf[buf][u] = stage[it];
     }
   };
-  auto mfma_chunk = [&](int buf, f32x4 (&acc)[NM][NT]) {
+  auto mfma_chunk = [&](int buf, f32x4 (&acc)[NM][NT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -387,14 +420,15 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          Mfma<CT>::k16(acc[m][nt], xa[kb], wbuf[buf][((kb * NM + m) * NT + nt) * 64 + lane]);
+          Mfma<CT>::k16(acc[m][nt], x_operand(kb),
+                        wbuf[buf][((kb * NM + m) * NT + nt) * 64 + lane]);
   };
   // Noise draws and biases of a chunk. Addresses are clamped into range and
   // invalid entries are masked later by selects, so no branch splits the block
   // that overlaps the matrix products with the epilogue.
   const bool has_bias = p.bias != nullptr;
   const float* bias_src = has_bias ? p.bias : reinterpret_cast<const float*>(p.wg);
-  auto load_eps = [&](int c, float (&ev)[NT][4], float (&bv)[NT]) {
+  auto load_eps = [&](int c, float (&ev)[NT][4], float (&bv)[NT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int e = min(cbase + c * EC + nt * 16 + lr, n - 1);
@@ -434,11 +468,11 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateParams p) {
     float hv[NT][4];
     bool cand_any = false;
     float colsum[NT];
-    auto products = [&]() {
+    auto products = [&]() __attribute__((always_inline)) {
       load_eps(more ? c + 1 : c, ev_next, bv_next);
       mfma_chunk((c + 1) & 1, acc_next);
     };
-    auto epilogue = [&]() {
+    auto epilogue = [&]() __attribute__((always_inline)) {
       // branch-free: invalid rows/experts are masked by selects
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {

@@ -62,13 +62,18 @@ hipError_t launch_gate(const GateLaunch& g, int32_t* topk_idx, float* topk_gate,
 // (token, expert) against the row's k-th logit and writes per-block column sums
 // partial [blocks][n]; corrects the selected pairs to the (k+1)-th threshold
 // from the routed rows (offsets / perm_token of the route of this selection)
-// into corr [n]; then reduces both into load [n].
+// into corr (corr_bytes of the pairs over n experts); then reduces both into
+// load [n].
 int gate_blocks(int64_t tokens);
-// The selected pairs' corrections are summed in up to kCorrSplitsMax slices
-// per expert (corr holds [n][kCorrSplitsMax] floats); corr_splits gives the
-// count used for `pairs` routed rows over n experts.
-constexpr int kCorrSplitsMax = 16;
-int corr_splits(int64_t pairs, int n);
+// The selected pairs' corrections are summed over slices of at most
+// kCorrSliceRows routed rows of one expert, one workgroup each, so that an
+// expert with many rows is spread over many workgroups. The corr region of
+// corr_bytes(pairs, n) bytes holds one float per slice (at most
+// corr_slices_max(pairs, n) slices), then each expert's first slice [n + 1]
+// (int32).
+constexpr int kCorrSliceRows = 256;
+int64_t corr_slices_max(int64_t pairs, int n);
+size_t corr_bytes(int64_t pairs, int n);
 hipError_t launch_load(const GateLaunch& g, const float* thresh, const int32_t* offsets,
                        const int32_t* perm_token, float* partial, float* corr, float* load,
                        hipStream_t s);
