@@ -672,8 +672,14 @@ static int ffn_part_rows(int64_t rows, int d, Dt dt) {
   return (int)std::min<int64_t>(ffn_rows_per_block(d, dt), rows);
 }
 
+// Units the plan can list: every unit has at least one row, so at most the
+// rows as well as at most ffn_max_blocks (before the split over hidden ranges).
+static int64_t ffn_units_max(int64_t rows, int n, int d, Dt dt) {
+  return std::min<int64_t>(ffn_max_blocks(rows, n, d, dt), rows);
+}
+
 static size_t ffn_list_bytes(int64_t rows, int n, int d, int h, Dt dt) {
-  const size_t b = (size_t)(4 + 4 * ffn_max_blocks(rows, n, d, dt) * ffn_hsplit(rows, n, d, h, dt)) *
+  const size_t b = (size_t)(4 + 4 * ffn_units_max(rows, n, d, dt) * ffn_hsplit(rows, n, d, h, dt)) *
                    sizeof(int32_t);
   return (b + 255) / 256 * 256;
 }
@@ -682,7 +688,7 @@ size_t ffn_plan_bytes(int64_t rows, int n, int d, int h, Dt dt) {
   const int hs = ffn_hsplit(rows, n, d, h, dt);
   size_t b = ffn_list_bytes(rows, n, d, h, dt);
   if (hs > 1)
-    b += (size_t)ffn_max_blocks(rows, n, d, dt) * hs * ffn_part_rows(rows, d, dt) * d *
+    b += (size_t)ffn_units_max(rows, n, d, dt) * hs * ffn_part_rows(rows, d, dt) * d *
          sizeof(float);
   return b;
 }
