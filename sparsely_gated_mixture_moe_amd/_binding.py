@@ -81,6 +81,7 @@ def lib():
         L.moe_combine.argtypes = [D, _P, _P, _P, _P, _P]
         L.moe_aux_losses.argtypes = [D, O, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
         L.moe_forward.argtypes = [D, O] + [_P] * 19 + [S, _P]
+        L.moe_forward_noalloc.argtypes = [D, O] + [_P] * 18 + [_P]
         HD = ctypes.POINTER(MoeHierDims)
         L.moe_hier_workspace_size.argtypes = [HD, O]
         L.moe_hier_workspace_size.restype = ctypes.c_size_t
@@ -93,7 +94,7 @@ def lib():
         L.moe_ffn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_double)]
         for f in ("moe_gate", "moe_route", "moe_expert_ffn", "moe_combine", "moe_aux_losses",
-                  "moe_forward", "moe_hier_forward", "moe_batchwise_forward", "moe_ffn_timing",
+                  "moe_forward", "moe_forward_noalloc", "moe_hier_forward", "moe_batchwise_forward", "moe_ffn_timing",
                   "moe_ffn_timing_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -386,6 +387,61 @@ def moe_forward(x, w_gate, w_noise, eps, w1, w2, k: int, *, b1=None, b2=None, ga
     y = f(x, eps, **extra, stream=stream)
     out = {"y": y, "importance": f.importance, "load": f.load, "losses": f.losses}
     out.update(extra)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
+
+
+def moe_forward_noalloc(x, w_gate, w_noise, eps, w1, w2, k: int, *, y=None, importance=None,
+                        load=None, losses=None, b1=None, b2=None, gate_bias=None,
+                        train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
+                        w_load: float = 0.1, capacity: int = 0, gate_order: int = 0,
+                        topk_idx=None, topk_gate=None, thresh=None, counts=None, perm_token=None,
+                        stream=None):
+    """The whole forward pass through ``moe_forward_noalloc``: the library
+    takes its workspace from its static per-device scratch (no allocation by
+    the library; outputs not given are allocated here by torch). Returns a dict
+    of the outputs."""
+    B, d = x.shape
+    n, h, _ = w1.shape
+    _dev(x, "x", w1.dtype, (B, d))
+    _dev(w_gate, "w_gate", shape=(n, d))
+    _dev(w_noise, "w_noise", w_gate.dtype, (n, d))
+    _dev(w2, "w2", w1.dtype, (n, d, h))
+    _dev(b1, "b1", w1.dtype, (n, h))
+    _dev(b2, "b2", w1.dtype, (n, d))
+    _dev(gate_bias, "gate_bias", torch.float32, (n,))
+    _dev(eps if train else None, "eps", torch.float32, (B, n))
+    dev = x.device
+    y = torch.empty((B, d), dtype=x.dtype, device=dev) if y is None else y
+    importance = torch.empty(n, dtype=torch.float32, device=dev) if importance is None else importance
+    load = torch.empty(n, dtype=torch.float32, device=dev) if load is None else load
+    losses = torch.empty(3, dtype=torch.float32, device=dev) if losses is None else losses
+    _dev(y, "y", x.dtype, (B, d))
+    for name, t, dt, shp in (("importance", importance, torch.float32, (n,)),
+                             ("load", load, torch.float32, (n,)),
+                             ("losses", losses, torch.float32, (3,)),
+                             ("topk_idx", topk_idx, torch.int32, (B, k)),
+                             ("topk_gate", topk_gate, torch.float32, (B, k)),
+                             ("thresh", thresh, torch.float32, (B, 2)),
+                             ("counts", counts, torch.int32, (n,)),
+                             ("perm_token", perm_token, torch.int32, (B * k,))):
+        _dev(t, name, dt, shp)
+    dims = make_dims(B, d, h, n, k, _dt(x), _dt(w1), _dt(w_gate), capacity)
+    opts = make_opts(train, noise_floor, w_importance, w_load, gate_order)
+    st = lib().moe_forward_noalloc(ctypes.byref(dims), ctypes.byref(opts), _ptr(x), _ptr(w_gate),
+                                   _ptr(w_noise), _ptr(gate_bias), _ptr(eps if train else None),
+                                   _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(y),
+                                   _ptr(importance), _ptr(load), _ptr(losses), _ptr(topk_idx),
+                                   _ptr(topk_gate), _ptr(thresh), _ptr(counts), _ptr(perm_token),
+                                   _stream(stream))
+    _check(st, "moe_forward_noalloc")
+    out = {"y": y, "importance": importance, "load": load, "losses": losses}
+    for name, t in (("topk_idx", topk_idx), ("topk_gate", topk_gate), ("thresh", thresh),
+                    ("counts", counts), ("perm_token", perm_token)):
+        if t is not None:
+            out[name] = t
     return out
 
 

@@ -600,6 +600,37 @@ moe_status moe_forward(const moe_dims* dims, const moe_gate_opts* opts, const vo
 
 namespace {
 
+// The static scratch of moe_forward_noalloc: each device the library runs on
+// holds its own copy until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address); it uses the address hipGetSymbolAddress gives for the current
+// device, kept per device on the device's first call.
+__device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "moe_forward_noalloc (current device)");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_forward_noalloc: device %d, at most %d devices", dev,
+                kScratchDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, "moe_forward_noalloc (scratch address)");
+    if (!p || !aligned(p, kAlign))
+      return fail(MOE_ERR_DEVICE, "moe_forward_noalloc: scratch address %p is not usable", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 moe_status check_batchwise(const moe_dims* d, const moe_gate_opts* o, int32_t m) {
   moe_status s;
   if ((s = check_dims(d)) != MOE_OK || (s = check_opts(o)) != MOE_OK) return s;
@@ -619,6 +650,28 @@ moe_status check_batchwise(const moe_dims* d, const moe_gate_opts* o, int32_t m)
 }
 
 }  // namespace
+
+moe_status moe_forward_noalloc(const moe_dims* dims, const moe_gate_opts* opts, const void* x,
+                               const void* w_gate, const void* w_noise, const float* gate_bias,
+                               const float* eps, const void* w1, const void* b1, const void* w2,
+                               const void* b2, void* y, float* importance, float* load,
+                               float* losses, int32_t* topk_idx_out, float* topk_gate_out,
+                               float* thresh_out, int32_t* counts_out, int32_t* perm_token_out,
+                               void* stream) {
+  moe_status s;
+  if ((s = check_dims(dims)) != MOE_OK || (s = check_opts(opts)) != MOE_OK) return s;
+  const size_t need = layout(dims, opts).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: these dims need %zu bytes of scratch, more than the "
+                "library's static %zu bytes (use moe_forward with a workspace)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != MOE_OK) return s;
+  return moe_forward(dims, opts, x, w_gate, w_noise, gate_bias, eps, w1, b1, w2, b2, y,
+                     importance, load, losses, topk_idx_out, topk_gate_out, thresh_out, counts_out,
+                     perm_token_out, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 size_t moe_batchwise_workspace_size(const moe_dims* dims, const moe_gate_opts* opts,
                                     int32_t rows_per_expert) {

@@ -30,7 +30,7 @@ def test_header_symbols_are_exported():
     assert "moe_forward" in names and len(names) >= 10
     for name in names:
         assert hasattr(L, name), f"{name} declared in moe.h but not exported"
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
 
 
 def dims(**kw):
@@ -219,3 +219,14 @@ def test_batchwise_pointer_and_workspace_checks():
     assert call_batchwise(d, o, 64, y=FAKE + 2) == INVALID and "aligned" in last_error()
     assert call_batchwise(d, o, 64, ws_bytes=need - 1) == WORKSPACE
     assert call_batchwise(d, o, 64, ws=FAKE + 16, ws_bytes=need) == INVALID
+
+
+def test_noalloc_rejects_dims_beyond_its_scratch():
+    """moe_forward_noalloc refuses dims whose workspace exceeds the static
+    scratch before any device call (the pointers here are fake)."""
+    L = B.lib()
+    d, o = dims(tokens=65536, n_experts=4096), opts()
+    assert L.moe_workspace_size(ctypes.byref(d), ctypes.byref(o)) > B.NOALLOC_SCRATCH_BYTES
+    st = L.moe_forward_noalloc(ctypes.byref(d), ctypes.byref(o), *([P()] * 18), None)
+    assert st == WORKSPACE
+    assert "static" in last_error() and str(B.NOALLOC_SCRATCH_BYTES) in last_error()
