@@ -82,6 +82,9 @@ def lib():
         L.moe_aux_losses.argtypes = [D, O, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
         L.moe_forward.argtypes = [D, O] + [_P] * 19 + [S, _P]
         L.moe_forward_noalloc.argtypes = [D, O] + [_P] * 18 + [_P]
+        L.moe_backward_workspace_size.argtypes = [D, O]
+        L.moe_backward_workspace_size.restype = ctypes.c_size_t
+        L.moe_backward.argtypes = [D, O] + [_P] * 15 + [ctypes.c_float] + [_P] * 9 + [S, _P]
         HD = ctypes.POINTER(MoeHierDims)
         L.moe_hier_workspace_size.argtypes = [HD, O]
         L.moe_hier_workspace_size.restype = ctypes.c_size_t
@@ -94,7 +97,8 @@ def lib():
         L.moe_ffn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_int64),
                                           ctypes.POINTER(ctypes.c_double)]
         for f in ("moe_gate", "moe_route", "moe_expert_ffn", "moe_combine", "moe_aux_losses",
-                  "moe_forward", "moe_forward_noalloc", "moe_hier_forward", "moe_batchwise_forward", "moe_ffn_timing",
+                  "moe_forward", "moe_forward_noalloc", "moe_backward", "moe_hier_forward",
+                  "moe_batchwise_forward", "moe_ffn_timing",
                   "moe_ffn_timing_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -442,6 +446,63 @@ def moe_forward_noalloc(x, w_gate, w_noise, eps, w1, w2, k: int, *, y=None, impo
                     ("counts", counts), ("perm_token", perm_token)):
         if t is not None:
             out[name] = t
+    return out
+
+
+def moe_backward(x, w_gate, w_noise, eps, w1, w2, k: int, topk_idx, topk_gate, thresh, importance,
+                 load, dy, *, b1=None, b2=None, gate_bias=None, train: bool = True,
+                 noise_floor: float = 1e-2, w_importance: float = 0.1, w_load: float = 0.1,
+                 aux_scale: float = 1.0, ws: Optional[torch.Tensor] = None,
+                 stream=None) -> Dict[str, torch.Tensor]:
+    """Gradients (fp32) of sum dy . y + aux_scale * (weighted losses) for x and
+    every parameter, from a forward pass's selection, thresholds, Importance
+    and Load: dx, dw_gate, dw_noise, dw1, dw2, plus dgate_bias / db1 / db2 for
+    the biases that are given."""
+    B, d = x.shape
+    n, h, _ = w1.shape
+    _dev(x, "x", w1.dtype, (B, d))
+    _dev(w_gate, "w_gate", shape=(n, d))
+    _dev(w_noise, "w_noise", w_gate.dtype, (n, d))
+    _dev(w2, "w2", w1.dtype, (n, d, h))
+    _dev(b1, "b1", w1.dtype, (n, h))
+    _dev(b2, "b2", w1.dtype, (n, d))
+    _dev(gate_bias, "gate_bias", torch.float32, (n,))
+    _dev(eps if train else None, "eps", torch.float32, (B, n))
+    _dev(topk_idx, "topk_idx", torch.int32, (B, k))
+    _dev(topk_gate, "topk_gate", torch.float32, (B, k))
+    _dev(thresh, "thresh", torch.float32, (B, 2))
+    _dev(importance, "importance", torch.float32, (n,))
+    _dev(load, "load", torch.float32, (n,))
+    _dev(dy, "dy", x.dtype, (B, d))
+    dims = make_dims(B, d, h, n, k, _dt(x), _dt(w1), _dt(w_gate))
+    opts = make_opts(train, noise_floor, w_importance, w_load)
+    dev = x.device
+    if ws is None:
+        nbytes = int(lib().moe_backward_workspace_size(ctypes.byref(dims), ctypes.byref(opts)))
+        if nbytes == 0:
+            _check(1, "moe_backward_workspace_size")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    out = {"dx": torch.empty((B, d), dtype=f32, device=dev),
+           "dw_gate": torch.empty((n, d), dtype=f32, device=dev),
+           "dw_noise": torch.empty((n, d), dtype=f32, device=dev),
+           "dw1": torch.empty((n, h, d), dtype=f32, device=dev),
+           "dw2": torch.empty((n, d, h), dtype=f32, device=dev)}
+    if gate_bias is not None:
+        out["dgate_bias"] = torch.empty(n, dtype=f32, device=dev)
+    if b1 is not None:
+        out["db1"] = torch.empty((n, h), dtype=f32, device=dev)
+    if b2 is not None:
+        out["db2"] = torch.empty((n, d), dtype=f32, device=dev)
+    st = lib().moe_backward(ctypes.byref(dims), ctypes.byref(opts), _ptr(x), _ptr(w_gate),
+                            _ptr(w_noise), _ptr(gate_bias), _ptr(eps if train else None),
+                            _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(topk_idx),
+                            _ptr(topk_gate), _ptr(thresh), _ptr(importance), _ptr(load), _ptr(dy),
+                            ctypes.c_float(aux_scale), _ptr(out["dx"]), _ptr(out["dw_gate"]),
+                            _ptr(out["dw_noise"]), _ptr(out.get("dgate_bias")), _ptr(out["dw1"]),
+                            _ptr(out.get("db1")), _ptr(out["dw2"]), _ptr(out.get("db2")),
+                            _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "moe_backward")
     return out
 
 

@@ -673,6 +673,91 @@ moe_status moe_forward_noalloc(const moe_dims* dims, const moe_gate_opts* opts, 
                      perm_token_out, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+size_t moe_backward_workspace_size(const moe_dims* dims, const moe_gate_opts* opts) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  if (opts && check_opts(opts) != MOE_OK) return 0;
+  return moe::backward_ws_bytes(dims->tokens, dims->n_experts, dims->k, dims->d_model,
+                                dims->d_hidden, to_dt(dims->act_dtype));
+}
+
+moe_status moe_backward(const moe_dims* dims, const moe_gate_opts* opts, const void* x,
+                        const void* w_gate, const void* w_noise, const float* gate_bias,
+                        const float* eps, const void* w1, const void* b1, const void* w2,
+                        const void* b2, const int32_t* topk_idx, const float* topk_gate,
+                        const float* thresh, const float* importance, const float* load,
+                        const void* dy, float aux_scale, float* dx, float* dw_gate,
+                        float* dw_noise, float* dgate_bias, float* dw1, float* db1, float* dw2,
+                        float* db2, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s;
+  if ((s = check_dims(dims)) != MOE_OK || (s = check_opts(opts)) != MOE_OK) return s;
+  if (dims->capacity != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward: capacity must be 0");
+  if (opts->gate_order != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward: gate_order must be 0");
+  if (!std::isfinite(aux_scale)) return fail(MOE_ERR_INVALID, "aux_scale must be finite");
+  if ((s = check_gate_args(dims, opts, x, w_gate, w_noise, gate_bias, eps, true)) != MOE_OK) return s;
+  REQ(w1, 16);
+  REQ(w2, 16);
+  OPT(b1, 4);
+  OPT(b2, 4);
+  REQN(topk_idx, 4, dims->tokens);
+  REQN(topk_gate, 4, dims->tokens);
+  REQN(thresh, 4, dims->tokens);
+  REQ(importance, 4);
+  REQ(load, 4);
+  REQN(dy, 16, dims->tokens);
+  REQN(dx, 16, dims->tokens);
+  REQ(dw_gate, 16);
+  REQ(dw_noise, 16);
+  OPT(dgate_bias, 4);
+  REQ(dw1, 16);
+  OPT(db1, 4);
+  REQ(dw2, 16);
+  OPT(db2, 4);
+  if (!moe::ffn_supported(dims->d_model, dims->d_hidden, to_dt(dims->act_dtype)))
+    return fail(MOE_ERR_UNSUPPORTED, "expert_ffn: unsupported shape");
+  const size_t need = moe::backward_ws_bytes(dims->tokens, dims->n_experts, dims->k,
+                                             dims->d_model, dims->d_hidden, to_dt(dims->act_dtype));
+  if ((s = check_ws(ws, ws_bytes, need)) != MOE_OK) return s;
+  moe::BackwardLaunch b;
+  b.tokens = dims->tokens;
+  b.d = dims->d_model;
+  b.h = dims->d_hidden;
+  b.n = dims->n_experts;
+  b.k = dims->k;
+  b.act_dt = to_dt(dims->act_dtype);
+  b.gate_dt = to_dt(dims->gate_dtype);
+  b.train = opts->train;
+  b.noise_floor = opts->noise_floor;
+  b.w_importance = opts->w_importance;
+  b.w_load = opts->w_load;
+  b.aux_scale = aux_scale;
+  b.x = x;
+  b.w_gate = w_gate;
+  b.w_noise = w_noise;
+  b.gate_bias = gate_bias;
+  b.eps = opts->train ? eps : nullptr;
+  b.w1 = w1;
+  b.b1 = b1;
+  b.w2 = w2;
+  b.b2 = b2;
+  b.topk_idx = topk_idx;
+  b.topk_gate = topk_gate;
+  b.thresh = thresh;
+  b.importance = importance;
+  b.load = load;
+  b.dy = dy;
+  b.dx = dx;
+  b.dw_gate = dw_gate;
+  b.dw_noise = dw_noise;
+  b.dgate_bias = dgate_bias;
+  b.dw1 = dw1;
+  b.db1 = db1;
+  b.dw2 = dw2;
+  b.db2 = db2;
+  return device_status(moe::launch_backward(b, ws, (hipStream_t)stream), "moe_backward");
+}
+
 size_t moe_batchwise_workspace_size(const moe_dims* dims, const moe_gate_opts* opts,
                                     int32_t rows_per_expert) {
   if (check_batchwise(dims, opts, rows_per_expert) != MOE_OK) return 0;

@@ -185,6 +185,29 @@ void batchwise_carve(BatchwiseLaunch& b, void* ws, int d, int h, Dt act_dt);
 hipError_t launch_batchwise(const BatchwiseLaunch& b, hipStream_t s, hipEvent_t ev0 = nullptr,
                             hipEvent_t ev1 = nullptr);
 
+// Backward pass: gradients of sum dy . y + aux_scale (w_importance CV^2(Imp) +
+// w_load CV^2(Load)) for x and every parameter (fp32), from the forward's
+// selection (topk_idx / topk_gate), thresholds, Importance and Load, with the
+// hidden activations recomputed. backward_ws_bytes sizes its workspace.
+struct BackwardLaunch {
+  int64_t tokens = 0;
+  int d = 0, h = 0, n = 0, k = 0;
+  Dt act_dt = kBF16, gate_dt = kBF16;  // experts share the activations' type
+  int train = 1;
+  float noise_floor = 0.f, w_importance = 0.f, w_load = 0.f, aux_scale = 1.f;
+  const void *x = nullptr, *w_gate = nullptr, *w_noise = nullptr;
+  const float* gate_bias = nullptr;
+  const float* eps = nullptr;
+  const void *w1 = nullptr, *b1 = nullptr, *w2 = nullptr, *b2 = nullptr;
+  const int32_t* topk_idx = nullptr;
+  const float *topk_gate = nullptr, *thresh = nullptr, *importance = nullptr, *load = nullptr;
+  const void* dy = nullptr;
+  float *dx = nullptr, *dw_gate = nullptr, *dw_noise = nullptr, *dgate_bias = nullptr;
+  float *dw1 = nullptr, *db1 = nullptr, *dw2 = nullptr, *db2 = nullptr;
+};
+size_t backward_ws_bytes(int64_t tokens, int n, int k, int d, int h, Dt act_dt);
+hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s);
+
 // Load as the hard count (train = 0) and the CV^2 losses.
 hipError_t launch_counts_to_load(const int32_t* counts, int n, float* load, hipStream_t s);
 hipError_t launch_offsets_to_load(const int32_t* offsets, int n, float* load, hipStream_t s);

@@ -30,7 +30,7 @@ def test_header_symbols_are_exported():
     assert "moe_forward" in names and len(names) >= 10
     for name in names:
         assert hasattr(L, name), f"{name} declared in moe.h but not exported"
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
 
 
 def dims(**kw):
@@ -230,3 +230,35 @@ def test_noalloc_rejects_dims_beyond_its_scratch():
     st = L.moe_forward_noalloc(ctypes.byref(d), ctypes.byref(o), *([P()] * 18), None)
     assert st == WORKSPACE
     assert "static" in last_error() and str(B.NOALLOC_SCRATCH_BYTES) in last_error()
+
+
+def call_backward(d, o, ws=FAKE, ws_bytes=1 << 40, aux=1.0, dw1=FAKE, dy=FAKE, topk=FAKE):
+    L = B.lib()
+    return L.moe_backward(ctypes.byref(d), ctypes.byref(o), P(), P(), P(), None, P(), P(), None,
+                          P(), None, P(topk), P(), P(), P(), P(), P(dy), ctypes.c_float(aux), P(),
+                          P(), P(), None, P(dw1), None, P(), None, P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,okw,aux,status,msg", [
+    ({"capacity": 8}, {}, 1.0, UNSUPPORTED, "capacity"),
+    ({}, {"gate_order": 1}, 1.0, UNSUPPORTED, "gate_order"),
+    ({}, {}, float("inf"), INVALID, "aux_scale"),
+    ({"k": 9, "n_experts": 100}, {}, 1.0, UNSUPPORTED, "k = 9"),
+    ({"d_hidden": 100}, {}, 1.0, UNSUPPORTED, "d_hidden"),
+])
+def test_backward_invalid_arguments(kw, okw, aux, status, msg):
+    assert call_backward(dims(**kw), opts(**okw), aux=aux) == status
+    assert msg in last_error()
+
+
+def test_backward_pointer_and_workspace_checks():
+    L = B.lib()
+    d, o = dims(), opts()
+    need = L.moe_backward_workspace_size(ctypes.byref(d), ctypes.byref(o))
+    # recomputed hidden rows, their gradients and the dense gate-logit gradients
+    assert need >= 1024 * 4 * 1024 * 4 + 1024 * 2 * 64 * 4
+    assert call_backward(d, o, dw1=0) == INVALID and "dw1 is NULL" in last_error()
+    assert call_backward(d, o, dy=FAKE + 4) == INVALID and "dy" in last_error()
+    assert call_backward(d, o, topk=0) == INVALID and "topk_idx" in last_error()
+    assert call_backward(d, o, ws_bytes=need - 256) == WORKSPACE and "needed" in last_error()
+    assert call_backward(d, o, ws=FAKE + 16, ws_bytes=need) == INVALID
