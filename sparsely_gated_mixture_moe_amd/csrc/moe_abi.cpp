@@ -211,8 +211,9 @@ moe_status check_gate_args(const moe_dims* d, const moe_gate_opts* o, const void
   REQ(wg, 16);
   if (o->train) REQ(wn, 16);
   else OPT(wn, 16);
-  OPT(bias, 4);
-  if (o->train && need_eps) REQN(eps, 4, d->tokens);
+  // the gate kernels copy biases and noise rows to LDS 16 bytes at a time
+  OPT(bias, 16);
+  if (o->train && need_eps) REQN(eps, 16, d->tokens);
   if (!moe::gate_supported(d->d_model, to_dt(d->act_dtype), to_dt(d->gate_dtype), d->k))
     return fail(MOE_ERR_UNSUPPORTED, "gate: unsupported shape or dtype combination");
   return MOE_OK;
@@ -844,8 +845,8 @@ moe_status moe_hier_forward(const moe_hier_dims* dims, const moe_gate_opts* opts
   if (opts->train) {
     REQ(w_noise1, 16);
     REQ(w_noise2, 16);
-    REQN(eps1, 4, B);
-    REQN(eps2, 4, B);
+    REQN(eps1, 16, B);
+    REQN(eps2, 16, B);
   } else {
     OPT(w_noise1, 16);
     OPT(w_noise2, 16);

@@ -89,6 +89,12 @@ def test_null_and_misaligned_pointers():
     assert call_gate(dims(), opts(), x=0) == INVALID and "x is NULL" in last_error()
     assert call_gate(dims(), opts(), x=FAKE + 4) == INVALID and "aligned" in last_error()
     assert call_gate(dims(), opts(), eps=0) == INVALID and "eps" in last_error()
+    # biases and noise rows are copied 16 bytes at a time: a 4-byte offset view is refused
+    assert call_gate(dims(), opts(), eps=FAKE + 4) == INVALID and "eps is not 16-byte" in last_error()
+    L = B.lib()
+    st = L.moe_gate(ctypes.byref(dims()), ctypes.byref(opts()), P(), P(), P(), P(FAKE + 4), P(),
+                    P(), P(), P(), None, 0, None)
+    assert st == INVALID and "bias is not 16-byte" in last_error()
     assert call_gate(dims(), opts(train=2)) == INVALID
     assert call_gate(dims(), opts(noise_floor=-1.0)) == INVALID
     assert call_gate(dims(), opts(noise_floor=float("nan"))) == INVALID
