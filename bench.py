@@ -376,6 +376,75 @@ def bench_batchwise(a, w, g, moe, torch):
     print(json.dumps(result), flush=True)
 
 
+def bench_backward(a, w, g, moe, torch, np, dg):
+    """The backward pass (moe_backward): one step = one call computing the
+    gradients of sum dy . y + the weighted losses for x, the gate weights and
+    bias and every expert's weights and biases, from one forward pass's
+    selection, thresholds, Importance and Load (recomputing the experts'
+    hidden activations)."""
+    B, d, h, n, k = w.tokens, w.d_model, w.d_hidden, w.n_experts, w.k
+    fwd = moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], k,
+                          gate_bias=g.get("gate_bias"), train=True, return_routing=True)
+    dy = torch.empty_like(g["x"]).normal_()
+    dims = moe.make_dims(B, d, h, n, k, moe._binding._dt(g["x"]), moe._binding._dt(g["w1"]),
+                         moe._binding._dt(g["w_gate"]))
+    nbytes = int(moe.lib().moe_backward_workspace_size(ctypes_byref(dims),
+                                                        ctypes_byref(moe.make_opts())))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=g["x"].device)
+
+    def step():
+        moe.moe_backward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], k,
+                         fwd["topk_idx"], fwd["topk_gate"], fwd["thresh"], fwd["importance"],
+                         fwd["load"], dy, gate_bias=g.get("gate_bias"), ws=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    per_step, total_ms = time_steps(step, a.steps, torch)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = median(per_step)
+    log(f"backward {ms_step:.3f} ms/step median")
+    cnt = fwd["counts"].cpu().numpy()
+    rows = int(cnt.sum())
+    used = int((cnt > 0).sum())
+    esize = 2 if w.expert_dtype == dg.BF16 else 4
+    # expert products: hidden, E, dA, dW2, dW1, dx rows (2 d h flops per routed row each);
+    # gate: c and u, dW_g and dW_noise, dx (2 d n flops per token each, twice)
+    flops = 6 * 2.0 * rows * d * h + 3 * 2 * 2.0 * B * d * n
+    # expert weights read, their fp32 gradients written; the dense [B, 2n] fp32 logit
+    # gradients written and read twice; x, dy, dx
+    nbytes_alg = (used * 2 * d * h * (esize + 4) + 3 * B * 2 * n * 4
+                  + 2 * B * d * esize + B * d * 4)
+    t = ms_step * 1e-3
+    # bf16 storage: the products run on the bf16 matrix cores (fp32 operands split into
+    # two bf16 parts); fp32 storage: on the fp32 matrix cores
+    peak = BF16_PEAK_TFLOPS if esize == 2 else FP32_PEAK_TFLOPS
+    result = {
+        "metric": "MoE-layer backward tokens/sec (4096 experts, k = 4)",
+        "value": B / t, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if esize == 2 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "n_experts": n,
+                   "k": k, "pass": "backward", "storage": "bf16" if esize == 2 else "f32"},
+        "roofline": {"kernel": "moe_backward (all kernels of one call)", "bound": "mfma",
+                     "achieved": flops / t / 1e12, "peak": peak, "unit": "TFLOP/s",
+                     "frac": flops / t / 1e12 / peak, "traffic": None,
+                     "alg_flops_per_launch": flops, "alg_bytes_per_launch": nbytes_alg,
+                     "hbm_frac": nbytes_alg / t / (HBM_PEAK_GBS * 1e9)},
+        "step": {"mean_ms": total_ms / a.steps, "min_ms": min(per_step), "max_ms": max(per_step)},
+        "wall_ms_per_step": 1000 * wall / a.steps,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def ctypes_byref(o):
+    import ctypes
+    return ctypes.byref(o)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -398,6 +467,8 @@ def main():
     ap.add_argument("--gating", default="topk", choices=("topk", "batchwise"),
                     help="batchwise: every expert takes its k B / n best rows of the batch "
                          "(moe_batchwise_forward) instead of every token its k best experts")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (moe_backward) instead of the forward")
     ap.add_argument("--train", type=int, default=1, choices=(0, 1),
                     help="1: noisy gating with the Load pass (the headline step); 0: inference")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -441,6 +512,9 @@ def main():
 
     if a.gating == "batchwise":
         bench_batchwise(a, w, g, moe, torch)
+        return
+    if a.backward:
+        bench_backward(a, w, g, moe, torch, np, dg)
         return
     cap = int(np.ceil(a.capacity_factor * B * k / n)) if a.capacity_factor > 0 else 0
     f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,

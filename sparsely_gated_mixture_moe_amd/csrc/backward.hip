@@ -266,6 +266,232 @@ __global__ __launch_bounds__(256) void wgrad_kernel(Wgrad p) {
 }
 
 // ---------------------------------------------------------------------------
+// The same products on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16), for
+// bf16 storage. Operands in bf16 storage are exact; an fp32 operand (the
+// recomputed hidden layer, the hidden and logit gradients) is split into
+// hi = bf16(v) and lo = bf16(v - hi), exact to about 2^-17 of v, and its
+// products take the hi and lo parts against the other operand (hi x lo'
+// cross terms of two split operands are kept, lo x lo' dropped). Row scales
+// (the gates) are applied where they keep an exact operand exact: in the row
+// products' epilogue, in the weight-gradient products to the split operand.
+// ---------------------------------------------------------------------------
+
+constexpr int kK16 = 32;  // K (or rows) per LDS step of the bf16 products
+constexpr int kP16 = 8;   // bf16 elements of padding per LDS row
+
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  const uint32_t h = f32_to_bf16_bits(v);
+  hi = (uint16_t)h;
+  lo = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(h));
+}
+
+__device__ __forceinline__ f32x4 mfma16(const U16& a, const U16& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_short8(a), as_short8(b), c, 0, 0, 0);
+}
+
+// Eight consecutive elements of row `row` from column `col` (zero past `lim`).
+template <typename T>
+__device__ __forceinline__ void load8_row(const void* base, int64_t row, int64_t ld, int col,
+                                          int lim, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (col + i < lim) ? ld_f<T>(base, row * ld + col + i) : 0.f;
+}
+
+template <typename TA, typename TW, typename TO, bool SA, bool SW>
+__global__ __launch_bounds__(256) void row_gemm16_kernel(RowGemm p) {
+  __shared__ __attribute__((aligned(16))) uint16_t ash[kT][kK16 + kP16];
+  __shared__ __attribute__((aligned(16))) uint16_t asl[SA ? kT : 1][kK16 + kP16];
+  __shared__ __attribute__((aligned(16))) uint16_t bsh[kT][kK16 + kP16];
+  __shared__ __attribute__((aligned(16))) uint16_t bsl[SW ? kT : 1][kK16 + kP16];
+  int g = 0;
+  int64_t r0, rend;
+  if (p.units) {
+    const int u = blockIdx.x;
+    if (u >= p.units[0]) return;
+    g = p.units[1 + 2 * u];
+    r0 = (int64_t)p.seg_off[g] + p.units[2 + 2 * u];
+    rend = p.seg_off[g + 1];
+  } else {
+    r0 = (int64_t)blockIdx.x * kT;
+    rend = p.rows;
+    if (r0 >= rend) return;
+  }
+  const int c0 = blockIdx.y * kT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, q = lane >> 4;
+  const char* wseg = reinterpret_cast<const char*>(p.w) + (int64_t)g * p.w_stride * sizeof(TW);
+  f32x4 acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // A: row tid / 4, K run (tid % 4) * 8 .. + 7
+  const int ar = tid >> 2, ak = (tid & 3) * 8;
+  const int64_t arow_p = r0 + ar;
+  const bool arow_ok = arow_p < rend;
+  const int64_t arow = arow_ok ? (p.gather ? (int64_t)p.gather[arow_p] : arow_p) : 0;
+  for (int k0 = 0; k0 < p.K; k0 += kK16) {
+    {
+      float v[8];
+      load8_row<TA>(p.a, arow, p.lda, k0 + ak, arow_ok ? p.K : 0, v);
+      uint16_t h[8], l[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) split_bf16(v[i], h[i], l[i]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ash[ar][ak + i] = h[i];
+      if constexpr (SA) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) asl[ar][ak + i] = l[i];
+      }
+    }
+    if (p.wt) {  // W [N][K]: 8 consecutive K of column n
+      const int n = tid >> 2, kq = (tid & 3) * 8;
+      float v[8];
+      load8_row<TW>(wseg, c0 + n, p.K, k0 + kq, (c0 + n < p.N) ? p.K : 0, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint16_t h, l;
+        split_bf16(v[i], h, l);
+        bsh[n][kq + i] = h;
+        if constexpr (SW) bsl[n][kq + i] = l;
+      }
+    } else {  // W [K][N]: 8 consecutive N of K row k
+      const int kr = tid >> 3, n8 = (tid & 7) * 8;
+      float v[8];
+      load8_row<TW>(wseg, k0 + kr, p.N, c0 + n8, (k0 + kr < p.K) ? p.N : 0, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint16_t h, l;
+        split_bf16(v[i], h, l);
+        bsh[n8 + i][kr] = h;
+        if constexpr (SW) bsl[n8 + i][kr] = l;
+      }
+    }
+    __syncthreads();
+    const U16 a = *reinterpret_cast<const U16*>(&ash[16 * wave + lr][8 * q]);
+    U16 al;
+    if constexpr (SA) al = *reinterpret_cast<const U16*>(&asl[16 * wave + lr][8 * q]);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const U16 b = *reinterpret_cast<const U16*>(&bsh[16 * ct + lr][8 * q]);
+      acc[ct] = mfma16(a, b, acc[ct]);
+      if constexpr (SA) acc[ct] = mfma16(al, b, acc[ct]);
+      if constexpr (SW) {
+        const U16 bl = *reinterpret_cast<const U16*>(&bsl[16 * ct + lr][8 * q]);
+        acc[ct] = mfma16(a, bl, acc[ct]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int c = c0 + 16 * ct + lr;
+    if (c >= p.N) continue;
+    float b = 0.f;
+    if (p.bias)
+      b = p.bias_f32 ? ld_f<float>(p.bias, (int64_t)g * p.N + c) : ld_f<TW>(p.bias, (int64_t)g * p.N + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t rp = r0 + 16 * wave + 4 * q + i;
+      if (rp >= rend) continue;
+      float v = acc[ct][i];
+      if (p.scale) v *= p.scale[rp];
+      v += b;
+      if (p.relu) v = v > 0.f ? v : 0.f;
+      if (p.mask) {
+        const float mv = p.mask_bf16 ? ld_f<bf16>(p.mask, rp * p.ldm + c)
+                                     : ld_f<float>(p.mask, rp * p.ldm + c);
+        v = mv > 0.f ? v : 0.f;
+      }
+      const int64_t o = rp * p.ldo + c;
+      if (p.accumulate) v += ld_f<TO>(p.out, o);
+      st_f<TO>(p.out, o, v);
+    }
+  }
+}
+
+template <typename TA, typename TB, bool SA, bool SB>
+__global__ __launch_bounds__(256) void wgrad16_kernel(Wgrad p) {
+  static_assert(SA || SB, "a row scale needs a split operand");
+  __shared__ __attribute__((aligned(16))) uint16_t ath[kT][kK16 + kP16];  // [m][row]
+  __shared__ __attribute__((aligned(16))) uint16_t atl[SA ? kT : 1][kK16 + kP16];
+  __shared__ __attribute__((aligned(16))) uint16_t bth[kT][kK16 + kP16];  // [n][row]
+  __shared__ __attribute__((aligned(16))) uint16_t btl[SB ? kT : 1][kK16 + kP16];
+  __shared__ float cst[kK16][kT + 1];  // the colsum's scaled A values, fp32
+  const int mtiles = (p.M + kT - 1) / kT;
+  const int m0 = (blockIdx.x % mtiles) * kT, n0 = (blockIdx.x / mtiles) * kT;
+  const int g = blockIdx.y;
+  const int64_t s0 = p.seg_off ? p.seg_off[g] : 0;
+  const int64_t s1 = p.seg_off ? p.seg_off[g + 1] : p.rows;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, q = lane >> 4;
+  const bool do_colsum = p.colsum != nullptr && n0 == 0;
+  f32x4 acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float cs = 0.f;
+  // loads: row tid / 8 of the step, 8 consecutive columns from (tid % 8) * 8
+  const int lrow = tid >> 3, lc = (tid & 7) * 8;
+  for (int64_t r = s0; r < s1; r += kK16) {
+    const int64_t rp = r + lrow;
+    const bool ok = rp < s1;
+    int64_t ra = 0, rb = 0;
+    float sa = 1.f, sb = 1.f;
+    if (ok) {
+      ra = p.a_gather ? (int64_t)p.a_gather[rp] : rp;
+      rb = p.b_gather ? (int64_t)p.b_gather[rp] : rp;
+      if (p.a_scale) sa = p.a_scale[rp];
+      if (p.b_scale) sb = p.b_scale[rp];
+    }
+    // the row's scale goes to a split operand, so that an exact one stays exact
+    const float s_a = SB ? 1.f : sa * sb, s_b = SB ? sa * sb : 1.f;
+    float va[8], vb[8];
+    load8_row<TA>(p.a, ra, p.lda, m0 + lc, ok ? p.M : 0, va);
+    load8_row<TB>(p.b, rb, p.ldb, n0 + lc, ok ? p.N : 0, vb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint16_t h, l;
+      split_bf16(s_a * va[i], h, l);
+      ath[lc + i][lrow] = h;
+      if constexpr (SA) atl[lc + i][lrow] = l;
+      split_bf16(s_b * vb[i], h, l);
+      bth[lc + i][lrow] = h;
+      if constexpr (SB) btl[lc + i][lrow] = l;
+      if (do_colsum) cst[lrow][lc + i] = sa * va[i];
+    }
+    __syncthreads();
+    if (do_colsum && tid < kT) {
+#pragma unroll
+      for (int i = 0; i < kK16; ++i) cs += cst[i][tid];
+    }
+    const U16 a = *reinterpret_cast<const U16*>(&ath[16 * wave + lr][8 * q]);
+    U16 al;
+    if constexpr (SA) al = *reinterpret_cast<const U16*>(&atl[16 * wave + lr][8 * q]);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const U16 b = *reinterpret_cast<const U16*>(&bth[16 * ct + lr][8 * q]);
+      acc[ct] = mfma16(a, b, acc[ct]);
+      if constexpr (SA) acc[ct] = mfma16(al, b, acc[ct]);
+      if constexpr (SB) {
+        const U16 bl = *reinterpret_cast<const U16*>(&btl[16 * ct + lr][8 * q]);
+        acc[ct] = mfma16(a, bl, acc[ct]);
+      }
+    }
+    __syncthreads();
+  }
+  float* og = p.out + (int64_t)g * p.out_stride;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int n = n0 + 16 * ct + lr;
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 16 * wave + 4 * q + i;
+      if (m < p.M) og[(int64_t)m * p.N + n] = acc[ct][i];
+    }
+  }
+  if (do_colsum && tid < kT && m0 + tid < p.M) p.colsum[(int64_t)g * p.M + m0 + tid] = cs;
+}
+
+// ---------------------------------------------------------------------------
 // Elementwise parts
 // ---------------------------------------------------------------------------
 
@@ -441,9 +667,22 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
-hipError_t run_row_gemm(const RowGemm& p, Dt ta, Dt tw, Dt to, int64_t grid_x, hipStream_t s) {
+// bf16 storage: the products on the bf16 matrix cores (fp32 operands split);
+// fp32 storage: on the fp32 matrix cores.
+hipError_t run_row_gemm(const RowGemm& p, Dt ta, Dt tw, Dt to, int64_t grid_x, hipStream_t s,
+                        bool bf16_cores = false) {
   if (grid_x <= 0) return hipSuccess;
   const dim3 grid((unsigned)grid_x, (unsigned)((p.N + kT - 1) / kT)), block(256);
+  if (bf16_cores && to == kF32) {
+#define MOE_RG16(A, W, SA, SW) \
+  hipLaunchKernelGGL((row_gemm16_kernel<A, W, float, SA, SW>), grid, block, 0, s, p)
+    if (ta == kBF16 && tw == kBF16) MOE_RG16(bf16, bf16, false, false);
+    else if (ta == kF32 && tw == kBF16) MOE_RG16(float, bf16, true, false);
+    else if (ta == kBF16 && tw == kF32) MOE_RG16(bf16, float, false, true);
+    else MOE_RG16(float, float, true, true);
+#undef MOE_RG16
+    return hipGetLastError();
+  }
 #define MOE_RG(A, W, O) hipLaunchKernelGGL((row_gemm_kernel<A, W, O>), grid, block, 0, s, p)
   if (ta == kBF16 && tw == kBF16 && to == kBF16) MOE_RG(bf16, bf16, bf16);
   else if (ta == kBF16 && tw == kBF16 && to == kF32) MOE_RG(bf16, bf16, float);
@@ -455,9 +694,19 @@ hipError_t run_row_gemm(const RowGemm& p, Dt ta, Dt tw, Dt to, int64_t grid_x, h
   return hipGetLastError();
 }
 
-hipError_t run_wgrad(const Wgrad& p, Dt ta, Dt tb, int nseg, hipStream_t s) {
+hipError_t run_wgrad(const Wgrad& p, Dt ta, Dt tb, int nseg, hipStream_t s,
+                     bool bf16_cores = false) {
   if (nseg <= 0) return hipSuccess;
   const dim3 grid((unsigned)(((p.M + kT - 1) / kT) * ((p.N + kT - 1) / kT)), (unsigned)nseg);
+  if (bf16_cores) {
+    if (ta == kBF16 && tb == kF32)
+      hipLaunchKernelGGL((wgrad16_kernel<bf16, float, false, true>), grid, dim3(256), 0, s, p);
+    else if (ta == kF32 && tb == kBF16)
+      hipLaunchKernelGGL((wgrad16_kernel<float, bf16, true, false>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((wgrad16_kernel<float, float, true, true>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
 #define MOE_WG(A, B_) hipLaunchKernelGGL((wgrad_kernel<A, B_>), grid, dim3(256), 0, s, p)
   if (ta == kBF16 && tb == kBF16) MOE_WG(bf16, bf16);
   else if (ta == kF32 && tb == kBF16) MOE_WG(float, bf16);
@@ -548,7 +797,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.relu = 1;
   r.out = hid;
   r.ldo = h;
-  if ((e = run_row_gemm(r, b.act_dt, b.act_dt, kF32, max_units, s)) != hipSuccess) return e;
+  if ((e = run_row_gemm(r, b.act_dt, b.act_dt, kF32, max_units, s, b.act_dt == kBF16)) != hipSuccess) return e;
   r = RowGemm{};
   r.units = units;
   r.seg_off = offsets;
@@ -563,7 +812,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.bias = b.b2;
   r.out = eo;
   r.ldo = d;
-  if ((e = run_row_gemm(r, kF32, b.act_dt, kF32, max_units, s)) != hipSuccess) return e;
+  if ((e = run_row_gemm(r, kF32, b.act_dt, kF32, max_units, s, b.act_dt == kBF16)) != hipSuccess) return e;
   // kept gates: task + Importance gradients through the kept softmax
   if (B > 0) {
     if (b.act_dt == kBF16)
@@ -592,7 +841,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.ldo = h;
   r.mask = hid;
   r.ldm = h;
-  if ((e = run_row_gemm(r, b.act_dt, b.act_dt, kF32, max_units, s)) != hipSuccess) return e;
+  if ((e = run_row_gemm(r, b.act_dt, b.act_dt, kF32, max_units, s, b.act_dt == kBF16)) != hipSuccess) return e;
   // dW2_e = sum (gate dy[token])^T hidden, db2_e = sum gate dy[token]
   Wgrad wg{};
   wg.seg_off = offsets;
@@ -608,7 +857,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   wg.out = b.dw2;
   wg.out_stride = (int64_t)d * h;
   wg.colsum = b.db2;
-  if ((e = run_wgrad(wg, b.act_dt, kF32, n, s)) != hipSuccess) return e;
+  if ((e = run_wgrad(wg, b.act_dt, kF32, n, s, b.act_dt == kBF16)) != hipSuccess) return e;
   // dW1_e = sum dA^T x[token], db1_e = sum dA
   wg = Wgrad{};
   wg.seg_off = offsets;
@@ -623,7 +872,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   wg.out = b.dw1;
   wg.out_stride = (int64_t)h * d;
   wg.colsum = b.db1;
-  if ((e = run_wgrad(wg, kF32, b.act_dt, n, s)) != hipSuccess) return e;
+  if ((e = run_wgrad(wg, kF32, b.act_dt, n, s, b.act_dt == kBF16)) != hipSuccess) return e;
   // dx per routed row: dA W1
   r = RowGemm{};
   r.units = units;
@@ -638,7 +887,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.N = d;
   r.out = dxe;
   r.ldo = d;
-  if ((e = run_row_gemm(r, kF32, b.act_dt, kF32, max_units, s)) != hipSuccess) return e;
+  if ((e = run_row_gemm(r, kF32, b.act_dt, kF32, max_units, s, b.act_dt == kBF16)) != hipSuccess) return e;
 
   // gate: c = x W_g^T + b, u = x W_noise^T into cu, then their gradients in place
   const int64_t rt = (B + kT - 1) / kT;
@@ -654,12 +903,12 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.bias_f32 = 1;
   r.out = cu;
   r.ldo = 2 * (int64_t)n;
-  if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s)) != hipSuccess) return e;
+  if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
   if (b.train) {
     r.w = b.w_noise;
     r.bias = nullptr;
     r.out = cu + n;
-    if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s)) != hipSuccess) return e;
+    if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
   }
   if (B > 0) {
     hipLaunchKernelGGL(pair_grad_kernel, dim3(blocks_for(B * n)), dim3(256), 0, s, B, n, k,
@@ -677,12 +926,12 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   wg.N = d;
   wg.out = b.dw_gate;
   wg.colsum = b.dgate_bias;
-  if ((e = run_wgrad(wg, kF32, b.act_dt, 1, s)) != hipSuccess) return e;
+  if ((e = run_wgrad(wg, kF32, b.act_dt, 1, s, b.act_dt == kBF16)) != hipSuccess) return e;
   if (b.train) {
     wg.a = cu + n;
     wg.out = b.dw_noise;
     wg.colsum = nullptr;
-    if ((e = run_wgrad(wg, kF32, b.act_dt, 1, s)) != hipSuccess) return e;
+    if ((e = run_wgrad(wg, kF32, b.act_dt, 1, s, b.act_dt == kBF16)) != hipSuccess) return e;
   } else {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for((int64_t)n * d)), dim3(256), 0, s,
                        b.dw_noise, (int64_t)n * d);
@@ -699,12 +948,12 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.N = d;
   r.out = dxg;
   r.ldo = d;
-  if ((e = run_row_gemm(r, kF32, b.gate_dt, kF32, rt, s)) != hipSuccess) return e;
+  if ((e = run_row_gemm(r, kF32, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
   if (b.train) {
     r.a = cu + n;
     r.w = b.w_noise;
     r.accumulate = 1;
-    if ((e = run_row_gemm(r, kF32, b.gate_dt, kF32, rt, s)) != hipSuccess) return e;
+    if ((e = run_row_gemm(r, kF32, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
   }
   if (B > 0) {
     hipLaunchKernelGGL(dx_sum_kernel, dim3(blocks_for(B * d)), dim3(256), 0, s, B, k, d, dxg, dxe,
