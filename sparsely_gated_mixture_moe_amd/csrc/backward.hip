@@ -18,6 +18,7 @@
 //     64 x 64 tile of dW_e per workgroup, the segment's rows in steps of 16,
 //     with the column sums of a (the bias gradients) on the side.
 // Every sum runs in a fixed order, so the results are deterministic.
+#include <algorithm>
 #include <cmath>
 
 #include "device_common.h"
@@ -266,43 +267,171 @@ __global__ __launch_bounds__(256) void wgrad_kernel(Wgrad p) {
 }
 
 // ---------------------------------------------------------------------------
-// The same products on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16), for
+// The same products on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16), for
 // bf16 storage. Operands in bf16 storage are exact; an fp32 operand (the
-// recomputed hidden layer, the hidden and logit gradients) is split into
-// hi = bf16(v) and lo = bf16(v - hi), exact to about 2^-17 of v, and its
-// products take the hi and lo parts against the other operand (hi x lo'
-// cross terms of two split operands are kept, lo x lo' dropped). Row scales
-// (the gates) are applied where they keep an exact operand exact: in the row
-// products' epilogue, in the weight-gradient products to the split operand.
+// recomputed hidden layer, the hidden and logit gradients, fp32 gate weights)
+// is split into hi = bf16(v) and lo = bf16(v - hi), exact to about 2^-17 of v,
+// and its products take the hi and lo parts against the other operand (hi x
+// lo' cross terms of two split operands are kept, lo x lo' dropped). Row
+// scales (the gates) are applied where they keep an exact operand exact: in
+// the row products' epilogue, in the weight-gradient products to the split
+// operand.
+//
+// Four waves (2 x 2) per workgroup, K in steps of 32 through two LDS buffers:
+// the next step's operands are loaded into registers (16-byte loads, fp32
+// split on the way) while the current step is multiplied. Tiles are 64 rows x
+// 256 columns for the row products (a 64-row unit of a segment), 128 x 128
+// for the weight gradients. An operand tile keeps its source's layout in LDS:
+//   K-major (source rows K-contiguous: x, dy, hidden, dA and logit-gradient
+//     rows, the rows of an [N][K] weight): [R][32] bf16, 64 bytes a row,
+//     16-byte unit u of row r at position u ^ (((r >> 1) ^ (r >> 3)) & 3); a
+//     fragment is one 16-byte read;
+//   K-indexed rows (a [K][N] weight, the routed rows of a weight gradient):
+//     [32][R] bf16, unit u of row k at position u ^ (4 ((k >> 3) & 1)); a
+//     fragment gathers its 8 K values with 8 two-byte reads.
+// Either placement keeps the reads of 8 (or 16) consecutive lanes, and those
+// of the two half-waves, in distinct banks.
 // ---------------------------------------------------------------------------
 
-constexpr int kK16 = 32;  // K (or rows) per LDS step of the bf16 products
-constexpr int kP16 = 8;   // bf16 elements of padding per LDS row
+constexpr int kBK = 32;  // K per step of the tiled bf16 products
 
-__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-  const uint32_t h = f32_to_bf16_bits(v);
-  hi = (uint16_t)h;
-  lo = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(h));
+__device__ __forceinline__ uint32_t split_pair(float a, float b, uint32_t& lo) {
+  const uint32_t ha = f32_to_bf16_bits(a), hb = f32_to_bf16_bits(b);
+  const uint32_t la = f32_to_bf16_bits(a - bf16_bits_to_f32(ha));
+  const uint32_t lb = f32_to_bf16_bits(b - bf16_bits_to_f32(hb));
+  lo = la | (lb << 16);
+  return ha | (hb << 16);
 }
 
-__device__ __forceinline__ f32x4 mfma16(const U16& a, const U16& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_short8(a), as_short8(b), c, 0, 0, 0);
-}
-
-// Eight consecutive elements of row `row` from column `col` (zero past `lim`).
-template <typename T>
-__device__ __forceinline__ void load8_row(const void* base, int64_t row, int64_t ld, int col,
-                                          int lim, float (&v)[8]) {
+// 8 consecutive elements from p: `valid` of them (0..8) are read, the rest are
+// 0; vec: the 8 are in range and 16-byte aligned (one or two vector loads).
+__device__ __forceinline__ void load8(const bf16* p, int valid, bool vec, uint32_t (&w)[4]) {
+  if (vec && valid == 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
+    return;
+  }
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (col + i < lim) ? ld_f<T>(base, row * ld + col + i) : 0.f;
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t a = 2 * j < valid ? q[2 * j] : 0u, b = 2 * j + 1 < valid ? q[2 * j + 1] : 0u;
+    w[j] = a | (b << 16);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, int valid, bool vec, float (&f)[8]) {
+  if (vec && valid == 8) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    f[0] = a.x;
+    f[1] = a.y;
+    f[2] = a.z;
+    f[3] = a.w;
+    f[4] = b.x;
+    f[5] = b.y;
+    f[6] = b.z;
+    f[7] = b.w;
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = j < valid ? p[j] : 0.f;
 }
 
-template <typename TA, typename TW, typename TO, bool SA, bool SW>
-__global__ __launch_bounds__(256) void row_gemm16_kernel(RowGemm p) {
-  __shared__ __attribute__((aligned(16))) uint16_t ash[kT][kK16 + kP16];
-  __shared__ __attribute__((aligned(16))) uint16_t asl[SA ? kT : 1][kK16 + kP16];
-  __shared__ __attribute__((aligned(16))) uint16_t bsh[kT][kK16 + kP16];
-  __shared__ __attribute__((aligned(16))) uint16_t bsl[SW ? kT : 1][kK16 + kP16];
+// One operand unit in registers between its load and its LDS store: raw bf16
+// bits, or fp32 values (split, times a scale, at the store).
+template <typename T>
+struct Stage8;
+template <>
+struct Stage8<bf16> {
+  uint32_t w[4];
+  __device__ __forceinline__ void load(const void* base, int64_t off, int valid, bool vec) {
+    load8(reinterpret_cast<const bf16*>(base) + off, valid, vec, w);
+  }
+  // hi (and no lo: bf16 operands are exact; a scale never lands here)
+  __device__ __forceinline__ void store(uint8_t* hi, uint8_t* lo, float scale) const {
+    (void)lo;
+    (void)scale;
+    *reinterpret_cast<uint4*>(hi) = uint4{w[0], w[1], w[2], w[3]};
+  }
+};
+template <>
+struct Stage8<float> {
+  float f[8];
+  __device__ __forceinline__ void load(const void* base, int64_t off, int valid, bool vec) {
+    load8(reinterpret_cast<const float*>(base) + off, valid, vec, f);
+  }
+  __device__ __forceinline__ void store(uint8_t* hi, uint8_t* lo, float scale) const {
+    uint4 h, l;
+    h.x = split_pair(scale * f[0], scale * f[1], l.x);
+    h.y = split_pair(scale * f[2], scale * f[3], l.y);
+    h.z = split_pair(scale * f[4], scale * f[5], l.z);
+    h.w = split_pair(scale * f[6], scale * f[7], l.w);
+    *reinterpret_cast<uint4*>(hi) = h;
+    *reinterpret_cast<uint4*>(lo) = l;
+  }
+};
+
+// LDS placement of a K-major tile ([R][32] bf16) and of a tile with K-indexed
+// rows ([32][R] bf16): byte offset of 16-byte unit u of row r (resp. k).
+__device__ __forceinline__ int kmaj_pos(int r, int u) {
+  return r * 64 + ((u ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
+}
+// The A (or B) operand of one 32x32x16 product at k16 step s: lane l supplies
+// row (column) r0 + l % 32 and K 16 s + 8 (l / 32) .. + 7.
+__device__ __forceinline__ U16 frag_kmaj(const uint8_t* t, int r0, int s, int lane) {
+  return *reinterpret_cast<const U16*>(t + kmaj_pos(r0 + (lane & 31), 2 * s + (lane >> 5)));
+}
+// Four K rows x 8 consecutive columns of a [K][N] operand, held between their
+// loads and their transposed LDS store: each column's 4 K values become 8
+// bytes of a K-major tile row (fp32 split into hi and lo on the way).
+template <typename T>
+struct StageT;
+template <>
+struct StageT<bf16> {
+  uint32_t w[4][4];
+  __device__ __forceinline__ void load(const void* base, int64_t off, int64_t ld, int krows,
+                                       int valid, bool vec) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      load8(reinterpret_cast<const bf16*>(base) + off + j * ld, j < krows ? valid : 0, vec, w[j]);
+  }
+  // column e (0..7) of the block: 4 bf16 K values
+  __device__ __forceinline__ void store(uint8_t* hi, uint8_t* lo, int e, int pos) const {
+    (void)lo;
+    const int sh = 16 * (e & 1), q = e >> 1;
+    const uint32_t v0 = (w[0][q] >> sh) & 0xFFFFu, v1 = (w[1][q] >> sh) & 0xFFFFu;
+    const uint32_t v2 = (w[2][q] >> sh) & 0xFFFFu, v3 = (w[3][q] >> sh) & 0xFFFFu;
+    *reinterpret_cast<uint2*>(hi + pos) = uint2{v0 | (v1 << 16), v2 | (v3 << 16)};
+  }
+};
+template <>
+struct StageT<float> {
+  float f[4][8];
+  __device__ __forceinline__ void load(const void* base, int64_t off, int64_t ld, int krows,
+                                       int valid, bool vec) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      load8(reinterpret_cast<const float*>(base) + off + j * ld, j < krows ? valid : 0, vec, f[j]);
+  }
+  __device__ __forceinline__ void store(uint8_t* hi, uint8_t* lo, int e, int pos) const {
+    uint32_t l0, l1;
+    const uint32_t h0 = split_pair(f[0][e], f[1][e], l0), h1 = split_pair(f[2][e], f[3][e], l1);
+    *reinterpret_cast<uint2*>(hi + pos) = uint2{h0, h1};
+    *reinterpret_cast<uint2*>(lo + pos) = uint2{l0, l1};
+  }
+};
+
+template <typename TA, typename TW, bool WT>
+__global__ __launch_bounds__(256) void row_tgemm_kernel(RowGemm p, int vec) {
+  constexpr bool SA = sizeof(TA) == 4, SW = sizeof(TW) == 4;
+  constexpr int TM = 64, TN = 256;
+  constexpr int ABYTES = TM * 64, BBYTES = TN * 64;  // one bf16 tile of each operand
+  __shared__ __attribute__((aligned(16))) uint8_t ah[2][ABYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t al[SA ? 2 : 1][SA ? ABYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t bh[2][BBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t bl[SW ? 2 : 1][SW ? BBYTES : 16];
   int g = 0;
   int64_t r0, rend;
   if (p.units) {
@@ -312,87 +441,101 @@ __global__ __launch_bounds__(256) void row_gemm16_kernel(RowGemm p) {
     r0 = (int64_t)p.seg_off[g] + p.units[2 + 2 * u];
     rend = p.seg_off[g + 1];
   } else {
-    r0 = (int64_t)blockIdx.x * kT;
+    r0 = (int64_t)blockIdx.x * TM;
     rend = p.rows;
     if (r0 >= rend) return;
   }
-  const int c0 = blockIdx.y * kT;
+  const int n0 = blockIdx.y * TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, q = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool vv = vec != 0;
   const char* wseg = reinterpret_cast<const char*>(p.w) + (int64_t)g * p.w_stride * sizeof(TW);
-  f32x4 acc[4];
+  // A: row tid / 4 of the unit, K unit tid % 4
+  const int ar = tid >> 2, au = tid & 3;
+  const bool arow_ok = r0 + ar < rend;
+  const int64_t arow = arow_ok ? (p.gather ? (int64_t)p.gather[r0 + ar] : r0 + ar) : 0;
+  Stage8<TA> sa;
+  Stage8<TW> sb[4];  // [N][K] weights: 4 units of K-contiguous rows
+  StageT<TW> st;     // [K][N] weights: K rows k0 + 4 (tid / 32) .. + 3, columns 8 (tid % 32) .. + 7
+  auto load = [&](int k0) __attribute__((always_inline)) {
+    const int ka = k0 + 8 * au;
+    sa.load(p.a, arow * p.lda + ka, arow_ok ? std::min(8, std::max(0, p.K - ka)) : 0, vv);
+    if constexpr (WT) {
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // A: row tid / 4, K run (tid % 4) * 8 .. + 7
-  const int ar = tid >> 2, ak = (tid & 3) * 8;
-  const int64_t arow_p = r0 + ar;
-  const bool arow_ok = arow_p < rend;
-  const int64_t arow = arow_ok ? (p.gather ? (int64_t)p.gather[arow_p] : arow_p) : 0;
-  for (int k0 = 0; k0 < p.K; k0 += kK16) {
-    {
-      float v[8];
-      load8_row<TA>(p.a, arow, p.lda, k0 + ak, arow_ok ? p.K : 0, v);
-      uint16_t h[8], l[8];
+      for (int i = 0; i < 4; ++i) {  // row n0 + tid / 4 + 64 i, K unit tid % 4
+        const int n = n0 + (tid >> 2) + 64 * i, kb = k0 + 8 * (tid & 3);
+        sb[i].load(wseg, (int64_t)n * p.K + kb, n < p.N ? std::min(8, std::max(0, p.K - kb)) : 0, vv);
+      }
+    } else {
+      const int kr = k0 + 4 * (tid >> 5), nb = n0 + 8 * (tid & 31);
+      st.load(wseg, (int64_t)kr * p.N + nb, p.N, std::max(0, std::min(4, p.K - kr)),
+              std::min(8, std::max(0, p.N - nb)), vv);
+    }
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+    const int pa = kmaj_pos(ar, au);
+    sa.store(ah[buf] + pa, al[SA ? buf : 0] + (SA ? pa : 0), 1.f);
+    if constexpr (WT) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) split_bf16(v[i], h[i], l[i]);
+      for (int i = 0; i < 4; ++i) {
+        const int pb = kmaj_pos((tid >> 2) + 64 * i, tid & 3);
+        sb[i].store(bh[buf] + pb, bl[SW ? buf : 0] + (SW ? pb : 0), 1.f);
+      }
+    } else {
+      const int kq = tid >> 5, nu = tid & 31;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ash[ar][ak + i] = h[i];
-      if constexpr (SA) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) asl[ar][ak + i] = l[i];
+      for (int e = 0; e < 8; ++e) {
+        const int pb = kmaj_pos(8 * nu + e, kq >> 1) + 8 * (kq & 1);
+        st.store(bh[buf], bl[SW ? buf : 0], e, pb);
       }
     }
-    if (p.wt) {  // W [N][K]: 8 consecutive K of column n
-      const int n = tid >> 2, kq = (tid & 3) * 8;
-      float v[8];
-      load8_row<TW>(wseg, c0 + n, p.K, k0 + kq, (c0 + n < p.N) ? p.K : 0, v);
+  };
+  f32x16 acc[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint16_t h, l;
-        split_bf16(v[i], h, l);
-        bsh[n][kq + i] = h;
-        if constexpr (SW) bsl[n][kq + i] = l;
-      }
-    } else {  // W [K][N]: 8 consecutive N of K row k
-      const int kr = tid >> 3, n8 = (tid & 7) * 8;
-      float v[8];
-      load8_row<TW>(wseg, k0 + kr, p.N, c0 + n8, (k0 + kr < p.K) ? p.N : 0, v);
+  for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint16_t h, l;
-        split_bf16(v[i], h, l);
-        bsh[n8 + i][kr] = h;
-        if constexpr (SW) bsl[n8 + i][kr] = l;
-      }
-    }
-    __syncthreads();
-    const U16 a = *reinterpret_cast<const U16*>(&ash[16 * wave + lr][8 * q]);
-    U16 al;
-    if constexpr (SA) al = *reinterpret_cast<const U16*>(&asl[16 * wave + lr][8 * q]);
+    for (int j = 0; j < 16; ++j) acc[nb][j] = 0.f;
+  const int nk = (p.K + kBK - 1) / kBK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) load((ks + 1) * kBK);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const U16 b = *reinterpret_cast<const U16*>(&bsh[16 * ct + lr][8 * q]);
-      acc[ct] = mfma16(a, b, acc[ct]);
-      if constexpr (SA) acc[ct] = mfma16(al, b, acc[ct]);
-      if constexpr (SW) {
-        const U16 bl = *reinterpret_cast<const U16*>(&bsl[16 * ct + lr][8 * q]);
-        acc[ct] = mfma16(a, bl, acc[ct]);
+    for (int s = 0; s < kBK / 16; ++s) {
+      const U16 a = frag_kmaj(ah[buf], wm * 32, s, lane);
+      U16 a2;
+      if constexpr (SA) a2 = frag_kmaj(al[buf], wm * 32, s, lane);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int c0 = wn * 128 + nb * 32;
+        const U16 b = frag_kmaj(bh[buf], c0, s, lane);
+        Mfma<bf16>::k32(acc[nb], a, b);
+        if constexpr (SA) Mfma<bf16>::k32(acc[nb], a2, b);
+        if constexpr (SW) {
+          const U16 b2 = frag_kmaj(bl[buf], c0, s, lane);
+          Mfma<bf16>::k32(acc[nb], a, b2);
+        }
       }
     }
+    if (ks + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
+  // C layout: lane holds column l % 32 of each 32-column block, rows
+  // 8 (j / 4) + 4 (l / 32) + j % 4 of its wave's 32
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int c = c0 + 16 * ct + lr;
+  for (int nb = 0; nb < 4; ++nb) {
+    const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
     if (c >= p.N) continue;
     float b = 0.f;
     if (p.bias)
       b = p.bias_f32 ? ld_f<float>(p.bias, (int64_t)g * p.N + c) : ld_f<TW>(p.bias, (int64_t)g * p.N + c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t rp = r0 + 16 * wave + 4 * q + i;
+    for (int j = 0; j < 16; ++j) {
+      const int64_t rp = r0 + wm * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
       if (rp >= rend) continue;
-      float v = acc[ct][i];
+      float v = acc[nb][j];
       if (p.scale) v *= p.scale[rp];
       v += b;
       if (p.relu) v = v > 0.f ? v : 0.f;
@@ -402,93 +545,172 @@ __global__ __launch_bounds__(256) void row_gemm16_kernel(RowGemm p) {
         v = mv > 0.f ? v : 0.f;
       }
       const int64_t o = rp * p.ldo + c;
-      if (p.accumulate) v += ld_f<TO>(p.out, o);
-      st_f<TO>(p.out, o, v);
+      if (p.accumulate) v += ld_f<float>(p.out, o);
+      st_f<float>(p.out, o, v);
     }
   }
 }
 
-template <typename TA, typename TB, bool SA, bool SB>
-__global__ __launch_bounds__(256) void wgrad16_kernel(Wgrad p) {
+// Weight gradients: TM x TM output tiles, NW waves in a 2 x (NW / 2) grid;
+// the first half of the threads loads A, the second half B, each thread 4
+// rows x 8 columns per step, transposed into K-major tiles.
+template <typename TA, typename TB, int TM, int NW>
+__global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec) {
+  constexpr bool SA = sizeof(TA) == 4, SB = sizeof(TB) == 4;
   static_assert(SA || SB, "a row scale needs a split operand");
-  __shared__ __attribute__((aligned(16))) uint16_t ath[kT][kK16 + kP16];  // [m][row]
-  __shared__ __attribute__((aligned(16))) uint16_t atl[SA ? kT : 1][kK16 + kP16];
-  __shared__ __attribute__((aligned(16))) uint16_t bth[kT][kK16 + kP16];  // [n][row]
-  __shared__ __attribute__((aligned(16))) uint16_t btl[SB ? kT : 1][kK16 + kP16];
-  __shared__ float cst[kK16][kT + 1];  // the colsum's scaled A values, fp32
-  const int mtiles = (p.M + kT - 1) / kT;
-  const int m0 = (blockIdx.x % mtiles) * kT, n0 = (blockIdx.x / mtiles) * kT;
+  static_assert(TM * 2 == NW * 64, "one 4 x 8 block of A or B per thread");
+  constexpr int TN = TM, BYTES = TM * 64;
+  constexpr int WM = TM / 2, WN = TN / (NW / 2), MB = WM / 32, NB = WN / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t ah[2][BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t al[SA ? 2 : 1][SA ? BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t bh[2][BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t bl[SB ? 2 : 1][SB ? BYTES : 16];
+  __shared__ float csr[8][TM];  // the colsum's per-thread partials
+  const int mtiles = (p.M + TM - 1) / TM;
+  const int m0 = (blockIdx.x % mtiles) * TM, n0 = (blockIdx.x / mtiles) * TN;
   const int g = blockIdx.y;
   const int64_t s0 = p.seg_off ? p.seg_off[g] : 0;
   const int64_t s1 = p.seg_off ? p.seg_off[g + 1] : p.rows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, q = lane >> 4;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
+  const bool vv = vec != 0;
   const bool do_colsum = p.colsum != nullptr && n0 == 0;
-  f32x4 acc[4];
+  // this thread's block: operand B for the second half of the threads
+  const bool isb = tid >= TM;
+  const int bt = isb ? tid - TM : tid;
+  const int kq = bt / (TM / 8), mu = bt % (TM / 8);  // rows 4 kq .. + 3, columns 8 mu .. + 7
+  const int c0 = (isb ? n0 : m0) + 8 * mu;
+  const int clim = isb ? p.N : p.M;
+  const int nvalid = std::min(8, std::max(0, clim - c0));
+  // a thread stages either an A block or a B block
+  union Staged {
+    StageT<TA> a;
+    StageT<TB> b;
+  } stg;
+  StageT<TA>& sa = stg.a;
+  StageT<TB>& sb = stg.b;
+  float cs[8];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float cs = 0.f;
-  // loads: row tid / 8 of the step, 8 consecutive columns from (tid % 8) * 8
-  const int lrow = tid >> 3, lc = (tid & 7) * 8;
-  for (int64_t r = s0; r < s1; r += kK16) {
-    const int64_t rp = r + lrow;
-    const bool ok = rp < s1;
-    int64_t ra = 0, rb = 0;
-    float sa = 1.f, sb = 1.f;
-    if (ok) {
-      ra = p.a_gather ? (int64_t)p.a_gather[rp] : rp;
-      rb = p.b_gather ? (int64_t)p.b_gather[rp] : rp;
-      if (p.a_scale) sa = p.a_scale[rp];
-      if (p.b_scale) sb = p.b_scale[rp];
-    }
-    // the row's scale goes to a split operand, so that an exact one stays exact
-    const float s_a = SB ? 1.f : sa * sb, s_b = SB ? sa * sb : 1.f;
-    float va[8], vb[8];
-    load8_row<TA>(p.a, ra, p.lda, m0 + lc, ok ? p.M : 0, va);
-    load8_row<TB>(p.b, rb, p.ldb, n0 + lc, ok ? p.N : 0, vb);
+  for (int i = 0; i < 8; ++i) cs[i] = 0.f;
+  auto load = [&](int64_t r) __attribute__((always_inline)) {
+    const int64_t rb = r + 4 * kq;
+    const int krows = (int)std::max<int64_t>(0, std::min<int64_t>(4, s1 - rb));
+    // rows are gathered one by one, so load row by row
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint16_t h, l;
-      split_bf16(s_a * va[i], h, l);
-      ath[lc + i][lrow] = h;
-      if constexpr (SA) atl[lc + i][lrow] = l;
-      split_bf16(s_b * vb[i], h, l);
-      bth[lc + i][lrow] = h;
-      if constexpr (SB) btl[lc + i][lrow] = l;
-      if (do_colsum) cst[lrow][lc + i] = sa * va[i];
-    }
-    __syncthreads();
-    if (do_colsum && tid < kT) {
+    for (int j = 0; j < 4; ++j) {
+      const int64_t rp = rb + j;
+      const bool ok = j < krows;
+      float fa = 1.f, fb = 1.f;
+      int64_t row = 0;
+      if (ok) {
+        if (p.a_scale) fa = p.a_scale[rp];
+        if (p.b_scale) fb = p.b_scale[rp];
+        const int32_t* gat = isb ? p.b_gather : p.a_gather;
+        row = gat ? (int64_t)gat[rp] : rp;
+      }
+      // the row's scale goes to a split operand, so that an exact one stays exact
+      const float sc = (isb == SB) ? fa * fb : 1.f;
+      if (!isb) {
+        if constexpr (SA) {
+          load8(reinterpret_cast<const float*>(p.a) + row * p.lda + c0, ok ? nvalid : 0, vv, sa.f[j]);
+          if (do_colsum) {
 #pragma unroll
-      for (int i = 0; i < kK16; ++i) cs += cst[i][tid];
-    }
-    const U16 a = *reinterpret_cast<const U16*>(&ath[16 * wave + lr][8 * q]);
-    U16 al;
-    if constexpr (SA) al = *reinterpret_cast<const U16*>(&atl[16 * wave + lr][8 * q]);
+            for (int e = 0; e < 8; ++e) cs[e] += fa * sa.f[j][e];
+          }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const U16 b = *reinterpret_cast<const U16*>(&bth[16 * ct + lr][8 * q]);
-      acc[ct] = mfma16(a, b, acc[ct]);
-      if constexpr (SA) acc[ct] = mfma16(al, b, acc[ct]);
-      if constexpr (SB) {
-        const U16 bl = *reinterpret_cast<const U16*>(&btl[16 * ct + lr][8 * q]);
-        acc[ct] = mfma16(a, bl, acc[ct]);
+          for (int e = 0; e < 8; ++e) sa.f[j][e] *= sc;
+        } else {
+          load8(reinterpret_cast<const bf16*>(p.a) + row * p.lda + c0, ok ? nvalid : 0, vv, sa.w[j]);
+          if (do_colsum) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              cs[e] += fa * bf16_bits_to_f32((sa.w[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          }
+        }
+      } else {
+        if constexpr (SB) {
+          load8(reinterpret_cast<const float*>(p.b) + row * p.ldb + c0, ok ? nvalid : 0, vv, sb.f[j]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sb.f[j][e] *= sc;
+        } else {
+          load8(reinterpret_cast<const bf16*>(p.b) + row * p.ldb + c0, ok ? nvalid : 0, vv, sb.w[j]);
+        }
       }
     }
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pos = kmaj_pos(8 * mu + e, kq >> 1) + 8 * (kq & 1);
+      if (!isb) sa.store(ah[buf], al[SA ? buf : 0], e, pos);
+      else sb.store(bh[buf], bl[SB ? buf : 0], e, pos);
+    }
+  };
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mb][nb][j] = 0.f;
+  const int64_t nk = (s1 - s0 + kBK - 1) / kBK;
+  if (nk > 0) {
+    load(s0);
+    store(0);
+  }
+  __syncthreads();
+  for (int64_t ks = 0; ks < nk; ++ks) {
+    const int buf = (int)(ks & 1);
+    if (ks + 1 < nk) load(s0 + (ks + 1) * kBK);
+#pragma unroll
+    for (int s = 0; s < kBK / 16; ++s) {
+      U16 a[MB], a2[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        a[mb] = frag_kmaj(ah[buf], wm * WM + mb * 32, s, lane);
+        if constexpr (SA) a2[mb] = frag_kmaj(al[buf], wm * WM + mb * 32, s, lane);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const U16 b = frag_kmaj(bh[buf], wn * WN + nb * 32, s, lane);
+        U16 b2;
+        if constexpr (SB) b2 = frag_kmaj(bl[buf], wn * WN + nb * 32, s, lane);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          Mfma<bf16>::k32(acc[mb][nb], a[mb], b);
+          if constexpr (SA) Mfma<bf16>::k32(acc[mb][nb], a2[mb], b);
+          if constexpr (SB) Mfma<bf16>::k32(acc[mb][nb], a[mb], b2);
+        }
+      }
+    }
+    if (ks + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
   float* og = p.out + (int64_t)g * p.out_stride;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int n = n0 + 16 * ct + lr;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n0 + wn * WN + nb * 32 + (lane & 31);
     if (n >= p.N) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 16 * wave + 4 * q + i;
-      if (m < p.M) og[(int64_t)m * p.N + n] = acc[ct][i];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int m = m0 + wm * WM + mb * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+        if (m < p.M) og[(int64_t)m * p.N + n] = acc[mb][nb][j];
+      }
+  }
+  if (do_colsum) {  // the 8 threads of a column unit hold rows 4 kq .. : add in kq order
+    if (!isb) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) csr[kq][8 * mu + e] = cs[e];
+    }
+    __syncthreads();
+    if (tid < TM && m0 + tid < p.M) {
+      float v = 0.f;
+      for (int i = 0; i < 8; ++i) v += csr[i][tid];
+      p.colsum[(int64_t)g * p.M + m0 + tid] = v;
     }
   }
-  if (do_colsum && tid < kT && m0 + tid < p.M) p.colsum[(int64_t)g * p.M + m0 + tid] = cs;
 }
 
 // ---------------------------------------------------------------------------
@@ -604,10 +826,10 @@ __global__ __launch_bounds__(256) void pair_grad_kernel(int64_t B, int n, int k,
                                                         const float* __restrict__ dHk,
                                                         const float* __restrict__ dload,
                                                         float* __restrict__ cu) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= B * n) return;
-  const int64_t t = idx / n;
-  const int i = (int)(idx - t * n);
+  // one token per blockIdx.x, 256 experts per blockIdx.y
+  const int64_t t = blockIdx.x;
+  const int i = blockIdx.y * 256 + threadIdx.x;
+  if (i >= n) return;
   float dh = 0.f;
   bool kept = false;
   for (int j = 0; j < k; ++j)
@@ -621,19 +843,21 @@ __global__ __launch_bounds__(256) void pair_grad_kernel(int64_t B, int n, int k,
     return;
   }
   const float c = row[i], u = row[n + i];
-  const float sigma = fmaxf(u, 0.f) + log1pf(expf(-fabsf(u))) + floor_;
+  const float sigma = softplus_f(u) + floor_;
+  const float rs = rcp_f(sigma);
   const float thr = kept ? thresh[t * 2 + 1] : thresh[t * 2];
   float pc = 0.f, ps = 0.f;
   if (!isinf(thr)) {
-    const float z = (c - thr) / sigma;
-    const float ph = expf(-0.5f * z * z) * 0.3989422804014327f;
-    pc = ph / sigma;
-    ps = -ph * z / sigma;
+    const float z = (c - thr) * rs;
+    const float ph = exp_native(-0.5f * z * z) * 0.3989422804014327f;  // phi(z)
+    pc = ph * rs;
+    ps = -ph * z * rs;
   }
   const float dl = dload[i];
   const float dc = dh + dl * pc;
   const float dsig = dh * eps[t * n + i] + dl * ps;
-  const float sg = u >= 0.f ? 1.f / (1.f + expf(-u)) : expf(u) / (1.f + expf(u));
+  const float eu = exp_native(-fabsf(u));  // Softplus'(u) = sigmoid(u)
+  const float sg = (u >= 0.f ? 1.f : eu) * rcp_f(1.f + eu);
   row[i] = dc;
   row[n + i] = dsig * sg;
 }
@@ -656,6 +880,34 @@ __global__ __launch_bounds__(256) void dx_sum_kernel(int64_t B, int k, int d,
   dx[idx] = v;
 }
 
+// Row chunks of a weight gradient over all B tokens (the gate's): chunk i is
+// rows [i B / S, (i + 1) B / S).
+__global__ __launch_bounds__(64) void chunk_offsets_kernel(int32_t* __restrict__ off, int S,
+                                                           int64_t B) {
+  for (int i = threadIdx.x; i <= S; i += 64) off[i] = (int32_t)((int64_t)i * B / S);
+}
+
+// dW_g (rows < n of the [M][d] partials) and dW_noise (rows n .. 2n - 1), and
+// the gate bias's gradient from the partial column sums: the S chunks' partial
+// sums added in chunk order.
+__global__ __launch_bounds__(256) void gate_wgrad_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ pcol, int S, int n, int M, int d,
+    float* __restrict__ dwg, float* __restrict__ dwn, float* __restrict__ dgb) {
+  const int64_t md = (int64_t)M * d;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < md) {
+    float v = 0.f;
+    for (int c = 0; c < S; ++c) v += part[c * md + i];
+    if (i < (int64_t)n * d) dwg[i] = v;
+    else dwn[i - (int64_t)n * d] = v;
+  } else if (i < md + n && dgb) {
+    const int m = (int)(i - md);
+    float v = 0.f;
+    for (int c = 0; c < S; ++c) v += pcol[(int64_t)c * M + m];
+    dgb[m] = v;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -669,20 +921,35 @@ unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 // bf16 storage: the products on the bf16 matrix cores (fp32 operands split);
 // fp32 storage: on the fp32 matrix cores.
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
+
 hipError_t run_row_gemm(const RowGemm& p, Dt ta, Dt tw, Dt to, int64_t grid_x, hipStream_t s,
                         bool bf16_cores = false) {
   if (grid_x <= 0) return hipSuccess;
-  const dim3 grid((unsigned)grid_x, (unsigned)((p.N + kT - 1) / kT)), block(256);
   if (bf16_cores && to == kF32) {
-#define MOE_RG16(A, W, SA, SW) \
-  hipLaunchKernelGGL((row_gemm16_kernel<A, W, float, SA, SW>), grid, block, 0, s, p)
-    if (ta == kBF16 && tw == kBF16) MOE_RG16(bf16, bf16, false, false);
-    else if (ta == kF32 && tw == kBF16) MOE_RG16(float, bf16, true, false);
-    else if (ta == kBF16 && tw == kF32) MOE_RG16(bf16, float, false, true);
-    else MOE_RG16(float, float, true, true);
-#undef MOE_RG16
+    // 16-byte operand loads when every unit of 8 is in range and aligned
+    const size_t wsz = tw == kBF16 ? 2 : 4;
+    const int vec = aligned16(p.a) && aligned16(p.w) && p.lda % 8 == 0 && p.K % 8 == 0 &&
+                    p.N % 8 == 0 && (p.w_stride * wsz) % 16 == 0;
+    const dim3 grid((unsigned)grid_x, (unsigned)((p.N + 255) / 256)), block(256);
+#define MOE_RT(A, W, WT) \
+  hipLaunchKernelGGL((row_tgemm_kernel<A, W, WT>), grid, block, 0, s, p, vec)
+    const bool a32 = ta == kF32, w32 = tw == kF32;
+    if (p.wt) {
+      if (!a32 && !w32) MOE_RT(bf16, bf16, true);
+      else if (a32 && !w32) MOE_RT(float, bf16, true);
+      else if (!a32 && w32) MOE_RT(bf16, float, true);
+      else MOE_RT(float, float, true);
+    } else {
+      if (!a32 && !w32) MOE_RT(bf16, bf16, false);
+      else if (a32 && !w32) MOE_RT(float, bf16, false);
+      else if (!a32 && w32) MOE_RT(bf16, float, false);
+      else MOE_RT(float, float, false);
+    }
+#undef MOE_RT
     return hipGetLastError();
   }
+  const dim3 grid((unsigned)grid_x, (unsigned)((p.N + kT - 1) / kT)), block(256);
 #define MOE_RG(A, W, O) hipLaunchKernelGGL((row_gemm_kernel<A, W, O>), grid, block, 0, s, p)
   if (ta == kBF16 && tw == kBF16 && to == kBF16) MOE_RG(bf16, bf16, bf16);
   else if (ta == kBF16 && tw == kBF16 && to == kF32) MOE_RG(bf16, bf16, float);
@@ -694,19 +961,34 @@ hipError_t run_row_gemm(const RowGemm& p, Dt ta, Dt tw, Dt to, int64_t grid_x, h
   return hipGetLastError();
 }
 
+// big_ok: 256 x 256 tiles allowed (segments short enough that their number,
+// not one segment's length, sets the work per tile)
 hipError_t run_wgrad(const Wgrad& p, Dt ta, Dt tb, int nseg, hipStream_t s,
-                     bool bf16_cores = false) {
+                     bool bf16_cores = false, bool big_ok = true) {
   if (nseg <= 0) return hipSuccess;
-  const dim3 grid((unsigned)(((p.M + kT - 1) / kT) * ((p.N + kT - 1) / kT)), (unsigned)nseg);
   if (bf16_cores) {
-    if (ta == kBF16 && tb == kF32)
-      hipLaunchKernelGGL((wgrad16_kernel<bf16, float, false, true>), grid, dim3(256), 0, s, p);
-    else if (ta == kF32 && tb == kBF16)
-      hipLaunchKernelGGL((wgrad16_kernel<float, bf16, true, false>), grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((wgrad16_kernel<float, float, true, true>), grid, dim3(256), 0, s, p);
+    const int vec = aligned16(p.a) && aligned16(p.b) && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
+                    p.M % 8 == 0 && p.N % 8 == 0;
+    // 256 x 256 tiles (eight waves) once both dimensions fill them, else 128 x 128
+    const bool big = big_ok && p.M >= 256 && p.N >= 256;
+    const int tm = big ? 256 : 128;
+    const dim3 grid((unsigned)(((p.M + tm - 1) / tm) * ((p.N + tm - 1) / tm)), (unsigned)nseg);
+#define MOE_WT(A, B_)                                                                          \
+  if (big)                                                                                     \
+    hipLaunchKernelGGL((wgrad_tgemm_kernel<A, B_, 256, 8>), grid, dim3(512), 0, s, p, vec);    \
+  else                                                                                         \
+    hipLaunchKernelGGL((wgrad_tgemm_kernel<A, B_, 128, 4>), grid, dim3(256), 0, s, p, vec)
+    if (ta == kBF16 && tb == kF32) {
+      MOE_WT(bf16, float);
+    } else if (ta == kF32 && tb == kBF16) {
+      MOE_WT(float, bf16);
+    } else {
+      MOE_WT(float, float);
+    }
+#undef MOE_WT
     return hipGetLastError();
   }
+  const dim3 grid((unsigned)(((p.M + kT - 1) / kT) * ((p.N + kT - 1) / kT)), (unsigned)nseg);
 #define MOE_WG(A, B_) hipLaunchKernelGGL((wgrad_kernel<A, B_>), grid, dim3(256), 0, s, p)
   if (ta == kBF16 && tb == kBF16) MOE_WG(bf16, bf16);
   else if (ta == kF32 && tb == kBF16) MOE_WG(float, bf16);
@@ -717,7 +999,24 @@ hipError_t run_wgrad(const Wgrad& p, Dt ta, Dt tb, int nseg, hipStream_t s,
   return hipGetLastError();
 }
 
+// Chunks of the gate's weight gradient: enough workgroups for the chip
+// (about 2048 of the 128 x 128 tiles over the [2n][d] output), at least 512
+// rows a chunk, at most 32 chunks.
+int gate_wgrad_chunks(int64_t B, int n, int d) {
+  const int64_t tiles = ((2 * (int64_t)n + 127) / 128) * (((int64_t)d + 127) / 128);
+  int64_t c = std::max<int64_t>(1, 2048 / std::max<int64_t>(1, tiles));
+  c = std::min<int64_t>(c, 32);
+  c = std::min<int64_t>(c, std::max<int64_t>(1, B / 512));
+  return (int)c;
+}
+
 }  // namespace
+
+static size_t gate_chunk_bytes(int64_t B, int n, int d) {
+  const size_t S = (size_t)gate_wgrad_chunks(B, n, d);
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  return al(S * 2 * n * d * 4) + al(S * 2 * n * 4) + al((S + 1) * 4);
+}
 
 size_t backward_ws_bytes(int64_t B, int n, int k, int d, int h, Dt act_dt) {
   const int64_t P = B * k;
@@ -734,7 +1033,8 @@ size_t backward_ws_bytes(int64_t B, int n, int k, int d, int h, Dt act_dt) {
          + al((size_t)P * h * 4)                                                // dA
          + al((size_t)P * d * 4)                                                // dx per pair
          + al((size_t)B * 2 * n * 4)                                            // c|u grads
-         + al((size_t)B * d * 4);                                               // dx via gate
+         + al((size_t)B * d * 4)                                                // dx via gate
+         + gate_chunk_bytes(B, n, d);                                           // dW_g chunks
 }
 
 hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
@@ -766,6 +1066,10 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   float* dxe = reinterpret_cast<float*>(take((size_t)P * d * 4));
   float* cu = reinterpret_cast<float*>(take((size_t)B * 2 * n * 4));
   float* dxg = reinterpret_cast<float*>(take((size_t)B * d * 4));
+  const int S = gate_wgrad_chunks(B, n, d);
+  float* gpart = reinterpret_cast<float*>(take((size_t)S * 2 * n * d * 4));
+  float* gcol = reinterpret_cast<float*>(take((size_t)S * 2 * n * 4));
+  int32_t* gchunk = reinterpret_cast<int32_t*>(take((size_t)(S + 1) * 4));
   hipError_t e;
 
   // routing of the forward's selection, and the 64-row units of its segments
@@ -857,7 +1161,10 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   wg.out = b.dw2;
   wg.out_stride = (int64_t)d * h;
   wg.colsum = b.db2;
-  if ((e = run_wgrad(wg, b.act_dt, kF32, n, s, b.act_dt == kBF16)) != hipSuccess) return e;
+  // long segments (over 256 rows per expert on average) keep 128 x 128 tiles, so that
+  // one popular expert's rows are spread over more workgroups
+  const bool short_segs = P < 256 * (int64_t)n;
+  if ((e = run_wgrad(wg, b.act_dt, kF32, n, s, b.act_dt == kBF16, short_segs)) != hipSuccess) return e;
   // dW1_e = sum dA^T x[token], db1_e = sum dA
   wg = Wgrad{};
   wg.seg_off = offsets;
@@ -872,7 +1179,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   wg.out = b.dw1;
   wg.out_stride = (int64_t)h * d;
   wg.colsum = b.db1;
-  if ((e = run_wgrad(wg, kF32, b.act_dt, n, s, b.act_dt == kBF16)) != hipSuccess) return e;
+  if ((e = run_wgrad(wg, kF32, b.act_dt, n, s, b.act_dt == kBF16, short_segs)) != hipSuccess) return e;
   // dx per routed row: dA W1
   r = RowGemm{};
   r.units = units;
@@ -911,28 +1218,35 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
     if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
   }
   if (B > 0) {
-    hipLaunchKernelGGL(pair_grad_kernel, dim3(blocks_for(B * n)), dim3(256), 0, s, B, n, k,
+    hipLaunchKernelGGL(pair_grad_kernel, dim3((unsigned)B, (unsigned)((n + 255) / 256)), dim3(256), 0, s, B, n, k,
                        b.train, b.noise_floor, b.eps, b.thresh, b.topk_idx, dHk, dload, cu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // dW_g = dc^T x, db_g = sum dc; dW_noise = du^T x
+  // dW_g = dc^T x, db_g = sum dc; dW_noise = du^T x: one product over the [B][2n]
+  // logit gradients (n columns without noise), the B rows in S chunks whose
+  // partial sums are added in chunk order
+  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(64), 0, s, gchunk, S, B);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int gm = b.train ? 2 * n : n;
   wg = Wgrad{};
+  wg.seg_off = gchunk;
   wg.rows = B;
   wg.a = cu;
   wg.lda = 2 * (int64_t)n;
   wg.b = b.x;
   wg.ldb = d;
-  wg.M = n;
+  wg.M = gm;
   wg.N = d;
-  wg.out = b.dw_gate;
-  wg.colsum = b.dgate_bias;
-  if ((e = run_wgrad(wg, kF32, b.act_dt, 1, s, b.act_dt == kBF16)) != hipSuccess) return e;
-  if (b.train) {
-    wg.a = cu + n;
-    wg.out = b.dw_noise;
-    wg.colsum = nullptr;
-    if ((e = run_wgrad(wg, kF32, b.act_dt, 1, s, b.act_dt == kBF16)) != hipSuccess) return e;
-  } else {
+  wg.out = gpart;
+  wg.out_stride = (int64_t)gm * d;
+  wg.colsum = gcol;
+  // 256 x 256 tiles while they still give 512 workgroups with the chunks
+  const bool gate_big = ((gm + 255) / 256) * (int64_t)((d + 255) / 256) * S >= 512;
+  if ((e = run_wgrad(wg, kF32, b.act_dt, S, s, b.act_dt == kBF16, gate_big)) != hipSuccess) return e;
+  hipLaunchKernelGGL(gate_wgrad_reduce_kernel, dim3(blocks_for((int64_t)gm * d + n)), dim3(256),
+                     0, s, gpart, gcol, S, n, gm, d, b.dw_gate, b.dw_noise, b.dgate_bias);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!b.train) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for((int64_t)n * d)), dim3(256), 0, s,
                        b.dw_noise, (int64_t)n * d);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -355,6 +355,11 @@ FFN_CASES = [
     ("flat_bf16_n4096", {"tokens": 2, "n_experts": 64}, True),
     ("tiny_fp32", {"tokens": 5}, True),
     ("flat_bf16_n4096", {"tokens": 20, "n_experts": 16, "d_model": 256, "d_hidden": 384}, False),
+    # long segments: many 96-row units of one expert, ragged tails, a 768-unit hidden layer
+    ("flat_bf16_n4096", {"tokens": 2600, "n_experts": 8, "k": 2}, True),
+    ("flat_bf16_n4096", {"tokens": 1500, "n_experts": 4, "k": 1, "d_model": 256,
+                         "d_hidden": 256}, False),
+    ("zipf_bf16_n256", {"tokens": 4100, "n_experts": 16, "k": 3, "d_hidden": 768}, True),
 ]
 
 
