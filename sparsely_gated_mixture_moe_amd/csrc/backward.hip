@@ -202,7 +202,48 @@ struct Wgrad {
   int64_t out_stride;
   // optional: colsum[g * M + m] = sum over g's rows of a[p][m], in row order
   float* colsum;
+  // optional row chunks (wg_chunk_plan_kernel): blockIdx.y is chunk c = (g,
+  // first row, end row, slot) of chunks[1 + 4c ..], chunks[0] the count; a
+  // chunk with slot >= 0 writes its partial sums to part + slot * M * N (and
+  // its column sums to pcol + slot * M) instead of out_g and colsum
+  const int32_t* chunks;
+  float* part;
+  float* pcol;
 };
+
+// The rows, output and column-sum destination of a weight-gradient workgroup.
+struct WgSeg {
+  bool valid;
+  int g;
+  int64_t s0, s1;
+  float* out;
+  float* colsum;
+};
+__device__ __forceinline__ WgSeg wg_segment(const Wgrad& p) {
+  WgSeg r;
+  if (p.chunks) {
+    const int c = blockIdx.y;
+    r.valid = c < p.chunks[0];
+    if (!r.valid) return r;
+    const int32_t* e = p.chunks + 1 + 4 * c;
+    r.g = e[0];
+    r.s0 = e[1];
+    r.s1 = e[2];
+    const int slot = e[3];
+    r.out = slot < 0 ? p.out + (int64_t)r.g * p.out_stride : p.part + (int64_t)slot * p.M * p.N;
+    r.colsum = !p.colsum ? nullptr
+               : slot < 0 ? p.colsum + (int64_t)r.g * p.M
+                          : p.pcol + (int64_t)slot * p.M;
+    return r;
+  }
+  r.valid = true;
+  r.g = blockIdx.y;
+  r.s0 = p.seg_off ? p.seg_off[r.g] : 0;
+  r.s1 = p.seg_off ? p.seg_off[r.g + 1] : p.rows;
+  r.out = p.out + (int64_t)r.g * p.out_stride;
+  r.colsum = p.colsum ? p.colsum + (int64_t)r.g * p.M : nullptr;
+  return r;
+}
 
 template <typename TA, typename TB>
 __global__ __launch_bounds__(256) void wgrad_kernel(Wgrad p) {
@@ -210,12 +251,12 @@ __global__ __launch_bounds__(256) void wgrad_kernel(Wgrad p) {
   __shared__ float bt[kKS][kT + 1];
   const int mtiles = (p.M + kT - 1) / kT;
   const int m0 = (blockIdx.x % mtiles) * kT, n0 = (blockIdx.x / mtiles) * kT;
-  const int g = blockIdx.y;
-  const int64_t s0 = p.seg_off ? p.seg_off[g] : 0;
-  const int64_t s1 = p.seg_off ? p.seg_off[g + 1] : p.rows;
+  const WgSeg sg = wg_segment(p);
+  if (!sg.valid) return;
+  const int64_t s0 = sg.s0, s1 = sg.s1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, q = lane >> 4;
-  const bool do_colsum = p.colsum != nullptr && n0 == 0;
+  const bool do_colsum = sg.colsum != nullptr && n0 == 0;
   f32x4 acc[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -252,7 +293,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(Wgrad p) {
     }
     __syncthreads();
   }
-  float* og = p.out + (int64_t)g * p.out_stride;
+  float* og = sg.out;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const int n = n0 + 16 * ct + lr;
@@ -263,7 +304,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(Wgrad p) {
       if (m < p.M) og[(int64_t)m * p.N + n] = acc[ct][i];
     }
   }
-  if (do_colsum && tid < kT && m0 + tid < p.M) p.colsum[(int64_t)g * p.M + m0 + tid] = cs;
+  if (do_colsum && tid < kT && m0 + tid < p.M) sg.colsum[m0 + tid] = cs;
 }
 
 // ---------------------------------------------------------------------------
@@ -568,13 +609,13 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec) 
   __shared__ float csr[8][TM];  // the colsum's per-thread partials
   const int mtiles = (p.M + TM - 1) / TM;
   const int m0 = (blockIdx.x % mtiles) * TM, n0 = (blockIdx.x / mtiles) * TN;
-  const int g = blockIdx.y;
-  const int64_t s0 = p.seg_off ? p.seg_off[g] : 0;
-  const int64_t s1 = p.seg_off ? p.seg_off[g + 1] : p.rows;
+  const WgSeg sg = wg_segment(p);
+  if (!sg.valid) return;
+  const int64_t s0 = sg.s0, s1 = sg.s1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const bool vv = vec != 0;
-  const bool do_colsum = p.colsum != nullptr && n0 == 0;
+  const bool do_colsum = sg.colsum != nullptr && n0 == 0;
   // this thread's block: operand B for the second half of the threads
   const bool isb = tid >= TM;
   const int bt = isb ? tid - TM : tid;
@@ -686,7 +727,7 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec) 
     if (ks + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
-  float* og = p.out + (int64_t)g * p.out_stride;
+  float* og = sg.out;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = n0 + wn * WN + nb * 32 + (lane & 31);
@@ -708,7 +749,7 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec) 
     if (tid < TM && m0 + tid < p.M) {
       float v = 0.f;
       for (int i = 0; i < 8; ++i) v += csr[i][tid];
-      p.colsum[(int64_t)g * p.M + m0 + tid] = v;
+      sg.colsum[m0 + tid] = v;
     }
   }
 }
@@ -908,6 +949,94 @@ __global__ __launch_bounds__(256) void gate_wgrad_reduce_kernel(
   }
 }
 
+// Row chunks of the per-expert weight gradients: segment g (offsets[g] ..
+// offsets[g + 1]) in ceil(rows / ch) chunks of at most ch rows (one chunk when
+// empty). A segment of one chunk writes its gradient directly (slot -1); the
+// chunks of a longer one get consecutive partial-sum slots, and multi lists
+// it as (g, first slot, slots) for wg_chunk_reduce_kernel. One workgroup;
+// thread t owns a contiguous span of segments.
+__global__ __launch_bounds__(1024) void wg_chunk_plan_kernel(const int32_t* __restrict__ offsets,
+                                                             int n, int ch,
+                                                             int32_t* __restrict__ chunks,
+                                                             int32_t* __restrict__ multi) {
+  __shared__ int sc[1024], ss[1024], sm[1024];
+  const int t = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int g0 = min(n, t * per), g1 = min(n, g0 + per);
+  int c = 0, sl = 0, mu = 0;
+  for (int g = g0; g < g1; ++g) {
+    const int rows = offsets[g + 1] - offsets[g];
+    const int k = rows > ch ? (rows + ch - 1) / ch : 1;
+    c += k;
+    if (k > 1) {
+      sl += k;
+      ++mu;
+    }
+  }
+  sc[t] = c;
+  ss[t] = sl;
+  sm[t] = mu;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int vc = t >= o ? sc[t - o] : 0, vs = t >= o ? ss[t - o] : 0, vm = t >= o ? sm[t - o] : 0;
+    __syncthreads();
+    sc[t] += vc;
+    ss[t] += vs;
+    sm[t] += vm;
+    __syncthreads();
+  }
+  int pc = sc[t] - c, ps = ss[t] - sl, pm = sm[t] - mu;
+  for (int g = g0; g < g1; ++g) {
+    const int a = offsets[g], rows = offsets[g + 1] - a;
+    const int k = rows > ch ? (rows + ch - 1) / ch : 1;
+    if (k > 1) {
+      multi[1 + 3 * pm] = g;
+      multi[2 + 3 * pm] = ps;
+      multi[3 + 3 * pm] = k;
+      ++pm;
+    }
+    for (int j = 0; j < k; ++j) {
+      int32_t* e = chunks + 1 + 4 * pc;
+      e[0] = g;
+      e[1] = a + j * ch;
+      e[2] = min(a + rows, a + (j + 1) * ch);
+      e[3] = k > 1 ? ps + j : -1;
+      ++pc;
+    }
+    if (k > 1) ps += k;
+  }
+  if (t == 1023) {
+    chunks[0] = sc[t];
+    multi[0] = sm[t];
+  }
+}
+
+// out_g (and colsum_g) of each multi-chunk segment: its chunks' partial sums
+// added in chunk order. blockIdx.y: entry of the multi list.
+__global__ __launch_bounds__(256) void wg_chunk_reduce_kernel(const int32_t* __restrict__ multi,
+                                                              const float* __restrict__ part,
+                                                              const float* __restrict__ pcol,
+                                                              int M, int N,
+                                                              float* __restrict__ out,
+                                                              int64_t out_stride,
+                                                              float* __restrict__ colsum) {
+  if ((int)blockIdx.y >= multi[0]) return;
+  const int32_t* e = multi + 1 + 3 * blockIdx.y;
+  const int g = e[0], s0 = e[1], ns = e[2];
+  const int64_t mn = (int64_t)M * N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < mn) {
+    float v = 0.f;
+    for (int j = 0; j < ns; ++j) v += part[(int64_t)(s0 + j) * mn + i];
+    out[(int64_t)g * out_stride + i] = v;
+  }
+  if (colsum && i < M) {
+    float v = 0.f;
+    for (int j = 0; j < ns; ++j) v += pcol[(int64_t)(s0 + j) * M + i];
+    colsum[(int64_t)g * M + i] = v;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -1012,6 +1141,27 @@ int gate_wgrad_chunks(int64_t B, int n, int d) {
 
 }  // namespace
 
+// Row chunks of the per-expert weight gradients: at most ch rows, ch at least
+// 2048 and large enough that the partial sums of the longest segments fit in
+// 256 MiB (a multi-chunk segment has more than ch rows, so its chunks number
+// under 2 rows / ch and all of them under 2 P / ch).
+static int wg_chunk_rows(int64_t P, int h, int d) {
+  const double need = 2.0 * (double)P * h * d * 4.0 / (256.0 * 1024 * 1024);
+  int64_t ch = std::max<int64_t>(2048, (int64_t)std::ceil(need));
+  return (int)((ch + 31) / 32 * 32);
+}
+static int64_t wg_max_chunks(int64_t P, int n, int ch) { return n + P / ch + 1; }
+static int64_t wg_max_slots(int64_t P, int ch) { return 2 * P / ch + 1; }
+static int64_t wg_max_multi(int64_t P, int n, int ch) { return std::min<int64_t>(n, P / ch) + 1; }
+static size_t wg_chunk_bytes(int64_t P, int n, int d, int h) {
+  const int ch = wg_chunk_rows(P, h, d);
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  return al((size_t)(1 + 4 * wg_max_chunks(P, n, ch)) * 4) +
+         al((size_t)(1 + 3 * wg_max_multi(P, n, ch)) * 4) +
+         al((size_t)wg_max_slots(P, ch) * h * d * 4) +
+         al((size_t)wg_max_slots(P, ch) * std::max(h, d) * 4);
+}
+
 static size_t gate_chunk_bytes(int64_t B, int n, int d) {
   const size_t S = (size_t)gate_wgrad_chunks(B, n, d);
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
@@ -1034,7 +1184,8 @@ size_t backward_ws_bytes(int64_t B, int n, int k, int d, int h, Dt act_dt) {
          + al((size_t)P * d * 4)                                                // dx per pair
          + al((size_t)B * 2 * n * 4)                                            // c|u grads
          + al((size_t)B * d * 4)                                                // dx via gate
-         + gate_chunk_bytes(B, n, d);                                           // dW_g chunks
+         + gate_chunk_bytes(B, n, d)                                            // dW_g chunks
+         + wg_chunk_bytes(P, n, d, h);                                          // dW_e chunks
 }
 
 hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
@@ -1070,6 +1221,12 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   float* gpart = reinterpret_cast<float*>(take((size_t)S * 2 * n * d * 4));
   float* gcol = reinterpret_cast<float*>(take((size_t)S * 2 * n * 4));
   int32_t* gchunk = reinterpret_cast<int32_t*>(take((size_t)(S + 1) * 4));
+  const int wch = wg_chunk_rows(P, h, d);
+  const int64_t wmax_chunks = wg_max_chunks(P, n, wch), wmax_multi = wg_max_multi(P, n, wch);
+  int32_t* wchunks = reinterpret_cast<int32_t*>(take((size_t)(1 + 4 * wmax_chunks) * 4));
+  int32_t* wmulti = reinterpret_cast<int32_t*>(take((size_t)(1 + 3 * wmax_multi) * 4));
+  float* wpart = reinterpret_cast<float*>(take((size_t)wg_max_slots(P, wch) * h * d * 4));
+  float* wpcol = reinterpret_cast<float*>(take((size_t)wg_max_slots(P, wch) * std::max(h, d) * 4));
   hipError_t e;
 
   // routing of the forward's selection, and the 64-row units of its segments
@@ -1146,6 +1303,17 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.mask = hid;
   r.ldm = h;
   if ((e = run_row_gemm(r, b.act_dt, b.act_dt, kF32, max_units, s, b.act_dt == kBF16)) != hipSuccess) return e;
+  // the per-expert weight gradients run over row chunks of at most wch rows (a long
+  // segment's chunks write partial sums, added in chunk order afterwards)
+  hipLaunchKernelGGL(wg_chunk_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, n, wch, wchunks,
+                     wmulti);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  auto chunk_reduce = [&](const Wgrad& w) {
+    hipLaunchKernelGGL(wg_chunk_reduce_kernel,
+                       dim3(blocks_for((int64_t)w.M * w.N), (unsigned)wmax_multi), dim3(256), 0,
+                       s, wmulti, wpart, wpcol, w.M, w.N, w.out, w.out_stride, w.colsum);
+    return hipGetLastError();
+  };
   // dW2_e = sum (gate dy[token])^T hidden, db2_e = sum gate dy[token]
   Wgrad wg{};
   wg.seg_off = offsets;
@@ -1161,10 +1329,14 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   wg.out = b.dw2;
   wg.out_stride = (int64_t)d * h;
   wg.colsum = b.db2;
+  wg.chunks = wchunks;
+  wg.part = wpart;
+  wg.pcol = wpcol;
   // long segments (over 256 rows per expert on average) keep 128 x 128 tiles, so that
   // one popular expert's rows are spread over more workgroups
   const bool short_segs = P < 256 * (int64_t)n;
-  if ((e = run_wgrad(wg, b.act_dt, kF32, n, s, b.act_dt == kBF16, short_segs)) != hipSuccess) return e;
+  if ((e = run_wgrad(wg, b.act_dt, kF32, (int)wmax_chunks, s, b.act_dt == kBF16, short_segs)) != hipSuccess) return e;
+  if ((e = chunk_reduce(wg)) != hipSuccess) return e;
   // dW1_e = sum dA^T x[token], db1_e = sum dA
   wg = Wgrad{};
   wg.seg_off = offsets;
@@ -1179,7 +1351,11 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   wg.out = b.dw1;
   wg.out_stride = (int64_t)h * d;
   wg.colsum = b.db1;
-  if ((e = run_wgrad(wg, kF32, b.act_dt, n, s, b.act_dt == kBF16, short_segs)) != hipSuccess) return e;
+  wg.chunks = wchunks;
+  wg.part = wpart;
+  wg.pcol = wpcol;
+  if ((e = run_wgrad(wg, kF32, b.act_dt, (int)wmax_chunks, s, b.act_dt == kBF16, short_segs)) != hipSuccess) return e;
+  if ((e = chunk_reduce(wg)) != hipSuccess) return e;
   // dx per routed row: dA W1
   r = RowGemm{};
   r.units = units;

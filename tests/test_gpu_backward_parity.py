@@ -41,6 +41,13 @@ CASES = [
     ("flat_bf16_n4096", {"tokens": 2048, "n_experts": 512}, True, False, (0.1, 0.1), 1.0),
     ("flat_bf16_n4096", {"tokens": 700, "n_experts": 96, "k": 6, "d_model": 256}, False, True,
      (0.1, 0.1), 1.0),
+    # segments over 2048 rows: the experts' weight gradients in row chunks whose partial
+    # sums are added afterwards (fp32 kernel; bf16 with 128- and 256-wide tiles)
+    ("tiny_fp32", {"tokens": 6000, "n_experts": 3, "k": 2}, True, True, (0.1, 0.1), 1.0),
+    ("flat_bf16_n4096", {"tokens": 8192, "n_experts": 4, "k": 2, "d_model": 256,
+                         "d_hidden": 256}, True, True, (0.1, 0.1), 1.0),
+    ("zipf_bf16_n256", {"tokens": 4000, "n_experts": 64, "d_hidden": 256}, True, False,
+     (0.1, 0.1), 1.0),
 ]
 
 
