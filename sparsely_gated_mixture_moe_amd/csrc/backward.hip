@@ -86,6 +86,10 @@ struct RowGemm {
   int accumulate;
   void* out;
   int64_t ldo;
+  // optional (with mask): rowdot[p * rd_n + blockIdx.y] = sum over the tile's
+  // columns c of acc[p][c] * mask[p][c], the product before scale, bias and mask
+  float* rowdot;
+  int rd_n;
 };
 
 template <typename TA, typename TW, typename TO>
@@ -117,16 +121,12 @@ __global__ __launch_bounds__(256) void row_gemm_kernel(RowGemm p) {
   const int64_t arow_p = r0 + ar;
   const bool arow_ok = arow_p < rend;
   int64_t arow = 0;
-  float ascale = 1.f;
-  if (arow_ok) {
-    arow = p.gather ? (int64_t)p.gather[arow_p] : arow_p;
-    if (p.scale) ascale = p.scale[arow_p];
-  }
+  if (arow_ok) arow = p.gather ? (int64_t)p.gather[arow_p] : arow_p;
   for (int k0 = 0; k0 < p.K; k0 += kKS) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kk = k0 + ak + i;
-      as[ar][ak + i] = (arow_ok && kk < p.K) ? ascale * ld_f<TA>(p.a, arow * p.lda + kk) : 0.f;
+      as[ar][ak + i] = (arow_ok && kk < p.K) ? ld_f<TA>(p.a, arow * p.lda + kk) : 0.f;
     }
     if (p.wt) {  // W [N][K]: thread reads 4 consecutive K of one column n
       const int n = tid >> 2, kq = (tid & 3) * 4;
@@ -153,6 +153,7 @@ __global__ __launch_bounds__(256) void row_gemm_kernel(RowGemm p) {
     __syncthreads();
   }
   // C layout: lane holds rows 4q + i of its wave's 16, column lr of each tile
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const int c = c0 + 16 * ct + lr;
@@ -164,16 +165,32 @@ __global__ __launch_bounds__(256) void row_gemm_kernel(RowGemm p) {
     for (int i = 0; i < 4; ++i) {
       const int64_t rp = r0 + 16 * wave + 4 * q + i;
       if (rp >= rend) continue;
-      float v = acc[ct][i] + b;
+      float v = acc[ct][i];
+      if (p.scale) v *= p.scale[rp];
+      v += b;
       if (p.relu) v = v > 0.f ? v : 0.f;
       if (p.mask) {
         const float mv = p.mask_bf16 ? ld_f<bf16>(p.mask, rp * p.ldm + c)
                                      : ld_f<float>(p.mask, rp * p.ldm + c);
         v = mv > 0.f ? v : 0.f;
+        rs[i] += acc[ct][i] * mv;
       }
       const int64_t o = rp * p.ldo + c;
       if (p.accumulate) v += ld_f<TO>(p.out, o);
       st_f<TO>(p.out, o, v);
+    }
+  }
+  if (p.rowdot) {  // over the 16 columns of each tile (lanes lr), then the 4 tiles were summed
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) rs[i] += __shfl_xor(rs[i], o);
+    if (lr == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t rp = r0 + 16 * wave + 4 * q + i;
+        if (rp < rend) p.rowdot[rp * p.rd_n + blockIdx.y] = rs[i];
+      }
     }
   }
 }
@@ -565,6 +582,9 @@ __global__ __launch_bounds__(256) void row_tgemm_kernel(RowGemm p, int vec) {
   }
   // C layout: lane holds column l % 32 of each 32-column block, rows
   // 8 (j / 4) + 4 (l / 32) + j % 4 of its wave's 32
+  float rs[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rs[j] = 0.f;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
@@ -584,11 +604,25 @@ __global__ __launch_bounds__(256) void row_tgemm_kernel(RowGemm p, int vec) {
         const float mv = p.mask_bf16 ? ld_f<bf16>(p.mask, rp * p.ldm + c)
                                      : ld_f<float>(p.mask, rp * p.ldm + c);
         v = mv > 0.f ? v : 0.f;
+        rs[j] += acc[nb][j] * mv;
       }
       const int64_t o = rp * p.ldo + c;
       if (p.accumulate) v += ld_f<float>(p.out, o);
       st_f<float>(p.out, o, v);
     }
+  }
+  if (p.rowdot) {  // over the wave's 128 columns (lanes l % 32), then the two column waves
+    __shared__ float rdsum[2][TM];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) rs[j] += __shfl_xor(rs[j], o);
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) rdsum[wn][wm * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)] = rs[j];
+    }
+    __syncthreads();
+    if (tid < TM && r0 + tid < rend) p.rowdot[(r0 + tid) * p.rd_n + blockIdx.y] = rdsum[0][tid] + rdsum[1][tid];
   }
 }
 
@@ -816,13 +850,17 @@ __global__ __launch_bounds__(1024) void cv2_grad_kernel(const float* __restrict_
 }
 
 // Per token, one wave: the gradient of each kept gate, dy_t . E(x_t) of its
-// expert (recomputed rows, fp32, at slot_pos) plus the Importance loss's
-// d/dImportance of the expert, then the kept softmax's backward, g_j (dg_j -
-// sum_l g_l dg_l), into dHk [B][k].
+// expert, plus the Importance loss's d/dImportance of the expert, then the
+// kept softmax's backward, g_j (dg_j - sum_l g_l dg_l), into dHk [B][k]. With
+// E = hidden W2^T + b2, dy . E = (dy W2) . hidden + dy . b2: the first term is
+// the dA product's row dot (rowdot, rd_n partial sums per routed row, added in
+// order), the second is formed here.
 template <typename TY>
 __global__ __launch_bounds__(256) void slot_grad_kernel(int64_t B, int k, int d,
                                                         const void* __restrict__ dy,
-                                                        const float* __restrict__ eo,
+                                                        const float* __restrict__ rowdot,
+                                                        int rd_n,
+                                                        const void* __restrict__ b2,
                                                         const int32_t* __restrict__ slot_pos,
                                                         const int32_t* __restrict__ topk_idx,
                                                         const float* __restrict__ topk_gate,
@@ -835,12 +873,15 @@ __global__ __launch_bounds__(256) void slot_grad_kernel(int64_t B, int k, int d,
   float sgd = 0.f;
   for (int j = 0; j < k; ++j) {
     const int64_t row = slot_pos[t * k + j];  // -1: a slot the route dropped (no expert)
+    const int e = topk_idx[t * k + j];
     float s = 0.f;
-    if (row >= 0)
-      for (int c = lane; c < d; c += 64) s += ld_f<TY>(dy, t * d + c) * eo[row * d + c];
+    if (row >= 0 && b2)
+      for (int c = lane; c < d; c += 64) s += ld_f<TY>(dy, t * d + c) * ld_f<TY>(b2, (int64_t)e * d + c);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    dg[j] = s + dimp[topk_idx[t * k + j]];
+    if (row >= 0)
+      for (int q = 0; q < rd_n; ++q) s += rowdot[row * rd_n + q];
+    dg[j] = s + dimp[e];
     gv[j] = topk_gate[t * k + j];
     sgd += gv[j] * dg[j];
   }
@@ -1052,10 +1093,13 @@ unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 // fp32 storage: on the fp32 matrix cores.
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
 
-hipError_t run_row_gemm(const RowGemm& p, Dt ta, Dt tw, Dt to, int64_t grid_x, hipStream_t s,
+hipError_t run_row_gemm(const RowGemm& p0, Dt ta, Dt tw, Dt to, int64_t grid_x, hipStream_t s,
                         bool bf16_cores = false) {
   if (grid_x <= 0) return hipSuccess;
-  if (bf16_cores && to == kF32) {
+  RowGemm p = p0;
+  const bool tiled = bf16_cores && to == kF32;
+  p.rd_n = tiled ? (p.N + 255) / 256 : (p.N + kT - 1) / kT;  // column tiles: the row dots' stride
+  if (tiled) {
     // 16-byte operand loads when every unit of 8 is in range and aligned
     const size_t wsz = tw == kBF16 ? 2 : 4;
     const int vec = aligned16(p.a) && aligned16(p.w) && p.lda % 8 == 0 && p.K % 8 == 0 &&
@@ -1178,7 +1222,7 @@ size_t backward_ws_bytes(int64_t B, int n, int k, int d, int h, Dt act_dt) {
          + al((size_t)(1 + 2 * max_units) * 4) + al((size_t)(n + 1) * 4)        // units
          + 2 * al((size_t)n * 4)                                                // dimp, dload
          + al((size_t)P * h * 4)                                                // hidden (fp32)
-         + al((size_t)P * d * 4)                                                // expert out
+         + al((size_t)P * ((h + kT - 1) / kT) * 4)                              // row dots
          + al((size_t)B * k * 4)                                                // dHk
          + al((size_t)P * h * 4)                                                // dA
          + al((size_t)P * d * 4)                                                // dx per pair
@@ -1211,7 +1255,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   float* dimp = reinterpret_cast<float*>(take((size_t)n * 4));
   float* dload = reinterpret_cast<float*>(take((size_t)n * 4));
   float* hid = reinterpret_cast<float*>(take((size_t)P * h * 4));
-  float* eo = reinterpret_cast<float*>(take((size_t)P * d * 4));
+  float* rowdot = reinterpret_cast<float*>(take((size_t)P * ((h + kT - 1) / kT) * 4));
   float* dHk = reinterpret_cast<float*>(take((size_t)B * k * 4));
   float* dA = reinterpret_cast<float*>(take((size_t)P * h * 4));
   float* dxe = reinterpret_cast<float*>(take((size_t)P * d * 4));
@@ -1239,9 +1283,8 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
                      b.aux_scale * b.w_importance, b.aux_scale * b.w_load, b.train, dimp, dload);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  // experts: hidden = ReLU(x W1^T + b1) and out = hidden W2^T + b2, both kept in fp32 (the
-  // forward pass rounds them to the storage type; the gradients here are those of the
-  // layer's unrounded function)
+  // experts: hidden = ReLU(x W1^T + b1), kept in fp32 (the forward pass rounds it to the
+  // storage type; the gradients here are those of the layer's unrounded function)
   RowGemm r{};
   r.units = units;
   r.seg_off = offsets;
@@ -1259,32 +1302,8 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.out = hid;
   r.ldo = h;
   if ((e = run_row_gemm(r, b.act_dt, b.act_dt, kF32, max_units, s, b.act_dt == kBF16)) != hipSuccess) return e;
-  r = RowGemm{};
-  r.units = units;
-  r.seg_off = offsets;
-  r.rows = P;
-  r.a = hid;
-  r.lda = h;
-  r.w = b.w2;
-  r.w_stride = (int64_t)d * h;
-  r.wt = 1;
-  r.K = h;
-  r.N = d;
-  r.bias = b.b2;
-  r.out = eo;
-  r.ldo = d;
-  if ((e = run_row_gemm(r, kF32, b.act_dt, kF32, max_units, s, b.act_dt == kBF16)) != hipSuccess) return e;
-  // kept gates: task + Importance gradients through the kept softmax
-  if (B > 0) {
-    if (b.act_dt == kBF16)
-      hipLaunchKernelGGL(slot_grad_kernel<bf16>, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, s,
-                         B, k, d, b.dy, eo, slot_pos, b.topk_idx, b.topk_gate, dimp, dHk);
-    else
-      hipLaunchKernelGGL(slot_grad_kernel<float>, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, s,
-                         B, k, d, b.dy, eo, slot_pos, b.topk_idx, b.topk_gate, dimp, dHk);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  // dA = (gate * dy[token]) W2 masked by hidden > 0
+  // dA = (gate * dy[token]) W2 masked by hidden > 0, and per routed row the dot of
+  // dy[token] W2 with hidden (for the kept gates' gradient dy . E)
   r = RowGemm{};
   r.units = units;
   r.seg_off = offsets;
@@ -1302,7 +1321,21 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.ldo = h;
   r.mask = hid;
   r.ldm = h;
+  r.rowdot = rowdot;
   if ((e = run_row_gemm(r, b.act_dt, b.act_dt, kF32, max_units, s, b.act_dt == kBF16)) != hipSuccess) return e;
+  // kept gates: task + Importance gradients through the kept softmax
+  if (B > 0) {
+    const int rd_n = b.act_dt == kBF16 ? (h + 255) / 256 : (h + kT - 1) / kT;  // as run_row_gemm
+    if (b.act_dt == kBF16)
+      hipLaunchKernelGGL(slot_grad_kernel<bf16>, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, s,
+                         B, k, d, b.dy, rowdot, rd_n, b.b2, slot_pos, b.topk_idx, b.topk_gate,
+                         dimp, dHk);
+    else
+      hipLaunchKernelGGL(slot_grad_kernel<float>, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, s,
+                         B, k, d, b.dy, rowdot, rd_n, b.b2, slot_pos, b.topk_idx, b.topk_gate,
+                         dimp, dHk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // the per-expert weight gradients run over row chunks of at most wch rows (a long
   // segment's chunks write partial sums, added in chunk order afterwards)
   hipLaunchKernelGGL(wg_chunk_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, n, wch, wchunks,
