@@ -410,9 +410,10 @@ def bench_backward(a, w, g, moe, torch, np, dg):
     rows = int(cnt.sum())
     used = int((cnt > 0).sum())
     esize = 2 if w.expert_dtype == dg.BF16 else 4
-    # expert products: hidden, E, dA, dW2, dW1, dx rows (2 d h flops per routed row each);
-    # gate: c and u, dW_g and dW_noise, dx (2 d n flops per token each, twice)
-    flops = 6 * 2.0 * rows * d * h + 3 * 2 * 2.0 * B * d * n
+    # expert products: hidden recompute, dA, dW2, dW1, dx rows (2 d h flops per routed row
+    # each; dy . E needs no recompute of E); gate: c and u, dW_g and dW_noise, dx (2 d n flops
+    # per token each, twice)
+    flops = 5 * 2.0 * rows * d * h + 3 * 2 * 2.0 * B * d * n
     # expert weights read, their fp32 gradients written; the dense [B, 2n] fp32 logit
     # gradients written and read twice; x, dy, dx
     nbytes_alg = (used * 2 * d * h * (esize + 4) + 3 * B * 2 * n * 4
