@@ -152,32 +152,46 @@ __global__ __launch_bounds__(256) void row_gemm_kernel(RowGemm p) {
     }
     __syncthreads();
   }
-  // C layout: lane holds rows 4q + i of its wave's 16, column lr of each tile
-  float rs[4] = {0.f, 0.f, 0.f, 0.f};
+  // C layout: lane holds rows 4q + i of its wave's 16, column lr of each tile.
+  // A tile's mask and accumulate values are loaded together (rows past the
+  // unit read its first row, columns past N column 0; neither is stored).
+  float rs[4] = {0.f, 0.f, 0.f, 0.f}, sc[4];
+  int64_t rr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t rp = r0 + 16 * wave + 4 * q + i;
+    rr[i] = rp < rend ? rp : r0;
+    sc[i] = p.scale ? p.scale[rr[i]] : 1.f;
+  }
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     const int c = c0 + 16 * ct + lr;
-    if (c >= p.N) continue;
+    const bool cok = c < p.N;
+    const int cc = cok ? c : 0;
     float b = 0.f;
     if (p.bias)
-      b = p.bias_f32 ? ld_f<float>(p.bias, (int64_t)g * p.N + c) : ld_f<TW>(p.bias, (int64_t)g * p.N + c);
+      b = p.bias_f32 ? ld_f<float>(p.bias, (int64_t)g * p.N + cc) : ld_f<TW>(p.bias, (int64_t)g * p.N + cc);
+    float mv[4], pv[4];
+    if (p.mask) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mv[i] = p.mask_bf16 ? ld_f<bf16>(p.mask, rr[i] * p.ldm + cc) : ld_f<float>(p.mask, rr[i] * p.ldm + cc);
+    }
+    if (p.accumulate) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = ld_f<TO>(p.out, rr[i] * p.ldo + cc);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t rp = r0 + 16 * wave + 4 * q + i;
-      if (rp >= rend) continue;
-      float v = acc[ct][i];
-      if (p.scale) v *= p.scale[rp];
-      v += b;
+      float v = acc[ct][i] * sc[i] + b;
       if (p.relu) v = v > 0.f ? v : 0.f;
       if (p.mask) {
-        const float mv = p.mask_bf16 ? ld_f<bf16>(p.mask, rp * p.ldm + c)
-                                     : ld_f<float>(p.mask, rp * p.ldm + c);
-        v = mv > 0.f ? v : 0.f;
-        rs[i] += acc[ct][i] * mv;
+        v = mv[i] > 0.f ? v : 0.f;
+        if (cok) rs[i] += acc[ct][i] * mv[i];
       }
-      const int64_t o = rp * p.ldo + c;
-      if (p.accumulate) v += ld_f<TO>(p.out, o);
-      st_f<TO>(p.out, o, v);
+      if (p.accumulate) v += pv[i];
+      const int64_t rp = r0 + 16 * wave + 4 * q + i;
+      if (cok && rp < rend) st_f<TO>(p.out, rp * p.ldo + c, v);
     }
   }
   if (p.rowdot) {  // over the 16 columns of each tile (lanes lr), then the 4 tiles were summed
@@ -482,7 +496,8 @@ struct StageT<float> {
 };
 
 template <typename TA, typename TW, bool WT>
-__global__ __launch_bounds__(256) void row_tgemm_kernel(RowGemm p, int vec) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void row_tgemm_kernel(RowGemm p, int vec) {
   constexpr bool SA = sizeof(TA) == 4, SW = sizeof(TW) == 4;
   constexpr int TM = 64, TN = 256;
   constexpr int ABYTES = TM * 64, BBYTES = TN * 64;  // one bf16 tile of each operand
@@ -581,35 +596,52 @@ __global__ __launch_bounds__(256) void row_tgemm_kernel(RowGemm p, int vec) {
     __syncthreads();
   }
   // C layout: lane holds column l % 32 of each 32-column block, rows
-  // 8 (j / 4) + 4 (l / 32) + j % 4 of its wave's 32
-  float rs[16];
+  // 8 (j / 4) + 4 (l / 32) + j % 4 of its wave's 32. Each block's mask and
+  // accumulate values are loaded together (rows past the unit read its first
+  // row, columns past N column 0; neither is stored), so their latencies overlap.
+  float rs[16], sc[16];
+  int32_t rr[16];  // routed rows are int32 indices
 #pragma unroll
-  for (int j = 0; j < 16; ++j) rs[j] = 0.f;
+  for (int j = 0; j < 16; ++j) {
+    rs[j] = 0.f;
+    const int64_t rp = r0 + wm * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+    rr[j] = (int32_t)(rp < rend ? rp : r0);
+    sc[j] = p.scale ? p.scale[rr[j]] : 1.f;
+  }
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int c = n0 + wn * 128 + nb * 32 + (lane & 31);
-    if (c >= p.N) continue;
+    const bool cok = c < p.N;
+    const int cc = cok ? c : 0;
     float b = 0.f;
     if (p.bias)
-      b = p.bias_f32 ? ld_f<float>(p.bias, (int64_t)g * p.N + c) : ld_f<TW>(p.bias, (int64_t)g * p.N + c);
+      b = p.bias_f32 ? ld_f<float>(p.bias, (int64_t)g * p.N + cc) : ld_f<TW>(p.bias, (int64_t)g * p.N + cc);
+    float mv[16], pv[16];
+    if (p.mask) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        mv[j] = p.mask_bf16 ? ld_f<bf16>(p.mask, (int64_t)rr[j] * p.ldm + cc)
+                            : ld_f<float>(p.mask, (int64_t)rr[j] * p.ldm + cc);
+    }
+    if (p.accumulate) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pv[j] = ld_f<float>(p.out, (int64_t)rr[j] * p.ldo + cc);
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int64_t rp = r0 + wm * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-      if (rp >= rend) continue;
-      float v = acc[nb][j];
-      if (p.scale) v *= p.scale[rp];
-      v += b;
+      float v = acc[nb][j] * sc[j] + b;
       if (p.relu) v = v > 0.f ? v : 0.f;
       if (p.mask) {
-        const float mv = p.mask_bf16 ? ld_f<bf16>(p.mask, rp * p.ldm + c)
-                                     : ld_f<float>(p.mask, rp * p.ldm + c);
-        v = mv > 0.f ? v : 0.f;
-        rs[j] += acc[nb][j] * mv;
+        v = mv[j] > 0.f ? v : 0.f;
+        if (cok) rs[j] += acc[nb][j] * mv[j];
       }
-      const int64_t o = rp * p.ldo + c;
-      if (p.accumulate) v += ld_f<float>(p.out, o);
-      st_f<float>(p.out, o, v);
+      if (p.accumulate) v += pv[j];
+      const int64_t rp = r0 + wm * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+      if (cok && rp < rend) st_f<float>(p.out, rp * p.ldo + c, v);
     }
+    // one block's loads at a time: keeps the next block's loads (and their
+    // registers) below this block's stores
+    asm volatile("" ::: "memory");
   }
   if (p.rowdot) {  // over the wave's 128 columns (lanes l % 32), then the two column waves
     __shared__ float rdsum[2][TM];
