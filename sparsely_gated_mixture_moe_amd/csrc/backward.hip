@@ -932,34 +932,12 @@ __global__ __launch_bounds__(256) void slot_grad_kernel(int64_t B, int k, int d,
 // sigma, dP/dsigma = -phi(z) z / sigma, z = (c - thr) / sigma, thr = v_{k+1}
 // for a kept expert, v_k otherwise (no threshold: 0). Without noise only dc
 // = [kept] dH.
-__global__ __launch_bounds__(256) void pair_grad_kernel(int64_t B, int n, int k, int train,
-                                                        float floor_,
-                                                        const float* __restrict__ eps,
-                                                        const float* __restrict__ thresh,
-                                                        const int32_t* __restrict__ topk_idx,
-                                                        const float* __restrict__ dHk,
-                                                        const float* __restrict__ dload,
-                                                        float* __restrict__ cu) {
-  // one token per blockIdx.x, 256 experts per blockIdx.y
-  const int64_t t = blockIdx.x;
-  const int i = blockIdx.y * 256 + threadIdx.x;
-  if (i >= n) return;
-  float dh = 0.f;
-  bool kept = false;
-  for (int j = 0; j < k; ++j)
-    if (topk_idx[t * k + j] == i) {
-      kept = true;
-      dh = dHk[t * k + j];
-    }
-  float* row = cu + t * 2 * (int64_t)n;
-  if (!train) {
-    row[i] = dh;
-    return;
-  }
-  const float c = row[i], u = row[n + i];
+__device__ __forceinline__ void pair_grad_one(float c, float u, float e, bool kept, float dh,
+                                              const float* thr2, float dl, float floor_,
+                                              float& dc, float& du) {
   const float sigma = softplus_f(u) + floor_;
   const float rs = rcp_f(sigma);
-  const float thr = kept ? thresh[t * 2 + 1] : thresh[t * 2];
+  const float thr = kept ? thr2[1] : thr2[0];
   float pc = 0.f, ps = 0.f;
   if (!isinf(thr)) {
     const float z = (c - thr) * rs;
@@ -967,13 +945,66 @@ __global__ __launch_bounds__(256) void pair_grad_kernel(int64_t B, int n, int k,
     pc = ph * rs;
     ps = -ph * z * rs;
   }
-  const float dl = dload[i];
-  const float dc = dh + dl * pc;
-  const float dsig = dh * eps[t * n + i] + dl * ps;
+  dc = dh + dl * pc;
+  const float dsig = dh * e + dl * ps;
   const float eu = exp_native(-fabsf(u));  // Softplus'(u) = sigmoid(u)
-  const float sg = (u >= 0.f ? 1.f : eu) * rcp_f(1.f + eu);
-  row[i] = dc;
-  row[n + i] = dsig * sg;
+  du = dsig * (u >= 0.f ? 1.f : eu) * rcp_f(1.f + eu);
+}
+
+// One token per blockIdx.x, 4 consecutive experts per thread (1024 per
+// blockIdx.y); vec: n % 4 == 0, so the 4 values of c, u and eps are 16-byte loads.
+__global__ __launch_bounds__(256) void pair_grad_kernel(int64_t B, int n, int k, int train,
+                                                        float floor_, int vec,
+                                                        const float* __restrict__ eps,
+                                                        const float* __restrict__ thresh,
+                                                        const int32_t* __restrict__ topk_idx,
+                                                        const float* __restrict__ dHk,
+                                                        const float* __restrict__ dload,
+                                                        float* __restrict__ cu) {
+  const int64_t t = blockIdx.x;
+  const int i0 = 4 * (blockIdx.y * 256 + threadIdx.x);
+  if (i0 >= n) return;
+  float dh[4] = {0.f, 0.f, 0.f, 0.f};
+  bool kept[4] = {false, false, false, false};
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[t * k + j] - i0;
+    if (e >= 0 && e < 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q == e) {
+          kept[q] = true;
+          dh[q] = dHk[t * k + j];
+        }
+    }
+  }
+  float* row = cu + t * 2 * (int64_t)n;
+  const int cnt = min(4, n - i0);
+  if (!train) {
+    for (int q = 0; q < cnt; ++q) row[i0 + q] = dh[q];
+    return;
+  }
+  const float* thr2 = thresh + t * 2;
+  if (vec && cnt == 4) {
+    const float4 c = *reinterpret_cast<const float4*>(row + i0);
+    const float4 u = *reinterpret_cast<const float4*>(row + n + i0);
+    const float4 e = *reinterpret_cast<const float4*>(eps + t * n + i0);
+    const float4 dl = *reinterpret_cast<const float4*>(dload + i0);
+    float4 dc, du;
+    pair_grad_one(c.x, u.x, e.x, kept[0], dh[0], thr2, dl.x, floor_, dc.x, du.x);
+    pair_grad_one(c.y, u.y, e.y, kept[1], dh[1], thr2, dl.y, floor_, dc.y, du.y);
+    pair_grad_one(c.z, u.z, e.z, kept[2], dh[2], thr2, dl.z, floor_, dc.z, du.z);
+    pair_grad_one(c.w, u.w, e.w, kept[3], dh[3], thr2, dl.w, floor_, dc.w, du.w);
+    *reinterpret_cast<float4*>(row + i0) = dc;
+    *reinterpret_cast<float4*>(row + n + i0) = du;
+    return;
+  }
+  for (int q = 0; q < cnt; ++q) {
+    float dc, du;
+    pair_grad_one(row[i0 + q], row[n + i0 + q], eps[t * n + i0 + q], kept[q], dh[q], thr2,
+                  dload[i0 + q], floor_, dc, du);
+    row[i0 + q] = dc;
+    row[n + i0 + q] = du;
+  }
 }
 
 // dx[t] = dxg[t] + sum over the token's slots of dxe[slot_pos[t][j]] (fp32, slot order).
@@ -1459,8 +1490,10 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
     if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
   }
   if (B > 0) {
-    hipLaunchKernelGGL(pair_grad_kernel, dim3((unsigned)B, (unsigned)((n + 255) / 256)), dim3(256), 0, s, B, n, k,
-                       b.train, b.noise_floor, b.eps, b.thresh, b.topk_idx, dHk, dload, cu);
+    const int vec = n % 4 == 0 && (reinterpret_cast<uintptr_t>(b.eps) & 15) == 0;
+    hipLaunchKernelGGL(pair_grad_kernel, dim3((unsigned)B, (unsigned)((n + 1023) / 1024)),
+                       dim3(256), 0, s, B, n, k, b.train, b.noise_floor, vec, b.eps, b.thresh,
+                       b.topk_idx, dHk, dload, cu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // dW_g = dc^T x, db_g = sum dc; dW_noise = du^T x: one product over the [B][2n]
