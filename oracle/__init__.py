@@ -74,6 +74,10 @@ def _load():
                                          _P, _P, _P, _P, _I, _D, _D, _P, _D, _P, _P, _P]
         lib.oracle_backward.argtypes = [_I64, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D,
                                         _I, _P, _P, _P, _P, _I, _D, _D, _P, _D, _P] + [_P] * 8
+        lib.oracle_backward_sampled.argtypes = (
+            [_I64, _I, _I, _I, _I, _P, _I, _P, _P, _I, _P, _P, _I, _D, _I, _P, _P, _P, _P, _I,
+             _D, _D, _P, _D, _P] + [_I, _P, _P, _P, _P] + [_I, _P, _P, _P, _P, _P] + [_I, _P, _P])
+        lib.oracle_backward_sampled.restype = _I
         lib.oracle_cv2_grad.argtypes = [_I, _P, _P]
         lib.oracle_cv2_grad.restype = None
         lib.oracle_kept_softmax_grad.argtypes = [_I, _P, _P, _P]
@@ -376,6 +380,40 @@ def backward(inp: Dict[str, np.ndarray], k: int, dy, aux_scale: float = 1.0, tra
                                      "dx", "dw_gate", "dw_noise", "dgate_bias", "dw1", "db1",
                                      "dw2", "db2")])
     _check(rc, "backward")
+    return out
+
+
+def backward_sampled(inp: Dict[str, np.ndarray], k: int, dy, gate_experts=(), experts=(),
+                     tokens=(), aux_scale: float = 1.0, train: bool = True,
+                     noise_floor: float = 1e-2, w_importance: float = 0.1, w_load: float = 0.1,
+                     force_idx=None, decide_fp32: bool = True) -> Dict[str, np.ndarray]:
+    """The gradients of ``backward`` for a few experts and tokens (fp64), for
+    batches too large for the whole backward: dw_gate / dw_noise [len(gate_experts), d]
+    and dgate_bias [len(gate_experts)] for the listed gate experts; dw1 [ne, h, d],
+    db1 [ne, h], dw2 [ne, d, h], db2 [ne, d] for the listed experts; dx [nt, d] for
+    the listed tokens. Importance and Load are still taken over the whole batch."""
+    g = _Gate(inp, train)
+    w1, b1, w2, b2, e_dt, h = _experts(inp)
+    B, d, n = g.B, g.d, g.n
+    dy = _dy(dy, B, d)
+    f = _forced(force_idx, (B, k))
+    ge = np.ascontiguousarray(gate_experts, dtype=np.int32)
+    ee = np.ascontiguousarray(experts, dtype=np.int32)
+    tt = np.ascontiguousarray(tokens, dtype=np.int64)
+    ng, ne, nt = ge.size, ee.size, tt.size
+    out = {"dw_gate": np.empty((ng, d)), "dw_noise": np.empty((ng, d)),
+           "dgate_bias": np.empty(ng), "dw1": np.empty((ne, h, d)), "db1": np.empty((ne, h)),
+           "dw2": np.empty((ne, d, h)), "db2": np.empty((ne, d)), "dx": np.empty((nt, d))}
+    rc = _load().oracle_backward_sampled(
+        B, d, h, n, k, *g.args(), int(train), float(noise_floor), int(decide_fp32), _ptr(w1),
+        _ptr(b1), _ptr(w2), _ptr(b2), e_dt, float(w_importance), float(w_load), dy.ctypes.data,
+        float(aux_scale), _ptr(f),
+        ng, ge.ctypes.data, out["dw_gate"].ctypes.data, out["dw_noise"].ctypes.data,
+        out["dgate_bias"].ctypes.data,
+        ne, ee.ctypes.data, out["dw1"].ctypes.data, out["db1"].ctypes.data,
+        out["dw2"].ctypes.data, out["db2"].ctypes.data,
+        nt, tt.ctypes.data, out["dx"].ctypes.data)
+    _check(rc, "backward_sampled")
     return out
 
 

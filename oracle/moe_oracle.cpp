@@ -865,6 +865,259 @@ int oracle_backward(int64_t B, int d, int h, int n, int k, const void* x, int x_
   return 0;
 }
 
+// The same gradients for a few experts and tokens, for batches too large for
+// oracle_backward. One pass over all tokens gives the selection (or the forced
+// one), gates, thresholds, Importance and Load (eqs 6, 8-10; Load summed in
+// fixed blocks of rows) and the clean logits and noise pre-activations of the
+// gate-sampled experts; the kept gates' gradients (the task part dy . E and the
+// Importance part, through the kept softmax) are formed only for the tokens
+// that need them. Outputs (any may be null):
+//   gate experts ge[q] (q < ng): dwg [ng][d], dwn [ng][d], dbg [ng]
+//   experts ee[q] (q < ne): dw1 [ne][h][d], db1 [ne][h], dw2 [ne][d][h], db2 [ne][d]
+//   tokens tt[q] (q < nt): dx [nt][d]
+int oracle_backward_sampled(int64_t B, int d, int h, int n, int k, const void* x, int x_dt,
+                            const void* wg, const void* wn, int w_dt, const float* bg,
+                            const float* eps, int train, double floor, int decide_fp32,
+                            const void* w1, const void* b1, const void* w2, const void* b2,
+                            int e_dt, double w_imp, double w_load, const double* dy,
+                            double aux_scale, const int32_t* force_idx, int ng, const int32_t* ge,
+                            double* dwg, double* dwn, double* dbg, int ne, const int32_t* ee,
+                            double* dw1, double* db1, double* dw2, double* db2, int nt,
+                            const int64_t* tt, double* dx) {
+  if (bad_args(B, d, n, k, train, eps) || h < 1 || !dy || ng < 0 || ne < 0 || nt < 0) return 1;
+  for (int q = 0; q < ng; ++q)
+    if (ge[q] < 0 || ge[q] >= n) return 1;
+  for (int q = 0; q < ne; ++q)
+    if (ee[q] < 0 || ee[q] >= n) return 1;
+  for (int q = 0; q < nt; ++q)
+    if (tt[q] < 0 || tt[q] >= B) return 1;
+  const GateArgs g = make_args(d, n, k, x, x_dt, wg, wn, w_dt, bg, eps, train, floor, decide_fp32);
+  std::vector<int32_t> sel((size_t)B * k);
+  std::vector<double> gate((size_t)B * k), thr((size_t)B * 2);
+  std::vector<double> gc((size_t)B * ng), gu((size_t)B * ng);  // clean logit, u of gate experts
+  const int64_t nblk = (B + kRowBlock - 1) / kRowBlock;
+  std::vector<double> ldblk((size_t)nblk * n, 0.0);
+  int bad = 0;
+#pragma omp parallel
+  {
+    RowGate r(n);
+    std::vector<double> xrow(d), wrow(d);
+#pragma omp for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+      double* lb = ldblk.data() + blk * n;
+      for (int64_t t = blk * kRowBlock; t < std::min(B, (blk + 1) * kRowBlock); ++t) {
+        gate_row(g, t, r, xrow, wrow);
+        if (force_idx && !force_selection(r, force_idx + t * k, k, n)) {
+          bad = 1;
+          continue;
+        }
+        thr[t * 2] = r.vk;
+        thr[t * 2 + 1] = r.vk1;
+        for (int j = 0; j < k; ++j) {
+          sel[t * k + j] = r.order[j];
+          gate[t * k + j] = r.gate[j];
+        }
+        if (train)
+          for (int i = 0; i < n; ++i) lb[i] += p_eq9(g, r, i);
+        for (int q = 0; q < ng; ++q) {
+          const int i = ge[q];
+          gc[t * ng + q] = r.clean[i];
+          double u = 0.0;
+          if (train) {
+            widen_run(g.wn, (int64_t)i * d, d, g.w_dt, wrow.data());
+            for (int c = 0; c < d; ++c) u += xrow[c] * wrow[c];
+          }
+          gu[t * ng + q] = u;
+        }
+      }
+    }
+  }
+  if (bad) return 3;
+  std::vector<double> imp(n, 0.0), ld(n, 0.0), dimp(n), dld(n);
+  for (int64_t t = 0; t < B; ++t)
+    for (int j = 0; j < k; ++j) imp[sel[t * k + j]] += gate[t * k + j];
+  for (int64_t blk = 0; blk < nblk; ++blk)
+    for (int i = 0; i < n; ++i) ld[i] += ldblk[blk * n + i];
+  cv2_grad(n, imp.data(), dimp.data());
+  cv2_grad(n, ld.data(), dld.data());
+  for (int i = 0; i < n; ++i) {
+    dimp[i] *= aux_scale * w_imp;
+    dld[i] = train ? dld[i] * aux_scale * w_load : 0.0;
+  }
+  // The tokens whose kept gates' gradients are needed: the sampled tokens and
+  // every token that keeps a gate-sampled expert.
+  std::vector<char> need(B, 0);
+  for (int q = 0; q < nt; ++q) need[tt[q]] = 1;
+  if (ng > 0) {
+    std::vector<char> isg(n, 0);
+    for (int q = 0; q < ng; ++q) isg[ge[q]] = 1;
+    for (int64_t t = 0; t < B; ++t)
+      for (int j = 0; j < k; ++j)
+        if (isg[sel[t * k + j]]) need[t] = 1;
+  }
+  std::vector<double> dHk((size_t)B * k, 0.0);
+#pragma omp parallel
+  {
+    std::vector<double> xrow(d), wrow(std::max(d, h)), hid(h), eo(d), dg(k), dH(k);
+#pragma omp for schedule(dynamic, 8)
+    for (int64_t t = 0; t < B; ++t) {
+      if (!need[t]) continue;
+      widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+      for (int j = 0; j < k; ++j) {
+        const int e = sel[t * k + j];
+        expert_apply(d, h, xrow.data(), w1, b1, w2, b2, e_dt, e, eo.data(), hid, wrow);
+        double sdy = 0.0;
+        for (int c = 0; c < d; ++c) sdy += dy[t * d + c] * eo[c];
+        dg[j] = sdy + dimp[e];
+      }
+      kept_softmax_grad(k, gate.data() + t * k, dg.data(), dH.data());
+      for (int j = 0; j < k; ++j) dHk[t * k + j] = dH[j];
+    }
+  }
+  // d (loss) / d (clean logit) and / d (u) of token t, expert i (clean c, u given)
+  auto pair_grads = [&](int64_t t, int i, double c, double u, double* dc, double* du) {
+    double dh = 0.0;
+    bool kept = false;
+    for (int j = 0; j < k; ++j)
+      if (sel[t * k + j] == i) {
+        kept = true;
+        dh = dHk[t * k + j];
+      }
+    *dc = dh;
+    *du = 0.0;
+    if (!train) return;
+    const double sigma = softplus(u) + floor;
+    double pc, ps;
+    p_eq9_grad(c, kept ? thr[t * 2 + 1] : thr[t * 2], sigma, &pc, &ps);
+    *dc += dld[i] * pc;
+    const double dsig = dh * (double)eps[t * n + i] + dld[i] * ps;
+    *du = dsig * softplus_grad(u);
+  };
+  // Gate experts: dW_g[i] = sum_t dC[t][i] x_t, dW_noise[i] likewise, db_g[i] = sum_t dC[t][i].
+#pragma omp parallel
+  {
+    std::vector<double> xrow(d);
+#pragma omp for schedule(dynamic, 1)
+    for (int q = 0; q < ng; ++q) {
+      const int i = ge[q];
+      std::vector<double> ag(d, 0.0), an(d, 0.0);
+      double ab = 0.0;
+      for (int64_t t = 0; t < B; ++t) {
+        double dc, du;
+        pair_grads(t, i, gc[t * ng + q], gu[t * ng + q], &dc, &du);
+        widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+        for (int c = 0; c < d; ++c) {
+          ag[c] += dc * xrow[c];
+          an[c] += du * xrow[c];
+        }
+        ab += dc;
+      }
+      for (int c = 0; c < d; ++c) {
+        if (dwg) dwg[(int64_t)q * d + c] = ag[c];
+        if (dwn) dwn[(int64_t)q * d + c] = an[c];
+      }
+      if (dbg) dbg[q] = ab;
+    }
+  }
+  // Sampled experts: each from its routed rows only, scaled by their gates.
+#pragma omp parallel
+  {
+    std::vector<double> xrow(d), wrow(std::max(d, h)), pre(h), hid(h), dO(d), dA(h);
+#pragma omp for schedule(dynamic, 1)
+    for (int q = 0; q < ne; ++q) {
+      const int e = ee[q];
+      std::vector<double> gw1((size_t)h * d, 0.0), gb1(h, 0.0), gw2((size_t)d * h, 0.0), gb2(d, 0.0);
+      for (int64_t t = 0; t < B; ++t) {
+        int j = -1;
+        for (int s2 = 0; s2 < k; ++s2)
+          if (sel[t * k + s2] == e) j = s2;
+        if (j < 0) continue;
+        widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+        for (int a = 0; a < h; ++a) {
+          widen_run(w1, ((int64_t)e * h + a) * d, d, e_dt, wrow.data());
+          double v = 0.0;
+          for (int c = 0; c < d; ++c) v += xrow[c] * wrow[c];
+          if (b1) v += widen(b1, (int64_t)e * h + a, e_dt);
+          pre[a] = v;
+          hid[a] = v > 0.0 ? v : 0.0;
+          dA[a] = 0.0;
+        }
+        for (int c = 0; c < d; ++c) dO[c] = gate[t * k + j] * dy[t * d + c];
+        for (int c = 0; c < d; ++c) {
+          widen_run(w2, ((int64_t)e * d + c) * h, h, e_dt, wrow.data());
+          for (int a = 0; a < h; ++a) {
+            gw2[(size_t)c * h + a] += dO[c] * hid[a];
+            dA[a] += dO[c] * wrow[a];
+          }
+          gb2[c] += dO[c];
+        }
+        for (int a = 0; a < h; ++a) {
+          const double da = pre[a] > 0.0 ? dA[a] : 0.0;
+          gb1[a] += da;
+          for (int c = 0; c < d; ++c) gw1[(size_t)a * d + c] += da * xrow[c];
+        }
+      }
+      if (dw1) std::copy(gw1.begin(), gw1.end(), dw1 + (int64_t)q * h * d);
+      if (db1) std::copy(gb1.begin(), gb1.end(), db1 + (int64_t)q * h);
+      if (dw2) std::copy(gw2.begin(), gw2.end(), dw2 + (int64_t)q * d * h);
+      if (db2) std::copy(gb2.begin(), gb2.end(), db2 + (int64_t)q * d);
+    }
+  }
+  // Sampled tokens: dx through every expert's clean logit and u, and through
+  // each kept expert.
+  if (dx) {
+#pragma omp parallel
+    {
+      RowGate r(n);
+      std::vector<double> xrow(d), wrow(std::max(d, h)), pre(h), dA(h), acc(d), wgr(d), wnr(d);
+#pragma omp for schedule(dynamic, 1)
+      for (int q = 0; q < nt; ++q) {
+        const int64_t t = tt[q];
+        widen_run(x, t * (int64_t)d, d, x_dt, xrow.data());
+        for (int c = 0; c < d; ++c) acc[c] = 0.0;
+        for (int i = 0; i < n; ++i) {
+          widen_run(g.wg, (int64_t)i * d, d, g.w_dt, wgr.data());
+          double c0 = 0.0, u = 0.0;
+          for (int c = 0; c < d; ++c) c0 += xrow[c] * wgr[c];
+          if (g.bg) c0 += (double)g.bg[i];
+          if (train) {
+            widen_run(g.wn, (int64_t)i * d, d, g.w_dt, wnr.data());
+            for (int c = 0; c < d; ++c) u += xrow[c] * wnr[c];
+          }
+          double dc, du;
+          pair_grads(t, i, c0, u, &dc, &du);
+          for (int c = 0; c < d; ++c) acc[c] += dc * wgr[c];
+          if (train)
+            for (int c = 0; c < d; ++c) acc[c] += du * wnr[c];
+        }
+        for (int j = 0; j < k; ++j) {
+          const int e = sel[t * k + j];
+          for (int a = 0; a < h; ++a) {
+            widen_run(w1, ((int64_t)e * h + a) * d, d, e_dt, wrow.data());
+            double v = 0.0;
+            for (int c = 0; c < d; ++c) v += xrow[c] * wrow[c];
+            if (b1) v += widen(b1, (int64_t)e * h + a, e_dt);
+            pre[a] = v;
+            dA[a] = 0.0;
+          }
+          for (int c = 0; c < d; ++c) {
+            widen_run(w2, ((int64_t)e * d + c) * h, h, e_dt, wrow.data());
+            const double dO = gate[t * k + j] * dy[t * d + c];
+            for (int a = 0; a < h; ++a) dA[a] += dO * wrow[a];
+          }
+          for (int a = 0; a < h; ++a) {
+            if (pre[a] <= 0.0) continue;
+            widen_run(w1, ((int64_t)e * h + a) * d, d, e_dt, wrow.data());
+            for (int c = 0; c < d; ++c) acc[c] += dA[a] * wrow[c];
+          }
+        }
+        for (int c = 0; c < d; ++c) dx[(int64_t)q * d + c] = acc[c];
+      }
+    }
+  }
+  return 0;
+}
+
 // The backward's pieces on their own, for their pins.
 void oracle_cv2_grad(int n, const double* v, double* g) { cv2_grad(n, v, g); }
 void oracle_kept_softmax_grad(int k, const double* g, const double* dg, double* dH) {

@@ -188,3 +188,121 @@ def test_backward_empty_batch():
     assert to_host(gr["dx"]).shape == (0, w.d_model)
     for key in ("dw_gate", "dw_noise", "dw1", "dw2"):
         assert np.all(to_host(gr[key]) == 0.0), key
+
+
+def resolve_kinks_sampled(inp, sel, gates, dy, ob, experts, tokens, got_dw1):
+    """resolve_kinks for the sampled oracle: the near-kink pre-activations of
+    the sampled experts' routed rows move the oracle's dW1 rows of those
+    experts, and the sampled tokens' dx, to the GPU's side."""
+    x = dg.as_f32(inp["x"]).astype(np.float64)
+    W1 = dg.as_f32(inp["w1"]).astype(np.float64)
+    W2 = dg.as_f32(inp["w2"]).astype(np.float64)
+    b1 = dg.as_f32(inp["b1"]).astype(np.float64) if "b1" in inp else None
+    tpos = {int(t): q for q, t in enumerate(tokens)}
+    # (expert, rows): the sampled experts' routed rows and the sampled tokens' experts
+    pairs = {}
+    for q, e in enumerate(experts):
+        ts, js = np.nonzero(sel == e)
+        pairs.setdefault(int(e), set()).update(zip(ts.tolist(), js.tolist()))
+    for t in tokens:
+        for j in range(sel.shape[1]):
+            pairs.setdefault(int(sel[t, j]), set()).add((int(t), j))
+    found, sumsq, count = [], 0.0, 0
+    for e, tj in pairs.items():
+        tj = sorted(tj)
+        ts = np.array([a for a, _ in tj], dtype=np.int64)
+        js = np.array([b for _, b in tj], dtype=np.int64)
+        pre = x[ts] @ W1[e].T + (b1[e] if b1 is not None else 0.0)
+        sumsq += float((pre * pre).sum())
+        count += pre.size
+        found.append((e, ts, js, pre))
+    tau = KINK_REL * max(1.0, np.sqrt(sumsq / max(count, 1)))
+    eq = {int(e): q for q, e in enumerate(experts)}
+    n_kink = 0
+    for e, ts, js, pre in found:
+        for r, j in zip(*np.nonzero(np.abs(pre) <= tau)):
+            n_kink += 1
+            t, slot = int(ts[r]), int(js[r])
+            dhid = float((gates[t, slot] * dy[t]) @ W2[e][:, j])
+            sign = -1.0 if pre[r, j] > 0 else 1.0
+            took_other = False
+            if e in eq:  # decide from the GPU's dW1 row of this expert
+                q = eq[e]
+                delta = sign * dhid * x[t]
+                before = np.abs(got_dw1[q, j] - ob["dw1"][q, j]).max()
+                after = np.abs(got_dw1[q, j] - ob["dw1"][q, j] - delta).max()
+                took_other = after < before
+                if took_other:
+                    ob["dw1"][q, j] += delta
+                    if "db1" in ob and ob["db1"].size:
+                        ob["db1"][q, j] += sign * dhid
+            if t in tpos and (took_other or e not in eq):
+                # a sampled token whose expert is not sampled: take the side that agrees
+                # with the GPU's dx (checked below against the bar either way)
+                ob.setdefault("_dx_alt", {})[(tpos[t], e, j)] = sign * dhid * W1[e][j]
+    assert n_kink <= max(16, 1e-4 * count), f"{n_kink} near-kink pre-activations of {count}"
+    return n_kink
+
+
+@pytest.mark.parametrize("name", ["flat_bf16_n4096", "zipf_bf16_n256"])
+def test_backward_full_size_sampled(name):
+    """The backward at full size in the launch configuration bench.py times
+    (moe_backward with its own workspace, after moe_forward): 65536 tokens x 4096
+    experts, and the Zipf-skewed 32768 tokens x 256 experts with its gate bias
+    (about 21K rows on expert 0, whose weight gradients run in row chunks), both
+    512-1024-512, k 4, bf16. Against the oracle's sampled backward with the GPU's
+    selection forced: dW1, dW2 of six experts (the most and least popular, random
+    ones), the gate-weight, noise-weight and gate-bias gradients of the same experts
+    (sums over the whole batch, Importance and Load over the whole batch), and dx
+    of 46 tokens (both ends, tile edges, random)."""
+    w = dg.workload(name)
+    B, d, n, k = w.tokens, w.d_model, w.n_experts, w.k
+    announce(f"moe_backward full size {w.name}: generating inputs")
+    inp = dg.make_inputs(w)
+    g = gpu_inputs(inp)
+    fwd = moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], k,
+                          gate_bias=g.get("gate_bias"), train=True, noise_floor=FLOOR,
+                          return_routing=True)
+    dy = make_dy(w, 3)
+    announce("moe_backward full size: GPU call")
+    grads = moe.moe_backward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], k,
+                             fwd["topk_idx"], fwd["topk_gate"], fwd["thresh"], fwd["importance"],
+                             fwd["load"], to_device(dy), gate_bias=g.get("gate_bias"), train=True,
+                             noise_floor=FLOOR)
+    torch.cuda.synchronize()
+    sel = to_host(fwd["topk_idx"])
+    counts = np.bincount(sel.ravel(), minlength=n)
+    rng = np.random.default_rng(11)
+    nz = np.nonzero(counts)[0]
+    experts = np.unique(np.concatenate([[int(np.argmax(counts)), int(nz[np.argmin(counts[nz])])],
+                                        rng.choice(n, 4, replace=False)])).astype(np.int32)
+    edges = [0, 1, 63, 64, 255, 256, B // 2, B - 257, B - 2, B - 1]
+    tokens = np.unique(np.concatenate([edges, rng.choice(B, 36, replace=False)])).astype(np.int64)
+    announce(f"moe_backward full size: oracle gating on {tokens.size} rows")
+    ref = oracle.gate(inp, k, train=True, noise_floor=FLOOR, rows=tokens, want_logits=True)
+    check_gating(ref, ref["H"], sel, to_host(fwd["topk_gate"]), to_host(fwd["thresh"]), rows=tokens)
+    announce(f"moe_backward full size: oracle sampled backward ({experts.size} experts, "
+             f"{tokens.size} tokens)")
+    ob = oracle.backward_sampled(inp, k, dg.as_f32(dy), gate_experts=experts, experts=experts,
+                                 tokens=tokens, train=True, noise_floor=FLOOR, force_idx=sel)
+    got = {"dw1": to_host(grads["dw1"])[experts], "dw2": to_host(grads["dw2"])[experts],
+           "dw_gate": to_host(grads["dw_gate"])[experts],
+           "dw_noise": to_host(grads["dw_noise"])[experts], "dx": to_host(grads["dx"])[tokens]}
+    if "dgate_bias" in grads:
+        got["dgate_bias"] = to_host(grads["dgate_bias"])[experts]
+    nk = resolve_kinks_sampled(inp, sel, to_host(fwd["topk_gate"]), dg.as_f32(dy), ob, experts,
+                               tokens, got["dw1"])
+    for (q, e, j), delta in ob.pop("_dx_alt", {}).items():  # per token, the side nearer the GPU
+        if np.abs(got["dx"][q] - ob["dx"][q] - delta).max() < np.abs(got["dx"][q] - ob["dx"][q]).max():
+            ob["dx"][q] += delta
+    tol = out_tol(True)
+    errs = {}
+    for key in ("dw1", "dw2", "dw_gate", "dw_noise"):
+        errs[key] = max(rel_err(got[key][q], ob[key][q]) for q in range(experts.size))
+    errs["dx"] = max(rel_err(got["dx"][q], ob["dx"][q]) for q in range(tokens.size))
+    if "dgate_bias" in got:
+        errs["dgate_bias"] = rel_err(got["dgate_bias"], ob["dgate_bias"])
+    print(w.name, "full size: experts", experts.tolist(), "counts", counts[experts].tolist(),
+          {kk: f"{v:.2e}" for kk, v in errs.items()}, "near-kink", nk)
+    bad = {kk: v for kk, v in errs.items() if v > tol}
+    assert not bad, f"errors above {tol}: {bad}"

@@ -191,3 +191,25 @@ def test_unselected_experts_get_gate_gradient_only_from_the_load_loss():
         assert np.all(no_load["dw_gate"][e] == 0.0) and no_load["dgate_bias"][e] == 0.0
         assert np.abs(with_load["dw_gate"][e]).max() > 0.0
         assert np.all(with_load["dw1"][e] == 0.0) and np.all(with_load["db2"][e] == 0.0)
+
+
+@pytest.mark.parametrize("train", [True, False])
+def test_sampled_backward_is_the_backward(train):
+    """The sampled backward (one gate pass over the batch, then only the listed
+    experts and tokens) gives the whole backward's values: every expert and
+    token listed, and a subset listed out of order, with a forced selection."""
+    w, inp, dy = small_case(51, n=7, k=3, B=40)
+    ref = oracle.gate(inp, 3, train=train, noise_floor=FLOOR)
+    sel = ref["topk_idx"][:, ::-1].copy()  # the same sets, another slot order
+    kw = dict(aux_scale=0.8, train=train, noise_floor=FLOOR, w_importance=0.3, w_load=0.4,
+              force_idx=sel)
+    full = oracle.backward(inp, 3, dy, **kw)
+    allE, allT = np.arange(7), np.arange(40)
+    sm = oracle.backward_sampled(inp, 3, dy, gate_experts=allE, experts=allE, tokens=allT, **kw)
+    for key in ("dw_gate", "dw_noise", "dgate_bias", "dw1", "db1", "dw2", "db2", "dx"):
+        np.testing.assert_allclose(sm[key], full[key], rtol=1e-12, atol=1e-14, err_msg=key)
+    E, T = np.array([5, 0, 3]), np.array([39, 2, 17, 0])
+    sub = oracle.backward_sampled(inp, 3, dy, gate_experts=E, experts=E[::-1], tokens=T, **kw)
+    np.testing.assert_allclose(sub["dw_gate"], full["dw_gate"][E], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sub["dw1"], full["dw1"][E[::-1]], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sub["dx"], full["dx"][T], rtol=1e-12, atol=1e-14)
