@@ -38,6 +38,12 @@ int oracle_backward(int64_t, int, int, int, int, const void*, int, const void*, 
                     const void*, const void*, int, double, double, const double*, double,
                     const int32_t*, double*, double*, double*, double*, double*, double*, double*,
                     double*);
+int oracle_backward_sampled(int64_t, int, int, int, int, const void*, int, const void*,
+                            const void*, int, const float*, const float*, int, double, int,
+                            const void*, const void*, const void*, const void*, int, double, double,
+                            const double*, double, const int32_t*, int, const int32_t*, double*,
+                            double*, double*, int, const int32_t*, double*, double*, double*,
+                            double*, int, const int64_t*, double*);
 int oracle_hier_gate(int64_t, const int64_t*, int, int, int, int, int, const void*, int,
                      const void*, const void*, const void*, const void*, int, const float*,
                      const float*, int, double, int, const int32_t*, const int32_t*, int32_t*,
@@ -153,6 +159,25 @@ int main() {
                            db2.data()) == 0,
            "oracle_backward");
     expect(finite(dx) && finite(dwg) && finite(dw1) && finite(dw2), "backward outputs finite");
+    // the sampled backward: two experts, three tokens (the last row included)
+    const int32_t se[2] = {n - 1, 0};
+    const int64_t st[3] = {B - 1, 0, B / 2};
+    std::vector<double> sg(2 * d), sn(2 * d), sb(2), s1(2 * h * d), sb1(2 * h), s2(2 * d * h),
+        sb2(2 * d), sx(3 * d);
+    expect(oracle_backward_sampled(B, d, h, n, k, x.data(), 0, wg.data(), wn.data(), 0, bg.data(),
+                                   eps.data(), train, 0.01, 1, w1.data(), b1.data(), w2.data(),
+                                   b2.data(), 0, 0.1, 0.1, dy.data(), 1.0, ii.data(), 2, se,
+                                   sg.data(), sn.data(), sb.data(), 2, se, s1.data(), sb1.data(),
+                                   s2.data(), sb2.data(), 3, st, sx.data()) == 0,
+           "oracle_backward_sampled");
+    expect(finite(sg) && finite(s1) && finite(sx), "sampled backward outputs finite");
+    const int32_t bad_e[1] = {n};
+    expect(oracle_backward_sampled(B, d, h, n, k, x.data(), 0, wg.data(), wn.data(), 0, bg.data(),
+                                   eps.data(), train, 0.01, 1, w1.data(), b1.data(), w2.data(),
+                                   b2.data(), 0, 0.1, 0.1, dy.data(), 1.0, ii.data(), 1, bad_e,
+                                   sg.data(), sn.data(), sb.data(), 0, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr, 0, nullptr, nullptr) == 1,
+           "oracle_backward_sampled rejects an expert index out of range");
   }
   // k == n: no (k+1)-th logit
   {
