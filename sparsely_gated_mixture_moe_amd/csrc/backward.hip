@@ -8,15 +8,19 @@
 // The experts' hidden activations are recomputed here, not stored by the
 // forward pass (the memory saving the same section describes).
 //
-// The matrix products run on the fp32 matrix cores (v_mfma_f32_16x16x4f32,
-// bf16 operands widened exactly), in two grouped forms over the contiguous
+// The matrix products come in two grouped forms over the contiguous
 // per-expert segments that routing produces:
 //   * row products: out[p] = f(a[p] . W_e) for the rows p of expert e's
-//     segment (a's rows optionally gathered through the token list and scaled
-//     by the row's gate), 64 x 64 output tiles, K in steps of 16 through LDS;
-//   * weight-gradient products: dW_e = sum over e's rows of a[p]^T b[p], one
-//     64 x 64 tile of dW_e per workgroup, the segment's rows in steps of 16,
-//     with the column sums of a (the bias gradients) on the side.
+//     segment (a's rows optionally gathered through the token list, the
+//     row's gate applied in the epilogue), in 64-row units of a segment;
+//   * weight-gradient products: dW_e = sum over e's rows of a[p]^T b[p], with
+//     the column sums of a (the bias gradients) on the side; long segments
+//     run in row chunks whose partial sums are added in chunk order.
+// For fp32 storage they run on the fp32 matrix cores (v_mfma_f32_16x16x4f32,
+// 64 x 64 tiles); for bf16 storage on the bf16 matrix cores (the tiled
+// kernels below). The expert outputs are never recomputed: the kept gates'
+// gradient needs only dy . E = (dy W2) . hidden + dy . b2, whose first term
+// the dA product forms in its epilogue.
 // Every sum runs in a fixed order, so the results are deterministic.
 #include <algorithm>
 #include <cmath>
@@ -231,7 +235,7 @@ struct Wgrad {
   // out_g [M][N] fp32 at out + g * out_stride (row stride N)
   float* out;
   int64_t out_stride;
-  // optional: colsum[g * M + m] = sum over g's rows of a[p][m], in row order
+  // optional: colsum[g * M + m] = sum over g's rows of a[p][m], in a fixed order
   float* colsum;
   // optional row chunks (wg_chunk_plan_kernel): blockIdx.y is chunk c = (g,
   // first row, end row, slot) of chunks[1 + 4c ..], chunks[0] the count; a
@@ -349,20 +353,18 @@ __global__ __launch_bounds__(256) void wgrad_kernel(Wgrad p) {
 // the row products' epilogue, in the weight-gradient products to the split
 // operand.
 //
-// Four waves (2 x 2) per workgroup, K in steps of 32 through two LDS buffers:
-// the next step's operands are loaded into registers (16-byte loads, fp32
-// split on the way) while the current step is multiplied. Tiles are 64 rows x
-// 256 columns for the row products (a 64-row unit of a segment), 128 x 128
-// for the weight gradients. An operand tile keeps its source's layout in LDS:
-//   K-major (source rows K-contiguous: x, dy, hidden, dA and logit-gradient
-//     rows, the rows of an [N][K] weight): [R][32] bf16, 64 bytes a row,
-//     16-byte unit u of row r at position u ^ (((r >> 1) ^ (r >> 3)) & 3); a
-//     fragment is one 16-byte read;
-//   K-indexed rows (a [K][N] weight, the routed rows of a weight gradient):
-//     [32][R] bf16, unit u of row k at position u ^ (4 ((k >> 3) & 1)); a
-//     fragment gathers its 8 K values with 8 two-byte reads.
-// Either placement keeps the reads of 8 (or 16) consecutive lanes, and those
-// of the two half-waves, in distinct banks.
+// Row products: four waves (2 x 2), 64 rows x 256 columns (a 64-row unit of a
+// segment); weight gradients: 128 x 128 tiles (four waves) or 256 x 256 (eight
+// waves, where segments are short). K runs in steps of 32 through two LDS
+// buffers; the next step's operands are loaded into registers (16-byte loads,
+// fp32 split on the way) while the current step is multiplied. Every operand
+// tile is K-major in LDS, [R][32] bf16, 64 bytes a row, 16-byte unit u of row
+// r at position u ^ (((r >> 1) ^ (r >> 3)) & 3), so that the 16-byte operand
+// reads of 8 (or 16) consecutive rows hit distinct banks; a fragment is one
+// such read. A K-contiguous source (x, dy, hidden, dA and logit-gradient rows,
+// the rows of an [N][K] weight) is stored as loaded; a source whose rows are
+// K-indexed (a [K][N] weight, the routed rows of a weight gradient) is
+// transposed in registers on its way in, 4 K rows x 8 columns per thread.
 // ---------------------------------------------------------------------------
 
 constexpr int kBK = 32;  // K per step of the tiled bf16 products
