@@ -126,7 +126,8 @@ __global__ __launch_bounds__(1024) void group_plan_kernel(const int32_t* __restr
 // workgroup; thread t owns a contiguous span of experts.
 __global__ __launch_bounds__(1024) void corr_slice_scan_kernel(const int32_t* __restrict__ offsets,
                                                                int n,
-                                                               int32_t* __restrict__ slice_start) {
+                                                               int32_t* __restrict__ slice_start,
+                                                               int32_t* __restrict__ slice_e) {
   __shared__ int part[1024];
   const int t = threadIdx.x;
   const int per = (n + 1023) / 1024;
@@ -145,7 +146,9 @@ __global__ __launch_bounds__(1024) void corr_slice_scan_kernel(const int32_t* __
   int pos = part[t] - s;
   for (int e = e0; e < e1; ++e) {
     slice_start[e] = pos;
-    pos += (offsets[e + 1] - offsets[e] + kCorrSliceRows - 1) / kCorrSliceRows;
+    const int ns = (offsets[e + 1] - offsets[e] + kCorrSliceRows - 1) / kCorrSliceRows;
+    for (int i = 0; i < ns; ++i) slice_e[pos + i] = e;  // each slice's expert
+    pos += ns;
   }
   if (t == 1023) slice_start[n] = part[t];
 }
@@ -179,14 +182,19 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float (&v)[
 // and sums Phi((clean - v_{k+1}) / sigma) - Phi((clean - v_k) / sigma), with
 // clean = x . W_g[e] (+ bias) and sigma = Softplus(x . W_noise[e]) + floor
 // recomputed by a dot product over d in fp32. Workgroup i, four waves, takes
-// slice i of the slices corr_slice_scan_kernel lists: the slice's expert e
-// is found by a binary search of slice_start, its rows are kCorrSliceRows
-// consecutive routed rows of e (fewer in e's last slice); lane l holds
-// elements 8 l .. 8 l + 7 of both weight rows (d <= 512); wave w takes the
-// slice's groups of eight with index w mod 4, all eight in flight at once;
-// the four waves' sums are added in wave order into corr[i], and the
-// reductions add an expert's slices in order. Workgroups past the number of
-// slices (the grid covers the largest possible count) exit at once.
+// slice i of the slices corr_slice_scan_kernel lists (its expert slice_e[i]):
+// kCorrSliceRows consecutive routed rows of e (fewer in e's last slice); lane
+// l holds elements 8 l .. 8 l + 7 of both weight rows (d <= 512); wave w
+// takes the slice's groups of eight rows with index w mod 4, all eight in
+// flight at once. A group's 16 partial dots per lane (clean and noise, eight
+// rows) are summed over the wave by a transposing reduction (each step
+// exchanges half of the values a lane holds with its partner, keeping the
+// other half), after which lane l holds the total of row (l / 4) % 8, clean
+// for l < 32 and noise otherwise; eight lanes then evaluate the eight rows'
+// Phi terms at once. The four waves' sums are added in wave order into
+// corr[i], and the reductions add an expert's slices in order. Workgroups past
+// the number of slices (the grid covers the largest possible count) exit at
+// once.
 // Secondary gates of a hierarchical layer: expert e is leaf (g, j) = (e / b,
 // e % b), its weights are row e of the [a * b, d] secondary weights, and token
 // t's thresholds are row t * k1 + r, where r is g's rank in sel1[t].
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
     const float* __restrict__ bias, int d, int n, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm_token, const float* __restrict__ thresh, float noise_floor,
     const int32_t* __restrict__ sel1, int k1, int b, const int32_t* __restrict__ slice_start,
-    float* __restrict__ corr) {
+    const int32_t* __restrict__ slice_e, float* __restrict__ corr) {
   constexpr int R = 8;
   static_assert(kCorrSliceRows % (4 * R) == 0, "slices are whole passes of the 4 x R rows");
   __shared__ float part[4];
@@ -204,15 +212,7 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
   const int wave = threadIdx.x >> 6;
   const int slice = blockIdx.x;
   if (slice >= slice_start[n]) return;  // uniform: past the number of slices
-  // the expert of this slice: the last e with slice_start[e] <= slice (experts
-  // without rows have no slice, so e is never one of them)
-  int lo = 0, hi = n;  // slice_start[lo] <= slice < slice_start[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (slice_start[mid] <= slice) lo = mid;
-    else hi = mid;
-  }
-  const int e = lo;
+  const int e = slice_e[slice];
   const int p0 = offsets[e] + (slice - slice_start[e]) * kCorrSliceRows;
   const int p1 = min(offsets[e + 1], p0 + kCorrSliceRows);
   const bool active = lane * 8 < d;
@@ -226,26 +226,17 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
   }
   const float be = bias ? bias[e] : 0.f;
   const int grp = e / b;
+  // after the reduction: this lane's row of the group, and whether it holds
+  // the noise dot (lanes 32-63) or the clean one
+  const bool hi5 = lane >= 32, b4 = (lane & 16) != 0, b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+  const int myr = (lane >> 2) & 7;
+  const bool evaluates = !hi5 && (lane & 3) == 0;  // 8 lanes, one row each
   float acc = 0.f;
   for (int p = p0 + wave * R; p < p1; p += 4 * R) {
-    int64_t t[R], row[R];
-    float c[R], u[R], th0[R], th1[R];
+    int64_t t[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) t[r] = perm_token[min(p + r, p1 - 1)];
-    // each row's thresholds (row of the secondary gate: the token's rank of
-    // the group), requested together with the rows of x
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      row[r] = t[r];
-      if (sel1) {
-        int rank = 0;
-        for (int j = 0; j < k1; ++j)
-          if (sel1[t[r] * k1 + j] == grp) rank = j;
-        row[r] = t[r] * k1 + rank;
-      }
-      th0[r] = thresh[row[r] * 2];
-      th1[r] = thresh[row[r] * 2 + 1];
-    }
+    float c[R], u[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       c[r] = u[r] = 0.f;
@@ -259,23 +250,49 @@ __global__ __launch_bounds__(256) void load_correction_kernel(
         }
       }
     }
+    // transposing reduction over the wave: lanes l, l ^ 32 (clean / noise),
+    // l ^ 16 (rows 0-3 / 4-7), l ^ 8, l ^ 4, then the quad
+    float v8[R];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        c[r] += __shfl_xor(c[r], o);
-        u[r] += __shfl_xor(u[r], o);
-      }
+    for (int i = 0; i < R; ++i) {
+      const float keep = hi5 ? u[i] : c[i], send = hi5 ? c[i] : u[i];
+      v8[i] = keep + __shfl_xor(send, 32);
     }
+    float v4[4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (p + r < p1) {  // uniform across the wave
-        const float inv = rcp_f(softplus_f(u[r]) + noise_floor);
-        const float cl = c[r] + be;
-        acc += phi_f((cl - th1[r]) * inv) - phi_f((cl - th0[r]) * inv);
+    for (int i = 0; i < 4; ++i) {
+      const float keep = b4 ? v8[4 + i] : v8[i], send = b4 ? v8[i] : v8[4 + i];
+      v4[i] = keep + __shfl_xor(send, 16);
+    }
+    float v2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float keep = b3 ? v4[2 + i] : v4[i], send = b3 ? v4[i] : v4[2 + i];
+      v2[i] = keep + __shfl_xor(send, 8);
+    }
+    float v1 = (b2 ? v2[1] : v2[0]) + __shfl_xor(b2 ? v2[0] : v2[1], 4);
+    v1 += __shfl_xor(v1, 2);
+    v1 += __shfl_xor(v1, 1);
+    const float un = __shfl_xor(v1, 32);  // the row's noise dot, for the clean lanes
+    const int pr = p + myr;
+    if (evaluates && pr < p1) {
+      const int64_t tok = perm_token[pr];
+      int64_t row = tok;
+      if (sel1) {
+        // the row of the secondary gate: the token's rank of the group
+        int rank = 0;
+        for (int j = 0; j < k1; ++j)
+          if (sel1[tok * k1 + j] == grp) rank = j;
+        row = tok * k1 + rank;
       }
+      const float th0 = thresh[row * 2], th1 = thresh[row * 2 + 1];
+      const float inv = rcp_f(softplus_f(un) + noise_floor);
+      const float cl = v1 + be;
+      acc += phi_f((cl - th1) * inv) - phi_f((cl - th0) * inv);
     }
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
   if (lane == 0) part[wave] = acc;
   __syncthreads();
   if (threadIdx.x == 0) corr[slice] = ((part[0] + part[1]) + part[2]) + part[3];
@@ -463,7 +480,9 @@ int64_t corr_slices_max(int64_t pairs, int n) {
 
 size_t corr_bytes(int64_t pairs, int n) {
   const size_t f = ((size_t)corr_slices_max(pairs, n) * sizeof(float) + 255) / 256 * 256;
-  return f + ((size_t)(n + 1) * sizeof(int32_t) + 255) / 256 * 256;
+  const size_t st = ((size_t)(n + 1) * sizeof(int32_t) + 255) / 256 * 256;
+  const size_t se = ((size_t)corr_slices_max(pairs, n) * sizeof(int32_t) + 255) / 256 * 256;
+  return f + st + se;
 }
 
 // The slice list of the corr region: after the slice sums.
@@ -477,14 +496,16 @@ hipError_t launch_load_correction(const GateLaunch& g, int n, int64_t pairs,
                                   const float* thresh, const int32_t* sel1, int k1, int b,
                                   float* corr, hipStream_t s) {
   int32_t* slice_start = corr_slice_start(corr, pairs, n);
-  hipLaunchKernelGGL(corr_slice_scan_kernel, dim3(1), dim3(1024), 0, s, offsets, n, slice_start);
+  int32_t* slice_e = slice_start + ((size_t)(n + 1) * sizeof(int32_t) + 255) / 256 * 256 / sizeof(int32_t);
+  hipLaunchKernelGGL(corr_slice_scan_kernel, dim3(1), dim3(1024), 0, s, offsets, n, slice_start,
+                     slice_e);
   const dim3 grid((unsigned)corr_slices_max(pairs, n)), block(256);
   const void* bias = g.units ? nullptr : g.bias;
   const float* bp = reinterpret_cast<const float*>(bias);
 #define MOE_CORR(XS, WS)                                                                      \
   hipLaunchKernelGGL((load_correction_kernel<XS, WS>), grid, block, 0, s, g.x, g.w_gate,      \
                      g.w_noise, bp, g.d, n, offsets, perm_token, thresh, g.noise_floor, sel1, \
-                     k1, b, slice_start, corr)
+                     k1, b, slice_start, slice_e, corr)
   if (g.x_dt == kBF16 && g.w_dt == kBF16) MOE_CORR(bf16, bf16);
   else if (g.x_dt == kBF16) MOE_CORR(bf16, float);
   else MOE_CORR(float, float);

@@ -70,7 +70,7 @@ int gate_blocks(int64_t tokens);
 // expert with many rows is spread over many workgroups. The corr region of
 // corr_bytes(pairs, n) bytes holds one float per slice (at most
 // corr_slices_max(pairs, n) slices), then each expert's first slice [n + 1]
-// (int32).
+// (int32), then each slice's expert [corr_slices_max] (int32).
 constexpr int kCorrSliceRows = 256;
 int64_t corr_slices_max(int64_t pairs, int n);
 size_t corr_bytes(int64_t pairs, int n);
