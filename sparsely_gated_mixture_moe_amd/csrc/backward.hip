@@ -254,10 +254,10 @@ struct WgSeg {
   float* out;
   float* colsum;
 };
-__device__ __forceinline__ WgSeg wg_segment(const Wgrad& p) {
+__device__ __forceinline__ WgSeg wg_segment(const Wgrad& p, int gy) {
   WgSeg r;
   if (p.chunks) {
-    const int c = blockIdx.y;
+    const int c = gy;
     r.valid = c < p.chunks[0];
     if (!r.valid) return r;
     const int32_t* e = p.chunks + 1 + 4 * c;
@@ -272,7 +272,7 @@ __device__ __forceinline__ WgSeg wg_segment(const Wgrad& p) {
     return r;
   }
   r.valid = true;
-  r.g = blockIdx.y;
+  r.g = gy;
   r.s0 = p.seg_off ? p.seg_off[r.g] : 0;
   r.s1 = p.seg_off ? p.seg_off[r.g + 1] : p.rows;
   r.out = p.out + (int64_t)r.g * p.out_stride;
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(Wgrad p) {
   __shared__ float bt[kKS][kT + 1];
   const int mtiles = (p.M + kT - 1) / kT;
   const int m0 = (blockIdx.x % mtiles) * kT, n0 = (blockIdx.x / mtiles) * kT;
-  const WgSeg sg = wg_segment(p);
+  const WgSeg sg = wg_segment(p, blockIdx.y);
   if (!sg.valid) return;
   const int64_t s0 = sg.s0, s1 = sg.s1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -412,6 +412,7 @@ __device__ __forceinline__ void load8(const float* p, int valid, bool vec, float
 #pragma unroll
   for (int j = 0; j < 8; ++j) f[j] = j < valid ? p[j] : 0.f;
 }
+
 
 // One operand unit in registers between its load and its LDS store: raw bf16
 // bits, or fp32 values (split, times a scale, at the store).
@@ -663,8 +664,30 @@ void row_tgemm_kernel(RowGemm p, int vec) {
 // Weight gradients: TM x TM output tiles, NW waves in a 2 x (NW / 2) grid;
 // the first half of the threads loads A, the second half B, each thread 4
 // rows x 8 columns per step, transposed into K-major tiles.
-template <typename TA, typename TB, int TM, int NW>
-__global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec) {
+//
+// PERSIST false: one tile per workgroup, tile blockIdx.x of segment blockIdx.y.
+// PERSIST true: the grid (a multiple of 8) walks the nseg segments' tiles in
+// order, tile T = v + i * gridDim.x, where v numbers the workgroups so that
+// consecutive v run on one XCD (workgroup b runs on XCD b % 8) and a segment's
+// tiles share that die's L2. A workgroup loads its next tile's first K step
+// before it writes the current tile out, so that the loads' latency hides
+// behind the stores.
+// Stand-ins read for a missing row scale or gather index.
+__device__ const float kOneF = 1.f;
+__device__ const int32_t kZeroI = 0;
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* v) {
+  return reinterpret_cast<P*>(uniform64((int64_t)reinterpret_cast<uintptr_t>(v)));
+}
+
+template <typename TA, typename TB, int TM, int NW, bool PERSIST>
+__global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec, int nseg) {
   constexpr bool SA = sizeof(TA) == 4, SB = sizeof(TB) == 4;
   static_assert(SA || SB, "a row scale needs a split operand");
   static_assert(TM * 2 == NW * 64, "one 4 x 8 block of A or B per thread");
@@ -676,21 +699,38 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec) 
   __shared__ __attribute__((aligned(16))) uint8_t bl[SB ? 2 : 1][SB ? BYTES : 16];
   __shared__ float csr[8][TM];  // the colsum's per-thread partials
   const int mtiles = (p.M + TM - 1) / TM;
-  const int m0 = (blockIdx.x % mtiles) * TM, n0 = (blockIdx.x / mtiles) * TN;
-  const WgSeg sg = wg_segment(p);
-  if (!sg.valid) return;
-  const int64_t s0 = sg.s0, s1 = sg.s1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tps = mtiles * ((p.N + TN - 1) / TN);  // tiles per segment
+  const int64_t tend = PERSIST ? (int64_t)tps * nseg : 0;
+  int64_t T = PERSIST ? (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8
+                      : (int64_t)blockIdx.y * tps + blockIdx.x;
+  if (PERSIST && T >= tend) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const bool vv = vec != 0;
-  const bool do_colsum = sg.colsum != nullptr && n0 == 0;
-  // this thread's block: operand B for the second half of the threads
-  const bool isb = tid >= TM;
+  // this thread's block: operand B for the second half of the threads (whole waves)
+  const bool isb = wave >= NW / 2;
   const int bt = isb ? tid - TM : tid;
   const int kq = bt / (TM / 8), mu = bt % (TM / 8);  // rows 4 kq .. + 3, columns 8 mu .. + 7
-  const int c0 = (isb ? n0 : m0) + 8 * mu;
   const int clim = isb ? p.N : p.M;
-  const int nvalid = std::min(8, std::max(0, clim - c0));
+  // the current tile (uniform over the workgroup): output corner, rows, destinations
+  int m0 = 0, n0 = 0;
+  int64_t s0 = 0, s1 = 0;
+  float* out = nullptr;
+  float* colsum = nullptr;
+  auto tile_at = [&](int64_t t) __attribute__((always_inline)) {
+    const int g = (int)(t / tps), tt = (int)(t - (int64_t)g * tps);
+    m0 = (tt % mtiles) * TM;
+    n0 = (tt / mtiles) * TN;
+    const WgSeg sg = wg_segment(p, g);
+    if (!sg.valid) return false;
+    s0 = uniform64(sg.s0);
+    s1 = uniform64(sg.s1);
+    out = uniform_ptr(sg.out);
+    colsum = n0 == 0 ? uniform_ptr(sg.colsum) : nullptr;
+    return true;
+  };
+  if (!tile_at(T)) return;
   // a thread stages either an A block or a B block
   union Staged {
     StageT<TA> a;
@@ -701,53 +741,115 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec) 
   float cs[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) cs[i] = 0.f;
-  auto load = [&](int64_t r) __attribute__((always_inline)) {
+  // Per staged row: the A and B row scales and whether it holds data (bit j
+  // of `on`). They are applied when the step is stored to LDS, after the
+  // products that hide the loads' latency: a step's index and scale loads
+  // issue together, then its data loads, and nothing waits on them before
+  // the store. A wave stages A or B only, so every branch here is uniform.
+  float rfa[4], rfb[4];
+  int on = 0;
+  auto load_rows = [&](const auto* src, int64_t ld, const int32_t* gat, int64_t r, auto& st)
+      __attribute__((always_inline)) {
     const int64_t rb = r + 4 * kq;
     const int krows = (int)std::max<int64_t>(0, std::min<int64_t>(4, s1 - rb));
-    // rows are gathered one by one, so load row by row
+    const int c0 = (isb ? n0 : m0) + 8 * mu;
+    const int nvalid = std::min(8, std::max(0, clim - c0));
+    // rows past the segment's end read its first row (s0 < s1 whenever a
+    // step is loaded) and stage zeros; a missing scale or gather reads a
+    // constant, so that every load here is unconditional and unused until
+    // the data loads (or the store)
+    int32_t ri[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t rp = rb + j;
-      const bool ok = j < krows;
-      float fa = 1.f, fb = 1.f;
-      int64_t row = 0;
-      if (ok) {
-        if (p.a_scale) fa = p.a_scale[rp];
-        if (p.b_scale) fb = p.b_scale[rp];
-        const int32_t* gat = isb ? p.b_gather : p.a_gather;
-        row = gat ? (int64_t)gat[rp] : rp;
+      const int64_t rp = j < krows ? rb + j : s0;
+      rfa[j] = *(p.a_scale ? p.a_scale + rp : &kOneF);
+      rfb[j] = *(p.b_scale ? p.b_scale + rp : &kOneF);
+      ri[j] = *(gat ? gat + rp : &kZeroI);
+    }
+    int64_t row[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) row[j] = gat ? (int64_t)ri[j] : (j < krows ? rb + j : s0);
+    on = 0;
+    if (vv) {
+      // nvalid is 0 or 8; a row without data reads element 0 of its operand
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = j < krows && nvalid == 8;
+        on |= ok ? (1 << j) : 0;
+        const int64_t off = ok ? row[j] * ld + c0 : 0;
+        if constexpr (sizeof(*src) == 4) {
+          const float4* q = reinterpret_cast<const float4*>(src + off);
+          const float4 x0 = q[0], x1 = q[1];
+          st.f[j][0] = x0.x; st.f[j][1] = x0.y; st.f[j][2] = x0.z; st.f[j][3] = x0.w;
+          st.f[j][4] = x1.x; st.f[j][5] = x1.y; st.f[j][6] = x1.z; st.f[j][7] = x1.w;
+        } else {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + off);
+          st.w[j][0] = v.x; st.w[j][1] = v.y; st.w[j][2] = v.z; st.w[j][3] = v.w;
+        }
       }
-      // the row's scale goes to a split operand, so that an exact one stays exact
-      const float sc = (isb == SB) ? fa * fb : 1.f;
-      if (!isb) {
-        if constexpr (SA) {
-          load8(reinterpret_cast<const float*>(p.a) + row * p.lda + c0, ok ? nvalid : 0, vv, sa.f[j]);
-          if (do_colsum) {
+    } else {
+      on = 0xF;  // load8 zero-fills what it does not read
 #pragma unroll
-            for (int e = 0; e < 8; ++e) cs[e] += fa * sa.f[j][e];
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sa.f[j][e] *= sc;
-        } else {
-          load8(reinterpret_cast<const bf16*>(p.a) + row * p.lda + c0, ok ? nvalid : 0, vv, sa.w[j]);
-          if (do_colsum) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              cs[e] += fa * bf16_bits_to_f32((sa.w[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-          }
-        }
-      } else {
-        if constexpr (SB) {
-          load8(reinterpret_cast<const float*>(p.b) + row * p.ldb + c0, ok ? nvalid : 0, vv, sb.f[j]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sb.f[j][e] *= sc;
-        } else {
-          load8(reinterpret_cast<const bf16*>(p.b) + row * p.ldb + c0, ok ? nvalid : 0, vv, sb.w[j]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int valid = j < krows ? nvalid : 0;
+        if constexpr (sizeof(*src) == 4) load8(src + row[j] * ld + c0, valid, false, st.f[j]);
+        else load8(src + row[j] * ld + c0, valid, false, st.w[j]);
       }
     }
   };
+  auto load = [&](int64_t r) __attribute__((always_inline)) {
+    if (!isb) load_rows(reinterpret_cast<const TA*>(p.a), p.lda, p.a_gather, r, sa);
+    else load_rows(reinterpret_cast<const TB*>(p.b), p.ldb, p.b_gather, r, sb);
+  };
   auto store = [&](int buf) __attribute__((always_inline)) {
+    // rows without data become zeros (a select: whatever they read stays out)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = (on >> j) & 1;
+      if (!isb) {
+        if constexpr (SA) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sa.f[j][e] = ok ? sa.f[j][e] : 0.f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sa.w[j][e] = ok ? sa.w[j][e] : 0u;
+        }
+      } else {
+        if constexpr (SB) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sb.f[j][e] = ok ? sb.f[j][e] : 0.f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sb.w[j][e] = ok ? sb.w[j][e] : 0u;
+        }
+      }
+    }
+    // the column sums take A's rows times their scale; the row's two scales
+    // go to the split operand, so that an exact one stays exact
+    if (!isb) {
+      if (colsum != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if constexpr (SA) cs[e] += rfa[j] * sa.f[j][e];
+            else cs[e] += rfa[j] * bf16_bits_to_f32((sa.w[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          }
+      }
+      if constexpr (!SB) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sa.f[j][e] *= rfa[j] * rfb[j];
+      }
+    } else {
+      if constexpr (SB) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sb.f[j][e] *= rfa[j] * rfb[j];
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int pos = kmaj_pos(8 * mu + e, kq >> 1) + 8 * (kq & 1);
@@ -755,70 +857,88 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec) 
       else sb.store(bh[buf], bl[SB ? buf : 0], e, pos);
     }
   };
-  f32x16 acc[MB][NB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mb][nb][j] = 0.f;
-  const int64_t nk = (s1 - s0 + kBK - 1) / kBK;
-  if (nk > 0) {
-    load(s0);
-    store(0);
-  }
-  __syncthreads();
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    const int buf = (int)(ks & 1);
-    if (ks + 1 < nk) load(s0 + (ks + 1) * kBK);
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      U16 a[MB], a2[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        a[mb] = frag_kmaj(ah[buf], wm * WM + mb * 32, s, lane);
-        if constexpr (SA) a2[mb] = frag_kmaj(al[buf], wm * WM + mb * 32, s, lane);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const U16 b = frag_kmaj(bh[buf], wn * WN + nb * 32, s, lane);
-        U16 b2;
-        if constexpr (SB) b2 = frag_kmaj(bl[buf], wn * WN + nb * 32, s, lane);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          Mfma<bf16>::k32(acc[mb][nb], a[mb], b);
-          if constexpr (SA) Mfma<bf16>::k32(acc[mb][nb], a2[mb], b);
-          if constexpr (SB) Mfma<bf16>::k32(acc[mb][nb], a[mb], b2);
-        }
-      }
-    }
-    if (ks + 1 < nk) store(buf ^ 1);
+  int64_t nk = (s1 - s0 + kBK - 1) / kBK;
+  if (nk > 0) load(s0);
+  for (;;) {
+    if (nk > 0) store(0);
     __syncthreads();
-  }
-  float* og = sg.out;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = n0 + wn * WN + nb * 32 + (lane & 31);
-    if (n >= p.N) continue;
+    f32x16 acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = m0 + wm * WM + mb * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-        if (m < p.M) og[(int64_t)m * p.N + n] = acc[mb][nb][j];
-      }
-  }
-  if (do_colsum) {  // the 8 threads of a column unit hold rows 4 kq .. : add in kq order
-    if (!isb) {
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) csr[kq][8 * mu + e] = cs[e];
+        for (int j = 0; j < 16; ++j) acc[mb][nb][j] = 0.f;
+    for (int64_t ks = 0; ks < nk; ++ks) {
+      const int buf = (int)(ks & 1);
+      if (ks + 1 < nk) load(s0 + (ks + 1) * kBK);
+#pragma unroll
+      for (int s = 0; s < kBK / 16; ++s) {
+        U16 a[MB], a2[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          a[mb] = frag_kmaj(ah[buf], wm * WM + mb * 32, s, lane);
+          if constexpr (SA) a2[mb] = frag_kmaj(al[buf], wm * WM + mb * 32, s, lane);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const U16 b = frag_kmaj(bh[buf], wn * WN + nb * 32, s, lane);
+          U16 b2;
+          if constexpr (SB) b2 = frag_kmaj(bl[buf], wn * WN + nb * 32, s, lane);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            Mfma<bf16>::k32(acc[mb][nb], a[mb], b);
+            if constexpr (SA) Mfma<bf16>::k32(acc[mb][nb], a2[mb], b);
+            if constexpr (SB) Mfma<bf16>::k32(acc[mb][nb], a[mb], b2);
+          }
+        }
+      }
+      if (ks + 1 < nk) store(buf ^ 1);
+      __syncthreads();
     }
-    __syncthreads();
-    if (tid < TM && m0 + tid < p.M) {
-      float v = 0.f;
-      for (int i = 0; i < 8; ++i) v += csr[i][tid];
-      sg.colsum[m0 + tid] = v;
+    // This tile's destinations; its column sums go to LDS (every wave is past
+    // the tile's last LDS read) before the next tile's first step, loaded here
+    // ahead of the stores, starts adding to cs.
+    const int om0 = m0, on0 = n0;
+    float* const og = out;
+    float* const ocs = colsum;
+    if (ocs && !isb) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        csr[kq][8 * mu + e] = cs[e];
+        cs[e] = 0.f;
+      }
     }
+    bool more = false;
+    if constexpr (PERSIST) {
+      T += gridDim.x;
+      if (T < tend && tile_at(T)) {
+        more = true;
+        nk = (s1 - s0 + kBK - 1) / kBK;
+        if (nk > 0) load(s0);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = on0 + wn * WN + nb * 32 + (lane & 31);
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int m = om0 + wm * WM + mb * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+          if (m < p.M) og[(int64_t)m * p.N + n] = acc[mb][nb][j];
+        }
+    }
+    if (ocs) {  // the 8 threads of a column unit hold rows 4 kq .. : add in kq order
+      __syncthreads();
+      if (tid < TM && om0 + tid < p.M) {
+        float v = 0.f;
+        for (int i = 0; i < 8; ++i) v += csr[i][tid];
+        ocs[om0 + tid] = v;
+      }
+    }
+    if (!more) break;
   }
 }
 
@@ -1006,6 +1126,60 @@ __global__ __launch_bounds__(256) void pair_grad_kernel(int64_t B, int n, int k,
                   dload[i0 + q], floor_, dc, du);
     row[i0 + q] = dc;
     row[n + i0 + q] = du;
+  }
+}
+
+// The selected pairs of each token (one wave per token), for a gradient pass
+// that took every pair as unselected: c and u from fp32 dot products of the
+// bf16 x row with the expert's gate weight rows (bias added to c), then
+// pair_grad_one with the (k+1)-th threshold and the pair's dH, over cu.
+__global__ __launch_bounds__(256) void kept_pair_grad_kernel(
+    int64_t B, int n, int k, int d, const bf16* __restrict__ x, const bf16* __restrict__ wg,
+    const bf16* __restrict__ wn, const float* __restrict__ bias, const float* __restrict__ eps,
+    const float* __restrict__ thresh, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ dHk, const float* __restrict__ dload, float floor_,
+    float* __restrict__ cu) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= B) return;
+  // lane l holds elements 8 l .. 8 l + 7 of the row (d <= 512, a multiple of 8)
+  const int c0 = 8 * lane;
+  const bool act = c0 < d;
+  float xv[8];
+  {
+    uint4 v = act ? *reinterpret_cast<const uint4*>(x + t * d + c0) : uint4{0u, 0u, 0u, 0u};
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = bf16_bits_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+  }
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[t * k + j];
+    if (e < 0 || e >= n) continue;  // uniform over the wave
+    float c = 0.f, u = 0.f;
+    if (act) {
+      const uint4 a = *reinterpret_cast<const uint4*>(wg + (int64_t)e * d + c0);
+      const uint4 q = *reinterpret_cast<const uint4*>(wn + (int64_t)e * d + c0);
+      const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        c = fmaf(xv[i], bf16_bits_to_f32((wa[i >> 1] >> (16 * (i & 1))) & 0xFFFFu), c);
+        u = fmaf(xv[i], bf16_bits_to_f32((wq[i >> 1] >> (16 * (i & 1))) & 0xFFFFu), u);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      c += __shfl_xor(c, o);
+      u += __shfl_xor(u, o);
+    }
+    if (lane == 0) {
+      if (bias) c += bias[e];
+      float dc, du;
+      pair_grad_one(c, u, eps[t * n + e], true, dHk[t * k + j], thresh + t * 2, dload[e], floor_,
+                    dc, du);
+      float* row = cu + t * 2 * (int64_t)n;
+      row[e] = dc;
+      row[n + e] = du;
+    }
   }
 }
 
@@ -1200,9 +1374,10 @@ hipError_t run_row_gemm(const RowGemm& p0, Dt ta, Dt tw, Dt to, int64_t grid_x, 
 }
 
 // big_ok: 256 x 256 tiles allowed (segments short enough that their number,
-// not one segment's length, sets the work per tile)
+// not one segment's length, sets the work per tile); persist_ok: those tiles
+// walked by one persistent workgroup per compute unit (many short tiles)
 hipError_t run_wgrad(const Wgrad& p, Dt ta, Dt tb, int nseg, hipStream_t s,
-                     bool bf16_cores = false, bool big_ok = true) {
+                     bool bf16_cores = false, bool big_ok = true, bool persist_ok = false) {
   if (nseg <= 0) return hipSuccess;
   if (bf16_cores) {
     const int vec = aligned16(p.a) && aligned16(p.b) && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
@@ -1210,18 +1385,35 @@ hipError_t run_wgrad(const Wgrad& p, Dt ta, Dt tb, int nseg, hipStream_t s,
     // 256 x 256 tiles (eight waves) once both dimensions fill them, else 128 x 128
     const bool big = big_ok && p.M >= 256 && p.N >= 256;
     const int tm = big ? 256 : 128;
-    const dim3 grid((unsigned)(((p.M + tm - 1) / tm) * ((p.N + tm - 1) / tm)), (unsigned)nseg);
+    const int64_t tps = (int64_t)((p.M + tm - 1) / tm) * ((p.N + tm - 1) / tm);
+    dim3 grid((unsigned)tps, (unsigned)nseg);
+    int pseg = 0;
+    if (big && persist_ok) {
+      // one workgroup per compute unit (its LDS allows one), a multiple of 8
+      int cus = 0;
+      const hipError_t e = device_cus(&cus);
+      if (e != hipSuccess) return e;
+      const int64_t want = (tps * nseg + 7) / 8 * 8;
+      grid = dim3((unsigned)std::min<int64_t>(want, std::max(8, cus / 8 * 8)), 1u);
+      pseg = nseg;
+    }
 #define MOE_WT(A, B_)                                                                          \
-  if (big)                                                                                     \
-    hipLaunchKernelGGL((wgrad_tgemm_kernel<A, B_, 256, 8>), grid, dim3(512), 0, s, p, vec);    \
+  if (big && pseg > 0)                                                                         \
+    hipLaunchKernelGGL((wgrad_tgemm_kernel<A, B_, 256, 8, true>), grid, dim3(512), 0, s, p,    \
+                       vec, pseg);                                                             \
+  else if (big)                                                                                \
+    hipLaunchKernelGGL((wgrad_tgemm_kernel<A, B_, 256, 8, false>), grid, dim3(512), 0, s, p,   \
+                       vec, 0);                                                                \
   else                                                                                         \
-    hipLaunchKernelGGL((wgrad_tgemm_kernel<A, B_, 128, 4>), grid, dim3(256), 0, s, p, vec)
+    hipLaunchKernelGGL((wgrad_tgemm_kernel<A, B_, 128, 4, false>), grid, dim3(256), 0, s, p,   \
+                       vec, 0)
+    // (the products that run on bf16 cores have one fp32 and one bf16 operand)
     if (ta == kBF16 && tb == kF32) {
       MOE_WT(bf16, float);
     } else if (ta == kF32 && tb == kBF16) {
       MOE_WT(float, bf16);
     } else {
-      MOE_WT(float, float);
+      return hipErrorInvalidValue;
     }
 #undef MOE_WT
     return hipGetLastError();
@@ -1279,7 +1471,7 @@ static size_t gate_chunk_bytes(int64_t B, int n, int d) {
 
 size_t backward_ws_bytes(int64_t B, int n, int k, int d, int h, Dt act_dt) {
   const int64_t P = B * k;
-  const size_t a = act_dt == kBF16 ? 2 : 4;
+  (void)act_dt;  // every staging buffer is fp32
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const int64_t max_units = gate_max_units(P, n, kT);
   return al((size_t)n * 4) + al((size_t)(n + 1) * 4) + 3 * al((size_t)P * 4)  // route
@@ -1300,7 +1492,6 @@ size_t backward_ws_bytes(int64_t B, int n, int k, int d, int h, Dt act_dt) {
 hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   const int64_t B = b.tokens, P = B * b.k;
   const int n = b.n, k = b.k, d = b.d, h = b.h;
-  const size_t a = b.act_dt == kBF16 ? 2 : 4;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   char* w = static_cast<char*>(ws);
   auto take = [&](size_t bytes) {
@@ -1433,7 +1624,9 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   // long segments (over 256 rows per expert on average) keep 128 x 128 tiles, so that
   // one popular expert's rows are spread over more workgroups
   const bool short_segs = P < 256 * (int64_t)n;
-  if ((e = run_wgrad(wg, b.act_dt, kF32, (int)wmax_chunks, s, b.act_dt == kBF16, short_segs)) != hipSuccess) return e;
+  if ((e = run_wgrad(wg, b.act_dt, kF32, (int)wmax_chunks, s, b.act_dt == kBF16, short_segs,
+                       short_segs)) != hipSuccess)
+    return e;
   if ((e = chunk_reduce(wg)) != hipSuccess) return e;
   // dW1_e = sum dA^T x[token], db1_e = sum dA
   wg = Wgrad{};
@@ -1452,7 +1645,9 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   wg.chunks = wchunks;
   wg.part = wpart;
   wg.pcol = wpcol;
-  if ((e = run_wgrad(wg, kF32, b.act_dt, (int)wmax_chunks, s, b.act_dt == kBF16, short_segs)) != hipSuccess) return e;
+  if ((e = run_wgrad(wg, kF32, b.act_dt, (int)wmax_chunks, s, b.act_dt == kBF16, short_segs,
+                       short_segs)) != hipSuccess)
+    return e;
   if ((e = chunk_reduce(wg)) != hipSuccess) return e;
   // dx per routed row: dA W1
   r = RowGemm{};
@@ -1470,33 +1665,61 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.ldo = d;
   if ((e = run_row_gemm(r, kF32, b.act_dt, kF32, max_units, s, b.act_dt == kBF16)) != hipSuccess) return e;
 
-  // gate: c = x W_g^T + b, u = x W_noise^T into cu, then their gradients in place
+  // gate: the gradients of every (token, expert) pair's clean logit and noise
+  // pre-activation into cu [B][2n]
   const int64_t rt = (B + kT - 1) / kT;
-  r = RowGemm{};
-  r.rows = B;
-  r.a = b.x;
-  r.lda = d;
-  r.w = b.w_gate;
-  r.wt = 1;
-  r.K = d;
-  r.N = n;
-  r.bias = b.gate_bias;  // fp32 whatever the weights' type
-  r.bias_f32 = 1;
-  r.out = cu;
-  r.ldo = 2 * (int64_t)n;
-  if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
-  if (b.train) {
-    r.w = b.w_noise;
-    r.bias = nullptr;
-    r.out = cu + n;
-    if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
-  }
-  if (B > 0) {
-    const int vec = n % 4 == 0 && (reinterpret_cast<uintptr_t>(b.eps) & 15) == 0;
-    hipLaunchKernelGGL(pair_grad_kernel, dim3((unsigned)B, (unsigned)((n + 1023) / 1024)),
-                       dim3(256), 0, s, B, n, k, b.train, b.noise_floor, vec, b.eps, b.thresh,
-                       b.topk_idx, dHk, dload, cu);
+  GateLaunch gl{};
+  gl.x = b.x;
+  gl.w_gate = b.w_gate;
+  gl.w_noise = b.w_noise;
+  gl.bias = b.gate_bias;
+  gl.eps = b.eps;
+  gl.tokens = B;
+  gl.d = d;
+  gl.n = n;
+  gl.k = k;
+  gl.x_dt = b.act_dt;
+  gl.w_dt = b.gate_dt;
+  gl.train = b.train;
+  gl.noise_floor = b.noise_floor;
+  if (B > 0 && gate_pair_grads_supported(gl)) {
+    // the gate's matrix-core pass takes every pair as unselected, then the
+    // selected pairs are rewritten from their own dot products
+    if ((e = launch_gate_pair_grads(gl, b.thresh, dload, cu, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(kept_pair_grad_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, s, B, n,
+                       k, d, static_cast<const bf16*>(b.x), static_cast<const bf16*>(b.w_gate),
+                       static_cast<const bf16*>(b.w_noise), b.gate_bias, b.eps, b.thresh,
+                       b.topk_idx, dHk, dload, b.noise_floor, cu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    // c = x W_g^T + b, u = x W_noise^T into cu, then their gradients in place
+    // (without noise only the selected pairs' dH, which needs neither)
+    r = RowGemm{};
+    r.rows = B;
+    r.a = b.x;
+    r.lda = d;
+    r.w = b.w_gate;
+    r.wt = 1;
+    r.K = d;
+    r.N = n;
+    r.bias = b.gate_bias;  // fp32 whatever the weights' type
+    r.bias_f32 = 1;
+    r.out = cu;
+    r.ldo = 2 * (int64_t)n;
+    if (b.train) {
+      if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
+      r.w = b.w_noise;
+      r.bias = nullptr;
+      r.out = cu + n;
+      if ((e = run_row_gemm(r, b.act_dt, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
+    }
+    if (B > 0) {
+      const int vec = n % 4 == 0 && (reinterpret_cast<uintptr_t>(b.eps) & 15) == 0;
+      hipLaunchKernelGGL(pair_grad_kernel, dim3((unsigned)B, (unsigned)((n + 1023) / 1024)),
+                         dim3(256), 0, s, B, n, k, b.train, b.noise_floor, vec, b.eps, b.thresh,
+                         b.topk_idx, dHk, dload, cu);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   // dW_g = dc^T x, db_g = sum dc; dW_noise = du^T x: one product over the [B][2n]
   // logit gradients (n columns without noise), the B rows in S chunks whose

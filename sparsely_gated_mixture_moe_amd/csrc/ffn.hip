@@ -579,22 +579,6 @@ __global__ __launch_bounds__(256) void ffn_split_reduce(FfnParams p, int hsplit)
   }
 }
 
-// Compute units of the current device (cached per device).
-hipError_t device_cus(int* cus) {
-  static int cache[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cache[dev] == 0) {
-    int v = 0;
-    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    cache[dev] = v > 0 ? v : 1;
-  }
-  *cus = cache[dev];
-  return hipSuccess;
-}
 
 template <typename T, int D>
 hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* offsets, int n,
@@ -644,6 +628,23 @@ int bm_for(int d) {
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* cus) {
+  static int cache[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cache[dev] == 0) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cache[dev] = v > 0 ? v : 1;
+  }
+  *cus = cache[dev];
+  return hipSuccess;
+}
 
 int ffn_rows_per_block(int d, Dt dt) { return dt == kBF16 ? bm_for<bf16>(d) : bm_for<float>(d); }
 

@@ -534,6 +534,23 @@ hipError_t launch_load_grouped(const GateLaunch& g, int groups, const int32_t* u
   return hipGetLastError();
 }
 
+bool gate_pair_grads_supported(const GateLaunch& g) {
+  return g.train && !g.units && gate_uses_g32(g);
+}
+
+hipError_t launch_gate_pair_grads(const GateLaunch& g, const float* thresh, const float* dload,
+                                  float* dcu, hipStream_t s) {
+  if (g.tokens == 0) return hipSuccess;
+  if (!gate_pair_grads_supported(g)) return hipErrorInvalidValue;
+  GateLaunch gs = g;
+  gs.ranges = gate_ranges(g);
+  GateParams p = make_params(gs);
+  p.sel_thr = thresh;
+  p.dload = dload;
+  p.dcu = dcu;
+  return gate_dispatch(gs, p, true, s);
+}
+
 hipError_t launch_load(const GateLaunch& g, const float* thresh, const int32_t* offsets,
                        const int32_t* perm_token, float* partial, float* corr, float* load,
                        hipStream_t s) {

@@ -34,6 +34,14 @@
 // moves, each step halving the values a lane holds), then over the block's
 // waves, in a fixed order (the selected pairs are corrected to the (k+1)-th
 // threshold separately).
+// The gradient pass (BWD) runs pass 2's products and, per pair, the
+// derivatives of its Load term P = Phi((clean - v_k) / sigma) times d loss /
+// d Load_i: with phi the normal density and z = (clean - v_k) / sigma,
+// d/d clean = phi(z) / sigma and d/d u = -phi(z) z / sigma Softplus'(u),
+// Softplus' the logistic function. They go to global memory one chunk late
+// (so that the stores have a whole chunk's work to complete before the
+// chunk's barrier, which waits for every memory operation in flight); the
+// selected pairs are rewritten separately.
 #pragma once
 
 #include "gate_impl.h"
@@ -62,8 +70,10 @@ __device__ const float kZeroBias[2 * kG32Chunk] = {};
 constexpr int kG32PhiValu = 30;
 constexpr int kG32HValu = 12;
 
-template <int D, int L, bool PASS2, bool SMX = false, bool SCORES = false, bool CL = false>
+template <int D, int L, bool PASS2, bool SMX = false, bool SCORES = false, bool CL = false,
+          bool BWD = false>
 __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
+  static_assert(!BWD || PASS2, "the gradient pass is a variant of the Load pass");
   RowTile tile;
   if (!resolve_tile<kG32Rows, bf16, D>(p, tile)) return;
   constexpr int UE = 8;          // bf16 per 16-byte unit
@@ -87,9 +97,10 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   __shared__ float ebuf[PASS2 || CL ? 1 : NE][PASS2 || CL ? 1 : ESLOT];
   __shared__ float thrbuf[PASS2 ? kG32Rows : 1];  // pass 2: each row's k-th logit
   // pass 2: each wave's copy of a chunk's 16 biases, double-buffered by chunk parity
-  // (CL: the same for a chunk's 32 biases)
-  __shared__ __attribute__((aligned(16))) float bbuf[PASS2 || CL ? 2 : 1][PASS2 || CL ? kG32Waves * EX : 1];
-  __shared__ float red[PASS2 ? 2 : 1][kG32Waves][EC];
+  // (CL: the same for a chunk's 32 biases; BWD: the 16 biases, then the 16 d loss / d Load)
+  constexpr int BW = BWD ? 2 * EX : EX;
+  __shared__ __attribute__((aligned(16))) float bbuf[PASS2 || CL ? 2 : 1][PASS2 || CL ? kG32Waves * BW : 1];
+  __shared__ float red[PASS2 && !BWD ? 2 : 1][kG32Waves][EC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -176,7 +187,15 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // that no compiler-inserted wait on the memory counter stalls the epilogue
   // behind the weight copies in flight.
   auto dma_bias = [&](int c, int slot) {
-    if (lane < EX / 4) copy16_to_lds(bias_src + c * bias_step + 4 * lane, &bbuf[slot][wave * EX]);
+    if constexpr (BWD) {
+      // lanes 0-3 the biases, lanes 4-7 d loss / d Load of the chunk's experts
+      if (lane < 2 * EX / 4)
+        copy16_to_lds(lane < EX / 4 ? bias_src + c * bias_step + 4 * lane
+                                    : p.dload + (int64_t)(cr.c0 + c) * EX + 4 * (lane - EX / 4),
+                      &bbuf[slot][wave * BW]);
+    } else {
+      if (lane < EX / 4) copy16_to_lds(bias_src + c * bias_step + 4 * lane, &bbuf[slot][wave * EX]);
+    }
   };
   // One chunk's products: 32 x 32 tile of (rows, clean|noise columns) over
   // the K-blocks. Fragments are read four ahead of their matrix product; the
@@ -262,6 +281,21 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // chunk's products) and fills accs[P ^ 1] (the next chunk's); the same for
   // pass 2's bias slots.
   f32x16 accs[2];
+  // BWD: the last chunk's gradients of this lane's 8 pairs, written one chunk
+  // late (dc then du); the lane's batch row (-1 past the tile's end)
+  float gdc[BWD ? 8 : 1], gdu[BWD ? 8 : 1];
+  const int64_t grow = BWD ? tile_iorow(p, tile, wrow0 + l32) : -1;
+  auto store_grads = [&](int c) __attribute__((always_inline)) {
+    if constexpr (BWD) {
+      if (grow >= 0) {
+        float* dst = p.dcu + grow * 2 * (int64_t)n + (int64_t)(cr.c0 + c) * EC + 4 * hi;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{gdc[0], gdc[1], gdc[2], gdc[3]};
+        *reinterpret_cast<f32x4*>(dst + 8) = f32x4{gdc[4], gdc[5], gdc[6], gdc[7]};
+        *reinterpret_cast<f32x4*>(dst + n) = f32x4{gdu[0], gdu[1], gdu[2], gdu[3]};
+        *reinterpret_cast<f32x4*>(dst + n + 8) = f32x4{gdu[4], gdu[5], gdu[6], gdu[7]};
+      }
+    }
+  };
   dma(0, wbuf0);
   if (nchunks > 1) dma(1, wbuf1);
   if constexpr (!PASS2 && !CL) {
@@ -278,6 +312,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // difference (threshold (k+1)-th) is added by a separate kernel.
   float thrk = 0.f;
   if constexpr (PASS2) thrk = thrbuf[wave * 32 + l32];
+  const bool thr_fin = !isinf(thrk);
 
   // One pass per chunk; P = c & 1 is a compile-time constant (the loop below
   // is unrolled by two) so each pass names its buffers statically.
@@ -297,6 +332,9 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
     }
     if (c + 2 < nchunks) dma(c + 2, wfill);
     asm volatile("" ::: "memory");
+    if constexpr (BWD) {
+      if (c > 0) store_grads(c - 1);
+    }
     if constexpr (!PASS2 && !CL) {
       if (c + NE - 1 < nchunks) dma_eps(c + NE - 1, (c + NE - 1) % NE);
     }
@@ -308,9 +346,14 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       // This lane's 8 biases and the first reads ahead are issued before the
       // woven region below: the scheduler keeps the weave's pattern only
       // when that region starts with the products and reads of K-blocks.
-      const float* br = &bbuf[P][wave * EC + 4 * hi];
+      const float* br = &bbuf[P][wave * BW + 4 * hi];
       const f32x4 b0 = *reinterpret_cast<const f32x4*>(br);
       const f32x4 b1 = *reinterpret_cast<const f32x4*>(br + 8);
+      f32x4 dl0{}, dl1{};
+      if constexpr (BWD) {
+        dl0 = *reinterpret_cast<const f32x4*>(br + EC);
+        dl1 = *reinterpret_cast<const f32x4*>(br + EC + 8);
+      }
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       typedef const __attribute__((address_space(3))) u32x4* LdsPtr;
       uint32_t base = (uint32_t)(uintptr_t)(wnext + lane);
@@ -340,8 +383,21 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         // pairs values i and i + 4, so it can start inside the weave
         const int e = (i >> 1) + 4 * (i & 1);
         const float clean = acc[e] + (e < 4 ? b0[e] : b1[e - 4]);
-        const float sigma = softplus_f(acc[8 + e]) + p.floor;
-        pv[e] = phi_f((clean - thrk) * rcp_f(sigma));
+        if constexpr (BWD) {
+          const float u = acc[8 + e];
+          const float t = exp_native(-fabsf(u));
+          const float sigma = fmaf(u + fabsf(u), 0.5f, log1p_small(t)) + p.floor;
+          const float rs = rcp_f(sigma);
+          const float z = (clean - thrk) * rs;
+          const float dl = e < 4 ? dl0[e] : dl1[e - 4];
+          // d loss / d clean = dl phi(z) / sigma; no threshold: no Load term
+          const float a = thr_fin ? dl * exp_native(-0.5f * z * z) * 0.3989422804014327f * rs : 0.f;
+          gdc[e] = a;
+          gdu[e] = thr_fin ? -a * z * (u >= 0.f ? 1.f : t) * rcp_f(1.f + t) : 0.f;
+        } else {
+          const float sigma = softplus_f(acc[8 + e]) + p.floor;
+          pv[e] = phi_f((clean - thrk) * rcp_f(sigma));
+        }
       }
       // reads ahead, then (product, read, vector work) triples
       constexpr int V = (kG32PhiValu + MPE - 1) / MPE;
@@ -353,6 +409,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!BWD) {
       // Column sums over the wave's 32 tokens (lanes of equal hi). Lane l
       // holds value j for expert 8 (j / 4) + 4 hi + j % 4. Each step pairs
       // lanes that hold the same values, keeps half of them and adds the
@@ -387,6 +444,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       if ((lane & 3) == 0) {
         const int j = (lane >> 2) & 7;
         red[P][wave][8 * (j >> 2) + 4 * hi + (j & 3)] = s1;
+      }
       }
     } else {
       // Selection pass: this chunk's noise draws and biases are read first,
@@ -496,7 +554,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 
-    if constexpr (PASS2) {
+    if constexpr (PASS2 && !BWD) {
       if (tid < EC) {
         float s = 0.f;
 #pragma unroll
@@ -508,6 +566,9 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   for (int c = 0; c < nchunks; c += 2) {
     chunk_pass(c, IntConst<0>{});
     if (c + 1 < nchunks) chunk_pass(c + 1, IntConst<1>{});
+  }
+  if constexpr (BWD) {
+    if (nchunks > 0) store_grads(nchunks - 1);
   }
   if constexpr (!PASS2 && !SCORES) {
     // The two halves of a token's experts (lanes l and l ^ 32) merge, then

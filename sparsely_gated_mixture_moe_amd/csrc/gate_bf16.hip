@@ -25,6 +25,8 @@ hipError_t gate_dispatch_bf16(const GateLaunch& g, const gate_detail::GateParams
         hipLaunchKernelGGL((gate32_kernel<DD, 9, false, false, false, true>), grid, block, 0, s, p); \
     } else if (p.scores) {                                                                 \
       hipLaunchKernelGGL((gate32_kernel<DD, 5, false, false, true>), grid, block, 0, s, p);  \
+    } else if (pass2 && p.dcu) {                                                           \
+      hipLaunchKernelGGL((gate32_kernel<DD, 5, true, false, false, false, true>), grid, block, 0, s, p); \
     } else if (pass2) {                                                                    \
       if (k4) hipLaunchKernelGGL((gate32_kernel<DD, 5, true>), grid, block, 0, s, p);      \
       else hipLaunchKernelGGL((gate32_kernel<DD, 9, true>), grid, block, 0, s, p);         \

@@ -49,6 +49,12 @@ struct GateParams {
   float* thresh;
   const float* sel_thr;  // pass 2: (k-th, (k+1)-th) logit of each row
   float* partial;
+  // Gradient pass (the Load pass's products, another epilogue; 32x32 kernel
+  // only): dload [n] is d loss / d Load; every pair's gradients with respect
+  // to its clean logit and noise pre-activation, taken as unselected, go to
+  // dcu [row][e] and dcu [row][n + e]. Null otherwise.
+  const float* dload;
+  float* dcu;
   // Selection of one expert range (gridDim.y ranges): each row's best L
   // (value, expert) go to [(row * gridDim.y + blockIdx.y) * L + j] instead of
   // the outputs above; null when every workgroup sweeps all experts.

@@ -48,6 +48,15 @@ struct GateLaunch {
   int gate_order = 0;
 };
 
+// The gradient pass of the gate (flat bf16 gate in training mode, the 32x32
+// kernel): for every (token, expert) pair, taken as unselected, d loss / d
+// clean logit and d loss / d noise pre-activation through the Load term
+// (threshold thresh [row][0], the k-th logit; dload [n] = d loss / d Load)
+// into dcu [B][2n] (clean at column e, noise at n + e).
+bool gate_pair_grads_supported(const GateLaunch& g);
+hipError_t launch_gate_pair_grads(const GateLaunch& g, const float* thresh, const float* dload,
+                                  float* dcu, hipStream_t s);
+
 // Batchwise gating's scores: H of every (token, expert) pair, written
 // expert-major to scores [n][sld], sld >= B (same arithmetic as launch_gate's H).
 hipError_t launch_scores(const GateLaunch& g, float* scores, int64_t sld, hipStream_t s);
@@ -207,6 +216,9 @@ struct BackwardLaunch {
 };
 size_t backward_ws_bytes(int64_t tokens, int n, int k, int d, int h, Dt act_dt);
 hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s);
+
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* cus);
 
 // Load as the hard count (train = 0) and the CV^2 losses.
 hipError_t launch_counts_to_load(const int32_t* counts, int n, float* load, hipStream_t s);
