@@ -73,6 +73,10 @@ struct RowGemm {
   int64_t lda;
   const int32_t* gather;
   const float* scale;
+  // a_blk > 0 (tiled bf16-core products only): a is in blocks of 16 K
+  // columns, a_blk rows each, 32 floats a row: element (p, k) at
+  // a + ((k / 16) * a_blk + row(p)) * 32 + k % 16 (lda unused)
+  int64_t a_blk;
   // W of segment g at w + g * w_stride: wt = 1: [N][K] row-major (out = a W^T);
   // wt = 0: [K][N] row-major (out = a W)
   const void* w;
@@ -222,9 +226,12 @@ struct Wgrad {
   // `rows` rows)
   const int32_t* seg_off;
   int64_t rows;
-  // a: [rows][M], b: [rows][N], each row optionally gathered and scaled
+  // a: [rows][M], b: [rows][N], each row optionally gathered and scaled;
+  // a_blk > 0 (tiled kernel only): a is in blocks of 32 M columns, a_blk rows
+  // each: element (row, m) at a + ((m / 32) * a_blk + row) * 32 + m % 32
   const void* a;
   int64_t lda;
+  int64_t a_blk;
   const int32_t* a_gather;
   const float* a_scale;
   const void* b;
@@ -368,6 +375,10 @@ __global__ __launch_bounds__(256) void wgrad_kernel(Wgrad p) {
 // ---------------------------------------------------------------------------
 
 constexpr int kBK = 32;  // K per step of the tiled bf16 products
+// rows per workgroup (and per unit) of the tiled row products: 64, two
+// workgroups per compute unit (128-row workgroups, one per compute unit, read
+// each weight tile half as often but hide less latency: slower)
+constexpr int kTR = 64;
 
 __device__ __forceinline__ uint32_t split_pair(float a, float b, uint32_t& lo) {
   const uint32_t ha = f32_to_bf16_bits(a), hb = f32_to_bf16_bits(b);
@@ -498,11 +509,14 @@ struct StageT<float> {
   }
 };
 
-template <typename TA, typename TW, bool WT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// Row products on bf16 cores: TM = 32 MR rows x 256 columns a workgroup, 2 MR
+// waves in an MR x 2 grid (32 rows x 128 columns each). The first 256 threads
+// stage the weights, all threads the rows.
+template <typename TA, typename TW, bool WT, int MR>
+__global__ __launch_bounds__(128 * MR) __attribute__((amdgpu_waves_per_eu(2)))
 void row_tgemm_kernel(RowGemm p, int vec) {
   constexpr bool SA = sizeof(TA) == 4, SW = sizeof(TW) == 4;
-  constexpr int TM = 64, TN = 256;
+  constexpr int TM = 32 * MR, TN = 256;
   constexpr int ABYTES = TM * 64, BBYTES = TN * 64;  // one bf16 tile of each operand
   __shared__ __attribute__((aligned(16))) uint8_t ah[2][ABYTES];
   __shared__ __attribute__((aligned(16))) uint8_t al[SA ? 2 : 1][SA ? ABYTES : 16];
@@ -522,8 +536,10 @@ void row_tgemm_kernel(RowGemm p, int vec) {
     if (r0 >= rend) return;
   }
   const int n0 = blockIdx.y * TN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const bool wstage = wave < 4;  // whole waves: the first 256 threads stage the weights
   const bool vv = vec != 0;
   const char* wseg = reinterpret_cast<const char*>(p.w) + (int64_t)g * p.w_stride * sizeof(TW);
   // A: row tid / 4 of the unit, K unit tid % 4
@@ -535,34 +551,40 @@ void row_tgemm_kernel(RowGemm p, int vec) {
   StageT<TW> st;     // [K][N] weights: K rows k0 + 4 (tid / 32) .. + 3, columns 8 (tid % 32) .. + 7
   auto load = [&](int k0) __attribute__((always_inline)) {
     const int ka = k0 + 8 * au;
-    sa.load(p.a, arow * p.lda + ka, arow_ok ? std::min(8, std::max(0, p.K - ka)) : 0, vv);
-    if constexpr (WT) {
+    const int64_t aoff = p.a_blk > 0 ? ((int64_t)(ka >> 4) * p.a_blk + arow) * 32 + (ka & 15)
+                                     : arow * p.lda + ka;
+    sa.load(p.a, aoff, arow_ok ? std::min(8, std::max(0, p.K - ka)) : 0, vv);
+    if (wstage) {
+      if constexpr (WT) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {  // row n0 + tid / 4 + 64 i, K unit tid % 4
-        const int n = n0 + (tid >> 2) + 64 * i, kb = k0 + 8 * (tid & 3);
-        sb[i].load(wseg, (int64_t)n * p.K + kb, n < p.N ? std::min(8, std::max(0, p.K - kb)) : 0, vv);
+        for (int i = 0; i < 4; ++i) {  // row n0 + tid / 4 + 64 i, K unit tid % 4
+          const int n = n0 + (tid >> 2) + 64 * i, kb = k0 + 8 * (tid & 3);
+          sb[i].load(wseg, (int64_t)n * p.K + kb, n < p.N ? std::min(8, std::max(0, p.K - kb)) : 0, vv);
+        }
+      } else {
+        const int kr = k0 + 4 * (tid >> 5), nb = n0 + 8 * (tid & 31);
+        st.load(wseg, (int64_t)kr * p.N + nb, p.N, std::max(0, std::min(4, p.K - kr)),
+                std::min(8, std::max(0, p.N - nb)), vv);
       }
-    } else {
-      const int kr = k0 + 4 * (tid >> 5), nb = n0 + 8 * (tid & 31);
-      st.load(wseg, (int64_t)kr * p.N + nb, p.N, std::max(0, std::min(4, p.K - kr)),
-              std::min(8, std::max(0, p.N - nb)), vv);
     }
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
     const int pa = kmaj_pos(ar, au);
     sa.store(ah[buf] + pa, al[SA ? buf : 0] + (SA ? pa : 0), 1.f);
-    if constexpr (WT) {
+    if (wstage) {
+      if constexpr (WT) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pb = kmaj_pos((tid >> 2) + 64 * i, tid & 3);
-        sb[i].store(bh[buf] + pb, bl[SW ? buf : 0] + (SW ? pb : 0), 1.f);
-      }
-    } else {
-      const int kq = tid >> 5, nu = tid & 31;
+        for (int i = 0; i < 4; ++i) {
+          const int pb = kmaj_pos((tid >> 2) + 64 * i, tid & 3);
+          sb[i].store(bh[buf] + pb, bl[SW ? buf : 0] + (SW ? pb : 0), 1.f);
+        }
+      } else {
+        const int kq = tid >> 5, nu = tid & 31;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int pb = kmaj_pos(8 * nu + e, kq >> 1) + 8 * (kq & 1);
-        st.store(bh[buf], bl[SW ? buf : 0], e, pb);
+        for (int e = 0; e < 8; ++e) {
+          const int pb = kmaj_pos(8 * nu + e, kq >> 1) + 8 * (kq & 1);
+          st.store(bh[buf], bl[SW ? buf : 0], e, pb);
+        }
       }
     }
   };
@@ -748,8 +770,8 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec, 
   // the store. A wave stages A or B only, so every branch here is uniform.
   float rfa[4], rfb[4];
   int on = 0;
-  auto load_rows = [&](const auto* src, int64_t ld, const int32_t* gat, int64_t r, auto& st)
-      __attribute__((always_inline)) {
+  auto load_rows = [&](const auto* src, int64_t ld, int64_t blk, const int32_t* gat, int64_t r,
+                       auto& st) __attribute__((always_inline)) {
     const int64_t rb = r + 4 * kq;
     const int krows = (int)std::max<int64_t>(0, std::min<int64_t>(4, s1 - rb));
     const int c0 = (isb ? n0 : m0) + 8 * mu;
@@ -776,7 +798,8 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec, 
       for (int j = 0; j < 4; ++j) {
         const bool ok = j < krows && nvalid == 8;
         on |= ok ? (1 << j) : 0;
-        const int64_t off = ok ? row[j] * ld + c0 : 0;
+        const int64_t off = !ok ? 0 : blk > 0 ? ((int64_t)(c0 >> 5) * blk + row[j]) * 32 + (c0 & 31)
+                                             : row[j] * ld + c0;
         if constexpr (sizeof(*src) == 4) {
           const float4* q = reinterpret_cast<const float4*>(src + off);
           const float4 x0 = q[0], x1 = q[1];
@@ -792,14 +815,16 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int valid = j < krows ? nvalid : 0;
-        if constexpr (sizeof(*src) == 4) load8(src + row[j] * ld + c0, valid, false, st.f[j]);
-        else load8(src + row[j] * ld + c0, valid, false, st.w[j]);
+        const int64_t off = blk > 0 ? ((int64_t)(c0 >> 5) * blk + row[j]) * 32 + (c0 & 31)
+                                    : row[j] * ld + c0;
+        if constexpr (sizeof(*src) == 4) load8(src + off, valid, false, st.f[j]);
+        else load8(src + off, valid, false, st.w[j]);
       }
     }
   };
   auto load = [&](int64_t r) __attribute__((always_inline)) {
-    if (!isb) load_rows(reinterpret_cast<const TA*>(p.a), p.lda, p.a_gather, r, sa);
-    else load_rows(reinterpret_cast<const TB*>(p.b), p.ldb, p.b_gather, r, sb);
+    if (!isb) load_rows(reinterpret_cast<const TA*>(p.a), p.lda, p.a_blk, p.a_gather, r, sa);
+    else load_rows(reinterpret_cast<const TB*>(p.b), p.ldb, (int64_t)0, p.b_gather, r, sb);
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
     // rows without data become zeros (a select: whatever they read stays out)
@@ -1132,7 +1157,9 @@ __global__ __launch_bounds__(256) void pair_grad_kernel(int64_t B, int n, int k,
 // The selected pairs of each token (one wave per token), for a gradient pass
 // that took every pair as unselected: c and u from fp32 dot products of the
 // bf16 x row with the expert's gate weight rows (bias added to c), then
-// pair_grad_one with the (k+1)-th threshold and the pair's dH, over cu.
+// pair_grad_one with the (k+1)-th threshold and the pair's dH, over cu in the
+// gradient pass's blocked layout (row t of expert block q = e / 16 at
+// cu + (q B + t) 32: the 16 clean-logit gradients, then the 16 noise ones).
 __global__ __launch_bounds__(256) void kept_pair_grad_kernel(
     int64_t B, int n, int k, int d, const bf16* __restrict__ x, const bf16* __restrict__ wg,
     const bf16* __restrict__ wn, const float* __restrict__ bias, const float* __restrict__ eps,
@@ -1176,9 +1203,9 @@ __global__ __launch_bounds__(256) void kept_pair_grad_kernel(
       float dc, du;
       pair_grad_one(c, u, eps[t * n + e], true, dHk[t * k + j], thresh + t * 2, dload[e], floor_,
                     dc, du);
-      float* row = cu + t * 2 * (int64_t)n;
-      row[e] = dc;
-      row[n + e] = du;
+      float* blk = cu + ((int64_t)(e >> 4) * B + t) * 32 + (e & 15);
+      blk[0] = dc;
+      blk[16] = du;
     }
   }
 }
@@ -1211,21 +1238,28 @@ __global__ __launch_bounds__(64) void chunk_offsets_kernel(int32_t* __restrict__
 // dW_g (rows < n of the [M][d] partials) and dW_noise (rows n .. 2n - 1), and
 // the gate bias's gradient from the partial column sums: the S chunks' partial
 // sums added in chunk order.
+// blk: the product's rows are in the blocked order of the gradient pass
+// (row 32 q + i: the clean logit of expert 16 q + i for i < 16, the noise
+// pre-activation of expert 16 q + i - 16 otherwise); else rows 0 .. n - 1 are
+// the clean logits and n .. M - 1 the noise pre-activations.
 __global__ __launch_bounds__(256) void gate_wgrad_reduce_kernel(
     const float* __restrict__ part, const float* __restrict__ pcol, int S, int n, int M, int d,
-    float* __restrict__ dwg, float* __restrict__ dwn, float* __restrict__ dgb) {
+    int blk, float* __restrict__ dwg, float* __restrict__ dwn, float* __restrict__ dgb) {
   const int64_t md = (int64_t)M * d;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < md) {
     float v = 0.f;
     for (int c = 0; c < S; ++c) v += part[c * md + i];
-    if (i < (int64_t)n * d) dwg[i] = v;
-    else dwn[i - (int64_t)n * d] = v;
+    const int m = (int)(i / d), col = (int)(i - (int64_t)m * d);
+    const bool noise = blk ? (m & 31) >= 16 : m >= n;
+    const int e = blk ? 16 * (m >> 5) + (m & 15) : (noise ? m - n : m);
+    (noise ? dwn : dwg)[(int64_t)e * d + col] = v;
   } else if (i < md + n && dgb) {
-    const int m = (int)(i - md);
+    const int e = (int)(i - md);
+    const int m = blk ? 32 * (e >> 4) + (e & 15) : e;
     float v = 0.f;
     for (int c = 0; c < S; ++c) v += pcol[(int64_t)c * M + m];
-    dgb[m] = v;
+    dgb[e] = v;
   }
 }
 
@@ -1337,15 +1371,18 @@ hipError_t run_row_gemm(const RowGemm& p0, Dt ta, Dt tw, Dt to, int64_t grid_x, 
   if (grid_x <= 0) return hipSuccess;
   RowGemm p = p0;
   const bool tiled = bf16_cores && to == kF32;
+  if (p.a_blk > 0 && (!tiled || p.gather || p.K % 16 != 0)) return hipErrorInvalidValue;
   p.rd_n = tiled ? (p.N + 255) / 256 : (p.N + kT - 1) / kT;  // column tiles: the row dots' stride
   if (tiled) {
     // 16-byte operand loads when every unit of 8 is in range and aligned
     const size_t wsz = tw == kBF16 ? 2 : 4;
     const int vec = aligned16(p.a) && aligned16(p.w) && p.lda % 8 == 0 && p.K % 8 == 0 &&
                     p.N % 8 == 0 && (p.w_stride * wsz) % 16 == 0;
-    const dim3 grid((unsigned)grid_x, (unsigned)((p.N + 255) / 256)), block(256);
+    // kTR rows a workgroup; without units the grid follows from the rows
+    if (!p.units) grid_x = (p.rows + kTR - 1) / kTR;
+    const dim3 grid((unsigned)grid_x, (unsigned)((p.N + 255) / 256)), block(4 * kTR);
 #define MOE_RT(A, W, WT) \
-  hipLaunchKernelGGL((row_tgemm_kernel<A, W, WT>), grid, block, 0, s, p, vec)
+  hipLaunchKernelGGL((row_tgemm_kernel<A, W, WT, kTR / 32>), grid, block, 0, s, p, vec)
     const bool a32 = ta == kF32, w32 = tw == kF32;
     if (p.wt) {
       if (!a32 && !w32) MOE_RT(bf16, bf16, true);
@@ -1379,6 +1416,7 @@ hipError_t run_row_gemm(const RowGemm& p0, Dt ta, Dt tw, Dt to, int64_t grid_x, 
 hipError_t run_wgrad(const Wgrad& p, Dt ta, Dt tb, int nseg, hipStream_t s,
                      bool bf16_cores = false, bool big_ok = true, bool persist_ok = false) {
   if (nseg <= 0) return hipSuccess;
+  if (p.a_blk > 0 && (!bf16_cores || p.a_gather || p.M % 32 != 0)) return hipErrorInvalidValue;
   if (bf16_cores) {
     const int vec = aligned16(p.a) && aligned16(p.b) && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
                     p.M % 8 == 0 && p.N % 8 == 0;
@@ -1505,8 +1543,11 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   float* perm_gate = reinterpret_cast<float*>(take((size_t)P * 4));
   int32_t* slot_pos = reinterpret_cast<int32_t*>(take((size_t)P * 4));
   int32_t* blockcnt = reinterpret_cast<int32_t*>(take((size_t)n * route_blocks(B) * 4));
-  const int64_t max_units = gate_max_units(P, n, kT);
-  int32_t* units = reinterpret_cast<int32_t*>(take((size_t)(1 + 2 * max_units) * 4));
+  // units of the row products: kTR rows on bf16 cores, kT otherwise (the
+  // workspace holds the larger count, kT's)
+  const int urows = b.act_dt == kBF16 ? kTR : kT;
+  const int64_t max_units = gate_max_units(P, n, urows);
+  int32_t* units = reinterpret_cast<int32_t*>(take((size_t)(1 + 2 * gate_max_units(P, n, kT)) * 4));
   int32_t* unit_start = reinterpret_cast<int32_t*>(take((size_t)(n + 1) * 4));
   float* dimp = reinterpret_cast<float*>(take((size_t)n * 4));
   float* dload = reinterpret_cast<float*>(take((size_t)n * 4));
@@ -1529,11 +1570,11 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   float* wpcol = reinterpret_cast<float*>(take((size_t)wg_max_slots(P, wch) * std::max(h, d) * 4));
   hipError_t e;
 
-  // routing of the forward's selection, and the 64-row units of its segments
+  // routing of the forward's selection, and the units of its segments
   e = launch_route(B, k, n, b.topk_idx, b.topk_gate, blockcnt, counts, offsets, perm_token,
                    perm_gate, slot_pos, nullptr, s);
   if (e != hipSuccess) return e;
-  e = launch_group_plan(offsets, n, kT, units, unit_start, s);
+  e = launch_group_plan(offsets, n, urows, units, unit_start, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(cv2_grad_kernel, dim3(1), dim3(1024), 0, s, b.importance, b.load, n,
                      b.aux_scale * b.w_importance, b.aux_scale * b.w_load, b.train, dimp, dload);
@@ -1682,7 +1723,9 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   gl.w_dt = b.gate_dt;
   gl.train = b.train;
   gl.noise_floor = b.noise_floor;
-  if (B > 0 && gate_pair_grads_supported(gl)) {
+  // fused: cu holds the gradient pass's blocked layout instead of [B][2n]
+  const bool fused = B > 0 && gate_pair_grads_supported(gl);
+  if (fused) {
     // the gate's matrix-core pass takes every pair as unselected, then the
     // selected pairs are rewritten from their own dot products
     if ((e = launch_gate_pair_grads(gl, b.thresh, dload, cu, s)) != hipSuccess) return e;
@@ -1732,6 +1775,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   wg.rows = B;
   wg.a = cu;
   wg.lda = 2 * (int64_t)n;
+  wg.a_blk = fused ? B : 0;
   wg.b = b.x;
   wg.ldb = d;
   wg.M = gm;
@@ -1743,7 +1787,8 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   const bool gate_big = ((gm + 255) / 256) * (int64_t)((d + 255) / 256) * S >= 512;
   if ((e = run_wgrad(wg, kF32, b.act_dt, S, s, b.act_dt == kBF16, gate_big)) != hipSuccess) return e;
   hipLaunchKernelGGL(gate_wgrad_reduce_kernel, dim3(blocks_for((int64_t)gm * d + n)), dim3(256),
-                     0, s, gpart, gcol, S, n, gm, d, b.dw_gate, b.dw_noise, b.dgate_bias);
+                     0, s, gpart, gcol, S, n, gm, d, fused ? 1 : 0, b.dw_gate, b.dw_noise,
+                     b.dgate_bias);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!b.train) {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks_for((int64_t)n * d)), dim3(256), 0, s,
@@ -1755,6 +1800,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.rows = B;
   r.a = cu;
   r.lda = 2 * (int64_t)n;
+  r.a_blk = fused ? B : 0;
   r.w = b.w_gate;
   r.wt = 0;
   r.K = n;
@@ -1763,7 +1809,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
   r.ldo = d;
   if ((e = run_row_gemm(r, kF32, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
   if (b.train) {
-    r.a = cu + n;
+    r.a = fused ? cu + 16 : cu + n;
     r.w = b.w_noise;
     r.accumulate = 1;
     if ((e = run_row_gemm(r, kF32, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;

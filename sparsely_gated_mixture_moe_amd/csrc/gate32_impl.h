@@ -288,11 +288,13 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   auto store_grads = [&](int c) __attribute__((always_inline)) {
     if constexpr (BWD) {
       if (grow >= 0) {
-        float* dst = p.dcu + grow * 2 * (int64_t)n + (int64_t)(cr.c0 + c) * EC + 4 * hi;
+        // the chunk's block: row grow's 16 clean-logit gradients, then its 16
+        // noise ones; a wave's four stores fill 32 consecutive 128-byte rows
+        float* dst = p.dcu + ((int64_t)(cr.c0 + c) * p.B + grow) * 32 + 4 * hi;
         *reinterpret_cast<f32x4*>(dst) = f32x4{gdc[0], gdc[1], gdc[2], gdc[3]};
         *reinterpret_cast<f32x4*>(dst + 8) = f32x4{gdc[4], gdc[5], gdc[6], gdc[7]};
-        *reinterpret_cast<f32x4*>(dst + n) = f32x4{gdu[0], gdu[1], gdu[2], gdu[3]};
-        *reinterpret_cast<f32x4*>(dst + n + 8) = f32x4{gdu[4], gdu[5], gdu[6], gdu[7]};
+        *reinterpret_cast<f32x4*>(dst + 16) = f32x4{gdu[0], gdu[1], gdu[2], gdu[3]};
+        *reinterpret_cast<f32x4*>(dst + 24) = f32x4{gdu[4], gdu[5], gdu[6], gdu[7]};
       }
     }
   };

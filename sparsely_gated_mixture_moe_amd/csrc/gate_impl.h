@@ -52,7 +52,9 @@ struct GateParams {
   // Gradient pass (the Load pass's products, another epilogue; 32x32 kernel
   // only): dload [n] is d loss / d Load; every pair's gradients with respect
   // to its clean logit and noise pre-activation, taken as unselected, go to
-  // dcu [row][e] and dcu [row][n + e]. Null otherwise.
+  // dcu in blocks of 16 experts: row r of block q (experts 16 q .. 16 q + 15)
+  // is 32 floats at dcu + (q B + r) 32, the 16 clean-logit gradients then the
+  // 16 noise ones. Null otherwise.
   const float* dload;
   float* dcu;
   // Selection of one expert range (gridDim.y ranges): each row's best L

@@ -52,7 +52,8 @@ struct GateLaunch {
 // kernel): for every (token, expert) pair, taken as unselected, d loss / d
 // clean logit and d loss / d noise pre-activation through the Load term
 // (threshold thresh [row][0], the k-th logit; dload [n] = d loss / d Load)
-// into dcu [B][2n] (clean at column e, noise at n + e).
+// into dcu [n / 16][B][32]: for expert block q and token t, the 16 clean
+// gradients of experts 16 q .. 16 q + 15, then their 16 noise gradients.
 bool gate_pair_grads_supported(const GateLaunch& g);
 hipError_t launch_gate_pair_grads(const GateLaunch& g, const float* thresh, const float* dload,
                                   float* dcu, hipStream_t s);
