@@ -48,6 +48,15 @@ CASES = [
                          "d_hidden": 256}, True, True, (0.1, 0.1), 1.0),
     ("zipf_bf16_n256", {"tokens": 4000, "n_experts": 64, "d_hidden": 256}, True, False,
      (0.1, 0.1), 1.0),
+    # bf16 gates in training mode take the gate's gradient pass (blocked pair gradients,
+    # selected pairs rewritten): with a gate bias and a ragged last tile, one 16-expert
+    # chunk, and k = 8
+    ("flat_bf16_n4096", {"tokens": 1000, "n_experts": 48, "k": 3, "d_model": 128}, True, True,
+     (0.3, 1.0), 2.0),
+    ("flat_bf16_n4096", {"tokens": 333, "n_experts": 16, "k": 2, "d_model": 256,
+                         "d_hidden": 128}, True, True, (0.1, 0.1), 1.0),
+    ("flat_bf16_n4096", {"tokens": 520, "n_experts": 32, "k": 8, "d_model": 256,
+                         "d_hidden": 256}, True, False, (0.1, 0.1), 1.0),
 ]
 
 
