@@ -512,9 +512,15 @@ struct StageT<float> {
 // Row products on bf16 cores: TM = 32 MR rows x 256 columns a workgroup, 2 MR
 // waves in an MR x 2 grid (32 rows x 128 columns each). The first 256 threads
 // stage the weights, all threads the rows.
+//
+// Work item w = (unit or row block) * ncb + column block, nwork items. The
+// workgroups of one XCD (workgroup b runs on XCD b % 8) take runs of 2 ncb
+// consecutive items, the XCDs taking turns, so that two consecutive units
+// (an expert's rows, its weights) and all their column blocks (the same rows)
+// meet in one L2.
 template <typename TA, typename TW, bool WT, int MR>
 __global__ __launch_bounds__(128 * MR) __attribute__((amdgpu_waves_per_eu(2)))
-void row_tgemm_kernel(RowGemm p, int vec) {
+void row_tgemm_kernel(RowGemm p, int vec, int64_t nwork, int ncb) {
   constexpr bool SA = sizeof(TA) == 4, SW = sizeof(TW) == 4;
   constexpr int TM = 32 * MR, TN = 256;
   constexpr int ABYTES = TM * 64, BBYTES = TN * 64;  // one bf16 tile of each operand
@@ -522,20 +528,25 @@ void row_tgemm_kernel(RowGemm p, int vec) {
   __shared__ __attribute__((aligned(16))) uint8_t al[SA ? 2 : 1][SA ? ABYTES : 16];
   __shared__ __attribute__((aligned(16))) uint8_t bh[2][BBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t bl[SW ? 2 : 1][SW ? BBYTES : 16];
+  const int64_t run = 2 * (int64_t)ncb, slot = blockIdx.x / 8;
+  const int64_t w = ((slot / run) * 8 + blockIdx.x % 8) * run + slot % run;
+  if (w >= nwork) return;
+  const int cb = (int)(w % ncb);
+  const int64_t ub = w / ncb;
   int g = 0;
   int64_t r0, rend;
   if (p.units) {
-    const int u = blockIdx.x;
-    if (u >= p.units[0]) return;
+    if (ub >= p.units[0]) return;
+    const int u = (int)ub;
     g = p.units[1 + 2 * u];
     r0 = (int64_t)p.seg_off[g] + p.units[2 + 2 * u];
     rend = p.seg_off[g + 1];
   } else {
-    r0 = (int64_t)blockIdx.x * TM;
+    r0 = ub * TM;
     rend = p.rows;
     if (r0 >= rend) return;
   }
-  const int n0 = blockIdx.y * TN;
+  const int n0 = cb * TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -679,7 +690,7 @@ void row_tgemm_kernel(RowGemm p, int vec) {
       for (int j = 0; j < 16; ++j) rdsum[wn][wm * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)] = rs[j];
     }
     __syncthreads();
-    if (tid < TM && r0 + tid < rend) p.rowdot[(r0 + tid) * p.rd_n + blockIdx.y] = rdsum[0][tid] + rdsum[1][tid];
+    if (tid < TM && r0 + tid < rend) p.rowdot[(r0 + tid) * p.rd_n + cb] = rdsum[0][tid] + rdsum[1][tid];
   }
 }
 
@@ -1378,11 +1389,14 @@ hipError_t run_row_gemm(const RowGemm& p0, Dt ta, Dt tw, Dt to, int64_t grid_x, 
     const size_t wsz = tw == kBF16 ? 2 : 4;
     const int vec = aligned16(p.a) && aligned16(p.w) && p.lda % 8 == 0 && p.K % 8 == 0 &&
                     p.N % 8 == 0 && (p.w_stride * wsz) % 16 == 0;
-    // kTR rows a workgroup; without units the grid follows from the rows
+    // kTR rows a workgroup; without units the grid follows from the rows. The
+    // grid covers whole rounds of 8 runs of 2 ncb items (see the kernel).
     if (!p.units) grid_x = (p.rows + kTR - 1) / kTR;
-    const dim3 grid((unsigned)grid_x, (unsigned)((p.N + 255) / 256)), block(4 * kTR);
+    const int ncb = (p.N + 255) / 256;
+    const int64_t nwork = grid_x * ncb, round = 16 * (int64_t)ncb;
+    const dim3 grid((unsigned)((nwork + round - 1) / round * round)), block(4 * kTR);
 #define MOE_RT(A, W, WT) \
-  hipLaunchKernelGGL((row_tgemm_kernel<A, W, WT, kTR / 32>), grid, block, 0, s, p, vec)
+  hipLaunchKernelGGL((row_tgemm_kernel<A, W, WT, kTR / 32>), grid, block, 0, s, p, vec, nwork, ncb)
     const bool a32 = ta == kF32, w32 = tw == kF32;
     if (p.wt) {
       if (!a32 && !w32) MOE_RT(bf16, bf16, true);
