@@ -263,17 +263,30 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   };
 
   // Pass 1: insert the lane's 8 values of chunk `chunk` (experts in
-  // increasing order) into its token's list; any lane with a candidate makes
-  // the wave run the insertions, which become rare once the lists are warm.
+  // increasing order) into its token's list. Each lane marks the values that
+  // beat its list's last entry and inserts them lowest first, one per trip of
+  // a loop that the wave runs as often as its busiest lane needs (once or
+  // twice when the lists are warm), the value picked by a select tree on the
+  // bits of its position. A marked value that an earlier insertion has since
+  // outranked is dropped by insert_new's own test, so the list is the one
+  // that inserting all values in order gives.
   auto insert_pairs = [&](const auto& hv, int chunk) {
     constexpr int NV = CL ? 16 : 8;
-    bool cand = false;
+    uint32_t marks = 0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) cand |= hv[i] > lv[L - 1];
-    if (__any(cand)) {
+    for (int i = 0; i < NV; ++i) marks |= (hv[i] > lv[L - 1] ? 1u : 0u) << i;
+    while (marks) {
+      const int j = __builtin_ctz(marks);
+      marks &= marks - 1;
+      float t[NV];
 #pragma unroll
-      for (int i = 0; i < NV; ++i)
-        insert_new<L>(lv, li, hv[i], (cr.c0 + chunk) * EX + 8 * (i / 4) + 4 * hi + (i % 4));
+      for (int i = 0; i < NV; ++i) t[i] = hv[i];
+#pragma unroll
+      for (int w = NV / 2, b = 1; w >= 1; w /= 2, b *= 2) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) t[i] = (j & b) ? t[2 * i + 1] : t[2 * i];
+      }
+      insert_new<L>(lv, li, t[0], (cr.c0 + chunk) * EX + 8 * (j >> 2) + 4 * hi + (j & 3));
     }
   };
 
