@@ -141,6 +141,42 @@ def profiled_traffic(workload):
     return int(fields["traffic_bytes_per_launch"])
 
 
+def library_gemms(torch, iters=20):
+    """The vendor GEMM (torch.matmul -> hipBLASLt) on dense versions of the
+    layer's products: the gate's x [B, d] times [W_g | W_noise] at the
+    4096-expert workload, and the two expert products over all routed rows of
+    the Zipf 256-expert workload (131072 rows) and of its most popular expert
+    (21504 rows). Reference points only: the fused kernels also add the noise,
+    the top-k and the routing, and write no [B, 2n] logits."""
+    shapes = [
+        ("gate product 65536 x 8192 x 512 (bf16 out)", 65536, 8192, 512, torch.bfloat16),
+        ("Zipf expert-0 first product 21504 x 1024 x 512", 21504, 1024, 512, torch.bfloat16),
+        ("Zipf expert-0 second product 21504 x 512 x 1024", 21504, 512, 1024, torch.bfloat16),
+        ("all routed rows, first product 131072 x 1024 x 512", 131072, 1024, 512, torch.bfloat16),
+        ("all routed rows, second product 131072 x 512 x 1024", 131072, 512, 1024, torch.bfloat16),
+        ("square 8192 x 8192 x 8192", 8192, 8192, 8192, torch.bfloat16),
+        ("fp32 32768 x 1024 x 512", 32768, 1024, 512, torch.float32),
+    ]
+    for name, m, n, kk, dt in shapes:
+        a = torch.randn(m, kk, device="cuda", dtype=dt)
+        b = torch.randn(n, kk, device="cuda", dtype=dt).t()
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        peak = BF16_PEAK_TFLOPS if dt == torch.bfloat16 else FP32_PEAK_TFLOPS
+        tf = 2.0 * m * n * kk / ms / 1e9
+        print(json.dumps({"gemm": name, "dtype": str(dt).replace("torch.", ""), "ms": ms,
+                          "tflops": tf, "frac": tf / peak}), flush=True)
+        del a, b, c
+
+
 def cpu_baseline(w, inp, target_s):
     """The oracle's whole forward pass on the first S tokens of the workload,
     S grown until one run takes about target_s seconds."""
@@ -483,6 +519,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes three times "
                          "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="only time the vendor GEMM (torch.matmul, hipBLASLt) on the layer's "
+                         "product shapes, as a reference point for the fused kernels")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -500,6 +539,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}), flush=True)
+        return
+
+    if a.library_gemms:
+        library_gemms(torch)
         return
 
     import datagen as dg
