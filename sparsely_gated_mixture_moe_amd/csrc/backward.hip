@@ -1227,16 +1227,27 @@ __global__ __launch_bounds__(256) void dx_sum_kernel(int64_t B, int k, int d,
                                                      const float* __restrict__ dxe,
                                                      const int32_t* __restrict__ slot_pos,
                                                      float* __restrict__ dx) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= B * d) return;
-  const int64_t t = idx / d;
-  const int c = (int)(idx - t * d);
-  float v = dxg[idx];
+  // four consecutive columns of one token per thread (d is a multiple of 4 and
+  // every buffer 16-byte aligned): 16-byte loads and stores, the token's slot
+  // positions read once; each element is still the gate path's value plus the
+  // k rows in slot order
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int du = d >> 2;
+  if (q >= B * du) return;
+  const int64_t t = q / du;
+  const int c = (int)(q - t * du) * 4;
+  f32x4 v = *reinterpret_cast<const f32x4*>(dxg + t * d + c);
   for (int j = 0; j < k; ++j) {
     const int64_t row = slot_pos[t * k + j];
-    if (row >= 0) v += dxe[row * d + c];
+    if (row >= 0) {
+      const f32x4 e = *reinterpret_cast<const f32x4*>(dxe + row * d + c);
+      v[0] += e[0];
+      v[1] += e[1];
+      v[2] += e[2];
+      v[3] += e[3];
+    }
   }
-  dx[idx] = v;
+  *reinterpret_cast<f32x4*>(dx + t * d + c) = v;
 }
 
 // Row chunks of a weight gradient over all B tokens (the gate's): chunk i is
@@ -1829,7 +1840,7 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
     if ((e = run_row_gemm(r, kF32, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
   }
   if (B > 0) {
-    hipLaunchKernelGGL(dx_sum_kernel, dim3(blocks_for(B * d)), dim3(256), 0, s, B, k, d, dxg, dxe,
+    hipLaunchKernelGGL(dx_sum_kernel, dim3(blocks_for(B * (d / 4))), dim3(256), 0, s, B, k, d, dxg, dxe,
                        slot_pos, b.dx);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

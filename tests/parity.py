@@ -33,10 +33,10 @@ NEAR_TIE_ABS = 1e-6
 
 def announce(msg: str) -> None:
     """Name the case about to run on the GPU (flushed, so a crash still shows
-    it), also appended to gpurun_out/gpu_cases.log, whose growth shows that a
-    long case is still making progress."""
+    it), also appended to gpu_cases.log in the output folder at the repository
+    root, whose growth shows that a long case is still making progress."""
     print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
-    with open(os.path.join(gpurun_out_dir(), "gpu_cases.log"), "a") as f:
+    with open(os.path.join(output_dir(), "gpu_cases.log"), "a") as f:
         f.write(msg + "\n")
 
 
@@ -168,7 +168,7 @@ def out_tol(act_is_bf16: bool) -> float:
     return TOL_BF16 if act_is_bf16 else TOL_F32
 
 
-def gpurun_out_dir() -> str:
+def output_dir() -> str:
     d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
     os.makedirs(d, exist_ok=True)
     return d
