@@ -181,6 +181,58 @@ def test_forward_exact_ties(case, train):
 
 
 # ---------------------------------------------------------------------------
+# Rising logits: every value is a candidate
+# ---------------------------------------------------------------------------
+
+def rising_inputs(w, seed):
+    """Zero gate weights and a gate bias of 4 e: the noisy logit of expert e
+    is H = 4 e + eps_te (Softplus(0) + f) with eps from {-1, 0, 1, 2}, so H
+    rises strictly with e in every row (the noise moves it by less than 1.5).
+    Each new value then beats every list entry so far: the selection pass's
+    insertion step takes all of a lane's values in every chunk, its most
+    expensive case, which random inputs never reach once the lists are warm."""
+    n = w.n_experts
+    inp = dg.make_inputs(w, experts=False)
+    zero = np.zeros((n, w.d_model), np.float32)
+    inp["w_gate"] = dg.f32_to_bf16(zero) if w.gate_dtype == dg.BF16 else zero
+    inp["w_noise"] = inp["w_gate"].copy()
+    inp["gate_bias"] = (4.0 * np.arange(n)).astype(np.float32)
+    rng = np.random.default_rng(seed)
+    inp["eps"] = rng.choice([-1.0, 0.0, 1.0, 2.0], size=(w.tokens, n)).astype(np.float32)
+    return inp
+
+
+RISING_CASES = [
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 4096}),
+    ("flat_bf16_n4096", {"tokens": 300, "n_experts": 512, "k": 8, "d_model": 256}),
+    ("tiny_fp32", {"tokens": 300, "n_experts": 256, "k": 4}),
+]
+
+
+@pytest.mark.parametrize("case", RISING_CASES, ids=[_tid(c + ("",)) for c in RISING_CASES])
+@pytest.mark.parametrize("train", [True, False])
+def test_gate_rising_logits(case, train):
+    """The last k experts, largest first, with the exact thresholds and gates,
+    whole and split sweeps, training and noise-free selection."""
+    name, kw = case
+    w = dg.workload(name, **kw)
+    announce(f"moe_gate rising logits {w.name} {kw} train={train}")
+    inp = rising_inputs(w, seed=w.tokens + 5 * w.n_experts)
+    ref = oracle.gate(inp, w.k, train=train, noise_floor=FLOOR, want_logits=True)
+    last = np.arange(w.n_experts - 1, w.n_experts - 1 - w.k, -1, dtype=np.int32)
+    assert np.array_equal(ref["topk_idx"], np.broadcast_to(last, ref["topk_idx"].shape))
+    g = gpu_inputs(inp)
+    dims, opts = dims_for(g, w, train)
+    ws = moe.workspace(dims, opts, g["x"].device)
+    for w_s in (ws, None):
+        idx, gate, thr = moe.moe_gate(g["x"], g["w_gate"], g["w_noise"],
+                                      g["eps"] if train else None, w.k, train=train,
+                                      noise_floor=FLOOR, gate_bias=g["gate_bias"], ws=w_s)
+        torch.cuda.synchronize()
+        check_exact(ref, to_host(idx), to_host(gate), to_host(thr), w.k)
+
+
+# ---------------------------------------------------------------------------
 # Gate bias through the 32x32 kernel (bf16 gate weights)
 # ---------------------------------------------------------------------------
 
