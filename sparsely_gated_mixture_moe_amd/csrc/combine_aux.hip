@@ -83,59 +83,72 @@ __global__ void offsets_to_load_kernel(const int32_t* __restrict__ offsets, int 
 
 // CV^2 = population variance / mean^2 of importance and of load, in fp64 with a
 // fixed reduction order; losses = {CV2(imp), CV2(load), w_imp CV2(imp) + w_load CV2(load)}.
-// One workgroup of 1024 threads; thread t holds elements t, t + 1024, ... of
-// both vectors in registers (n <= 32768), sums them in that order, then a tree
-// over the threads; the squared deviations are formed from the same registers.
-constexpr int kCvThreads = 1024;
-constexpr int kCvPer = 32;  // 32768 / 1024
-__global__ __launch_bounds__(kCvThreads) void cv2_losses_kernel(const float* __restrict__ imp,
-                                                                const float* __restrict__ load,
-                                                                int n, float w_imp, float w_load,
-                                                                float* __restrict__ losses) {
-  __shared__ double red[2][kCvThreads];
-  const int t = threadIdx.x;
-  float xi[kCvPer], xl[kCvPer];
+// One workgroup of T threads; thread t holds elements t, t + T, ... (PER of
+// them, T * PER >= n) of both vectors in registers and sums them in that order;
+// each wave adds its lanes' sums by a butterfly (lanes 32, 16, ..., 1 apart)
+// and the waves' totals are added in wave order after one barrier. The squared
+// deviations are formed from the same registers and reduced the same way.
+constexpr int kCvMax = 32768;
+
+__device__ __forceinline__ double cv_wave_sum(double v) {
 #pragma unroll
-  for (int j = 0; j < kCvPer; ++j) {
-    const int i = t + j * kCvThreads;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int T, int PER>
+__global__ __launch_bounds__(T) void cv2_losses_kernel(const float* __restrict__ imp,
+                                                       const float* __restrict__ load, int n,
+                                                       float w_imp, float w_load,
+                                                       float* __restrict__ losses) {
+  constexpr int W = T / 64;
+  __shared__ double red[2][2][W];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  float xi[PER], xl[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = t + j * T;
     xi[j] = i < n ? imp[i] : 0.f;
     xl[j] = i < n ? load[i] : 0.f;
   }
-  auto tree = [&](double a, double b, double (&out)[2]) {
-    red[0][t] = a;
-    red[1][t] = b;
-    __syncthreads();
-    for (int o = kCvThreads / 2; o > 0; o >>= 1) {
-      if (t < o) {
-        red[0][t] += red[0][t + o];
-        red[1][t] += red[1][t + o];
-      }
-      __syncthreads();
+  // the two block totals; slot s has its own LDS cells, so one barrier each
+  auto block_sum = [&](double a, double b, int s, double (&out)[2]) {
+    a = cv_wave_sum(a);
+    b = cv_wave_sum(b);
+    if (lane == 0) {
+      red[s][0][wave] = a;
+      red[s][1][wave] = b;
     }
-    out[0] = red[0][0];
-    out[1] = red[1][0];
     __syncthreads();
+    double u = 0.0, v = 0.0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      u += red[s][0][w];
+      v += red[s][1][w];
+    }
+    out[0] = u;
+    out[1] = v;
   };
   double si = 0.0, sl = 0.0;
 #pragma unroll
-  for (int j = 0; j < kCvPer; ++j) {
+  for (int j = 0; j < PER; ++j) {
     si += (double)xi[j];
     sl += (double)xl[j];
   }
   double sum[2];
-  tree(si, sl, sum);
+  block_sum(si, sl, 0, sum);
   const double mi = sum[0] / n, ml = sum[1] / n;
   double qi = 0.0, ql = 0.0;
 #pragma unroll
-  for (int j = 0; j < kCvPer; ++j) {
-    if (t + j * kCvThreads < n) {
+  for (int j = 0; j < PER; ++j) {
+    if (t + j * T < n) {
       const double di = (double)xi[j] - mi, dl = (double)xl[j] - ml;
       qi += di * di;
       ql += dl * dl;
     }
   }
   double q[2];
-  tree(qi, ql, q);
+  block_sum(qi, ql, 1, q);
   if (t == 0) {
     const double cvi = (n <= 1 || mi == 0.0) ? 0.0 : (q[0] / n) / (mi * mi);
     const double cvl = (n <= 1 || ml == 0.0) ? 0.0 : (q[1] / n) / (ml * ml);
@@ -179,9 +192,18 @@ hipError_t launch_offsets_to_load(const int32_t* offsets, int n, float* load, hi
 
 hipError_t launch_cv2_losses(const float* importance, const float* load, int n, float w_imp,
                              float w_load, float* losses, hipStream_t s) {
-  if (n > kCvThreads * kCvPer) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(cv2_losses_kernel, dim3(1), dim3(kCvThreads), 0, s, importance, load, n, w_imp,
-                     w_load, losses);
+  if (n > kCvMax) return hipErrorInvalidValue;
+  // as few threads as keep every thread's share small: 256 x 16 up to 4096
+  // experts, 512 x 32 up to 16384, 1024 x 32 beyond
+  if (n <= 4096)
+    hipLaunchKernelGGL((cv2_losses_kernel<256, 16>), dim3(1), dim3(256), 0, s, importance, load, n,
+                       w_imp, w_load, losses);
+  else if (n <= 16384)
+    hipLaunchKernelGGL((cv2_losses_kernel<512, 32>), dim3(1), dim3(512), 0, s, importance, load, n,
+                       w_imp, w_load, losses);
+  else
+    hipLaunchKernelGGL((cv2_losses_kernel<1024, 32>), dim3(1), dim3(1024), 0, s, importance, load,
+                       n, w_imp, w_load, losses);
   return hipGetLastError();
 }
 

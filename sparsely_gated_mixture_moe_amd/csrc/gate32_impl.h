@@ -263,15 +263,24 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   };
 
   // Pass 1: insert the lane's 8 values of chunk `chunk` (experts in
-  // increasing order) into its token's list. Each lane marks the values that
-  // beat its list's last entry and inserts them lowest first, one per trip of
-  // a loop that the wave runs as often as its busiest lane needs (once or
-  // twice when the lists are warm), the value picked by a select tree on the
-  // bits of its position. A marked value that an earlier insertion has since
-  // outranked is dropped by insert_new's own test, so the list is the one
-  // that inserting all values in order gives.
+  // increasing order) into its token's list. Once the lists are warm (from
+  // the range's fifth chunk on), each lane marks the values that beat its
+  // list's last entry and inserts them lowest first, one per trip of a loop
+  // that the wave runs as often as its busiest lane needs (once or twice),
+  // the value picked by a select tree on the bits of its position; a marked
+  // value that an earlier insertion has since outranked is dropped by
+  // insert_new's own test, so the list is the one that inserting all values
+  // in order gives. In the first chunks nearly every value is a candidate,
+  // and inserting each value in turn (a branch the wave takes when any lane
+  // needs it) is cheaper than a trip per value.
   auto insert_pairs = [&](const auto& hv, int chunk) {
     constexpr int NV = CL ? 16 : 8;
+    if (chunk < 4) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        insert_new<L>(lv, li, hv[i], (cr.c0 + chunk) * EX + 8 * (i / 4) + 4 * hi + (i % 4));
+      return;
+    }
     uint32_t marks = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) marks |= (hv[i] > lv[L - 1] ? 1u : 0u) << i;
