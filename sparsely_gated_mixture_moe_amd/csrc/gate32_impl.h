@@ -273,9 +273,9 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
   // in order gives. In the first chunks nearly every value is a candidate,
   // and inserting each value in turn (a branch the wave takes when any lane
   // needs it) is cheaper than a trip per value.
-  auto insert_pairs = [&](const auto& hv, int chunk) {
+  auto insert_pairs = [&](const auto& hv, int chunk, auto warm) {
     constexpr int NV = CL ? 16 : 8;
-    if (chunk < 4) {
+    if constexpr (!decltype(warm)::value) {
 #pragma unroll
       for (int i = 0; i < NV; ++i)
         insert_new<L>(lv, li, hv[i], (cr.c0 + chunk) * EX + 8 * (i / 4) + 4 * hi + (i % 4));
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
 
   // One pass per chunk; P = c & 1 is a compile-time constant (the loop below
   // is unrolled by two) so each pass names its buffers statically.
-  auto chunk_pass = [&](const int c, auto parity) {
+  auto chunk_pass = [&](const int c, auto parity, auto warm) {
     constexpr int P = decltype(parity)::value;
     U16* const wfill = P ? wbuf1 : wbuf0;       // buffer c & 1: chunk c + 2 goes here
     const U16* const wnext = P ? wbuf0 : wbuf1;  // buffer (c + 1) & 1: chunk c + 1
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
         }
       } else {
         if constexpr (SMX) es = expsum_add(es, hv);
-        insert_pairs(hv, c);
+        insert_pairs(hv, c, warm);
       }
     }
 
@@ -587,9 +587,18 @@ __global__ __launch_bounds__(kG32Threads) void gate32_kernel(GateParams p) {
       }
     }
   };
-  for (int c = 0; c < nchunks; c += 2) {
-    chunk_pass(c, IntConst<0>{});
-    if (c + 1 < nchunks) chunk_pass(c + 1, IntConst<1>{});
+  // the first kCold chunks of the range with the cold-list insertion (pass 1
+  // only; the other passes compile the same loop once)
+  constexpr int kCold = (PASS2 || SCORES) ? 0 : 4;
+  const int ncold = nchunks < kCold ? nchunks : kCold;
+  int c = 0;
+  for (; c < ncold; c += 2) {
+    chunk_pass(c, IntConst<0>{}, IntConst<0>{});
+    if (c + 1 < nchunks) chunk_pass(c + 1, IntConst<1>{}, IntConst<0>{});
+  }
+  for (; c < nchunks; c += 2) {
+    chunk_pass(c, IntConst<0>{}, IntConst<1>{});
+    if (c + 1 < nchunks) chunk_pass(c + 1, IntConst<1>{}, IntConst<1>{});
   }
   if constexpr (BWD) {
     if (nchunks > 0) store_grads(nchunks - 1);
