@@ -46,7 +46,10 @@
 //    Load = Load1_i * Load2_ij / |X_i| (0 when |X_i| = 0), where Load1 is the
 //    primary gate's Load over the batch, Load2_i the secondary gate's Load
 //    over the rows X_i routed to group i; both reduce to the flat losses
-//    when a = 1 or b = 1. PARITY UNPINNED beyond those reductions.
+//    when a = 1 or b = 1. Pinned at their limits only: those reductions, the
+//    dense mixture's gate sums, and the hard leaf counts that the leaf Load
+//    becomes at train = 0 and when the noise scale vanishes; between them the
+//    product form is a reading, as no page defines the hierarchy's losses.
 //
 // Weight layouts: w_gate/w_noise [n][d] (row i = expert i), w1 [n][h][d]
 // (row j = hidden unit j), w2 [n][d][h] (row c = output unit c). Hierarchical:

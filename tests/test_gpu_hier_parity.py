@@ -8,8 +8,9 @@ levels (so the secondary gates see the same groups in the same rank order),
 and every output is compared with it: leaf ids bit-exactly, gates, y,
 Importance, both levels' Load and the leaf Load, and the losses within the
 stated tolerances. The hierarchy's losses are this library's own reading
-(the pages give none); the oracle's version of them is parity unpinned
-beyond its reductions to the flat layer.
+(the pages give none); the oracle's version is pinned at its limits (the
+flat layer, the dense mixture, hard counts at train = 0 and with vanishing
+noise: tests/test_oracle_hier_pins.py).
 """
 import numpy as np
 import pytest

@@ -11,8 +11,18 @@ Each check ties the hierarchical oracle to something other than itself:
   * structural invariants: k1*k2 distinct leaves per token inside the chosen
     groups, leaf gates that are products of the two levels and sum to 1,
     Importance summing to B.
-The hierarchy's balancing losses appear on none of the pages: beyond the two
-reductions above they are parity unpinned.
+The hierarchy's balancing losses appear on none of the pages; the oracle's
+reading (leaf Importance = the leaf gate sums, leaf Load = Load1_i Load2_ij /
+|X_i|) is pinned at its limits:
+  * the two reductions above;
+  * with every expert kept and no noise, leaf Importance against the dense
+    mixture's gate products;
+  * with train = 0 both levels' Loads are hard counts, so the leaf Load is the
+    number of tokens at each leaf, counted here from the selection alone, and
+    the losses are the CV^2 of those counts and of the leaf gate sums;
+  * in training with the noise scale driven to zero every eq 9 term is
+    exactly 0 or 1, and the training formula gives the same hard counts.
+Between those limits the product form is a reading: no page defines it.
 """
 import numpy as np
 import pytest
@@ -187,3 +197,61 @@ def test_batch_sums_without_the_experts():
     assert "y" not in part
     for key, v in part.items():
         np.testing.assert_array_equal(v, full[key], err_msg=key)
+
+
+def _cv2(v):
+    """Population variance over the squared mean (0 for one entry or mean 0)."""
+    v = np.asarray(v, np.float64)
+    m = v.mean()
+    return 0.0 if v.size <= 1 or m == 0 else float(((v - m) ** 2).mean() / m ** 2)
+
+
+@pytest.mark.parametrize("a,b,k1,k2", [(4, 6, 2, 2), (8, 5, 3, 2), (3, 16, 1, 4)])
+def test_hard_leaf_load_is_the_leaf_count(a, b, k1, k2):
+    """train = 0: Load1_i = |X_i| and Load2_ij counts the rows of X_i that
+    picked j, so Load1_i Load2_ij / |X_i| is the number of tokens at leaf
+    (i, j); leaf Importance is each leaf's sum of leaf gates; the losses are
+    their CV^2 with weights 0.1."""
+    w = hier_wl(tokens=500, a=a, b=b, k1=k1, k2=k2)
+    inp = dg.make_hier_inputs(w, experts=False)
+    out = oracle.hier_forward(inp, k1, k2, train=False, with_y=False)
+    n = a * b
+    idx = out["leaf_idx"].ravel()
+    counts = np.bincount(idx, minlength=n).astype(np.float64)
+    np.testing.assert_allclose(out["load"], counts, rtol=1e-12, atol=0)
+    imp = np.bincount(idx, weights=out["leaf_gate"].ravel(), minlength=n)
+    np.testing.assert_allclose(out["importance"], imp, rtol=1e-12, atol=1e-12)
+    cvi, cvl = _cv2(imp), _cv2(counts)
+    np.testing.assert_allclose(out["losses"], [cvi, cvl, 0.1 * cvi + 0.1 * cvl],
+                               rtol=1e-10, atol=1e-15)
+    # the primary level's hard Load is its routed row count
+    np.testing.assert_allclose(out["load1"], out["rows1"], rtol=0, atol=0)
+    np.testing.assert_allclose(out["rows1"], np.bincount(idx // b, minlength=a) / k2)
+
+
+def test_vanishing_noise_leaf_load_is_the_leaf_count():
+    """train = 1 with the noise scale driven to zero: a constant feature
+    x[:, 0] = 1 and noise weights of -40 on it (all others 0) make every noise
+    pre-activation -40, so sigma = Softplus(-40) ~ 4e-18 with the floor at 0.
+    Each eq 9 term Phi((clean - thr) / sigma) is then exactly 0 or 1, the
+    selection is the noise-free one, and the training Loads of both levels and
+    of the leaves equal the hard counts."""
+    a, b, k1, k2 = 6, 8, 2, 3
+    w = hier_wl(tokens=400, a=a, b=b, k1=k1, k2=k2)
+    inp = dg.make_hier_inputs(w, experts=False)
+    x = inp["x"].copy()
+    x[:, 0] = 1.0
+    inp["x"] = x
+    wn = np.zeros_like(inp["w_noise"])
+    wn[:, 0] = -40.0
+    inp["w_noise"] = wn
+    wn2 = np.zeros_like(inp["w_noise2"])
+    wn2[:, :, 0] = -40.0
+    inp["w_noise2"] = wn2
+    tr = oracle.hier_forward(inp, k1, k2, train=True, noise_floor=0.0, with_y=False)
+    hard = oracle.hier_forward(inp, k1, k2, train=False, with_y=False)
+    np.testing.assert_array_equal(tr["leaf_idx"], hard["leaf_idx"])
+    counts = np.bincount(hard["leaf_idx"].ravel(), minlength=a * b).astype(np.float64)
+    np.testing.assert_allclose(tr["load"], counts, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(tr["load1"], tr["rows1"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(tr["losses"][1], _cv2(counts), rtol=1e-10)
