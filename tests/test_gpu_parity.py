@@ -411,6 +411,10 @@ def test_combine_parity(case):
 AUX_CASES = GATE_CASES[:4] + GATE_CASES[6:] + [
     ("flat_bf16_n4096", {"tokens": 16384, "n_experts": 8, "k": 2}),
     ("zipf_bf16_n256", {"tokens": 16384, "n_experts": 64}),
+    # every size class of the CV^2 kernel (up to 4096, 16384 and 32768 experts)
+    ("flat_bf16_n4096", {"tokens": 96, "n_experts": 4112, "d_model": 128}),
+    ("flat_bf16_n4096", {"tokens": 64, "n_experts": 20000, "d_model": 128}),
+    ("flat_bf16_n4096", {"tokens": 64, "n_experts": 32768, "k": 2, "d_model": 128}),
 ]
 
 
