@@ -1222,6 +1222,7 @@ __global__ __launch_bounds__(256) void kept_pair_grad_kernel(
 }
 
 // dx[t] = dxg[t] + sum over the token's slots of dxe[slot_pos[t][j]] (fp32, slot order).
+template <bool NT>
 __global__ __launch_bounds__(256) void dx_sum_kernel(int64_t B, int k, int d,
                                                      const float* __restrict__ dxg,
                                                      const float* __restrict__ dxe,
@@ -1240,7 +1241,13 @@ __global__ __launch_bounds__(256) void dx_sum_kernel(int64_t B, int k, int d,
   for (int j = 0; j < k; ++j) {
     const int64_t row = slot_pos[t * k + j];
     if (row >= 0) {
-      const f32x4 e = *reinterpret_cast<const f32x4*>(dxe + row * d + c);
+      f32x4 e;
+      if constexpr (NT) {
+        const U16 u = ld_unit_stream(dxe + row * d + c);
+        __builtin_memcpy(&e, &u, 16);
+      } else {
+        e = *reinterpret_cast<const f32x4*>(dxe + row * d + c);
+      }
       v[0] += e[0];
       v[1] += e[1];
       v[2] += e[2];
@@ -1840,8 +1847,13 @@ hipError_t launch_backward(const BackwardLaunch& b, void* ws, hipStream_t s) {
     if ((e = run_row_gemm(r, kF32, b.gate_dt, kF32, rt, s, b.act_dt == kBF16)) != hipSuccess) return e;
   }
   if (B > 0) {
-    hipLaunchKernelGGL(dx_sum_kernel, dim3(blocks_for(B * (d / 4))), dim3(256), 0, s, B, k, d, dxg, dxe,
-                       slot_pos, b.dx);
+    // the routed rows' dx (P x d fp32) is read once: non-temporal past the Infinity Cache
+    if ((int64_t)P * d * 4 > kStreamBytes)
+      hipLaunchKernelGGL((dx_sum_kernel<true>), dim3(blocks_for(B * (d / 4))), dim3(256), 0, s, B,
+                         k, d, dxg, dxe, slot_pos, b.dx);
+    else
+      hipLaunchKernelGGL((dx_sum_kernel<false>), dim3(blocks_for(B * (d / 4))), dim3(256), 0, s, B,
+                         k, d, dxg, dxe, slot_pos, b.dx);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

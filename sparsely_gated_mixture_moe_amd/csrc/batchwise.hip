@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void batch_tok_sort_kernel(const int32_t* __re
 // One wave per token: its gates (softmax of its scores, slot order) to
 // sel_gate, and y[tok] = sum over its slots, in slot order, of gate * expert
 // output (fp32 accumulation), one 16-byte unit of the row per lane and step.
-template <typename T>
+template <typename T, bool NT>
 __global__ __launch_bounds__(256) void batch_combine_kernel(
     const T* __restrict__ eo, const int32_t* __restrict__ tok_off,
     const int32_t* __restrict__ tok_sorted, const float* __restrict__ sel_score,
@@ -486,7 +486,9 @@ __global__ __launch_bounds__(256) void batch_combine_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         g[i] = q[i] >= 0 ? expf(sel_score[q[i]] - mx) / den : 0.f;
-        v[i] = q[i] >= 0 ? ld_unit(eo + (int64_t)q[i] * d + u * UE) : zero_unit();
+        v[i] = q[i] < 0 ? zero_unit()
+               : NT ? ld_unit_stream(eo + (int64_t)q[i] * d + u * UE)
+                    : ld_unit(eo + (int64_t)q[i] * d + u * UE);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -604,14 +606,20 @@ hipError_t launch_batchwise(const BatchwiseLaunch& b, hipStream_t s, hipEvent_t 
   if (e != hipSuccess) return e;
   if (B > 0) {
     const dim3 grid((unsigned)((B + 3) / 4));
-    if (b.act_dt == kBF16)
-      hipLaunchKernelGGL(batch_combine_kernel<bf16>, grid, dim3(256), 0, s,
-                         reinterpret_cast<const bf16*>(b.expert_out), b.tok_off, b.tok_sorted,
-                         b.sel_score, b.sel_gate, (int)B, b.gate.d, reinterpret_cast<bf16*>(b.y));
-    else
-      hipLaunchKernelGGL(batch_combine_kernel<float>, grid, dim3(256), 0, s,
-                         reinterpret_cast<const float*>(b.expert_out), b.tok_off, b.tok_sorted,
-                         b.sel_score, b.sel_gate, (int)B, b.gate.d, reinterpret_cast<float*>(b.y));
+    // expert outputs past the Infinity Cache's size: non-temporal loads (as in the combine)
+    const bool nt = (int64_t)slots * b.gate.d * (b.act_dt == kBF16 ? 2 : 4) > kStreamBytes;
+#define MOE_BCOMBINE(TT, NTV)                                                                    \
+  hipLaunchKernelGGL((batch_combine_kernel<TT, NTV>), grid, dim3(256), 0, s,                    \
+                     reinterpret_cast<const TT*>(b.expert_out), b.tok_off, b.tok_sorted,         \
+                     b.sel_score, b.sel_gate, (int)B, b.gate.d, reinterpret_cast<TT*>(b.y))
+    if (b.act_dt == kBF16) {
+      if (nt) MOE_BCOMBINE(bf16, true);
+      else MOE_BCOMBINE(bf16, false);
+    } else {
+      if (nt) MOE_BCOMBINE(float, true);
+      else MOE_BCOMBINE(float, false);
+    }
+#undef MOE_BCOMBINE
   }
   hipLaunchKernelGGL(batch_importance_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s,
                      b.counts, b.sel_gate, n, m, b.importance);

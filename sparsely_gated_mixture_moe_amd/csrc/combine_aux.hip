@@ -10,16 +10,6 @@ namespace {
 // y[t] = sum_j gate[t, j] * expert_out[slot_pos[t*k + j]], fp32 accumulation
 // in slot order. One thread per 16-byte unit of an output row: every read and
 // write is a full 16-byte access and a row is read contiguously.
-// A 16-byte load marked non-temporal: the expert outputs are read once, and a
-// wave's loads cover whole rows (full cache lines).
-__device__ __forceinline__ U16 ld_unit_stream(const void* p) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  U16 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
-
 template <typename T, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ eo,
                                                       const int32_t* __restrict__ slot_pos,
@@ -183,7 +173,7 @@ hipError_t launch_combine(int64_t tokens, int k, int d, Dt dt, const void* exper
   // read with non-temporal loads (5.7 against 5.2 TB/s for 268 MB); smaller
   // ones, just written by the expert FFN, are still in that cache, which the
   // non-temporal loads would pass by (slower: 30 against 27 us for 134 MB).
-  const bool nt = rows * d * (dt == kBF16 ? 2 : 4) > ((int64_t)192 << 20);
+  const bool nt = rows * d * (dt == kBF16 ? 2 : 4) > kStreamBytes;
 #define MOE_COMBINE(TT, NTV)                                                                      \
   hipLaunchKernelGGL((combine_kernel<TT, NTV>), grid, dim3(256), 0, s,                           \
                      reinterpret_cast<const TT*>(expert_out), slot_pos, topk_gate, tokens, k, d, \

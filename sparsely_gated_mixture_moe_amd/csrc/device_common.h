@@ -42,6 +42,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 __device__ __forceinline__ U16 ld_unit(const void* p) { return *reinterpret_cast<const U16*>(p); }
+
+// The same as a non-temporal load, for data read once in whole cache lines
+// (each wave instruction covering full 128-byte lines) from beyond the caches.
+__device__ __forceinline__ U16 ld_unit_stream(const void* p) {
+  typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+  const u32x4_ v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_*>(p));
+  U16 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// Arrays larger than this many bytes do not stay in the 256 MB Infinity Cache
+// between the kernel that writes them and the one that reads them once; those
+// reads go to HBM and are faster as non-temporal loads.
+constexpr int64_t kStreamBytes = (int64_t)192 << 20;
 __device__ __forceinline__ void st_unit(void* p, const U16& v) { *reinterpret_cast<U16*>(p) = v; }
 __device__ __forceinline__ U16 zero_unit() { return U16{{0u, 0u, 0u, 0u}}; }
 
