@@ -963,7 +963,13 @@ __global__ __launch_bounds__(NW * 64) void wgrad_tgemm_kernel(Wgrad p, int vec, 
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int m = om0 + wm * WM + mb * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-          if (m < p.M) og[(int64_t)m * p.N + n] = acc[mb][nb][j];
+          if (m < p.M) {
+            // persistent tiles (short segments) write gradients that no later
+            // kernel reads: non-temporal stores; the other tiles' chunk
+            // partials, summed by the next kernel, stay cached
+            if constexpr (PERSIST) __builtin_nontemporal_store(acc[mb][nb][j], &og[(int64_t)m * p.N + n]);
+            else og[(int64_t)m * p.N + n] = acc[mb][nb][j];
+          }
         }
     }
     if (ocs) {  // the 8 threads of a column unit hold rows 4 kq .. : add in kq order
