@@ -708,6 +708,11 @@ def main():
         "roofline": rl,
         "step": step,
         "stages": stages,
+        # rows per expert of the timed steps' routing (the load balance the FFN sees)
+        "routing": {"rows": rows, "used_experts": used,
+                    "rows_per_expert_mean": float(cnt.mean()),
+                    "rows_per_expert_max": int(cnt.max()),
+                    "rows_per_expert_min": int(cnt.min())},
         "wall_ms_per_step": 1000 * wall / a.steps,
         "cpu_baseline": None,
     }
