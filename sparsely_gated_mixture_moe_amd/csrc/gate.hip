@@ -410,7 +410,10 @@ int gate_ranges(const GateLaunch& g) {
                                  : (g.x_dt == kBF16 && g.w_dt == kBF16 ? GateShape<bf16>::kChunk
                                                                         : GateShape<float>::kChunk);
   const int nch = (g.n + w - 1) / w;
-  const int64_t want = std::min<int64_t>((kTarget + tiles - 1) / tiles, nch / 2);
+  // ranges of two chunks or more; the 16x16 kernel also splits a sweep of two
+  // or three chunks (a few dozen experts) into single chunks
+  const int cap = gate_uses_g32(g) ? nch / 2 : std::max(nch / 2, std::min(nch, 2));
+  const int64_t want = std::min<int64_t>((kTarget + tiles - 1) / tiles, cap);
   if (want <= 1) return 1;
   // equal ranges of `per` chunks, none empty
   const int per = (int)((nch + want - 1) / want);
