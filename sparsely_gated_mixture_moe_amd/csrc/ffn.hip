@@ -532,16 +532,35 @@ __global__ __launch_bounds__(1024) void ffn_plan(const int32_t* __restrict__ off
   }
   int pos = part[t] - s;
   FfnUnit* units = reinterpret_cast<FfnUnit*>(blocks + 4);
-  for (int e = e0; e < e1; ++e) {
-    const int seg = seg_start(e);
-    const int cnt = served(e);
-    for (int r = 0; r < cnt; r += bm) {
-      for (int q = 0; q < hsplit; ++q) {
-        const int hr = hsplit > 1 ? (q * hper) | (min(hper, nch - q * hper) << 16) : 0;
-        units[pos] = FfnUnit{e, seg + r, min(bm, cnt - r), hr};
-        ++pos;
-      }
+  const int lane = t & 63;
+  // unit u of an expert: row block u / hsplit, hidden range u % hsplit
+  auto unit_at = [&](int e, int seg, int cnt, int u) {
+    const int r = u / hsplit * bm, q = u % hsplit;
+    const int hr = hsplit > 1 ? (q * hper) | (min(hper, nch - q * hper) << 16) : 0;
+    return FfnUnit{e, seg + r, min(bm, cnt - r), hr};
+  };
+  // A thread lists the units of an expert with a few of them itself; an
+  // expert with many (a popular one) has its units listed by the whole wave,
+  // one such expert at a time, so that no thread writes hundreds in a row.
+  // Every unit lands at the same position either way.
+  for (int i = 0; i < per; ++i) {  // per is uniform over the workgroup
+    const int e = e0 + i;
+    const bool has = e < e1;
+    const int cnt = has ? served(e) : 0;
+    const int seg = has ? seg_start(e) : 0;
+    const int nu = (cnt + bm - 1) / bm * hsplit;
+    const bool many = nu > 8;
+    if (!many)
+      for (int u = 0; u < nu; ++u) units[pos + u] = unit_at(e, seg, cnt, u);
+    uint64_t m = __ballot(many);
+    while (m) {
+      const int j = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const int be = __shfl(e, j), bseg = __shfl(seg, j), bcnt = __shfl(cnt, j);
+      const int bnu = __shfl(nu, j), bpos = __shfl(pos, j);
+      for (int u = lane; u < bnu; u += 64) units[bpos + u] = unit_at(be, bseg, bcnt, u);
     }
+    pos += nu;
   }
   if (t == 1023) blocks[0] = part[t];
 }

@@ -151,8 +151,20 @@ __global__ void route_importance(const float* __restrict__ perm_gate,
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (e >= n) return;
+  // lane l adds positions l, l + 64, ... of the segment in ascending order;
+  // sixteen of them are loaded before any is added, so that a long segment
+  // (a popular expert) is not one load latency per step
+  const int end = offsets[e + 1];
   float s = 0.f;
-  for (int i = offsets[e] + lane; i < offsets[e + 1]; i += 64) s += perm_gate[i];
+  int i = offsets[e] + lane;
+  for (; i + 64 * 15 < end; i += 64 * 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = perm_gate[i + 64 * j];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += v[j];
+  }
+  for (; i < end; i += 64) s += perm_gate[i];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if (lane == 0) importance[e] = s;
