@@ -509,6 +509,9 @@ def main():
     ap.add_argument("--gate-order", type=int, default=0, choices=(0, 1),
                     help="0: softmax over the kept k (the pages); 1: softmax over all n, then "
                          "the kept k (Switch's order)")
+    ap.add_argument("--expert-layout", default="natural", choices=("natural", "packed"),
+                    help="packed: the expert weights are converted once, before timing, to the "
+                         "matrix-core operand layout (moe_pack_expert_weights, expert_layout=1)")
     ap.add_argument("--gating", default="topk", choices=("topk", "batchwise"),
                     help="batchwise: every expert takes its k B / n best rows of the batch "
                          "(moe_batchwise_forward) instead of every token its k best experts")
@@ -551,6 +554,8 @@ def main():
     w = dg.WORKLOADS[a.workload]
     if a.tokens > 0:
         w = dg.workload(a.workload, tokens=a.tokens)
+    if a.expert_layout != "natural" and (w.hierarchical or a.gating != "topk" or a.backward):
+        raise SystemExit("--expert-layout packed applies to the flat top-k forward only")
     if w.hierarchical:
         bench_hier(a, w)
         return
@@ -569,9 +574,13 @@ def main():
         bench_backward(a, w, g, moe, torch, np, dg)
         return
     cap = int(np.ceil(a.capacity_factor * B * k / n)) if a.capacity_factor > 0 else 0
+    layout = 1 if a.expert_layout == "packed" else 0
+    if layout:  # a one-time conversion of the weights, outside the timed steps
+        g["w1"], g["w2"] = moe.moe_pack_expert_weights(g["w1"], g["w2"])
+        torch.cuda.synchronize()
     f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,
                        gate_bias=g.get("gate_bias"), train=bool(a.train), capacity=cap,
-                       gate_order=a.gate_order)
+                       gate_order=a.gate_order, expert_layout=layout)
     dev = g["x"].device
     y = torch.empty((B, d), dtype=g["x"].dtype, device=dev)
     topk_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
@@ -614,7 +623,7 @@ def main():
                                                   capacity=cap), it, torch),
         "expert_ffn": time_calls(lambda: moe.moe_expert_ffn(
             g["x"], route["offsets"], route["perm_token"], g["w1"], g["w2"], k, ws=ws, out=eo,
-            capacity=cap), it, torch),
+            capacity=cap, expert_layout=layout), it, torch),
         "combine": time_calls(lambda: moe.moe_combine(eo, route["slot_pos"], topk_gate,
                                                       n_experts=n, out=y), it, torch),
     }
@@ -702,6 +711,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "n_experts": n,
                    "k": k, "train": a.train, "capacity": cap, "gate_order": a.gate_order,
+                   "expert_layout": a.expert_layout,
                    "act_dtype": "bf16" if w.act_dtype == dg.BF16 else "f32",
                    "expert_dtype": "bf16" if w.expert_dtype == dg.BF16 else "f32",
                    "gate_dtype": "bf16" if w.gate_dtype == dg.BF16 else "f32"},

@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH, MOE_BF16, MOE_F32, MoeBatchwiseForward, MoeDims, MoeError, MoeForward, MoeGateOpts,
     MoeHierDims, MoeHierForward, MoeHierOutputs, lib, make_dims, make_opts, moe_aux_losses,
     moe_backward, moe_batchwise_forward, moe_combine, moe_expert_ffn, moe_ffn_timing, moe_ffn_timing_read,
-    moe_forward, moe_forward_noalloc, moe_gate, moe_hier_forward, moe_route, moe_workspace_size,
+    moe_forward, moe_forward_noalloc, moe_gate, moe_hier_forward, moe_pack_expert_weights, moe_route,
+    moe_workspace_size,
     workspace, NOALLOC_SCRATCH_BYTES,
 )

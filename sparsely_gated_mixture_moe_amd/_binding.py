@@ -29,7 +29,8 @@ class MoeDims(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("d_model", ctypes.c_int32),
                 ("d_hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int), ("expert_dtype", ctypes.c_int),
-                ("gate_dtype", ctypes.c_int), ("capacity", ctypes.c_int32)]
+                ("gate_dtype", ctypes.c_int), ("capacity", ctypes.c_int32),
+                ("expert_layout", ctypes.c_int32)]
 
 
 class MoeGateOpts(ctypes.Structure):
@@ -78,6 +79,7 @@ def lib():
         L.moe_gate.argtypes = [D, O, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
         L.moe_route.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
         L.moe_expert_ffn.argtypes = [D, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
+        L.moe_pack_expert_weights.argtypes = [D, _P, _P, _P, _P, _P]
         L.moe_combine.argtypes = [D, _P, _P, _P, _P, _P]
         L.moe_aux_losses.argtypes = [D, O, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, S, _P]
         L.moe_forward.argtypes = [D, O] + [_P] * 19 + [S, _P]
@@ -159,9 +161,26 @@ def moe_ffn_timing_read() -> Tuple[int, float]:
 
 
 def make_dims(tokens: int, d_model: int, d_hidden: int, n_experts: int, k: int,
-              act_dtype: int, expert_dtype: int, gate_dtype: int, capacity: int = 0) -> MoeDims:
+              act_dtype: int, expert_dtype: int, gate_dtype: int, capacity: int = 0,
+              expert_layout: int = 0) -> MoeDims:
     return MoeDims(tokens, d_model, d_hidden, n_experts, k, act_dtype, expert_dtype, gate_dtype,
-                   capacity)
+                   capacity, expert_layout)
+
+
+def moe_pack_expert_weights(w1, w2, stream=None):
+    """(w1_packed, w2_packed): w1 [n, h, d] and w2 [n, d, h] in the packed operand layout
+    (expert_layout=1 of moe_expert_ffn / moe_forward); same shapes, dtypes and bytes, the
+    elements reordered."""
+    _dev(w1, "w1")
+    n, h, d = w1.shape
+    _dev(w2, "w2", w1.dtype, (n, d, h))
+    dims = make_dims(0, d, h, n, 1, _dt(w1), _dt(w1), _dt(w1))
+    w1p = torch.empty_like(w1)
+    w2p = torch.empty_like(w2)
+    st = lib().moe_pack_expert_weights(ctypes.byref(dims), _ptr(w1), _ptr(w2), _ptr(w1p),
+                                       _ptr(w2p), _stream(stream))
+    _check(st, "moe_pack_expert_weights")
+    return w1p, w2p
 
 
 def make_opts(train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
@@ -244,9 +263,10 @@ def moe_route(topk_idx, topk_gate, n_experts: int, *, d_model: int = 64,
 
 def moe_expert_ffn(x, offsets, perm_token, w1, w2, k: int, *, b1=None, b2=None,
                    ws: Optional[torch.Tensor] = None, out=None, capacity: int = 0,
-                   stream=None) -> torch.Tensor:
+                   expert_layout: int = 0, stream=None) -> torch.Tensor:
     """expert_out [B*k, d] in permutation order: E_e(x[perm_token[p]]) per segment (with
-    capacity > 0 only the first `capacity` rows of each segment are computed)."""
+    capacity > 0 only the first `capacity` rows of each segment are computed; with
+    expert_layout=1, w1 and w2 come from moe_pack_expert_weights)."""
     _dev(x, "x")
     B, d = x.shape
     _dev(w1, "w1", x.dtype)
@@ -256,7 +276,7 @@ def moe_expert_ffn(x, offsets, perm_token, w1, w2, k: int, *, b1=None, b2=None,
     _dev(b2, "b2", x.dtype, (n, d))
     _dev(offsets, "offsets", torch.int32, (n + 1,))
     _dev(perm_token, "perm_token", torch.int32, (B * k,))
-    dims = make_dims(B, d, h, n, k, _dt(x), _dt(w1), _dt(x), capacity)
+    dims = make_dims(B, d, h, n, k, _dt(x), _dt(w1), _dt(x), capacity, expert_layout)
     if ws is None:
         ws = workspace(dims, None, x.device)
     if out is None:
@@ -325,7 +345,8 @@ class MoeForward:
     def __init__(self, x_shape, w_gate, w_noise, w1, w2, k: int, *, b1=None, b2=None,
                  gate_bias=None, train: bool = True, noise_floor: float = 1e-2,
                  w_importance: float = 0.1, w_load: float = 0.1, act_dtype=None,
-                 capacity: int = 0, gate_order: int = 0):
+                 capacity: int = 0, gate_order: int = 0, expert_layout: int = 0):
+        """expert_layout=1: w1 and w2 come from moe_pack_expert_weights."""
         B, d = x_shape
         n, h, _ = w1.shape
         self.w_gate, self.w_noise, self.w1, self.w2, self.b1, self.b2 = w_gate, w_noise, w1, w2, b1, b2
@@ -338,7 +359,7 @@ class MoeForward:
         _dev(b2, "b2", w1.dtype, (n, d))
         _dev(gate_bias, "gate_bias", torch.float32, (n,))
         adt = _dt(w1) if act_dtype is None else act_dtype
-        self.dims = make_dims(B, d, h, n, k, adt, _dt(w1), _dt(w_gate), capacity)
+        self.dims = make_dims(B, d, h, n, k, adt, _dt(w1), _dt(w_gate), capacity, expert_layout)
         self.opts = make_opts(train, noise_floor, w_importance, w_load, gate_order)
         dev = w1.device
         self.ws = workspace(self.dims, self.opts, dev)
@@ -374,11 +395,11 @@ class MoeForward:
 def moe_forward(x, w_gate, w_noise, eps, w1, w2, k: int, *, b1=None, b2=None, gate_bias=None,
                 train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
                 w_load: float = 0.1, return_routing: bool = False, capacity: int = 0,
-                gate_order: int = 0, stream=None):
+                gate_order: int = 0, expert_layout: int = 0, stream=None):
     """One call of the whole forward pass; returns a dict of device tensors."""
     f = MoeForward(tuple(x.shape), w_gate, w_noise, w1, w2, k, b1=b1, b2=b2, gate_bias=gate_bias,
                    train=train, noise_floor=noise_floor, w_importance=w_importance, w_load=w_load,
-                   capacity=capacity, gate_order=gate_order)
+                   capacity=capacity, gate_order=gate_order, expert_layout=expert_layout)
     B, n = x.shape[0], w1.shape[0]
     extra = {}
     if return_routing:

@@ -76,6 +76,13 @@ __device__ __forceinline__ U16 ld_unit_g(GPtr p) {
   __builtin_memcpy(&r, &v, 16);
   return r;
 }
+__device__ __forceinline__ U16 ld_unit_g_stream(GPtr p) {
+  const u32x4 v =
+      __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(p));
+  U16 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
 
 template <typename T>
 __device__ __forceinline__ float load_scalar(const void* p, int64_t i) {
@@ -134,7 +141,11 @@ struct FfnUnit {
   int32_t e, seg, rows, hr;
 };
 
-template <typename T, int D>
+// PK: the expert weights are in the packed layout (pack_weights_kernel below):
+// each 16-row x 64-byte operand block is one contiguous kilobyte in lane
+// order, so every wave load reads eight whole 128-byte lines, and the loads
+// are non-temporal (the weights stream through once per unit).
+template <typename T, int D, bool PK>
 __global__ __launch_bounds__((FfnShape<T, D>::NW * 64))
 __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   using S = FfnShape<T, D>;
@@ -200,13 +211,18 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   auto w2_base = [&](int e) {
     return gptr(reinterpret_cast<const T*>(p.w2) + ((int64_t)e * D + 16 * S::CT2 * wave) * h);
   };
-  const uint32_t o1 = (uint32_t)((l16 * D + q * UE) * (int)sizeof(T));
-  const uint32_t o2 = (uint32_t)((l16 * h + q * UE) * (int)sizeof(T));
+  // Natural layout: lane (q, l16) reads row l16, elements [UE q, UE q + UE)
+  // of a 64-byte K-block. Packed: the same 16 bytes sit at lane * 16 of the
+  // block's kilobyte, and one element step along K is 16 elements in memory.
+  const uint32_t o1 = PK ? (uint32_t)(lane * 16) : (uint32_t)((l16 * D + q * UE) * (int)sizeof(T));
+  const uint32_t o2 = PK ? (uint32_t)(lane * 16) : (uint32_t)((l16 * h + q * UE) * (int)sizeof(T));
+  constexpr int64_t KSTEP = PK ? 16 * (int64_t)sizeof(T) : (int64_t)sizeof(T);  // bytes per K element
+  auto ld_w = [&](GPtr a) { return PK ? ld_unit_g_stream(a) : ld_unit_g(a); };
   auto w1_at = [&](GPtr w1w, int hc, int kb) {
-    return ld_unit_g(w1w + ((int64_t)hc * D + kb * 4 * UE) * (int64_t)sizeof(T) + o1);
+    return ld_w(w1w + (int64_t)hc * D * (int64_t)sizeof(T) + kb * 4 * UE * KSTEP + o1);
   };
   auto w2_at = [&](GPtr w2w, int hc, int kb, int i) {
-    return ld_unit_g(w2w + ((int64_t)i * 16 * h + hc + kb * 4 * UE) * (int64_t)sizeof(T) + o2);
+    return ld_w(w2w + (int64_t)i * 16 * h * (int64_t)sizeof(T) + ((int64_t)hc + kb * 4 * UE) * KSTEP + o2);
   };
   // b1 of the lane's 4 hidden units of a chunk travels with the chunk's first
   // W1 fragments, so the bias never waits on a load issued next to its use.
@@ -313,7 +329,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
       // each load's address from one base and an immediate offset instead of
       // keeping a pointer per K-block live across chunks and units
       GPtr w1c = w1w + (int64_t)hc * D * (int64_t)sizeof(T);
-      GPtr w2c = w2w + (int64_t)hc * (int64_t)sizeof(T);
+      GPtr w2c = w2w + (int64_t)hc * KSTEP;
       asm volatile("" : "+s"(w1c), "+s"(w2c));
       f32x4 acc1[S::T16];
 #pragma unroll
@@ -602,7 +618,7 @@ __global__ __launch_bounds__(256) void ffn_split_reduce(FfnParams p, int hsplit)
 template <typename T, int D>
 hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* offsets, int n,
                         int hsplit, int capacity, const int32_t* seg_counts, int seg_stride,
-                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, bool packed) {
   using S = FfnShape<T, D>;
   hipLaunchKernelGGL(ffn_plan, dim3(1), dim3(1024), 0, s, offsets, n, S::BM, hsplit,
                      p.h / S::HC, capacity, seg_counts, seg_stride,
@@ -626,13 +642,36 @@ hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* o
     const hipError_t er = hipEventRecord(ev0, s);
     if (er != hipSuccess) return er;
   }
-  hipLaunchKernelGGL((ffn_kernel<T, D>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
+  if (packed)
+    hipLaunchKernelGGL((ffn_kernel<T, D, true>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((ffn_kernel<T, D, false>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
   if (hsplit > 1)
     hipLaunchKernelGGL((ffn_split_reduce<T, D>), dim3((unsigned)(max_blocks / hsplit)), dim3(256),
                        0, s, p, hsplit);
   const hipError_t el = hipGetLastError();
   if (el != hipSuccess || !ev1) return el;
   return hipEventRecord(ev1, s);
+}
+
+// Packed expert weights. A matrix of R rows (R a multiple of 16) and K
+// columns (64-byte K-blocks of KB = 64 / sizeof(T) elements) is stored as
+// blocks of 16 rows x one K-block, row block by row block and K-block by
+// K-block, each block one kilobyte: lane c * 16 + r of the block holds the
+// 16 bytes at row r, elements [c UE, c UE + UE) of the K-block, the operand
+// a lane of the 16x16 products reads. One thread moves one 16-byte unit.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const char* __restrict__ src,
+                                                           char* __restrict__ dst, int64_t units,
+                                                           int64_t row_bytes) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const int64_t lane = u & 63;
+  const int64_t blk = u >> 6;                 // (row block, K-block), K-block fastest
+  const int64_t kbs = row_bytes / 64;         // K-blocks per row
+  const int64_t rb = blk / kbs, kb = blk - rb * kbs;
+  const int64_t row = rb * 16 + (lane & 15);
+  const int64_t off = row * row_bytes + kb * 64 + (lane >> 4) * 16;
+  st_unit(dst + u * 16, ld_unit(src + off));
 }
 
 template <typename T>
@@ -722,7 +761,7 @@ hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const v
                       const int32_t* offsets, const int32_t* perm_token, const void* w1,
                       const void* b1, const void* w2, const void* b2, void* expert_out,
                       int32_t* blocks, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
-                      int capacity, const int32_t* seg_counts, int seg_stride) {
+                      int capacity, const int32_t* seg_counts, int seg_stride, bool packed) {
   const int64_t mb = ffn_max_blocks(tokens * k, n, d, dt);
   const int hs = ffn_hsplit(tokens * k, n, d, h, dt);
   FfnParams p{x, offsets, perm_token, w1, b1, w2, b2, expert_out, blocks, h, nullptr, 0};
@@ -733,20 +772,30 @@ hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const v
   }
   if (dt == kBF16) {
     switch (d) {
-      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
-      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
-      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
-      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
+      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
     }
   } else {
     switch (d) {
-      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
-      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
-      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
-      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1);
+      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int64_t row_bytes,
+                               hipStream_t s) {
+  const int64_t units = rows * row_bytes / 16;
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const char*>(src), reinterpret_cast<char*>(dst), units,
+                     row_bytes);
+  return hipGetLastError();
 }
 
 }  // namespace moe

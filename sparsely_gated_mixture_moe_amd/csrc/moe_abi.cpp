@@ -51,6 +51,8 @@ moe_status check_dims(const moe_dims* d) {
     return fail(MOE_ERR_INVALID, "k = %d outside [1, n_experts = %d]", d->k, d->n_experts);
   if (d->k > 8) return fail(MOE_ERR_UNSUPPORTED, "k = %d > 8", d->k);
   if (d->capacity < 0) return fail(MOE_ERR_INVALID, "capacity = %d < 0", d->capacity);
+  if (d->expert_layout != 0 && d->expert_layout != 1)
+    return fail(MOE_ERR_INVALID, "expert_layout = %d is neither 0 nor 1", d->expert_layout);
   if (d->tokens * (int64_t)d->k > (int64_t)0x7FFFFFFE)
     return fail(MOE_ERR_INVALID, "tokens * k = %lld does not fit int32 indices",
                 (long long)(d->tokens * d->k));
@@ -239,7 +241,7 @@ moe_status check_hier_dims(const moe_hier_dims* h) {
   if (h->k1 * h->k2 > 8) return fail(MOE_ERR_UNSUPPORTED, "k1 * k2 = %d > 8", h->k1 * h->k2);
   // the leaf layer: the same limits as a flat layer with k = k1 * k2
   moe_dims leaf{h->tokens, h->d_model, h->d_hidden, h->groups * h->group_experts,
-                h->k1 * h->k2, h->act_dtype, h->expert_dtype, h->gate_dtype, 0};
+                h->k1 * h->k2, h->act_dtype, h->expert_dtype, h->gate_dtype, 0, 0};
   return check_dims(&leaf);
 }
 
@@ -481,8 +483,39 @@ moe_status moe_expert_ffn(const moe_dims* dims, const void* x, const int32_t* of
   return device_status(
       moe::launch_ffn(dims->tokens, dims->k, dims->d_model, dims->d_hidden, dims->n_experts,
                       to_dt(dims->act_dtype), x, offsets, perm_token, w1, b1, w2, b2, expert_out,
-                      at<int32_t>(ws, 0), (hipStream_t)stream, nullptr, nullptr, dims->capacity),
+                      at<int32_t>(ws, 0), (hipStream_t)stream, nullptr, nullptr, dims->capacity,
+                      nullptr, 0, dims->expert_layout == 1),
       "moe_expert_ffn");
+}
+
+moe_status moe_pack_expert_weights(const moe_dims* dims, const void* w1, const void* w2,
+                                   void* w1_packed, void* w2_packed, void* stream) {
+  moe_status s;
+  if ((s = check_dims(dims)) != MOE_OK) return s;
+  if (!moe::ffn_supported(dims->d_model, dims->d_hidden, to_dt(dims->act_dtype)))
+    return fail(MOE_ERR_UNSUPPORTED, "pack_expert_weights: unsupported shape");
+  REQ(w1, 16);
+  REQ(w2, 16);
+  REQ(w1_packed, 16);
+  REQ(w2_packed, 16);
+  const int64_t es = dims->expert_dtype == MOE_BF16 ? 2 : 4;
+  const int64_t n = dims->n_experts, d = dims->d_model, h = dims->d_hidden;
+  const int64_t bytes = n * h * d * es;  // each of w1, w2
+  const void* ins[2] = {w1, w2};
+  void* outs[2] = {w1_packed, w2_packed};
+  for (const void* a : ins)
+    for (void* b : outs) {
+      const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+      if (pa < pb + (uintptr_t)bytes && pb < pa + (uintptr_t)bytes)
+        return fail(MOE_ERR_INVALID, "pack_expert_weights: a packed output overlaps an input");
+    }
+  if ((uintptr_t)w1_packed < (uintptr_t)w2_packed + (uintptr_t)bytes &&
+      (uintptr_t)w2_packed < (uintptr_t)w1_packed + (uintptr_t)bytes)
+    return fail(MOE_ERR_INVALID, "pack_expert_weights: w1_packed and w2_packed overlap");
+  hipError_t e = moe::launch_pack_weights(w1, w1_packed, n * h, d * es, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = moe::launch_pack_weights(w2, w2_packed, n * d, h * es, (hipStream_t)stream);
+  return device_status(e, "moe_pack_expert_weights");
 }
 
 moe_status moe_combine(const moe_dims* dims, const void* expert_out, const int32_t* slot_pos,
@@ -583,7 +616,8 @@ moe_status moe_forward(const moe_dims* dims, const moe_gate_opts* opts, const vo
   timing_pair(&t0, &t1);
   e = moe::launch_ffn(dims->tokens, dims->k, dims->d_model, dims->d_hidden, dims->n_experts,
                       to_dt(dims->act_dtype), x, offsets, perm_token, w1, b1, w2, b2, expert_out,
-                      at<int32_t>(ws, L.ffn_blocks), st, t0, t1, dims->capacity);
+                      at<int32_t>(ws, L.ffn_blocks), st, t0, t1, dims->capacity, nullptr, 0,
+                      dims->expert_layout == 1);
   if (e != hipSuccess) return device_status(e, "moe_forward (expert_ffn)");
   e = moe::launch_combine(dims->tokens, dims->k, dims->d_model, to_dt(dims->act_dtype), expert_out,
                           slot_pos, topk_gate, y, st);
@@ -637,6 +671,8 @@ moe_status check_batchwise(const moe_dims* d, const moe_gate_opts* o, int32_t m)
   if ((s = check_dims(d)) != MOE_OK || (s = check_opts(o)) != MOE_OK) return s;
   if (d->capacity != 0)
     return fail(MOE_ERR_UNSUPPORTED, "batchwise gating: capacity must be 0 (m bounds each expert)");
+  if (d->expert_layout != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "batchwise gating: expert_layout must be 0");
   if (o->gate_order != 0)
     return fail(MOE_ERR_UNSUPPORTED, "batchwise gating: gate_order must be 0");
   if (d->tokens > 65536)
@@ -693,6 +729,8 @@ moe_status moe_backward(const moe_dims* dims, const moe_gate_opts* opts, const v
   if ((s = check_dims(dims)) != MOE_OK || (s = check_opts(opts)) != MOE_OK) return s;
   if (dims->capacity != 0)
     return fail(MOE_ERR_UNSUPPORTED, "moe_backward: capacity must be 0");
+  if (dims->expert_layout != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward: expert_layout must be 0");
   if (opts->gate_order != 0)
     return fail(MOE_ERR_UNSUPPORTED, "moe_backward: gate_order must be 0");
   if (!std::isfinite(aux_scale)) return fail(MOE_ERR_INVALID, "aux_scale must be finite");

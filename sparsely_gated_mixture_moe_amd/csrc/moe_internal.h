@@ -142,7 +142,16 @@ hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const v
                       const void* b1, const void* w2, const void* b2, void* expert_out,
                       int32_t* blocks /* [2*max_blocks + 1] */, hipStream_t s,
                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, int capacity = 0,
-                      const int32_t* seg_counts = nullptr, int seg_stride = 0);
+                      const int32_t* seg_counts = nullptr, int seg_stride = 0,
+                      bool packed = false);
+// packed: w1 and w2 are in the packed layout that launch_pack_weights writes.
+
+// Copies a row-major matrix of `rows` rows (a multiple of 16) and row_bytes
+// bytes per row (a multiple of 64) into the packed layout of the expert FFN's
+// weight operands (16-row x 64-byte blocks, one kilobyte each, in the order
+// the product's lanes read them). src and dst must not overlap.
+hipError_t launch_pack_weights(const void* src, void* dst, int64_t rows, int64_t row_bytes,
+                               hipStream_t s);
 
 // Weighted sum.
 hipError_t launch_combine(int64_t tokens, int k, int d, Dt dt, const void* expert_out,

@@ -30,12 +30,12 @@ def test_header_symbols_are_exported():
     assert "moe_forward" in names and len(names) >= 10
     for name in names:
         assert hasattr(L, name), f"{name} declared in moe.h but not exported"
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
 
 
 def dims(**kw):
     base = dict(tokens=1024, d_model=512, d_hidden=1024, n_experts=64, k=4, act_dtype=1,
-                expert_dtype=1, gate_dtype=1, capacity=0)
+                expert_dtype=1, gate_dtype=1, capacity=0, expert_layout=0)
     base.update(kw)
     return B.MoeDims(*[base[f] for f, _ in B.MoeDims._fields_])
 
@@ -268,3 +268,22 @@ def test_backward_pointer_and_workspace_checks():
     assert call_backward(d, o, topk=0) == INVALID and "topk_idx" in last_error()
     assert call_backward(d, o, ws_bytes=need - 256) == WORKSPACE and "needed" in last_error()
     assert call_backward(d, o, ws=FAKE + 16, ws_bytes=need) == INVALID
+
+
+def test_pack_expert_weights_and_layout_rejections():
+    L = B.lib()
+    d = dims()
+    nbytes = 64 * 1024 * 512 * 2  # each of w1, w2 at these dims
+    w1, w2, p1, p2 = FAKE, FAKE + nbytes, FAKE + 2 * nbytes, FAKE + 3 * nbytes
+
+    def pack(*ptrs, dd=d):
+        return L.moe_pack_expert_weights(ctypes.byref(dd), *[P(v) for v in ptrs], None)
+
+    assert pack(w1, w2, p1 + 8, p2) == INVALID and "16-byte" in last_error()
+    assert pack(w1, w2, w1 + 16, p2) == INVALID and "overlaps an input" in last_error()
+    assert pack(w1, w2, p1, w2 + nbytes - 16) == INVALID and "overlaps an input" in last_error()
+    assert pack(w1, w2, p1, p1 + 1024) == INVALID and "overlap" in last_error()
+    assert pack(w1, w2, p1, p2, dd=dims(d_model=96)) == UNSUPPORTED
+    assert pack(w1, w2, p1, p2, dd=dims(expert_layout=2)) == INVALID
+    assert "expert_layout" in last_error()
+    assert call_gate(dims(expert_layout=-1), opts()) == INVALID

@@ -1,0 +1,127 @@
+"""GPU checks of the packed expert-weight layout (moe_pack_expert_weights and
+expert_layout = 1), through the C ABI.
+
+The layout is a storage format of E_i's weights (eq 1, section "How a
+mixture-of-experts layer works"): packing moves bytes, so the packed tensors
+are compared byte for byte with the layout the header defines, rebuilt here
+with NumPy; the expert products then read the same values in the same order,
+so their outputs are compared bit for bit with the natural layout's, and
+against the oracle at the usual bar."""
+import numpy as np
+import pytest
+
+import datagen as dg
+import oracle
+from parity import announce, gpu_inputs, out_tol, rel_err, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import sparsely_gated_mixture_moe_amd as moe  # noqa: E402
+
+FLOOR = 1e-2
+
+
+def packed_reference(w: np.ndarray) -> np.ndarray:
+    """The packed byte image of a stack of row-major matrices w [n, R, K]:
+    16-row x 64-byte blocks, row blocks outer and column blocks inner, byte
+    16 (16 c + r) + b of a block = byte 16 c + b of the block's row r."""
+    raw = np.ascontiguousarray(w).view(np.uint8)
+    n, R, KB = raw.shape
+    blocks = raw.reshape(n, R // 16, 16, KB // 64, 4, 16)   # e, rb, r, kb, c, byte
+    return np.ascontiguousarray(blocks.transpose(0, 1, 3, 4, 2, 5)).reshape(-1)
+
+
+def _bytes(t) -> np.ndarray:
+    return to_host(t.contiguous().view(torch.uint8)).reshape(-1)
+
+
+@pytest.mark.parametrize("dt,n,h,d", [(torch.bfloat16, 3, 128, 64), (torch.float32, 2, 256, 128),
+                                      (torch.bfloat16, 2, 1024, 512), (torch.float32, 1, 128, 512)])
+def test_pack_layout(dt, n, h, d):
+    announce(f"moe_pack_expert_weights {dt} n={n} h={h} d={d}")
+    gen = torch.Generator().manual_seed(n * 1000 + h + d)
+    w1 = torch.randn((n, h, d), generator=gen).to(dt).cuda()
+    w2 = torch.randn((n, d, h), generator=gen).to(dt).cuda()
+    p1, p2 = moe.moe_pack_expert_weights(w1, w2)
+    torch.cuda.synchronize()
+    for w, p in ((w1, p1), (w2, p2)):
+        host = to_host(w.contiguous().view(torch.uint8)).reshape(w.shape[0], w.shape[1], -1)
+        assert np.array_equal(_bytes(p), packed_reference(host))
+
+
+FFN_CASES = [
+    ("tiny_fp32", {"tokens": 300}, True),
+    ("tiny_fp32", {"tokens": 333, "n_experts": 37, "k": 3, "d_model": 128}, False),
+    ("flat_fp32_n32", {"tokens": 1000}, True),
+    ("zipf_bf16_n256", {"tokens": 4100, "n_experts": 16, "k": 3, "d_hidden": 768}, True),
+    ("flat_bf16_n4096", {"tokens": 2000, "n_experts": 64, "d_model": 256}, False),
+    ("flat_bf16_n4096", {"tokens": 1500, "n_experts": 128}, True),
+]
+
+
+@pytest.mark.parametrize("case", FFN_CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(FFN_CASES)])
+def test_packed_expert_ffn(case):
+    name, kw, bias = case
+    w = dg.workload(name, **kw)
+    announce(f"moe_expert_ffn packed {w.name} {kw} bias={bias}")
+    inp = dg.make_inputs(w, with_bias=bias)
+    ref = oracle.gate(inp, w.k, train=True, noise_floor=FLOOR)
+    rt = oracle.route(ref["topk_idx"], ref["topk_gate"], w.n_experts)
+    g = gpu_inputs(inp)
+    offsets, perm = to_device(rt["offsets"]), to_device(rt["perm_token"])
+    p1, p2 = moe.moe_pack_expert_weights(g["w1"], g["w2"])
+    nat = moe.moe_expert_ffn(g["x"], offsets, perm, g["w1"], g["w2"], w.k, b1=g.get("b1"),
+                             b2=g.get("b2"))
+    pk = moe.moe_expert_ffn(g["x"], offsets, perm, p1, p2, w.k, b1=g.get("b1"), b2=g.get("b2"),
+                            expert_layout=1)
+    torch.cuda.synchronize()
+    assert torch.equal(nat.view(torch.uint8), pk.view(torch.uint8))
+    experts = np.repeat(np.arange(w.n_experts, dtype=np.int32), rt["counts"])
+    err = rel_err(to_host(pk), oracle.expert_pairs(inp, rt["perm_token"], experts))
+    print(w.name, kw, "packed expert_out err", err)
+    assert err <= out_tol(w.act_dtype == dg.BF16)
+
+
+# (workload, overrides, train, expert biases)
+FWD_CASES = [
+    ("flat_bf16_n4096", {"tokens": 700}, True, True),
+    ("flat_bf16_n4096", {"tokens": 3, "n_experts": 512}, True, False),  # split units (few rows)
+    ("zipf_bf16_n256", {"tokens": 3000}, True, False),
+    ("flat_fp32_n32", {"tokens": 900}, False, True),
+    ("flat_bf16_n4096", {"tokens": 64, "n_experts": 256, "capacity": 1}, True, False),
+    ("flat_bf16_n4096", {}, True, False),                                # the benchmark's size
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(FWD_CASES)])
+def test_packed_forward(case):
+    """moe_forward with packed weights: y, the selection and the losses
+    bit-identical to the natural layout's; y against the oracle on sampled rows."""
+    name, kw, train, bias = case
+    kw = dict(kw)
+    cap = kw.pop("capacity", 0)
+    w = dg.workload(name, **kw)
+    B, d, n, k = w.tokens, w.d_model, w.n_experts, w.k
+    announce(f"moe_forward packed {w.name} {kw} capacity={cap}")
+    inp = dg.make_inputs(w, with_bias=bias)
+    g = gpu_inputs(inp)
+    p1, p2 = moe.moe_pack_expert_weights(g["w1"], g["w2"])
+    outs = []
+    for layout, (w1, w2) in ((0, (g["w1"], g["w2"])), (1, (p1, p2))):
+        outs.append(moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], w1, w2, k,
+                                    b1=g.get("b1"), b2=g.get("b2"), gate_bias=g.get("gate_bias"),
+                                    train=train, capacity=cap, return_routing=True,
+                                    expert_layout=layout))
+    torch.cuda.synchronize()
+    a, b = outs
+    for key in ("y", "importance", "load", "losses", "topk_idx", "topk_gate", "counts"):
+        assert torch.equal(a[key].view(torch.uint8), b[key].view(torch.uint8)), key
+    if cap:  # capacity's y is checked against the oracle with the natural layout
+        return
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, B - 1], rng.choice(B, min(B, 64), replace=False)]))
+    y_ref = oracle.y_rows(inp, k, rows=rows, train=train, noise_floor=FLOOR)
+    err = rel_err(to_host(b["y"])[rows], y_ref)
+    print(w.name, kw, "packed y err", err)
+    assert err <= out_tol(w.act_dtype == dg.BF16)
