@@ -509,9 +509,11 @@ def main():
     ap.add_argument("--gate-order", type=int, default=0, choices=(0, 1),
                     help="0: softmax over the kept k (the pages); 1: softmax over all n, then "
                          "the kept k (Switch's order)")
-    ap.add_argument("--expert-layout", default="natural", choices=("natural", "packed"),
-                    help="packed: the expert weights are converted once, before timing, to the "
-                         "matrix-core operand layout (moe_pack_expert_weights, expert_layout=1)")
+    ap.add_argument("--expert-layout", default="packed", choices=("natural", "packed"),
+                    help="packed (default): the expert weights are converted once, before timing, to "
+                         "the matrix-core operand layout (moe_pack_expert_weights, "
+                         "expert_layout=1); the hierarchical, batchwise and backward lines read "
+                         "the natural layout")
     ap.add_argument("--gating", default="topk", choices=("topk", "batchwise"),
                     help="batchwise: every expert takes its k B / n best rows of the batch "
                          "(moe_batchwise_forward) instead of every token its k best experts")
@@ -554,8 +556,8 @@ def main():
     w = dg.WORKLOADS[a.workload]
     if a.tokens > 0:
         w = dg.workload(a.workload, tokens=a.tokens)
-    if a.expert_layout != "natural" and (w.hierarchical or a.gating != "topk" or a.backward):
-        raise SystemExit("--expert-layout packed applies to the flat top-k forward only")
+    if w.hierarchical or a.gating != "topk" or a.backward:
+        a.expert_layout = "natural"  # the packed layout is read by the flat top-k forward only
     if w.hierarchical:
         bench_hier(a, w)
         return

@@ -143,9 +143,11 @@ struct FfnUnit {
 
 // PK: the expert weights are in the packed layout (pack_weights_kernel below):
 // each 16-row x 64-byte operand block is one contiguous kilobyte in lane
-// order, so every wave load reads eight whole 128-byte lines, and the loads
-// are non-temporal (the weights stream through once per unit).
-template <typename T, int D, bool PK>
+// order, so every wave load reads eight whole 128-byte lines. NT (packed
+// only): the weight loads are non-temporal, for batches in which each
+// expert's weights are read about once (no unit of the same expert follows
+// to find them in the caches).
+template <typename T, int D, bool PK, bool NT>
 __global__ __launch_bounds__((FfnShape<T, D>::NW * 64))
 __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   using S = FfnShape<T, D>;
@@ -217,7 +219,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_kernel(FfnParams p) {
   const uint32_t o1 = PK ? (uint32_t)(lane * 16) : (uint32_t)((l16 * D + q * UE) * (int)sizeof(T));
   const uint32_t o2 = PK ? (uint32_t)(lane * 16) : (uint32_t)((l16 * h + q * UE) * (int)sizeof(T));
   constexpr int64_t KSTEP = PK ? 16 * (int64_t)sizeof(T) : (int64_t)sizeof(T);  // bytes per K element
-  auto ld_w = [&](GPtr a) { return PK ? ld_unit_g_stream(a) : ld_unit_g(a); };
+  static_assert(PK || !NT, "non-temporal weight loads read whole lines only when packed");
+  auto ld_w = [&](GPtr a) { return NT ? ld_unit_g_stream(a) : ld_unit_g(a); };
   auto w1_at = [&](GPtr w1w, int hc, int kb) {
     return ld_w(w1w + (int64_t)hc * D * (int64_t)sizeof(T) + kb * 4 * UE * KSTEP + o1);
   };
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(256) void ffn_split_reduce(FfnParams p, int hsplit)
 
 
 template <typename T, int D>
-hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* offsets, int n,
+hipError_t ffn_launch_t(int64_t rows, int64_t max_blocks, const FfnParams& p, const int32_t* offsets, int n,
                         int hsplit, int capacity, const int32_t* seg_counts, int seg_stride,
                         hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, bool packed) {
   using S = FfnShape<T, D>;
@@ -642,10 +645,18 @@ hipError_t ffn_launch_t(int64_t max_blocks, const FfnParams& p, const int32_t* o
     const hipError_t er = hipEventRecord(ev0, s);
     if (er != hipSuccess) return er;
   }
-  if (packed)
-    hipLaunchKernelGGL((ffn_kernel<T, D, true>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
+  // Streamed weights: at most one unit per expert on average (the rows the
+  // workspace is sized for over the experts fit one unit each).
+  const bool once = rows <= (int64_t)n * S::BM;
+  if (packed && once)
+    hipLaunchKernelGGL((ffn_kernel<T, D, true, true>), dim3((unsigned)grid), dim3(S::NW * 64), 0,
+                       s, p);
+  else if (packed)
+    hipLaunchKernelGGL((ffn_kernel<T, D, true, false>), dim3((unsigned)grid), dim3(S::NW * 64), 0,
+                       s, p);
   else
-    hipLaunchKernelGGL((ffn_kernel<T, D, false>), dim3((unsigned)grid), dim3(S::NW * 64), 0, s, p);
+    hipLaunchKernelGGL((ffn_kernel<T, D, false, false>), dim3((unsigned)grid), dim3(S::NW * 64), 0,
+                       s, p);
   if (hsplit > 1)
     hipLaunchKernelGGL((ffn_split_reduce<T, D>), dim3((unsigned)(max_blocks / hsplit)), dim3(256),
                        0, s, p, hsplit);
@@ -772,17 +783,17 @@ hipError_t launch_ffn(int64_t tokens, int k, int d, int h, int n, Dt dt, const v
   }
   if (dt == kBF16) {
     switch (d) {
-      case 64: return ffn_launch_t<bf16, 64>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
-      case 128: return ffn_launch_t<bf16, 128>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
-      case 256: return ffn_launch_t<bf16, 256>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
-      case 512: return ffn_launch_t<bf16, 512>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 64: return ffn_launch_t<bf16, 64>(tokens * k, mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 128: return ffn_launch_t<bf16, 128>(tokens * k, mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 256: return ffn_launch_t<bf16, 256>(tokens * k, mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 512: return ffn_launch_t<bf16, 512>(tokens * k, mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
     }
   } else {
     switch (d) {
-      case 64: return ffn_launch_t<float, 64>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
-      case 128: return ffn_launch_t<float, 128>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
-      case 256: return ffn_launch_t<float, 256>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
-      case 512: return ffn_launch_t<float, 512>(mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 64: return ffn_launch_t<float, 64>(tokens * k, mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 128: return ffn_launch_t<float, 128>(tokens * k, mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 256: return ffn_launch_t<float, 256>(tokens * k, mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
+      case 512: return ffn_launch_t<float, 512>(tokens * k, mb, p, offsets, n, hs, capacity, seg_counts, seg_stride, s, ev0, ev1, packed);
     }
   }
   return hipErrorInvalidValue;
