@@ -353,7 +353,7 @@ def bench_hier(a, w):
     print(json.dumps(result), flush=True)
 
 
-def bench_batchwise(a, w, g, moe, torch):
+def bench_batchwise(a, w, g, moe, torch, layout=0):
     """Batchwise gating (section "What the paper measured"): one step = one
     moe_batchwise_forward call (expert-major scores, each expert's top m =
     k B / n rows, token lists, expert FFNs, softmax and weighted sum,
@@ -361,7 +361,8 @@ def bench_batchwise(a, w, g, moe, torch):
     B, d, h, n, k = w.tokens, w.d_model, w.d_hidden, w.n_experts, w.k
     m = max(1, k * B // n)
     f = moe.MoeBatchwiseForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], m,
-                                gate_bias=g.get("gate_bias"), train=bool(a.train))
+                                gate_bias=g.get("gate_bias"), train=bool(a.train),
+                                expert_layout=layout)
     y = torch.empty((B, d), dtype=g["x"].dtype, device=g["x"].device)
 
     def step():
@@ -396,7 +397,8 @@ def bench_batchwise(a, w, g, moe, torch):
         "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if w.act_dtype == 1 else "f32", "data": "synthetic",
         "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "n_experts": n,
-                   "k": k, "gating": "batchwise", "rows_per_expert": m, "train": a.train},
+                   "k": k, "gating": "batchwise", "rows_per_expert": m, "train": a.train,
+                   "expert_layout": a.expert_layout},
         "roofline": {"kernel": "ffn_kernel (expert FFN)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
@@ -556,8 +558,8 @@ def main():
     w = dg.WORKLOADS[a.workload]
     if a.tokens > 0:
         w = dg.workload(a.workload, tokens=a.tokens)
-    if w.hierarchical or a.gating != "topk" or a.backward:
-        a.expert_layout = "natural"  # the packed layout is read by the flat top-k forward only
+    if w.hierarchical or a.backward:
+        a.expert_layout = "natural"  # the packed layout is read by the flat forward passes only
     if w.hierarchical:
         bench_hier(a, w)
         return
@@ -569,17 +571,17 @@ def main():
     g = {key: to_device(v, torch, np) for key, v in inp.items()}
     torch.cuda.synchronize()
 
+    layout = 1 if a.expert_layout == "packed" else 0
+    if layout:  # a one-time conversion of the weights, outside the timed steps
+        g["w1"], g["w2"] = moe.moe_pack_expert_weights(g["w1"], g["w2"])
+        torch.cuda.synchronize()
     if a.gating == "batchwise":
-        bench_batchwise(a, w, g, moe, torch)
+        bench_batchwise(a, w, g, moe, torch, layout)
         return
     if a.backward:
         bench_backward(a, w, g, moe, torch, np, dg)
         return
     cap = int(np.ceil(a.capacity_factor * B * k / n)) if a.capacity_factor > 0 else 0
-    layout = 1 if a.expert_layout == "packed" else 0
-    if layout:  # a one-time conversion of the weights, outside the timed steps
-        g["w1"], g["w2"] = moe.moe_pack_expert_weights(g["w1"], g["w2"])
-        torch.cuda.synchronize()
     f = moe.MoeForward((B, d), g["w_gate"], g["w_noise"], g["w1"], g["w2"], k,
                        gate_bias=g.get("gate_bias"), train=bool(a.train), capacity=cap,
                        gate_order=a.gate_order, expert_layout=layout)

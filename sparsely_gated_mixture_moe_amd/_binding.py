@@ -536,7 +536,7 @@ class MoeBatchwiseForward:
     def __init__(self, x_shape, w_gate, w_noise, w1, w2, rows_per_expert: int, *, b1=None,
                  b2=None, gate_bias=None, expert_threshold=None, train: bool = True,
                  noise_floor: float = 1e-2, w_importance: float = 0.1, w_load: float = 0.1,
-                 act_dtype=None):
+                 act_dtype=None, expert_layout: int = 0):
         B, d = x_shape
         n, h, _ = w1.shape
         self.w_gate, self.w_noise, self.w1, self.w2, self.b1, self.b2 = w_gate, w_noise, w1, w2, b1, b2
@@ -551,7 +551,7 @@ class MoeBatchwiseForward:
         _dev(expert_threshold, "expert_threshold", torch.float32, (n,))
         adt = _dt(w1) if act_dtype is None else act_dtype
         self.m = int(rows_per_expert)
-        self.dims = make_dims(B, d, h, n, 1, adt, _dt(w1), _dt(w_gate))
+        self.dims = make_dims(B, d, h, n, 1, adt, _dt(w1), _dt(w_gate), 0, expert_layout)
         self.opts = make_opts(train, noise_floor, w_importance, w_load)
         size = lib().moe_batchwise_workspace_size(ctypes.byref(self.dims), ctypes.byref(self.opts),
                                                   self.m)
@@ -589,13 +589,14 @@ class MoeBatchwiseForward:
 def moe_batchwise_forward(x, w_gate, w_noise, eps, w1, w2, rows_per_expert: int, *, b1=None,
                           b2=None, gate_bias=None, expert_threshold=None, train: bool = True,
                           noise_floor: float = 1e-2, w_importance: float = 0.1,
-                          w_load: float = 0.1, stream=None):
+                          w_load: float = 0.1, expert_layout: int = 0, stream=None):
     """One call of the batchwise-gated forward pass; returns a dict of device
     tensors (y, counts, sel_token, sel_score, sel_gate [n * m], importance,
     load, losses)."""
     f = MoeBatchwiseForward(tuple(x.shape), w_gate, w_noise, w1, w2, rows_per_expert, b1=b1, b2=b2,
                             gate_bias=gate_bias, expert_threshold=expert_threshold, train=train,
-                            noise_floor=noise_floor, w_importance=w_importance, w_load=w_load)
+                            noise_floor=noise_floor, w_importance=w_importance, w_load=w_load,
+                            expert_layout=expert_layout)
     y = f(x, eps, stream=stream)
     return {"y": y, "counts": f.counts, "sel_token": f.sel_token, "sel_score": f.sel_score,
             "sel_gate": f.sel_gate, "importance": f.importance, "load": f.load,

@@ -602,7 +602,7 @@ hipError_t launch_batchwise(const BatchwiseLaunch& b, hipStream_t s, hipEvent_t 
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   e = launch_ffn(slots, 1, b.gate.d, b.h, n, b.act_dt, b.gate.x, nullptr, b.sel_token, b.w1, b.b1,
-                 b.w2, b.b2, b.expert_out, b.ffn_blocks, s, ev0, ev1, 0, b.counts, m);
+                 b.w2, b.b2, b.expert_out, b.ffn_blocks, s, ev0, ev1, 0, b.counts, m, b.packed);
   if (e != hipSuccess) return e;
   if (B > 0) {
     const dim3 grid((unsigned)((B + 3) / 4));

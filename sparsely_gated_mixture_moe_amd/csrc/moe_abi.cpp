@@ -671,8 +671,6 @@ moe_status check_batchwise(const moe_dims* d, const moe_gate_opts* o, int32_t m)
   if ((s = check_dims(d)) != MOE_OK || (s = check_opts(o)) != MOE_OK) return s;
   if (d->capacity != 0)
     return fail(MOE_ERR_UNSUPPORTED, "batchwise gating: capacity must be 0 (m bounds each expert)");
-  if (d->expert_layout != 0)
-    return fail(MOE_ERR_UNSUPPORTED, "batchwise gating: expert_layout must be 0");
   if (o->gate_order != 0)
     return fail(MOE_ERR_UNSUPPORTED, "batchwise gating: gate_order must be 0");
   if (d->tokens > 65536)
@@ -842,6 +840,7 @@ moe_status moe_batchwise_forward(const moe_dims* dims, const moe_gate_opts* opts
   b.b1 = b1;
   b.w2 = w2;
   b.b2 = b2;
+  b.packed = dims->expert_layout == 1;
   b.w_importance = opts->w_importance;
   b.w_load = opts->w_load;
   b.y = y;

@@ -180,6 +180,7 @@ struct BatchwiseLaunch {
   int h = 0;
   Dt act_dt = kBF16;
   const void *w1 = nullptr, *b1 = nullptr, *w2 = nullptr, *b2 = nullptr;
+  bool packed = false;  // w1, w2 in the packed layout of launch_pack_weights
   float w_importance = 0.f, w_load = 0.f;
   // outputs
   void* y = nullptr;

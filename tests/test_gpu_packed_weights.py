@@ -125,3 +125,22 @@ def test_packed_forward(case):
     err = rel_err(to_host(b["y"])[rows], y_ref)
     print(w.name, kw, "packed y err", err)
     assert err <= out_tol(w.act_dtype == dg.BF16)
+
+
+@pytest.mark.parametrize("B,n,m,train", [(700, 64, 44, True), (4096, 512, 32, False)])
+def test_packed_batchwise(B, n, m, train):
+    """moe_batchwise_forward with packed weights: outputs bit-identical to the
+    natural layout's (the batchwise path itself is checked against the oracle
+    with natural weights)."""
+    w = dg.workload("flat_bf16_n4096", tokens=B, n_experts=n)
+    announce(f"moe_batchwise_forward packed B={B} n={n} m={m} train={train}")
+    inp = dg.make_inputs(w, with_bias=True)
+    g = gpu_inputs(inp)
+    p1, p2 = moe.moe_pack_expert_weights(g["w1"], g["w2"])
+    outs = [moe.moe_batchwise_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], w1, w2, m,
+                                      b1=g.get("b1"), b2=g.get("b2"), train=train,
+                                      expert_layout=layout)
+            for layout, (w1, w2) in ((0, (g["w1"], g["w2"])), (1, (p1, p2)))]
+    torch.cuda.synchronize()
+    for key in ("y", "counts", "sel_token", "sel_gate", "importance", "load", "losses"):
+        assert torch.equal(outs[0][key].view(torch.uint8), outs[1][key].view(torch.uint8)), key
