@@ -285,8 +285,12 @@ def bench_hier(a, w):
          "w1": upload(w, "w1", (n, h, d), torch, dg), "w2": upload(w, "w2", (n, d, h), torch, dg)}
     torch.cuda.synchronize()
     log(f"inputs resident after {time.time() - t0:.1f} s")
+    layout = 1 if a.expert_layout == "packed" else 0
+    if layout:  # a one-time conversion of the leaf weights, outside the timed steps
+        g["w1"], g["w2"] = moe.moe_pack_expert_weights(g["w1"], g["w2"])
+        torch.cuda.synchronize()
     f = moe.MoeHierForward((B, d), g["w_gate"], g["w_noise"], g["w_gate2"], g["w_noise2"],
-                           g["w1"], g["w2"], k1, k2, train=True)
+                           g["w1"], g["w2"], k1, k2, train=True, expert_layout=layout)
     dev = g["x"].device
     y = torch.empty((B, d), dtype=g["x"].dtype, device=dev)
     leaf_idx = torch.empty((B, K), dtype=torch.int32, device=dev)
@@ -336,7 +340,8 @@ def bench_hier(a, w):
         "warmup": a.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "tokens": B, "d_model": d, "d_hidden": h, "groups": ga,
-                   "group_experts": gb, "k1": k1, "k2": k2, "train": 1},
+                   "group_experts": gb, "k1": k1, "k2": k2, "train": 1,
+                   "expert_layout": a.expert_layout},
         "roofline": {"kernel": "ffn_kernel (expert FFN over the leaves)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
@@ -558,8 +563,8 @@ def main():
     w = dg.WORKLOADS[a.workload]
     if a.tokens > 0:
         w = dg.workload(a.workload, tokens=a.tokens)
-    if w.hierarchical or a.backward:
-        a.expert_layout = "natural"  # the packed layout is read by the flat forward passes only
+    if a.backward:
+        a.expert_layout = "natural"  # the packed layout is read by the forward passes only
     if w.hierarchical:
         bench_hier(a, w)
         return

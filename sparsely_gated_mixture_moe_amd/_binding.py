@@ -44,7 +44,7 @@ class MoeHierDims(ctypes.Structure):
                 ("d_hidden", ctypes.c_int32), ("groups", ctypes.c_int32),
                 ("group_experts", ctypes.c_int32), ("k1", ctypes.c_int32), ("k2", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int), ("expert_dtype", ctypes.c_int),
-                ("gate_dtype", ctypes.c_int)]
+                ("gate_dtype", ctypes.c_int), ("expert_layout", ctypes.c_int32)]
 
 
 _HIER_OUT_FIELDS = ("topk_idx", "topk_gate", "counts", "group_idx", "group_gate", "group_thresh",
@@ -611,7 +611,7 @@ class MoeHierForward:
 
     def __init__(self, x_shape, w_gate1, w_noise1, w_gate2, w_noise2, w1, w2, k1: int, k2: int, *,
                  b1=None, b2=None, train: bool = True, noise_floor: float = 1e-2,
-                 w_importance: float = 0.1, w_load: float = 0.1):
+                 w_importance: float = 0.1, w_load: float = 0.1, expert_layout: int = 0):
         B, d = x_shape
         a, b, _ = w_gate2.shape
         n, h, _ = w1.shape
@@ -626,7 +626,8 @@ class MoeHierForward:
         _dev(b1, "b1", w1.dtype, (n, h))
         _dev(b2, "b2", w1.dtype, (n, d))
         self.w = (w_gate1, w_noise1, w_gate2, w_noise2, w1, b1, w2, b2)
-        self.dims = MoeHierDims(B, d, h, a, b, k1, k2, _dt(w1), _dt(w1), _dt(w_gate1))
+        self.dims = MoeHierDims(B, d, h, a, b, k1, k2, _dt(w1), _dt(w1), _dt(w_gate1),
+                                expert_layout)
         self.opts = make_opts(train, noise_floor, w_importance, w_load)
         dev = w1.device
         nbytes = int(lib().moe_hier_workspace_size(ctypes.byref(self.dims), ctypes.byref(self.opts)))
@@ -681,12 +682,12 @@ class MoeHierForward:
 def moe_hier_forward(x, w_gate1, w_noise1, eps1, w_gate2, w_noise2, eps2, w1, w2, k1: int, k2: int,
                      *, b1=None, b2=None, train: bool = True, noise_floor: float = 1e-2,
                      w_importance: float = 0.1, w_load: float = 0.1, return_all: bool = False,
-                     stream=None):
+                     expert_layout: int = 0, stream=None):
     """One call of the hierarchical forward pass; returns a dict of device tensors
     (with ``return_all`` also every optional output of the C call)."""
     f = MoeHierForward(tuple(x.shape), w_gate1, w_noise1, w_gate2, w_noise2, w1, w2, k1, k2,
                        b1=b1, b2=b2, train=train, noise_floor=noise_floor,
-                       w_importance=w_importance, w_load=w_load)
+                       w_importance=w_importance, w_load=w_load, expert_layout=expert_layout)
     extra = {}
     if return_all:
         extra = {name: torch.empty(shp, dtype=dt, device=x.device)

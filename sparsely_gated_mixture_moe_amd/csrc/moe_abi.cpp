@@ -227,6 +227,8 @@ moe_status check_gate_args(const moe_dims* d, const moe_gate_opts* o, const void
 
 moe_status check_hier_dims(const moe_hier_dims* h) {
   if (!h) return fail(MOE_ERR_INVALID, "dims is NULL");
+  if (h->expert_layout != 0 && h->expert_layout != 1)
+    return fail(MOE_ERR_INVALID, "expert_layout = %d is neither 0 nor 1", h->expert_layout);
   if (h->groups < 1 || h->group_experts < 1)
     return fail(MOE_ERR_INVALID, "groups = %d and group_experts = %d must be positive",
                 h->groups, h->group_experts);
@@ -980,7 +982,8 @@ moe_status moe_hier_forward(const moe_hier_dims* dims, const moe_gate_opts* opts
   hipEvent_t t0, t1;
   timing_pair(&t0, &t1);
   e = moe::launch_ffn(B, K, dims->d_model, dims->d_hidden, n, x_dt, x, offsets, perm_token, w1, b1,
-                      w2, b2, expert_out, at<int32_t>(ws, L.ffn_blocks), st, t0, t1);
+                      w2, b2, expert_out, at<int32_t>(ws, L.ffn_blocks), st, t0, t1, 0, nullptr,
+                      0, dims->expert_layout == 1);
   if (e != hipSuccess) return device_status(e, "moe_hier_forward (expert_ffn)");
   e = moe::launch_combine(B, K, dims->d_model, x_dt, expert_out, slot_pos, topk_gate, y, st);
   if (e != hipSuccess) return device_status(e, "moe_hier_forward (combine)");

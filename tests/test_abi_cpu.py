@@ -147,7 +147,7 @@ def test_status_strings():
 
 def hdims(**kw):
     base = dict(tokens=1024, d_model=512, d_hidden=1024, groups=16, group_experts=32, k1=2, k2=2,
-                act_dtype=1, expert_dtype=1, gate_dtype=1)
+                act_dtype=1, expert_dtype=1, gate_dtype=1, expert_layout=0)
     base.update(kw)
     return B.MoeHierDims(*[base[f] for f, _ in B.MoeHierDims._fields_])
 

@@ -144,3 +144,28 @@ def test_packed_batchwise(B, n, m, train):
     torch.cuda.synchronize()
     for key in ("y", "counts", "sel_token", "sel_gate", "importance", "load", "losses"):
         assert torch.equal(outs[0][key].view(torch.uint8), outs[1][key].view(torch.uint8)), key
+
+
+@pytest.mark.parametrize("B,a,b,k1,k2,d,h,dt", [(1000, 8, 32, 2, 2, 128, 256, dg.BF16),
+                                                (300, 4, 6, 2, 2, 64, 128, dg.F32),
+                                                (4096, 32, 64, 2, 2, 512, 128, dg.BF16)])
+def test_packed_hier_forward(B, a, b, k1, k2, d, h, dt):
+    """moe_hier_forward with packed leaf weights: every output bit-identical
+    to the natural layout's (the hierarchical path itself is checked against
+    the oracle with natural weights)."""
+    w = dg.workload("hier_bf16_16384", tokens=B, d_model=d, d_hidden=h, groups=a,
+                    group_experts=b, k1=k1, k2=k2, n_experts=a * b, k=k1 * k2,
+                    act_dtype=dt, expert_dtype=dt, gate_dtype=dt)
+    announce(f"moe_hier_forward packed B={B} a={a} b={b} k={k1}x{k2} d={d} h={h}")
+    inp = dg.make_hier_inputs(w, with_bias=True)
+    g = gpu_inputs(inp)
+    p1, p2 = moe.moe_pack_expert_weights(g["w1"], g["w2"])
+    outs = [moe.moe_hier_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w_gate2"],
+                                 g["w_noise2"], g["eps2"], w1, w2, k1, k2, b1=g.get("b1"),
+                                 b2=g.get("b2"), train=True, noise_floor=FLOOR, return_all=True,
+                                 expert_layout=layout)
+            for layout, (w1, w2) in ((0, (g["w1"], g["w2"])), (1, (p1, p2)))]
+    torch.cuda.synchronize()
+    assert outs[0].keys() == outs[1].keys()
+    for key in outs[0]:
+        assert torch.equal(outs[0][key].view(torch.uint8), outs[1][key].view(torch.uint8)), key
