@@ -321,7 +321,8 @@ def bench_hier(a, w):
         "route_leaves": time_calls(lambda: moe.moe_route(leaf_idx, leaf_gate, n, d_model=d, ws=ws),
                                    it, torch),
         "expert_ffn": time_calls(lambda: moe.moe_expert_ffn(
-            g["x"], route["offsets"], route["perm_token"], g["w1"], g["w2"], K, ws=ws, out=eo),
+            g["x"], route["offsets"], route["perm_token"], g["w1"], g["w2"], K, ws=ws, out=eo,
+            expert_layout=layout),
             it, torch),
     }
     log("stages (ms): " + ", ".join(f"{k_}={v:.3f}" for k_, v in stages.items()))
