@@ -423,7 +423,7 @@ def moe_forward_noalloc(x, w_gate, w_noise, eps, w1, w2, k: int, *, y=None, impo
                         train: bool = True, noise_floor: float = 1e-2, w_importance: float = 0.1,
                         w_load: float = 0.1, capacity: int = 0, gate_order: int = 0,
                         topk_idx=None, topk_gate=None, thresh=None, counts=None, perm_token=None,
-                        stream=None):
+                        expert_layout: int = 0, stream=None):
     """The whole forward pass through ``moe_forward_noalloc``: the library
     takes its workspace from its static per-device scratch (no allocation by
     the library; outputs not given are allocated here by torch). Returns a dict
@@ -453,7 +453,7 @@ def moe_forward_noalloc(x, w_gate, w_noise, eps, w1, w2, k: int, *, y=None, impo
                              ("counts", counts, torch.int32, (n,)),
                              ("perm_token", perm_token, torch.int32, (B * k,))):
         _dev(t, name, dt, shp)
-    dims = make_dims(B, d, h, n, k, _dt(x), _dt(w1), _dt(w_gate), capacity)
+    dims = make_dims(B, d, h, n, k, _dt(x), _dt(w1), _dt(w_gate), capacity, expert_layout)
     opts = make_opts(train, noise_floor, w_importance, w_load, gate_order)
     st = lib().moe_forward_noalloc(ctypes.byref(dims), ctypes.byref(opts), _ptr(x), _ptr(w_gate),
                                    _ptr(w_noise), _ptr(gate_bias), _ptr(eps if train else None),

@@ -169,3 +169,20 @@ def test_packed_hier_forward(B, a, b, k1, k2, d, h, dt):
     assert outs[0].keys() == outs[1].keys()
     for key in outs[0]:
         assert torch.equal(outs[0][key].view(torch.uint8), outs[1][key].view(torch.uint8)), key
+
+
+def test_packed_forward_noalloc():
+    """The allocation-free forward with packed weights: y and the losses
+    bit-identical to moe_forward with the natural layout."""
+    w = dg.workload("flat_bf16_n4096", tokens=900, n_experts=256)
+    announce("moe_forward_noalloc packed B=900 n=256")
+    inp = dg.make_inputs(w, with_bias=True)
+    g = gpu_inputs(inp)
+    p1, p2 = moe.moe_pack_expert_weights(g["w1"], g["w2"])
+    kw = dict(b1=g.get("b1"), b2=g.get("b2"), gate_bias=g.get("gate_bias"), train=True)
+    a = moe.moe_forward(g["x"], g["w_gate"], g["w_noise"], g["eps"], g["w1"], g["w2"], w.k, **kw)
+    b = moe.moe_forward_noalloc(g["x"], g["w_gate"], g["w_noise"], g["eps"], p1, p2, w.k,
+                                expert_layout=1, **kw)
+    torch.cuda.synchronize()
+    for key in ("y", "importance", "load", "losses"):
+        assert torch.equal(a[key].view(torch.uint8), b[key].view(torch.uint8)), key
